@@ -1,0 +1,215 @@
+/*
+ * CPU oracle for the Mamba-2 SSD selective-scan forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code with the HIP library.
+ *
+ * What it computes is the plain definition, one timestep at a time, in fp64:
+ *
+ *   dt_t   = clamp(softplus(dt_raw_t + dt_bias_h), dt_min, dt_max)
+ *   a_t    = exp(dt_t * A_h)                       (scalar decay per head)
+ *   h_t    = a_t * h_{t-1} + dt_t * x_t (outer) B_t   h_{-1} = initial state
+ *   y_t    = C_t . h_t + D_h * x_t
+ *   out_t  = y_t * silu(z_t)                         (only when z is given)
+ *
+ * Sources, by page (the pages are GitHub threads about the mamba kernels):
+ *  - The recurrence is the Mamba-2 state-space-duality (SSD) layer of
+ *    Dao & Gu, "Transformers are SSMs" (2024), which the flash-linear-attention
+ *    PR #49 page refers to ("Section 7.2 of the Mamba-2 paper").
+ *  - dt is a discretization input absorbed into the log-gate dt*A, A is
+ *    constant in time, there is no 1/sqrt(d) scaling of C.B, and B/C are shared
+ *    by groups of heads like grouped-query keys: the same page, its list of
+ *    differences between the simple_gla kernel and the mamba2_ssd kernel.
+ *  - dt_bias, dt_limit, D (one value per head), the SiLU gate applied before
+ *    any norm, initial_states and return_final_states: mamba issue #647, the
+ *    repro script's arguments.
+ *  - Continuation from a given state (chunked prefill): mamba issue #488.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *  - the state is stored as h[p][n] (headdim x dstate), the transpose of the
+ *    B x^T form; the mathematics are identical;
+ *  - y_t includes token t's own contribution (h_t is updated before use);
+ *  - the input is scaled by dt (not the zero-order-hold (e^{dtA}-1)/A);
+ *  - head h reads group g = h / (nheads / ngroups) (contiguous blocks);
+ *  - dt_limit clamps after softplus; softplus is always applied;
+ *  - the D skip is added before the gate: out = (C.h + D x) * silu(z).
+ *
+ * Layouts (row-major, contiguous):
+ *   x, z        [batch, seqlen, nheads, headdim]           float32 values
+ *   dt_raw      [batch, seqlen, nheads]                    float32 values
+ *   B, C        [batch, seqlen, ngroups, dstate]           float32 values
+ *   A, D, dt_bias [nheads]                                 float32 values
+ *   init, final [batch, nheads, headdim, dstate]           fp64
+ *   out         [batch, seqlen, nheads, headdim]           fp64
+ * The inputs arrive as float32 because every input of the method is an fp32
+ * or bf16 value, which float32 holds exactly; all arithmetic is fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(u) = log(1 + e^u), in the form that neither overflows nor
+ * cancels: max(u,0) + log1p(e^{-|u|}). */
+static double softplus(double u) { return (u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u))); }
+
+/* Discretization step of one (b, t, h): softplus of the biased raw value,
+ * clamped to [dt_min, dt_max] (mamba issue #647 passes dt_limit=(0, inf)). */
+static double step_dt(const float* dt_raw, const float* dt_bias, double dt_min, double dt_max,
+                      int64_t L, int64_t H, int64_t b, int64_t t, int64_t h) {
+    double u = (double)dt_raw[(b * L + t) * H + h] + (dt_bias ? (double)dt_bias[h] : 0.0);
+    double dt = softplus(u);
+    if (dt < dt_min) dt = dt_min;
+    if (dt > dt_max) dt = dt_max;
+    return dt;
+}
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+int oracle_max_threads(int nthreads) { return set_threads(nthreads); }
+
+/*
+ * The whole forward: out (and final state) for every (b, h) whose entry in
+ * head_mask is non-zero (head_mask == NULL: all).  Entries of out for masked-
+ * out heads are left untouched, so a caller can sample a few heads of a large
+ * problem.  Returns 0, or -1 on bad shapes.
+ */
+int oracle_ssd_fwd(const float* x, const float* dt_raw, const float* A, const float* B,
+                   const float* C, const float* D, const float* z, const float* dt_bias,
+                   double dt_min, double dt_max, const double* init, double* out,
+                   double* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
+                   int64_t headdim, int64_t dstate, int64_t ngroups,
+                   const unsigned char* head_mask, int nthreads) {
+    if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0)
+        return -1;
+    set_threads(nthreads);
+    const int64_t L = seqlen, H = nheads, P = headdim, N = dstate, G = ngroups;
+    const int64_t heads_per_group = H / G;
+    const int64_t pairs = batch * H;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        if (head_mask && !head_mask[bh]) continue;
+        const int64_t b = bh / H, h = bh % H;
+        const int64_t g = h / heads_per_group;
+        double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));
+        if (init)
+            memcpy(S, init + (b * H + h) * P * N, sizeof(double) * (size_t)(P * N));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(P * N));
+        const double Ah = (double)A[h];
+        const double Dh = D ? (double)D[h] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double dt = step_dt(dt_raw, dt_bias, dt_min, dt_max, L, H, b, t, h);
+            const double a = exp(dt * Ah);
+            const float* xt = x + ((b * L + t) * H + h) * P;
+            const float* Bt = B + ((b * L + t) * G + g) * N;
+            const float* Ct = C + ((b * L + t) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                const double u = dt * (double)xt[p];
+                double* Sp = S + p * N;
+                double y = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    Sp[n] = a * Sp[n] + u * (double)Bt[n];
+                    y += Sp[n] * (double)Ct[n];
+                }
+                y += Dh * (double)xt[p];
+                if (z) {
+                    const double zz = (double)z[((b * L + t) * H + h) * P + p];
+                    y *= zz / (1.0 + exp(-zz));
+                }
+                out[((b * L + t) * H + h) * P + p] = y;
+            }
+        }
+        if (final_states) memcpy(final_states + (b * H + h) * P * N, S, sizeof(double) * (size_t)(P * N));
+        free(S);
+    }
+    return 0;
+}
+
+/*
+ * Per-chunk intermediates of the chunked form, each written out from its
+ * definition (chunk c covers t in [c*Q, min((c+1)*Q, L))):
+ *   dt_out  [b, H, nc, Q]      dt_t                      (0 past the end)
+ *   cum_out [b, H, nc, Q]      sum_{r=cQ..t} dt_r*A_h    (held constant past the end)
+ *   chunk_states [b, nc, H, P, N]  the recurrence run over chunk c alone,
+ *                              starting from a zero state
+ *   states_in    [b, nc, H, P, N]  the state of the full recurrence just
+ *                              before chunk c's first step (init for c = 0)
+ * Any output pointer may be NULL.  Returns 0, or -1 on bad shapes.
+ */
+int oracle_ssd_chunk_intermediates(const float* x, const float* dt_raw, const float* A,
+                                   const float* B, const float* dt_bias, double dt_min,
+                                   double dt_max, const double* init, double* dt_out,
+                                   double* cum_out, double* chunk_states, double* states_in,
+                                   int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int64_t ngroups,
+                                   int64_t chunk_size, int nthreads) {
+    if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0 || chunk_size <= 0)
+        return -1;
+    set_threads(nthreads);
+    const int64_t L = seqlen, H = nheads, P = headdim, N = dstate, G = ngroups, Q = chunk_size;
+    const int64_t nc = (L + Q - 1) / Q;
+    const int64_t heads_per_group = H / G;
+    const int64_t pairs = batch * H;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        const int64_t b = bh / H, h = bh % H;
+        const int64_t g = h / heads_per_group;
+        const double Ah = (double)A[h];
+        double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));  /* full recurrence */
+        double* Sc = (double*)malloc(sizeof(double) * (size_t)(P * N)); /* chunk-local */
+        if (init)
+            memcpy(S, init + (b * H + h) * P * N, sizeof(double) * (size_t)(P * N));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(P * N));
+        for (int64_t c = 0; c < nc; ++c) {
+            const size_t state_off = (size_t)(((b * nc + c) * H + h) * P * N);
+            if (states_in) memcpy(states_in + state_off, S, sizeof(double) * (size_t)(P * N));
+            memset(Sc, 0, sizeof(double) * (size_t)(P * N));
+            double cum = 0.0;
+            for (int64_t q = 0; q < Q; ++q) {
+                const int64_t t = c * Q + q;
+                const size_t k = (size_t)(((b * H + h) * nc + c) * Q + q);
+                if (t >= L) {
+                    if (dt_out) dt_out[k] = 0.0;
+                    if (cum_out) cum_out[k] = cum;
+                    continue;
+                }
+                const double dt = step_dt(dt_raw, dt_bias, dt_min, dt_max, L, H, b, t, h);
+                cum += dt * Ah;
+                if (dt_out) dt_out[k] = dt;
+                if (cum_out) cum_out[k] = cum;
+                const double a = exp(dt * Ah);
+                const float* xt = x + ((b * L + t) * H + h) * P;
+                const float* Bt = B + ((b * L + t) * G + g) * N;
+                for (int64_t p = 0; p < P; ++p) {
+                    const double u = dt * (double)xt[p];
+                    for (int64_t n = 0; n < N; ++n) {
+                        S[p * N + n] = a * S[p * N + n] + u * (double)Bt[n];
+                        Sc[p * N + n] = a * Sc[p * N + n] + u * (double)Bt[n];
+                    }
+                }
+            }
+            if (chunk_states) memcpy(chunk_states + state_off, Sc, sizeof(double) * (size_t)(P * N));
+        }
+        free(S);
+        free(Sc);
+    }
+    return 0;
+}

@@ -1,0 +1,405 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each check below compares the C recurrence with a result fixed independently:
+the quadratic (masked-attention) form, closed forms, library routines
+(scipy.signal.lfilter, numpy.logaddexp), invariances of the mathematics, or
+the values printed on the mamba issue #647 page.  ``test_pins_catch_planted
+_mistakes`` compiles copies of the oracle with a mistake planted in each and
+checks that some pin fails for every one of them.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+from scipy.signal import lfilter
+from scipy.special import expit
+
+import oracle
+from oracle.quadratic import ssd_fwd_quadratic
+from ssd_workloads import random_small
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(1e-300, np.max(np.abs(b))))
+
+
+def _args(inp, with_init=True):
+    kw = dict(D=inp["D"], z=inp["z"], dt_bias=inp["dt_bias"])
+    if with_init and inp["initial_states"] is not None:
+        kw["initial_states"] = inp["initial_states"]
+    return (inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"]), kw
+
+
+# --------------------------------------------------------------------------
+# Pin functions: each takes an oracle front (module or OracleLib) and asserts.
+# --------------------------------------------------------------------------
+
+def pin_quadratic_form(orc):
+    """Recurrence == quadratic masked-attention form (flash-linear-attention
+    PR #49: q=C, k=B, v=dt*x, gate dt*A, no scaling, grouped keys)."""
+    cases = [
+        dict(seed=11, batch=2, seqlen=37, nheads=4, headdim=8, dstate=4, ngroups=2, init=True),
+        dict(seed=12, batch=1, seqlen=64, nheads=2, headdim=4, dstate=16, ngroups=1, gate=False),
+        dict(seed=13, batch=1, seqlen=23, nheads=6, headdim=3, dstate=5, ngroups=6, skip=False,
+             init=True),
+        dict(seed=14, batch=2, seqlen=50, nheads=4, headdim=8, dstate=8, ngroups=4),
+    ]
+    for c in cases:
+        inp = random_small(**c)
+        a, kw = _args(inp)
+        for lim in [(0.0, float("inf")), (0.01, 0.2)]:
+            out, fin = orc.ssd_fwd(*a, **kw, dt_limit=lim, return_final_states=True)
+            qo, qf = ssd_fwd_quadratic(*a, **kw, dt_limit=lim)
+            assert _rel(out, qo) < 1e-12, c
+            assert _rel(fin, qf) < 1e-12, c
+
+
+def pin_ngroups_invariance(orc):
+    """B, C replicated over G groups give exactly the G = 1 result."""
+    inp = random_small(21, batch=2, seqlen=40, nheads=8, headdim=4, dstate=8, ngroups=1,
+                       init=True)
+    a, kw = _args(inp)
+    ref, rfin = orc.ssd_fwd(*a, **kw, return_final_states=True)
+    x, dt, A, B, C = a
+    for G in (2, 4, 8):
+        out, fin = orc.ssd_fwd(x, dt, A, np.repeat(B, G, axis=2), np.repeat(C, G, axis=2), **kw,
+                               return_final_states=True)
+        assert np.array_equal(out, ref) and np.array_equal(fin, rfin), G
+
+
+def pin_head_group_map(orc):
+    """Head h reads group h // (H/G): each head equals a one-head run on its group."""
+    inp = random_small(22, batch=1, seqlen=30, nheads=6, headdim=4, dstate=4, ngroups=3,
+                       init=True)
+    a, kw = _args(inp)
+    out, fin = orc.ssd_fwd(*a, **kw, return_final_states=True)
+    x, dt, A, B, C = a
+    for h in range(6):
+        g = h // 2
+        o1, f1 = orc.ssd_fwd(x[:, :, h:h + 1], dt[:, :, h:h + 1], A[h:h + 1], B[:, :, g:g + 1],
+                             C[:, :, g:g + 1], D=inp["D"][h:h + 1], z=inp["z"][:, :, h:h + 1],
+                             dt_bias=inp["dt_bias"][h:h + 1],
+                             initial_states=inp["initial_states"][:, h:h + 1],
+                             return_final_states=True)
+        assert np.array_equal(o1[:, :, 0], out[:, :, h]) and np.array_equal(f1[:, 0], fin[:, h])
+
+
+def pin_continuation(orc):
+    """Scanning [0,k) then [k,L) from the returned state equals one full scan
+    (the chunked-prefill use of initial states, mamba issue #488)."""
+    inp = random_small(31, batch=2, seqlen=48, nheads=4, headdim=4, dstate=8, ngroups=2,
+                       init=True)
+    a, kw = _args(inp)
+    full, ffin = orc.ssd_fwd(*a, **kw, return_final_states=True)
+    x, dt, A, B, C = a
+    for k in (16, 17, 1, 47):
+        sl1, sl2 = slice(0, k), slice(k, None)
+        o1, f1 = orc.ssd_fwd(x[:, sl1], dt[:, sl1], A, B[:, sl1], C[:, sl1], D=inp["D"],
+                             z=inp["z"][:, sl1], dt_bias=inp["dt_bias"],
+                             initial_states=inp["initial_states"], return_final_states=True)
+        o2, f2 = orc.ssd_fwd(x[:, sl2], dt[:, sl2], A, B[:, sl2], C[:, sl2], D=inp["D"],
+                             z=inp["z"][:, sl2], dt_bias=inp["dt_bias"], initial_states=f1,
+                             return_final_states=True)
+        assert _rel(np.concatenate([o1, o2], axis=1), full) < 1e-13, k
+        assert _rel(f2, ffin) < 1e-13, k
+
+
+def pin_no_decay_prefix_sum(orc):
+    """A = 0: the state is a plain running sum of dt_s x_s B_s^T."""
+    inp = random_small(41, batch=1, seqlen=33, nheads=2, headdim=3, dstate=5, ngroups=1,
+                       gate=False)
+    A0 = np.zeros_like(inp["A"])
+    out = orc.ssd_fwd(inp["x"], inp["dt"], A0, inp["B"], inp["C"], D=inp["D"],
+                      dt_bias=inp["dt_bias"])
+    dtv = np.logaddexp(0.0, inp["dt"].astype(np.float64) + inp["dt_bias"])
+    for h in range(2):
+        upd = np.einsum("t,tp,tn->tpn", dtv[0, :, h], inp["x"][0, :, h].astype(np.float64),
+                        inp["B"][0, :, 0].astype(np.float64))
+        S = np.cumsum(upd, axis=0)
+        y = np.einsum("tpn,tn->tp", S, inp["C"][0, :, 0].astype(np.float64))
+        y += float(inp["D"][h]) * inp["x"][0, :, h].astype(np.float64)
+        assert _rel(out[0, :, h], y) < 1e-12
+
+
+def pin_geometric_series(orc):
+    """Constant dt, x, B, C: y_t = dt (B.C) x (1 - a^{t+1}) / (1 - a) + D x."""
+    L, P, N = 40, 3, 4
+    rng = np.random.default_rng(42)
+    xr = rng.standard_normal(P).astype(np.float32).astype(np.float64)
+    Br = rng.standard_normal(N).astype(np.float32)
+    Cr = rng.standard_normal(N).astype(np.float32)
+    x = np.broadcast_to(xr, (1, L, 1, P)).astype(np.float32)
+    B = np.broadcast_to(Br, (1, L, 1, N)).copy()
+    C = np.broadcast_to(Cr, (1, L, 1, N)).copy()
+    dtc, Ah, Dh = 0.125, -0.75, 0.5
+    dt = np.zeros((1, L, 1), np.float32)  # dt_limit (c, c) forces dt = c
+    out = orc.ssd_fwd(x, dt, np.array([Ah], np.float32), B, C, D=np.array([Dh], np.float32),
+                      dt_limit=(dtc, dtc))
+    a = np.exp(dtc * Ah)
+    t = np.arange(L)[:, None]
+    bc = float(np.dot(Br.astype(np.float64), Cr.astype(np.float64)))
+    want = dtc * bc * xr[None, :] * (1 - a ** (t + 1)) / (1 - a) + Dh * xr[None, :]
+    assert _rel(out[0, :, 0], want) < 1e-12
+
+
+def pin_iir_filter(orc):
+    """Constant dt: each state element is the first-order IIR filter
+    h_t = a h_{t-1} + dt x_t B_t (scipy.signal.lfilter), and y = C.h + D x."""
+    inp = random_small(51, batch=1, seqlen=64, nheads=1, headdim=2, dstate=3, ngroups=1,
+                       gate=False, init=True)
+    dtc = 0.3
+    out, fin = orc.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                           dt_limit=(dtc, dtc), initial_states=inp["initial_states"],
+                           return_final_states=True)
+    a = np.exp(dtc * float(inp["A"][0]))
+    x = inp["x"][0, :, 0].astype(np.float64)
+    B = inp["B"][0, :, 0].astype(np.float64)
+    C = inp["C"][0, :, 0].astype(np.float64)
+    h0 = inp["initial_states"][0, 0].astype(np.float64)
+    y = float(inp["D"][0]) * x
+    for p in range(2):
+        for n in range(3):
+            sig = dtc * x[:, p] * B[:, n]
+            hpn, _ = lfilter([1.0], [1.0, -a], sig, zi=[a * h0[p, n]])
+            y[:, p] += hpn * C[:, n]
+            assert abs(hpn[-1] - fin[0, 0, p, n]) < 1e-12 * max(1.0, abs(hpn[-1]))
+    assert _rel(out[0, :, 0], y) < 1e-12
+
+
+def pin_single_step(orc):
+    """L = 1: y_0 = dt (C.B) x + a C.h0 + D x, gated."""
+    inp = random_small(61, batch=1, seqlen=1, nheads=2, headdim=3, dstate=4, ngroups=1,
+                       init=True)
+    a_, kw = _args(inp)
+    out, fin = orc.ssd_fwd(*a_, **kw, return_final_states=True)
+    for h in range(2):
+        dt = np.logaddexp(0.0, float(inp["dt"][0, 0, h]) + float(inp["dt_bias"][h]))
+        a = np.exp(dt * float(inp["A"][h]))
+        x = inp["x"][0, 0, h].astype(np.float64)
+        B = inp["B"][0, 0, 0].astype(np.float64)
+        C = inp["C"][0, 0, 0].astype(np.float64)
+        h0 = inp["initial_states"][0, h].astype(np.float64)
+        hn = a * h0 + dt * np.outer(x, B)
+        y = hn @ C + float(inp["D"][h]) * x
+        zz = inp["z"][0, 0, h].astype(np.float64)
+        assert _rel(out[0, 0, h], y * zz * expit(zz)) < 1e-13
+        assert _rel(fin[0, h], hn) < 1e-13
+
+
+def pin_zero_B_or_C(orc):
+    """B = 0 or C = 0 (no initial state): out = D x silu(z)."""
+    inp = random_small(71, batch=1, seqlen=20, nheads=2, headdim=3, dstate=4, ngroups=1)
+    zz = inp["z"].astype(np.float64)
+    want = (inp["D"][None, None, :, None].astype(np.float64) * inp["x"].astype(np.float64)
+            * zz * expit(zz))
+    zero = np.zeros_like(inp["B"])
+    for B, C in ((zero, inp["C"]), (inp["B"], zero)):
+        out = orc.ssd_fwd(inp["x"], inp["dt"], inp["A"], B, C, D=inp["D"], z=inp["z"],
+                          dt_bias=inp["dt_bias"])
+        assert _rel(out, want) < 1e-14
+
+
+def pin_gate_and_linearity(orc):
+    """out(z) = out(no z) * silu(z); without gate or initial state the map is
+    linear in x."""
+    inp = random_small(81, batch=1, seqlen=25, nheads=2, headdim=4, dstate=4, ngroups=1)
+    base = orc.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                       dt_bias=inp["dt_bias"])
+    gated = orc.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                        z=inp["z"], dt_bias=inp["dt_bias"])
+    zz = inp["z"].astype(np.float64)
+    assert _rel(gated, base * zz * expit(zz)) < 1e-13
+    # dyadic inputs (k / 64, |k| < 2^10), so that 0.5 x1 - 2 x2 is exact in fp32
+    rng = np.random.default_rng(82)
+    x1 = (np.round(rng.standard_normal(inp["x"].shape) * 64) / 64).astype(np.float32)
+    x2 = (np.round(rng.standard_normal(inp["x"].shape) * 64) / 64).astype(np.float32)
+    run = lambda xx: orc.ssd_fwd(xx, inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                                 dt_bias=inp["dt_bias"])
+    mix = (0.5 * x1.astype(np.float64) - 2.0 * x2).astype(np.float32)
+    assert np.array_equal(mix.astype(np.float64), 0.5 * x1.astype(np.float64) - 2.0 * x2)
+    assert _rel(run(mix), 0.5 * run(x1) - 2.0 * run(x2)) < 1e-12
+
+
+def pin_dt_and_cumsum(orc):
+    """Intermediates: dt = clip(softplus(dt_raw + bias)) (numpy.logaddexp) and
+    cum = running sum of dt*A inside each chunk, ragged last chunk included."""
+    inp = random_small(91, batch=2, seqlen=45, nheads=3, headdim=2, dstate=2, ngroups=1)
+    for lim in [(0.0, float("inf")), (0.02, 0.5)]:
+        r = orc.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], 16,
+                                    dt_bias=inp["dt_bias"], dt_limit=lim)
+        u = inp["dt"].astype(np.float64) + inp["dt_bias"]
+        want = np.clip(np.logaddexp(0.0, u), *lim)                 # [b, L, H]
+        padded = np.zeros((2, 48, 3))
+        padded[:, :45] = want
+        got = r["dt"].reshape(2, 3, 48).transpose(0, 2, 1)
+        assert np.max(np.abs(got - padded)) < 1e-15
+        dA = padded * inp["A"].astype(np.float64)[None, None, :]
+        cum = np.cumsum(dA.reshape(2, 3, 16, 3), axis=2)           # [b, nc, Q, H]
+        assert np.max(np.abs(r["cum"] - cum.transpose(0, 3, 1, 2))) < 1e-13
+
+
+def pin_softplus_extremes(orc):
+    """softplus(u) ~ u for large u and ~ e^u for very negative u (no overflow)."""
+    x = np.ones((1, 4, 1, 1), np.float32)
+    B = np.ones((1, 4, 1, 1), np.float32)
+    dt = np.array([[[60.0], [-60.0], [0.0], [700.0]]], np.float32)
+    r = orc.chunk_intermediates(x, dt, np.array([-1.0], np.float32), B, 4)
+    got = r["dt"][0, 0, 0]
+    assert abs(got[0] - 60.0) < 1e-12 and abs(got[1] / np.exp(-60.0) - 1) < 1e-12
+    assert abs(got[2] - np.log(2.0)) < 1e-15 and got[3] == 700.0
+
+
+def pin_chunk_states(orc):
+    """chunk_states[c] = sum_{t in c} exp(cum_last - cum_t) dt_t x_t B_t^T and
+    states_in[c] = final state of a full run over [0, cQ)."""
+    inp = random_small(101, batch=1, seqlen=40, nheads=2, headdim=3, dstate=4, ngroups=1,
+                       init=True)
+    Q = 16
+    r = orc.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
+                                dt_bias=inp["dt_bias"], initial_states=inp["initial_states"])
+    x = inp["x"].astype(np.float64)
+    B = inp["B"].astype(np.float64)
+    for c in range(3):
+        for h in range(2):
+            lo, hi = c * Q, min(40, (c + 1) * Q)
+            dtc = r["dt"][0, h, c, :hi - lo]
+            cum = r["cum"][0, h, c, :hi - lo]
+            w = np.exp(cum[-1] - cum) * dtc
+            want = np.einsum("t,tp,tn->pn", w, x[0, lo:hi, h], B[0, lo:hi, 0])
+            assert _rel(r["chunk_states"][0, c, h], want) < 1e-12
+        if c > 0:
+            sl = slice(0, c * Q)
+            _, fin = orc.ssd_fwd(inp["x"][:, sl], inp["dt"][:, sl], inp["A"], inp["B"][:, sl],
+                                 inp["C"][:, sl], dt_bias=inp["dt_bias"],
+                                 initial_states=inp["initial_states"], return_final_states=True)
+            assert _rel(r["states_in"][0, c], fin[0]) < 1e-13
+        else:
+            assert np.array_equal(r["states_in"][0, 0], inp["initial_states"][0].astype(np.float64))
+
+
+def pin_head_mask(orc):
+    """A sampled run equals the full run on the sampled (b, h) pairs."""
+    inp = random_small(111, batch=2, seqlen=20, nheads=4, headdim=3, dstate=4, ngroups=2)
+    a, kw = _args(inp)
+    full = orc.ssd_fwd(*a, **kw)
+    mask = np.zeros((2, 4), bool)
+    mask[0, 1] = mask[1, 3] = True
+    part = orc.ssd_fwd(*a, **kw, head_mask=mask)
+    assert np.array_equal(part[0, :, 1], full[0, :, 1]) and np.array_equal(part[1, :, 3],
+                                                                          full[1, :, 3])
+    assert np.isnan(part[0, :, 0]).all()
+
+
+def pin_batch_permutation(orc):
+    """Permuting the batch permutes the outputs."""
+    inp = random_small(121, batch=3, seqlen=15, nheads=2, headdim=2, dstate=3, ngroups=1,
+                       init=True)
+    a, kw = _args(inp)
+    out = orc.ssd_fwd(*a, **kw)
+    perm = [2, 0, 1]
+    pa = [t[perm] if t.ndim > 1 else t for t in a]
+    pk = {k: (v[perm] if (v is not None and v.ndim > 1) else v) for k, v in kw.items()}
+    assert np.array_equal(orc.ssd_fwd(*pa, **pk), out[perm])
+
+
+def _block_out000(orc, ngroups, per_group_norm):
+    """out[0,0,0] of the Mamba-2 block of mamba issue #647's repro script.
+
+    Only token 0 matters for out[0,0,0].  With every input 0.1 the causal
+    width-4 conv sees one tap at t = 0: 0.1*0.1 + 0.1, then SiLU, for each of
+    x, B, C; dt_raw = 0.1, dt_bias = 0.1; z = 0.1.  The oracle's scan gives the
+    gated y; the test then applies the RMSNorm (weight 0.1, eps 1e-5) over the
+    whole width or per group, and the all-0.1 out_proj row plus bias 0.1."""
+    dim, P, N, H = 2048, 64, 128, 32
+    conv0 = 0.1 * 0.1 + 0.1
+    s = conv0 * expit(conv0)
+    x = np.full((1, 1, H, P), s, np.float32)
+    B = np.full((1, 1, ngroups, N), s, np.float32)
+    dt = np.full((1, 1, H), 0.1, np.float32)
+    A = np.full((H,), -1.0, np.float32)
+    D = (np.arange(H) * 1000.0).astype(np.float32)
+    z = np.full((1, 1, H, P), 0.1, np.float32)
+    y = orc.ssd_fwd(x, dt, A, B, B.copy(), D=D, z=z,
+                    dt_bias=np.full((H,), 0.1, np.float32))[0, 0].reshape(dim)
+    parts = y.reshape(ngroups if per_group_norm else 1, -1)
+    normed = parts / np.sqrt((parts ** 2).mean(axis=1, keepdims=True) + 1e-5) * 0.1
+    return 0.1 * normed.sum() + 0.1
+
+
+def pin_page_printed_block_values(orc):
+    """The values printed on the mamba issue #647 page (tests/golden): the
+    full-width norm gives the python reference's 17.6951 for every ngroups, a
+    per-group norm gives the combined kernel's 18.8725 / 19.5926.  The page's
+    values come from fp32 GPU runs printed to 4 decimals, and its two fp32
+    implementations already differ by 1e-4 at ngroups = 1 (17.6950 vs 17.6951),
+    so agreement is asked to 2e-4.  The scan's own recurrence moves this value
+    by only ~1e-4 (token 0 only); what the fixture pins is dt = softplus(raw +
+    bias), the per-head D skip and the gate feeding the block."""
+    rows = [l.split() for l in open(os.path.join(ROOT, "tests/golden/block_out000_ngroups.txt"))
+            if l.strip() and not l.startswith("#")]
+    for g, combined, ref in rows:
+        g, combined, ref = int(g), float(combined), float(ref)
+        assert abs(_block_out000(orc, g, False) - ref) <= 2e-4
+        assert abs(_block_out000(orc, g, True) - combined) <= 2e-4
+
+
+PINS = [pin_quadratic_form, pin_ngroups_invariance, pin_head_group_map, pin_continuation,
+        pin_no_decay_prefix_sum, pin_geometric_series, pin_iir_filter, pin_single_step,
+        pin_zero_B_or_C, pin_gate_and_linearity, pin_dt_and_cumsum, pin_softplus_extremes,
+        pin_chunk_states, pin_head_mask, pin_batch_permutation,
+        pin_page_printed_block_values]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(oracle)
+
+
+# Mistakes planted in copies of the oracle source: (description, old, new).
+MUTANTS = [
+    ("decay sign flipped", "const double a = exp(dt * Ah);", "const double a = exp(-dt * Ah);"),
+    ("decay dropped", "Sp[n] = a * Sp[n] + u * (double)Bt[n];", "Sp[n] = Sp[n] + u * (double)Bt[n];"),
+    ("C read as B", "y += Sp[n] * (double)Ct[n];", "y += Sp[n] * (double)Bt[n];"),
+    ("group map h % G", "const int64_t g = h / heads_per_group;\n        double* S",
+     "const int64_t g = h % G;\n        double* S"),
+    ("D skip dropped", "y += Dh * (double)xt[p];", "y += 0.0 * (double)xt[p];"),
+    ("input not scaled by dt", "const double u = dt * (double)xt[p];\n                double* Sp",
+     "const double u = (double)xt[p];\n                double* Sp"),
+    ("softplus wrong", "log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
+    ("dt_bias dropped", "(dt_bias ? (double)dt_bias[h] : 0.0)", "0.0"),
+    ("sigmoid gate", "y *= zz / (1.0 + exp(-zz));", "y *= 1.0 / (1.0 + exp(-zz));"),
+    ("output before update",
+     "Sp[n] = a * Sp[n] + u * (double)Bt[n];\n                    y += Sp[n] * (double)Ct[n];",
+     "y += Sp[n] * (double)Ct[n];\n                    Sp[n] = a * Sp[n] + u * (double)Bt[n];"),
+    ("initial state ignored", "if (init)\n            memcpy(S, init + (b * H + h) * P * N, "
+     "sizeof(double) * (size_t)(P * N));\n        else\n            memset(S, 0, sizeof(double) * "
+     "(size_t)(P * N));\n        const double Ah",
+     "memset(S, 0, sizeof(double) * (size_t)(P * N));\n        const double Ah"),
+    ("x transposed index", "const float* xt = x + ((b * L + t) * H + h) * P;\n            const float* Bt = B + ((b * L + t) * G + g) * N;\n            const float* Ct",
+     "const float* xt = x + ((b * L + (L - 1 - t)) * H + h) * P;\n            const float* Bt = B + ((b * L + t) * G + g) * N;\n            const float* Ct"),
+    ("dt clamp swapped", "if (dt < dt_min) dt = dt_min;", "if (dt < dt_min) dt = dt_max;"),
+]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc needed to build oracle mutants")
+def test_pins_catch_planted_mistakes():
+    src = open(oracle.SOURCE).read()
+    with tempfile.TemporaryDirectory() as tmp:
+        for i, (desc, old, new) in enumerate(MUTANTS):
+            assert src.count(old) >= 1, f"mutation anchor missing: {desc}"
+            msrc = os.path.join(tmp, f"m{i}.c")
+            with open(msrc, "w") as f:
+                f.write(src.replace(old, new, 1))
+            lib = oracle.OracleLib(oracle.compile_library(msrc, os.path.join(tmp, f"m{i}.so")))
+            caught = []
+            for pin in PINS:
+                try:
+                    pin(lib)
+                except (AssertionError, ValueError, FloatingPointError):
+                    caught.append(pin.__name__)
+            assert caught, f"no pin catches the planted mistake: {desc}"

@@ -1,0 +1,162 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD chunked selective-scan
+ * forward.
+ *
+ * The operation (per batch row b and head h, t = 0 .. seqlen-1):
+ *
+ *   dt_t  = min(max(softplus(dt_raw[b,t,h] + dt_bias[h]), dt_min), dt_max)
+ *   h_t   = exp(dt_t * A[h]) * h_{t-1} + dt_t * x[b,t,h,:] (outer) B[b,t,g,:]
+ *   y_t   = h_t . C[b,t,g,:] + D[h] * x[b,t,h,:]
+ *   out[b,t,h,:] = y_t * silu(z[b,t,h,:])            (y_t when z is NULL)
+ *
+ * with g = h / (nheads / ngroups), h_{-1} = initial_states[b,h] (zeros when
+ * NULL) and final_states[b,h] = h_{seqlen-1}.  The state h_t is stored as a
+ * headdim x dstate matrix (element [p][n]).
+ *
+ * Where each piece comes from (the pages are GitHub threads on the mamba
+ * kernels):
+ *  - the recurrence is the Mamba-2 state-space-duality layer (Dao & Gu 2024),
+ *    which the flash-linear-attention PR #49 page ("Replace mamba2
+ *    mamba_chunk_scan_combined triton kernel by simple_gla triton kernel")
+ *    cites; the same page's list of differences between simple_gla and the
+ *    mamba2_ssd kernel fixes the [batch, seq, head, hidden] layout, the
+ *    absence of a 1/sqrt(d) scale on C.B, dt as a discretization input folded
+ *    into the gate dt*A with A constant in time, and B/C shared by groups of
+ *    heads ("group query attention");
+ *  - dt_bias, dt_limit, D with one value per head, the SiLU gate applied
+ *    before any norm, initial_states and return_final_states are the
+ *    arguments of the repro script on mamba issue #647 ("...exhibit large
+ *    numerical differences when ngroups > 1");
+ *  - starting from a given state for chunked prefill is mamba issue #488
+ *    ("feat: Initial state support for Mamba SSM (1)").
+ *
+ * The work is done in chunks of chunk_size timesteps: a dt/cumsum pass, a
+ * per-chunk state pass on the matrix cores, a sequential inter-chunk state
+ * pass, and a chunk-scan pass with the D-skip / z-gate epilogue fused in.
+ * The result does not depend on chunk_size beyond rounding.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+/* Element type of x, dt, B, C, z and out.  A, D, dt_bias, dt_limit and both
+ * state tensors are always float32; accumulation is always float32. */
+#define SSD_F32 0
+#define SSD_BF16 1
+
+/* Status codes. */
+#define SSD_OK 0
+#define SSD_ERR_INVALID_ARG (-1) /* null required pointer, negative or zero size where a
+                                    positive one is needed, nheads % ngroups != 0, dt_min or
+                                    dt_max NaN, dt_min > dt_max, unknown dtype, out
+                                    overlapping an input, final_states partially overlapping
+                                    initial_states */
+#define SSD_ERR_UNSUPPORTED (-2) /* a (headdim, dstate, chunk_size) combination not compiled:
+                                    headdim must be 64, dstate one of 16/32/64/128, chunk_size
+                                    one of 64/128/256 */
+#define SSD_ERR_ALIGNMENT (-3)   /* x, z, out, B, C, states not 16-byte aligned; dt, A, D,
+                                    dt_bias not aligned to their element; workspace not
+                                    256-byte aligned */
+#define SSD_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than ssd_scan_fwd_workspace_size */
+#define SSD_ERR_HIP (-5)         /* a kernel launch failed (hipGetLastError) */
+
+/*
+ * ssd_scan_fwd -- enqueue the forward on `stream`.
+ *
+ * Arguments (all pointers are device memory owned by the caller):
+ *   x        [batch, seqlen, nheads, headdim]   dtype       required
+ *   dt       [batch, seqlen, nheads]            dtype       required (raw, before softplus)
+ *   A        [nheads]                           float32     required
+ *   B        [batch, seqlen, ngroups, dstate]   dtype       required
+ *   C        [batch, seqlen, ngroups, dstate]   dtype       required
+ *   D        [nheads]                           float32     NULL: no skip term
+ *   z        [batch, seqlen, nheads, headdim]   dtype       NULL: no gate
+ *   dt_bias  [nheads]                           float32     NULL: zero bias
+ *   dt_min, dt_max    clamp applied after softplus ((0, +inf) leaves dt unchanged)
+ *   chunk_size        timesteps per chunk (64, 128 or 256)
+ *   ngroups           number of B/C groups; must divide nheads
+ *   initial_states [batch, nheads, headdim, dstate] float32  NULL: zero state
+ *   out      [batch, seqlen, nheads, headdim]   dtype       required; written
+ *   final_states [batch, nheads, headdim, dstate] float32   NULL: not returned;
+ *                     may be the same pointer as initial_states (in-place
+ *                     continuation), but must not partially overlap it
+ *   batch, seqlen     >= 0 (batch == 0: nothing is done; seqlen == 0:
+ *                     final_states = initial_states or zeros)
+ *   nheads, headdim, dstate  > 0
+ *   dtype    SSD_F32 or SSD_BF16 (bf16 output is rounded to nearest even)
+ *   workspace, workspace_bytes  scratch of at least
+ *                     ssd_scan_fwd_workspace_size(...) bytes, 256-byte aligned
+ *   stream   HIP stream the kernels are enqueued on (0: the null stream)
+ *
+ * All tensors are contiguous row-major.  `out` must not overlap any input.
+ * Every argument is checked before anything is enqueued; on an error nothing
+ * is launched and nothing is written.  The call does not synchronize: errors
+ * inside a kernel surface at the caller's next synchronization.  The library
+ * allocates no memory and keeps no pointer after the call returns; calls are
+ * reentrant and deterministic (bitwise identical results run to run).
+ *
+ * After the enqueued work completes, the workspace holds the intermediates
+ * (float32, in this order, each region starting on a 256-byte boundary):
+ *   dt        [batch, nheads, nchunks, chunk_size]   0 past the sequence end
+ *   dA_cumsum [batch, nheads, nchunks, chunk_size]   in-chunk running sum of dt*A
+ *   chunk_states [batch, nchunks, nheads, headdim, dstate]  each chunk's own
+ *             contribution (the recurrence over the chunk from a zero state)
+ *   states_in [batch, nchunks, nheads, headdim, dstate]  the state entering
+ *             each chunk
+ * with nchunks = ceil(seqlen / chunk_size).
+ */
+int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
+                 int chunk_size, int ngroups, const float* initial_states, void* out,
+                 float* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
+                 int64_t headdim, int64_t dstate, int dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssd_scan_fwd needs for these sizes (0 for an empty
+ * problem).  Returns 0 as well for arguments ssd_scan_fwd would reject;
+ * pure host computation, no HIP call. */
+size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
+                                   int dtype);
+
+/* Static text for a status code ("unknown status" for others). */
+const char* ssd_status_string(int status);
+
+/* SSD_ABI_VERSION of the loaded library. */
+int ssd_abi_version(void);
+
+/*
+ * Per-stage timing, for measurement.  A timing object holds HIP events;
+ * ssd_scan_fwd_timed behaves exactly like ssd_scan_fwd and also records an
+ * event before the first stage and after each stage on `stream`.
+ * ssd_timing_read waits for those events and writes the milliseconds spent in
+ * each stage (SSD_NUM_STAGES floats: dt/cumsum, chunk state, state passing,
+ * chunk scan).  Returns SSD_OK or SSD_ERR_HIP / SSD_ERR_INVALID_ARG.
+ */
+#define SSD_NUM_STAGES 4
+typedef struct ssd_timing ssd_timing;
+int ssd_timing_create(ssd_timing** out);
+int ssd_timing_destroy(ssd_timing* t);
+int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       float dt_min, float dt_max, int chunk_size, int ngroups,
+                       const float* initial_states, void* out, float* final_states,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, ssd_timing* timing);
+int ssd_timing_read(ssd_timing* t, float* stage_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,194 @@
+"""ctypes binding of ``libssd.so`` (the C ABI in ``include/ssd.h``).
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates the outputs and the workspace with torch, and passes raw
+device pointers plus torch's current HIP stream to ``ssd_scan_fwd``.  Every
+step of the scan runs in the HIP kernels; there is no other code path, and a
+missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_F32 = 0
+SSD_BF16 = 1
+SSD_NUM_STAGES = 4
+STAGES = ("dt_cumsum", "chunk_state", "state_passing", "chunk_scan")
+
+_lib = None
+
+
+class SsdError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ssd_scan_fwd failed: {message} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libssd.so``.  torch is imported first so that the library binds
+    to the HIP runtime torch already loaded (both carry the same soname), and
+    torch's streams are valid handles for it."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (binds the HIP runtime first)
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with __graft_entry__.build() "
+            "(python -m selective_state_space_ssd_amd._build); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    p, i64, f, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    fwd_args = [p, p, p, p, p, p, p, p, f, f, i, i, p, p, p, i64, i64, i64, i64, i64, i, p,
+                ctypes.c_size_t, p]
+    lib.ssd_scan_fwd.argtypes = fwd_args
+    lib.ssd_scan_fwd.restype = i
+    lib.ssd_scan_fwd_timed.argtypes = fwd_args + [p]
+    lib.ssd_scan_fwd_timed.restype = i
+    lib.ssd_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
+    lib.ssd_scan_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_status_string.argtypes = [i]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_abi_version.argtypes = []
+    lib.ssd_abi_version.restype = i
+    lib.ssd_timing_create.argtypes = [ctypes.POINTER(p)]
+    lib.ssd_timing_create.restype = i
+    lib.ssd_timing_destroy.argtypes = [p]
+    lib.ssd_timing_destroy.restype = i
+    lib.ssd_timing_read.argtypes = [p, ctypes.POINTER(ctypes.c_float)]
+    lib.ssd_timing_read.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssd_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load_library().ssd_abi_version())
+
+
+def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype) -> int:
+    return int(load_library().ssd_scan_fwd_workspace_size(
+        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+
+
+def _check(status: int):
+    if status != 0:
+        raise SsdError(status, status_string(status))
+
+
+class Timing:
+    """Per-stage HIP-event timing of one ``scan_fwd`` call (see ssd_timing_*)."""
+
+    def __init__(self):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.ssd_timing_create(ctypes.byref(h)))
+        self.handle = h
+
+    def read(self):
+        """Milliseconds per stage, in STAGES order (waits for the events)."""
+        buf = (ctypes.c_float * SSD_NUM_STAGES)()
+        _check(load_library().ssd_timing_read(self.handle, buf))
+        return [float(v) for v in buf]
+
+    def __del__(self):
+        if getattr(self, "handle", None) is not None and _lib is not None:
+            _lib.ssd_timing_destroy(self.handle)
+            self.handle = None
+
+
+def scan_fwd_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min, dt_max,
+                 chunk_size, ngroups, init_ptr, out_ptr, final_ptr, batch, seqlen, nheads,
+                 headdim, dstate, dtype, ws_ptr, ws_bytes, stream, timing: Optional[Timing] = None
+                 ) -> int:
+    """Direct call of the C entry point with integer pointers; returns the status."""
+    lib = load_library()
+    args = (x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, float(dt_min),
+            float(dt_max), int(chunk_size), int(ngroups), init_ptr, out_ptr, final_ptr,
+            int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(dtype), ws_ptr,
+            int(ws_bytes), stream)
+    if timing is None:
+        return int(lib.ssd_scan_fwd(*args))
+    return int(lib.ssd_scan_fwd_timed(*args, timing.handle))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.inf),
+             chunk_size: int = 128, initial_states=None, return_final_states: bool = False,
+             out=None, final_states=None, workspace=None, timing: Optional[Timing] = None):
+    """SSD chunked selective-scan forward on the GPU.
+
+    x [b, L, H, P], dt [b, L, H], B/C [b, L, G, N], z like x: float32 or
+    bfloat16 (all the same); A, D, dt_bias [H] and initial_states [b, H, P, N]
+    float32.  Returns out (x's dtype), or (out, final_states) with
+    ``return_final_states``.  ``out``, ``final_states`` and ``workspace``
+    (uint8) may be given to avoid allocations; ``final_states`` may be the
+    ``initial_states`` tensor itself (in-place continuation)."""
+    import torch
+
+    load_library()
+    if x.dtype == torch.float32:
+        dtype = SSD_F32
+    elif x.dtype == torch.bfloat16:
+        dtype = SSD_BF16
+    else:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if x.dim() != 4 or B.dim() != 4 or C.shape != B.shape or dt.dim() != 3:
+        raise ValueError("expected x [b,L,H,P], dt [b,L,H], B and C [b,L,G,N]")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, L, H) or tuple(B.shape[:2]) != (b, L):
+        raise ValueError("dt / B / C shapes do not match x")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    for name, t, want in (("dt", dt, x.dtype), ("B", B, x.dtype), ("C", C, x.dtype),
+                          ("z", z, x.dtype), ("A", A, torch.float32), ("D", D, torch.float32),
+                          ("dt_bias", dt_bias, torch.float32),
+                          ("initial_states", initial_states, torch.float32)):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, x on {dev}")
+        if t.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tuple(A.shape) != (H,):
+        raise ValueError("A must have shape [nheads]")
+    for name, t in (("D", D), ("dt_bias", dt_bias)):
+        if t is not None and tuple(t.shape) != (H,):
+            raise ValueError(f"{name} must have shape [nheads]")
+    if z is not None and z.shape != x.shape:
+        raise ValueError("z must have x's shape")
+    if initial_states is not None and tuple(initial_states.shape) != (b, H, P, N):
+        raise ValueError("initial_states must have shape [b, H, P, N]")
+
+    if out is None:
+        out = torch.empty_like(x)
+    if return_final_states and final_states is None:
+        final_states = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    ws_bytes = workspace_size(b, L, H, P, N, G, chunk_size, dtype)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    status = scan_fwd_raw(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+        dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),
+        _ptr(final_states) if return_final_states else None, b, L, H, P, N, dtype,
+        _ptr(workspace), workspace.numel(), stream, timing)
+    _check(status)
+    return (out, final_states) if return_final_states else out

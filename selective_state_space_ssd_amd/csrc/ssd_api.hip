@@ -1,0 +1,256 @@
+// C ABI of the SSD scan forward: argument checks, workspace layout and the
+// launch sequence.  Declarations and the contract are in include/ssd.h.
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+
+#include "../../include/ssd.h"
+#include "ssd_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte range [p, p + n) of a tensor; used for overlap checks.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + (uintptr_t)bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Multiply non-negative sizes, failing on int64 overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Layout {
+  int64_t nc = 0;
+  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, total = 0;
+};
+
+// Shape checks shared by the workspace query and the entry point.
+int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int ngroups, int chunk_size, int dtype, Layout* lay) {
+  if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+      chunk_size <= 0)
+    return SSD_ERR_INVALID_ARG;
+  if (nheads % ngroups != 0) return SSD_ERR_INVALID_ARG;
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  if (!ssd::config_supported(headdim, dstate, chunk_size)) return SSD_ERR_UNSUPPORTED;
+  const int64_t nc = (seqlen + chunk_size - 1) / chunk_size;
+  // every element count must fit in int64 and every grid in its limits
+  int64_t t1, t2, t3, pn, per_chunk;
+  if (!mul_ok(batch, seqlen, &t1) || !mul_ok(t1, nheads, &t2) || !mul_ok(t2, headdim, &t3))
+    return SSD_ERR_INVALID_ARG;
+  if (!mul_ok(t1, ngroups, &t2) || !mul_ok(t2, dstate, &t3)) return SSD_ERR_INVALID_ARG;
+  if (!mul_ok(headdim, dstate, &pn) || !mul_ok(pn, nheads, &per_chunk)) return SSD_ERR_INVALID_ARG;
+  int64_t units;
+  if (!mul_ok(batch, nc, &t1) || !mul_ok(t1, nheads, &units)) return SSD_ERR_INVALID_ARG;
+  if (units > INT32_MAX || nc > 65535 || batch > 65535 || nheads > 65535)
+    return SSD_ERR_UNSUPPORTED;
+  int64_t dtn, stn;
+  if (!mul_ok(units, chunk_size, &dtn) || !mul_ok(units, pn, &stn)) return SSD_ERR_INVALID_ARG;
+  if (stn > INT64_MAX / 8) return SSD_ERR_INVALID_ARG;
+  lay->nc = nc;
+  lay->off_dt = 0;
+  lay->off_cum = round_up((size_t)dtn * 4);
+  lay->off_states = lay->off_cum + round_up((size_t)dtn * 4);
+  lay->off_states_in = lay->off_states + round_up((size_t)stn * 4);
+  lay->total = lay->off_states_in + round_up((size_t)stn * 4);
+  if (batch == 0 || seqlen == 0) lay->total = 0;
+  return SSD_OK;
+}
+
+int validate(const void* x, const void* dt, const float* A, const void* B, const void* C,
+             const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
+             int chunk_size, int ngroups, const float* initial_states, void* out,
+             float* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
+             int64_t headdim, int64_t dstate, int dtype, void* workspace,
+             size_t workspace_bytes, Layout* lay) {
+  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, lay);
+  if (st != SSD_OK) return st;
+  if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return SSD_ERR_INVALID_ARG;
+  if (!A) return SSD_ERR_INVALID_ARG;
+  const bool nonempty = batch > 0 && seqlen > 0;
+  if (nonempty && (!x || !dt || !B || !C || !out)) return SSD_ERR_INVALID_ARG;
+
+  const size_t es = dtype == SSD_BF16 ? 2 : 4;
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4)) return SSD_ERR_ALIGNMENT;
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(B, 16) ||
+      !aligned(C, 16) || !aligned(dt, es) || !aligned(initial_states, 16) ||
+      !aligned(final_states, 16))
+    return SSD_ERR_ALIGNMENT;
+  // overlap rules: out against every input; final against init (equal is fine)
+  const int64_t nx = batch * seqlen * nheads * headdim;
+  const int64_t nbc = batch * seqlen * ngroups * dstate;
+  const int64_t nst = batch * nheads * headdim * dstate;
+  if (nonempty) {
+    const Span so = span(out, nx * (int64_t)es);
+    const Span ins[] = {span(x, nx * (int64_t)es), span(dt, batch * seqlen * nheads * (int64_t)es),
+                        span(B, nbc * (int64_t)es), span(C, nbc * (int64_t)es),
+                        z ? span(z, nx * (int64_t)es) : Span{0, 0}};
+    for (const Span& s : ins)
+      if (s.hi > s.lo && overlap(so, s)) return SSD_ERR_INVALID_ARG;
+    if (final_states && overlap(so, span(final_states, nst * 4))) return SSD_ERR_INVALID_ARG;
+    if (lay->total > 0 && overlap(so, span(workspace, (int64_t)lay->total)))
+      return SSD_ERR_INVALID_ARG;
+  }
+  if (final_states && initial_states && final_states != initial_states &&
+      overlap(span(final_states, nst * 4), span(initial_states, nst * 4)))
+    return SSD_ERR_INVALID_ARG;
+  // the workspace is checked last: a call that gets past it launches kernels
+  if (lay->total > 0) {
+    if (!workspace || workspace_bytes < lay->total) return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return SSD_ERR_ALIGNMENT;
+  }
+  return SSD_OK;
+}
+
+}  // namespace
+
+struct ssd_timing {
+  hipEvent_t ev[SSD_NUM_STAGES + 1];
+  bool recorded;
+};
+
+static int run(const void* x, const void* dt, const float* A, const void* B, const void* C,
+               const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
+               int chunk_size, int ngroups, const float* initial_states, void* out,
+               float* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
+               int64_t headdim, int64_t dstate, int dtype, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, ssd_timing* timing) {
+  Layout lay;
+  int st = validate(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups,
+                    initial_states, out, final_states, batch, seqlen, nheads, headdim, dstate,
+                    dtype, workspace, workspace_bytes, &lay);
+  if (st != SSD_OK) return st;
+  if (batch == 0) return SSD_OK;
+
+  ssd::Problem p;
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
+  p.dt_min = dt_min; p.dt_max = dt_max; p.init = initial_states; p.out = out;
+  p.final_states = final_states;
+  p.b = batch; p.L = seqlen; p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups;
+  p.Q = chunk_size; p.nc = lay.nc; p.bf16 = dtype == SSD_BF16;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_dt = lay.total ? reinterpret_cast<float*>(ws + lay.off_dt) : nullptr;
+  p.ws_cum = lay.total ? reinterpret_cast<float*>(ws + lay.off_cum) : nullptr;
+  p.ws_states = lay.total ? reinterpret_cast<float*>(ws + lay.off_states) : nullptr;
+  p.ws_states_in = lay.total ? reinterpret_cast<float*>(ws + lay.off_states_in) : nullptr;
+
+  auto mark = [&](int i) -> bool {
+    return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
+  };
+  if (!mark(0)) return SSD_ERR_HIP;
+  if (seqlen > 0) {
+    if (ssd::launch_dt_cumsum(p, stream) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
+    if (ssd::launch_chunk_state(p, stream) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
+  } else if (!mark(1) || !mark(2)) {
+    return SSD_ERR_HIP;
+  }
+  // state passing also covers seqlen == 0: final = initial state (or zeros)
+  if (seqlen > 0 || final_states) {
+    if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
+  }
+  if (!mark(3)) return SSD_ERR_HIP;
+  if (seqlen > 0 && ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!mark(4)) return SSD_ERR_HIP;
+  if (timing) timing->recorded = true;
+  return SSD_OK;
+}
+
+extern "C" {
+
+int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
+                 int chunk_size, int ngroups, const float* initial_states, void* out,
+                 float* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
+                 int64_t headdim, int64_t dstate, int dtype, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
+             out, final_states, batch, seqlen, nheads, headdim, dstate, dtype, workspace,
+             workspace_bytes, stream, nullptr);
+}
+
+int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
+                       const void* C, const float* D, const void* z, const float* dt_bias,
+                       float dt_min, float dt_max, int chunk_size, int ngroups,
+                       const float* initial_states, void* out, float* final_states,
+                       int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, ssd_timing* timing) {
+  if (!timing) return SSD_ERR_INVALID_ARG;
+  return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
+             out, final_states, batch, seqlen, nheads, headdim, dstate, dtype, workspace,
+             workspace_bytes, stream, timing);
+}
+
+size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
+                                   int dtype) {
+  Layout lay;
+  if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, &lay) !=
+      SSD_OK)
+    return 0;
+  return lay.total;
+}
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SSD_ERR_ALIGNMENT: return "misaligned pointer";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+int ssd_timing_create(ssd_timing** out) {
+  if (!out) return SSD_ERR_INVALID_ARG;
+  ssd_timing* t = new (std::nothrow) ssd_timing();
+  if (!t) return SSD_ERR_HIP;
+  for (int i = 0; i <= SSD_NUM_STAGES; ++i) {
+    if (hipEventCreate(&t->ev[i]) != hipSuccess) {
+      for (int k = 0; k < i; ++k) (void)hipEventDestroy(t->ev[k]);
+      delete t;
+      return SSD_ERR_HIP;
+    }
+  }
+  t->recorded = false;
+  *out = t;
+  return SSD_OK;
+}
+
+int ssd_timing_destroy(ssd_timing* t) {
+  if (!t) return SSD_ERR_INVALID_ARG;
+  for (int i = 0; i <= SSD_NUM_STAGES; ++i) (void)hipEventDestroy(t->ev[i]);
+  delete t;
+  return SSD_OK;
+}
+
+int ssd_timing_read(ssd_timing* t, float* stage_ms) {
+  if (!t || !stage_ms || !t->recorded) return SSD_ERR_INVALID_ARG;
+  if (hipEventSynchronize(t->ev[SSD_NUM_STAGES]) != hipSuccess) return SSD_ERR_HIP;
+  for (int i = 0; i < SSD_NUM_STAGES; ++i) {
+    if (hipEventElapsedTime(&stage_ms[i], t->ev[i], t->ev[i + 1]) != hipSuccess)
+      return SSD_ERR_HIP;
+  }
+  return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Device-side helpers shared by the SSD scan kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // storage of a bfloat16 value
+
+constexpr int kWave = 64;
+
+// ---- element conversion ---------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---- loads of 1 / 4 consecutive elements as fp32 --------------------------
+
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ float ld1(const bf16_t* p) { return to_f32(*p); }
+
+// p must be aligned to 4 elements.
+__device__ __forceinline__ f4 ld4(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ f4 ld4(const bf16_t* p) {
+  uint2 v = *reinterpret_cast<const uint2*>(p);
+  f4 r;
+  r[0] = bf16_lo(v.x);
+  r[1] = bf16_hi(v.x);
+  r[2] = bf16_lo(v.y);
+  r[3] = bf16_hi(v.y);
+  return r;
+}
+
+__device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
+__device__ __forceinline__ void st4(bf16_t* p, f4 v) {
+  uint2 w;
+  w.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+  w.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+
+// ---- matrix core ------------------------------------------------------------
+// v_mfma_f32_16x16x4_f32: D[16x16] += A[16x4] * B[4x16].  Lane l supplies
+// A[l%16][l/16] and B[l/16][l%16]; D element (row 4*(l/16)+r, col l%16) is
+// register r of lane l.
+__device__ __forceinline__ f4 mfma16x16x4(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---- math -------------------------------------------------------------------
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+
+// ---- launch order -------------------------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).  This
+// maps block i to a work index so that consecutive work indices (heads of one
+// group, which share B and C) run on the same XCD and share its L2.  It is a
+// bijection of [0, nblocks) for any nblocks.
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t nblocks) {
+  const int64_t q = nblocks / 8, rem = nblocks % 8;
+  const int64_t x = i % 8, k = i / 8;
+  return x * q + (x < rem ? x : rem) + k;
+}
+
+}  // namespace ssd

@@ -1,0 +1,43 @@
+// Internal launch interface between the C ABI (ssd_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// One validated problem.  Sizes follow the notation of the scan:
+// b = batch, L = seqlen, H = nheads, P = headdim, N = dstate, G = ngroups,
+// Q = chunk_size, nc = ceil(L / Q).
+struct Problem {
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;        // may be null
+  const void* z;         // may be null
+  const float* dt_bias;  // may be null
+  float dt_min, dt_max;
+  const float* init;     // may be null
+  void* out;
+  float* final_states;   // may be null
+  int64_t b, L, H, P, N, G, Q, nc;
+  bool bf16;
+  // workspace regions (float32)
+  float* ws_dt;          // [b, H, nc, Q]
+  float* ws_cum;         // [b, H, nc, Q]
+  float* ws_states;      // [b, nc, H, P, N]  chunk-local states
+  float* ws_states_in;   // [b, nc, H, P, N]  state entering each chunk
+};
+
+// Each launcher enqueues one stage on `stream` and returns hipGetLastError().
+hipError_t launch_dt_cumsum(const Problem& p, hipStream_t stream);
+hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
+hipError_t launch_state_passing(const Problem& p, hipStream_t stream);
+hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
+
+// True when (P, N, Q) is one of the compiled tile configurations.
+bool config_supported(int64_t P, int64_t N, int64_t Q);
+
+}  // namespace ssd

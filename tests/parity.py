@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the C ABI, compare with the oracle element by element."""
+import numpy as np
+import torch
+
+import selective_state_space_ssd_amd as ssd
+
+# Elementwise bars: |gpu - ref| <= tol * (1 + |ref|).  fp32 inputs: 1e-3; bf16
+# inputs (fp32 state and accumulation, bf16 output): 2e-2.  The (1 + |ref|)
+# form keeps near-zero outputs from inflating relative errors.
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def device():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a GPU")
+    return torch.device("cuda:0")
+
+
+def upload(inp, dtype):
+    """numpy inputs -> dict of device tensors (bf16 from the exact bit patterns)."""
+    dev = device()
+    t = {}
+    for k in ("x", "z", "B", "C", "dt"):
+        v = inp.get(k)
+        if v is None:
+            t[k] = None
+        elif dtype == "bf16":
+            t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            t[k] = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+    for k in ("A", "D", "dt_bias", "initial_states"):
+        v = inp.get(k)
+        t[k] = None if v is None else torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(dev)
+    return t
+
+
+def run_gpu(t, chunk_size, dt_limit=(0.0, float("inf")), init=None, final=True, **kw):
+    res = ssd.scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                       dt_bias=t["dt_bias"], dt_limit=dt_limit, chunk_size=chunk_size,
+                       initial_states=init, return_final_states=final, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def np64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def compare(name, got, ref, tol, mask=None):
+    """Assert |got - ref| <= tol (1 + |ref|) everywhere (where mask is true);
+    report max|diff|, mean(diff), mean|diff| and the worst index."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    diff = got - ref
+    scaled = np.abs(diff) / (1.0 + np.abs(ref))
+    worst = np.unravel_index(int(np.argmax(scaled)), scaled.shape) if scaled.size else ()
+    stats = (f"{name}: n={diff.size} max|d|={np.max(np.abs(diff)) if diff.size else 0:.3e} "
+             f"mean(d)={diff.mean() if diff.size else 0:.3e} "
+             f"mean|d|={np.abs(diff).mean() if diff.size else 0:.3e} "
+             f"max scaled={scaled.max() if scaled.size else 0:.3e} at {worst} (tol {tol})")
+    log(stats)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    assert np.all(scaled <= tol), stats
+    return stats

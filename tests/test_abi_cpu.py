@@ -1,0 +1,163 @@
+"""C ABI checks that need no GPU.
+
+The library must load and export every function ``include/ssd.h`` declares,
+and every rejected argument must come back with its status code before any
+HIP call is made.  Fake pointer values are passed; none is ever dereferenced
+because every case below fails validation.  No case supplies a workspace of
+the needed size unless another argument is invalid, and the workspace is the
+last thing validated, so no case can reach a kernel launch.
+"""
+import ctypes
+import glob
+import math
+import os
+import re
+
+import pytest
+
+import selective_state_space_ssd_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(ssd_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("ssd_scan_fwd", "ssd_scan_fwd_workspace_size", "ssd_status_string",
+                 "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
+                 "ssd_timing_read", "ssd_timing_destroy"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ssd.binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert ssd.abi_version() == 1
+    assert ssd.status_string(0) == "ok"
+    seen = {ssd.status_string(s) for s in (INVALID, UNSUPPORTED, ALIGN, WORKSPACE, -5)}
+    assert len(seen) == 5 and "unknown status" not in seen
+    assert ssd.status_string(12345) == "unknown status"
+
+
+def _ws(b, L, H, P, N, G, Q, dt=0):
+    return ssd.workspace_size(b, L, H, P, N, G, Q, dt)
+
+
+def test_workspace_size_formula():
+    def r(v):
+        return (v + 255) // 256 * 256
+    for (b, L, H, P, N, G, Q) in [(2, 2048, 32, 64, 128, 1, 128), (1, 300, 4, 64, 16, 1, 64),
+                                  (8, 4096, 64, 64, 128, 8, 256), (3, 1, 2, 64, 32, 2, 128)]:
+        nc = math.ceil(L / Q)
+        want = 2 * r(b * H * nc * Q * 4) + 2 * r(b * nc * H * P * N * 4)
+        assert _ws(b, L, H, P, N, G, Q) == want
+        assert _ws(b, L, H, P, N, G, Q, 1) == want  # intermediates are fp32 for bf16 too
+    assert _ws(0, 100, 4, 64, 16, 1, 64) == 0
+    assert _ws(2, 0, 4, 64, 16, 1, 64) == 0
+    assert _ws(2, 100, 4, 64, 16, 3, 64) == 0       # rejected: 3 does not divide 4
+    assert _ws(2, 100, 4, 32, 16, 1, 64) == 0       # rejected: headdim 32 not compiled
+
+
+# A base argument set with distinct, 256-byte-aligned fake addresses.
+BASE = dict(x=0x10000000, dt=0x20000000, A=0x30000000, B=0x40000000, C=0x50000000,
+            D=0x60000000, z=0x70000000, dt_bias=0x80000000, dt_min=0.0, dt_max=math.inf,
+            chunk_size=64, ngroups=1, init=0x90000000, out=0xA0000000, final=0xB0000000,
+            batch=1, seqlen=100, nheads=4, headdim=64, dstate=16, dtype=0, ws=None, ws_bytes=0,
+            stream=None)
+
+
+def call(**changes):
+    a = dict(BASE)
+    a.update(changes)
+    st = ssd.scan_fwd_raw(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                          a["dt_bias"], a["dt_min"], a["dt_max"], a["chunk_size"],
+                          a["ngroups"], a["init"], a["out"], a["final"], a["batch"],
+                          a["seqlen"], a["nheads"], a["headdim"], a["dstate"], a["dtype"],
+                          a["ws"], a["ws_bytes"], a["stream"])
+    return st
+
+
+CASES = [
+    ("null x", dict(x=None), INVALID),
+    ("null dt", dict(dt=None), INVALID),
+    ("null A", dict(A=None), INVALID),
+    ("null B", dict(B=None), INVALID),
+    ("null C", dict(C=None), INVALID),
+    ("null out", dict(out=None), INVALID),
+    ("negative batch", dict(batch=-1), INVALID),
+    ("negative seqlen", dict(seqlen=-5), INVALID),
+    ("zero heads", dict(nheads=0), INVALID),
+    ("zero headdim", dict(headdim=0), INVALID),
+    ("zero dstate", dict(dstate=0), INVALID),
+    ("zero groups", dict(ngroups=0), INVALID),
+    ("zero chunk", dict(chunk_size=0), INVALID),
+    ("groups do not divide heads", dict(ngroups=3), INVALID),
+    ("unknown dtype", dict(dtype=7), INVALID),
+    ("dt_min NaN", dict(dt_min=math.nan), INVALID),
+    ("dt_max NaN", dict(dt_max=math.nan), INVALID),
+    ("dt_min > dt_max", dict(dt_min=0.5, dt_max=0.1), INVALID),
+    ("headdim 32", dict(headdim=32), UNSUPPORTED),
+    ("dstate 256", dict(dstate=256), UNSUPPORTED),
+    ("dstate 24", dict(dstate=24), UNSUPPORTED),
+    ("chunk 32", dict(chunk_size=32), UNSUPPORTED),
+    ("chunk 100", dict(chunk_size=100), UNSUPPORTED),
+    ("too many chunks", dict(seqlen=64 * 65536), UNSUPPORTED),
+    ("x misaligned", dict(x=0x10000004), ALIGN),
+    ("out misaligned", dict(out=0xA0000008), ALIGN),
+    ("B misaligned", dict(B=0x40000002), ALIGN),
+    ("C misaligned", dict(C=0x50000004), ALIGN),
+    ("z misaligned", dict(z=0x70000004), ALIGN),
+    ("dt misaligned fp32", dict(dt=0x20000002), ALIGN),
+    ("dt misaligned bf16", dict(dt=0x20000001, dtype=1), ALIGN),
+    ("A misaligned", dict(A=0x30000002), ALIGN),
+    ("init misaligned", dict(init=0x90000004), ALIGN),
+    ("final misaligned", dict(final=0xB0000004), ALIGN),
+    ("out overlaps x", dict(out=0x10000000 + 256), INVALID),
+    ("out overlaps z", dict(out=0x70000000 - 256), INVALID),
+    ("out overlaps B", dict(out=0x40000000), INVALID),
+    ("out overlaps final", dict(final=0xA0000000 + 1024), INVALID),
+    ("final partially overlaps init", dict(final=0x90000000 + 4096), INVALID),
+    ("no workspace", dict(), WORKSPACE),
+    ("workspace too small", dict(ws=0xC0000000, ws_bytes=1024), WORKSPACE),
+    ("final aliases init exactly (valid, stops at workspace)", dict(final=0x90000000),
+     WORKSPACE),
+    ("bf16 dt 2-byte aligned (valid, stops at workspace)", dict(dt=0x20000002, dtype=1),
+     WORKSPACE),
+    ("optional pointers absent (valid, stops at workspace)",
+     dict(D=None, z=None, dt_bias=None, init=None, final=None), WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("desc,changes,want", CASES, ids=[c[0] for c in CASES])
+def test_rejected_before_launch(desc, changes, want):
+    assert want != OK
+    assert call(**changes) == want
+
+
+def test_empty_batch_is_a_no_op():
+    # batch == 0: nothing to compute, nothing launched
+    assert call(batch=0) == OK
+    assert call(batch=0, x=None, dt=None, B=None, C=None, out=None) == OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        ssd.scan_fwd(x, torch.zeros(1, 4, 2), torch.zeros(2), torch.zeros(1, 4, 1, 16),
+                     torch.zeros(1, 4, 1, 16))

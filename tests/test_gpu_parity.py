@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every comparison is element by element at the bar of tests/parity.py
+(fp32 inputs 1e-3 * (1 + |ref|), bf16 inputs 2e-2 * (1 + |ref|)).  Small
+cases span several chunks and a ragged tail and are checked everywhere;
+the full-size workloads are checked everywhere where the oracle is quick and
+on sampled (batch, head) pairs -- every timestep and channel of them -- where
+it is not.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_ssd_amd as ssd
+from parity import TOL, compare, log, np64, run_gpu, upload
+from ssd_workloads import WORKLOADS, Workload, make_inputs, small
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, dt_limit=(0.0, math.inf), init=None, head_mask=None):
+    return oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                          z=inp["z"], dt_bias=inp["dt_bias"], dt_limit=dt_limit,
+                          initial_states=init, return_final_states=True, head_mask=head_mask)
+
+
+def _case(seed, b, L, H, P, N, G, Q, dtype, **kw):
+    return Workload(f"case{seed}", b, L, H, P, N, G, Q, dtype, seed, **kw)
+
+
+# --------------------------------------------------------------------------
+# small problems, full comparison (several chunks + a ragged tail)
+# --------------------------------------------------------------------------
+
+SMALL = [(dt, Q, N) for dt in ("f32", "bf16") for Q in (64, 128, 256) for N in (16, 128)]
+SMALL += [("f32", 128, 32), ("f32", 128, 64), ("bf16", 64, 32), ("bf16", 256, 64)]
+
+
+@pytest.mark.parametrize("dtype,Q,N", SMALL, ids=[f"{d}-Q{q}-N{n}" for d, q, n in SMALL])
+def test_small_ragged(dtype, Q, N):
+    L = 2 * Q + Q // 2 + 7
+    w = _case(1000 + Q + N, 2, L, 4, 64, N, 2, Q, dtype, init=True)
+    log(f"test_small_ragged {dtype} Q={Q} N={N} L={L}")
+    inp = make_inputs(w)
+    t = upload(inp, dtype)
+    out, fin = run_gpu(t, Q, init=t["initial_states"])
+    ref, rfin = _oracle(inp, init=inp["initial_states"])
+    compare("out", np64(out), ref, TOL[dtype])
+    compare("final", np64(fin), rfin, TOL[dtype])
+
+
+def _ws_regions(ws, b, L, H, P, N, Q):
+    nc = -(-L // Q)
+    r = lambda v: (v + 255) // 256 * 256
+    dtn, stn = b * H * nc * Q, b * nc * H * P * N
+    f = ws.view(torch.float32)
+    o_cum = r(dtn * 4) // 4
+    o_st = o_cum + r(dtn * 4) // 4
+    o_in = o_st + r(stn * 4) // 4
+    return {"dt": f[:dtn].view(b, H, nc, Q), "cum": f[o_cum:o_cum + dtn].view(b, H, nc, Q),
+            "chunk_states": f[o_st:o_st + stn].view(b, nc, H, P, N),
+            "states_in": f[o_in:o_in + stn].view(b, nc, H, P, N)}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stage_intermediates(dtype):
+    """Each stage's output in the workspace against the oracle's per-chunk
+    intermediates: dt and dA_cumsum (stage 1), chunk-local states (stage 2),
+    states entering each chunk (stage 3)."""
+    b, L, H, P, N, G, Q = 2, 300, 4, 64, 128, 2, 128
+    w = _case(77, b, L, H, P, N, G, Q, dtype, init=True)
+    log(f"test_stage_intermediates {dtype}")
+    inp = make_inputs(w)
+    t = upload(inp, dtype)
+    ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0),
+                     dtype=torch.uint8, device=t["x"].device)
+    run_gpu(t, Q, init=t["initial_states"], workspace=ws)
+    got = {k: np64(v) for k, v in _ws_regions(ws, b, L, H, P, N, Q).items()}
+    ref = oracle.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
+                                     dt_bias=inp["dt_bias"], initial_states=inp["initial_states"])
+    valid = np.zeros((b, H, 3, Q), bool)
+    valid.reshape(b, H, -1)[:, :, :L] = True
+    compare("dt", got["dt"], ref["dt"], 1e-5, mask=valid)
+    compare("dA_cumsum", got["cum"], ref["cum"], 1e-4, mask=valid)
+    compare("chunk_states", got["chunk_states"], ref["chunk_states"], TOL[dtype])
+    compare("states_in", got["states_in"], ref["states_in"], TOL[dtype])
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+EDGE = [
+    ("L=1", dict(seqlen=1)),
+    ("L<Q", dict(seqlen=45)),
+    ("L=Q", dict(seqlen=128)),
+    ("L=Q+1", dict(seqlen=129)),
+    ("G=H", dict(ngroups=8, nheads=8)),
+    ("no gate, no skip", dict(gate=False, skip=False)),
+    ("dt_limit", dict(), ),
+]
+
+
+@pytest.mark.parametrize("desc,changes", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(desc, changes):
+    base = dict(seqlen=200, nheads=4, ngroups=2, gate=True, skip=True)
+    base.update(changes)
+    w = _case(300, 2, base["seqlen"], base["nheads"], 64, 128, base["ngroups"], 128, "f32",
+              gate=base["gate"], skip=base["skip"], init=True)
+    lim = (0.01, 0.05) if desc == "dt_limit" else (0.0, math.inf)
+    log(f"test_edge_cases {desc}")
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    out, fin = run_gpu(t, 128, dt_limit=lim, init=t["initial_states"])
+    ref, rfin = _oracle(inp, dt_limit=lim, init=inp["initial_states"])
+    compare("out", np64(out), ref, TOL["f32"])
+    compare("final", np64(fin), rfin, TOL["f32"])
+
+
+def test_no_bias_no_init():
+    w = _case(301, 1, 333, 4, 64, 64, 1, 64, "f32")
+    inp = make_inputs(w)
+    inp["dt_bias"] = None
+    t = upload(inp, "f32")
+    out, fin = run_gpu(t, 64)
+    ref, rfin = _oracle(inp)
+    compare("out", np64(out), ref, TOL["f32"])
+    compare("final", np64(fin), rfin, TOL["f32"])
+    out2 = run_gpu(t, 64, final=False)
+    assert torch.equal(out, out2)
+
+
+def test_empty_sequence_and_batch():
+    dev = torch.device("cuda:0")
+    H, P, N = 4, 64, 16
+    x = torch.zeros(2, 0, H, P, device=dev)
+    dt = torch.zeros(2, 0, H, device=dev)
+    A = -torch.ones(H, device=dev)
+    Bc = torch.zeros(2, 0, 1, N, device=dev)
+    init = torch.randn(2, H, P, N, device=dev)
+    out, fin = ssd.scan_fwd(x, dt, A, Bc, Bc.clone(), chunk_size=64, initial_states=init,
+                            return_final_states=True)
+    torch.cuda.synchronize()
+    assert out.shape == x.shape and torch.equal(fin, init)
+    out, fin = ssd.scan_fwd(x, dt, A, Bc, Bc.clone(), chunk_size=64, return_final_states=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fin) == 0
+    x0 = torch.zeros(0, 10, H, P, device=dev)
+    out = ssd.scan_fwd(x0, torch.zeros(0, 10, H, device=dev), A,
+                       torch.zeros(0, 10, 1, N, device=dev), torch.zeros(0, 10, 1, N, device=dev),
+                       chunk_size=64)
+    assert out.shape == x0.shape
+
+
+def test_unsupported_raises():
+    dev = torch.device("cuda:0")
+    x = torch.zeros(1, 8, 2, 32, device=dev)
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.scan_fwd(x, torch.zeros(1, 8, 2, device=dev), -torch.ones(2, device=dev),
+                     torch.zeros(1, 8, 1, 16, device=dev), torch.zeros(1, 8, 1, 16, device=dev),
+                     chunk_size=64)
+    assert e.value.status == -2
+
+
+# --------------------------------------------------------------------------
+# properties of the GPU path
+# --------------------------------------------------------------------------
+
+def test_ngroups_invariance():
+    """B, C replicated over G groups give bit-identical outputs to G = 1."""
+    w = small("f32_b2_L2048_H32_P64_N128_G1_Q128", seqlen=700, seed=21, init=True)
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    ref_out, ref_fin = run_gpu(t, 128, init=t["initial_states"])
+    for G in (2, 4):
+        t2 = dict(t)
+        t2["B"] = t["B"].repeat_interleave(G, dim=2).contiguous()
+        t2["C"] = t["C"].repeat_interleave(G, dim=2).contiguous()
+        out, fin = run_gpu(t2, 128, init=t["initial_states"])
+        assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin), G
+
+
+def test_chunk_size_invariance():
+    w = _case(400, 2, 1000, 4, 64, 128, 2, 128, "f32", init=True)
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    ref, rfin = _oracle(inp, init=inp["initial_states"])
+    outs = {}
+    for Q in (64, 128, 256):
+        out, fin = run_gpu(t, Q, init=t["initial_states"])
+        compare(f"out Q={Q}", np64(out), ref, TOL["f32"])
+        compare(f"final Q={Q}", np64(fin), rfin, TOL["f32"])
+        outs[Q] = np64(out)
+    compare("Q=64 vs Q=256", outs[64], outs[256], TOL["f32"])
+
+
+def test_deterministic():
+    w = small("f32_b2_L2048_H32_P64_N128_G2_Q128", seqlen=1000, seed=31)
+    t = upload(make_inputs(w), "f32")
+    a, fa = run_gpu(t, 128)
+    b, fb = run_gpu(t, 128)
+    assert torch.equal(a, b) and torch.equal(fa, fb)
+
+
+def test_inplace_continuation():
+    """final_states may be the initial_states buffer (chunked prefill in place)."""
+    w = _case(500, 2, 2 * 257, 4, 64, 64, 2, 128, "f32", init=True)
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    full, ffin = run_gpu(t, 128, init=t["initial_states"])
+    state = t["initial_states"].clone()
+    outs = []
+    for lo, hi in ((0, 257), (257, 514)):
+        seg = {k: (v[:, lo:hi].contiguous() if k in ("x", "z", "B", "C", "dt") else v)
+               for k, v in t.items()}
+        out, fin = run_gpu(seg, 128, init=state, final_states=state)
+        assert fin.data_ptr() == state.data_ptr()
+        outs.append(out)
+    compare("segments vs full", np64(torch.cat(outs, dim=1)), np64(full), TOL["f32"])
+    compare("final in place", np64(state), np64(ffin), TOL["f32"])
+
+
+# --------------------------------------------------------------------------
+# the full-size workloads
+# --------------------------------------------------------------------------
+
+def _sample_mask(b, H, k, seed):
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((b, H), bool)
+    idx = rng.choice(b * H, size=min(k, b * H), replace=False)
+    mask.reshape(-1)[idx] = True
+    mask[b - 1, H - 1] = True  # always the last pair
+    return mask
+
+
+FULL = list(WORKLOADS)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload(name):
+    w = WORKLOADS[name]
+    log(f"test_workload {name}: generating inputs")
+    inp = make_inputs(w)
+    t = upload(inp, w.dtype)
+    tol = TOL[w.dtype]
+    big = w.batch * w.seqlen * w.nheads > 2 * 2048 * 32
+    mask = _sample_mask(w.batch, w.nheads, 6, w.seed) if big else None
+    if w.segments == 1:
+        log(f"test_workload {name}: GPU run")
+        out, fin = run_gpu(t, w.chunk_size)
+    else:
+        seg = w.seqlen // w.segments
+        state = None
+        outs = []
+        for i in range(w.segments):
+            log(f"test_workload {name}: GPU segment {i}")
+            sl = {k: (v[:, i * seg:(i + 1) * seg].contiguous()
+                      if k in ("x", "z", "B", "C", "dt") and v is not None else v)
+                  for k, v in t.items()}
+            o, state = run_gpu(sl, w.chunk_size, init=state)
+            outs.append(o)
+        out, fin = torch.cat(outs, dim=1), state
+        full_out, full_fin = run_gpu(t, w.chunk_size)
+        compare("segments vs one GPU scan", np64(out), np64(full_out), tol)
+        compare("segment final vs one GPU scan", np64(fin), np64(full_fin), tol)
+    log(f"test_workload {name}: oracle")
+    ref, rfin = _oracle(inp, head_mask=mask)
+    got, gfin = np64(out), np64(fin)
+    if mask is not None:
+        sel = np.broadcast_to(mask[:, None, :, None], ref.shape)
+        compare("out (sampled heads)", got, ref, tol, mask=sel)
+        compare("final (sampled heads)", gfin, rfin,
+                tol, mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))
+    else:
+        compare("out", got, ref, tol)
+        compare("final", gfin, rfin, tol)

@@ -1,0 +1,224 @@
+"""Throughput of the SSD scan forward on one MI355X.
+
+One step = one pass of the whole scan (dt/cumsum, chunk state, state passing,
+chunk scan with the D/z epilogue) over the fp32 workload batch 2 x seqlen
+2048, 32 heads of 64, dstate 128, chunk 128, at ngroups 1, 2 and 4: three
+ssd_scan_fwd calls, 3 x 4096 tokens.  Inputs are seeded, synthetic and
+resident in HBM before timing starts; two copies of every input rotate across
+steps so that consecutive steps touch more memory than the 256 MB Infinity
+Cache holds.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline of the
+dominant kernel (its algorithmic flops per launch over its mean launch time,
+measured with HIP events recorded by the library on the launch stream), and
+the CPU oracle's throughput on the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from ssd_workloads import BENCH_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def alg_flops(w):
+    """Algorithmic flops of one call, by stage (chunked SSD, causal, C.B^T once
+    per group): chunk state 2QPN per (chunk, head); state passing 2PN per
+    (chunk, head); chunk scan 2QPN + PQ(Q+1) per (chunk, head) plus NQ(Q+1)
+    per (chunk, group)."""
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    nc = math.ceil(L / Q)
+    return {
+        "dt_cumsum": b * L * H * 2.0,
+        "chunk_state": b * nc * H * 2.0 * Q * P * N,
+        "state_passing": b * nc * H * 2.0 * P * N,
+        "chunk_scan": b * nc * (H * (2.0 * Q * P * N + P * Q * (Q + 1)) + G * N * Q * (Q + 1)),
+    }
+
+
+def alg_bytes(w):
+    """Bytes the method must move: read x, dt, B, C, (z), (init), A, D, dt_bias;
+    write out, (final).  Intermediates are not counted."""
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    es = 2 if w.dtype == "bf16" else 4
+    n = b * L * H * P * es * (2 + (1 if w.gate else 0))     # x, out, z
+    n += b * L * H * es + 2 * b * L * G * N * es              # dt, B, C
+    n += 3 * H * 4
+    st = b * H * P * N * 4
+    n += st * ((1 if w.init else 0) + (1 if w.final else 0))
+    return n
+
+
+def cpu_baseline(workloads, min_seconds=10.0):
+    """The oracle (untuned fp64 recurrence, OpenMP over batch x heads) on the
+    whole step, repeated until at least `min_seconds` have passed."""
+    import oracle
+    inputs = [make_inputs(w) for w in workloads]
+    threads = oracle.max_threads()
+    tokens, elapsed, passes = 0, 0.0, 0
+    while elapsed < min_seconds:
+        for w, inp in zip(workloads, inputs):
+            t0 = time.perf_counter()
+            oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                           z=inp["z"], dt_bias=inp["dt_bias"])
+            elapsed += time.perf_counter() - t0
+            tokens += w.tokens
+        passes += 1
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} full step(s): ngroups 1, 2, 4 at batch 2 x seqlen 2048 "
+                      f"({tokens} tokens, {elapsed:.1f} s, fp64 recurrence)",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the scan is built and measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_ssd_amd as ssd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    workloads = [WORKLOADS[n] for n in BENCH_WORKLOADS]
+    stream = torch.cuda.current_stream(dev)
+
+    # inputs, two copies of each, plus outputs and one shared workspace
+    calls = []   # per rotation copy: list of argument tuples for ssd_scan_fwd
+    keep = []
+    ws_bytes = max(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                      w.ngroups, w.chunk_size, 0) for w in workloads)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    for copy in range(2):
+        args_copy = []
+        for w in workloads:
+            inp = make_inputs(w)
+            t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items()
+                 if isinstance(v, np.ndarray)}
+            out = torch.empty_like(t["x"])
+            keep.append((t, out))
+            args_copy.append((
+                t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(),
+                t["C"].data_ptr(), t["D"].data_ptr(), t["z"].data_ptr(),
+                t["dt_bias"].data_ptr(), 0.0, math.inf, w.chunk_size, w.ngroups, None,
+                out.data_ptr(), None, w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                ssd.SSD_F32, ws.data_ptr(), ws_bytes, stream.cuda_stream))
+        calls.append(args_copy)
+
+    def step(k, timings=None):
+        for i, a in enumerate(calls[k % 2]):
+            st = ssd.scan_fwd_raw(*a, timing=None if timings is None else timings[i])
+            if st != 0:
+                raise ssd.SsdError(st, ssd.status_string(st))
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-stage durations: the same steps again, with the library recording a
+    # HIP event around each stage on the launch stream
+    timings = [[ssd.Timing() for _ in workloads] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, timings[k])
+    torch.cuda.synchronize()
+    elapsed_ev = time.perf_counter() - t1
+    stage_ms = np.array([[tm.read() for tm in row] for row in timings])  # [steps, calls, stages]
+    mean_ms = stage_ms.mean(axis=0)                                        # [calls, stages]
+
+    tokens = sum(w.tokens for w in workloads)
+    value = tokens * args.steps / elapsed
+    flops = [alg_flops(w) for w in workloads]
+    per_stage_total = mean_ms.sum(axis=0)
+    dom = int(np.argmax(per_stage_total))
+    dom_name = ssd.STAGES[dom]
+    dom_flops = sum(f[dom_name] for f in flops)
+    dom_s = per_stage_total[dom] / 1e3
+    achieved = dom_flops / dom_s / 1e12
+    path_flops = sum(sum(f.values()) for f in flops)
+    step_s = elapsed / args.steps
+    path_bytes = sum(alg_bytes(w) for w in workloads)
+
+    line = {
+        "metric": "SSD scan fwd tokens/sec at 1 MI355X; % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "ssd_scan_fwd f32 batch 2 x seqlen 2048, 32 heads x headdim 64, "
+                        "dstate 128, chunk 128, ngroups 1/2/4 (3 calls per step), "
+                        "z gate and D skip on, dt_limit (0, inf)",
+            "batch": 2, "seqlen": 2048, "nheads": 32, "headdim": 64, "dstate": 128,
+            "chunk_size": 128, "ngroups": [1, 2, 4], "tokens_per_step": tokens,
+        },
+        "roofline": {
+            "kernel": dom_name,
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
+            "traffic": None,
+            "launches_timed": args.steps * len(workloads),
+            "mean_launch_us": dom_s / len(workloads) * 1e6,
+        },
+        "path": {
+            "alg_tflops_per_s": path_flops / step_s / 1e12,
+            "mfma_frac": path_flops / step_s / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+            "alg_gbytes_per_s": path_bytes / step_s / 1e9,
+            "hbm_frac": path_bytes / step_s / 1e9 / PEAK_HBM_GBS,
+            "stage_us_per_call": {s: float(per_stage_total[i] / len(workloads) * 1e3)
+                                  for i, s in enumerate(ssd.STAGES)},
+            "event_pass_ms_per_step": elapsed_ev / args.steps * 1e3,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(workloads),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

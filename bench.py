@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="before the steps, run 3 plain device copies of this many MiB "
+                         "(reference kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -138,6 +141,15 @@ def main():
             st = ssd.scan_fwd_raw(*a, timing=None if timings is None else timings[i])
             if st != 0:
                 raise ssd.SsdError(st, ssd.status_string(st))
+
+    if args.copy_mb > 0:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for k in range(args.warmup):
         step(k)

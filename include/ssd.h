@@ -108,11 +108,17 @@ extern "C" {
  * (float32, in this order, each region starting on a 256-byte boundary):
  *   dt        [batch, nheads, nchunks, chunk_size]   0 past the sequence end
  *   dA_cumsum [batch, nheads, nchunks, chunk_size]   in-chunk running sum of dt*A
- *   chunk_states [batch, nchunks, nheads, headdim, dstate]  each chunk's own
- *             contribution (the recurrence over the chunk from a zero state)
- *   states_in [batch, nchunks, nheads, headdim, dstate]  the state entering
- *             each chunk
- * with nchunks = ceil(seqlen / chunk_size).
+ *   chunk_states [batch, nchunks, nheads] blocks of headdim*dstate floats:
+ *             each chunk's own contribution (the recurrence over the chunk
+ *             from a zero state)
+ *   states_in [batch, nchunks, nheads] blocks of headdim*dstate floats: the
+ *             state entering each chunk
+ * with nchunks = ceil(seqlen / chunk_size).  Inside a state block (headdim
+ * 64) element (p, n) sits at float offset
+ *   ((q*2 + p%2)*64 + 32*k + p/2)*4 + n%4,  k = n / (dstate/2),
+ *   q = (n % (dstate/2)) / 4,
+ * i.e. float4 tiles of four consecutive n, ordered so that the kernels read
+ * and write them with one contiguous 1 KB access per wave.
  */
 int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                  const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,

@@ -5,7 +5,7 @@
 #include <cstdlib>
 #include <new>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "ssd_kernels.h"
 
 namespace {
@@ -154,7 +154,9 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   };
   if (!mark(0)) return SSD_ERR_HIP;
   if (seqlen > 0) {
-    if (ssd::launch_dt_cumsum(p, stream) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
+    if (!ssd::chunk_state_fuses_dt(p) && ssd::launch_dt_cumsum(p, stream) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (!mark(1)) return SSD_ERR_HIP;
     if (ssd::launch_chunk_state(p, stream) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
   } else if (!mark(1) || !mark(2)) {
     return SSD_ERR_HIP;

@@ -73,10 +73,11 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     const float* hsrc = states_in + u * (int64_t)(P * N);
 #pragma unroll
     for (int i = 0; i < P * N / 4 / 256; ++i) {
-      const int e = (i * 256 + tid) * 4;
-      const int p = e / N, n = e % N;
+      const int k = i * 256 + tid;  // float4 index in the tiled state layout
+      int p, n;
+      state_tile_coords(k, N, &p, &n);
       const int prow = 16 * (p % 4) + p / 4;
-      *reinterpret_cast<f4*>(&h_lds[prow * HS + n]) = ld4(hsrc + e);
+      *reinterpret_cast<f4*>(&h_lds[prow * HS + n]) = ld4(hsrc + 4 * k);
     }
     const int64_t dc = ((b * H + h) * nc + c) * Q;
     if (tid < Q) {
@@ -192,8 +193,331 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Four heads of one group per workgroup, two waves per head (Q = 64 or 128,
+// N = 64 or 128, nheads / ngroups a multiple of 4).
+//
+// The group's C and B tiles of the chunk are staged in LDS once.  The four
+// waves first compute the causal 32 x 32 tiles of G^T = B C^T (G[t][s] =
+// C_t . B_s) on v_mfma_f32_32x32x2_f32, shared by the four heads, and park
+// them in LDS in register order.  Each wave then holds half of its head's
+// Q x 64 output in accumulators (t-tiles {h, Q/32-1-h} of wave half h, x 2
+// p-tiles of 32 x 32, so both halves do the same causal work):
+//   1. acc = C . H_in^T        (A: C rows from LDS; B: H_in, tiled layout,
+//                               one coalesced float4 per lane per 4 k-steps)
+//   2. acc *= exp(cum_t)
+//   3. per s-tile si: acc[ti] += (G^T tile * exp(cum_t - cum_s) * dt_s,
+//      causal) . x  for ti >= si; t-tile si is then complete and goes
+//      through the D-skip / z-gate epilogue at once.
+// The D skip is folded into the diagonal of the masked matrix (M[t][t] += D),
+// so x is read once, as the B operand of step 3; its rows for the next s-tile
+// stream into a rolling register buffer while the current s-tile computes.
+// Lane l covers p = 2*(l%32) + pj of p-tile pj and, in the accumulator,
+// rows 8*(r/4) + 4*(l/32) + r%4 of register r, so every store is one float2
+// per lane, two full 256-byte rows per instruction.
+// ---------------------------------------------------------------------------
+
+template <int NT>
+__device__ __forceinline__ void tile_of(int tau, int* si, int* ti) {
+  // causal tiles numbered ti*(ti+1)/2 + si, si <= ti
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (tau >= t * (t + 1) / 2 && tau < (t + 1) * (t + 2) / 2) {
+      *ti = t;
+      *si = tau - t * (t + 1) / 2;
+    }
+}
+
+template <typename T, int Q, int N, bool GATE>
+__global__ __launch_bounds__(512) void chunk_scan_group_kernel(
+    const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
+    const float* __restrict__ Dv, const T* __restrict__ z, const float* __restrict__ ws_dt,
+    const float* __restrict__ ws_cum, const float* __restrict__ states_in, T* __restrict__ out,
+    int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+  constexpr int P = 64, NT = Q / 32, CS = N + 4, NG = NT * (NT + 1) / 2, KQ = N / 8;
+  constexpr int NW = 8;                   // waves: two per head
+  constexpr int GW = (NG + NW - 1) / NW;  // G tiles per wave, at most
+  constexpr int NS = NT / 2;              // t-tiles per wave
+  constexpr int BGS = (Q * CS > NG * 1024) ? Q * CS : NG * 1024;
+  constexpr int HR = 3;                   // ring of state loads: two steps ahead
+  constexpr float kLog2e = 1.4426950408889634f;
+  static_assert((Q == 64 || Q == 128) && (N == 64 || N == 128), "tile");
+  __shared__ float c_lds[Q * CS];
+  __shared__ float bg_lds[BGS];  // B tile, then the G^T tiles
+  __shared__ float cum_lds[4][Q];  // running sums in log2 units (cum * log2 e)
+  __shared__ float dt_lds[4][Q];
+
+  const int64_t HQ = H / 4;
+  const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*HQ + hq)
+  const int64_t hq = u % HQ, c = (u / HQ) % nc, b = u / (HQ * nc);
+  const int64_t h0 = 4 * hq;
+  const int64_t g = h0 / (H / G);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int slot = wave >> 1, half = wave & 1;
+  const int i = lane % 32, kk = lane / 32;
+  const int64_t h = h0 + slot;
+  const int64_t t0 = c * Q;
+  const int64_t xs = H * P;
+  // last real row of this chunk, clamped to the chunk (rows past it are padding)
+  const int last = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
+  // t-tiles of this wave: {half, NT-1-half} (NT = 4) or {half} (NT = 2); equal
+  // causal work for both halves when NT = 4
+  auto own = [&](int j) { return j == 0 ? half : NT - 1 - half; };
+  const int smax = own(NS - 1) > own(0) ? own(NS - 1) : own(0);  // last s-tile needed
+
+  // ---- 0. stage C, B, cum, dt ------------------------------------------------
+  {
+    const T* cs = Cm + ((b * L + t0) * G + g) * N;
+    const T* bs = Bm + ((b * L + t0) * G + g) * N;
+    const int64_t rs = G * N;
+#pragma unroll
+    for (int k = 0; k < Q * N / (4 * 64 * NW); ++k) {
+      const int e = (k * 64 * NW + tid) * 4;
+      const int row = e / N, col = e % N;
+      const int r = row < last ? row : last;
+      f4 cv = ld4(cs + r * rs + col), bv = ld4(bs + r * rs + col);
+      if (row > last) cv = bv = f4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f4*>(&c_lds[row * CS + col]) = cv;
+      *reinterpret_cast<f4*>(&bg_lds[row * CS + col]) = bv;
+    }
+    for (int k = tid; k < 4 * Q; k += 64 * NW) {
+      const int w = k / Q, t = k % Q;
+      const int64_t o = ((b * H + h0 + w) * nc + c) * Q + t;
+      cum_lds[w][t] = ws_cum[o] * kLog2e;
+      dt_lds[w][t] = ws_dt[o];
+    }
+  }
+  __syncthreads();
+
+  // ---- first per-head loads, in flight during the shared G phase -------------
+  const T* xh = x + ((b * L + t0) * H + h) * P + 2 * i;
+  const T* zh = z + ((b * L + t0) * H + h) * P + 2 * i;  // read only when GATE
+  T* oh = out + ((b * L + t0) * H + h) * P + 2 * i;
+  const float* hs = states_in + ((b * nc + c) * H + h) * (int64_t)(P * N) + 4 * lane;
+  f4 hv[HR][2];
+#pragma unroll
+  for (int q = 0; q < HR - 1; ++q) {
+    hv[q][0] = ld4(hs + (2 * q) * 256);
+    hv[q][1] = ld4(hs + (2 * q + 1) * 256);
+  }
+  // x rows of s-tile si held by this lane: 32*si + 8*(m/4) + 4*kk + m%4.  One
+  // rolling buffer: slots 4R..4R+3 are refilled with the next s-tile's rows as
+  // soon as the MFMAs of step R have consumed them.  Padding rows read the last
+  // real row and are zeroed.
+  f2 xv[16];
+  auto load_x = [&](int si, int R) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int srow = 32 * si + 8 * R + 4 * kk + e;
+      const f2 v = ld2(xh + (srow < last ? srow : last) * xs);
+      xv[4 * R + e] = srow <= last ? v : f2{0.f, 0.f};
+    }
+  };
+#pragma unroll
+  for (int R = 0; R < 4; ++R) load_x(0, R);
+  // z rows of the t-tile this wave emits next (its first owned tile now; the
+  // second one is loaded as soon as the first has been emitted)
+  f2 zv[16];
+  auto load_z = [&](int ti) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int srow = 32 * ti + 8 * (m / 4) + 4 * kk + (m % 4);
+      zv[m] = ld2(zh + (srow < last ? srow : last) * xs);
+    }
+  };
+  if constexpr (GATE) load_z(own(0));
+
+  // ---- 1. causal tiles of G^T = B C^T, shared by the four heads ---------------
+  f16x gt[GW];
+#pragma unroll
+  for (int k = 0; k < GW; ++k) {
+    gt[k] = zero16();
+    const int tau = wave + NW * k;
+    if (tau < NG) {
+      int si = 0, ti = 0;
+      tile_of<NT>(tau, &si, &ti);
+      const float* ap = &bg_lds[(32 * si + i) * CS + (N / 2) * kk];
+      const float* bp = &c_lds[(32 * ti + i) * CS + (N / 2) * kk];
+#pragma unroll 4
+      for (int q = 0; q < KQ; ++q) {
+        const f4 av = *reinterpret_cast<const f4*>(ap + 4 * q);
+        const f4 bv = *reinterpret_cast<const f4*>(bp + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gt[k] = mfma32x32x2(av[e], bv[e], gt[k]);
+      }
+    }
+  }
+  __syncthreads();  // every read of the B tile is done
+#pragma unroll
+  for (int k = 0; k < GW; ++k) {
+    const int tau = wave + NW * k;
+    if (tau < NG) {
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f4 v;
+        v[0] = gt[k][4 * R];
+        v[1] = gt[k][4 * R + 1];
+        v[2] = gt[k][4 * R + 2];
+        v[3] = gt[k][4 * R + 3];
+        *reinterpret_cast<f4*>(&bg_lds[((tau * 4 + R) * 64 + lane) * 4]) = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  const float* cumw = cum_lds[slot];
+  const float* dtw = dt_lds[slot];
+  float ct[NS], ect[NS];  // cum_t (log2 units) and exp(cum_t) of this lane's A-operand row
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    ct[j] = cumw[32 * own(j) + i];
+    ect[j] = exp2f(ct[j]);
+  }
+
+  // ---- 2. state part: acc = (exp(cum_t) C) . H_in^T ---------------------------
+  f16x acc[NS][2];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) acc[j][0] = acc[j][1] = zero16();
+  auto load_c = [&](int q, f4 (&cv)[NS]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      cv[j] = *reinterpret_cast<const f4*>(&c_lds[(32 * own(j) + i) * CS + (N / 2) * kk + 4 * q]);
+  };
+  f4 cnext[NS];
+  load_c(0, cnext);
+#pragma unroll
+  for (int q = 0; q < KQ; ++q) {
+    const int rs = q % HR;
+    if (q + HR - 1 < KQ) {
+      const int nq = q + HR - 1, ns = nq % HR;
+      hv[ns][0] = ld4(hs + (2 * nq) * 256);
+      hv[ns][1] = ld4(hs + (2 * nq + 1) * 256);
+    }
+    f4 cv[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) cv[j] = cnext[j] * ect[j];
+    if (q + 1 < KQ) load_c(q + 1, cnext);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        acc[j][0] = mfma32x32x2(cv[j][e], hv[rs][0][e], acc[j][0]);
+        acc[j][1] = mfma32x32x2(cv[j][e], hv[rs][1][e], acc[j][1]);
+      }
+  }
+
+  // ---- 3. in-chunk part per s-tile, then the epilogue of t-tile si ------------
+  // The D skip rides on the diagonal of the decay-masked matrix: M[t][t] gets
+  // + D_h, so the epilogue needs no x.  The four masked values of step R+1 are
+  // computed while the MFMAs of step R run.
+  const float Dh = Dv ? Dv[h] : 0.0f;
+  const bool full = last == Q - 1;  // uniform: no padding rows in this chunk
+#pragma unroll
+  for (int si = 0; si < NT; ++si) {
+    if (si > smax) break;  // uniform per wave
+    // masked values mv[j][e] of step R: G^T(s, t) * 2^(ct - cs) * dt_s, causal on
+    // the diagonal tile, plus D at s == t
+    auto masked = [&](int R, float (&mv)[NS][4]) {
+      const f4 cs4 = *reinterpret_cast<const f4*>(&cumw[32 * si + 8 * R + 4 * kk]);
+      const f4 ds4 = *reinterpret_cast<const f4*>(&dtw[32 * si + 8 * R + 4 * kk]);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int ti = own(j) >= si ? own(j) : si;  // tiles below si are not used
+        const f4 gv = *reinterpret_cast<const f4*>(
+            &bg_lds[(((ti * (ti + 1) / 2 + si) * 4 + R) * 64 + lane) * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = gv[e] * exp2f(ct[j] - cs4[e]) * ds4[e];
+          if (own(j) == si) {
+            const int sl = 8 * R + 4 * kk + e;  // s within the tile
+            v = (sl < i) ? v : (sl == i ? v + Dh : 0.0f);
+          }
+          mv[j][e] = v;
+        }
+      }
+    };
+    float mcur[NS][4], mnext[NS][4];
+    masked(0, mcur);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      float x0[4], x1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x0[e] = xv[4 * R + e][0];
+        x1[e] = xv[4 * R + e][1];
+      }
+      if (si + 1 <= smax) load_x(si + 1, R);  // refill the slots just read
+      if (R + 1 < 4) masked(R + 1, mnext);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          if (own(j) < si) continue;  // uniform
+          acc[j][0] = mfma32x32x2(mcur[j][e], x0[e], acc[j][0]);
+          acc[j][1] = mfma32x32x2(mcur[j][e], x1[e], acc[j][1]);
+        }
+      if (R + 1 < 4) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mcur[j][e] = mnext[j][e];
+      }
+    }
+    // epilogue of t-tile si if this wave owns it: rows 32*si + 8*(r/4) + 4*kk + r%4
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (own(j) != si) continue;  // uniform
+      auto emit = [&](int r) {
+        const int trow = 32 * si + 8 * (r / 4) + 4 * kk + (r % 4);
+        f2 y;
+        y[0] = acc[j][0][r];
+        y[1] = acc[j][1][r];
+        if constexpr (GATE) {
+          y[0] *= silu(zv[r][0]);
+          y[1] *= silu(zv[r][1]);
+        }
+        st2(oh + trow * xs, y);
+      };
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) emit(r);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * si + 8 * (r / 4) + 4 * kk + (r % 4) <= last) emit(r);
+      }
+      if constexpr (GATE) {
+        if (j + 1 < NS) load_z(own(j + 1));
+      }
+    }
+  }
+}
+
+// True when the four-heads-per-workgroup kernel handles this problem.
+static bool use_group_kernel(const Problem& p) {
+  return (p.Q == 64 || p.Q == 128) && (p.N == 64 || p.N == 128) && ((p.H / p.G) % 4 == 0);
+}
+
 template <typename T, int Q, int N>
 static void launch_qn(const Problem& p, hipStream_t s) {
+  if constexpr ((Q == 64 || Q == 128) && (N == 64 || N == 128)) {
+    if (use_group_kernel(p)) {
+      const int64_t nunits = p.b * p.nc * (p.H / 4);
+      if (p.z)
+        hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, true>), dim3((unsigned)nunits),
+                           dim3(512), 0, s, static_cast<const T*>(p.x),
+                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,
+                           static_cast<const T*>(p.z), p.ws_dt, p.ws_cum, p.ws_states_in,
+                           static_cast<T*>(p.out), p.L, p.H, p.G, p.nc, nunits);
+      else
+        hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, false>), dim3((unsigned)nunits),
+                           dim3(512), 0, s, static_cast<const T*>(p.x),
+                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,
+                           static_cast<const T*>(p.z), p.ws_dt, p.ws_cum, p.ws_states_in,
+                           static_cast<T*>(p.out), p.L, p.H, p.G, p.nc, nunits);
+      return;
+    }
+  }
   const int64_t nunits = p.b * p.nc * p.H;
   hipLaunchKernelGGL((chunk_scan_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(256), 0, s,
                      static_cast<const T*>(p.x), static_cast<const T*>(p.B),

@@ -3,29 +3,155 @@
 //   S_c[p][n] = sum_{t in chunk c} x_t[p] * w_t * B_t[n],
 //   w_t = exp(cum_last - cum_t) * dt_t,
 //
-// i.e. the recurrence run over the chunk alone from a zero state.  One
-// workgroup (4 waves) per (batch, chunk, head); the [P x Q] x [Q x N] product
-// runs on v_mfma_f32_16x16x4_f32 with fp32 accumulation.
+// i.e. the recurrence run over the chunk alone from a zero state, as a
+// [P x Q] x [Q x N] product on the matrix cores with fp32 accumulation.  The
+// contraction index is time.  Results go to the workspace in the tiled state
+// layout (ssd_device.h).
 //
-// Operands go from global memory straight into the MFMA lane layout: the
-// contraction index is time, and within one 4-deep MFMA step lane l handles
-// timestep 4*k + l/16.  Rows of x and B are contiguous in p and n, so a lane
-// reads MB consecutive x values and NB consecutive B values of its row; the
-// p (n) index of a 16-wide MFMA block is therefore strided by MB (NB).
-#include "ssd_device.h"
+// Two kernels:
+//  * chunk_state_wave_kernel (N = 64 or 128): two waves per (chunk, head),
+//    four heads per workgroup.  The first wave of a head computes dt and the
+//    in-chunk cumsum (stage 1, fused here); then each wave holds half of the
+//    n columns of the state tile in accumulators of v_mfma_f32_32x32x2_f32
+//    while it walks the chunk two timesteps per MFMA.  It computes
+//    S^T = B^T (w x): lane l supplies B[t][32*nt + l%32] (A operand) and
+//    w_t x[t][2*(l%32) + pt] (B operand) for timestep t = 2m + l/32, so x is
+//    read as float2 and each register group of the result is four
+//    consecutive n of one p -- one float4 of the tiled layout.
+//  * chunk_state_kernel (any N): four waves per (chunk, head) on
+//    v_mfma_f32_16x16x4_f32, after a separate stage-1 launch.
+#include "ssd_dt.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
 
-// Wave tiling of the P x N (64 x N) state: each wave owns MB x NB blocks of
-// 16 x 16.  Waves split n first, then p.
+// ---------------------------------------------------------------------------
+// one wave per (chunk, head), stage 1 fused
+// ---------------------------------------------------------------------------
+
+template <typename T, int Q, int N>
+__global__ __launch_bounds__(512) void chunk_state_wave_kernel(
+    const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ dt_raw,
+    const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
+    float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states, int64_t L,
+    int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+  constexpr int P = 64, NTN = N / 32, NTW = NTN / 2, E = Q / kWave;
+  static_assert(N == 64 || N == 128, "tile");
+  __shared__ float w_lds[4][2][Q / 2];  // [head][t % 2][t / 2]
+
+  const int64_t HQ = (H + 3) / 4;
+  const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*HQ + hq)
+  const int64_t hq = u % HQ, c = (u / HQ) % nc, b = u / (HQ * nc);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int slot = wave >> 1, half = wave & 1;  // two waves per head
+  const int64_t h = hq * 4 + slot;
+  const bool active = h < H;
+
+  if (active && half == 0) {
+    float dtv[E], cum[E], cum_last;
+    wave_dt_cumsum<T, Q>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c, h, L,
+                         H, nc, ws_dt, ws_cum, dtv, cum, &cum_last);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const int t = lane * E + k;
+      w_lds[slot][t & 1][t >> 1] = __expf(cum_last - cum[k]) * dtv[k];
+    }
+  }
+  __syncthreads();
+  if (!active) return;  // after the only barrier
+
+  const int64_t g = h / (H / G);
+  const int i = lane % 32, kk = lane / 32;
+  const int64_t t0 = c * Q;
+  const T* xb = x + ((b * L + t0) * H + h) * P + 2 * i;
+  const T* bb = Bm + ((b * L + t0) * G + g) * N + 32 * NTW * half + i;
+  const int64_t xs = H * P, bs = G * N;
+  const float* wrow = w_lds[slot][kk];  // w of timesteps 2m + kk, m = 0 .. Q/2-1
+
+  f16x acc[NTW][2];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) acc[nt][0] = acc[nt][1] = zero16();
+
+  // Loads run PF steps ahead of the MFMAs through a ring of registers.  Rows
+  // past the sequence end are clamped to the last row (always readable) and
+  // their operands replaced by zeros, so the loop body has no divergent
+  // branch and every load can be in flight while earlier steps compute.
+  constexpr int PF = 8, KS = Q / 2;
+  static_assert(KS % PF == 0, "ring");
+  const int64_t last = L - 1 - t0;  // last readable row of this chunk
+  auto row = [&](int m) -> int64_t {
+    const int64_t t = 2 * m + kk;
+    return t < last ? t : last;
+  };
+  f2 xr[PF];
+  float br[PF][NTW];
+#pragma unroll
+  for (int d = 0; d < PF; ++d) {
+    const int64_t t = row(d);
+    xr[d] = ld2(xb + t * xs);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bb + t * bs + 32 * nt);
+  }
+  for (int m0 = 0; m0 < KS; m0 += PF) {
+    f4 wv[PF / 4];
+#pragma unroll
+    for (int k = 0; k < PF / 4; ++k) wv[k] = *reinterpret_cast<const f4*>(wrow + m0 + 4 * k);
+#pragma unroll
+    for (int d = 0; d < PF; ++d) {
+      const int m = m0 + d;
+      // rows past the end contribute exactly zero (selects, not branches)
+      const bool ok = 2 * m + kk <= last;
+      const float w = wv[d / 4][d % 4];
+      const float x0 = ok ? xr[d][0] * w : 0.0f, x1 = ok ? xr[d][1] * w : 0.0f;
+      float bv[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) bv[nt] = ok ? br[d][nt] : 0.0f;
+      if (m + PF < KS) {  // uniform: refill the slot for step m + PF
+        const int64_t t = row(m + PF);
+        xr[d] = ld2(xb + t * xs);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bb + t * bs + 32 * nt);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        acc[nt][0] = mfma32x32x2(bv[nt], x0, acc[nt][0]);
+        acc[nt][1] = mfma32x32x2(bv[nt], x1, acc[nt][1]);
+      }
+    }
+  }
+
+  // register 4R+e of tile (nt, pt): n = 32*(NTW*half + nt) + 8*R + 4*kk + e, p = 2*i + pt
+  float* dst = states + ((b * nc + c) * H + h) * (int64_t)(P * N);
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        f4 v;
+        v[0] = acc[nt][pt][4 * R];
+        v[1] = acc[nt][pt][4 * R + 1];
+        v[2] = acc[nt][pt][4 * R + 2];
+        v[3] = acc[nt][pt][4 * R + 3];
+        const int n = 32 * (NTW * half + nt) + 8 * R + 4 * kk;
+        st4(dst + state_tile_offset(2 * i + pt, n, N), v);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// general: four waves per (chunk, head)
+// ---------------------------------------------------------------------------
+
+// Wave tiling of the 64 x N state in 16 x 16 blocks: each wave owns MB x NB
+// blocks; waves split n first, then p.  Lane l handles timestep 4k + l/16 of
+// MFMA step k and reads MB consecutive x values and NB consecutive B values,
+// so the p (n) index inside a block is strided by MB (NB).
 template <int N>
 struct StateTile {
-  static constexpr int NB = N >= 128 ? 2 : 1;        // n-blocks per wave
-  static constexpr int MB = (N / 16) / NB;            // p-blocks per wave (MB*NB = N/16)
-  static constexpr int WN = N / (16 * NB);            // waves along n
-  static constexpr int WP = 4 / WN;                   // waves along p
-  static_assert(MB * NB * 4 == 4 * (N / 16), "tile");
+  static constexpr int NB = N >= 128 ? 2 : 1;
+  static constexpr int MB = (N / 16) / NB;
+  static constexpr int WN = N / (16 * NB);
+  static constexpr int WP = 4 / WN;
   static_assert(WN * WP == 4 && MB * 16 * WP == 64, "P = 64 split");
 };
 
@@ -39,14 +165,14 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
   constexpr int MB = Tl::MB, NB = Tl::NB, WP = Tl::WP;
   __shared__ float w_lds[Q];
 
-  const int64_t u = xcd_remap(blockIdx.x, nunits);  // unit = ((b*nc + c)*H + h)
+  const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*H + h)
   const int64_t h = u % H;
   const int64_t c = (u / H) % nc;
   const int64_t b = u / (H * nc);
   const int64_t g = h / (H / G);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
-  const int64_t dc = ((b * H + h) * nc + c) * Q;  // dt / cum of this chunk
+  const int64_t dc = ((b * H + h) * nc + c) * Q;
   if (tid < Q) {
     const float cum_last = ws_cum[dc + Q - 1];
     w_lds[tid] = __expf(cum_last - ws_cum[dc + tid]) * ws_dt[dc + tid];
@@ -105,16 +231,29 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
     for (int j = 0; j < MB; ++j) {
       const int p = p0 + MB * (4 * lk + r) + j;
 #pragma unroll
-      for (int jn = 0; jn < NB; ++jn) dst[p * N + n0 + NB * li + jn] = acc[j][jn][r];
+      for (int jn = 0; jn < NB; ++jn)
+        dst[state_tile_offset(p, n0 + NB * li + jn, N)] = acc[j][jn][r];
     }
 }
 
+// ---------------------------------------------------------------------------
+
+bool chunk_state_fuses_dt(const Problem& p) { return p.N == 64 || p.N == 128; }
+
 template <typename T, int Q, int N>
 static void launch_qn(const Problem& p, hipStream_t s) {
-  const int64_t nunits = p.b * p.nc * p.H;
-  hipLaunchKernelGGL((chunk_state_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(256), 0, s,
-                     static_cast<const T*>(p.x), static_cast<const T*>(p.B), p.ws_dt, p.ws_cum,
-                     p.ws_states, p.L, p.H, p.G, p.nc, nunits);
+  if constexpr (N == 64 || N == 128) {
+    const int64_t nunits = p.b * p.nc * ((p.H + 3) / 4);
+    hipLaunchKernelGGL((chunk_state_wave_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(512), 0,
+                       s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
+                       static_cast<const T*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.ws_dt,
+                       p.ws_cum, p.ws_states, p.L, p.H, p.G, p.nc, nunits);
+  } else {
+    const int64_t nunits = p.b * p.nc * p.H;
+    hipLaunchKernelGGL((chunk_state_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(256), 0, s,
+                       static_cast<const T*>(p.x), static_cast<const T*>(p.B), p.ws_dt, p.ws_cum,
+                       p.ws_states, p.L, p.H, p.G, p.nc, nunits);
+  }
 }
 
 template <typename T, int Q>

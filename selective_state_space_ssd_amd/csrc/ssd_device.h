@@ -6,7 +6,9 @@
 
 namespace ssd {
 
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16x __attribute__((ext_vector_type(16)));
 typedef uint16_t bf16_t;  // storage of a bfloat16 value
 
 constexpr int kWave = 64;
@@ -43,6 +45,21 @@ __device__ __forceinline__ f4 ld4(const bf16_t* p) {
   return r;
 }
 
+// p must be aligned to 2 elements.
+__device__ __forceinline__ f2 ld2(const float* p) { return *reinterpret_cast<const f2*>(p); }
+__device__ __forceinline__ f2 ld2(const bf16_t* p) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+  f2 r;
+  r[0] = bf16_lo(w);
+  r[1] = bf16_hi(w);
+  return r;
+}
+
+__device__ __forceinline__ void st2(float* p, f2 v) { *reinterpret_cast<f2*>(p) = v; }
+__device__ __forceinline__ void st2(bf16_t* p, f2 v) {
+  *reinterpret_cast<uint32_t*>(p) = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+}
+
 __device__ __forceinline__ void st4(float* p, f4 v) { *reinterpret_cast<f4*>(p) = v; }
 __device__ __forceinline__ void st4(bf16_t* p, f4 v) {
   uint2 w;
@@ -57,6 +74,37 @@ __device__ __forceinline__ void st4(bf16_t* p, f4 v) {
 // register r of lane l.
 __device__ __forceinline__ f4 mfma16x16x4(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x2_f32: D[32x32] += A[32x2] * B[2x32].  Lane l supplies
+// A[l%32][l/32] and B[l/32][l%32]; register r of lane l holds D element
+// (row 8*(r/4) + 4*(l/32) + r%4, col l%32).
+__device__ __forceinline__ f16x mfma32x32x2(float a, float b, f16x c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x zero16() {
+  f16x z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// ---- state layout in the workspace ------------------------------------------
+// A [P = 64][N] state block is stored in tiles of four consecutive n: the
+// float4 at index ((q*2 + pj)*64 + lane) holds row p = 2*(lane%32) + pj,
+// columns n = (N/2)*(lane/32) + 4*q + 0..3.  A wave that walks q reads (and
+// the chunk-state kernel writes) 1 KB of contiguous memory per instruction.
+__device__ __forceinline__ int state_tile_offset(int p, int n, int N) {
+  const int half = N / 2;
+  const int kk = n / half, q = (n % half) >> 2, e = n & 3;
+  return (((q * 2 + (p & 1)) * 64) + 32 * kk + (p >> 1)) * 4 + e;
+}
+// Row p and first column n of the float4 at tile index k (inverse of above).
+__device__ __forceinline__ void state_tile_coords(int k, int N, int* p, int* n) {
+  const int lane = k & 63, pj = (k >> 6) & 1, q = k >> 7;
+  *p = 2 * (lane & 31) + pj;
+  *n = (N / 2) * (lane >> 5) + 4 * q;
 }
 
 // ---- math -------------------------------------------------------------------

@@ -1,0 +1,72 @@
+// Per-wave discretization step and in-chunk running sum (stage 1 of the scan),
+// shared by the standalone dt/cumsum kernel and the chunk-state kernel that
+// fuses it.
+//
+//   dt_t  = clamp(softplus(dt_raw_t + dt_bias_h), dt_min, dt_max)
+//   cum_t = sum_{r = chunk start .. t} dt_r * A_h
+//
+// dt is a discretization input folded into the log-gate dt*A with A constant
+// per head (flash-linear-attention PR #49, its list of differences between
+// simple_gla and the mamba2_ssd kernel); dt_bias and dt_limit are arguments of
+// the repro script on mamba issue #647.
+#pragma once
+
+#include "ssd_device.h"
+
+namespace ssd {
+
+// softplus(u) = log(1 + e^u) in a form that neither overflows nor cancels.
+__device__ __forceinline__ float softplus(float u) {
+  return fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u)));
+}
+
+// One wave computes dt and cum for the Q timesteps of chunk c of head h
+// (batch b).  Lane l owns timesteps l*E .. l*E+E-1 (E = Q/64); it sums them
+// serially and a wave-wide inclusive scan of the lane totals gives its offset.
+// Steps past the sequence end get dt = 0 and dA = 0, so the chunk's last cum
+// is the cum of its last real step.  Writes dt and cum to the workspace and
+// returns them in dt_out / cum_out (the lane's E values) and the chunk's last
+// cum in *cum_last.
+template <typename T, int Q>
+__device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, float a, float bias,
+                                               float dt_min, float dt_max, int64_t b, int64_t c,
+                                               int64_t h, int64_t L, int64_t H, int64_t nc,
+                                               float* __restrict__ ws_dt,
+                                               float* __restrict__ ws_cum, float (&dt_out)[Q / 64],
+                                               float (&cum_out)[Q / 64], float* cum_last) {
+  constexpr int E = Q / kWave;
+  const int lane = threadIdx.x % kWave;
+  float run[E];
+  float total = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t t = c * Q + (int64_t)lane * E + i;
+    float d = 0.0f;
+    if (t < L) {
+      d = softplus(ld1(dt_raw + (b * L + t) * H + h) + bias);
+      // comparisons (not fminf/fmaxf) so that a NaN input stays NaN
+      d = d < dt_min ? dt_min : d;
+      d = d > dt_max ? dt_max : d;
+    }
+    dt_out[i] = d;
+    total += d * a;
+    run[i] = total;
+  }
+  float incl = total;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  const float base = incl - total;
+  *cum_last = __shfl(incl, kWave - 1, kWave);
+  const int64_t o = ((b * H + h) * nc + c) * Q + (int64_t)lane * E;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    cum_out[i] = base + run[i];
+    ws_dt[o + i] = dt_out[i];
+    ws_cum[o + i] = cum_out[i];
+  }
+}
+
+}  // namespace ssd

@@ -27,8 +27,8 @@ struct Problem {
   // workspace regions (float32)
   float* ws_dt;          // [b, H, nc, Q]
   float* ws_cum;         // [b, H, nc, Q]
-  float* ws_states;      // [b, nc, H, P, N]  chunk-local states
-  float* ws_states_in;   // [b, nc, H, P, N]  state entering each chunk
+  float* ws_states;      // [b, nc, H] tiled P x N blocks: chunk-local states
+  float* ws_states_in;   // [b, nc, H] tiled P x N blocks: state entering each chunk
 };
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().
@@ -36,6 +36,10 @@ hipError_t launch_dt_cumsum(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_passing(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
+
+// True when the chunk-state kernel chosen for this problem also computes dt
+// and its in-chunk cumsum (stage 1), so no separate stage-1 launch is needed.
+bool chunk_state_fuses_dt(const Problem& p);
 
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);

@@ -35,21 +35,39 @@ def _case(seed, b, L, H, P, N, G, Q, dtype, **kw):
 # small problems, full comparison (several chunks + a ragged tail)
 # --------------------------------------------------------------------------
 
-SMALL = [(dt, Q, N) for dt in ("f32", "bf16") for Q in (64, 128, 256) for N in (16, 128)]
-SMALL += [("f32", 128, 32), ("f32", 128, 64), ("bf16", 64, 32), ("bf16", 256, 64)]
+# (dtype, Q, N, nheads, ngroups).  nheads / ngroups = 2 takes the general
+# chunk-scan kernel; a multiple of 4 takes the four-heads-per-workgroup one
+# (Q 64/128, N 64/128); nheads = 6 leaves idle waves in the chunk-state kernel.
+SMALL = [(dt, Q, N, 4, 2) for dt in ("f32", "bf16") for Q in (64, 128, 256) for N in (16, 128)]
+SMALL += [("f32", 128, 32, 4, 2), ("f32", 128, 64, 4, 2), ("bf16", 64, 32, 4, 2),
+          ("bf16", 256, 64, 4, 2)]
+SMALL += [(dt, Q, N, 8, G) for dt in ("f32", "bf16") for Q in (64, 128) for N in (64, 128)
+          for G in (1, 2)]
+SMALL += [("f32", 128, 128, 6, 3), ("f32", 64, 64, 12, 3), ("bf16", 128, 128, 16, 1)]
 
 
-@pytest.mark.parametrize("dtype,Q,N", SMALL, ids=[f"{d}-Q{q}-N{n}" for d, q, n in SMALL])
-def test_small_ragged(dtype, Q, N):
+@pytest.mark.parametrize("dtype,Q,N,H,G", SMALL,
+                         ids=[f"{d}-Q{q}-N{n}-H{h}-G{g}" for d, q, n, h, g in SMALL])
+def test_small_ragged(dtype, Q, N, H, G):
     L = 2 * Q + Q // 2 + 7
-    w = _case(1000 + Q + N, 2, L, 4, 64, N, 2, Q, dtype, init=True)
-    log(f"test_small_ragged {dtype} Q={Q} N={N} L={L}")
+    w = _case(1000 + Q + N + H, 2, L, H, 64, N, G, Q, dtype, init=True)
+    log(f"test_small_ragged {dtype} Q={Q} N={N} H={H} G={G} L={L}")
     inp = make_inputs(w)
     t = upload(inp, dtype)
     out, fin = run_gpu(t, Q, init=t["initial_states"])
     ref, rfin = _oracle(inp, init=inp["initial_states"])
     compare("out", np64(out), ref, TOL[dtype])
     compare("final", np64(fin), rfin, TOL[dtype])
+
+
+def _state_tile_offsets(N):
+    """offs[p, n] = float offset of state element (p, n) in a tiled block
+    (the workspace layout documented in include/ssd.h; headdim 64)."""
+    p = np.arange(64)[:, None]
+    n = np.arange(N)[None, :]
+    half = N // 2
+    k, q, e = n // half, (n % half) // 4, n % 4
+    return (((q * 2 + p % 2) * 64) + 32 * k + p // 2) * 4 + e
 
 
 def _ws_regions(ws, b, L, H, P, N, Q):
@@ -60,17 +78,26 @@ def _ws_regions(ws, b, L, H, P, N, Q):
     o_cum = r(dtn * 4) // 4
     o_st = o_cum + r(dtn * 4) // 4
     o_in = o_st + r(stn * 4) // 4
+    offs = torch.from_numpy(_state_tile_offsets(N).reshape(-1)).to(ws.device)
+
+    def dense(block):
+        return block.view(b, nc, H, P * N)[..., offs].view(b, nc, H, P, N)
+
     return {"dt": f[:dtn].view(b, H, nc, Q), "cum": f[o_cum:o_cum + dtn].view(b, H, nc, Q),
-            "chunk_states": f[o_st:o_st + stn].view(b, nc, H, P, N),
-            "states_in": f[o_in:o_in + stn].view(b, nc, H, P, N)}
+            "chunk_states": dense(f[o_st:o_st + stn]),
+            "states_in": dense(f[o_in:o_in + stn])}
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_stage_intermediates(dtype):
+INTER = [("f32", 128, 128), ("bf16", 128, 128), ("f32", 64, 16), ("bf16", 256, 32),
+         ("f32", 256, 64)]
+
+
+@pytest.mark.parametrize("dtype,Q,N", INTER, ids=[f"{d}-Q{q}-N{n}" for d, q, n in INTER])
+def test_stage_intermediates(dtype, Q, N):
     """Each stage's output in the workspace against the oracle's per-chunk
     intermediates: dt and dA_cumsum (stage 1), chunk-local states (stage 2),
     states entering each chunk (stage 3)."""
-    b, L, H, P, N, G, Q = 2, 300, 4, 64, 128, 2, 128
+    b, L, H, P, G = 2, 2 * Q + 44, 4, 64, 2
     w = _case(77, b, L, H, P, N, G, Q, dtype, init=True)
     log(f"test_stage_intermediates {dtype}")
     inp = make_inputs(w)
@@ -82,6 +109,7 @@ def test_stage_intermediates(dtype):
     ref = oracle.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
                                      dt_bias=inp["dt_bias"], initial_states=inp["initial_states"])
     valid = np.zeros((b, H, 3, Q), bool)
+    assert -(-L // Q) == 3
     valid.reshape(b, H, -1)[:, :, :L] = True
     compare("dt", got["dt"], ref["dt"], 1e-5, mask=valid)
     compare("dA_cumsum", got["cum"], ref["cum"], 1e-4, mask=valid)

@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the step once as a HIP graph per input copy, replay "
+                         "it, and report the replay rate as the value")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the steps, run 3 plain device copies of this many MiB "
                          "(reference kernel for calibrating HBM byte counters)")
@@ -133,12 +136,13 @@ def main():
                 t["C"].data_ptr(), t["D"].data_ptr(), t["z"].data_ptr(),
                 t["dt_bias"].data_ptr(), 0.0, math.inf, w.chunk_size, w.ngroups, None,
                 out.data_ptr(), None, w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                ssd.SSD_F32, ws.data_ptr(), ws_bytes, stream.cuda_stream))
+                ssd.SSD_F32, ws.data_ptr(), ws_bytes))
         calls.append(args_copy)
 
     def step(k, timings=None):
+        s = torch.cuda.current_stream(dev).cuda_stream
         for i, a in enumerate(calls[k % 2]):
-            st = ssd.scan_fwd_raw(*a, timing=None if timings is None else timings[i])
+            st = ssd.scan_fwd_raw(*a, s, timing=None if timings is None else timings[i])
             if st != 0:
                 raise ssd.SsdError(st, ssd.status_string(st))
 
@@ -155,12 +159,32 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps
+    # eager launches: exactly `steps` steps
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(k)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager = time.perf_counter() - t0
+
+    # the same step captured as one HIP graph per input copy (three calls,
+    # nine kernels, no allocation or memset inside), replayed
+    elapsed_graph = None
+    if args.graph:
+        graphs = []
+        for k in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        for k in range(args.warmup):
+            graphs[k % 2].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graphs[k % 2].replay()
+        torch.cuda.synchronize()
+        elapsed_graph = time.perf_counter() - t0
+    elapsed = elapsed_graph if elapsed_graph is not None else elapsed_eager
 
     # per-stage durations: the same steps again, with the library recording a
     # HIP event around each stage on the launch stream
@@ -206,6 +230,7 @@ def main():
                         "z gate and D skip on, dt_limit (0, inf)",
             "batch": 2, "seqlen": 2048, "nheads": 32, "headdim": 64, "dstate": 128,
             "chunk_size": 128, "ngroups": [1, 2, 4], "tokens_per_step": tokens,
+            "launch": "hip graph replay" if elapsed_graph is not None else "eager",
         },
         "roofline": {
             "kernel": dom_name,
@@ -226,6 +251,8 @@ def main():
             "stage_us_per_call": {s: float(per_stage_total[i] / len(workloads) * 1e3)
                                   for i, s in enumerate(ssd.STAGES)},
             "event_pass_ms_per_step": elapsed_ev / args.steps * 1e3,
+            "eager_ms_per_step": elapsed_eager / args.steps * 1e3,
+            "eager_tokens_per_s": tokens * args.steps / elapsed_eager,
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(workloads),
     }

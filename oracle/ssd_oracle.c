@@ -26,7 +26,7 @@
  *    repro script's arguments.
  *  - Continuation from a given state (chunked prefill): mamba issue #488.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - the state is stored as h[p][n] (headdim x dstate), the transpose of the
  *    B x^T form; the mathematics are identical;
  *  - y_t includes token t's own contribution (h_t is updated before use);

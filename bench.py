@@ -40,7 +40,7 @@ def alg_flops(w):
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     nc = math.ceil(L / Q)
     return {
-        "dt_cumsum": b * L * H * 2.0,
+        "prep": b * L * H * 2.0,
         "chunk_state": b * nc * H * 2.0 * Q * P * N,
         "state_passing": b * nc * H * 2.0 * P * N,
         "chunk_scan": b * nc * (H * (2.0 * Q * P * N + P * Q * (Q + 1)) + G * N * Q * (Q + 1)),

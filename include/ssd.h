@@ -113,6 +113,9 @@ extern "C" {
  *             from a zero state)
  *   states_in [batch, nchunks, nheads] blocks of headdim*dstate floats: the
  *             state entering each chunk
+ *   B^T       [batch, nchunks, ngroups] blocks of dstate x chunk_size bf16
+ *             (present only when dtype is SSD_BF16, chunk_size 128 or 256 and
+ *             dstate 64 or 128: the bf16 matrix-core kernels' transposed B)
  * with nchunks = ceil(seqlen / chunk_size).  Inside a state block (headdim
  * 64) element (p, n) sits at float offset
  *   ((q*2 + p%2)*64 + 32*k + p/2)*4 + n%4,  k = n / (dstate/2),
@@ -145,8 +148,10 @@ int ssd_abi_version(void);
  * ssd_scan_fwd_timed behaves exactly like ssd_scan_fwd and also records an
  * event before the first stage and after each stage on `stream`.
  * ssd_timing_read waits for those events and writes the milliseconds spent in
- * each stage (SSD_NUM_STAGES floats: dt/cumsum, chunk state, state passing,
- * chunk scan).  Returns SSD_OK or SSD_ERR_HIP / SSD_ERR_INVALID_ARG.
+ * each stage (SSD_NUM_STAGES floats: prep -- the dt/cumsum kernel, or the B^T
+ * transpose of the bf16 kernels, empty when dt/cumsum is fused into the chunk
+ * state --, chunk state, state passing, chunk scan).  Returns SSD_OK or
+ * SSD_ERR_HIP / SSD_ERR_INVALID_ARG.
  */
 #define SSD_NUM_STAGES 4
 typedef struct ssd_timing ssd_timing;

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libssd.so")
 SSD_F32 = 0
 SSD_BF16 = 1
 SSD_NUM_STAGES = 4
-STAGES = ("dt_cumsum", "chunk_state", "state_passing", "chunk_scan")
+STAGES = ("prep", "chunk_state", "state_passing", "chunk_scan")
 
 _lib = None
 

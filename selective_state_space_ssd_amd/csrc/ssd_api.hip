@@ -36,8 +36,14 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 struct Layout {
   int64_t nc = 0;
-  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, total = 0;
+  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0, total = 0;
 };
+
+// The bf16 matrix-core path (same rule as ssd::use_bf16_kernels).
+bool bf16_path(int dtype, int64_t dstate, int chunk_size) {
+  return dtype == SSD_BF16 && (chunk_size == 128 || chunk_size == 256) &&
+         (dstate == 64 || dstate == 128);
+}
 
 // Shape checks shared by the workspace query and the entry point.
 int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
@@ -67,7 +73,13 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
   lay->off_cum = round_up((size_t)dtn * 4);
   lay->off_states = lay->off_cum + round_up((size_t)dtn * 4);
   lay->off_states_in = lay->off_states + round_up((size_t)stn * 4);
-  lay->total = lay->off_states_in + round_up((size_t)stn * 4);
+  lay->off_bt = lay->off_states_in + round_up((size_t)stn * 4);
+  lay->total = lay->off_bt;
+  if (bf16_path(dtype, dstate, chunk_size)) {
+    int64_t btn;
+    if (!mul_ok(batch * nc * ngroups, dstate * chunk_size, &btn)) return SSD_ERR_INVALID_ARG;
+    lay->total += round_up((size_t)btn * 2);
+  }
   if (batch == 0 || seqlen == 0) lay->total = 0;
   return SSD_OK;
 }
@@ -148,12 +160,18 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.ws_cum = lay.total ? reinterpret_cast<float*>(ws + lay.off_cum) : nullptr;
   p.ws_states = lay.total ? reinterpret_cast<float*>(ws + lay.off_states) : nullptr;
   p.ws_states_in = lay.total ? reinterpret_cast<float*>(ws + lay.off_states_in) : nullptr;
+  p.ws_bt = lay.total ? reinterpret_cast<uint16_t*>(ws + lay.off_bt) : nullptr;
 
   auto mark = [&](int i) -> bool {
     return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
   };
   if (!mark(0)) return SSD_ERR_HIP;
-  if (seqlen > 0) {
+  const bool bf16k = ssd::use_bf16_kernels(p);
+  if (seqlen > 0 && bf16k) {
+    // prep (B^T), then the chunk state with dt/cumsum fused in
+    if (ssd::launch_bf16_stage(p, stream, 0) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
+    if (ssd::launch_bf16_stage(p, stream, 1) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
+  } else if (seqlen > 0) {
     if (!ssd::chunk_state_fuses_dt(p) && ssd::launch_dt_cumsum(p, stream) != hipSuccess)
       return SSD_ERR_HIP;
     if (!mark(1)) return SSD_ERR_HIP;
@@ -166,7 +184,10 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
   }
   if (!mark(3)) return SSD_ERR_HIP;
-  if (seqlen > 0 && ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (seqlen > 0) {
+    const hipError_t e = bf16k ? ssd::launch_bf16_stage(p, stream, 2) : ssd::launch_chunk_scan(p, stream);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+  }
   if (!mark(4)) return SSD_ERR_HIP;
   if (timing) timing->recorded = true;
   return SSD_OK;

@@ -83,6 +83,79 @@ __device__ __forceinline__ f16x mfma32x32x2(float a, float b, f16x c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// ---- bf16 matrix-core operands ------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] * B[16x32].  Lane l supplies
+// A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; the result has the
+// layout of the 32x32x2 fp32 instruction above.
+__device__ __forceinline__ f16x mfma32x32x16(s16x8 a, s16x8 b, f16x c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Pack two fp32 into two bf16 (round to nearest even) in one 32-bit word:
+// one v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight fp32 -> one 8 x bf16 operand.
+__device__ __forceinline__ s16x8 to_bf16x8(const float (&v)[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]);
+  w.w = pack_bf16x2(v[6], v[7]);
+  return __builtin_bit_cast(s16x8, w);
+}
+
+// Split eight fp32 into two bf16 operands, hi = bf16(v) and lo = bf16(v - hi)
+// (v - hi is exact in fp32).  hi + lo carries 16 significant bits, so the
+// pair of products A.hi + A.lo of an exact bf16 operand A is accurate to about
+// 2^-16 relative, where a single bf16 operand gives 2^-8.
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], s16x8& hi, s16x8& lo) {
+  uint4 h, l;
+  h.x = pack_bf16x2(v[0], v[1]);
+  h.y = pack_bf16x2(v[2], v[3]);
+  h.z = pack_bf16x2(v[4], v[5]);
+  h.w = pack_bf16x2(v[6], v[7]);
+  l.x = pack_bf16x2(v[0] - bf16_lo(h.x), v[1] - bf16_hi(h.x));
+  l.y = pack_bf16x2(v[2] - bf16_lo(h.y), v[3] - bf16_hi(h.y));
+  l.z = pack_bf16x2(v[4] - bf16_lo(h.z), v[5] - bf16_hi(h.z));
+  l.w = pack_bf16x2(v[6] - bf16_lo(h.w), v[7] - bf16_hi(h.w));
+  hi = __builtin_bit_cast(s16x8, h);
+  lo = __builtin_bit_cast(s16x8, l);
+}
+
+// Transposed read of four bf16 from an LDS tile X (row-major, ld elements per
+// row, ld and c0 multiples of 4): lane l receives X[r0 + 0..3][c0 + l%32],
+// where r0 may differ between the two halves of the wave (lanes 0-31 and
+// 32-63).  ds_read_b64_tr_b16: in every group of 16 lanes, lane 4a + e gets
+// element e of the 8-byte words read by lanes a, a+4, a+8, a+12 of the group;
+// so lane m of a group reads row r0 + m/4 at column c0 + 16*(group%2) + 4*(m%4).
+__device__ __forceinline__ s16x4 lds_tr4(const bf16_t* lds, int ld, int r0, int c0) {
+  const int lane = threadIdx.x % 64;
+  const int m = lane % 16, half = (lane / 16) % 2;
+  const bf16_t* p = lds + (r0 + m / 4) * ld + c0 + 16 * half + 4 * (m % 4);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// B operand of a 32x32x16 MFMA whose contraction index is the row index of an
+// LDS tile: lane l supplies rows {r0 + 0..3} and {r1 + 0..3} of column c0 + l%32.
+__device__ __forceinline__ s16x8 lds_tr_operand(const bf16_t* lds, int ld, int r0, int r1, int c0) {
+  const s16x4 a = lds_tr4(lds, ld, r0, c0), b = lds_tr4(lds, ld, r1, c0);
+  s16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
 __device__ __forceinline__ f16x zero16() {
   f16x z;
 #pragma unroll

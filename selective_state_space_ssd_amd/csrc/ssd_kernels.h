@@ -29,6 +29,7 @@ struct Problem {
   float* ws_cum;         // [b, H, nc, Q]
   float* ws_states;      // [b, nc, H] tiled P x N blocks: chunk-local states
   float* ws_states_in;   // [b, nc, H] tiled P x N blocks: state entering each chunk
+  uint16_t* ws_bt;       // [b, nc, G] blocks of N x Q bf16: B^T per chunk (bf16 kernels only)
 };
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().
@@ -40,6 +41,12 @@ hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
 // True when the chunk-state kernel chosen for this problem also computes dt
 // and its in-chunk cumsum (stage 1), so no separate stage-1 launch is needed.
 bool chunk_state_fuses_dt(const Problem& p);
+
+// bf16 matrix-core kernels (bf16 inputs, Q 128/256, N 64/128): stage 0 is the
+// B^T prep, stage 1 the chunk state (with dt/cumsum fused), stage 2 the chunk
+// scan.  The state passing between them is the common stage-3 kernel.
+bool use_bf16_kernels(const Problem& p);
+hipError_t launch_bf16_stage(const Problem& p, hipStream_t stream, int stage);
 
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);

@@ -66,7 +66,10 @@ def test_workspace_size_formula():
         nc = math.ceil(L / Q)
         want = 2 * r(b * H * nc * Q * 4) + 2 * r(b * nc * H * P * N * 4)
         assert _ws(b, L, H, P, N, G, Q) == want
-        assert _ws(b, L, H, P, N, G, Q, 1) == want  # intermediates are fp32 for bf16 too
+        # intermediates are fp32 for bf16 too; the bf16 matrix-core kernels
+        # (chunk 128/256, dstate 64/128) add B^T per (chunk, group) in bf16
+        bt = r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
+        assert _ws(b, L, H, P, N, G, Q, 1) == want + bt
     assert _ws(0, 100, 4, 64, 16, 1, 64) == 0
     assert _ws(2, 0, 4, 64, 16, 1, 64) == 0
     assert _ws(2, 100, 4, 64, 16, 3, 64) == 0       # rejected: 3 does not divide 4

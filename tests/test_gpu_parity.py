@@ -124,28 +124,33 @@ def test_stage_intermediates(dtype, Q, N):
 EDGE = [
     ("L=1", dict(seqlen=1)),
     ("L<Q", dict(seqlen=45)),
-    ("L=Q", dict(seqlen=128)),
-    ("L=Q+1", dict(seqlen=129)),
+    ("L=Q", dict(seqlen="Q")),
+    ("L=Q+1", dict(seqlen="Q+1")),
     ("G=H", dict(ngroups=8, nheads=8)),
     ("no gate, no skip", dict(gate=False, skip=False)),
     ("dt_limit", dict(), ),
 ]
+# fp32 at chunk 128 and bf16 at chunk 256 (the bf16 matrix-core kernels)
+EDGE_PATHS = [("f32", 128), ("bf16", 256)]
+EDGE_CASES = [(d, q, desc, ch) for d, q in EDGE_PATHS for desc, ch in EDGE]
 
 
-@pytest.mark.parametrize("desc,changes", EDGE, ids=[e[0] for e in EDGE])
-def test_edge_cases(desc, changes):
+@pytest.mark.parametrize("dtype,Q,desc,changes", EDGE_CASES,
+                         ids=[f"{d}-Q{q}-{e}" for d, q, e, _ in EDGE_CASES])
+def test_edge_cases(dtype, Q, desc, changes):
     base = dict(seqlen=200, nheads=4, ngroups=2, gate=True, skip=True)
     base.update(changes)
-    w = _case(300, 2, base["seqlen"], base["nheads"], 64, 128, base["ngroups"], 128, "f32",
+    L = {"Q": Q, "Q+1": Q + 1}.get(base["seqlen"], base["seqlen"])
+    w = _case(300, 2, L, base["nheads"], 64, 128, base["ngroups"], Q, dtype,
               gate=base["gate"], skip=base["skip"], init=True)
     lim = (0.01, 0.05) if desc == "dt_limit" else (0.0, math.inf)
-    log(f"test_edge_cases {desc}")
+    log(f"test_edge_cases {dtype} Q={Q} {desc}")
     inp = make_inputs(w)
-    t = upload(inp, "f32")
-    out, fin = run_gpu(t, 128, dt_limit=lim, init=t["initial_states"])
+    t = upload(inp, dtype)
+    out, fin = run_gpu(t, Q, dt_limit=lim, init=t["initial_states"])
     ref, rfin = _oracle(inp, dt_limit=lim, init=inp["initial_states"])
-    compare("out", np64(out), ref, TOL["f32"])
-    compare("final", np64(fin), rfin, TOL["f32"])
+    compare("out", np64(out), ref, TOL[dtype])
+    compare("final", np64(fin), rfin, TOL[dtype])
 
 
 def test_no_bias_no_init():
@@ -197,17 +202,19 @@ def test_unsupported_raises():
 # properties of the GPU path
 # --------------------------------------------------------------------------
 
-def test_ngroups_invariance():
+@pytest.mark.parametrize("dtype,Q", [("f32", 128), ("bf16", 256)])
+def test_ngroups_invariance(dtype, Q):
     """B, C replicated over G groups give bit-identical outputs to G = 1."""
-    w = small("f32_b2_L2048_H32_P64_N128_G1_Q128", seqlen=700, seed=21, init=True)
+    w = small("f32_b2_L2048_H32_P64_N128_G1_Q128", seqlen=700, seed=21, init=True,
+              dtype=dtype, chunk_size=Q)
     inp = make_inputs(w)
-    t = upload(inp, "f32")
-    ref_out, ref_fin = run_gpu(t, 128, init=t["initial_states"])
+    t = upload(inp, dtype)
+    ref_out, ref_fin = run_gpu(t, Q, init=t["initial_states"])
     for G in (2, 4):
         t2 = dict(t)
         t2["B"] = t["B"].repeat_interleave(G, dim=2).contiguous()
         t2["C"] = t["C"].repeat_interleave(G, dim=2).contiguous()
-        out, fin = run_gpu(t2, 128, init=t["initial_states"])
+        out, fin = run_gpu(t2, Q, init=t["initial_states"])
         assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin), G
 
 

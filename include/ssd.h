@@ -104,8 +104,18 @@ extern "C" {
  * allocates no memory and keeps no pointer after the call returns; calls are
  * reentrant and deterministic (bitwise identical results run to run).
  *
- * After the enqueued work completes, the workspace holds the intermediates
- * (float32, in this order, each region starting on a 256-byte boundary):
+ * Two kernel paths.  bf16 inputs with headdim 64 and dstate 64 or 128 take
+ * the fused path by default (see ssd_set_option): one set-up kernel and one
+ * scan kernel, in which each workgroup handles 128 timesteps of one (batch,
+ * head) and hands the state to the workgroup of the next 128 timesteps
+ * through the workspace (the chunked form gives the same result for any block
+ * length, up to rounding; chunk_size is still checked).  Every other case
+ * takes the staged path: dt/cumsum, chunk state, state passing and chunk
+ * scan kernels with their intermediates in the workspace.
+ *
+ * Staged path: after the enqueued work completes, the workspace holds the
+ * intermediates (float32, in this order, each region starting on a 256-byte
+ * boundary):
  *   dt        [batch, nheads, nchunks, chunk_size]   0 past the sequence end
  *   dA_cumsum [batch, nheads, nchunks, chunk_size]   in-chunk running sum of dt*A
  *   chunk_states [batch, nchunks, nheads] blocks of headdim*dstate floats:
@@ -122,6 +132,18 @@ extern "C" {
  *   q = (n % (dstate/2)) / 4,
  * i.e. float4 tiles of four consecutive n, ordered so that the kernels read
  * and write them with one contiguous 1 KB access per wave.
+ *
+ * Fused path: the workspace holds, each region on a 256-byte boundary,
+ *   ring   [batch*nheads][2] state blocks (tiled as above): the states
+ *          handed between consecutive 128-step blocks
+ *   flags  [batch*nheads][ceil(seqlen/128)] uint32 ready flags
+ *   control 9 uint32: eight ticket counters, then an error word that is
+ *          non-zero if a workgroup gave up waiting for its entering state
+ *          (outputs are then invalid; it cannot happen unless the device
+ *          stops making progress).  Its byte offset is
+ *          ssd_scan_fwd_workspace_size(...) - 256 + 32.
+ * The workspace of one call must not be in use by another call at the same
+ * time (true of both paths).
  */
 int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
                  const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
@@ -144,14 +166,32 @@ const char* ssd_status_string(int status);
 int ssd_abi_version(void);
 
 /*
+ * Process-wide options.  SSD_OPT_BF16_PATH selects the kernel path of bf16
+ * problems that the fused path covers: SSD_BF16_PATH_AUTO (default, fused),
+ * SSD_BF16_PATH_STAGED or SSD_BF16_PATH_FUSED.  The workspace size depends on
+ * the path, so set options before querying it; do not change them while
+ * another thread is between the query and the call.  ssd_set_option returns
+ * SSD_OK or SSD_ERR_INVALID_ARG; ssd_get_option the value or
+ * SSD_ERR_INVALID_ARG.  Host only, no HIP call.
+ */
+#define SSD_OPT_BF16_PATH 1
+#define SSD_BF16_PATH_AUTO 0
+#define SSD_BF16_PATH_STAGED 1
+#define SSD_BF16_PATH_FUSED 2
+int ssd_set_option(int option, int value);
+int ssd_get_option(int option);
+
+/*
  * Per-stage timing, for measurement.  A timing object holds HIP events;
  * ssd_scan_fwd_timed behaves exactly like ssd_scan_fwd and also records an
  * event before the first stage and after each stage on `stream`.
  * ssd_timing_read waits for those events and writes the milliseconds spent in
  * each stage (SSD_NUM_STAGES floats: prep -- the dt/cumsum kernel, or the B^T
  * transpose of the bf16 kernels, empty when dt/cumsum is fused into the chunk
- * state --, chunk state, state passing, chunk scan).  Returns SSD_OK or
- * SSD_ERR_HIP / SSD_ERR_INVALID_ARG.
+ * state --, chunk state, state passing, chunk scan).  On the fused path prep
+ * is the set-up kernel, the scan kernel is reported as chunk scan and the two
+ * middle stages are empty.  Returns SSD_OK or SSD_ERR_HIP /
+ * SSD_ERR_INVALID_ARG.
  */
 #define SSD_NUM_STAGES 4
 typedef struct ssd_timing ssd_timing;

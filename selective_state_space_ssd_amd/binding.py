@@ -20,6 +20,8 @@ SSD_F32 = 0
 SSD_BF16 = 1
 SSD_NUM_STAGES = 4
 STAGES = ("prep", "chunk_state", "state_passing", "chunk_scan")
+SSD_OPT_BF16_PATH = 1
+BF16_PATHS = {"auto": 0, "staged": 1, "fused": 2}
 
 _lib = None
 
@@ -58,6 +60,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
     lib.ssd_abi_version.restype = i
+    lib.ssd_set_option.argtypes = [i, i]
+    lib.ssd_set_option.restype = i
+    lib.ssd_get_option.argtypes = [i]
+    lib.ssd_get_option.restype = i
     lib.ssd_timing_create.argtypes = [ctypes.POINTER(p)]
     lib.ssd_timing_create.restype = i
     lib.ssd_timing_destroy.argtypes = [p]
@@ -74,6 +80,19 @@ def status_string(status: int) -> str:
 
 def abi_version() -> int:
     return int(load_library().ssd_abi_version())
+
+
+def set_bf16_path(name: str) -> str:
+    """Select the kernel path of bf16 problems ("auto", "staged" or "fused",
+    process-wide); returns the previous setting."""
+    lib = load_library()
+    prev = {v: k for k, v in BF16_PATHS.items()}[lib.ssd_get_option(SSD_OPT_BF16_PATH)]
+    _check(lib.ssd_set_option(SSD_OPT_BF16_PATH, BF16_PATHS[name]))
+    return prev
+
+
+def get_bf16_path() -> str:
+    return {v: k for k, v in BF16_PATHS.items()}[load_library().ssd_get_option(SSD_OPT_BF16_PATH)]
 
 
 def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype) -> int:

@@ -36,13 +36,27 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 struct Layout {
   int64_t nc = 0;
-  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0, total = 0;
+  bool fused = false;
+  // staged path
+  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0;
+  // fused bf16 path
+  size_t off_ring = 0, off_flags = 0, off_ctl = 0;
+  size_t total = 0;
 };
 
-// The bf16 matrix-core path (same rule as ssd::use_bf16_kernels).
+// Process-wide options (ssd_set_option).
+int g_bf16_path = SSD_BF16_PATH_AUTO;
+
+// The staged bf16 matrix-core kernels (same rule as ssd::use_bf16_kernels).
 bool bf16_path(int dtype, int64_t dstate, int chunk_size) {
   return dtype == SSD_BF16 && (chunk_size == 128 || chunk_size == 256) &&
          (dstate == 64 || dstate == 128);
+}
+
+// The fused bf16 kernel (same rule as ssd::use_fused_bf16, plus the option).
+bool fused_path(int dtype, int64_t headdim, int64_t dstate) {
+  return dtype == SSD_BF16 && headdim == 64 && (dstate == 64 || dstate == 128) &&
+         g_bf16_path != SSD_BF16_PATH_STAGED;
 }
 
 // Shape checks shared by the workspace query and the entry point.
@@ -69,6 +83,20 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
   if (!mul_ok(units, chunk_size, &dtn) || !mul_ok(units, pn, &stn)) return SSD_ERR_INVALID_ARG;
   if (stn > INT64_MAX / 8) return SSD_ERR_INVALID_ARG;
   lay->nc = nc;
+  if (fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
+    const int64_t nblk = ssd::fused_blocks(seqlen);
+    int64_t nchain, grid, ringn, flagn;
+    if (!mul_ok(batch, nheads, &nchain) || !mul_ok(nchain, nblk, &grid) ||
+        !mul_ok(nchain, 2 * pn, &ringn) || !mul_ok(nchain, nblk, &flagn))
+      return SSD_ERR_INVALID_ARG;
+    if (grid > INT32_MAX || ringn > INT64_MAX / 8) return SSD_ERR_UNSUPPORTED;
+    lay->fused = true;
+    lay->off_ring = 0;
+    lay->off_flags = round_up((size_t)ringn * 4);
+    lay->off_ctl = lay->off_flags + round_up((size_t)flagn * 4);
+    lay->total = lay->off_ctl + kAlign;
+    return SSD_OK;
+  }
   lay->off_dt = 0;
   lay->off_cum = round_up((size_t)dtn * 4);
   lay->off_states = lay->off_cum + round_up((size_t)dtn * 4);
@@ -156,16 +184,28 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.b = batch; p.L = seqlen; p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups;
   p.Q = chunk_size; p.nc = lay.nc; p.bf16 = dtype == SSD_BF16;
   char* ws = static_cast<char*>(workspace);
-  p.ws_dt = lay.total ? reinterpret_cast<float*>(ws + lay.off_dt) : nullptr;
-  p.ws_cum = lay.total ? reinterpret_cast<float*>(ws + lay.off_cum) : nullptr;
-  p.ws_states = lay.total ? reinterpret_cast<float*>(ws + lay.off_states) : nullptr;
-  p.ws_states_in = lay.total ? reinterpret_cast<float*>(ws + lay.off_states_in) : nullptr;
-  p.ws_bt = lay.total ? reinterpret_cast<uint16_t*>(ws + lay.off_bt) : nullptr;
+  const bool staged_ws = lay.total && !lay.fused;
+  p.ws_dt = staged_ws ? reinterpret_cast<float*>(ws + lay.off_dt) : nullptr;
+  p.ws_cum = staged_ws ? reinterpret_cast<float*>(ws + lay.off_cum) : nullptr;
+  p.ws_states = staged_ws ? reinterpret_cast<float*>(ws + lay.off_states) : nullptr;
+  p.ws_states_in = staged_ws ? reinterpret_cast<float*>(ws + lay.off_states_in) : nullptr;
+  p.ws_bt = staged_ws ? reinterpret_cast<uint16_t*>(ws + lay.off_bt) : nullptr;
+  p.fs_ring = lay.fused ? reinterpret_cast<float*>(ws + lay.off_ring) : nullptr;
+  p.fs_flags = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_flags) : nullptr;
+  p.fs_ctl = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_ctl) : nullptr;
 
   auto mark = [&](int i) -> bool {
     return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
   };
   if (!mark(0)) return SSD_ERR_HIP;
+  if (lay.fused) {
+    // set-up (tickets, flags, ring slot 0), then the one scan kernel
+    if (ssd::launch_fused_bf16(p, stream, 0) != hipSuccess) return SSD_ERR_HIP;
+    if (!mark(1) || !mark(2) || !mark(3)) return SSD_ERR_HIP;
+    if (ssd::launch_fused_bf16(p, stream, 1) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
+    if (timing) timing->recorded = true;
+    return SSD_OK;
+  }
   const bool bf16k = ssd::use_bf16_kernels(p);
   if (seqlen > 0 && bf16k) {
     // prep (B^T), then the chunk state with dt/cumsum fused in
@@ -242,6 +282,20 @@ const char* ssd_status_string(int status) {
 }
 
 int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+int ssd_set_option(int option, int value) {
+  if (option != SSD_OPT_BF16_PATH) return SSD_ERR_INVALID_ARG;
+  if (value != SSD_BF16_PATH_AUTO && value != SSD_BF16_PATH_STAGED &&
+      value != SSD_BF16_PATH_FUSED)
+    return SSD_ERR_INVALID_ARG;
+  g_bf16_path = value;
+  return SSD_OK;
+}
+
+int ssd_get_option(int option) {
+  if (option != SSD_OPT_BF16_PATH) return SSD_ERR_INVALID_ARG;
+  return g_bf16_path;
+}
 
 int ssd_timing_create(ssd_timing** out) {
   if (!out) return SSD_ERR_INVALID_ARG;

@@ -26,7 +26,7 @@ __device__ __forceinline__ float softplus(float u) {
 // Steps past the sequence end get dt = 0 and dA = 0, so the chunk's last cum
 // is the cum of its last real step.  Writes dt and cum to the workspace and
 // returns them in dt_out / cum_out (the lane's E values) and the chunk's last
-// cum in *cum_last.
+// cum in *cum_last.  ws_dt / ws_cum may be null (nothing stored).
 template <typename T, int Q>
 __device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, float a, float bias,
                                                float dt_min, float dt_max, int64_t b, int64_t c,
@@ -64,8 +64,10 @@ __device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, flo
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     cum_out[i] = base + run[i];
-    ws_dt[o + i] = dt_out[i];
-    ws_cum[o + i] = cum_out[i];
+    if (ws_dt) {
+      ws_dt[o + i] = dt_out[i];
+      ws_cum[o + i] = cum_out[i];
+    }
   }
 }
 

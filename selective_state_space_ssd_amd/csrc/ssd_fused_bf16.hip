@@ -1,0 +1,422 @@
+// Fused bf16 scan: all stages of the chunked scan in one kernel, with the
+// state handed from chunk to chunk through a two-slot ring in memory.
+//
+// One workgroup handles one block of 128 timesteps of one (batch, head)
+// "chain".  Everything that does not depend on the state entering the block
+// runs first: dt and its running sum (stage 1), the block's own state
+// contribution S = B^T diag(w) x with w_t = exp(cum_last - cum_t) dt_t
+// (stage 2), and the in-block output (C B^T o L) x with the D skip on the
+// diagonal (the diagonal part of stage 4).  Then the workgroup waits for the
+// entering state H_in of its chain, copies it to LDS, publishes the leaving
+// state exp(cum_last) H_in + S for the next block (stage 3, one link of the
+// inter-chunk recurrence), and finishes the output with C H_in^T scaled by
+// exp(cum_t) and the z gate (stage 5).  The states never make a round trip
+// through HBM: each chain's ring is 64 KB and stays in the caches.
+//
+// The block length is 128 whatever chunk size the caller names: the chunked
+// form gives the same result for any block length up to rounding, and 128
+// keeps the LDS footprint at two workgroups per CU and the causal C B^T
+// work per token at half that of 256.
+//
+// Ordering: a workgroup takes a ticket from a per-class counter when it
+// starts and handles the block that ticket names, block-major, so the block
+// it waits for always belongs to a workgroup that started earlier (resident
+// or finished).  No workgroup can wait on one that has not started, whatever
+// order the hardware dispatches in.  Classes (blockIdx % 8) partition the
+// chains group by group, so the heads that share B and C run on the same XCD
+// when workgroups are dealt round-robin to the XCDs.  The wait is bounded:
+// past the limit the workgroup records an error word and carries on.
+//
+// Operand precision as in the staged bf16 kernels: x, B, C enter the matrix
+// cores as they are; the decay-weighted B^T, the entering state and the
+// decay-masked C B^T values are split into hi/lo bf16 pairs.
+#include "ssd_bf16_tiles.h"
+#include "ssd_dt.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+using namespace bf16t;
+
+namespace {
+constexpr int FQ = 128;           // timesteps per block
+constexpr int FNT = FQ / 32;      // t-tiles per block
+constexpr int kClasses = 8;
+template <int N>
+constexpr int b_ld() { return N + 32; }  // B tile row stride: rows 1..3 apart on disjoint banks
+
+// Four fp32 stored with device (agent) scope: written through to the memory
+// side rather than held in this XCD's L2.
+__device__ __forceinline__ void st4_agent(float* p, f4 v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) __hip_atomic_store(p + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt vmcnt(0): this wave's vector memory operations, stores included,
+// have completed (gfx9 encoding: vmcnt 0, expcnt and lgkmcnt at their maxima).
+__device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int N>
+struct FusedLds {
+  static constexpr int kX = FQ * kXLD;                           // bf16
+  static constexpr int kB = FQ * b_ld<N>();                      // bf16
+  static constexpr int kH = kP * N * 2;                          // fp32 state as bf16 units
+  static constexpr int kBH = kB > kH ? kB : kH;
+};
+}  // namespace
+
+// Zeroes the tickets and flags of one call, writes each chain's entering
+// state (initial_states or zero) into ring slot 0 in the tiled layout and
+// marks block 0 of every chain ready.
+template <int N>
+__global__ __launch_bounds__(256) void fused_prep_kernel(const float* __restrict__ init,
+                                                         float* __restrict__ ring,
+                                                         unsigned* __restrict__ flags,
+                                                         unsigned* __restrict__ ctl, int64_t nchain,
+                                                         int64_t nblk) {
+  const int64_t chain = blockIdx.x;
+  const int tid = threadIdx.x;
+  float* slot = ring + chain * 2 * (kP * N);
+  for (int e = tid; e < kP * N / 4; e += 256) {
+    // tiled float4 index e -> (p, n0): e = (q*2 + p%2)*64 + 32*k + p/2
+    const int lane = e % 64, pj = (e / 64) % 2, q = e / 128;
+    const int p = 2 * (lane % 32) + pj, n0 = (N / 2) * (lane / 32) + 4 * q;
+    f4 v = init ? ld4(init + (chain * kP + p) * N + n0) : f4{0.f, 0.f, 0.f, 0.f};
+    st4(slot + 4 * e, v);
+  }
+  for (int64_t c = tid; c < nblk; c += 256) flags[chain * nblk + c] = c == 0 ? 1u : 0u;
+  if (chain == 0 && tid < kClasses + 1) ctl[tid] = 0u;  // tickets, then the error word
+}
+
+template <int N, bool GATE>
+__global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
+    const bf16_t* __restrict__ dt_raw, const float* __restrict__ A,
+    const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Dv,
+    const bf16_t* __restrict__ z, bf16_t* __restrict__ out, float* __restrict__ final_states,
+    float* __restrict__ ring, unsigned* __restrict__ flags, unsigned* __restrict__ ctl, int64_t L,
+    int64_t H, int64_t G, int64_t nblk, int64_t nchain, int nclass, unsigned spin_limit) {
+  static_assert(N == 64 || N == 128, "dstate 64 or 128");
+  constexpr int KS = N / 16;                // k-steps over n
+  constexpr int NPT = N == 128 ? 2 : 1;     // p-halves of the block state per wave
+  constexpr int BLD = b_ld<N>();
+  using Lds = FusedLds<N>;
+  __shared__ __align__(16) bf16_t x_lds[Lds::kX];
+  __shared__ __align__(16) bf16_t bh_lds[Lds::kBH];  // B tile, then the entering state (hi/lo)
+  __shared__ __align__(16) float cum2_lds[FQ];        // running sum of dt*A, log2 units
+  __shared__ __align__(16) float dt_lds[FQ];
+  __shared__ __align__(16) float w_lds[FQ];           // exp(cum_last - cum_t) dt_t
+  __shared__ __align__(16) float u_lds[FQ];           // exp(cum_end(tile of s) - cum_s) dt_s
+  __shared__ float dlast_lds;
+  __shared__ unsigned ticket_lds;
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int i = lane % 32, kk = lane / 32;
+
+  // ---- which block: ticket order within this workgroup's class ----
+  const int cls = (int)(blockIdx.x % (unsigned)nclass);
+  if (tid == 0) ticket_lds = atomicAdd(&ctl[cls], 1u);
+  __syncthreads();
+  const int64_t tk = ticket_lds;
+  const int64_t cpc = nchain / nclass;  // chains per class
+  const int64_t c = tk / cpc, jj = tk % cpc;
+  const int64_t hpg = H / G;
+  const int64_t gg = (jj / hpg) * nclass + cls;  // b*G + g
+  const int64_t b = gg / G, g = gg % G, h = g * hpg + jj % hpg;
+  const int64_t chain = b * H + h;
+  const int64_t t0 = c * FQ;
+  const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
+  const int64_t xs = H * kP, bs = G * N;
+
+  // ---- phase A: everything that does not need the entering state ----
+  XTile<FQ> xt;
+  RowTile<FQ, N> bt;
+  load_x_tile<FQ>(xt, x + ((b * L + t0) * H + h) * kP, xs, last);
+  load_rows<FQ, N>(bt, Bm + ((b * L + t0) * G + g) * N, bs, last);
+  if (wave == 0) {
+    constexpr int E = FQ / kWave;
+    static_assert(E == 2, "two timesteps per lane");
+    float dtv[E], cum[E], cum_last;
+    wave_dt_cumsum<bf16_t, FQ>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c, h,
+                               L, H, nblk, nullptr, nullptr, dtv, cum, &cum_last);
+    // lane l holds t = 2l, 2l + 1; the last step of its 32-step tile is lane 16 (l/16) + 15
+    const float cend = __shfl(cum[1], 16 * (lane / 16) + 15, kWave);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const int t = lane * E + k;
+      cum2_lds[t] = cum[k] * kLog2e;
+      dt_lds[t] = dtv[k];
+      w_lds[t] = __expf(cum_last - cum[k]) * dtv[k];
+      u_lds[t] = __expf(cend - cum[k]) * dtv[k];
+    }
+    if (lane == 0) dlast_lds = __expf(cum_last);
+  }
+  store_x_tile<FQ>(x_lds, xt, last);
+  store_rows<FQ, N>(bh_lds, BLD, bt, last);
+  __syncthreads();
+
+  // block state contribution S^T[n][p] = sum_t B[t][n] w_t x[t][p]; wave w
+  // owns n-tile w (N = 128, both p-halves) or n-tile w/2, p-half w%2 (N = 64)
+  const int snt = N == 128 ? wave : wave / 2;
+  const int spt0 = N == 128 ? 0 : wave % 2;
+  f16x sacc[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) sacc[j] = zero16();
+#pragma unroll 2
+  for (int ks = 0; ks < FQ / 16; ++ks) {
+    const int r0 = 16 * ks + 8 * kk;
+    const s16x8 braw = lds_tr_operand(bh_lds, BLD, r0, r0 + 4, 32 * snt);
+    const f4 w0 = *reinterpret_cast<const f4*>(w_lds + r0);
+    const f4 w1 = *reinterpret_cast<const f4*>(w_lds + r0 + 4);
+    const uint4 bw = __builtin_bit_cast(uint4, braw);
+    const float av[8] = {bf16_lo(bw.x) * w0[0], bf16_hi(bw.x) * w0[1], bf16_lo(bw.y) * w0[2],
+                         bf16_hi(bw.y) * w0[3], bf16_lo(bw.z) * w1[0], bf16_hi(bw.z) * w1[1],
+                         bf16_lo(bw.w) * w1[2], bf16_hi(bw.w) * w1[3]};
+    s16x8 ahi, alo;
+    split_bf16x8(av, ahi, alo);
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const s16x8 bop = lds_tr_operand(x_lds, kXLD, r0, r0 + 4, 32 * (spt0 + j));
+      sacc[j] = mfma32x32x16(ahi, bop, sacc[j]);
+      sacc[j] = mfma32x32x16(alo, bop, sacc[j]);
+    }
+  }
+
+  // in-block output: wave w owns p-half pt = w%2 of t-tiles {3 - w/2, w/2};
+  // each (t-tile, s-tile <= t-tile) product G^T = B_s C_t^T is formed by the
+  // two waves of that t-tile (one per p-half).  Contraction index n of lane
+  // (i, kk) at step ks: (N/2) kk + 8 ks + 0..7, the same in C.H_in^T below.
+  // Decay of an s-tile below the diagonal, split at the tile's last step e:
+  // exp(cum_t - cum_s) dt_s = exp(cum_t - cum_e) * u_s, both factors <= 1.
+  const int ypt = wave % 2, ya = wave / 2;
+  const int ti0 = FNT - 1 - ya, ti1 = ya;
+  const bf16_t* Cb = Cm + ((b * L + t0) * G + g) * N + (N / 2) * kk;
+  const float Dh = Dv ? Dv[h] : 0.0f;
+  f16x yacc[2];
+  s16x8 creg[KS];  // after the loop: the C rows of t-tile ti1
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ti = jt == 0 ? ti0 : ti1;
+    {
+      const int tr = 32 * ti + i;
+      const int r = tr < last ? tr : last;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        creg[ks] = ld_bf16x8(Cb + r * bs + 8 * ks);
+        if (tr > last) creg[ks] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    const float ct = cum2_lds[32 * ti + i];
+    f16x acc = zero16();
+    for (int si = 0; si <= ti; ++si) {
+      f16x gt = zero16();
+      const bf16_t* brow = bh_lds + (32 * si + i) * BLD + (N / 2) * kk;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        gt = mfma32x32x16(ld_bf16x8(brow + 8 * ks), creg[ks], gt);  // G^T[s][t]
+      // register r: s = 32 si + 8 (r/4) + 4 kk + r%4, t = 32 ti + i
+      float mv[16];
+      if (si < ti) {
+        const float rs = exp2f(ct - cum2_lds[32 * si + 31]);
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          const f4 u = *reinterpret_cast<const f4*>(u_lds + 32 * si + 8 * R + 4 * kk);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) mv[4 * R + q] = gt[4 * R + q] * rs * u[q];
+        }
+      } else {
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          const f4 cs = *reinterpret_cast<const f4*>(cum2_lds + 32 * si + 8 * R + 4 * kk);
+          const f4 ds = *reinterpret_cast<const f4*>(dt_lds + 32 * si + 8 * R + 4 * kk);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int sl = 8 * R + 4 * kk + q;
+            const float v = gt[4 * R + q] * exp2f(ct - cs[q]) * ds[q];
+            mv[4 * R + q] = sl < i ? v : (sl == i ? v + Dh : 0.0f);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float mm[8] = {mv[8 * m], mv[8 * m + 1], mv[8 * m + 2], mv[8 * m + 3],
+                             mv[8 * m + 4], mv[8 * m + 5], mv[8 * m + 6], mv[8 * m + 7]};
+        s16x8 mhi, mlo;
+        split_bf16x8(mm, mhi, mlo);
+        const int r0 = 32 * si + 16 * m + 4 * kk;
+        const s16x8 bop = lds_tr_operand(x_lds, kXLD, r0, r0 + 8, 32 * ypt);
+        acc = mfma32x32x16(mhi, bop, acc);
+        acc = mfma32x32x16(mlo, bop, acc);
+      }
+    }
+    yacc[jt] = acc;
+  }
+
+  // ---- phase B: the entering state ----
+  __syncthreads();  // B tile no longer read; its space takes the state
+  if (tid == 0) {
+    const unsigned* f = flags + chain * nblk + c;
+    unsigned spins = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > spin_limit) {
+        atomicOr(&ctl[kClasses], 1u);
+        break;
+      }
+    }
+    // the other waves of this workgroup run on the same CU: one acquire (L1
+    // and L2 invalidation) before the barrier covers their loads as well
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+
+  // Each thread loads the entering state at the elements of its own S tiles,
+  // publishes exp(cum_last) H_in + S there, and leaves H_in split into hi/lo
+  // bf16 in LDS in the operand order of C.H_in^T:
+  //   hsplit[half][(ks*2 + pt)*64 + lane] = 8 bf16 of H[2 (lane%32) + pt][(N/2)(lane/32) + 8 ks + 0..7]
+  const float* hin = ring + (chain * 2 + (c & 1)) * (kP * N);
+  f4 hreg[NPT][4];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j)
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+      hreg[j][R] = ld4(hin + state_tile_offset(2 * i + spt0 + j, 32 * snt + 8 * R + 4 * kk, N));
+  // C rows of t-tile ti0 (those of ti1 are still in creg) and z of both,
+  // rows clamped to the sequence
+  s16x8 creg0[KS];
+  {
+    const int tr = 32 * ti0 + i;
+    const int r = tr < last ? tr : last;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) creg0[ks] = ld_bf16x8(Cb + r * bs + 8 * ks);
+  }
+  const bf16_t* zh = z + ((b * L + t0) * H + h) * kP + 2 * i + ypt;
+  bf16_t zreg[2][16];
+  if constexpr (GATE) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int ti = jt == 0 ? ti0 : ti1;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
+        zreg[jt][rr] = zh[(tl < last ? tl : last) * xs];
+      }
+    }
+  }
+  {
+    const float dl = dlast_lds;
+    const bool more = c + 1 < nblk;
+    float* hout = ring + (chain * 2 + ((c + 1) & 1)) * (kP * N);
+    uint2* hs_hi = reinterpret_cast<uint2*>(bh_lds);
+    uint2* hs_lo = hs_hi + KS * 2 * 64 * 2;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int p = 2 * i + spt0 + j;
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const int n0 = 32 * snt + 8 * R + 4 * kk;
+        const f4 hv = hreg[j][R];
+        f4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = dl * hv[e] + sacc[j][4 * R + e];
+        if (more)
+          st4_agent(hout + state_tile_offset(p, n0, N), v);
+        else if (final_states)
+          st4(final_states + (chain * kP + p) * N + n0, v);
+        // operand slot of (p, n0..n0+3): ks = (n0 % (N/2)) / 8, reader lane
+        // 32 (n0 / (N/2)) + i, half 4-element piece kk of the 8
+        const int rks = (n0 % (N / 2)) / 8, rlane = 32 * (n0 / (N / 2)) + i;
+        const int slot = ((rks * 2 + (spt0 + j)) * 64 + rlane) * 2 + kk;
+        const uint32_t h01 = pack_bf16x2(hv[0], hv[1]), h23 = pack_bf16x2(hv[2], hv[3]);
+        hs_hi[slot] = uint2{h01, h23};
+        hs_lo[slot] = uint2{pack_bf16x2(hv[0] - bf16_lo(h01), hv[1] - bf16_hi(h01)),
+                            pack_bf16x2(hv[2] - bf16_lo(h23), hv[3] - bf16_hi(h23))};
+      }
+    }
+    // the state went out with device-scope stores (written through to the
+    // memory side); waiting for them to complete makes them visible to any
+    // XCD that invalidates its caches, as the consumer does after the flag
+    if (more) wait_vmem_stores();
+    __syncthreads();  // state published by every wave; H_in split complete in LDS
+    if (more && tid == 0)
+      __hip_atomic_store(flags + chain * nblk + c + 1, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // C H_in^T, decayed from the block start, plus the in-block part; epilogue
+  const uint4* hs_hi4 = reinterpret_cast<const uint4*>(bh_lds);
+  const uint4* hs_lo4 = hs_hi4 + KS * 2 * 64;
+  bf16_t* oh = out + ((b * L + t0) * H + h) * kP + 2 * i + ypt;
+#pragma unroll
+  for (int jt = 1; jt >= 0; --jt) {  // ti1 first: its C rows are loaded already
+    const int ti = jt == 0 ? ti0 : ti1;
+    const int tr = 32 * ti + i;
+    f16x acc = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const s16x8 cv = tr > last ? s16x8{0, 0, 0, 0, 0, 0, 0, 0} : (jt == 0 ? creg0[ks] : creg[ks]);
+      const s16x8 hhi = __builtin_bit_cast(s16x8, hs_hi4[(ks * 2 + ypt) * 64 + lane]);
+      const s16x8 hlo = __builtin_bit_cast(s16x8, hs_lo4[(ks * 2 + ypt) * 64 + lane]);
+      acc = mfma32x32x16(cv, hhi, acc);
+      acc = mfma32x32x16(cv, hlo, acc);
+    }
+    float y[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
+      y[rr] = yacc[jt][rr] + acc[rr] * exp2f(cum2_lds[tl]);
+      if constexpr (GATE) y[rr] *= silu(to_f32(zreg[jt][rr]));
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
+      if (tl <= last) oh[tl * xs] = (bf16_t)f32_to_bf16_bits(y[rr]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+bool use_fused_bf16(const Problem& p) {
+  return p.bf16 && p.P == kP && (p.N == 64 || p.N == 128);
+}
+
+int64_t fused_blocks(int64_t L) { return (L + FQ - 1) / FQ; }
+
+int fused_classes(int64_t b, int64_t G) { return (b * G) % kClasses == 0 ? kClasses : 1; }
+
+template <int N>
+static void launch_fused_n(const Problem& p, hipStream_t s, int stage) {
+  const int64_t nblk = fused_blocks(p.L), nchain = p.b * p.H;
+  if (stage == 0) {
+    hipLaunchKernelGGL((fused_prep_kernel<N>), dim3((unsigned)nchain), dim3(256), 0, s, p.init,
+                       p.fs_ring, p.fs_flags, p.fs_ctl, nchain, nblk);
+    return;
+  }
+  const int nclass = fused_classes(p.b, p.G);
+  const unsigned spin_limit = 1u << 22;
+  const dim3 grid((unsigned)(nchain * nblk));
+  const auto* xb = static_cast<const bf16_t*>(p.x);
+  const auto* Bb = static_cast<const bf16_t*>(p.B);
+  const auto* Cb = static_cast<const bf16_t*>(p.C);
+  const auto* db = static_cast<const bf16_t*>(p.dt);
+  const auto* zb = static_cast<const bf16_t*>(p.z);
+  auto* ob = static_cast<bf16_t*>(p.out);
+  if (p.z)
+    hipLaunchKernelGGL((fused_scan_bf16_kernel<N, true>), grid, dim3(256), 0, s, xb, Bb, Cb, db,
+                       p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.final_states, p.fs_ring,
+                       p.fs_flags, p.fs_ctl, p.L, p.H, p.G, nblk, nchain, nclass, spin_limit);
+  else
+    hipLaunchKernelGGL((fused_scan_bf16_kernel<N, false>), grid, dim3(256), 0, s, xb, Bb, Cb, db,
+                       p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.final_states, p.fs_ring,
+                       p.fs_flags, p.fs_ctl, p.L, p.H, p.G, nblk, nchain, nclass, spin_limit);
+}
+
+hipError_t launch_fused_bf16(const Problem& p, hipStream_t s, int stage) {
+  if (p.N == 128)
+    launch_fused_n<128>(p, s, stage);
+  else
+    launch_fused_n<64>(p, s, stage);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

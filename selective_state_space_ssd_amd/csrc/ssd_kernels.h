@@ -30,6 +30,10 @@ struct Problem {
   float* ws_states;      // [b, nc, H] tiled P x N blocks: chunk-local states
   float* ws_states_in;   // [b, nc, H] tiled P x N blocks: state entering each chunk
   uint16_t* ws_bt;       // [b, nc, G] blocks of N x Q bf16: B^T per chunk (bf16 kernels only)
+  // fused bf16 kernel
+  float* fs_ring;        // [b*H chains][2 slots] tiled P x N states
+  unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
+  unsigned* fs_ctl;      // 8 ticket counters, then the error word
 };
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().
@@ -47,6 +51,12 @@ bool chunk_state_fuses_dt(const Problem& p);
 // scan.  The state passing between them is the common stage-3 kernel.
 bool use_bf16_kernels(const Problem& p);
 hipError_t launch_bf16_stage(const Problem& p, hipStream_t stream, int stage);
+
+// Fused bf16 kernel (bf16 inputs, P 64, N 64/128): stage 0 is the set-up
+// kernel, stage 1 the scan.  Blocks of 128 timesteps whatever Q is.
+bool use_fused_bf16(const Problem& p);
+int64_t fused_blocks(int64_t L);
+hipError_t launch_fused_bf16(const Problem& p, hipStream_t stream, int stage);
 
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);

@@ -1,5 +1,7 @@
 """Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
 through the C ABI, compare with the oracle element by element."""
+from contextlib import contextmanager
+
 import numpy as np
 import torch
 
@@ -9,6 +11,22 @@ import selective_state_space_ssd_amd as ssd
 # inputs (fp32 state and accumulation, bf16 output): 2e-2.  The (1 + |ref|)
 # form keeps near-zero outputs from inflating relative errors.
 TOL = {"f32": 1e-3, "bf16": 2e-2}
+
+
+@contextmanager
+def bf16_path(name):
+    """Run the enclosed calls with the bf16 kernel path `name` ("fused",
+    "staged" or "auto")."""
+    prev = ssd.set_bf16_path(name)
+    try:
+        yield
+    finally:
+        ssd.set_bf16_path(prev)
+
+
+def paths_for(dtype):
+    """The kernel paths a problem of this dtype can take."""
+    return ("fused", "staged") if dtype == "bf16" else ("auto",)
 
 
 def log(msg):

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("ssd_scan_fwd", "ssd_scan_fwd_workspace_size", "ssd_status_string",
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
-                 "ssd_timing_read", "ssd_timing_destroy"):
+                 "ssd_timing_read", "ssd_timing_destroy", "ssd_set_option", "ssd_get_option"):
         assert want in names
 
 
@@ -58,18 +58,53 @@ def _ws(b, L, H, P, N, G, Q, dt=0):
     return ssd.workspace_size(b, L, H, P, N, G, Q, dt)
 
 
+def _r(v):
+    return (v + 255) // 256 * 256
+
+
+SIZES = [(2, 2048, 32, 64, 128, 1, 128), (1, 300, 4, 64, 16, 1, 64),
+         (8, 4096, 64, 64, 128, 8, 256), (3, 1, 2, 64, 32, 2, 128), (1, 200, 4, 64, 64, 2, 64)]
+
+
 def test_workspace_size_formula():
-    def r(v):
-        return (v + 255) // 256 * 256
-    for (b, L, H, P, N, G, Q) in [(2, 2048, 32, 64, 128, 1, 128), (1, 300, 4, 64, 16, 1, 64),
-                                  (8, 4096, 64, 64, 128, 8, 256), (3, 1, 2, 64, 32, 2, 128)]:
+    prev = ssd.set_bf16_path("staged")
+    try:
+        for (b, L, H, P, N, G, Q) in SIZES:
+            nc = math.ceil(L / Q)
+            want = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+            assert _ws(b, L, H, P, N, G, Q) == want
+            # intermediates are fp32 for bf16 too; the staged bf16 matrix-core
+            # kernels (chunk 128/256, dstate 64/128) add B^T per (chunk, group)
+            bt = _r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
+            assert _ws(b, L, H, P, N, G, Q, 1) == want + bt
+    finally:
+        ssd.set_bf16_path(prev)
+
+
+def test_workspace_size_fused_bf16():
+    """Fused bf16 path (dstate 64/128): ring of two states per (batch, head),
+    one flag per 128-step block, one 256-byte control region."""
+    assert ssd.get_bf16_path() == "auto"
+    for (b, L, H, P, N, G, Q) in SIZES:
         nc = math.ceil(L / Q)
-        want = 2 * r(b * H * nc * Q * 4) + 2 * r(b * nc * H * P * N * 4)
-        assert _ws(b, L, H, P, N, G, Q) == want
-        # intermediates are fp32 for bf16 too; the bf16 matrix-core kernels
-        # (chunk 128/256, dstate 64/128) add B^T per (chunk, group) in bf16
-        bt = r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
-        assert _ws(b, L, H, P, N, G, Q, 1) == want + bt
+        staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+        assert _ws(b, L, H, P, N, G, Q) == staged  # fp32 is always staged
+        if N in (64, 128):
+            want = _r(b * H * 2 * P * N * 4) + _r(b * H * math.ceil(L / 128) * 4) + 256
+        else:
+            want = staged  # dstate 16/32: staged
+        assert _ws(b, L, H, P, N, G, Q, 1) == want
+
+
+def test_options():
+    lib = ssd.load_library()
+    assert lib.ssd_get_option(1) == 0
+    assert lib.ssd_set_option(1, 7) == INVALID
+    assert lib.ssd_set_option(2, 0) == INVALID
+    assert lib.ssd_get_option(2) == INVALID
+    prev = ssd.set_bf16_path("fused")
+    assert prev == "auto" and ssd.get_bf16_path() == "fused"
+    assert ssd.set_bf16_path(prev) == "fused" and ssd.get_bf16_path() == "auto"
     assert _ws(0, 100, 4, 64, 16, 1, 64) == 0
     assert _ws(2, 0, 4, 64, 16, 1, 64) == 0
     assert _ws(2, 100, 4, 64, 16, 3, 64) == 0       # rejected: 3 does not divide 4

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, compare, log, np64, run_gpu, upload
+from parity import TOL, bf16_path, compare, log, np64, paths_for, run_gpu, upload
 from ssd_workloads import WORKLOADS, Workload, make_inputs, small
 
 pytestmark = pytest.mark.gpu
@@ -44,6 +44,9 @@ SMALL += [("f32", 128, 32, 4, 2), ("f32", 128, 64, 4, 2), ("bf16", 64, 32, 4, 2)
 SMALL += [(dt, Q, N, 8, G) for dt in ("f32", "bf16") for Q in (64, 128) for N in (64, 128)
           for G in (1, 2)]
 SMALL += [("f32", 128, 128, 6, 3), ("f32", 64, 64, 12, 3), ("bf16", 128, 128, 16, 1)]
+# batch * ngroups a multiple of 8: the fused bf16 kernel deals its chains to
+# eight ticket classes (one group per class here)
+SMALL += [("bf16", 256, 128, 8, 4), ("bf16", 128, 64, 8, 8)]
 
 
 @pytest.mark.parametrize("dtype,Q,N,H,G", SMALL,
@@ -51,13 +54,15 @@ SMALL += [("f32", 128, 128, 6, 3), ("f32", 64, 64, 12, 3), ("bf16", 128, 128, 16
 def test_small_ragged(dtype, Q, N, H, G):
     L = 2 * Q + Q // 2 + 7
     w = _case(1000 + Q + N + H, 2, L, H, 64, N, G, Q, dtype, init=True)
-    log(f"test_small_ragged {dtype} Q={Q} N={N} H={H} G={G} L={L}")
     inp = make_inputs(w)
     t = upload(inp, dtype)
-    out, fin = run_gpu(t, Q, init=t["initial_states"])
     ref, rfin = _oracle(inp, init=inp["initial_states"])
-    compare("out", np64(out), ref, TOL[dtype])
-    compare("final", np64(fin), rfin, TOL[dtype])
+    for path in paths_for(dtype):
+        log(f"test_small_ragged {dtype} Q={Q} N={N} H={H} G={G} L={L} path={path}")
+        with bf16_path(path):
+            out, fin = run_gpu(t, Q, init=t["initial_states"])
+        compare(f"out {path}", np64(out), ref, TOL[dtype])
+        compare(f"final {path}", np64(fin), rfin, TOL[dtype])
 
 
 def _state_tile_offsets(N):
@@ -102,9 +107,10 @@ def test_stage_intermediates(dtype, Q, N):
     log(f"test_stage_intermediates {dtype}")
     inp = make_inputs(w)
     t = upload(inp, dtype)
-    ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0),
-                     dtype=torch.uint8, device=t["x"].device)
-    run_gpu(t, Q, init=t["initial_states"], workspace=ws)
+    with bf16_path("staged"):  # the intermediates live in the staged path's workspace
+        ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0),
+                         dtype=torch.uint8, device=t["x"].device)
+        run_gpu(t, Q, init=t["initial_states"], workspace=ws)
     got = {k: np64(v) for k, v in _ws_regions(ws, b, L, H, P, N, Q).items()}
     ref = oracle.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
                                      dt_bias=inp["dt_bias"], initial_states=inp["initial_states"])
@@ -144,13 +150,15 @@ def test_edge_cases(dtype, Q, desc, changes):
     w = _case(300, 2, L, base["nheads"], 64, 128, base["ngroups"], Q, dtype,
               gate=base["gate"], skip=base["skip"], init=True)
     lim = (0.01, 0.05) if desc == "dt_limit" else (0.0, math.inf)
-    log(f"test_edge_cases {dtype} Q={Q} {desc}")
     inp = make_inputs(w)
     t = upload(inp, dtype)
-    out, fin = run_gpu(t, Q, dt_limit=lim, init=t["initial_states"])
     ref, rfin = _oracle(inp, dt_limit=lim, init=inp["initial_states"])
-    compare("out", np64(out), ref, TOL[dtype])
-    compare("final", np64(fin), rfin, TOL[dtype])
+    for path in paths_for(dtype):
+        log(f"test_edge_cases {dtype} Q={Q} {desc} path={path}")
+        with bf16_path(path):
+            out, fin = run_gpu(t, Q, dt_limit=lim, init=t["initial_states"])
+        compare(f"out {path}", np64(out), ref, TOL[dtype])
+        compare(f"final {path}", np64(fin), rfin, TOL[dtype])
 
 
 def test_no_bias_no_init():
@@ -209,13 +217,15 @@ def test_ngroups_invariance(dtype, Q):
               dtype=dtype, chunk_size=Q)
     inp = make_inputs(w)
     t = upload(inp, dtype)
-    ref_out, ref_fin = run_gpu(t, Q, init=t["initial_states"])
-    for G in (2, 4):
-        t2 = dict(t)
-        t2["B"] = t["B"].repeat_interleave(G, dim=2).contiguous()
-        t2["C"] = t["C"].repeat_interleave(G, dim=2).contiguous()
-        out, fin = run_gpu(t2, Q, init=t["initial_states"])
-        assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin), G
+    for path in paths_for(dtype):
+        with bf16_path(path):
+            ref_out, ref_fin = run_gpu(t, Q, init=t["initial_states"])
+            for G in (2, 4, 8):
+                t2 = dict(t)
+                t2["B"] = t["B"].repeat_interleave(G, dim=2).contiguous()
+                t2["C"] = t["C"].repeat_interleave(G, dim=2).contiguous()
+                out, fin = run_gpu(t2, Q, init=t["initial_states"])
+                assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin), (path, G)
 
 
 def test_chunk_size_invariance():
@@ -274,6 +284,28 @@ def _sample_mask(b, H, k, seed):
 FULL = list(WORKLOADS)
 
 
+def _run_workload(w, t, name):
+    if w.segments == 1:
+        log(f"test_workload {name}: GPU run")
+        return run_gpu(t, w.chunk_size)
+    seg = w.seqlen // w.segments
+    state = None
+    outs = []
+    for i in range(w.segments):
+        log(f"test_workload {name}: GPU segment {i}")
+        sl = {k: (v[:, i * seg:(i + 1) * seg].contiguous()
+                  if k in ("x", "z", "B", "C", "dt") and v is not None else v)
+              for k, v in t.items()}
+        o, state = run_gpu(sl, w.chunk_size, init=state)
+        outs.append(o)
+    out, fin = torch.cat(outs, dim=1), state
+    full_out, full_fin = run_gpu(t, w.chunk_size)
+    tol = TOL[w.dtype]
+    compare("segments vs one GPU scan", np64(out), np64(full_out), tol)
+    compare("segment final vs one GPU scan", np64(fin), np64(full_fin), tol)
+    return out, fin
+
+
 @pytest.mark.parametrize("name", FULL)
 def test_workload(name):
     w = WORKLOADS[name]
@@ -283,32 +315,20 @@ def test_workload(name):
     tol = TOL[w.dtype]
     big = w.batch * w.seqlen * w.nheads > 2 * 2048 * 32
     mask = _sample_mask(w.batch, w.nheads, 6, w.seed) if big else None
-    if w.segments == 1:
-        log(f"test_workload {name}: GPU run")
-        out, fin = run_gpu(t, w.chunk_size)
-    else:
-        seg = w.seqlen // w.segments
-        state = None
-        outs = []
-        for i in range(w.segments):
-            log(f"test_workload {name}: GPU segment {i}")
-            sl = {k: (v[:, i * seg:(i + 1) * seg].contiguous()
-                      if k in ("x", "z", "B", "C", "dt") and v is not None else v)
-                  for k, v in t.items()}
-            o, state = run_gpu(sl, w.chunk_size, init=state)
-            outs.append(o)
-        out, fin = torch.cat(outs, dim=1), state
-        full_out, full_fin = run_gpu(t, w.chunk_size)
-        compare("segments vs one GPU scan", np64(out), np64(full_out), tol)
-        compare("segment final vs one GPU scan", np64(fin), np64(full_fin), tol)
+    results = {}
+    for path in paths_for(w.dtype):
+        with bf16_path(path):
+            out, fin = _run_workload(w, t, f"{name} [{path}]")
+        results[path] = (np64(out), np64(fin))
+        del out, fin
     log(f"test_workload {name}: oracle")
     ref, rfin = _oracle(inp, head_mask=mask)
-    got, gfin = np64(out), np64(fin)
-    if mask is not None:
-        sel = np.broadcast_to(mask[:, None, :, None], ref.shape)
-        compare("out (sampled heads)", got, ref, tol, mask=sel)
-        compare("final (sampled heads)", gfin, rfin,
-                tol, mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))
-    else:
-        compare("out", got, ref, tol)
-        compare("final", gfin, rfin, tol)
+    for path, (got, gfin) in results.items():
+        if mask is not None:
+            sel = np.broadcast_to(mask[:, None, :, None], ref.shape)
+            compare(f"out (sampled heads) {path}", got, ref, tol, mask=sel)
+            compare(f"final (sampled heads) {path}", gfin, rfin,
+                    tol, mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))
+        else:
+            compare(f"out {path}", got, ref, tol)
+            compare(f"final {path}", gfin, rfin, tol)

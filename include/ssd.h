@@ -168,7 +168,10 @@ int ssd_abi_version(void);
 /*
  * Process-wide options.  SSD_OPT_BF16_PATH selects the kernel path of bf16
  * problems that the fused path covers: SSD_BF16_PATH_AUTO (default, fused),
- * SSD_BF16_PATH_STAGED or SSD_BF16_PATH_FUSED.  The workspace size depends on
+ * SSD_BF16_PATH_STAGED, SSD_BF16_PATH_FUSED (fused, kernel form chosen from
+ * the shape), SSD_BF16_PATH_FUSED_HEAD (one workgroup per 128-step block and
+ * head) or SSD_BF16_PATH_FUSED_GROUP (one workgroup per 128-step block, B/C
+ * group and set of up to 8 of its heads).  The workspace size depends on
  * the path, so set options before querying it; do not change them while
  * another thread is between the query and the call.  ssd_set_option returns
  * SSD_OK or SSD_ERR_INVALID_ARG; ssd_get_option the value or
@@ -178,6 +181,8 @@ int ssd_abi_version(void);
 #define SSD_BF16_PATH_AUTO 0
 #define SSD_BF16_PATH_STAGED 1
 #define SSD_BF16_PATH_FUSED 2
+#define SSD_BF16_PATH_FUSED_HEAD 3
+#define SSD_BF16_PATH_FUSED_GROUP 4
 int ssd_set_option(int option, int value);
 int ssd_get_option(int option);
 

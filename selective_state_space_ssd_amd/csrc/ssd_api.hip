@@ -193,6 +193,9 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.fs_ring = lay.fused ? reinterpret_cast<float*>(ws + lay.off_ring) : nullptr;
   p.fs_flags = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_flags) : nullptr;
   p.fs_ctl = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_ctl) : nullptr;
+  p.fused_kind = g_bf16_path == SSD_BF16_PATH_FUSED_HEAD    ? 1
+                 : g_bf16_path == SSD_BF16_PATH_FUSED_GROUP ? 2
+                                                            : 0;
 
   auto mark = [&](int i) -> bool {
     return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
@@ -285,9 +288,7 @@ int ssd_abi_version(void) { return SSD_ABI_VERSION; }
 
 int ssd_set_option(int option, int value) {
   if (option != SSD_OPT_BF16_PATH) return SSD_ERR_INVALID_ARG;
-  if (value != SSD_BF16_PATH_AUTO && value != SSD_BF16_PATH_STAGED &&
-      value != SSD_BF16_PATH_FUSED)
-    return SSD_ERR_INVALID_ARG;
+  if (value < SSD_BF16_PATH_AUTO || value > SSD_BF16_PATH_FUSED_GROUP) return SSD_ERR_INVALID_ARG;
   g_bf16_path = value;
   return SSD_OK;
 }

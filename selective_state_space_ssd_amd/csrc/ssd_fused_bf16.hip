@@ -41,14 +41,54 @@ namespace {
 constexpr int FQ = 128;           // timesteps per block
 constexpr int FNT = FQ / 32;      // t-tiles per block
 constexpr int kClasses = 8;
-template <int N>
-constexpr int b_ld() { return N + 32; }  // B tile row stride: rows 1..3 apart on disjoint banks
 
-// Four fp32 stored with device (agent) scope: written through to the memory
-// side rather than held in this XCD's L2.
-__device__ __forceinline__ void st4_agent(float* p, f4 v) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) __hip_atomic_store(p + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The B tile sits in LDS unpadded (N bf16 per row) with its 16-byte chunks
+// XOR-swizzled by row, so that both the row reads of C.B^T (lanes on
+// consecutive rows) and the transposed reads of the state product (lanes on
+// four rows, two chunks) land on distinct banks.
+template <int N>
+__device__ __forceinline__ int bswz(int r) {
+  if constexpr (N == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+template <int N>
+__device__ __forceinline__ int b_off(int r, int col) {  // element offset of (r, col)
+  return r * N + ((((col >> 3) ^ bswz<N>(r))) << 3) + (col & 7);
+}
+
+// Transposed read of the swizzled B tile (see lds_tr4): lane l receives
+// B[r0 + 0..3][c0 + l%32].
+template <int N>
+__device__ __forceinline__ s16x4 b_tr4(const bf16_t* lds, int r0, int c0) {
+  const int lane = threadIdx.x % 64;
+  const int m = lane % 16, half = (lane / 16) % 2;
+  const bf16_t* p = lds + b_off<N>(r0 + m / 4, c0 + 16 * half + 4 * (m % 4));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+template <int N>
+__device__ __forceinline__ s16x8 b_tr_operand(const bf16_t* lds, int r0, int r1, int c0) {
+  const s16x4 a = b_tr4<N>(lds, r0, c0), b = b_tr4<N>(lds, r1, c0);
+  s16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
+// 2^x with v_exp_f32 (results below the normal range flush to zero).
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// z * sigmoid(z) with v_exp_f32 and v_rcp_f32.
+__device__ __forceinline__ float fsilu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + fexp2(-z * 1.4426950408889634f));
+}
+
+// Four fp32 stored with device (agent) scope (cache policy sc1) in one
+// 16-byte buffer store: written through to the memory side rather than held
+// in this XCD's L2.  `slot` is wave-uniform; `byte_off` < slot_bytes.
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ void st4_agent(float* slot, int slot_bytes, int byte_off, f4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(slot, 0, slot_bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                         r, byte_off, 0, kCachePolicySc1);
 }
 
 // s_waitcnt vmcnt(0): this wave's vector memory operations, stores included,
@@ -57,10 +97,11 @@ __device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(
 
 template <int N>
 struct FusedLds {
-  static constexpr int kX = FQ * kXLD;                           // bf16
-  static constexpr int kB = FQ * b_ld<N>();                      // bf16
-  static constexpr int kH = kP * N * 2;                          // fp32 state as bf16 units
-  static constexpr int kBH = kB > kH ? kB : kH;
+  static constexpr int kX = FQ * kXLD;            // x tile (bf16)
+  static constexpr int kB = FQ * N;               // B tile (bf16)
+  static constexpr int kH = kP * N * 2;           // entering state, hi/lo bf16
+  static constexpr int kY = FQ * kP * 2;          // output tile, fp32
+  static constexpr int kBH = kB > kH ? (kB > kY ? kB : kY) : (kH > kY ? kH : kY);
 };
 }  // namespace
 
@@ -98,7 +139,6 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
   constexpr int KS = N / 16;                // k-steps over n
   constexpr int NPT = N == 128 ? 2 : 1;     // p-halves of the block state per wave
-  constexpr int BLD = b_ld<N>();
   using Lds = FusedLds<N>;
   __shared__ __align__(16) bf16_t x_lds[Lds::kX];
   __shared__ __align__(16) bf16_t bh_lds[Lds::kBH];  // B tile, then the entering state (hi/lo)
@@ -116,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
   const int cls = (int)(blockIdx.x % (unsigned)nclass);
   if (tid == 0) ticket_lds = atomicAdd(&ctl[cls], 1u);
   __syncthreads();
-  const int64_t tk = ticket_lds;
+  const int64_t tk = __builtin_amdgcn_readfirstlane(ticket_lds);  // uniform: scalar index math
   const int64_t cpc = nchain / nclass;  // chains per class
   const int64_t c = tk / cpc, jj = tk % cpc;
   const int64_t hpg = H / G;
@@ -151,7 +191,13 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
     if (lane == 0) dlast_lds = __expf(cum_last);
   }
   store_x_tile<FQ>(x_lds, xt, last);
-  store_rows<FQ, N>(bh_lds, BLD, bt, last);
+#pragma unroll
+  for (int k = 0; k < RowTile<FQ, N>::ITER; ++k) {  // B tile, swizzled chunks
+    const int e = k * 256 + tid;
+    const int row = e / (N / 8), chunk = e % (N / 8);
+    *reinterpret_cast<uint4*>(bh_lds + row * N + ((chunk ^ bswz<N>(row)) << 3)) =
+        row > last ? uint4{0u, 0u, 0u, 0u} : bt.v[k];
+  }
   __syncthreads();
 
   // block state contribution S^T[n][p] = sum_t B[t][n] w_t x[t][p]; wave w
@@ -164,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
 #pragma unroll 2
   for (int ks = 0; ks < FQ / 16; ++ks) {
     const int r0 = 16 * ks + 8 * kk;
-    const s16x8 braw = lds_tr_operand(bh_lds, BLD, r0, r0 + 4, 32 * snt);
+    const s16x8 braw = b_tr_operand<N>(bh_lds, r0, r0 + 4, 32 * snt);
     const f4 w0 = *reinterpret_cast<const f4*>(w_lds + r0);
     const f4 w1 = *reinterpret_cast<const f4*>(w_lds + r0 + 4);
     const uint4 bw = __builtin_bit_cast(uint4, braw);
@@ -209,14 +255,16 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
     f16x acc = zero16();
     for (int si = 0; si <= ti; ++si) {
       f16x gt = zero16();
-      const bf16_t* brow = bh_lds + (32 * si + i) * BLD + (N / 2) * kk;
+      const int brw = 32 * si + i;
+      const bf16_t* brow = bh_lds + brw * N;
+      const int bsw = bswz<N>(brw);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        gt = mfma32x32x16(ld_bf16x8(brow + 8 * ks), creg[ks], gt);  // G^T[s][t]
+      for (int ks = 0; ks < KS; ++ks)  // B[s][(N/2) kk + 8 ks + 0..7]: chunk (N/16) kk + ks
+        gt = mfma32x32x16(ld_bf16x8(brow + ((((N / 16) * kk + ks) ^ bsw) << 3)), creg[ks], gt);
       // register r: s = 32 si + 8 (r/4) + 4 kk + r%4, t = 32 ti + i
       float mv[16];
       if (si < ti) {
-        const float rs = exp2f(ct - cum2_lds[32 * si + 31]);
+        const float rs = fexp2(ct - cum2_lds[32 * si + 31]);
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
           const f4 u = *reinterpret_cast<const f4*>(u_lds + 32 * si + 8 * R + 4 * kk);
@@ -231,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int sl = 8 * R + 4 * kk + q;
-            const float v = gt[4 * R + q] * exp2f(ct - cs[q]) * ds[q];
+            const float v = gt[4 * R + q] * fexp2(ct - cs[q]) * ds[q];
             mv[4 * R + q] = sl < i ? v : (sl == i ? v + Dh : 0.0f);
           }
         }
@@ -289,17 +337,15 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) creg0[ks] = ld_bf16x8(Cb + r * bs + 8 * ks);
   }
-  const bf16_t* zh = z + ((b * L + t0) * H + h) * kP + 2 * i + ypt;
-  bf16_t zreg[2][16];
+  // z for the coalesced epilogue: thread piece k covers row (k*256 + tid)/8,
+  // columns 8 ((k*256 + tid) % 8) + 0..7
+  constexpr int EP = FQ * kP / 8 / 256;
+  uint4 zv[EP];
   if constexpr (GATE) {
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-      const int ti = jt == 0 ? ti0 : ti1;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
-        zreg[jt][rr] = zh[(tl < last ? tl : last) * xs];
-      }
+    for (int k = 0; k < EP; ++k) {
+      const int e = k * 256 + tid, row = e / 8, col = (e % 8) * 8;
+      zv[k] = *reinterpret_cast<const uint4*>(z + ((b * L + t0 + (row < last ? row : last)) * H + h) * kP + col);
     }
   }
   {
@@ -319,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = dl * hv[e] + sacc[j][4 * R + e];
         if (more)
-          st4_agent(hout + state_tile_offset(p, n0, N), v);
+          st4_agent(hout, kP * N * 4, 4 * state_tile_offset(p, n0, N), v);
         else if (final_states)
           st4(final_states + (chain * kP + p) * N + n0, v);
         // operand slot of (p, n0..n0+3): ks = (n0 % (N/2)) / 8, reader lane
@@ -342,10 +388,10 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // C H_in^T, decayed from the block start, plus the in-block part; epilogue
+  // C H_in^T, decayed from the block start, plus the in-block part
   const uint4* hs_hi4 = reinterpret_cast<const uint4*>(bh_lds);
   const uint4* hs_lo4 = hs_hi4 + KS * 2 * 64;
-  bf16_t* oh = out + ((b * L + t0) * H + h) * kP + 2 * i + ypt;
+  float ysum[2][16];
 #pragma unroll
   for (int jt = 1; jt >= 0; --jt) {  // ti1 first: its C rows are loaded already
     const int ti = jt == 0 ? ti0 : ti1;
@@ -359,17 +405,44 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
       acc = mfma32x32x16(cv, hhi, acc);
       acc = mfma32x32x16(cv, hlo, acc);
     }
-    float y[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
-      y[rr] = yacc[jt][rr] + acc[rr] * exp2f(cum2_lds[tl]);
-      if constexpr (GATE) y[rr] *= silu(to_f32(zreg[jt][rr]));
+      ysum[jt][rr] = yacc[jt][rr] + acc[rr] * fexp2(cum2_lds[tl]);
     }
+  }
+  // epilogue through LDS: the fp32 output tile [t][p], then z gate and
+  // 16-byte stores of eight consecutive p per thread
+  __syncthreads();  // every wave is done with the state split
+  float* y_lds = reinterpret_cast<float*>(bh_lds);
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    const int ti = jt == 0 ? ti0 : ti1;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
-      if (tl <= last) oh[tl * xs] = (bf16_t)f32_to_bf16_bits(y[rr]);
+      y_lds[tl * kP + 2 * i + ypt] = ysum[jt][rr];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < EP; ++k) {
+    const int e = k * 256 + tid, row = e / 8, col = (e % 8) * 8;
+    const f4 y0 = *reinterpret_cast<const f4*>(y_lds + row * kP + col);
+    const f4 y1 = *reinterpret_cast<const f4*>(y_lds + row * kP + col + 4);
+    float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    if constexpr (GATE) {
+      const uint32_t zw[4] = {zv[k].x, zv[k].y, zv[k].z, zv[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        yv[2 * q] *= fsilu(bf16_lo(zw[q]));
+        yv[2 * q + 1] *= fsilu(bf16_hi(zw[q]));
+      }
+    }
+    if (row <= last) {
+      const uint4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
+                       pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])};
+      *reinterpret_cast<uint4*>(out + ((b * L + t0 + row) * H + h) * kP + col) = o;
     }
   }
 }
@@ -412,6 +485,10 @@ static void launch_fused_n(const Problem& p, hipStream_t s, int stage) {
 }
 
 hipError_t launch_fused_bf16(const Problem& p, hipStream_t s, int stage) {
+  // the group kernel runs only when asked for: on the measured workloads the
+  // per-head kernel is faster (its workgroups hide each other's latency)
+  const bool group = stage == 1 && p.fused_kind == 2;
+  if (group) return launch_fused_group_bf16(p, s);
   if (p.N == 128)
     launch_fused_n<128>(p, s, stage);
   else

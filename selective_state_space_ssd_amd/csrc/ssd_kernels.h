@@ -34,6 +34,7 @@ struct Problem {
   float* fs_ring;        // [b*H chains][2 slots] tiled P x N states
   unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
   unsigned* fs_ctl;      // 8 ticket counters, then the error word
+  int fused_kind;        // 0: choose, 1: per-head kernel, 2: group kernel
 };
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().
@@ -57,6 +58,10 @@ hipError_t launch_bf16_stage(const Problem& p, hipStream_t stream, int stage);
 bool use_fused_bf16(const Problem& p);
 int64_t fused_blocks(int64_t L);
 hipError_t launch_fused_bf16(const Problem& p, hipStream_t stream, int stage);
+
+// Group form of the fused kernel: one workgroup per (block, group, head set).
+int64_t fused_group_units(const Problem& p);
+hipError_t launch_fused_group_bf16(const Problem& p, hipStream_t stream);
 
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);

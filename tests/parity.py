@@ -26,7 +26,7 @@ def bf16_path(name):
 
 def paths_for(dtype):
     """The kernel paths a problem of this dtype can take."""
-    return ("fused", "staged") if dtype == "bf16" else ("auto",)
+    return ("fused_head", "fused_group", "staged") if dtype == "bf16" else ("auto",)
 
 
 def log(msg):

@@ -100,6 +100,7 @@ def test_options():
     lib = ssd.load_library()
     assert lib.ssd_get_option(1) == 0
     assert lib.ssd_set_option(1, 7) == INVALID
+    assert lib.ssd_set_option(1, -1) == INVALID
     assert lib.ssd_set_option(2, 0) == INVALID
     assert lib.ssd_get_option(2) == INVALID
     prev = ssd.set_bf16_path("fused")

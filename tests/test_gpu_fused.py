@@ -1,6 +1,7 @@
-"""GPU checks specific to the fused bf16 kernel: its hand-off of states
-between workgroups (error word, reuse of a workspace, determinism, in-place
-continuation) and its agreement with the staged bf16 kernels."""
+"""GPU checks specific to the fused bf16 kernels (per-head and group forms):
+their hand-off of states between workgroups (error word, reuse of a
+workspace, determinism, in-place continuation) and their agreement with the
+staged bf16 kernels."""
 import math
 
 import numpy as np
@@ -14,6 +15,8 @@ from ssd_workloads import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
+KINDS = ("fused_head", "fused_group")
+
 
 def _error_word(ws):
     # control region = the last 256 bytes: 8 ticket counters, then the error word
@@ -26,14 +29,15 @@ def _inputs(seed, b=2, L=700, H=8, N=128, G=4, init=True):
     return w, inp, upload(inp, "bf16")
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("b,L,H,N,G", [(2, 700, 8, 128, 4), (1, 1000, 6, 64, 3),
-                                       (4, 129, 16, 128, 2)])
-def test_fused_reuse_and_error_word(b, L, H, N, G):
+                                       (4, 129, 16, 128, 2), (1, 400, 24, 128, 2)])
+def test_fused_reuse_and_error_word(kind, b, L, H, N, G):
     """Two calls on one workspace: bitwise-equal outputs, error word 0
     (the set-up kernel re-arms the flags and tickets each call)."""
     w, inp, t = _inputs(600 + L, b, L, H, N, G)
-    log(f"test_fused_reuse b={b} L={L} H={H} N={N} G={G}")
-    with bf16_path("fused"):
+    log(f"test_fused_reuse {kind} b={b} L={L} H={H} N={N} G={G}")
+    with bf16_path(kind):
         ws = torch.empty(ssd.workspace_size(b, L, H, 64, N, G, 256, 1), dtype=torch.uint8,
                          device=t["x"].device)
         o1, f1 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
@@ -48,10 +52,11 @@ def test_fused_reuse_and_error_word(b, L, H, N, G):
     compare("final", np64(f1), rfin, TOL["bf16"])
 
 
-def test_fused_inplace_continuation():
+@pytest.mark.parametrize("kind", KINDS)
+def test_fused_inplace_continuation(kind):
     """final_states may be the initial_states buffer on the fused path too."""
     w, inp, t = _inputs(610, b=2, L=2 * 300, H=8, N=128, G=8)
-    with bf16_path("fused"):
+    with bf16_path(kind):
         full, ffin = run_gpu(t, 256, init=t["initial_states"])
         state = t["initial_states"].clone()
         outs = []
@@ -65,27 +70,29 @@ def test_fused_inplace_continuation():
     compare("final in place", np64(state), np64(ffin), 1e-4)
 
 
-def test_fused_matches_staged():
-    """The two bf16 paths differ only in rounding order: outputs within two
-    bf16 ulps of each other, final states within 1e-4 (1 + |ref|)."""
+@pytest.mark.parametrize("kind", KINDS)
+def test_fused_matches_staged(kind):
+    """The bf16 paths differ only in rounding order: outputs within two bf16
+    ulps of each other, final states within 1e-4 (1 + |ref|)."""
     w, inp, t = _inputs(620, b=2, L=1500, H=16, N=128, G=2)
     res = {}
-    for path in ("fused", "staged"):
+    for path in (kind, "staged"):
         with bf16_path(path):
             res[path] = [np64(v) for v in run_gpu(t, 256, init=t["initial_states"])]
-    o_f, f_f = res["fused"]
+    o_f, f_f = res[kind]
     o_s, f_s = res["staged"]
-    compare("fused vs staged out", o_f, o_s, 2 * 2.0 ** -8)
-    compare("fused vs staged final", f_f, f_s, 1e-4)
+    compare(f"{kind} vs staged out", o_f, o_s, 2 * 2.0 ** -8)
+    compare(f"{kind} vs staged final", f_f, f_s, 1e-4)
 
 
-def test_fused_repeat_bitwise():
+@pytest.mark.parametrize("kind", KINDS)
+def test_fused_repeat_bitwise(kind):
     """Many back-to-back calls of a problem with hundreds of chains in flight
     (2048 workgroups) on one workspace: every call bitwise identical to the
     first and error word 0.  A state read before its producer's stores were
     visible would make a call differ."""
     w, inp, t = _inputs(630, b=4, L=2048, H=32, N=128, G=8)
-    with bf16_path("fused"):
+    with bf16_path(kind):
         ws = torch.empty(ssd.workspace_size(4, 2048, 32, 64, 128, 8, 256, 1), dtype=torch.uint8,
                          device=t["x"].device)
         o0, f0 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)

@@ -10,8 +10,10 @@ Cache holds.
 
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (its algorithmic flops per launch over its mean launch time,
-measured with HIP events recorded by the library on the launch stream), and
-the CPU oracle's throughput on the same workload.
+measured with HIP events recorded by the library on the launch stream), the
+CPU oracle's throughput on the same workload, and (unless --no-bf16) the
+bf16 workload batch 8 x seqlen 4096 measured the same way against the HBM
+roofline.
 """
 import argparse
 import json
@@ -81,6 +83,60 @@ def cpu_baseline(workloads, min_seconds=10.0):
             "cpu": _cpu_model()}
 
 
+def bf16_workload(steps, warmup, name="bf16_b8_L4096_H64_P64_N128_G8_Q256"):
+    """The bf16 workload (batch 8 x seqlen 4096, 64 heads, 8 groups, chunk 256,
+    z and D on, final states returned) on the default bf16 path: calls per
+    second over `steps` calls after `warmup`, with the algorithmic bytes of a
+    call over its mean duration against the HBM peak."""
+    import torch
+    import selective_state_space_ssd_amd as ssd
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(w)
+    t = {}
+    for k in ("x", "z", "B", "C", "dt"):
+        t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
+    for k in ("A", "D", "dt_bias"):
+        t[k] = torch.from_numpy(inp[k]).to(dev)
+    del inp
+    out = torch.empty_like(t["x"])
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    wsz = ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                             w.chunk_size, ssd.SSD_BF16)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    a = (t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(),
+         t["C"].data_ptr(), t["D"].data_ptr(), t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0,
+         math.inf, w.chunk_size, w.ngroups, None, out.data_ptr(), fin.data_ptr(), w.batch,
+         w.seqlen, w.nheads, w.headdim, w.dstate, ssd.SSD_BF16, ws.data_ptr(), wsz)
+    s = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        st = ssd.scan_fwd_raw(*a, s)
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    nbytes = alg_bytes(w)
+    return {
+        "workload": "ssd_scan_fwd bf16 batch 8 x seqlen 4096, 64 heads x headdim 64, dstate "
+                    "128, ngroups 8, chunk 256, z gate and D on, final states returned",
+        "path": ssd.get_bf16_path(),
+        "tokens_per_s": w.tokens / el,
+        "ms_per_call": el * 1e3,
+        "calls": steps,
+        "roofline": {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
+                     "alg_bytes": nbytes},
+    }
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -97,6 +153,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true",
+                    help="skip the second measured workload (bf16, batch 8 x seqlen 4096)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture the step once as a HIP graph per input copy, replay "
                          "it, and report the replay rate as the value")
@@ -256,6 +314,10 @@ def main():
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(workloads),
     }
+    if not args.no_bf16:
+        del keep, calls, ws
+        torch.cuda.empty_cache()
+        line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3)]
     print(json.dumps(line), flush=True)
 
 

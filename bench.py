@@ -34,6 +34,25 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 
+# Kernel sources whose counters the committed traffic summary describes.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_scan_group_f32_b2_L2048_traffic.json")
+
+
+def measured_traffic(kernel_stage):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when there is none or the kernel's
+    sources have changed since the counters were taken."""
+    import json
+    if kernel_stage != "chunk_scan" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    from rocprof_summary import sources_hash
+    t = json.load(open(TRAFFIC_FILE))
+    csrc = os.path.join(ROOT, "selective_state_space_ssd_amd", "csrc")
+    if sources_hash([os.path.join(csrc, n) for n in t["sources"]]) != t["sources_sha256_16"]:
+        return None
+    return t["bytes_per_dispatch"]
+
+
 def alg_flops(w):
     """Algorithmic flops of one call, by stage (chunked SSD, causal, C.B^T once
     per group): chunk state 2QPN per (chunk, head); state passing 2PN per
@@ -297,7 +316,7 @@ def main():
             "peak": PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(dom_name),
             "launches_timed": args.steps * len(workloads),
             "mean_launch_us": dom_s / len(workloads) * 1e6,
         },

@@ -4,6 +4,12 @@
                                            (from a --kernel-trace --stats run)
   python rocprof_summary.py --pmc DIR ...  per-kernel mean of each collected counter
                                            per dispatch (from --pmc runs)
+  python rocprof_summary.py --traffic FETCH_DIR WRITE_DIR KERNEL COPY_MIB SRC...
+      HBM bytes per dispatch of the kernel whose name contains KERNEL, from a
+      FETCH_SIZE run and a WRITE_SIZE run of the same command, each scaled by
+      what the counter reads for the plain device copy of COPY_MIB MiB in that
+      command; prints JSON with a hash of the source files SRC (the counters
+      describe those sources only)
 
 DIR holds the run's ``*_results.db`` (rocprofv3's SQLite output).
 """
@@ -49,8 +55,60 @@ def pmc_means(path):
     return {k: {c: (sum(v) / len(v), len(v)) for c, v in d.items()} for k, d in acc.items()}
 
 
+def sources_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic(fetch_dir, write_dir, kernel, copy_mib, sources):
+    f = pmc_means(fetch_dir)
+    w = pmc_means(write_dir)
+    copy_kib = copy_mib * 1024.0
+
+    def pick(d, counter, sub):
+        hits = [(k, v[counter]) for k, v in d.items() if sub in k and counter in v]
+        if len(hits) != 1:
+            raise SystemExit(f"{counter}: {len(hits)} kernels match {sub!r}: {[h[0] for h in hits]}")
+        return hits[0]
+
+    # the calibration copy: the largest single dispatch of a copy kernel (the
+    # COPY_MIB device-to-device copy; small uploads use the same kernel)
+    def copy_reading(path, counter):
+        con = sqlite3.connect(_db(path))
+        v = con.execute("select max(value) from counters_collection where counter_name = ? and "
+                        "lower(kernel_name) like '%copy%'", (counter,)).fetchone()[0]
+        if not v:
+            raise SystemExit(f"{counter}: no copy kernel in the run")
+        return float(v)
+
+    fk, (fetch_kib, nf) = pick(f, "FETCH_SIZE", kernel)
+    wk, (write_kib, nw) = pick(w, "WRITE_SIZE", kernel)
+    ff = copy_kib / copy_reading(fetch_dir, "FETCH_SIZE")
+    wf = copy_kib / copy_reading(write_dir, "WRITE_SIZE")
+    return {
+        "kernel": short(fk),
+        "dispatches": [nf, nw],
+        "fetch_kib_per_dispatch": fetch_kib,
+        "write_kib_per_dispatch": write_kib,
+        "fetch_factor": ff,
+        "write_factor": wf,
+        "bytes_per_dispatch": (fetch_kib * ff + write_kib * wf) * 1024.0,
+        "copy_mib": copy_mib,
+        "sources": [os.path.basename(p) for p in sources],
+        "sources_sha256_16": sources_hash(sources),
+    }
+
+
 if __name__ == "__main__":
-    if sys.argv[1] == "--pmc":
+    if sys.argv[1] == "--traffic":
+        import json
+        fd, wd, kern, mib = sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5])
+        print(json.dumps(traffic(fd, wd, kern, mib, sys.argv[6:]), indent=1))
+    elif sys.argv[1] == "--pmc":
         merged = defaultdict(dict)
         for d in sys.argv[2:]:
             for k, cs in pmc_means(d).items():

@@ -246,6 +246,8 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   __shared__ float bg_lds[BGS];  // B tile, then the G^T tiles
   __shared__ float cum_lds[4][Q];  // running sums in log2 units (cum * log2 e)
   __shared__ float dt_lds[4][Q];
+  // u_s = 2^(cum_e - cum_s) dt_s, e = last step of s's 32-step tile (<= dt_s)
+  __shared__ __align__(16) float u_lds[4][Q];
 
   const int64_t HQ = H / 4;
   const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*HQ + hq)
@@ -283,8 +285,11 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     for (int k = tid; k < 4 * Q; k += 64 * NW) {
       const int w = k / Q, t = k % Q;
       const int64_t o = ((b * H + h0 + w) * nc + c) * Q + t;
-      cum_lds[w][t] = ws_cum[o] * kLog2e;
-      dt_lds[w][t] = ws_dt[o];
+      const float cum2 = ws_cum[o] * kLog2e, dtv = ws_dt[o];
+      const float cend2 = ws_cum[o - t + (t | 31)] * kLog2e;
+      cum_lds[w][t] = cum2;
+      dt_lds[w][t] = dtv;
+      u_lds[w][t] = fast_exp2(cend2 - cum2) * dtv;
     }
   }
   __syncthreads();
@@ -367,11 +372,12 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
 
   const float* cumw = cum_lds[slot];
   const float* dtw = dt_lds[slot];
+  const float* uw = u_lds[slot];
   float ct[NS], ect[NS];  // cum_t (log2 units) and exp(cum_t) of this lane's A-operand row
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     ct[j] = cumw[32 * own(j) + i];
-    ect[j] = exp2f(ct[j]);
+    ect[j] = fast_exp2(ct[j]);
   }
 
   // ---- 2. state part: acc = (exp(cum_t) C) . H_in^T ---------------------------
@@ -416,23 +422,31 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   for (int si = 0; si < NT; ++si) {
     if (si > smax) break;  // uniform per wave
     // masked values mv[j][e] of step R: G^T(s, t) * 2^(ct - cs) * dt_s, causal on
-    // the diagonal tile, plus D at s == t
+    // the diagonal tile, plus D at s == t.  Below the diagonal the decay is
+    // split at the s-tile's last step e: 2^(ct - ce) * u_s, both factors <= 1,
+    // so one exp per lane and tile; the diagonal tile keeps the direct form.
+    float rs[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) rs[j] = fast_exp2(ct[j] - cumw[32 * si + 31]);
     auto masked = [&](int R, float (&mv)[NS][4]) {
       const f4 cs4 = *reinterpret_cast<const f4*>(&cumw[32 * si + 8 * R + 4 * kk]);
       const f4 ds4 = *reinterpret_cast<const f4*>(&dtw[32 * si + 8 * R + 4 * kk]);
+      const f4 us4 = *reinterpret_cast<const f4*>(&uw[32 * si + 8 * R + 4 * kk]);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int ti = own(j) >= si ? own(j) : si;  // tiles below si are not used
         const f4 gv = *reinterpret_cast<const f4*>(
             &bg_lds[(((ti * (ti + 1) / 2 + si) * 4 + R) * 64 + lane) * 4]);
+        if (own(j) == si) {  // uniform
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = gv[e] * exp2f(ct[j] - cs4[e]) * ds4[e];
-          if (own(j) == si) {
+          for (int e = 0; e < 4; ++e) {
+            const float v = gv[e] * fast_exp2(ct[j] - cs4[e]) * ds4[e];
             const int sl = 8 * R + 4 * kk + e;  // s within the tile
-            v = (sl < i) ? v : (sl == i ? v + Dh : 0.0f);
+            mv[j][e] = (sl < i) ? v : (sl == i ? v + Dh : 0.0f);
           }
-          mv[j][e] = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mv[j][e] = gv[e] * rs[j] * us4[e];
         }
       }
     };

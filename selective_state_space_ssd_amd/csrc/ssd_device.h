@@ -182,7 +182,15 @@ __device__ __forceinline__ void state_tile_coords(int k, int N, int* p, int* n) 
 
 // ---- math -------------------------------------------------------------------
 
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + __expf(-v)); }
+// 2^x on v_exp_f32 (results below the normal range flush to zero) and 1/x on
+// v_rcp_f32 (1 ulp): the decays and gates here are all in (0, 1] or feed a
+// bf16/fp32 output far coarser than these errors.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v)
+__device__ __forceinline__ float silu(float v) {
+  return v * fast_rcp(1.0f + fast_exp2(-v * 1.4426950408889634f));
+}
 
 // ---- launch order -------------------------------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).  This

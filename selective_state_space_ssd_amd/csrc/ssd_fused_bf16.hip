@@ -74,6 +74,28 @@ __device__ __forceinline__ s16x8 b_tr_operand(const bf16_t* lds, int r0, int r1,
   return v;
 }
 
+// The x tile sits in LDS unpadded (64 bf16 per row, columns permuted as in
+// stage_x_tile) with 16-byte chunk j of row r at j ^ (r & 2): the four rows of
+// a transposed read then land on distinct banks.
+__device__ __forceinline__ int x_off(int r, int col) {
+  return r * kP + ((((col >> 3) ^ (r & 2))) << 3) + (col & 7);
+}
+__device__ __forceinline__ s16x4 x_tr4(const bf16_t* lds, int r0, int c0) {
+  const int lane = threadIdx.x % 64;
+  const int m = lane % 16, half = (lane / 16) % 2;
+  const bf16_t* p = lds + x_off(r0 + m / 4, c0 + 16 * half + 4 * (m % 4));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+// B operand from the x tile: lane l gets x rows {r0 + 0..3} and {r1 + 0..3} of
+// LDS column c0 + l%32.
+__device__ __forceinline__ s16x8 x_tr_operand(const bf16_t* lds, int r0, int r1, int c0) {
+  const s16x4 a = x_tr4(lds, r0, c0), b = x_tr4(lds, r1, c0);
+  s16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
 // 2^x with v_exp_f32 (results below the normal range flush to zero).
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // z * sigmoid(z) with v_exp_f32 and v_rcp_f32.
@@ -97,7 +119,7 @@ __device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(
 
 template <int N>
 struct FusedLds {
-  static constexpr int kX = FQ * kXLD;            // x tile (bf16)
+  static constexpr int kX = FQ * kP;              // x tile (bf16, swizzled)
   static constexpr int kB = FQ * N;               // B tile (bf16)
   static constexpr int kH = kP * N * 2;           // entering state, hi/lo bf16
   static constexpr int kY = FQ * kP * 2;          // output tile, fp32
@@ -129,7 +151,7 @@ __global__ __launch_bounds__(256) void fused_prep_kernel(const float* __restrict
 }
 
 template <int N, bool GATE>
-__global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void fused_scan_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const bf16_t* __restrict__ dt_raw, const float* __restrict__ A,
     const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Dv,
@@ -146,6 +168,7 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
   __shared__ __align__(16) float dt_lds[FQ];
   __shared__ __align__(16) float w_lds[FQ];           // exp(cum_last - cum_t) dt_t
   __shared__ __align__(16) float u_lds[FQ];           // exp(cum_end(tile of s) - cum_s) dt_s
+  __shared__ __align__(16) float et_lds[FQ];          // exp(cum_t)
   __shared__ float dlast_lds;
   __shared__ unsigned ticket_lds;
 
@@ -187,10 +210,21 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
       dt_lds[t] = dtv[k];
       w_lds[t] = __expf(cum_last - cum[k]) * dtv[k];
       u_lds[t] = __expf(cend - cum[k]) * dtv[k];
+      et_lds[t] = __expf(cum[k]);
     }
     if (lane == 0) dlast_lds = __expf(cum_last);
   }
-  store_x_tile<FQ>(x_lds, xt, last);
+#pragma unroll
+  for (int k = 0; k < XTile<FQ>::ITER; ++k) {  // x tile, permuted columns, swizzled chunks
+    const int e = (k * 256 + tid) * 8;
+    const int row = e / kP, col = e % kP;
+    const uint4 v = xt.v[k];
+    const uint32_t m = row > last ? 0u : 0xffffffffu;
+    const uint2 even = {((v.x & 0xffffu) | (v.y << 16)) & m, ((v.z & 0xffffu) | (v.w << 16)) & m};
+    const uint2 odd = {((v.x >> 16) | (v.y & 0xffff0000u)) & m, ((v.z >> 16) | (v.w & 0xffff0000u)) & m};
+    *reinterpret_cast<uint2*>(x_lds + x_off(row, col / 2)) = even;
+    *reinterpret_cast<uint2*>(x_lds + x_off(row, 32 + col / 2)) = odd;
+  }
 #pragma unroll
   for (int k = 0; k < RowTile<FQ, N>::ITER; ++k) {  // B tile, swizzled chunks
     const int e = k * 256 + tid;
@@ -199,33 +233,6 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
         row > last ? uint4{0u, 0u, 0u, 0u} : bt.v[k];
   }
   __syncthreads();
-
-  // block state contribution S^T[n][p] = sum_t B[t][n] w_t x[t][p]; wave w
-  // owns n-tile w (N = 128, both p-halves) or n-tile w/2, p-half w%2 (N = 64)
-  const int snt = N == 128 ? wave : wave / 2;
-  const int spt0 = N == 128 ? 0 : wave % 2;
-  f16x sacc[NPT];
-#pragma unroll
-  for (int j = 0; j < NPT; ++j) sacc[j] = zero16();
-#pragma unroll 2
-  for (int ks = 0; ks < FQ / 16; ++ks) {
-    const int r0 = 16 * ks + 8 * kk;
-    const s16x8 braw = b_tr_operand<N>(bh_lds, r0, r0 + 4, 32 * snt);
-    const f4 w0 = *reinterpret_cast<const f4*>(w_lds + r0);
-    const f4 w1 = *reinterpret_cast<const f4*>(w_lds + r0 + 4);
-    const uint4 bw = __builtin_bit_cast(uint4, braw);
-    const float av[8] = {bf16_lo(bw.x) * w0[0], bf16_hi(bw.x) * w0[1], bf16_lo(bw.y) * w0[2],
-                         bf16_hi(bw.y) * w0[3], bf16_lo(bw.z) * w1[0], bf16_hi(bw.z) * w1[1],
-                         bf16_lo(bw.w) * w1[2], bf16_hi(bw.w) * w1[3]};
-    s16x8 ahi, alo;
-    split_bf16x8(av, ahi, alo);
-#pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-      const s16x8 bop = lds_tr_operand(x_lds, kXLD, r0, r0 + 4, 32 * (spt0 + j));
-      sacc[j] = mfma32x32x16(ahi, bop, sacc[j]);
-      sacc[j] = mfma32x32x16(alo, bop, sacc[j]);
-    }
-  }
 
   // in-block output: wave w owns p-half pt = w%2 of t-tiles {3 - w/2, w/2};
   // each (t-tile, s-tile <= t-tile) product G^T = B_s C_t^T is formed by the
@@ -238,10 +245,10 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
   const bf16_t* Cb = Cm + ((b * L + t0) * G + g) * N + (N / 2) * kk;
   const float Dh = Dv ? Dv[h] : 0.0f;
   f16x yacc[2];
-  s16x8 creg[KS];  // after the loop: the C rows of t-tile ti1
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
     const int ti = jt == 0 ? ti0 : ti1;
+    s16x8 creg[KS];
     {
       const int tr = 32 * ti + i;
       const int r = tr < last ? tr : last;
@@ -291,12 +298,39 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
         s16x8 mhi, mlo;
         split_bf16x8(mm, mhi, mlo);
         const int r0 = 32 * si + 16 * m + 4 * kk;
-        const s16x8 bop = lds_tr_operand(x_lds, kXLD, r0, r0 + 8, 32 * ypt);
+        const s16x8 bop = x_tr_operand(x_lds, r0, r0 + 8, 32 * ypt);
         acc = mfma32x32x16(mhi, bop, acc);
         acc = mfma32x32x16(mlo, bop, acc);
       }
     }
     yacc[jt] = acc;
+  }
+
+  // block state contribution S^T[n][p] = sum_t B[t][n] w_t x[t][p]; wave w
+  // owns n-tile w (N = 128, both p-halves) or n-tile w/2, p-half w%2 (N = 64)
+  const int snt = N == 128 ? wave : wave / 2;
+  const int spt0 = N == 128 ? 0 : wave % 2;
+  f16x sacc[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) sacc[j] = zero16();
+#pragma unroll 2
+  for (int ks = 0; ks < FQ / 16; ++ks) {
+    const int r0 = 16 * ks + 8 * kk;
+    const s16x8 braw = b_tr_operand<N>(bh_lds, r0, r0 + 4, 32 * snt);
+    const f4 w0 = *reinterpret_cast<const f4*>(w_lds + r0);
+    const f4 w1 = *reinterpret_cast<const f4*>(w_lds + r0 + 4);
+    const uint4 bw = __builtin_bit_cast(uint4, braw);
+    const float av[8] = {bf16_lo(bw.x) * w0[0], bf16_hi(bw.x) * w0[1], bf16_lo(bw.y) * w0[2],
+                         bf16_hi(bw.y) * w0[3], bf16_lo(bw.z) * w1[0], bf16_hi(bw.z) * w1[1],
+                         bf16_lo(bw.w) * w1[2], bf16_hi(bw.w) * w1[3]};
+    s16x8 ahi, alo;
+    split_bf16x8(av, ahi, alo);
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const s16x8 bop = x_tr_operand(x_lds, r0, r0 + 4, 32 * (spt0 + j));
+      sacc[j] = mfma32x32x16(ahi, bop, sacc[j]);
+      sacc[j] = mfma32x32x16(alo, bop, sacc[j]);
+    }
   }
 
   // ---- phase B: the entering state ----
@@ -328,24 +362,18 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
 #pragma unroll
     for (int R = 0; R < 4; ++R)
       hreg[j][R] = ld4(hin + state_tile_offset(2 * i + spt0 + j, 32 * snt + 8 * R + 4 * kk, N));
-  // C rows of t-tile ti0 (those of ti1 are still in creg) and z of both,
-  // rows clamped to the sequence
-  s16x8 creg0[KS];
+  // C rows 64..127 of the block (t-tiles 2 and 3, i.e. ti0 of every wave;
+  // ti1's rows are still in creg) go to the x tile's space, swizzled like the
+  // B tile; loads now, LDS stores after the state update
+  constexpr int CITER = (FQ / 2) * N / 8 / 256;
+  uint4 cv[CITER];
   {
-    const int tr = 32 * ti0 + i;
-    const int r = tr < last ? tr : last;
+    const bf16_t* src = Cm + ((b * L + t0) * G + g) * N;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) creg0[ks] = ld_bf16x8(Cb + r * bs + 8 * ks);
-  }
-  // z for the coalesced epilogue: thread piece k covers row (k*256 + tid)/8,
-  // columns 8 ((k*256 + tid) % 8) + 0..7
-  constexpr int EP = FQ * kP / 8 / 256;
-  uint4 zv[EP];
-  if constexpr (GATE) {
-#pragma unroll
-    for (int k = 0; k < EP; ++k) {
-      const int e = k * 256 + tid, row = e / 8, col = (e % 8) * 8;
-      zv[k] = *reinterpret_cast<const uint4*>(z + ((b * L + t0 + (row < last ? row : last)) * H + h) * kP + col);
+    for (int k = 0; k < CITER; ++k) {
+      const int e = k * 256 + tid;
+      const int row = FQ / 2 + e / (N / 8), chunk = e % (N / 8);
+      cv[k] = *reinterpret_cast<const uint4*>(src + (row < last ? row : last) * bs + chunk * 8);
     }
   }
   {
@@ -381,34 +409,65 @@ __global__ __launch_bounds__(256, 2) void fused_scan_bf16_kernel(
     // the state went out with device-scope stores (written through to the
     // memory side); waiting for them to complete makes them visible to any
     // XCD that invalidates its caches, as the consumer does after the flag
+#pragma unroll
+    for (int k = 0; k < CITER; ++k) {
+      const int e = k * 256 + tid;
+      const int row = e / (N / 8), chunk = e % (N / 8);
+      *reinterpret_cast<uint4*>(x_lds + b_off<N>(row, chunk * 8)) =
+          FQ / 2 + row > last ? uint4{0u, 0u, 0u, 0u} : cv[k];
+    }
     if (more) wait_vmem_stores();
-    __syncthreads();  // state published by every wave; H_in split complete in LDS
+    __syncthreads();  // state published by every wave; H_in split and C rows in LDS
     if (more && tid == 0)
       __hip_atomic_store(flags + chain * nblk + c + 1, 1u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  // C rows of t-tile ti1 (rows 0..63 are not in LDS)
+  s16x8 creg[KS];
+  {
+    const int tr = 32 * ti1 + i;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) creg[ks] = ld_bf16x8(Cb + (tr < last ? tr : last) * bs + 8 * ks);
+  }
   // C H_in^T, decayed from the block start, plus the in-block part
   const uint4* hs_hi4 = reinterpret_cast<const uint4*>(bh_lds);
   const uint4* hs_lo4 = hs_hi4 + KS * 2 * 64;
   float ysum[2][16];
 #pragma unroll
-  for (int jt = 1; jt >= 0; --jt) {  // ti1 first: its C rows are loaded already
+  for (int jt = 0; jt < 2; ++jt) {  // ti0 first: its C rows are in LDS already
     const int ti = jt == 0 ? ti0 : ti1;
     const int tr = 32 * ti + i;
     f16x acc = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const s16x8 cv = tr > last ? s16x8{0, 0, 0, 0, 0, 0, 0, 0} : (jt == 0 ? creg0[ks] : creg[ks]);
+      // C[32 ti + i][(N/2) kk + 8 ks + 0..7]: registers (ti1) or the LDS copy (ti0)
+      s16x8 ca = creg[ks];
+      if (jt == 0)
+        ca = ld_bf16x8(x_lds + b_off<N>(32 * ti - FQ / 2 + i, (N / 2) * kk + 8 * ks));
+      const s16x8 cvv = tr > last ? s16x8{0, 0, 0, 0, 0, 0, 0, 0} : ca;
       const s16x8 hhi = __builtin_bit_cast(s16x8, hs_hi4[(ks * 2 + ypt) * 64 + lane]);
       const s16x8 hlo = __builtin_bit_cast(s16x8, hs_lo4[(ks * 2 + ypt) * 64 + lane]);
-      acc = mfma32x32x16(cv, hhi, acc);
-      acc = mfma32x32x16(cv, hlo, acc);
+      acc = mfma32x32x16(cvv, hhi, acc);
+      acc = mfma32x32x16(cvv, hlo, acc);
     }
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int tl = 32 * ti + 8 * (rr / 4) + 4 * kk + (rr % 4);
-      ysum[jt][rr] = yacc[jt][rr] + acc[rr] * fexp2(cum2_lds[tl]);
+    for (int R = 0; R < 4; ++R) {
+      const f4 et = *reinterpret_cast<const f4*>(et_lds + 32 * ti + 8 * R + 4 * kk);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ysum[jt][4 * R + q] = yacc[jt][4 * R + q] + acc[4 * R + q] * et[q];
+    }
+  }
+  // z for the coalesced epilogue: thread piece k covers row (k*256 + tid)/8,
+  // columns 8 ((k*256 + tid) % 8) + 0..7 (rows clamped to the sequence)
+  constexpr int EP = FQ * kP / 8 / 256;
+  uint4 zv[EP];
+  if constexpr (GATE) {
+#pragma unroll
+    for (int k = 0; k < EP; ++k) {
+      const int e = k * 256 + tid, row = e / 8, col = (e % 8) * 8;
+      zv[k] = *reinterpret_cast<const uint4*>(
+          z + ((b * L + t0 + (row < last ? row : last)) * H + h) * kP + col);
     }
   }
   // epilogue through LDS: the fp32 output tile [t][p], then z gate and

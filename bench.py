@@ -12,8 +12,8 @@ Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (its algorithmic flops per launch over its mean launch time,
 measured with HIP events recorded by the library on the launch stream), the
 CPU oracle's throughput on the same workload, and (unless --no-bf16) the
-bf16 workload batch 8 x seqlen 4096 measured the same way against the HBM
-roofline.
+bf16 workload batch 8 x seqlen 4096 and a one-token bf16 decode step (batch
+128, state in place), each against the HBM roofline.
 """
 import argparse
 import json
@@ -149,6 +149,59 @@ def bf16_workload(steps, warmup, name="bf16_b8_L4096_H64_P64_N128_G8_Q256"):
         "path": ssd.get_bf16_path(),
         "tokens_per_s": w.tokens / el,
         "ms_per_call": el * 1e3,
+        "calls": steps,
+        "roofline": {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
+                     "alg_bytes": nbytes},
+    }
+
+
+def decode_workload(steps, warmup, batch=128, nheads=64, dstate=128, ngroups=8):
+    """One-token decode steps (bf16 inputs, fp32 state updated in place, z and D
+    on): the short-sequence kernel.  Bound by reading and writing the state, so
+    the roofline is HBM on the state bytes plus the token's inputs."""
+    import torch
+    import selective_state_space_ssd_amd as ssd
+    dev = torch.device("cuda:0")
+    P = 64
+    g = torch.Generator(device="cpu").manual_seed(11)
+
+    def bf(*shape):
+        return torch.randn(*shape, generator=g).to(torch.bfloat16).to(dev)
+
+    x, z = bf(batch, 1, nheads, P), bf(batch, 1, nheads, P)
+    dt = bf(batch, 1, nheads)
+    B, C = bf(batch, 1, ngroups, dstate), bf(batch, 1, ngroups, dstate)
+    A = (-torch.exp(torch.rand(nheads, generator=g) * math.log(16.0))).to(dev)
+    D = torch.randn(nheads, generator=g).to(dev)
+    dt_bias = torch.full((nheads,), -2.0).to(dev)
+    state = torch.randn(batch, nheads, P, dstate, generator=g).to(dev)
+    out = torch.empty_like(x)
+    a = (x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(),
+         z.data_ptr(), dt_bias.data_ptr(), 0.0, math.inf, 128, ngroups, state.data_ptr(),
+         out.data_ptr(), state.data_ptr(), batch, 1, nheads, P, dstate, ssd.SSD_BF16, None, 0)
+    s = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        st = ssd.scan_fwd_raw(*a, s)
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    nbytes = 2 * batch * nheads * P * dstate * 4 + batch * (
+        3 * nheads * P * 2 + nheads * 2 + 2 * ngroups * dstate * 2)
+    return {
+        "workload": f"one-token decode, bf16 inputs, batch {batch}, {nheads} heads x headdim 64, "
+                    f"dstate {dstate}, ngroups {ngroups}, z and D on, fp32 state in place",
+        "tokens_per_s": batch / el,
+        "us_per_call": el * 1e6,
         "calls": steps,
         "roofline": {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
@@ -336,7 +389,8 @@ def main():
     if not args.no_bf16:
         del keep, calls, ws
         torch.cuda.empty_cache()
-        line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3)]
+        line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3),
+                                   decode_workload(max(20, args.steps), 5)]
     print(json.dumps(line), flush=True)
 
 

@@ -104,9 +104,17 @@ extern "C" {
  * allocates no memory and keeps no pointer after the call returns; calls are
  * reentrant and deterministic (bitwise identical results run to run).
  *
- * Two kernel paths.  bf16 inputs with headdim 64 and dstate 64 or 128 take
- * the fused path by default (see ssd_set_option): one set-up kernel and one
- * scan kernel, in which each workgroup handles 128 timesteps of one (batch,
+ * Short sequences (seqlen <= 16, either dtype, any supported shape) take
+ * the step kernel: the recurrence run step by step from initial_states, one
+ * workgroup per (batch, head) with the state held in registers (serving one
+ * token at a time, or a few speculative tokens, continuing a state).  It
+ * needs no workspace (ssd_scan_fwd_workspace_size returns 0; workspace may
+ * be NULL) and ignores chunk_size beyond checking it.  final_states may be
+ * initial_states.
+ *
+ * Longer sequences take one of two kernel paths.  bf16 inputs with headdim 64
+ * and dstate 64 or 128 take the fused path by default (see ssd_set_option):
+ * one set-up kernel and one scan kernel, in which each workgroup handles 128 timesteps of one (batch,
  * head) and hands the state to the workgroup of the next 128 timesteps
  * through the workspace (the chunked form gives the same result for any block
  * length, up to rounding; chunk_size is still checked).  Every other case
@@ -153,7 +161,7 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
                  size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace ssd_scan_fwd needs for these sizes (0 for an empty
- * problem).  Returns 0 as well for arguments ssd_scan_fwd would reject;
+ * problem and for seqlen <= 16).  Returns 0 as well for arguments ssd_scan_fwd would reject;
  * pure host computation, no HIP call. */
 size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
                                    int64_t headdim, int64_t dstate, int ngroups, int chunk_size,

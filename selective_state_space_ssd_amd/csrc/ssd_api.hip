@@ -36,6 +36,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 struct Layout {
   int64_t nc = 0;
+  bool decode = false;  // seqlen <= kDecodeMaxL: step-by-step kernel, no workspace
   bool fused = false;
   // staged path
   size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0;
@@ -83,6 +84,11 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
   if (!mul_ok(units, chunk_size, &dtn) || !mul_ok(units, pn, &stn)) return SSD_ERR_INVALID_ARG;
   if (stn > INT64_MAX / 8) return SSD_ERR_INVALID_ARG;
   lay->nc = nc;
+  if (ssd::use_decode(seqlen)) {
+    lay->decode = true;
+    lay->total = 0;
+    return SSD_OK;
+  }
   if (fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
     const int64_t nblk = ssd::fused_blocks(seqlen);
     int64_t nchain, grid, ringn, flagn;
@@ -201,6 +207,14 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
   };
   if (!mark(0)) return SSD_ERR_HIP;
+  if (lay.decode) {
+    if (!mark(1) || !mark(2) || !mark(3)) return SSD_ERR_HIP;
+    if ((seqlen > 0 || final_states) && ssd::launch_decode(p, stream) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (!mark(4)) return SSD_ERR_HIP;
+    if (timing) timing->recorded = true;
+    return SSD_OK;
+  }
   if (lay.fused) {
     // set-up (tickets, flags, ring slot 0), then the one scan kernel
     if (ssd::launch_fused_bf16(p, stream, 0) != hipSuccess) return SSD_ERR_HIP;

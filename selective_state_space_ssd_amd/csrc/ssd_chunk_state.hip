@@ -9,10 +9,10 @@
 // layout (ssd_device.h).
 //
 // Two kernels:
-//  * chunk_state_wave_kernel (N = 64 or 128): two waves per (chunk, head),
-//    four heads per workgroup.  The first wave of a head computes dt and the
-//    in-chunk cumsum (stage 1, fused here); then each wave holds half of the
-//    n columns of the state tile in accumulators of v_mfma_f32_32x32x2_f32
+//  * chunk_state_wave_kernel (N = 64 or 128): WPH waves per (chunk, head)
+//    (two as launched), 8 waves per workgroup.  The first wave of a head
+//    computes dt and the in-chunk cumsum (stage 1, fused here); then each wave
+//    holds 32-column n-tiles of the state tile in accumulators of v_mfma_f32_32x32x2_f32
 //    while it walks the chunk two timesteps per MFMA.  It computes
 //    S^T = B^T (w x): lane l supplies B[t][32*nt + l%32] (A operand) and
 //    w_t x[t][2*(l%32) + pt] (B operand) for timestep t = 2m + l/32, so x is
@@ -29,22 +29,24 @@ namespace ssd {
 // one wave per (chunk, head), stage 1 fused
 // ---------------------------------------------------------------------------
 
-template <typename T, int Q, int N>
+template <typename T, int Q, int N, int WPH>
 __global__ __launch_bounds__(512) void chunk_state_wave_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ dt_raw,
     const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
     float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states, int64_t L,
     int64_t H, int64_t G, int64_t nc, int64_t nunits) {
-  constexpr int P = 64, NTN = N / 32, NTW = NTN / 2, E = Q / kWave;
-  static_assert(N == 64 || N == 128, "tile");
-  __shared__ float w_lds[4][2][Q / 2];  // [head][t % 2][t / 2]
+  // WPH waves per head, each owning NTW n-tiles (both p-halves); HPW heads per
+  // workgroup of 8 waves
+  constexpr int P = 64, NTN = N / 32, NTW = NTN / WPH, HPW = 8 / WPH, E = Q / kWave;
+  static_assert((N == 64 || N == 128) && NTW >= 1 && NTW * WPH == NTN, "tile");
+  __shared__ float w_lds[HPW][2][Q / 2];  // [head][t % 2][t / 2]
 
-  const int64_t HQ = (H + 3) / 4;
+  const int64_t HQ = (H + HPW - 1) / HPW;
   const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*HQ + hq)
   const int64_t hq = u % HQ, c = (u / HQ) % nc, b = u / (HQ * nc);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int slot = wave >> 1, half = wave & 1;  // two waves per head
-  const int64_t h = hq * 4 + slot;
+  const int slot = wave / WPH, half = wave % WPH;  // head within the workgroup, wave within the head
+  const int64_t h = hq * HPW + slot;
   const bool active = h < H;
 
   if (active && half == 0) {
@@ -243,8 +245,12 @@ bool chunk_state_fuses_dt(const Problem& p) { return p.N == 64 || p.N == 128; }
 template <typename T, int Q, int N>
 static void launch_qn(const Problem& p, hipStream_t s) {
   if constexpr (N == 64 || N == 128) {
-    const int64_t nunits = p.b * p.nc * ((p.H + 3) / 4);
-    hipLaunchKernelGGL((chunk_state_wave_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(512), 0,
+    // two waves per head: four (one n-tile each) double the waves in flight
+    // but load every x row four times, and measured slower (48 vs 39 us on
+    // batch 2 x seqlen 2048, 32 heads, dstate 128)
+    constexpr int WPH = 2;
+    const int64_t nunits = p.b * p.nc * ((p.H + (8 / WPH) - 1) / (8 / WPH));
+    hipLaunchKernelGGL((chunk_state_wave_kernel<T, Q, N, WPH>), dim3((unsigned)nunits), dim3(512), 0,
                        s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
                        static_cast<const T*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.ws_dt,
                        p.ws_cum, p.ws_states, p.L, p.H, p.G, p.nc, nunits);

@@ -63,6 +63,12 @@ hipError_t launch_fused_bf16(const Problem& p, hipStream_t stream, int stage);
 int64_t fused_group_units(const Problem& p);
 hipError_t launch_fused_group_bf16(const Problem& p, hipStream_t stream);
 
+// Short sequences: the recurrence step by step, one workgroup per (batch,
+// head), no workspace.  Used for seqlen <= kDecodeMaxL whatever the chunk size.
+constexpr int kDecodeMaxL = 16;
+bool use_decode(int64_t seqlen);
+hipError_t launch_decode(const Problem& p, hipStream_t stream);
+
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);
 

@@ -58,12 +58,22 @@ def _ws(b, L, H, P, N, G, Q, dt=0):
     return ssd.workspace_size(b, L, H, P, N, G, Q, dt)
 
 
+DECODE_MAX_L = 16  # sequences this short take the step-by-step kernel
+
+
+def test_short_sequences_need_no_workspace():
+    for L in (1, 2, 16):
+        assert _ws(2, L, 4, 64, 128, 1, 128) == 0 and _ws(2, L, 4, 64, 128, 1, 256, 1) == 0
+    assert _ws(2, 17, 4, 64, 128, 1, 128) > 0
+
+
 def _r(v):
     return (v + 255) // 256 * 256
 
 
 SIZES = [(2, 2048, 32, 64, 128, 1, 128), (1, 300, 4, 64, 16, 1, 64),
-         (8, 4096, 64, 64, 128, 8, 256), (3, 1, 2, 64, 32, 2, 128), (1, 200, 4, 64, 64, 2, 64)]
+         (8, 4096, 64, 64, 128, 8, 256), (3, 1, 2, 64, 32, 2, 128), (1, 200, 4, 64, 64, 2, 64),
+         (2, 17, 4, 64, 128, 2, 128)]
 
 
 def test_workspace_size_formula():
@@ -72,11 +82,13 @@ def test_workspace_size_formula():
         for (b, L, H, P, N, G, Q) in SIZES:
             nc = math.ceil(L / Q)
             want = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+            if L <= DECODE_MAX_L:
+                want = 0
             assert _ws(b, L, H, P, N, G, Q) == want
             # intermediates are fp32 for bf16 too; the staged bf16 matrix-core
             # kernels (chunk 128/256, dstate 64/128) add B^T per (chunk, group)
             bt = _r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
-            assert _ws(b, L, H, P, N, G, Q, 1) == want + bt
+            assert _ws(b, L, H, P, N, G, Q, 1) == (want + bt if want else 0)
     finally:
         ssd.set_bf16_path(prev)
 
@@ -88,6 +100,9 @@ def test_workspace_size_fused_bf16():
     for (b, L, H, P, N, G, Q) in SIZES:
         nc = math.ceil(L / Q)
         staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+        if L <= DECODE_MAX_L:  # short sequences: the step-by-step kernel, no workspace
+            assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
+            continue
         assert _ws(b, L, H, P, N, G, Q) == staged  # fp32 is always staged
         if N in (64, 128):
             want = _r(b * H * 2 * P * N * 4) + _r(b * H * math.ceil(L / 128) * 4) + 256

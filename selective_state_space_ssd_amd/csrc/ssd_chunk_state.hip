@@ -108,8 +108,10 @@ __global__ __launch_bounds__(512) void chunk_state_wave_kernel(
       float bv[NTW];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) bv[nt] = ok ? br[d][nt] : 0.0f;
-      if (m + PF < KS) {  // uniform: refill the slot for step m + PF
-        const int64_t t = row(m + PF);
+      {  // refill the slot for step m + PF; past the chunk end it re-reads a
+         // valid row (unused), so the loads are issued unconditionally and
+         // the compiler's count of loads in flight stays exact across steps
+        const int64_t t = row(m + PF < KS ? m + PF : KS - 1);
         xr[d] = ld2(xb + t * xs);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bb + t * bs + 32 * nt);
@@ -119,6 +121,9 @@ __global__ __launch_bounds__(512) void chunk_state_wave_kernel(
         acc[nt][0] = mfma32x32x2(bv[nt], x0, acc[nt][0]);
         acc[nt][1] = mfma32x32x2(bv[nt], x1, acc[nt][1]);
       }
+      // keep each step's loads and MFMAs in program order: the scheduler
+      // would otherwise sink the refills next to their uses
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 

@@ -53,6 +53,10 @@ def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 
 
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -63,10 +67,11 @@ class OracleLib:
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
         p, i64, d = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
-        lib.oracle_ssd_fwd.argtypes = [p] * 8 + [d, d, p, p, p] + [i64] * 6 + [p, ctypes.c_int]
+        lib.oracle_ssd_fwd.argtypes = ([p] * 8 + [d, d, p, p, p, p] + [i64] * 6 +
+                                       [p, ctypes.c_int])
         lib.oracle_ssd_fwd.restype = ctypes.c_int
         lib.oracle_ssd_chunk_intermediates.argtypes = (
-            [p] * 5 + [d, d] + [p] * 5 + [i64] * 7 + [ctypes.c_int])
+            [p] * 5 + [d, d] + [p] * 6 + [i64] * 7 + [ctypes.c_int])
         lib.oracle_ssd_chunk_intermediates.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = [ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -77,11 +82,13 @@ class OracleLib:
 
     def ssd_fwd(self, x, dt, A, B, C, D=None, z=None, dt_bias=None,
                 dt_limit=(0.0, float("inf")), initial_states=None, return_final_states=False,
-                head_mask=None, nthreads=0):
+                head_mask=None, nthreads=0, seq_idx=None):
         x, dt, A, B, C = _f32(x), _f32(dt), _f32(A), _f32(B), _f32(C)
         D, z, dt_bias = _f32(D), _f32(z), _f32(dt_bias)
         init = _f64(initial_states)
+        seq = _i32(seq_idx)
         b, L, H, P = x.shape
+        assert seq is None or seq.shape == (b, L)
         G, N = B.shape[2], B.shape[3]
         assert dt.shape == (b, L, H) and B.shape == (b, L, G, N) and C.shape == B.shape
         assert A.shape == (H,)
@@ -95,16 +102,19 @@ class OracleLib:
         rc = self.lib.oracle_ssd_fwd(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
             float(dt_limit[0]), float(dt_limit[1]), _ptr(init), _ptr(out), _ptr(final),
-            b, L, H, P, N, G, _ptr(mask), int(nthreads))
+            _ptr(seq), b, L, H, P, N, G, _ptr(mask), int(nthreads))
         if rc != 0:
             raise ValueError("oracle_ssd_fwd rejected the shapes")
         return (out, final) if return_final_states else out
 
     def chunk_intermediates(self, x, dt, A, B, chunk_size, dt_bias=None,
-                            dt_limit=(0.0, float("inf")), initial_states=None, nthreads=0):
+                            dt_limit=(0.0, float("inf")), initial_states=None, nthreads=0,
+                            seq_idx=None):
         x, dt, A, B, dt_bias = _f32(x), _f32(dt), _f32(A), _f32(B), _f32(dt_bias)
         init = _f64(initial_states)
+        seq = _i32(seq_idx)
         b, L, H, P = x.shape
+        assert seq is None or seq.shape == (b, L)
         G, N = B.shape[2], B.shape[3]
         Q = int(chunk_size)
         nc = (L + Q - 1) // Q
@@ -117,7 +127,7 @@ class OracleLib:
         rc = self.lib.oracle_ssd_chunk_intermediates(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(dt_bias), float(dt_limit[0]),
             float(dt_limit[1]), _ptr(init), _ptr(res["dt"]), _ptr(res["cum"]),
-            _ptr(res["chunk_states"]), _ptr(res["states_in"]), b, L, H, P, N, G, Q,
+            _ptr(res["chunk_states"]), _ptr(res["states_in"]), _ptr(seq), b, L, H, P, N, G, Q,
             int(nthreads))
         if rc != 0:
             raise ValueError("oracle_ssd_chunk_intermediates rejected the shapes")
@@ -143,7 +153,8 @@ def max_threads(nthreads: int = 0) -> int:
 
 def ssd_fwd(*args, **kwargs):
     """Plain recurrence.  x [b,L,H,P], dt [b,L,H], A/D/dt_bias [H], B/C [b,L,G,N],
-    z like x, initial_states [b,H,P,N].  Returns out [b,L,H,P] fp64 (and, with
+    z like x, initial_states [b,H,P,N], seq_idx [b,L] int32 (the state resets
+    where it changes).  Returns out [b,L,H,P] fp64 (and, with
     ``return_final_states``, the final state [b,H,P,N] fp64).  ``head_mask``
     [b,H] restricts the work to some (b, h) pairs; other outputs are NaN."""
     return _lib().ssd_fwd(*args, **kwargs)

@@ -17,6 +17,13 @@ h_t = a_t h_{t-1} + dt_t x_t B_t^T gives, with c_t = sum_{r<=t} dt_r A:
   h_{L-1} = exp(c_{L-1}) h_{-1} + sum_s exp(c_{L-1} - c_s) dt_s x_s B_s^T
 
 and out = y * silu(z) when a gate is given.
+
+With seq_idx (several sequences packed along a batch row; the state restarts
+from zero where the label changes) a pair (t, s) interacts only when no
+sequence starts in (s, t]: with k_t the number of sequence starts up to t,
+the decay mask keeps s <= t with k_s = k_t, the initial state reaches only
+the steps with k_t = 0, and the final state sums only over the steps of the
+row's last sequence (plus the initial state if the row holds one sequence).
 """
 from __future__ import annotations
 
@@ -38,8 +45,15 @@ def _segment_sums(dA: np.ndarray) -> np.ndarray:
     return seg
 
 
+def _sequence_counts(seq_row) -> np.ndarray:
+    """k_t = number of steps r <= t (r > 0) whose label differs from step r-1's."""
+    seq_row = np.asarray(seq_row)
+    starts = np.concatenate([[0], (seq_row[1:] != seq_row[:-1]).astype(np.int64)])
+    return np.cumsum(starts)
+
+
 def ssd_fwd_quadratic(x, dt, A, B, C, D=None, z=None, dt_bias=None,
-                      dt_limit=(0.0, float("inf")), initial_states=None):
+                      dt_limit=(0.0, float("inf")), initial_states=None, seq_idx=None):
     """Same arguments and layouts as ``oracle.ssd_fwd``; returns (out, final)."""
     x = np.asarray(x, dtype=np.float64)
     dt = np.asarray(dt, dtype=np.float64)
@@ -54,20 +68,25 @@ def ssd_fwd_quadratic(x, dt, A, B, C, D=None, z=None, dt_bias=None,
     out = np.zeros((b, L, H, P))
     final = np.zeros((b, H, P, N))
     for bi in range(b):
+        k = _sequence_counts(seq_idx[bi]) if seq_idx is not None else np.zeros(L, np.int64)
+        same = k[:, None] == k[None, :]                  # [t, s]: same packed sequence
+        first = (k == 0).astype(np.float64)              # steps the initial state reaches
+        last = (k == k[-1]).astype(np.float64) if L else k.astype(np.float64)
         for h in range(H):
             g = h // hpg
             dA = dtv[bi, :, h] * A[h]
             seg = _segment_sums(dA)                      # [t, s]
-            decay = np.exp(seg)                          # 0 above the diagonal
+            decay = np.exp(seg) * same                   # 0 above the diagonal
             scores = C[bi, :, g, :] @ B[bi, :, g, :].T   # [t, s] = C_t . B_s
             v = dtv[bi, :, h][:, None] * x[bi, :, h, :]  # [s, p]
             y = (decay * scores) @ v
             c = np.cumsum(dA)
-            fin = (np.exp(c[-1] - c)[:, None] * v).T @ B[bi, :, g, :]  # [p, n]
+            fin = ((np.exp(c[-1] - c) * last)[:, None] * v).T @ B[bi, :, g, :]  # [p, n]
             if initial_states is not None:
                 h0 = np.asarray(initial_states, dtype=np.float64)[bi, h]  # [p, n]
-                y += np.exp(c)[:, None] * (C[bi, :, g, :] @ h0.T)
-                fin += np.exp(c[-1]) * h0
+                y += (np.exp(c) * first)[:, None] * (C[bi, :, g, :] @ h0.T)
+                if L == 0 or k[-1] == 0:
+                    fin += (np.exp(c[-1]) if L else 1.0) * h0
             if D is not None:
                 y += float(D[h]) * x[bi, :, h, :]
             if z is not None:

@@ -25,6 +25,8 @@
  *    any norm, initial_states and return_final_states: mamba issue #647, the
  *    repro script's arguments.
  *  - Continuation from a given state (chunked prefill): mamba issue #488.
+ *  - seq_idx (several sequences packed along one batch row): an argument of
+ *    the chunked-scan call in mamba issue #647's repro script.
  *
  * Readings taken where the pages are silent:
  *  - the state is stored as h[p][n] (headdim x dstate), the transpose of the
@@ -33,13 +35,20 @@
  *  - the input is scaled by dt (not the zero-order-hold (e^{dtA}-1)/A);
  *  - head h reads group g = h / (nheads / ngroups) (contiguous blocks);
  *  - dt_limit clamps after softplus; softplus is always applied;
- *  - the D skip is added before the gate: out = (C.h + D x) * silu(z).
+ *  - the D skip is added before the gate: out = (C.h + D x) * silu(z);
+ *  - seq_idx [batch, seqlen] (optional) labels the packed sequence each step
+ *    belongs to; wherever it changes between steps t-1 and t a new sequence
+ *    starts and the state is reset to zero before step t's update (nothing
+ *    flows across the boundary).  initial_states is the state entering step
+ *    0, i.e. that of the row's first sequence, and final_states the state
+ *    after the last step, i.e. that of the row's last sequence.
  *
  * Layouts (row-major, contiguous):
  *   x, z        [batch, seqlen, nheads, headdim]           float32 values
  *   dt_raw      [batch, seqlen, nheads]                    float32 values
  *   B, C        [batch, seqlen, ngroups, dstate]           float32 values
  *   A, D, dt_bias [nheads]                                 float32 values
+ *   seq_idx     [batch, seqlen]                            int32 labels
  *   init, final [batch, nheads, headdim, dstate]           fp64
  *   out         [batch, seqlen, nheads, headdim]           fp64
  * The inputs arrive as float32 because every input of the method is an fp32
@@ -56,6 +65,12 @@
 /* softplus(u) = log(1 + e^u), in the form that neither overflows nor
  * cancels: max(u,0) + log1p(e^{-|u|}). */
 static double softplus(double u) { return (u > 0.0 ? u : 0.0) + log1p(exp(-fabs(u))); }
+
+/* True when step t of batch row b starts a new packed sequence: its label
+ * differs from step t-1's.  Step 0 continues from the initial state. */
+static int new_sequence(const int32_t* seq_idx, int64_t L, int64_t b, int64_t t) {
+    return seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1];
+}
 
 /* Discretization step of one (b, t, h): softplus of the biased raw value,
  * clamped to [dt_min, dt_max] (mamba issue #647 passes dt_limit=(0, inf)). */
@@ -89,9 +104,9 @@ int oracle_max_threads(int nthreads) { return set_threads(nthreads); }
 int oracle_ssd_fwd(const float* x, const float* dt_raw, const float* A, const float* B,
                    const float* C, const float* D, const float* z, const float* dt_bias,
                    double dt_min, double dt_max, const double* init, double* out,
-                   double* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
-                   int64_t headdim, int64_t dstate, int64_t ngroups,
-                   const unsigned char* head_mask, int nthreads) {
+                   double* final_states, const int32_t* seq_idx, int64_t batch,
+                   int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                   int64_t ngroups, const unsigned char* head_mask, int nthreads) {
     if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
         nheads % ngroups != 0)
         return -1;
@@ -113,6 +128,7 @@ int oracle_ssd_fwd(const float* x, const float* dt_raw, const float* A, const fl
         const double Ah = (double)A[h];
         const double Dh = D ? (double)D[h] : 0.0;
         for (int64_t t = 0; t < L; ++t) {
+            if (new_sequence(seq_idx, L, b, t)) memset(S, 0, sizeof(double) * (size_t)(P * N));
             const double dt = step_dt(dt_raw, dt_bias, dt_min, dt_max, L, H, b, t, h);
             const double a = exp(dt * Ah);
             const float* xt = x + ((b * L + t) * H + h) * P;
@@ -149,13 +165,15 @@ int oracle_ssd_fwd(const float* x, const float* dt_raw, const float* A, const fl
  *                              starting from a zero state
  *   states_in    [b, nc, H, P, N]  the state of the full recurrence just
  *                              before chunk c's first step (init for c = 0)
+ * With seq_idx both recurrences reset to zero where a new sequence starts.
  * Any output pointer may be NULL.  Returns 0, or -1 on bad shapes.
  */
 int oracle_ssd_chunk_intermediates(const float* x, const float* dt_raw, const float* A,
                                    const float* B, const float* dt_bias, double dt_min,
                                    double dt_max, const double* init, double* dt_out,
                                    double* cum_out, double* chunk_states, double* states_in,
-                                   int64_t batch, int64_t seqlen, int64_t nheads,
+                                   const int32_t* seq_idx, int64_t batch, int64_t seqlen,
+                                   int64_t nheads,
                                    int64_t headdim, int64_t dstate, int64_t ngroups,
                                    int64_t chunk_size, int nthreads) {
     if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
@@ -190,6 +208,10 @@ int oracle_ssd_chunk_intermediates(const float* x, const float* dt_raw, const fl
                     if (dt_out) dt_out[k] = 0.0;
                     if (cum_out) cum_out[k] = cum;
                     continue;
+                }
+                if (new_sequence(seq_idx, L, b, t)) {
+                    memset(S, 0, sizeof(double) * (size_t)(P * N));
+                    memset(Sc, 0, sizeof(double) * (size_t)(P * N));
                 }
                 const double dt = step_dt(dt_raw, dt_bias, dt_min, dt_max, L, H, b, t, h);
                 cum += dt * Ah;

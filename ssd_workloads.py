@@ -135,6 +135,26 @@ def make_inputs(w: Workload) -> dict:
     return out
 
 
+def make_seq_idx(batch: int, seqlen: int, mean_len: float, seed: int) -> np.ndarray:
+    """Labels of packed sequences, int32 [batch, seqlen].
+
+    Each row is filled with sequences whose lengths are drawn uniformly from
+    [1, 2*mean_len - 1] (the last one cut at the row end), labelled 0, 1, 2,
+    ... in order.  A generator of its own (seeded by ``seed``), so drawing
+    labels leaves every other input unchanged."""
+    rng = np.random.default_rng(seed)
+    hi = max(1, int(round(2 * mean_len - 1)))
+    out = np.empty((batch, seqlen), dtype=np.int32)
+    for b in range(batch):
+        t, label = 0, 0
+        while t < seqlen:
+            n = int(rng.integers(1, hi + 1))
+            out[b, t:t + n] = label
+            t += n
+            label += 1
+    return out
+
+
 def random_small(seed: int, batch=2, seqlen=37, nheads=4, headdim=8, dstate=4, ngroups=2,
                  gate=True, skip=True, init=False, dtype="f32") -> dict:
     """Small inputs with the same distributions, for oracle self-tests."""

@@ -19,7 +19,7 @@ from scipy.special import expit
 
 import oracle
 from oracle.quadratic import ssd_fwd_quadratic
-from ssd_workloads import random_small
+from ssd_workloads import make_seq_idx, random_small
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -348,11 +348,117 @@ def pin_page_printed_block_values(orc):
         assert abs(_block_out000(orc, g, True) - combined) <= 2e-4
 
 
+def _starts(seq_row):
+    """Steps where a new packed sequence begins (0 included)."""
+    return [0] + [t for t in range(1, len(seq_row)) if seq_row[t] != seq_row[t - 1]]
+
+
+def pin_seq_idx_quadratic_form(orc):
+    """Packed sequences: the recurrence with resets == the quadratic form with
+    the same-sequence mask (a different route to the same result)."""
+    cases = [
+        dict(seed=61, batch=2, seqlen=45, nheads=4, headdim=6, dstate=5, ngroups=2, init=True),
+        dict(seed=62, batch=1, seqlen=64, nheads=2, headdim=4, dstate=8, ngroups=1, gate=False),
+        dict(seed=63, batch=3, seqlen=20, nheads=2, headdim=3, dstate=4, ngroups=2, init=True,
+             skip=False),
+    ]
+    for i, c in enumerate(cases):
+        inp = random_small(**c)
+        a, kw = _args(inp)
+        seqs = [make_seq_idx(c["batch"], c["seqlen"], m, 100 + i) for m in (1.5, 6, 40)]
+        # labels that come back to an earlier value still start a new sequence
+        seqs.append((seqs[1] % 2).astype(np.int32))
+        for seq in seqs:
+            for lim in [(0.0, float("inf")), (0.01, 0.2)]:
+                out, fin = orc.ssd_fwd(*a, **kw, dt_limit=lim, return_final_states=True,
+                                       seq_idx=seq)
+                qo, qf = ssd_fwd_quadratic(*a, **kw, dt_limit=lim, seq_idx=seq)
+                assert _rel(out, qo) < 1e-12, (c, seq)
+                assert _rel(fin, qf) < 1e-12, (c, seq)
+
+
+def pin_seq_idx_separate_scans(orc):
+    """A packed row equals its sequences scanned one by one: the first from
+    the initial state, every later one from zero; the final state is the last
+    sequence's."""
+    inp = random_small(64, batch=2, seqlen=50, nheads=4, headdim=4, dstate=6, ngroups=2,
+                       init=True)
+    a, kw = _args(inp)
+    x, dt, A, B, C = a
+    seq = make_seq_idx(2, 50, 9, 7)
+    out, fin = orc.ssd_fwd(*a, **kw, return_final_states=True, seq_idx=seq)
+    for b in range(2):
+        st = _starts(seq[b]) + [50]
+        for j in range(len(st) - 1):
+            sl = slice(st[j], st[j + 1])
+            init = inp["initial_states"][b:b + 1] if j == 0 else None
+            o1, f1 = orc.ssd_fwd(x[b:b + 1, sl], dt[b:b + 1, sl], A, B[b:b + 1, sl],
+                                 C[b:b + 1, sl], D=inp["D"], z=inp["z"][b:b + 1, sl],
+                                 dt_bias=inp["dt_bias"], initial_states=init,
+                                 return_final_states=True)
+            assert np.array_equal(o1[0], out[b, sl]), (b, j)
+        assert np.array_equal(f1[0], fin[b]), b
+
+
+def pin_seq_idx_trivial_labels(orc):
+    """One label per row (any value) is the plain scan, bit for bit; a new
+    sequence at every step leaves only each token's own term:
+    y_t = dt_t (C_t . B_t) x_t + D x_t (+ exp(dt_0 A) C_0 . h0 at t = 0)."""
+    inp = random_small(65, batch=2, seqlen=19, nheads=2, headdim=3, dstate=4, ngroups=1,
+                       init=True)
+    a, kw = _args(inp)
+    ref, rfin = orc.ssd_fwd(*a, **kw, return_final_states=True)
+    out, fin = orc.ssd_fwd(*a, **kw, return_final_states=True,
+                           seq_idx=np.full((2, 19), 7, np.int32))
+    assert np.array_equal(out, ref) and np.array_equal(fin, rfin)
+    every = np.tile(np.arange(19, dtype=np.int32), (2, 1))
+    out, fin = orc.ssd_fwd(*a, **kw, return_final_states=True, seq_idx=every)
+    x, dt, A, B, C = (v.astype(np.float64) for v in a)
+    dtv = np.logaddexp(0.0, dt + inp["dt_bias"].astype(np.float64))      # [b, t, h]
+    cb = np.einsum("btn,btn->bt", C[:, :, 0], B[:, :, 0])               # [b, t]
+    y = (dtv * cb[:, :, None])[..., None] * x + inp["D"][None, None, :, None] * x
+    h0 = inp["initial_states"].astype(np.float64)
+    y[:, 0] += (np.exp(dtv[:, 0] * A)[..., None] *
+                np.einsum("bn,bhpn->bhp", C[:, 0, 0], h0))
+    zz = inp["z"].astype(np.float64)
+    y *= zz * expit(zz)
+    assert _rel(out, y) < 1e-12
+    want_fin = np.einsum("bh,bhp,bn->bhpn", dtv[:, -1], x[:, -1], B[:, -1, 0])
+    assert _rel(fin, want_fin) < 1e-12
+
+
+def pin_seq_idx_chunk_intermediates(orc):
+    """Chunk intermediates under packed sequences: the chunk-local state is the
+    chunk scanned alone (with its resets) from zero, and the state entering a
+    chunk is the full packed scan's final state over the steps before it."""
+    inp = random_small(66, batch=1, seqlen=40, nheads=2, headdim=3, dstate=4, ngroups=1,
+                       init=True)
+    a, kw = _args(inp)
+    x, dt, A, B, C = a
+    seq = make_seq_idx(1, 40, 5, 8)
+    Q = 16
+    res = orc.chunk_intermediates(x, dt, A, B, Q, dt_bias=inp["dt_bias"],
+                                  initial_states=inp["initial_states"], seq_idx=seq)
+    for c in range(3):
+        sl = slice(c * Q, min(40, (c + 1) * Q))
+        _, f_local = orc.ssd_fwd(x[:, sl], dt[:, sl], A, B[:, sl], C[:, sl],
+                                 dt_bias=inp["dt_bias"], return_final_states=True,
+                                 seq_idx=seq[:, sl])
+        assert _rel(res["chunk_states"][:, c], f_local) < 1e-13, c
+        if c > 0:
+            pre = slice(0, c * Q)
+            _, f_pre = orc.ssd_fwd(x[:, pre], dt[:, pre], A, B[:, pre], C[:, pre],
+                                   dt_bias=inp["dt_bias"], initial_states=inp["initial_states"],
+                                   return_final_states=True, seq_idx=seq[:, pre])
+            assert _rel(res["states_in"][:, c], f_pre) < 1e-13, c
+
+
 PINS = [pin_quadratic_form, pin_ngroups_invariance, pin_head_group_map, pin_continuation,
         pin_no_decay_prefix_sum, pin_geometric_series, pin_iir_filter, pin_single_step,
         pin_zero_B_or_C, pin_gate_and_linearity, pin_dt_and_cumsum, pin_softplus_extremes,
         pin_chunk_states, pin_head_mask, pin_batch_permutation,
-        pin_page_printed_block_values]
+        pin_page_printed_block_values, pin_seq_idx_quadratic_form, pin_seq_idx_separate_scans,
+        pin_seq_idx_trivial_labels, pin_seq_idx_chunk_intermediates]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -383,6 +489,14 @@ MUTANTS = [
     ("x transposed index", "const float* xt = x + ((b * L + t) * H + h) * P;\n            const float* Bt = B + ((b * L + t) * G + g) * N;\n            const float* Ct",
      "const float* xt = x + ((b * L + (L - 1 - t)) * H + h) * P;\n            const float* Bt = B + ((b * L + t) * G + g) * N;\n            const float* Ct"),
     ("dt clamp swapped", "if (dt < dt_min) dt = dt_min;", "if (dt < dt_min) dt = dt_max;"),
+    ("sequence reset ignored",
+     "            if (new_sequence(seq_idx, L, b, t)) memset(S, 0, sizeof(double) * (size_t)(P * N));\n",
+     ""),
+    ("sequence reset one step late", "seq_idx[b * L + t] != seq_idx[b * L + t - 1]",
+     "t > 1 && seq_idx[b * L + t - 1] != seq_idx[b * L + t - 2]"),
+    ("chunk-local state not reset",
+     "                    memset(Sc, 0, sizeof(double) * (size_t)(P * N));\n                }",
+     "                }"),
 ]
 
 

@@ -167,6 +167,45 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
                                    int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
                                    int dtype);
 
+/*
+ * Packed sequences: ssd_scan_fwd over batch rows that each hold several
+ * sequences one after another (the seq_idx argument of the chunked scan in
+ * mamba issue #647's repro script).
+ *
+ *   seq_idx  [batch, seqlen]  int32, 4-byte aligned, required (non-NULL when
+ *            batch and seqlen are > 0): a label per step.  Wherever the label
+ *            of step t differs from that of step t-1 a new sequence starts:
+ *            the state is reset to zero before step t, so nothing flows from
+ *            one sequence into the next.  Labels need not be ordered; only
+ *            changes between neighbouring steps count.
+ *
+ * initial_states is the state entering the row's first sequence and
+ * final_states the state after the row's last step (its last sequence).
+ * Every other argument, the checks and the execution rules are those of
+ * ssd_scan_fwd; `out` must not overlap seq_idx either.  The call takes the
+ * staged path (or, for seqlen <= 16, the step kernel) whatever the bf16 path
+ * option, and needs ssd_scan_fwd_varlen_workspace_size(...) bytes of
+ * workspace: the staged layout above followed, on a 256-byte boundary, by
+ *   seg [batch, nchunks, chunk_size] int32: for step q of chunk c the number
+ *       of sequence starts at steps c*chunk_size .. c*chunk_size + q (steps
+ *       past the sequence end repeat the last count).
+ * Returns the ssd_scan_fwd status codes (SSD_ERR_INVALID_ARG for a missing
+ * seq_idx).
+ */
+int ssd_scan_fwd_varlen(const void* x, const void* dt, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* dt_bias,
+                        float dt_min, float dt_max, int chunk_size, int ngroups,
+                        const float* initial_states, void* out, float* final_states,
+                        const int32_t* seq_idx, int64_t batch, int64_t seqlen, int64_t nheads,
+                        int64_t headdim, int64_t dstate, int dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssd_scan_fwd_varlen needs (0 for an empty problem, for
+ * seqlen <= 16 and for rejected arguments); pure host computation. */
+size_t ssd_scan_fwd_varlen_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                          int64_t headdim, int64_t dstate, int ngroups,
+                                          int chunk_size, int dtype);
+
 /* Static text for a status code ("unknown status" for others). */
 const char* ssd_status_string(int status);
 

@@ -54,6 +54,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_scan_fwd.restype = i
     lib.ssd_scan_fwd_timed.argtypes = fwd_args + [p]
     lib.ssd_scan_fwd_timed.restype = i
+    lib.ssd_scan_fwd_varlen.argtypes = fwd_args[:15] + [p] + fwd_args[15:]
+    lib.ssd_scan_fwd_varlen.restype = i
+    lib.ssd_scan_fwd_varlen_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
+    lib.ssd_scan_fwd_varlen_workspace_size.restype = ctypes.c_size_t
     lib.ssd_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
     lib.ssd_scan_fwd_workspace_size.restype = ctypes.c_size_t
     lib.ssd_status_string.argtypes = [i]
@@ -100,6 +104,13 @@ def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, 
         batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
 
 
+def varlen_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
+                          dtype) -> int:
+    """Workspace bytes of a packed-sequence (seq_idx) call."""
+    return int(load_library().ssd_scan_fwd_varlen_workspace_size(
+        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+
+
 def _check(status: int):
     if status != 0:
         raise SsdError(status, status_string(status))
@@ -141,13 +152,25 @@ def scan_fwd_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, 
     return int(lib.ssd_scan_fwd_timed(*args, timing.handle))
 
 
+def scan_fwd_varlen_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min,
+                        dt_max, chunk_size, ngroups, init_ptr, out_ptr, final_ptr, seq_ptr, batch,
+                        seqlen, nheads, headdim, dstate, dtype, ws_ptr, ws_bytes, stream) -> int:
+    """Direct call of ``ssd_scan_fwd_varlen`` with integer pointers; returns the status."""
+    return int(load_library().ssd_scan_fwd_varlen(
+        x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, float(dt_min),
+        float(dt_max), int(chunk_size), int(ngroups), init_ptr, out_ptr, final_ptr, seq_ptr,
+        int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(dtype), ws_ptr,
+        int(ws_bytes), stream))
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
 def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.inf),
              chunk_size: int = 128, initial_states=None, return_final_states: bool = False,
-             out=None, final_states=None, workspace=None, timing: Optional[Timing] = None):
+             out=None, final_states=None, workspace=None, timing: Optional[Timing] = None,
+             seq_idx=None):
     """SSD chunked selective-scan forward on the GPU.
 
     x [b, L, H, P], dt [b, L, H], B/C [b, L, G, N], z like x: float32 or
@@ -155,7 +178,9 @@ def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.i
     float32.  Returns out (x's dtype), or (out, final_states) with
     ``return_final_states``.  ``out``, ``final_states`` and ``workspace``
     (uint8) may be given to avoid allocations; ``final_states`` may be the
-    ``initial_states`` tensor itself (in-place continuation)."""
+    ``initial_states`` tensor itself (in-place continuation).  ``seq_idx``
+    [b, L] int32 packs several sequences per row (the state resets where the
+    label changes; ``ssd_scan_fwd_varlen``)."""
     import torch
 
     load_library()
@@ -195,15 +220,30 @@ def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.i
         raise ValueError("z must have x's shape")
     if initial_states is not None and tuple(initial_states.shape) != (b, H, P, N):
         raise ValueError("initial_states must have shape [b, H, P, N]")
+    if seq_idx is not None:
+        if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (b, L):
+            raise ValueError("seq_idx must be int32 of shape [b, L]")
+        if seq_idx.device != dev or not seq_idx.is_contiguous():
+            raise ValueError("seq_idx must be a contiguous tensor on x's device")
+        if timing is not None:
+            raise ValueError("per-stage timing is not offered for seq_idx calls")
 
     if out is None:
         out = torch.empty_like(x)
     if return_final_states and final_states is None:
         final_states = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
-    ws_bytes = workspace_size(b, L, H, P, N, G, chunk_size, dtype)
+    size_fn = workspace_size if seq_idx is None else varlen_workspace_size
+    ws_bytes = size_fn(b, L, H, P, N, G, chunk_size, dtype)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if seq_idx is not None:
+        _check(scan_fwd_varlen_raw(
+            _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+            dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),
+            _ptr(final_states) if return_final_states else None, _ptr(seq_idx), b, L, H, P, N,
+            dtype, _ptr(workspace), workspace.numel(), stream))
+        return (out, final_states) if return_final_states else out
     status = scan_fwd_raw(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
         dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),

@@ -38,8 +38,8 @@ struct Layout {
   int64_t nc = 0;
   bool decode = false;  // seqlen <= kDecodeMaxL: step-by-step kernel, no workspace
   bool fused = false;
-  // staged path
-  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0;
+  // staged path (off_seg: packed-sequence counts, varlen calls only)
+  size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0, off_seg = 0;
   // fused bf16 path
   size_t off_ring = 0, off_flags = 0, off_ctl = 0;
   size_t total = 0;
@@ -61,8 +61,10 @@ bool fused_path(int dtype, int64_t headdim, int64_t dstate) {
 }
 
 // Shape checks shared by the workspace query and the entry point.
+// varlen: the call carries seq_idx (packed sequences); it takes the staged
+// path and its workspace ends with the per-chunk sequence-start counts.
 int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                 int ngroups, int chunk_size, int dtype, Layout* lay) {
+                 int ngroups, int chunk_size, int dtype, bool varlen, Layout* lay) {
   if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
       chunk_size <= 0)
     return SSD_ERR_INVALID_ARG;
@@ -89,7 +91,7 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     lay->total = 0;
     return SSD_OK;
   }
-  if (fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
+  if (!varlen && fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
     const int64_t nblk = ssd::fused_blocks(seqlen);
     int64_t nchain, grid, ringn, flagn;
     if (!mul_ok(batch, nheads, &nchain) || !mul_ok(nchain, nblk, &grid) ||
@@ -114,6 +116,12 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     if (!mul_ok(batch * nc * ngroups, dstate * chunk_size, &btn)) return SSD_ERR_INVALID_ARG;
     lay->total += round_up((size_t)btn * 2);
   }
+  if (varlen) {
+    int64_t segn;
+    if (!mul_ok(batch * nc, chunk_size, &segn)) return SSD_ERR_INVALID_ARG;
+    lay->off_seg = lay->total;
+    lay->total += round_up((size_t)segn * 4);
+  }
   if (batch == 0 || seqlen == 0) lay->total = 0;
   return SSD_OK;
 }
@@ -121,15 +129,18 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
 int validate(const void* x, const void* dt, const float* A, const void* B, const void* C,
              const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
              int chunk_size, int ngroups, const float* initial_states, void* out,
-             float* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
-             int64_t headdim, int64_t dstate, int dtype, void* workspace,
-             size_t workspace_bytes, Layout* lay) {
-  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, lay);
+             float* final_states, const int32_t* seq_idx, bool varlen, int64_t batch,
+             int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+             void* workspace, size_t workspace_bytes, Layout* lay) {
+  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, varlen,
+                        lay);
   if (st != SSD_OK) return st;
   if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return SSD_ERR_INVALID_ARG;
   if (!A) return SSD_ERR_INVALID_ARG;
   const bool nonempty = batch > 0 && seqlen > 0;
   if (nonempty && (!x || !dt || !B || !C || !out)) return SSD_ERR_INVALID_ARG;
+  if (varlen && nonempty && !seq_idx) return SSD_ERR_INVALID_ARG;
+  if (!aligned(seq_idx, 4)) return SSD_ERR_ALIGNMENT;
 
   const size_t es = dtype == SSD_BF16 ? 2 : 4;
   if (!aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4)) return SSD_ERR_ALIGNMENT;
@@ -145,7 +156,8 @@ int validate(const void* x, const void* dt, const float* A, const void* B, const
     const Span so = span(out, nx * (int64_t)es);
     const Span ins[] = {span(x, nx * (int64_t)es), span(dt, batch * seqlen * nheads * (int64_t)es),
                         span(B, nbc * (int64_t)es), span(C, nbc * (int64_t)es),
-                        z ? span(z, nx * (int64_t)es) : Span{0, 0}};
+                        z ? span(z, nx * (int64_t)es) : Span{0, 0},
+                        seq_idx ? span(seq_idx, batch * seqlen * 4) : Span{0, 0}};
     for (const Span& s : ins)
       if (s.hi > s.lo && overlap(so, s)) return SSD_ERR_INVALID_ARG;
     if (final_states && overlap(so, span(final_states, nst * 4))) return SSD_ERR_INVALID_ARG;
@@ -173,13 +185,13 @@ struct ssd_timing {
 static int run(const void* x, const void* dt, const float* A, const void* B, const void* C,
                const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
                int chunk_size, int ngroups, const float* initial_states, void* out,
-               float* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
-               int64_t headdim, int64_t dstate, int dtype, void* workspace,
-               size_t workspace_bytes, hipStream_t stream, ssd_timing* timing) {
+               float* final_states, const int32_t* seq_idx, bool varlen, int64_t batch,
+               int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+               void* workspace, size_t workspace_bytes, hipStream_t stream, ssd_timing* timing) {
   Layout lay;
   int st = validate(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups,
-                    initial_states, out, final_states, batch, seqlen, nheads, headdim, dstate,
-                    dtype, workspace, workspace_bytes, &lay);
+                    initial_states, out, final_states, seq_idx, varlen, batch, seqlen, nheads,
+                    headdim, dstate, dtype, workspace, workspace_bytes, &lay);
   if (st != SSD_OK) return st;
   if (batch == 0) return SSD_OK;
 
@@ -187,6 +199,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = z; p.dt_bias = dt_bias;
   p.dt_min = dt_min; p.dt_max = dt_max; p.init = initial_states; p.out = out;
   p.final_states = final_states;
+  p.seq_idx = varlen ? seq_idx : nullptr;
   p.b = batch; p.L = seqlen; p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups;
   p.Q = chunk_size; p.nc = lay.nc; p.bf16 = dtype == SSD_BF16;
   char* ws = static_cast<char*>(workspace);
@@ -196,6 +209,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.ws_states = staged_ws ? reinterpret_cast<float*>(ws + lay.off_states) : nullptr;
   p.ws_states_in = staged_ws ? reinterpret_cast<float*>(ws + lay.off_states_in) : nullptr;
   p.ws_bt = staged_ws ? reinterpret_cast<uint16_t*>(ws + lay.off_bt) : nullptr;
+  p.ws_seg = staged_ws && varlen ? reinterpret_cast<int32_t*>(ws + lay.off_seg) : nullptr;
   p.fs_ring = lay.fused ? reinterpret_cast<float*>(ws + lay.off_ring) : nullptr;
   p.fs_flags = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_flags) : nullptr;
   p.fs_ctl = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_ctl) : nullptr;
@@ -224,6 +238,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     return SSD_OK;
   }
   const bool bf16k = ssd::use_bf16_kernels(p);
+  if (p.ws_seg && ssd::launch_seq_count(p, stream) != hipSuccess) return SSD_ERR_HIP;
   if (seqlen > 0 && bf16k) {
     // prep (B^T), then the chunk state with dt/cumsum fused in
     if (ssd::launch_bf16_stage(p, stream, 0) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
@@ -259,8 +274,20 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
                  int64_t headdim, int64_t dstate, int dtype, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
-             out, final_states, batch, seqlen, nheads, headdim, dstate, dtype, workspace,
-             workspace_bytes, stream, nullptr);
+             out, final_states, nullptr, false, batch, seqlen, nheads, headdim, dstate, dtype,
+             workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssd_scan_fwd_varlen(const void* x, const void* dt, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* dt_bias,
+                        float dt_min, float dt_max, int chunk_size, int ngroups,
+                        const float* initial_states, void* out, float* final_states,
+                        const int32_t* seq_idx, int64_t batch, int64_t seqlen, int64_t nheads,
+                        int64_t headdim, int64_t dstate, int dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
+             out, final_states, seq_idx, true, batch, seqlen, nheads, headdim, dstate, dtype,
+             workspace, workspace_bytes, stream, nullptr);
 }
 
 int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
@@ -272,16 +299,26 @@ int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void
                        hipStream_t stream, ssd_timing* timing) {
   if (!timing) return SSD_ERR_INVALID_ARG;
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
-             out, final_states, batch, seqlen, nheads, headdim, dstate, dtype, workspace,
-             workspace_bytes, stream, timing);
+             out, final_states, nullptr, false, batch, seqlen, nheads, headdim, dstate, dtype,
+             workspace, workspace_bytes, stream, timing);
 }
 
 size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
                                    int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
                                    int dtype) {
   Layout lay;
-  if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, &lay) !=
-      SSD_OK)
+  if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
+                   &lay) != SSD_OK)
+    return 0;
+  return lay.total;
+}
+
+size_t ssd_scan_fwd_varlen_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                          int64_t headdim, int64_t dstate, int ngroups,
+                                          int chunk_size, int dtype) {
+  Layout lay;
+  if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, true,
+                   &lay) != SSD_OK)
     return 0;
   return lay.total;
 }

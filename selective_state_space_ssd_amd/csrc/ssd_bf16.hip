@@ -17,6 +17,10 @@
 // single bf16 rounding of the entering state or of the masked C.B^T values,
 // outputs of N(0,1) inputs at dstate 128 miss the bf16 bar of 2e-2 (1 + |y|)
 // by up to 2x.  All sums are fp32 and the state passing stays fp32.
+//
+// Packed sequences (seq_idx): ws_seg masks the decay-weighted B^T (steps of
+// the chunk's last sequence only), the state part (steps of the chunk's first
+// sequence only) and the masked C.B^T (pairs of one sequence only).
 #include "ssd_bf16_tiles.h"
 #include "ssd_dt.h"
 #include "ssd_kernels.h"
@@ -73,8 +77,8 @@ template <int Q, int N>
 __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ bt, const bf16_t* __restrict__ dt_raw,
     const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
-    float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states, int64_t L,
-    int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+    float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states,
+    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
   constexpr int NPT = N == 128 ? 2 : 1;  // p-halves per wave
   __shared__ bf16_t x_lds[Q * kXLD];
@@ -92,8 +96,14 @@ __global__ __launch_bounds__(256) void chunk_state_bf16_kernel(
     float dtv[Q / kWave], cum[Q / kWave], cum_last;
     wave_dt_cumsum<bf16_t, Q>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c, h,
                               L, H, nc, ws_dt, ws_cum, dtv, cum, &cum_last);
+    // packed sequences: only the chunk's last sequence reaches its end state
+    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
 #pragma unroll
-    for (int k = 0; k < Q / kWave; ++k) w_lds[lane * (Q / kWave) + k] = __expf(cum_last - cum[k]) * dtv[k];
+    for (int k = 0; k < Q / kWave; ++k) {
+      const int t = lane * (Q / kWave) + k;
+      const bool keep = !sc || sc[t] == sc[Q - 1];
+      w_lds[t] = keep ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
+    }
   }
   stage_x_tile<Q>(x_lds, x + ((b * L + t0) * H + h) * kP, H * kP, last);
   __syncthreads();
@@ -154,12 +164,13 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const float* __restrict__ Dv, const bf16_t* __restrict__ z, const float* __restrict__ ws_dt,
     const float* __restrict__ ws_cum, const float* __restrict__ states_in, bf16_t* __restrict__ out,
-    int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   constexpr int NT = Q / 32, NS = NT / 4, KS = N / 16;
   static_assert(NT == 4 || NT == 8, "chunk 128 or 256");
   __shared__ bf16_t x_lds[Q * kXLD];
   __shared__ float cum_lds[Q];  // log2 units
   __shared__ float dt_lds[Q];
+  __shared__ int32_t seg_lds[Q];  // sequence starts counted from the chunk start (0: no seq_idx)
 
   const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*H + h)
   const int64_t h = u % H, c = (u / H) % nc, b = u / (H * nc);
@@ -176,6 +187,7 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
     for (int t = tid; t < Q; t += 256) {
       cum_lds[t] = ws_cum[dc + t] * kLog2e;
       dt_lds[t] = ws_dt[dc + t];
+      seg_lds[t] = seg ? seg[(b * nc + c) * Q + t] : 0;
     }
   }
   __syncthreads();
@@ -215,15 +227,18 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
         acc[pt] = mfma32x32x16(creg[ks], hlo, acc[pt]);
       }
     }
-    // 2. decay from the chunk start, rows 32 ti + 8 (r/4) + 4 kk + r%4
+    // 2. decay from the chunk start, rows 32 ti + 8 (r/4) + 4 kk + r%4; with
+    // packed sequences the entering state reaches only the first one
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float e = exp2f(cum_lds[32 * ti + 8 * (r / 4) + 4 * kk + (r % 4)]);
+      const int tr = 32 * ti + 8 * (r / 4) + 4 * kk + (r % 4);
+      const float e = seg_lds[tr] == 0 ? exp2f(cum_lds[tr]) : 0.0f;
       acc[0][r] *= e;
       acc[1][r] *= e;
     }
-    // 3. in-chunk part
+    // 3. in-chunk part (steps of different packed sequences do not interact)
     const float ct = cum_lds[32 * ti + i];
+    const int kt = seg_lds[32 * ti + i];
     for (int si = 0; si <= ti; ++si) {
       f16x gt = zero16();
       {
@@ -244,7 +259,7 @@ __global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(
           const int r = 8 * m + e;
           const int sl = 8 * (r / 4) + 4 * kk + (r % 4);  // s within the tile
           const int s = 32 * si + sl;
-          float v = gt[r] * exp2f(ct - cum_lds[s]) * dt_lds[s];
+          float v = seg_lds[s] == kt ? gt[r] * exp2f(ct - cum_lds[s]) * dt_lds[s] : 0.0f;
           if (si == ti) v = (sl < i) ? v : (sl == i ? v + Dh : 0.0f);
           mv[e] = v;
         }
@@ -303,21 +318,22 @@ static void launch_bf16_qn(const Problem& p, hipStream_t s, int stage) {
     const int64_t nunits = p.b * p.nc * p.H;
     hipLaunchKernelGGL((chunk_state_bf16_kernel<Q, N>), dim3((unsigned)nunits), dim3(256), 0, s, x,
                        p.ws_bt, static_cast<const bf16_t*>(p.dt), p.A, p.dt_bias, p.dt_min,
-                       p.dt_max, p.ws_dt, p.ws_cum, p.ws_states, p.L, p.H, p.G, p.nc, nunits);
+                       p.dt_max, p.ws_dt, p.ws_cum, p.ws_states, p.ws_seg, p.L, p.H, p.G, p.nc,
+                       nunits);
   } else {
     const int64_t nunits = p.b * p.nc * p.H;
     if (p.z)
       hipLaunchKernelGGL((chunk_scan_bf16_kernel<Q, N, true>), dim3((unsigned)nunits), dim3(256),
                          0, s, x, static_cast<const bf16_t*>(p.B),
                          static_cast<const bf16_t*>(p.C), p.D, static_cast<const bf16_t*>(p.z),
-                         p.ws_dt, p.ws_cum, p.ws_states_in, static_cast<bf16_t*>(p.out), p.L, p.H,
-                         p.G, p.nc, nunits);
+                         p.ws_dt, p.ws_cum, p.ws_states_in, static_cast<bf16_t*>(p.out),
+                         p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
     else
       hipLaunchKernelGGL((chunk_scan_bf16_kernel<Q, N, false>), dim3((unsigned)nunits), dim3(256),
                          0, s, x, static_cast<const bf16_t*>(p.B),
                          static_cast<const bf16_t*>(p.C), p.D, static_cast<const bf16_t*>(p.z),
-                         p.ws_dt, p.ws_cum, p.ws_states_in, static_cast<bf16_t*>(p.out), p.L, p.H,
-                         p.G, p.nc, nunits);
+                         p.ws_dt, p.ws_cum, p.ws_states_in, static_cast<bf16_t*>(p.out),
+                         p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
   }
 }
 

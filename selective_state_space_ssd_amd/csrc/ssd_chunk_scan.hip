@@ -25,6 +25,10 @@
 // Only pairwise decays exp(cum_t - cum_s) with s <= t are formed, and they are
 // at most 1, so nothing overflows however negative the running sums get.
 //
+// Packed sequences (seq_idx): with k_t the count of sequence starts from the
+// chunk start to t (ws_seg), the state part keeps rows with k_t = 0 and the
+// in-chunk part keeps pairs with k_s = k_t (no start in (s, t]).
+//
 // Lane layout: in the accumulator, register r of lane l holds row
 // t = 16*tb + 4*(l/16) + r and column p = 4*(l%16) + j of p-block j, so a lane
 // stores four consecutive p of one row.  The state is staged with its rows
@@ -40,7 +44,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ Dv, const T* __restrict__ z, const float* __restrict__ ws_dt,
     const float* __restrict__ ws_cum, const float* __restrict__ states_in, T* __restrict__ out,
-    int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   constexpr int P = 64;
   constexpr int NK = N / 4;      // MFMA k-steps over n (4 per step)
   constexpr int HS = N + 4;      // padded row stride of the staged state
@@ -49,6 +53,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
   __shared__ float h_lds[P * HS];
   __shared__ float cum_lds[Q];
   __shared__ float dt_lds[Q];
+  __shared__ int32_t seg_lds[Q];  // 0 everywhere without seq_idx
 
   const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*H + h)
   const int64_t h = u % H;
@@ -83,6 +88,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     if (tid < Q) {
       cum_lds[tid] = ws_cum[dc + tid];
       dt_lds[tid] = ws_dt[dc + tid];
+      seg_lds[tid] = seg ? seg[(b * nc + c) * Q + tid] : 0;
     }
   }
   __syncthreads();
@@ -135,7 +141,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     // 2. decay from the chunk start
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = __expf(cum_lds[16 * tb + 4 * lk + r]);
+      const int tr = 16 * tb + 4 * lk + r;
+      const float e = seg_lds[tr] == 0 ? __expf(cum_lds[tr]) : 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[j][r] *= e;
     }
@@ -143,6 +150,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
     // 3. in-chunk part, causal s-blocks
     const int tcol = 16 * tb + li;
     const float cum_t = cum_lds[tcol];
+    const int k_t = seg_lds[tcol];
     for (int sb = 0; sb <= tb; ++sb) {
       float breg[NK];
       {
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
       for (int r = 0; r < 4; ++r) {
         const int srow = 16 * sb + 4 * lk + r;
         const float wgt = __expf(cum_t - cum_lds[srow]) * dt_lds[srow];
-        const float mv = (srow <= tcol) ? gacc[r] * wgt : 0.0f;
+        const float mv = (srow <= tcol && seg_lds[srow] == k_t) ? gacc[r] * wgt : 0.0f;
         const f4 xv = *reinterpret_cast<const f4*>(&x_lds[srow * P + 4 * li]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x4(mv, xv[j], acc[j]);
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ Dv, const T* __restrict__ z, const float* __restrict__ ws_dt,
     const float* __restrict__ ws_cum, const float* __restrict__ states_in, T* __restrict__ out,
-    int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   constexpr int P = 64, NT = Q / 32, CS = N + 4, NG = NT * (NT + 1) / 2, KQ = N / 8;
   constexpr int NW = 8;                   // waves: two per head
   constexpr int GW = (NG + NW - 1) / NW;  // G tiles per wave, at most
@@ -246,8 +254,10 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   __shared__ float bg_lds[BGS];  // B tile, then the G^T tiles
   __shared__ float cum_lds[4][Q];  // running sums in log2 units (cum * log2 e)
   __shared__ float dt_lds[4][Q];
-  // u_s = 2^(cum_e - cum_s) dt_s, e = last step of s's 32-step tile (<= dt_s)
+  // u_s = 2^(cum_e - cum_s) dt_s, e = last step of s's 32-step tile (<= dt_s);
+  // 0 when a packed sequence starts in (s, e]
   __shared__ __align__(16) float u_lds[4][Q];
+  __shared__ __align__(16) int32_t seg_lds[Q];  // sequence starts from the chunk start (0: no seq_idx)
 
   const int64_t HQ = H / 4;
   const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*HQ + hq)
@@ -282,14 +292,17 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
       *reinterpret_cast<f4*>(&c_lds[row * CS + col]) = cv;
       *reinterpret_cast<f4*>(&bg_lds[row * CS + col]) = bv;
     }
+    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
     for (int k = tid; k < 4 * Q; k += 64 * NW) {
       const int w = k / Q, t = k % Q;
       const int64_t o = ((b * H + h0 + w) * nc + c) * Q + t;
       const float cum2 = ws_cum[o] * kLog2e, dtv = ws_dt[o];
       const float cend2 = ws_cum[o - t + (t | 31)] * kLog2e;
+      const bool keep = !sc || sc[t] == sc[t | 31];
       cum_lds[w][t] = cum2;
       dt_lds[w][t] = dtv;
-      u_lds[w][t] = fast_exp2(cend2 - cum2) * dtv;
+      u_lds[w][t] = keep ? fast_exp2(cend2 - cum2) * dtv : 0.0f;
+      if (w == 0) seg_lds[t] = sc ? sc[t] : 0;
     }
   }
   __syncthreads();
@@ -373,11 +386,15 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   const float* cumw = cum_lds[slot];
   const float* dtw = dt_lds[slot];
   const float* uw = u_lds[slot];
-  float ct[NS], ect[NS];  // cum_t (log2 units) and exp(cum_t) of this lane's A-operand row
+  // cum_t (log2 units) and exp(cum_t) of this lane's A-operand row; with
+  // packed sequences the entering state reaches only the chunk's first one
+  float ct[NS], ect[NS];
+  int kt[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     ct[j] = cumw[32 * own(j) + i];
-    ect[j] = fast_exp2(ct[j]);
+    kt[j] = seg_lds[32 * own(j) + i];
+    ect[j] = kt[j] == 0 ? fast_exp2(ct[j]) : 0.0f;
   }
 
   // ---- 2. state part: acc = (exp(cum_t) C) . H_in^T ---------------------------
@@ -425,13 +442,18 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     // the diagonal tile, plus D at s == t.  Below the diagonal the decay is
     // split at the s-tile's last step e: 2^(ct - ce) * u_s, both factors <= 1,
     // so one exp per lane and tile; the diagonal tile keeps the direct form.
+    // A start in (s, t] is one in (s, e] or in (e, t] (e = 32 si + 31 lies
+    // between them), so the packed-sequence mask splits like the decay: u_s
+    // carries the first half, rs the second.
     float rs[NS];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) rs[j] = fast_exp2(ct[j] - cumw[32 * si + 31]);
+    for (int j = 0; j < NS; ++j)
+      rs[j] = kt[j] == seg_lds[32 * si + 31] ? fast_exp2(ct[j] - cumw[32 * si + 31]) : 0.0f;
     auto masked = [&](int R, float (&mv)[NS][4]) {
       const f4 cs4 = *reinterpret_cast<const f4*>(&cumw[32 * si + 8 * R + 4 * kk]);
       const f4 ds4 = *reinterpret_cast<const f4*>(&dtw[32 * si + 8 * R + 4 * kk]);
       const f4 us4 = *reinterpret_cast<const f4*>(&uw[32 * si + 8 * R + 4 * kk]);
+      const int4 ks4 = *reinterpret_cast<const int4*>(&seg_lds[32 * si + 8 * R + 4 * kk]);
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int ti = own(j) >= si ? own(j) : si;  // tiles below si are not used
@@ -442,7 +464,8 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
           for (int e = 0; e < 4; ++e) {
             const float v = gv[e] * fast_exp2(ct[j] - cs4[e]) * ds4[e];
             const int sl = 8 * R + 4 * kk + e;  // s within the tile
-            mv[j][e] = (sl < i) ? v : (sl == i ? v + Dh : 0.0f);
+            const int ks = e == 0 ? ks4.x : e == 1 ? ks4.y : e == 2 ? ks4.z : ks4.w;
+            mv[j][e] = (sl < i) ? (ks == kt[j] ? v : 0.0f) : (sl == i ? v + Dh : 0.0f);
           }
         } else {
 #pragma unroll
@@ -522,13 +545,13 @@ static void launch_qn(const Problem& p, hipStream_t s) {
                            dim3(512), 0, s, static_cast<const T*>(p.x),
                            static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,
                            static_cast<const T*>(p.z), p.ws_dt, p.ws_cum, p.ws_states_in,
-                           static_cast<T*>(p.out), p.L, p.H, p.G, p.nc, nunits);
+                           static_cast<T*>(p.out), p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
       else
         hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, false>), dim3((unsigned)nunits),
                            dim3(512), 0, s, static_cast<const T*>(p.x),
                            static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,
                            static_cast<const T*>(p.z), p.ws_dt, p.ws_cum, p.ws_states_in,
-                           static_cast<T*>(p.out), p.L, p.H, p.G, p.nc, nunits);
+                           static_cast<T*>(p.out), p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
       return;
     }
   }
@@ -536,8 +559,8 @@ static void launch_qn(const Problem& p, hipStream_t s) {
   hipLaunchKernelGGL((chunk_scan_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(256), 0, s,
                      static_cast<const T*>(p.x), static_cast<const T*>(p.B),
                      static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.ws_dt,
-                     p.ws_cum, p.ws_states_in, static_cast<T*>(p.out), p.L, p.H, p.G, p.nc,
-                     nunits);
+                     p.ws_cum, p.ws_states_in, static_cast<T*>(p.out), p.ws_seg, p.L, p.H, p.G,
+                     p.nc, nunits);
 }
 
 template <typename T, int Q>

@@ -8,6 +8,10 @@
 // contraction index is time.  Results go to the workspace in the tiled state
 // layout (ssd_device.h).
 //
+// Packed sequences (seq_idx): only the steps of the chunk's last sequence
+// reach the chunk's end state, so w_t = 0 for steps whose sequence-start count
+// (ws_seg) differs from the chunk's last one.
+//
 // Two kernels:
 //  * chunk_state_wave_kernel (N = 64 or 128): WPH waves per (chunk, head)
 //    (two as launched), 8 waves per workgroup.  The first wave of a head
@@ -33,8 +37,8 @@ template <typename T, int Q, int N, int WPH>
 __global__ __launch_bounds__(512) void chunk_state_wave_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ dt_raw,
     const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
-    float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states, int64_t L,
-    int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+    float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states,
+    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   // WPH waves per head, each owning NTW n-tiles (both p-halves); HPW heads per
   // workgroup of 8 waves
   constexpr int P = 64, NTN = N / 32, NTW = NTN / WPH, HPW = 8 / WPH, E = Q / kWave;
@@ -53,10 +57,12 @@ __global__ __launch_bounds__(512) void chunk_state_wave_kernel(
     float dtv[E], cum[E], cum_last;
     wave_dt_cumsum<T, Q>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c, h, L,
                          H, nc, ws_dt, ws_cum, dtv, cum, &cum_last);
+    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
 #pragma unroll
     for (int k = 0; k < E; ++k) {
       const int t = lane * E + k;
-      w_lds[slot][t & 1][t >> 1] = __expf(cum_last - cum[k]) * dtv[k];
+      const bool keep = !sc || sc[t] == sc[Q - 1];
+      w_lds[slot][t & 1][t >> 1] = keep ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
     }
   }
   __syncthreads();
@@ -165,8 +171,8 @@ struct StateTile {
 template <typename T, int Q, int N>
 __global__ __launch_bounds__(256) void chunk_state_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ ws_dt,
-    const float* __restrict__ ws_cum, float* __restrict__ states, int64_t L, int64_t H,
-    int64_t G, int64_t nc, int64_t nunits) {
+    const float* __restrict__ ws_cum, float* __restrict__ states, const int32_t* __restrict__ seg,
+    int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   constexpr int P = 64;
   using Tl = StateTile<N>;
   constexpr int MB = Tl::MB, NB = Tl::NB, WP = Tl::WP;
@@ -182,7 +188,9 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(
   const int64_t dc = ((b * H + h) * nc + c) * Q;
   if (tid < Q) {
     const float cum_last = ws_cum[dc + Q - 1];
-    w_lds[tid] = __expf(cum_last - ws_cum[dc + tid]) * ws_dt[dc + tid];
+    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
+    const bool keep = !sc || sc[tid] == sc[Q - 1];
+    w_lds[tid] = keep ? __expf(cum_last - ws_cum[dc + tid]) * ws_dt[dc + tid] : 0.0f;
   }
   __syncthreads();
 
@@ -258,12 +266,12 @@ static void launch_qn(const Problem& p, hipStream_t s) {
     hipLaunchKernelGGL((chunk_state_wave_kernel<T, Q, N, WPH>), dim3((unsigned)nunits), dim3(512), 0,
                        s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
                        static_cast<const T*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.ws_dt,
-                       p.ws_cum, p.ws_states, p.L, p.H, p.G, p.nc, nunits);
+                       p.ws_cum, p.ws_states, p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
   } else {
     const int64_t nunits = p.b * p.nc * p.H;
     hipLaunchKernelGGL((chunk_state_kernel<T, Q, N>), dim3((unsigned)nunits), dim3(256), 0, s,
                        static_cast<const T*>(p.x), static_cast<const T*>(p.B), p.ws_dt, p.ws_cum,
-                       p.ws_states, p.L, p.H, p.G, p.nc, nunits);
+                       p.ws_states, p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
   }
 }
 

@@ -12,6 +12,9 @@
 //   h_t   = exp(dt_t A_h) h_{t-1} + dt_t x_t (outer) B_t
 //   y_t   = C_t . h_t + D_h x_t,   out_t = y_t silu(z_t)
 //
+// Packed sequences (seq_idx): where the label changes between steps t-1 and
+// t a new sequence starts and the state is reset to zero before step t.
+//
 // 256 threads: thread k owns row p = k / 4 and columns n in
 // [(k % 4) N/4, (k % 4 + 1) N/4) of the state; the C . h_t reduction over n
 // is four partial sums combined with two lane shuffles (the four threads of a
@@ -31,7 +34,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ x, const T* __restrict__ dt_raw, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dv,
     const T* __restrict__ z, const float* __restrict__ dt_bias, float dt_min, float dt_max,
-    const float* init, T* __restrict__ out, float* fin, int64_t L, int64_t H, int64_t G) {
+    const float* init, T* __restrict__ out, float* fin, const int32_t* __restrict__ seq,
+    int64_t L, int64_t H, int64_t G) {
   constexpr int NT = N / 4;  // state columns per thread
   const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
   const int64_t g = h / (H / G);
@@ -53,6 +57,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const float a_h = A[h], bias = dt_bias ? dt_bias[h] : 0.0f, Dh = Dv ? Dv[h] : 0.0f;
 
   for (int64_t t = 0; t < L; ++t) {
+    if (seq && t > 0 && seq[b * L + t] != seq[b * L + t - 1]) {  // uniform per workgroup
+#pragma unroll
+      for (int j = 0; j < NT; ++j) s[j] = 0.0f;
+    }
     float d = softplus(to_f32(dt_raw[(b * L + t) * H + h]) + bias);
     d = d < dt_min ? dt_min : d;  // comparisons, so that NaN stays NaN
     d = d > dt_max ? dt_max : d;
@@ -98,8 +106,8 @@ static void launch_decode_t(const Problem& p, hipStream_t s) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const T*>(p.x),
                        static_cast<const T*>(p.dt), p.A, static_cast<const T*>(p.B),
                        static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.dt_bias,
-                       p.dt_min, p.dt_max, p.init, static_cast<T*>(p.out), p.final_states, p.L,
-                       p.H, p.G);
+                       p.dt_min, p.dt_max, p.init, static_cast<T*>(p.out), p.final_states,
+                       p.seq_idx, p.L, p.H, p.G);
   };
   switch (p.N) {
     case 16: go(decode_kernel<T, 16>); break;

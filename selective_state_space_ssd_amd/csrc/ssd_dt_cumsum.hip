@@ -23,6 +23,63 @@ __global__ __launch_bounds__(256) void dt_cumsum_kernel(const T* __restrict__ dt
                        nc, ws_dt, ws_cum, dtv, cum, &last);
 }
 
+// Packed sequences (seq_idx): per chunk, the running count of sequence starts.
+// A start is a step whose label differs from the previous step's (mamba issue
+// #647's repro passes seq_idx to the chunked scan; the state does not flow
+// across a start).  One wave per (batch, chunk); lane l owns steps
+// l*E .. l*E+E-1 and a wave-wide inclusive scan adds the lanes' counts.  The
+// kernels mask with these counts: steps s <= t of one chunk interact only if
+// their counts are equal, the entering state reaches step t only if its count
+// is 0, and a chunk whose last count is non-zero drops the carried state.
+template <int Q>
+__global__ __launch_bounds__(256) void seq_count_kernel(const int32_t* __restrict__ seq,
+                                                       int32_t* __restrict__ ws_seg, int64_t L,
+                                                       int64_t nc, int64_t nunits) {
+  constexpr int E = Q / kWave;
+  const int64_t u = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // b*nc + c
+  if (u >= nunits) return;  // whole wave leaves together; no barrier follows
+  const int64_t c = u % nc, b = u / nc;
+  const int lane = threadIdx.x % kWave;
+  int run[E];
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t t = c * Q + (int64_t)lane * E + i;
+    if (t >= 1 && t < L) total += seq[b * L + t] != seq[b * L + t - 1];
+    run[i] = total;
+  }
+  int incl = total;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  const int base = incl - total;
+  int32_t* dst = ws_seg + u * Q + lane * E;
+#pragma unroll
+  for (int i = 0; i < E; ++i) dst[i] = base + run[i];
+}
+
+hipError_t launch_seq_count(const Problem& p, hipStream_t s) {
+  const int64_t nunits = p.b * p.nc;
+  const dim3 grid((unsigned)((nunits + 3) / 4));
+  switch (p.Q) {
+    case 64:
+      hipLaunchKernelGGL((seq_count_kernel<64>), grid, dim3(256), 0, s, p.seq_idx, p.ws_seg, p.L,
+                         p.nc, nunits);
+      break;
+    case 128:
+      hipLaunchKernelGGL((seq_count_kernel<128>), grid, dim3(256), 0, s, p.seq_idx, p.ws_seg,
+                         p.L, p.nc, nunits);
+      break;
+    case 256:
+      hipLaunchKernelGGL((seq_count_kernel<256>), grid, dim3(256), 0, s, p.seq_idx, p.ws_seg,
+                         p.L, p.nc, nunits);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int Q>
 static void launch_q(const Problem& p, hipStream_t s) {
   dim3 grid((unsigned)((p.H + 3) / 4), (unsigned)p.nc, (unsigned)p.b);

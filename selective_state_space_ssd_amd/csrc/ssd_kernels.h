@@ -22,6 +22,7 @@ struct Problem {
   const float* init;     // may be null
   void* out;
   float* final_states;   // may be null
+  const int32_t* seq_idx;  // [b, L] labels of packed sequences; null: one per row
   int64_t b, L, H, P, N, G, Q, nc;
   bool bf16;
   // workspace regions (float32)
@@ -30,6 +31,8 @@ struct Problem {
   float* ws_states;      // [b, nc, H] tiled P x N blocks: chunk-local states
   float* ws_states_in;   // [b, nc, H] tiled P x N blocks: state entering each chunk
   uint16_t* ws_bt;       // [b, nc, G] blocks of N x Q bf16: B^T per chunk (bf16 kernels only)
+  int32_t* ws_seg;       // [b, nc, Q] sequence starts counted from the chunk start
+                         // (seq_idx only; null otherwise)
   // fused bf16 kernel
   float* fs_ring;        // [b*H chains][2 slots] tiled P x N states
   unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
@@ -39,6 +42,9 @@ struct Problem {
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().
 hipError_t launch_dt_cumsum(const Problem& p, hipStream_t stream);
+// Packed sequences: ws_seg[b][c][q] = number of steps t in [c*Q, c*Q + q]
+// (t >= 1, t < L) whose seq_idx differs from step t-1's; constant past L.
+hipError_t launch_seq_count(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_passing(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);

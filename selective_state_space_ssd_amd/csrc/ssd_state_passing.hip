@@ -9,6 +9,9 @@
 // sequentially over chunks and in parallel over (batch, head, p, n); each
 // thread carries four consecutive state elements (one float4 of the tiled
 // state layout) in registers and keeps four chunks of loads in flight.
+// Packed sequences (seq_idx): a chunk in which a new sequence starts drops the
+// carried state (decay 0); its own contribution S_c already holds only the
+// steps of its last sequence.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
 
@@ -17,7 +20,8 @@ namespace ssd {
 template <int N>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float* __restrict__ states, const float* __restrict__ ws_cum, const float* init,
-    float* __restrict__ states_in, float* final_states, int64_t H, int64_t nc, int64_t Q) {
+    float* __restrict__ states_in, float* final_states, const int32_t* __restrict__ seg,
+    int64_t H, int64_t nc, int64_t Q) {
   constexpr int PN = 64 * N;
   constexpr int U = 4;  // chunks in flight
   const int64_t h = blockIdx.y, b = blockIdx.z;
@@ -35,10 +39,12 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
   for (int64_t c0 = 0; c0 < nc; c0 += U) {
     f4 s[U];
     float decay[U];
+    bool carry[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       if (c0 + j < nc) {
         s[j] = ld4(src + (c0 + j) * cstride);
+        carry[j] = !seg || seg[(b * nc + c0 + j) * Q + Q - 1] == 0;
         decay[j] = __expf(cum[(c0 + j) * Q]);
       }
     }
@@ -46,7 +52,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     for (int j = 0; j < U; ++j) {
       if (c0 + j < nc) {
         st4(dst + (c0 + j) * cstride, hs);
-        hs = decay[j] * hs + s[j];
+        hs = carry[j] ? decay[j] * hs + s[j] : s[j];
       }
     }
   }
@@ -57,7 +63,7 @@ template <int N>
 static void launch_n(const Problem& p, hipStream_t s) {
   dim3 grid((unsigned)((64 * N / 4 + 255) / 256), (unsigned)p.H, (unsigned)p.b);
   hipLaunchKernelGGL((state_passing_kernel<N>), grid, dim3(256), 0, s, p.ws_states, p.ws_cum,
-                     p.init, p.ws_states_in, p.final_states, p.H, p.nc, p.Q);
+                     p.init, p.ws_states_in, p.final_states, p.ws_seg, p.H, p.nc, p.Q);
 }
 
 hipError_t launch_state_passing(const Problem& p, hipStream_t stream) {

@@ -87,3 +87,33 @@ def compare(name, got, ref, tol, mask=None):
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     assert np.all(scaled <= tol), stats
     return stats
+
+
+def state_tile_offsets(N):
+    """offs[p, n] = float offset of state element (p, n) in a tiled block
+    (the workspace layout documented in include/ssd.h; headdim 64)."""
+    p = np.arange(64)[:, None]
+    n = np.arange(N)[None, :]
+    half = N // 2
+    k, q, e = n // half, (n % half) // 4, n % 4
+    return (((q * 2 + p % 2) * 64) + 32 * k + p // 2) * 4 + e
+
+
+def ws_regions(ws, b, L, H, P, N, Q):
+    """The staged path's intermediates in a workspace (layout of include/ssd.h),
+    states untiled to [b, nc, H, P, N]."""
+    nc = -(-L // Q)
+    r = lambda v: (v + 255) // 256 * 256
+    dtn, stn = b * H * nc * Q, b * nc * H * P * N
+    f = ws.view(torch.float32)
+    o_cum = r(dtn * 4) // 4
+    o_st = o_cum + r(dtn * 4) // 4
+    o_in = o_st + r(stn * 4) // 4
+    offs = torch.from_numpy(state_tile_offsets(N).reshape(-1)).to(ws.device)
+
+    def dense(block):
+        return block.view(b, nc, H, P * N)[..., offs].view(b, nc, H, P, N)
+
+    return {"dt": f[:dtn].view(b, H, nc, Q), "cum": f[o_cum:o_cum + dtn].view(b, H, nc, Q),
+            "chunk_states": dense(f[o_st:o_st + stn]),
+            "states_in": dense(f[o_in:o_in + stn])}

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("ssd_scan_fwd", "ssd_scan_fwd_workspace_size", "ssd_status_string",
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
-                 "ssd_timing_read", "ssd_timing_destroy", "ssd_set_option", "ssd_get_option"):
+                 "ssd_timing_read", "ssd_timing_destroy", "ssd_set_option", "ssd_get_option",
+                 "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size"):
         assert want in names
 
 
@@ -109,6 +110,23 @@ def test_workspace_size_fused_bf16():
         else:
             want = staged  # dstate 16/32: staged
         assert _ws(b, L, H, P, N, G, Q, 1) == want
+
+
+def test_workspace_size_varlen():
+    """Packed-sequence calls: the staged layout (also for bf16 shapes the fused
+    path would take) plus [b, nc, Q] int32 sequence-start counts; nothing for
+    seqlen <= 16."""
+    for (b, L, H, P, N, G, Q) in SIZES:
+        nc = math.ceil(L / Q)
+        staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+        for dt in (0, 1):
+            got = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, dt)
+            if L <= DECODE_MAX_L:
+                assert got == 0
+                continue
+            bt = _r(b * nc * G * N * Q * 2) if (dt and Q in (128, 256) and N in (64, 128)) else 0
+            assert got == staged + bt + _r(b * nc * Q * 4)
+    assert ssd.varlen_workspace_size(2, 100, 4, 64, 16, 3, 64, 0) == 0  # rejected shapes
 
 
 def test_options():
@@ -201,6 +219,33 @@ CASES = [
 def test_rejected_before_launch(desc, changes, want):
     assert want != OK
     assert call(**changes) == want
+
+
+def call_varlen(seq=0xD0000000, **changes):
+    a = dict(BASE)
+    a.update(changes)
+    return ssd.scan_fwd_varlen_raw(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                   a["dt_bias"], a["dt_min"], a["dt_max"], a["chunk_size"],
+                                   a["ngroups"], a["init"], a["out"], a["final"], seq,
+                                   a["batch"], a["seqlen"], a["nheads"], a["headdim"],
+                                   a["dstate"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+VARLEN_CASES = [
+    ("seq_idx missing", dict(seq=None), INVALID),
+    ("seq_idx misaligned", dict(seq=0xD0000002), ALIGN),
+    ("out overlaps seq_idx", dict(seq=0xA0000000 + 64), INVALID),
+    ("shape checks as ssd_scan_fwd", dict(ngroups=3), INVALID),
+    ("valid, stops at workspace", dict(), WORKSPACE),
+    ("bf16 fused shape still needs the staged workspace", dict(dtype=1, dstate=128,
+     chunk_size=128, ws=0xC0000000, ws_bytes=ssd.workspace_size(1, 100, 4, 64, 128, 1, 128, 1)),
+     WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("desc,changes,want", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+def test_varlen_rejected_before_launch(desc, changes, want):
+    assert call_varlen(**changes) == want
 
 
 def test_empty_batch_is_a_no_op():

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, bf16_path, compare, log, np64, paths_for, run_gpu, upload
+from parity import TOL, bf16_path, compare, log, np64, paths_for, run_gpu, upload, ws_regions
 from ssd_workloads import WORKLOADS, Workload, make_inputs, small
 
 pytestmark = pytest.mark.gpu
@@ -65,34 +65,6 @@ def test_small_ragged(dtype, Q, N, H, G):
         compare(f"final {path}", np64(fin), rfin, TOL[dtype])
 
 
-def _state_tile_offsets(N):
-    """offs[p, n] = float offset of state element (p, n) in a tiled block
-    (the workspace layout documented in include/ssd.h; headdim 64)."""
-    p = np.arange(64)[:, None]
-    n = np.arange(N)[None, :]
-    half = N // 2
-    k, q, e = n // half, (n % half) // 4, n % 4
-    return (((q * 2 + p % 2) * 64) + 32 * k + p // 2) * 4 + e
-
-
-def _ws_regions(ws, b, L, H, P, N, Q):
-    nc = -(-L // Q)
-    r = lambda v: (v + 255) // 256 * 256
-    dtn, stn = b * H * nc * Q, b * nc * H * P * N
-    f = ws.view(torch.float32)
-    o_cum = r(dtn * 4) // 4
-    o_st = o_cum + r(dtn * 4) // 4
-    o_in = o_st + r(stn * 4) // 4
-    offs = torch.from_numpy(_state_tile_offsets(N).reshape(-1)).to(ws.device)
-
-    def dense(block):
-        return block.view(b, nc, H, P * N)[..., offs].view(b, nc, H, P, N)
-
-    return {"dt": f[:dtn].view(b, H, nc, Q), "cum": f[o_cum:o_cum + dtn].view(b, H, nc, Q),
-            "chunk_states": dense(f[o_st:o_st + stn]),
-            "states_in": dense(f[o_in:o_in + stn])}
-
-
 INTER = [("f32", 128, 128), ("bf16", 128, 128), ("f32", 64, 16), ("bf16", 256, 32),
          ("f32", 256, 64)]
 
@@ -111,7 +83,7 @@ def test_stage_intermediates(dtype, Q, N):
         ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0),
                          dtype=torch.uint8, device=t["x"].device)
         run_gpu(t, Q, init=t["initial_states"], workspace=ws)
-    got = {k: np64(v) for k, v in _ws_regions(ws, b, L, H, P, N, Q).items()}
+    got = {k: np64(v) for k, v in ws_regions(ws, b, L, H, P, N, Q).items()}
     ref = oracle.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
                                      dt_bias=inp["dt_bias"], initial_states=inp["initial_states"])
     valid = np.zeros((b, H, 3, Q), bool)

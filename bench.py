@@ -11,9 +11,11 @@ Cache holds.
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (its algorithmic flops per launch over its mean launch time,
 measured with HIP events recorded by the library on the launch stream), the
-CPU oracle's throughput on the same workload, and (unless --no-bf16) the
-bf16 workload batch 8 x seqlen 4096 and a one-token bf16 decode step (batch
-128, state in place), each against the HBM roofline.
+CPU oracle's throughput on the same workload, and (unless --no-bf16) three
+more workloads: bf16 batch 8 x seqlen 4096 and a one-token bf16 decode step
+(batch 128, state in place), against the HBM roofline, and the fp32 batch 2 x
+seqlen 2048 shape holding packed sequences (seq_idx), against the fp32
+matrix roofline.
 """
 import argparse
 import json
@@ -27,7 +29,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from ssd_workloads import BENCH_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
+from ssd_workloads import BENCH_WORKLOADS, WORKLOADS, make_inputs, make_seq_idx  # noqa: E402
 
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -206,6 +208,68 @@ def decode_workload(steps, warmup, batch=128, nheads=64, dstate=128, ngroups=8):
         "roofline": {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
                      "alg_bytes": nbytes},
+    }
+
+
+def varlen_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mean_len=256):
+    """Packed sequences (seq_idx) on the fp32 batch 2 x seqlen 2048 shape: each row
+    holds sequences of mean length `mean_len` (uniform lengths 1 .. 2*mean-1).
+    Calls alternate between two input copies, like the main measurement; the
+    same calls without seq_idx are timed alongside.  The chunked form does the
+    same work with or without sequence starts, so the roofline is the whole
+    call's algorithmic flops over its time against the fp32 matrix peak."""
+    import torch
+    import selective_state_space_ssd_amd as ssd
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    ws_bytes = ssd.varlen_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                         w.ngroups, w.chunk_size, ssd.SSD_F32)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    seq = torch.from_numpy(make_seq_idx(w.batch, w.seqlen, mean_len, 77)).to(dev)
+    keep, calls = [], []
+    for _ in range(2):
+        t = {k: torch.from_numpy(v).to(dev) for k, v in make_inputs(w).items()
+             if isinstance(v, np.ndarray)}
+        out = torch.empty_like(t["x"])
+        keep.append((t, out))
+        calls.append((t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(),
+                      t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(),
+                      t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0, math.inf, w.chunk_size,
+                      w.ngroups, None, out.data_ptr(), None))
+    tail = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, ssd.SSD_F32, ws.data_ptr(),
+            ws_bytes, torch.cuda.current_stream(dev).cuda_stream)
+
+    def run(k, packed):
+        a = calls[k % 2]
+        st = (ssd.scan_fwd_varlen_raw(*a, seq.data_ptr(), *tail) if packed
+              else ssd.scan_fwd_raw(*a, *tail))
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    res = {}
+    for packed in (True, False):
+        for k in range(warmup):
+            run(k, packed)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            run(k, packed)
+        torch.cuda.synchronize()
+        res[packed] = (time.perf_counter() - t0) / steps
+    el = res[True]
+    fl = sum(alg_flops(w).values())
+    nseq = int((seq[:, 1:] != seq[:, :-1]).sum().item()) + w.batch
+    return {
+        "workload": f"ssd_scan_fwd_varlen f32 batch 2 x seqlen 2048 holding {nseq} packed "
+                    f"sequences (mean length {mean_len}), 32 heads x headdim 64, dstate 128, "
+                    "chunk 128, ngroups 1, z gate and D on",
+        "tokens_per_s": w.tokens / el,
+        "us_per_call": el * 1e6,
+        "plain_us_per_call": res[False] * 1e6,
+        "calls": steps,
+        "roofline": {"bound": "mfma", "achieved": fl / el / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+                     "alg_flops": fl},
     }
 
 
@@ -390,7 +454,8 @@ def main():
         del keep, calls, ws
         torch.cuda.empty_cache()
         line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3),
-                                   decode_workload(max(20, args.steps), 5)]
+                                   decode_workload(max(20, args.steps), 5),
+                                   varlen_workload(max(20, args.steps), 5)]
     print(json.dumps(line), flush=True)
 
 

@@ -206,6 +206,56 @@ size_t ssd_scan_fwd_varlen_workspace_size(int64_t batch, int64_t seqlen, int64_t
                                           int64_t headdim, int64_t dstate, int ngroups,
                                           int chunk_size, int dtype);
 
+/*
+ * Block forward around the scan: the fused Mamba-2 block of mamba issue #647's
+ * repro (mamba_split_conv1d_scan_combined) up to, not including, its out_proj
+ * linear.  With dim = nheads * headdim:
+ *
+ *   zxbcdt  [batch, seqlen, 2*dim + 2*ngroups*dstate + nheads]  dtype
+ *           per token [z (dim) | x (dim) | B (ngroups*dstate) | C (ngroups*dstate)
+ *           | dt (nheads)]
+ *   conv1d_weight [dim + 2*ngroups*dstate, conv_width] float32, required
+ *   conv1d_bias   [dim + 2*ngroups*dstate] float32, NULL: no bias
+ *   conv_width    2, 3 or 4
+ *   rmsnorm_weight [dim] float32, NULL: no norm (out = y * silu(z))
+ *   rmsnorm_eps   >= 0, finite (used only with a weight)
+ *   norm_groups   the norm's mean runs over dim / norm_groups channels: 1 for
+ *                 the whole width, ngroups for one slice per B/C group (the
+ *                 page's python reference and fused kernel respectively);
+ *                 must divide dim; dim <= 15360, norm_groups <= 256
+ *   out     [batch, seqlen, dim]  dtype; written
+ *   every other argument as for ssd_scan_fwd (dt_bias, A, D, dt_min/dt_max,
+ *   chunk_size, ngroups, initial_states, final_states, sizes, dtype, stream).
+ *
+ * Steps, all on `stream`:
+ *   1. xBC = SiLU(causal depthwise conv(xBC) + bias): conv[t][c] =
+ *      sum_k weight[c][k] * xBC[t - (conv_width-1) + k][c], zeros before step
+ *      0; x, B, C land in the workspace in the input dtype, dt is copied;
+ *   2. the scan of ssd_scan_fwd on them, without a gate, into out;
+ *   3. out = g / sqrt(mean(g^2) + eps) * rmsnorm_weight with g = out * silu(z)
+ *      (gate before norm), in place.
+ * Workspace: ssd_split_conv1d_scan_fwd_workspace_size(...) bytes, 256-byte
+ * aligned: x [b,L,H,P], B and C [b,L,G,N], dt [b,L,H] (input dtype, each on a
+ * 256-byte boundary), then the scan's workspace.  out must not overlap
+ * zxbcdt, the workspace or final_states.  Status codes as for ssd_scan_fwd
+ * (SSD_ERR_UNSUPPORTED also for conv_width, dim or norm_groups out of range).
+ */
+int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
+                              const float* conv1d_bias, const float* dt_bias, const float* A,
+                              const float* D, int chunk_size, const float* initial_states,
+                              float dt_min, float dt_max, const float* rmsnorm_weight,
+                              float rmsnorm_eps, int64_t headdim, int ngroups, int norm_groups,
+                              void* out, float* final_states, int64_t batch, int64_t seqlen,
+                              int64_t nheads, int64_t dstate, int conv_width, int dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssd_split_conv1d_scan_fwd needs (0 for an empty problem
+ * and for rejected arguments); pure host computation. */
+size_t ssd_split_conv1d_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                                int64_t headdim, int64_t dstate, int ngroups,
+                                                int chunk_size, int dtype, int conv_width,
+                                                int norm_groups);
+
 /* Static text for a status code ("unknown status" for others). */
 const char* ssd_status_string(int status);
 

@@ -58,6 +58,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_scan_fwd_varlen.restype = i
     lib.ssd_scan_fwd_varlen_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
     lib.ssd_scan_fwd_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_split_conv1d_scan_fwd.argtypes = (
+        [p, p, p, p, p, p, i, p, f, f, p, f, i64, i, i, p, p, i64, i64, i64, i64, i, i, p,
+         ctypes.c_size_t, p])
+    lib.ssd_split_conv1d_scan_fwd.restype = i
+    lib.ssd_split_conv1d_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i,
+                                                             i, i]
+    lib.ssd_split_conv1d_scan_fwd_workspace_size.restype = ctypes.c_size_t
     lib.ssd_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
     lib.ssd_scan_fwd_workspace_size.restype = ctypes.c_size_t
     lib.ssd_status_string.argtypes = [i]
@@ -109,6 +116,14 @@ def varlen_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk
     """Workspace bytes of a packed-sequence (seq_idx) call."""
     return int(load_library().ssd_scan_fwd_varlen_workspace_size(
         batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+
+
+def block_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
+                         conv_width=4, norm_groups=1) -> int:
+    """Workspace bytes of a block call (split + conv1d, scan, gated RMSNorm)."""
+    return int(load_library().ssd_split_conv1d_scan_fwd_workspace_size(
+        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, conv_width,
+        norm_groups))
 
 
 def _check(status: int):
@@ -165,6 +180,78 @@ def scan_fwd_varlen_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bia
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def split_conv1d_scan_fwd_raw(zx_ptr, cw_ptr, cb_ptr, dt_bias_ptr, A_ptr, D_ptr, chunk_size,
+                              init_ptr, dt_min, dt_max, norm_w_ptr, eps, headdim, ngroups,
+                              norm_groups, out_ptr, final_ptr, batch, seqlen, nheads, dstate,
+                              conv_width, dtype, ws_ptr, ws_bytes, stream) -> int:
+    """Direct call of ``ssd_split_conv1d_scan_fwd``; returns the status."""
+    return int(load_library().ssd_split_conv1d_scan_fwd(
+        zx_ptr, cw_ptr, cb_ptr, dt_bias_ptr, A_ptr, D_ptr, int(chunk_size), init_ptr,
+        float(dt_min), float(dt_max), norm_w_ptr, float(eps), int(headdim), int(ngroups),
+        int(norm_groups), out_ptr, final_ptr, int(batch), int(seqlen), int(nheads), int(dstate),
+        int(conv_width), int(dtype), ws_ptr, int(ws_bytes), stream))
+
+
+def split_conv1d_scan_fwd(zxbcdt, conv1d_weight, conv1d_bias, dt_bias, A, D, chunk_size: int,
+                          headdim: int, ngroups: int, dstate: int, rmsnorm_weight=None,
+                          rmsnorm_eps: float = 1e-5, norm_groups: int = 1,
+                          dt_limit=(0.0, math.inf), initial_states=None,
+                          return_final_states: bool = False, out=None, final_states=None,
+                          workspace=None):
+    """The Mamba-2 block around the scan (mamba issue #647's fused block up to
+    its out_proj): zxbcdt [b, L, 2 dim + 2 G N + H] float32 or bfloat16,
+    conv1d_weight [dim + 2 G N, W] and bias, dt_bias, A, D, rmsnorm_weight
+    [dim] float32.  Returns out [b, L, dim] (zxbcdt's dtype), or (out,
+    final_states)."""
+    import torch
+
+    load_library()
+    if zxbcdt.dtype == torch.float32:
+        dtype = SSD_F32
+    elif zxbcdt.dtype == torch.bfloat16:
+        dtype = SSD_BF16
+    else:
+        raise TypeError(f"zxbcdt must be float32 or bfloat16, got {zxbcdt.dtype}")
+    if zxbcdt.dim() != 3 or conv1d_weight.dim() != 2:
+        raise ValueError("expected zxbcdt [b, L, width] and conv1d_weight [channels, W]")
+    b, L, width = zxbcdt.shape
+    H = A.shape[0]
+    dim = H * headdim
+    if width != 2 * dim + 2 * ngroups * dstate + H:
+        raise ValueError("zxbcdt width must be 2*dim + 2*ngroups*dstate + nheads")
+    if conv1d_weight.shape[0] != dim + 2 * ngroups * dstate:
+        raise ValueError("conv1d_weight must have dim + 2*ngroups*dstate rows")
+    dev = zxbcdt.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    for name, t in (("zxbcdt", zxbcdt), ("conv1d_weight", conv1d_weight),
+                    ("conv1d_bias", conv1d_bias), ("dt_bias", dt_bias), ("A", A), ("D", D),
+                    ("rmsnorm_weight", rmsnorm_weight), ("initial_states", initial_states)):
+        if t is None:
+            continue
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on zxbcdt's device")
+        if name != "zxbcdt" and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    W = conv1d_weight.shape[1]
+    if out is None:
+        out = torch.empty((b, L, dim), dtype=zxbcdt.dtype, device=dev)
+    if return_final_states and final_states is None:
+        final_states = torch.empty((b, H, headdim, dstate), dtype=torch.float32, device=dev)
+    ws_bytes = block_workspace_size(b, L, H, headdim, dstate, ngroups, chunk_size, dtype, W,
+                                    norm_groups)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(split_conv1d_scan_fwd_raw(
+        _ptr(zxbcdt), _ptr(conv1d_weight), _ptr(conv1d_bias), _ptr(dt_bias), _ptr(A), _ptr(D),
+        chunk_size, _ptr(initial_states), dt_limit[0], dt_limit[1], _ptr(rmsnorm_weight),
+        rmsnorm_eps, headdim, ngroups, norm_groups, _ptr(out),
+        _ptr(final_states) if return_final_states else None, b, L, H, dstate, W, dtype,
+        _ptr(workspace), workspace.numel(), stream))
+    return (out, final_states) if return_final_states else out
 
 
 def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.inf),

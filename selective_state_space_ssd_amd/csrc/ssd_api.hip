@@ -175,6 +175,38 @@ int validate(const void* x, const void* dt, const float* A, const void* B, const
   return SSD_OK;
 }
 
+// Block forward (split + conv1d prologue, scan, gated RMSNorm epilogue): its
+// workspace holds x, B, C and dt in the input dtype, then the scan's own.
+struct BlockLayout {
+  Layout scan;
+  size_t off_x = 0, off_b = 0, off_c = 0, off_dt = 0, off_scan = 0, total = 0;
+};
+
+int block_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int ngroups, int chunk_size, int dtype, int conv_width, int norm_groups,
+                 BlockLayout* bl) {
+  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
+                        &bl->scan);
+  if (st != SSD_OK) return st;
+  if (!ssd::block_supported(nheads * headdim, norm_groups, conv_width)) return SSD_ERR_UNSUPPORTED;
+  // grids: the prologue tiles time by 32 steps (y dimension <= 65535), the
+  // norm takes one workgroup per token
+  if (seqlen > 65535LL * 32 || batch * seqlen > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+  const size_t es = dtype == SSD_BF16 ? 2 : 4;
+  // element counts fit in int64: check_shapes checked b*L*H*P and b*L*G*N
+  const size_t nx = (size_t)(batch * seqlen * nheads * headdim);
+  const size_t nbc = (size_t)(batch * seqlen * ngroups * dstate);
+  const size_t ndt = (size_t)(batch * seqlen * nheads);
+  bl->off_x = 0;
+  bl->off_b = round_up(nx * es);
+  bl->off_c = bl->off_b + round_up(nbc * es);
+  bl->off_dt = bl->off_c + round_up(nbc * es);
+  bl->off_scan = bl->off_dt + round_up(ndt * es);
+  bl->total = bl->off_scan + bl->scan.total;
+  if (batch == 0 || seqlen == 0) bl->total = 0;
+  return SSD_OK;
+}
+
 }  // namespace
 
 struct ssd_timing {
@@ -301,6 +333,82 @@ int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
              out, final_states, nullptr, false, batch, seqlen, nheads, headdim, dstate, dtype,
              workspace, workspace_bytes, stream, timing);
+}
+
+int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
+                              const float* conv1d_bias, const float* dt_bias, const float* A,
+                              const float* D, int chunk_size, const float* initial_states,
+                              float dt_min, float dt_max, const float* rmsnorm_weight,
+                              float rmsnorm_eps, int64_t headdim, int ngroups, int norm_groups,
+                              void* out, float* final_states, int64_t batch, int64_t seqlen,
+                              int64_t nheads, int64_t dstate, int conv_width, int dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  BlockLayout bl;
+  int st = block_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
+                        conv_width, norm_groups, &bl);
+  if (st != SSD_OK) return st;
+  if (!A) return SSD_ERR_INVALID_ARG;
+  const bool nonempty = batch > 0 && seqlen > 0;
+  if (nonempty && (!zxbcdt || !conv1d_weight || !out)) return SSD_ERR_INVALID_ARG;
+  if (rmsnorm_weight && !(rmsnorm_eps >= 0.0f && std::isfinite(rmsnorm_eps)))
+    return SSD_ERR_INVALID_ARG;
+  const size_t es = dtype == SSD_BF16 ? 2 : 4;
+  if (!aligned(zxbcdt, es) || !aligned(conv1d_weight, 4) || !aligned(conv1d_bias, 4) ||
+      !aligned(rmsnorm_weight, 4) || !aligned(out, 16))
+    return SSD_ERR_ALIGNMENT;
+  const int64_t dim = nheads * headdim;
+  const int64_t width = 2 * dim + 2 * (int64_t)ngroups * dstate + nheads;
+  if (nonempty) {
+    const Span so = span(out, batch * seqlen * dim * (int64_t)es);
+    if (overlap(so, span(zxbcdt, batch * seqlen * width * (int64_t)es))) return SSD_ERR_INVALID_ARG;
+    if (bl.total > 0 && overlap(so, span(workspace, (int64_t)bl.total))) return SSD_ERR_INVALID_ARG;
+    if (final_states &&
+        overlap(so, span(final_states, batch * nheads * headdim * dstate * (int64_t)4)))
+      return SSD_ERR_INVALID_ARG;
+  }
+  if (bl.total > 0) {
+    if (!workspace || workspace_bytes < bl.total) return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return SSD_ERR_ALIGNMENT;
+  }
+  if (batch == 0) return SSD_OK;
+  char* ws = static_cast<char*>(workspace);
+  ssd::BlockProblem q;
+  q.zxbcdt = zxbcdt;
+  q.conv_w = conv1d_weight;
+  q.conv_b = conv1d_bias;
+  q.W = conv_width;
+  q.x = nonempty ? ws + bl.off_x : nullptr;
+  q.B = nonempty ? ws + bl.off_b : nullptr;
+  q.C = nonempty ? ws + bl.off_c : nullptr;
+  q.dt = nonempty ? ws + bl.off_dt : nullptr;
+  q.y = out;
+  q.out = out;
+  q.norm_w = rmsnorm_weight;
+  q.eps = rmsnorm_eps;
+  q.norm_groups = norm_groups;
+  q.b = batch; q.L = seqlen; q.H = nheads; q.P = headdim; q.N = dstate; q.G = ngroups;
+  q.bf16 = dtype == SSD_BF16;
+  if (nonempty && ssd::launch_conv_split(q, stream) != hipSuccess) return SSD_ERR_HIP;
+  // the scan without the gate, straight into out; the epilogue gates and
+  // normalises it in place
+  st = run(q.x, q.dt, A, q.B, q.C, D, nullptr, dt_bias, dt_min, dt_max, chunk_size, ngroups,
+           initial_states, out, final_states, nullptr, false, batch, seqlen, nheads, headdim,
+           dstate, dtype, nonempty ? ws + bl.off_scan : nullptr,
+           nonempty ? workspace_bytes - bl.off_scan : 0, stream, nullptr);
+  if (st != SSD_OK) return st;
+  if (nonempty && ssd::launch_gated_rmsnorm(q, stream) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+size_t ssd_split_conv1d_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                                int64_t headdim, int64_t dstate, int ngroups,
+                                                int chunk_size, int dtype, int conv_width,
+                                                int norm_groups) {
+  BlockLayout bl;
+  if (block_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, conv_width,
+                   norm_groups, &bl) != SSD_OK)
+    return 0;
+  return bl.total;
 }
 
 size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,

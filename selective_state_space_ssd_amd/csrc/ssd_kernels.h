@@ -75,6 +75,33 @@ constexpr int kDecodeMaxL = 16;
 bool use_decode(int64_t seqlen);
 hipError_t launch_decode(const Problem& p, hipStream_t stream);
 
+// Block-level prologue / epilogue around the scan (ssd_block.hip).  The
+// prologue turns the packed in-projection zxbcdt [b, L, 2 dim + 2 G N + H]
+// into x, B, C (causal depthwise conv of width W + SiLU) and dt; the epilogue
+// is the gated RMSNorm out = norm(y * silu(z)) * weight (or the gate alone).
+constexpr int kNormMaxDim = 15360;   // channels per token the norm holds in LDS (60 KB)
+constexpr int kNormMaxGroups = 256;
+struct BlockProblem {
+  const void* zxbcdt;
+  const float* conv_w;   // [dim + 2 G N, W]
+  const float* conv_b;   // [dim + 2 G N], may be null
+  int W;
+  void* x;               // [b, L, H, P]  prologue outputs (input dtype)
+  void* B;               // [b, L, G, N]
+  void* C;               // [b, L, G, N]
+  void* dt;              // [b, L, H]
+  const void* y;         // [b, L, dim] scan output (may be out)
+  void* out;             // [b, L, dim]
+  const float* norm_w;   // [dim], may be null (gate only)
+  float eps;
+  int norm_groups;
+  int64_t b, L, H, P, N, G;
+  bool bf16;
+};
+bool block_supported(int64_t dim, int norm_groups, int conv_width);
+hipError_t launch_conv_split(const BlockProblem& q, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const BlockProblem& q, hipStream_t stream);
+
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);
 

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for want in ("ssd_scan_fwd", "ssd_scan_fwd_workspace_size", "ssd_status_string",
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
                  "ssd_timing_read", "ssd_timing_destroy", "ssd_set_option", "ssd_get_option",
-                 "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size"):
+                 "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size",
+                 "ssd_split_conv1d_scan_fwd", "ssd_split_conv1d_scan_fwd_workspace_size"):
         assert want in names
 
 
@@ -246,6 +247,62 @@ VARLEN_CASES = [
 @pytest.mark.parametrize("desc,changes,want", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
 def test_varlen_rejected_before_launch(desc, changes, want):
     assert call_varlen(**changes) == want
+
+
+def test_workspace_size_block():
+    """Block calls: x [b,L,H,P], B and C [b,L,G,N], dt [b,L,H] in the input
+    dtype, then the scan's workspace for the same problem."""
+    for (b, L, H, P, N, G, Q) in SIZES:
+        for dt in (0, 1):
+            es = 2 if dt else 4
+            pre = (_r(b * L * H * P * es) + 2 * _r(b * L * G * N * es) + _r(b * L * H * es))
+            want = pre + _ws(b, L, H, P, N, G, Q, dt)
+            assert ssd.block_workspace_size(b, L, H, P, N, G, Q, dt, 4, 1) == want
+    assert ssd.block_workspace_size(2, 100, 4, 64, 16, 1, 64, 0, 5, 1) == 0   # conv width 5
+    assert ssd.block_workspace_size(2, 100, 4, 64, 16, 1, 64, 0, 4, 3) == 0   # 3 does not divide 256
+    assert ssd.block_workspace_size(2, 100, 256, 64, 16, 1, 64, 0, 4, 1) == 0  # dim 16384 > 15360
+    assert ssd.block_workspace_size(0, 100, 4, 64, 16, 1, 64, 0, 4, 1) == 0
+
+
+BLOCK = dict(zx=0x10000000, cw=0x20000000, cb=0x30000000, dt_bias=0x40000000, A=0x50000000,
+             D=0x60000000, Q=64, init=None, dt_min=0.0, dt_max=math.inf, nw=0x70000000,
+             eps=1e-5, P=64, G=1, ng=1, out=0x80000000, final=None, b=1, L=100, H=4, N=16,
+             W=4, dtype=0, ws=None, ws_bytes=0, stream=None)
+
+
+def call_block(**changes):
+    a = dict(BLOCK)
+    a.update(changes)
+    return ssd.split_conv1d_scan_fwd_raw(a["zx"], a["cw"], a["cb"], a["dt_bias"], a["A"], a["D"],
+                                         a["Q"], a["init"], a["dt_min"], a["dt_max"], a["nw"],
+                                         a["eps"], a["P"], a["G"], a["ng"], a["out"], a["final"],
+                                         a["b"], a["L"], a["H"], a["N"], a["W"], a["dtype"],
+                                         a["ws"], a["ws_bytes"], a["stream"])
+
+
+BLOCK_CASES = [
+    ("conv width 5", dict(W=5), UNSUPPORTED),
+    ("conv width 1", dict(W=1), UNSUPPORTED),
+    ("norm groups do not divide dim", dict(ng=3), UNSUPPORTED),
+    ("negative eps", dict(eps=-1.0), INVALID),
+    ("NaN eps", dict(eps=math.nan), INVALID),
+    ("null zxbcdt", dict(zx=None), INVALID),
+    ("null conv weight", dict(cw=None), INVALID),
+    ("null A", dict(A=None), INVALID),
+    ("out misaligned", dict(out=0x80000008), ALIGN),
+    ("conv weight misaligned", dict(cw=0x20000002), ALIGN),
+    ("out overlaps zxbcdt", dict(out=0x10000000 + 4096), INVALID),
+    ("groups do not divide heads", dict(G=3), INVALID),
+    ("no workspace", dict(), WORKSPACE),
+    ("valid without bias, weight or D (stops at workspace)", dict(cb=None, nw=None, D=None),
+     WORKSPACE),
+    ("eps ignored without a weight (stops at workspace)", dict(nw=None, eps=-1.0), WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("desc,changes,want", BLOCK_CASES, ids=[c[0] for c in BLOCK_CASES])
+def test_block_rejected_before_launch(desc, changes, want):
+    assert call_block(**changes) == want
 
 
 def test_empty_batch_is_a_no_op():

@@ -1,0 +1,196 @@
+"""GPU parity of the block around the scan (ssd_split_conv1d_scan_fwd: zxbcdt
+split, causal depthwise conv1d + SiLU, the scan, gated RMSNorm) against the
+block oracle (oracle/block.py), element by element, and against the outputs
+printed on the mamba issue #647 page at the page's own configuration."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_ssd_amd as ssd
+from oracle import block
+from parity import TOL, compare, log, np64
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DEV = "cuda:0"
+
+
+def _round_bf16_bits(a):
+    """float32 -> (bf16 bit patterns, the rounded values), nearest even."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _inputs(seed, b, L, H, P, N, G, W, dtype, bias=True, weight=True, init=False):
+    rng = np.random.default_rng(seed)
+    dim, gn = H * P, G * N
+    width = 2 * dim + 2 * gn + H
+    zx = rng.standard_normal((b, L, width)).astype(np.float32)
+    inp = {
+        "zxbcdt": zx,
+        "conv_weight": (0.5 * rng.standard_normal((dim + 2 * gn, W))).astype(np.float32),
+        "conv_bias": (0.1 * rng.standard_normal((dim + 2 * gn,))).astype(np.float32) if bias
+        else None,
+        "dt_bias": np.log(np.expm1(rng.uniform(1e-3, 1e-1, H))).astype(np.float32),
+        "A": (-np.exp(rng.uniform(0.0, np.log(16.0), H))).astype(np.float32),
+        "D": rng.standard_normal(H).astype(np.float32),
+        "rmsnorm_weight": rng.uniform(0.5, 1.5, dim).astype(np.float32) if weight else None,
+        "initial_states": rng.standard_normal((b, H, P, N)).astype(np.float32) if init else None,
+    }
+    if dtype == "bf16":
+        inp["zx_bits"], inp["zxbcdt"] = _round_bf16_bits(zx)
+    return inp
+
+
+def _upload(inp, dtype):
+    t = {k: (None if v is None else torch.from_numpy(v).to(DEV)) for k, v in inp.items()
+         if k not in ("zxbcdt", "zx_bits")}
+    if dtype == "bf16":
+        t["zxbcdt"] = torch.from_numpy(inp["zx_bits"].view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        t["zxbcdt"] = torch.from_numpy(inp["zxbcdt"]).to(DEV)
+    return t
+
+
+def _gpu(t, Q, P, G, N, norm_groups, eps=1e-5, workspace=None):
+    res = ssd.split_conv1d_scan_fwd(
+        t["zxbcdt"], t["conv_weight"], t["conv_bias"], t["dt_bias"], t["A"], t["D"], Q, P, G, N,
+        rmsnorm_weight=t["rmsnorm_weight"], rmsnorm_eps=eps, norm_groups=norm_groups,
+        initial_states=t["initial_states"], return_final_states=True, workspace=workspace)
+    torch.cuda.synchronize()
+    return res
+
+
+def _oracle(inp, H, P, G, N, norm_groups, dtype, eps=1e-5):
+    return block.split_conv1d_scan(
+        oracle.ssd_fwd, inp["zxbcdt"], inp["conv_weight"], inp["conv_bias"], inp["dt_bias"],
+        inp["A"], inp["D"], H, P, G, N, rmsnorm_weight=inp["rmsnorm_weight"], eps=eps,
+        norm_groups=norm_groups, initial_states=inp["initial_states"], dtype=dtype)
+
+
+def _page_rows():
+    path = os.path.join(ROOT, "tests/golden/block_out000_ngroups.txt")
+    return [(int(r[0]), float(r[1]), float(r[2])) for r in
+            (l.split() for l in open(path) if l.strip() and not l.startswith("#"))]
+
+
+@pytest.mark.parametrize("ngroups", [1, 2, 4])
+def test_block_page_configuration(ngroups):
+    """mamba issue #647's repro at its own size: batch 2, seqlen 2048, dim 2048
+    (32 heads of 64), dstate 128, conv width 4, chunk 128, fp32, every tensor
+    0.1, A = -1, D = 1000 h, eps 1e-5.  out_proj (all 0.1, bias 0.1) of
+    out[0, 0, :] must print as the page does: 17.6951 with the whole-width
+    norm, 18.8725 / 19.5926 per group; and every output matches the oracle."""
+    b, L, H, P, N, W, Q = 2, 2048, 32, 64, 128, 4, 128
+    dim, gn = H * P, ngroups * N
+    inp = {
+        "zxbcdt": np.full((b, L, 2 * dim + 2 * gn + H), 0.1, np.float32),
+        "conv_weight": np.full((dim + 2 * gn, W), 0.1, np.float32),
+        "conv_bias": np.full((dim + 2 * gn,), 0.1, np.float32),
+        "dt_bias": np.full((H,), 0.1, np.float32), "A": np.full((H,), -1.0, np.float32),
+        "D": (np.arange(H) * 1000.0).astype(np.float32),
+        "rmsnorm_weight": np.full((dim,), 0.1, np.float32), "initial_states": None,
+    }
+    t = _upload(inp, "f32")
+    row = {g: (comb, ref) for g, comb, ref in _page_rows()}[ngroups]
+    for norm_groups, want in ((1, row[1]), (ngroups, row[0])):
+        log(f"test_block_page_configuration ngroups={ngroups} norm_groups={norm_groups}")
+        out, _ = _gpu(t, Q, P, ngroups, N, norm_groups)
+        o = np64(out)
+        got = 0.1 * o[0, 0].sum() + 0.1
+        log(f"  out_proj(out[0,0,:])[0] = {got:.5f} (page prints {want})")
+        assert abs(got - want) <= 2e-4
+        ref, _ = _oracle(inp, H, P, ngroups, N, norm_groups, "f32")
+        compare("out", o, ref, TOL["f32"])
+
+
+# (dtype, nheads, dstate, ngroups, chunk, conv width, norm_groups, bias, weight, init)
+CASES = [
+    ("f32", 8, 128, 2, 128, 4, 1, True, True, True),
+    ("f32", 8, 128, 2, 128, 4, 2, True, True, False),
+    ("f32", 8, 128, 2, 128, 3, 1, False, True, True),
+    ("f32", 4, 16, 1, 64, 2, 4, True, True, False),
+    ("f32", 8, 64, 4, 64, 4, 1, True, False, True),
+    ("bf16", 8, 128, 4, 256, 4, 4, True, True, True),
+    ("bf16", 8, 128, 2, 128, 4, 1, True, True, False),
+    ("bf16", 4, 32, 2, 64, 4, 2, False, False, True),
+]
+
+
+@pytest.mark.parametrize("dtype,H,N,G,Q,W,ng,bias,weight,init", CASES,
+                         ids=[f"{c[0]}-H{c[1]}-N{c[2]}-G{c[3]}-Q{c[4]}-W{c[5]}-ng{c[6]}"
+                              f"{'' if c[7] else '-nobias'}{'' if c[8] else '-gateonly'}"
+                              for c in CASES])
+def test_block_parity(dtype, H, N, G, Q, W, ng, bias, weight, init):
+    P = 64
+    for L in (2 * Q + Q // 2 + 7, 5):
+        b = 2
+        inp = _inputs(5000 + H + N + Q + W + L, b, L, H, P, N, G, W, dtype, bias, weight, init)
+        t = _upload(inp, dtype)
+        log(f"test_block_parity {dtype} H={H} N={N} G={G} Q={Q} W={W} ng={ng} L={L}")
+        out, fin = _gpu(t, Q, P, G, N, ng)
+        ref, rfin = _oracle(inp, H, P, G, N, ng, dtype)
+        compare("out", np64(out), ref, TOL[dtype])
+        compare("final", np64(fin), rfin, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_prologue_outputs(dtype):
+    """The prologue's x, B, C and dt in the workspace against the oracle's
+    split and conv (x, B, C held in the input dtype)."""
+    b, L, H, P, N, G, W, Q = 2, 300, 8, 64, 128, 2, 4, 128
+    inp = _inputs(5100, b, L, H, P, N, G, W, dtype)
+    t = _upload(inp, dtype)
+    code = ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32
+    ws = torch.zeros(ssd.block_workspace_size(b, L, H, P, N, G, Q, code, W, 1), dtype=torch.uint8,
+                     device=DEV)
+    log(f"test_block_prologue_outputs {dtype}")
+    _gpu(t, Q, P, G, N, 1, workspace=ws)
+    es = 2 if dtype == "bf16" else 4
+    r = lambda v: (v + 255) // 256 * 256
+    sizes = {"x": b * L * H * P, "B": b * L * G * N, "C": b * L * G * N, "dt": b * L * H}
+    parts = block.split_conv1d(inp["zxbcdt"], inp["conv_weight"], inp["conv_bias"], H, P, G, N,
+                               dtype)
+    off = 0
+    for k in ("x", "B", "C", "dt"):
+        raw = ws[off:off + sizes[k] * es]
+        v = raw.view(torch.bfloat16) if dtype == "bf16" else raw.view(torch.float32)
+        got = v.float().cpu().numpy().astype(np.float64)
+        want = np.asarray(parts[k], np.float64).reshape(-1)
+        if k == "dt" or dtype == "f32":
+            tol = 0.0 if k == "dt" else 1e-6
+            assert np.max(np.abs(got - want) / (1 + np.abs(want))) <= tol, k
+        else:
+            # bf16: the GPU rounds its fp32 conv, the oracle its fp64 conv; they
+            # may land on neighbouring bf16 values where the activation sits
+            # within fp32 rounding of a halfway point
+            ulp = 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-30)) - 7)
+            assert np.all(np.abs(got - want) <= ulp + 1e-30), k
+            assert np.mean(got != want) < 1e-2, k
+        off += r(sizes[k] * es)
+
+
+def test_block_full_size_bf16():
+    """The bf16 batch 8 x seqlen 4096 shape (64 heads of 64, dstate 128, 8
+    groups, chunk 256) as a block with the per-group norm; rows 0 and 7 of the
+    batch against the oracle (every token, channel and head of them)."""
+    b, L, H, P, N, G, W, Q = 8, 4096, 64, 64, 128, 8, 4, 256
+    inp = _inputs(5200, b, L, H, P, N, G, W, "bf16", init=False)
+    t = _upload(inp, "bf16")
+    log("test_block_full_size_bf16: GPU")
+    out, fin = _gpu(t, Q, P, G, N, G)
+    got, gfin = np64(out), np64(fin)
+    del out, fin
+    for r in (0, 7):
+        log(f"test_block_full_size_bf16: oracle row {r}")
+        sub = dict(inp)
+        sub["zxbcdt"] = inp["zxbcdt"][r:r + 1]
+        ref, rfin = _oracle(sub, H, P, G, N, G, "bf16")
+        compare(f"out row {r}", got[r:r + 1], ref, TOL["bf16"])
+        compare(f"final row {r}", gfin[r:r + 1], rfin, TOL["bf16"])

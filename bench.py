@@ -15,7 +15,9 @@ CPU oracle's throughput on the same workload, and (unless --no-bf16) three
 more workloads: bf16 batch 8 x seqlen 4096 and a one-token bf16 decode step
 (batch 128, state in place), against the HBM roofline, and the fp32 batch 2 x
 seqlen 2048 shape holding packed sequences (seq_idx), against the fp32
-matrix roofline.
+matrix roofline, and the block around the scan (conv1d prologue, gated RMSNorm
+epilogue) at the fp32 2 x 2048 size, its prologue and epilogue against the HBM
+roofline.
 """
 import argparse
 import json
@@ -273,6 +275,86 @@ def varlen_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mea
     }
 
 
+def block_workload(steps, warmup, ngroups=1, norm_groups=1):
+    """The block around the scan (split + conv1d + SiLU prologue, scan, gated
+    RMSNorm epilogue) at mamba issue #647's repro size: fp32, batch 2 x seqlen
+    2048, dim 2048 (32 heads of 64), dstate 128, conv width 4, chunk 128, with
+    seeded random inputs.  Calls alternate two input copies.  The scan alone on
+    same-shaped inputs (no gate) is timed alongside; the difference is the
+    prologue and epilogue, whose algorithmic bytes over that time give the
+    HBM roofline line."""
+    import torch
+    import selective_state_space_ssd_amd as ssd
+    b, L, H, P, N, W, Q = 2, 2048, 32, 64, 128, 4, 128
+    G = ngroups
+    dim, gn = H * P, G * N
+    width = 2 * dim + 2 * gn + H
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(21)
+    f = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev)
+    zx = [f(b, L, width) for _ in range(2)]
+    cw, cb = 0.5 * f(dim + 2 * gn, W), 0.1 * f(dim + 2 * gn)
+    dt_bias = torch.full((H,), -2.0, device=dev)
+    A = -torch.exp(torch.from_numpy(rng.uniform(0, math.log(16.0), H).astype(np.float32)).to(dev))
+    D, nw = f(H), 1.0 + 0.1 * f(dim)
+    out = torch.empty((b, L, dim), device=dev)
+    wsz = ssd.block_workspace_size(b, L, H, P, N, G, Q, ssd.SSD_F32, W, norm_groups)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+    # the scan alone on same-shaped inputs, no gate (the scan inside the block)
+    xs = [f(b, L, H, P) for _ in range(2)]
+    Bs, Cs, dts = f(b, L, G, N), f(b, L, G, N), f(b, L, H)
+    y = torch.empty_like(xs[0])
+    swsz = ssd.workspace_size(b, L, H, P, N, G, Q, ssd.SSD_F32)
+    sws = torch.empty(swsz, dtype=torch.uint8, device=dev)
+
+    def block_call(k):
+        st = ssd.split_conv1d_scan_fwd_raw(
+            zx[k % 2].data_ptr(), cw.data_ptr(), cb.data_ptr(), dt_bias.data_ptr(), A.data_ptr(),
+            D.data_ptr(), Q, None, 0.0, math.inf, nw.data_ptr(), 1e-5, P, G, norm_groups,
+            out.data_ptr(), None, b, L, H, N, W, ssd.SSD_F32, ws.data_ptr(), wsz, s)
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    def scan_call(k):
+        st = ssd.scan_fwd_raw(xs[k % 2].data_ptr(), dts.data_ptr(), A.data_ptr(), Bs.data_ptr(),
+                              Cs.data_ptr(), D.data_ptr(), None, dt_bias.data_ptr(), 0.0,
+                              math.inf, Q, G, None, y.data_ptr(), None, b, L, H, P, N,
+                              ssd.SSD_F32, sws.data_ptr(), swsz, s)
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    res = {}
+    for name, fn in (("block", block_call), ("scan", scan_call)):
+        for k in range(warmup):
+            fn(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            fn(k)
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / steps
+    extra = res["block"] - res["scan"]
+    # prologue: read the xBC and dt columns (plus a 3-step halo per 32-step
+    # tile) and write x, B, C, dt; epilogue: read y and z, write out
+    halo = 1.0 + (W - 1) / 32.0
+    nbytes = b * L * 4 * ((dim + 2 * gn + H) * (1.0 + halo) + 3 * dim)
+    return {
+        "workload": f"ssd_split_conv1d_scan_fwd f32 batch 2 x seqlen 2048, dim 2048 (32 heads x "
+                    f"headdim 64), dstate 128, ngroups {G}, conv width 4, chunk 128, gated "
+                    f"RMSNorm over {'the whole width' if norm_groups == 1 else 'each group'}",
+        "tokens_per_s": b * L / res["block"],
+        "us_per_call": res["block"] * 1e6,
+        "scan_alone_us_per_call": res["scan"] * 1e6,
+        "calls": steps,
+        "roofline": {"kernels": "prologue + epilogue (block time minus scan time)",
+                     "bound": "hbm", "achieved": nbytes / extra / 1e9 if extra > 0 else None,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": nbytes / extra / 1e9 / PEAK_HBM_GBS if extra > 0 else None,
+                     "alg_bytes": nbytes},
+    }
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -455,7 +537,8 @@ def main():
         torch.cuda.empty_cache()
         line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3),
                                    decode_workload(max(20, args.steps), 5),
-                                   varlen_workload(max(20, args.steps), 5)]
+                                   varlen_workload(max(20, args.steps), 5),
+                                   block_workload(max(20, args.steps), 5)]
     print(json.dumps(line), flush=True)
 
 

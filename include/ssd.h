@@ -217,7 +217,8 @@ size_t ssd_scan_fwd_varlen_workspace_size(int64_t batch, int64_t seqlen, int64_t
  *   conv1d_weight [dim + 2*ngroups*dstate, conv_width] float32, required
  *   conv1d_bias   [dim + 2*ngroups*dstate] float32, NULL: no bias
  *   conv_width    2, 3 or 4
- *   rmsnorm_weight [dim] float32, NULL: no norm (out = y * silu(z))
+ *   rmsnorm_weight [dim] float32, 16-byte aligned, NULL: no norm
+ *                 (out = y * silu(z))
  *   rmsnorm_eps   >= 0, finite (used only with a weight)
  *   norm_groups   the norm's mean runs over dim / norm_groups channels: 1 for
  *                 the whole width, ngroups for one slice per B/C group (the

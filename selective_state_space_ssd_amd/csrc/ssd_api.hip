@@ -354,7 +354,7 @@ int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
     return SSD_ERR_INVALID_ARG;
   const size_t es = dtype == SSD_BF16 ? 2 : 4;
   if (!aligned(zxbcdt, es) || !aligned(conv1d_weight, 4) || !aligned(conv1d_bias, 4) ||
-      !aligned(rmsnorm_weight, 4) || !aligned(out, 16))
+      !aligned(rmsnorm_weight, 16) || !aligned(out, 16))
     return SSD_ERR_ALIGNMENT;
   const int64_t dim = nheads * headdim;
   const int64_t width = 2 * dim + 2 * (int64_t)ngroups * dstate + nheads;

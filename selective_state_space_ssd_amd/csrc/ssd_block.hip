@@ -45,37 +45,38 @@ __device__ __forceinline__ T from_f32(float v) {
 
 // One thread per channel (consecutive lanes: consecutive channels, so every
 // load and store of a wave is one contiguous run), kConvTT timesteps per
-// workgroup with the last W-1 inputs in registers.  Channels past dim + 2GN
-// are the dt columns: copied, no conv.
+// workgroup.  All kConvTT + W - 1 inputs of the tile are loaded first, from
+// rows clamped into [0, L) and zeroed outside, so they are in flight together.
+// Channels past dim + 2GN are the dt columns: copied, no conv.
 template <typename T, int W>
 __global__ __launch_bounds__(256) void conv_split_kernel(
     const T* __restrict__ zx, const float* __restrict__ cw, const float* __restrict__ cb,
     T* __restrict__ xo, T* __restrict__ bo, T* __restrict__ co, T* __restrict__ dto, int64_t L,
     int64_t dim, int64_t gn, int64_t H) {
+  constexpr int NV = kConvTT + W - 1;
   const int64_t nch = dim + 2 * gn;
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.y * kConvTT, b = blockIdx.z;
   if (c >= nch + H) return;  // no barrier in this kernel
   const int64_t width = 2 * dim + 2 * gn + H;
   const T* src = zx + b * L * width + dim + c;  // column dim + c of row t: src[t * width]
-  const int64_t t1 = t0 + kConvTT < L ? t0 + kConvTT : L;
-  if (c >= nch) {  // dt column h = c - nch
-    T* dst = dto + b * L * H + (c - nch);
-    for (int64_t t = t0; t < t1; ++t) dst[t * H] = src[t * width];
-    return;
-  }
-  float w[W];
+  float v[NV];  // v[k]: step t0 - (W-1) + k
 #pragma unroll
-  for (int k = 0; k < W; ++k) w[k] = cw[c * W + k];
-  const float bias = cb ? cb[c] : 0.0f;
-  float win[W];  // win[W-1] is the current step
-#pragma unroll
-  for (int k = 0; k < W - 1; ++k) {
+  for (int k = 0; k < NV; ++k) {
     const int64_t t = t0 - (W - 1) + k;
-    win[k] = t >= 0 ? to_f32(src[t * width]) : 0.0f;
+    const int64_t tc = t < 0 ? 0 : (t < L ? t : L - 1);
+    const float e = to_f32(src[tc * width]);
+    v[k] = (t >= 0 && t < L) ? e : 0.0f;
   }
   T* dst;
   int64_t stride;
+  if (c >= nch) {  // dt column h = c - nch: copied
+    dst = dto + b * L * H + (c - nch);
+#pragma unroll
+    for (int j = 0; j < kConvTT; ++j)
+      if (t0 + j < L) dst[(t0 + j) * H] = from_f32<T>(v[j + W - 1]);
+    return;
+  }
   if (c < dim) {
     dst = xo + b * L * dim + c;
     stride = dim;
@@ -86,39 +87,56 @@ __global__ __launch_bounds__(256) void conv_split_kernel(
     dst = co + b * L * gn + (c - dim - gn);
     stride = gn;
   }
-  for (int64_t t = t0; t < t1; ++t) {
-    win[W - 1] = to_f32(src[t * width]);
+  float w[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) w[k] = cw[c * W + k];
+  const float bias = cb ? cb[c] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < kConvTT; ++j) {
     float acc = bias;
 #pragma unroll
-    for (int k = 0; k < W; ++k) acc += w[k] * win[k];
-    dst[t * stride] = from_f32<T>(silu_accurate(acc));
-#pragma unroll
-    for (int k = 0; k < W - 1; ++k) win[k] = win[k + 1];
+    for (int k = 0; k < W; ++k) acc += w[k] * v[j + k];
+    if (t0 + j < L) dst[(t0 + j) * stride] = from_f32<T>(silu_accurate(acc));
   }
 }
 
 // One workgroup per token: g = y * silu(z) into LDS, one wave per norm slice
 // (looping) sums g^2, then every thread scales its channels.  y may be out
-// (in place): the row is read completely before the first write.
-template <typename T>
+// (in place): the row is read completely before the first write.  dim is a
+// multiple of 64 (headdim 64), so y, out and weight rows take 4-element
+// accesses; z does too when its rows are aligned (VZ).
+template <typename T, bool VZ>
 __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(
     const T* y, const T* __restrict__ zx, const float* __restrict__ weight, float eps,
     T* out, int64_t dim, int64_t width, int norm_groups) {
-  extern __shared__ float norm_lds[];  // dim floats of g, then norm_groups scales
+  extern __shared__ __align__(16) float norm_lds[];  // dim floats of g, then the scales
+  f4* g4 = reinterpret_cast<f4*>(norm_lds);
   float* g_lds = norm_lds;
   float* inv_lds = norm_lds + dim;
   const int64_t row = blockIdx.x;  // b * L + t
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const T* yr = y + row * dim;
   const T* zr = zx + row * width;  // z = the first dim columns of the row
-  for (int64_t c = tid; c < dim; c += 256) g_lds[c] = to_f32(yr[c]) * silu(to_f32(zr[c]));
+  for (int64_t c = 4 * tid; c < dim; c += 1024) {
+    const f4 yv = ld4(yr + c);
+    f4 zv;
+    if constexpr (VZ) {
+      zv = ld4(zr + c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zv[e] = to_f32(zr[c + e]);
+    }
+    f4 g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = yv[e] * silu(zv[e]);
+    g4[c / 4] = g;
+  }
   T* orow = out + row * dim;
-  if (!weight) {
-    __syncthreads();  // uniform: every thread takes this branch or none
-    for (int64_t c = tid; c < dim; c += 256) orow[c] = from_f32<T>(g_lds[c]);
+  __syncthreads();
+  if (!weight) {  // uniform: the gate alone
+    for (int64_t c = 4 * tid; c < dim; c += 1024) st4(orow + c, g4[c / 4]);
     return;
   }
-  __syncthreads();
   const int64_t gs = dim / norm_groups;
   for (int k = wave; k < norm_groups; k += 256 / kWave) {
     float s = 0.0f;
@@ -128,8 +146,15 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(
     if (lane == 0) inv_lds[k] = rsqrtf(s / (float)gs + eps);
   }
   __syncthreads();
-  for (int64_t c = tid; c < dim; c += 256)
-    orow[c] = from_f32<T>(g_lds[c] * inv_lds[c / gs] * weight[c]);
+  for (int64_t c = 4 * tid; c < dim; c += 1024) {
+    const f4 g = g4[c / 4];
+    const f4 wv = ld4(weight + c);
+    const float inv = inv_lds[c / gs];  // the scale of all four when gs % 4 == 0
+    f4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = g[e] * (gs % 4 == 0 ? inv : inv_lds[(c + e) / gs]) * wv[e];
+    st4(orow + c, o);
+  }
 }
 
 bool block_supported(int64_t dim, int norm_groups, int conv_width) {
@@ -166,14 +191,27 @@ hipError_t launch_gated_rmsnorm(const BlockProblem& q, hipStream_t s) {
   const int64_t dim = q.H * q.P, width = 2 * dim + 2 * q.G * q.N + q.H;
   const dim3 grid((unsigned)(q.b * q.L));
   const size_t lds = (size_t)(dim + q.norm_groups) * sizeof(float);
-  if (q.bf16)
-    hipLaunchKernelGGL((gated_rmsnorm_kernel<bf16_t>), grid, dim3(256), lds, s,
-                       static_cast<const bf16_t*>(q.y), static_cast<const bf16_t*>(q.zxbcdt),
-                       q.norm_w, q.eps, static_cast<bf16_t*>(q.out), dim, width, q.norm_groups);
-  else
-    hipLaunchKernelGGL((gated_rmsnorm_kernel<float>), grid, dim3(256), lds, s,
-                       static_cast<const float*>(q.y), static_cast<const float*>(q.zxbcdt),
-                       q.norm_w, q.eps, static_cast<float*>(q.out), dim, width, q.norm_groups);
+  const size_t es = q.bf16 ? 2 : 4;
+  // z rows start every width elements from zxbcdt: 4-element loads need every
+  // row start 4-element aligned (4 * es bytes)
+  const bool vz = (width % 4 == 0) && (reinterpret_cast<uintptr_t>(q.zxbcdt) % (4 * es) == 0);
+  auto go = [&](auto kern, auto tp) {
+    using T = decltype(tp);
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, static_cast<const T*>(q.y),
+                       static_cast<const T*>(q.zxbcdt), q.norm_w, q.eps, static_cast<T*>(q.out),
+                       dim, width, q.norm_groups);
+  };
+  if (q.bf16) {
+    if (vz)
+      go(gated_rmsnorm_kernel<bf16_t, true>, bf16_t{});
+    else
+      go(gated_rmsnorm_kernel<bf16_t, false>, bf16_t{});
+  } else {
+    if (vz)
+      go(gated_rmsnorm_kernel<float, true>, 0.0f);
+    else
+      go(gated_rmsnorm_kernel<float, false>, 0.0f);
+  }
   return hipGetLastError();
 }
 

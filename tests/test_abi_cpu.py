@@ -291,6 +291,7 @@ BLOCK_CASES = [
     ("null A", dict(A=None), INVALID),
     ("out misaligned", dict(out=0x80000008), ALIGN),
     ("conv weight misaligned", dict(cw=0x20000002), ALIGN),
+    ("norm weight not 16-byte aligned", dict(nw=0x70000004), ALIGN),
     ("out overlaps zxbcdt", dict(out=0x10000000 + 4096), INVALID),
     ("groups do not divide heads", dict(G=3), INVALID),
     ("no workspace", dict(), WORKSPACE),

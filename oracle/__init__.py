@@ -8,6 +8,7 @@ Two independent formulations of the same forward are held here:
 
 * ``ssd_fwd`` / ``chunk_intermediates`` -- the plain per-timestep recurrence
   in fp64, written in C (``ssd_oracle.c``) and called through ctypes;
+  ``ssd_bwd`` -- its adjoint (the gradients), step by step, in the same file;
 * ``quadratic.ssd_fwd_quadratic`` -- the dual "masked attention" form in
   NumPy fp64 (q = C, k = B, v = dt * x, log-gate dt*A, no 1/sqrt(d) scale),
   written from the flash-linear-attention PR #49 page's mapping between
@@ -73,6 +74,8 @@ class OracleLib:
         lib.oracle_ssd_chunk_intermediates.argtypes = (
             [p] * 5 + [d, d] + [p] * 6 + [i64] * 7 + [ctypes.c_int])
         lib.oracle_ssd_chunk_intermediates.restype = ctypes.c_int
+        lib.oracle_ssd_bwd.argtypes = ([p] * 8 + [d, d] + [p] * 13 + [i64] * 6 + [ctypes.c_int])
+        lib.oracle_ssd_bwd.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = [ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -106,6 +109,32 @@ class OracleLib:
         if rc != 0:
             raise ValueError("oracle_ssd_fwd rejected the shapes")
         return (out, final) if return_final_states else out
+
+    def ssd_bwd(self, x, dt, A, B, C, dout, D=None, z=None, dt_bias=None,
+                dt_limit=(0.0, float("inf")), initial_states=None, dfinal=None, seq_idx=None,
+                nthreads=0):
+        x, dt, A, B, C = _f32(x), _f32(dt), _f32(A), _f32(B), _f32(C)
+        D, z, dt_bias = _f32(D), _f32(z), _f32(dt_bias)
+        init, dout, dfinal = _f64(initial_states), _f64(dout), _f64(dfinal)
+        seq = _i32(seq_idx)
+        b, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dout.shape == x.shape and (dfinal is None or dfinal.shape == (b, H, P, N))
+        g = {"dx": np.zeros((b, L, H, P)), "dz": np.zeros((b, L, H, P)),
+             "ddt": np.zeros((b, L, H)), "dA": np.zeros(H), "dB": np.zeros((b, L, G, N)),
+             "dC": np.zeros((b, L, G, N)), "dD": np.zeros(H), "ddt_bias": np.zeros(H),
+             "dinitial_states": np.zeros((b, H, P, N))}
+        rc = self.lib.oracle_ssd_bwd(
+            _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+            float(dt_limit[0]), float(dt_limit[1]), _ptr(init), _ptr(seq), _ptr(dout),
+            _ptr(dfinal), _ptr(g["dx"]), _ptr(g["dz"]), _ptr(g["ddt"]), _ptr(g["dA"]),
+            _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddt_bias"]),
+            _ptr(g["dinitial_states"]), b, L, H, P, N, G, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_ssd_bwd rejected the shapes")
+        if z is None:
+            g["dz"] = None
+        return g
 
     def chunk_intermediates(self, x, dt, A, B, chunk_size, dt_bias=None,
                             dt_limit=(0.0, float("inf")), initial_states=None, nthreads=0,
@@ -158,6 +187,13 @@ def ssd_fwd(*args, **kwargs):
     ``return_final_states``, the final state [b,H,P,N] fp64).  ``head_mask``
     [b,H] restricts the work to some (b, h) pairs; other outputs are NaN."""
     return _lib().ssd_fwd(*args, **kwargs)
+
+
+def ssd_bwd(*args, **kwargs):
+    """Gradients of sum(dout * out) + sum(dfinal * final) with respect to every
+    input of ``ssd_fwd``: a dict with dx, dz (None without z), ddt (for dt_raw),
+    dA, dB, dC, dD, ddt_bias and dinitial_states, fp64."""
+    return _lib().ssd_bwd(*args, **kwargs)
 
 
 def chunk_intermediates(*args, **kwargs):

@@ -14,6 +14,7 @@ import tempfile
 
 import numpy as np
 import pytest
+import torch
 from scipy.signal import lfilter
 from scipy.special import expit
 
@@ -453,12 +454,123 @@ def pin_seq_idx_chunk_intermediates(orc):
             assert _rel(res["states_in"][:, c], f_pre) < 1e-13, c
 
 
+def _torch_forward(inp, dt_limit, seq=None, init=True):
+    """The forward recurrence as plain torch fp64 CPU ops, for autograd: a route
+    to the gradient independent of the oracle's hand-written adjoint."""
+    T = lambda a: None if a is None else torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    t = {k: T(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "z", "dt_bias")}
+    t["init"] = T(inp["initial_states"]) if init and inp["initial_states"] is not None else None
+    x, B, C = t["x"], t["B"], t["C"]
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    u = t["dt"] + (t["dt_bias"] if t["dt_bias"] is not None else 0.0)
+    sp = torch.clamp(u, min=0.0) + torch.log1p(torch.exp(-u.abs()))
+    dtv = torch.clamp(sp, dt_limit[0], dt_limit[1])
+    hg = torch.arange(H) // (H // G)
+    h = t["init"] if t["init"] is not None else torch.zeros(b, H, P, N, dtype=torch.float64)
+    outs = []
+    for s_ in range(L):
+        if seq is not None and s_ > 0:
+            keep = torch.tensor((seq[:, s_] == seq[:, s_ - 1]).astype(np.float64))
+            h = h * keep[:, None, None, None]
+        a = torch.exp(dtv[:, s_] * t["A"])                                  # [b, H]
+        Bt, Ct = B[:, s_][:, hg], C[:, s_][:, hg]                          # [b, H, N]
+        h = a[..., None, None] * h + (dtv[:, s_][..., None, None] * x[:, s_][..., None] *
+                                      Bt[:, :, None, :])
+        y = (h * Ct[:, :, None, :]).sum(-1)
+        if t["D"] is not None:
+            y = y + t["D"][None, :, None] * x[:, s_]
+        if t["z"] is not None:
+            y = y * t["z"][:, s_] * torch.sigmoid(t["z"][:, s_])
+        outs.append(y)
+    return t, torch.stack(outs, 1), h
+
+
+def _bwd_check(orc, inp, lim, seq, rng, init=True, tol=1e-10):
+    dout = rng.standard_normal(inp["x"].shape)
+    b, L, H, P = inp["x"].shape
+    N = inp["B"].shape[3]
+    dfin = rng.standard_normal((b, H, P, N))
+    t, out, fin = _torch_forward(inp, lim, seq, init)
+    loss = (out * torch.tensor(dout)).sum() + (fin * torch.tensor(dfin)).sum()
+    loss.backward()
+    a, kw = _args(inp, with_init=init)
+    g = orc.ssd_bwd(*a, dout, **kw, dt_limit=lim, dfinal=dfin, seq_idx=seq)
+    pairs = [("dx", "x"), ("ddt", "dt"), ("dA", "A"), ("dB", "B"), ("dC", "C"), ("dD", "D"),
+             ("dz", "z"), ("ddt_bias", "dt_bias")]
+    if init and inp["initial_states"] is not None:
+        pairs.append(("dinitial_states", "init"))
+    for gk, tk in pairs:
+        if t[tk] is None:
+            continue
+        assert _rel(g[gk], t[tk].grad.numpy()) < tol, (gk, _rel(g[gk], t[tk].grad.numpy()))
+
+
+def pin_bwd_autograd(orc):
+    """The adjoint (every gradient) equals torch autograd through a plain fp64
+    forward: gate, D, bias, initial state, groups, an active dt_limit clamp,
+    and packed-sequence resets."""
+    rng = np.random.default_rng(71)
+    cases = [
+        (dict(seed=81, batch=2, seqlen=21, nheads=4, headdim=3, dstate=4, ngroups=2, init=True),
+         (0.0, float("inf")), None),
+        (dict(seed=82, batch=1, seqlen=70, nheads=2, headdim=2, dstate=3, ngroups=1, init=True),
+         (0.02, 0.5), None),
+        (dict(seed=83, batch=2, seqlen=30, nheads=2, headdim=3, dstate=2, ngroups=2, init=True,
+              gate=False, skip=False), (0.0, float("inf")), "seq"),
+    ]
+    for c, lim, seqk in cases:
+        inp = random_small(**c)
+        seq = make_seq_idx(c["batch"], c["seqlen"], 6, 5) if seqk else None
+        _bwd_check(orc, inp, lim, seq, rng)
+    inp = random_small(84, batch=1, seqlen=9, nheads=2, headdim=2, dstate=2, ngroups=1)
+    _bwd_check(orc, inp, (0.0, float("inf")), None, rng, init=False)
+
+
+def pin_bwd_finite_differences(orc):
+    """The gradient's directional derivative matches central differences of the
+    forward oracle in random directions of every input at once."""
+    rng = np.random.default_rng(72)
+    inp = random_small(85, batch=2, seqlen=40, nheads=4, headdim=4, dstate=4, ngroups=2,
+                       init=True)
+    a, kw = _args(inp)
+    x, dt, A, B, C = a
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    dout = rng.standard_normal(x.shape)
+    dfin = rng.standard_normal((b, H, P, N))
+    g = orc.ssd_bwd(*a, dout, **kw, dfinal=dfin)
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "dt_bias": "ddt_bias", "initial_states": "dinitial_states"}
+    base = dict(x=x, dt=dt, A=A, B=B, C=C, D=inp["D"], z=inp["z"], dt_bias=inp["dt_bias"],
+                initial_states=inp["initial_states"])
+
+    def f(vals):
+        out, fin = orc.ssd_fwd(vals["x"], vals["dt"], vals["A"], vals["B"], vals["C"], D=vals["D"],
+                               z=vals["z"], dt_bias=vals["dt_bias"],
+                               initial_states=vals["initial_states"], return_final_states=True)
+        return float((out * dout).sum() + (fin * dfin).sum())
+
+    for trial in range(3):
+        eps = 1e-3
+        plus, minus, lin = {}, {}, 0.0
+        for k, v in base.items():
+            d = rng.standard_normal(v.shape)
+            vp = (v.astype(np.float64) + eps * d).astype(np.float32)
+            vm = (v.astype(np.float64) - eps * d).astype(np.float32)
+            plus[k], minus[k] = vp, vm
+            lin += float((g[names[k]] * (vp.astype(np.float64) - vm.astype(np.float64))).sum())
+        fd = f(plus) - f(minus)
+        assert abs(fd - lin) <= 1e-4 * max(1.0, abs(lin)), (trial, fd, lin)
+
+
 PINS = [pin_quadratic_form, pin_ngroups_invariance, pin_head_group_map, pin_continuation,
         pin_no_decay_prefix_sum, pin_geometric_series, pin_iir_filter, pin_single_step,
         pin_zero_B_or_C, pin_gate_and_linearity, pin_dt_and_cumsum, pin_softplus_extremes,
         pin_chunk_states, pin_head_mask, pin_batch_permutation,
         pin_page_printed_block_values, pin_seq_idx_quadratic_form, pin_seq_idx_separate_scans,
-        pin_seq_idx_trivial_labels, pin_seq_idx_chunk_intermediates]
+        pin_seq_idx_trivial_labels, pin_seq_idx_chunk_intermediates, pin_bwd_autograd,
+        pin_bwd_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -494,6 +606,20 @@ MUTANTS = [
      ""),
     ("sequence reset one step late", "seq_idx[b * L + t] != seq_idx[b * L + t - 1]",
      "t > 1 && seq_idx[b * L + t - 1] != seq_idx[b * L + t - 2]"),
+    ("adjoint: dB without dt", "dBt[n] = dtv * s;", "dBt[n] = s;"),
+    ("adjoint: decay term of ddt dropped", "const double ddt = gxb + Ah * a * gh;",
+     "const double ddt = gxb;"),
+    ("adjoint: gradient not decayed", "gs[k] = reset ? 0.0 : a * gs[k];",
+     "gs[k] = reset ? 0.0 : gs[k];"),
+    ("adjoint: dC from the previous state", "s += cur[p * N + n] * dyp[p];",
+     "s += prev[p * N + n] * dyp[p];"),
+    ("adjoint: softplus derivative sign", "ddt * pass / (1.0 + exp(-u))",
+     "ddt * pass / (1.0 + exp(u))"),
+    ("adjoint: silu derivative", "(1.0 + zz * (1.0 - sg))", "(1.0 + zz * sg)"),
+    ("adjoint: reset does not cut the gradient", "gs[k] = reset ? 0.0 : a * gs[k];",
+     "gs[k] = a * gs[k];"),
+    ("adjoint: clamp passes the gradient outside", "(sp >= dt_min && sp <= dt_max) ? 1.0 : 0.0",
+     "1.0"),
     ("chunk-local state not reset",
      "                    memset(Sc, 0, sizeof(double) * (size_t)(P * N));\n                }",
      "                }"),

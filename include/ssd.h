@@ -257,6 +257,50 @@ size_t ssd_split_conv1d_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, i
                                                 int chunk_size, int dtype, int conv_width,
                                                 int norm_groups);
 
+/*
+ * Backward of ssd_scan_fwd (float32 inputs, dtype SSD_F32): the gradients of
+ *     l = sum(dout * out) + sum(dfinal_states * final_states)
+ * with respect to every input, for training (the pages note the backward as
+ * missing or separate).  Arguments x .. initial_states, the sizes and dtype are
+ * those of the forward call; chunk_size is checked as there (the gradients do
+ * not depend on it: the backward works in 64-step blocks).
+ *
+ *   dout            [batch, seqlen, nheads, headdim]  required
+ *   dfinal_states   [batch, nheads, headdim, dstate]  NULL: zero
+ *   dx              [batch, seqlen, nheads, headdim]  required
+ *   ddt             [batch, seqlen, nheads]  gradient of dt (the raw input);
+ *                   zero where dt_limit clamps softplus(dt + dt_bias)
+ *   dA              [nheads]                          required
+ *   dB, dC          [batch, seqlen, ngroups, dstate]  required (summed over
+ *                   the heads of each group)
+ *   dD              [nheads]    exactly when D is given
+ *   dz              like x      exactly when z is given
+ *   ddt_bias        [nheads]    exactly when dt_bias is given
+ *   dinitial_states [batch, nheads, headdim, dstate]  NULL: not returned
+ * All float32, contiguous; x, B, C, z, dout, dx, dz, dB, dC and the state
+ * tensors 16-byte aligned, the others 4-byte aligned.  No output may overlap
+ * an input, another output or the workspace.
+ *
+ * The forward is re-run inside (dt, running sums, the states entering each
+ * block and the ungated output go to the workspace), then the reverse pass.
+ * Workspace: ssd_scan_bwd_workspace_size(...) bytes, 256-byte aligned.  Like
+ * the forward the call is asynchronous and deterministic.  Status codes as
+ * for ssd_scan_fwd; SSD_ERR_UNSUPPORTED for bf16.
+ */
+int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                 const float* D, const float* z, const float* dt_bias, float dt_min, float dt_max,
+                 int chunk_size, int ngroups, const float* initial_states, const float* dout,
+                 const float* dfinal_states, float* dx, float* ddt, float* dA, float* dB,
+                 float* dC, float* dD, float* dz, float* ddt_bias, float* dinitial_states,
+                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace ssd_scan_bwd needs (0 for an empty problem and for
+ * rejected arguments); pure host computation. */
+size_t ssd_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
+                                   int dtype);
+
 /* Static text for a status code ("unknown status" for others). */
 const char* ssd_status_string(int status);
 

@@ -62,6 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         [p, p, p, p, p, p, i, p, f, f, p, f, i64, i, i, p, p, i64, i64, i64, i64, i, i, p,
          ctypes.c_size_t, p])
     lib.ssd_split_conv1d_scan_fwd.restype = i
+    lib.ssd_scan_bwd.argtypes = ([p] * 8 + [f, f, i, i] + [p] * 12 + [i64] * 5 +
+                                 [i, p, ctypes.c_size_t, p])
+    lib.ssd_scan_bwd.restype = i
+    lib.ssd_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
+    lib.ssd_scan_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ssd_split_conv1d_scan_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i,
                                                              i, i]
     lib.ssd_split_conv1d_scan_fwd_workspace_size.restype = ctypes.c_size_t
@@ -126,6 +131,13 @@ def block_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_
         norm_groups))
 
 
+def bwd_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
+                       dtype=SSD_F32) -> int:
+    """Workspace bytes of a backward call."""
+    return int(load_library().ssd_scan_bwd_workspace_size(
+        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+
+
 def _check(status: int):
     if status != 0:
         raise SsdError(status, status_string(status))
@@ -180,6 +192,64 @@ def scan_fwd_varlen_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bia
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def scan_bwd_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min, dt_max,
+                 chunk_size, ngroups, init_ptr, dout_ptr, dfinal_ptr, dx_ptr, ddt_ptr, dA_ptr,
+                 dB_ptr, dC_ptr, dD_ptr, dz_ptr, ddt_bias_ptr, dinit_ptr, batch, seqlen, nheads,
+                 headdim, dstate, dtype, ws_ptr, ws_bytes, stream) -> int:
+    """Direct call of ``ssd_scan_bwd``; returns the status."""
+    return int(load_library().ssd_scan_bwd(
+        x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, float(dt_min),
+        float(dt_max), int(chunk_size), int(ngroups), init_ptr, dout_ptr, dfinal_ptr, dx_ptr,
+        ddt_ptr, dA_ptr, dB_ptr, dC_ptr, dD_ptr, dz_ptr, ddt_bias_ptr, dinit_ptr, int(batch),
+        int(seqlen), int(nheads), int(headdim), int(dstate), int(dtype), ws_ptr, int(ws_bytes),
+        stream))
+
+
+def scan_bwd(x, dt, A, B, C, dout, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.inf),
+             chunk_size: int = 128, initial_states=None, dfinal_states=None,
+             return_dinitial_states: bool = True, workspace=None):
+    """Gradients of sum(dout * out) + sum(dfinal_states * final_states) of
+    ``scan_fwd`` (float32 inputs) with respect to x, dt (raw), A, B, C, D, z,
+    dt_bias and the initial state.  Returns a dict of float32 tensors: dx, ddt,
+    dA, dB, dC, and dD / dz / ddt_bias when D / z / dt_bias are given,
+    dinitial_states when asked for."""
+    import torch
+
+    load_library()
+    if x.dtype != torch.float32:
+        raise TypeError("the backward takes float32 inputs")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("dout", dout),
+                    ("D", D), ("z", z), ("dt_bias", dt_bias), ("initial_states", initial_states),
+                    ("dfinal_states", dfinal_states)):
+        if t is None:
+            continue
+        if t.device != dev or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor on x's device")
+    if tuple(dout.shape) != (b, L, H, P):
+        raise ValueError("dout must have x's shape")
+    e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = {"dx": e(b, L, H, P), "ddt": e(b, L, H), "dA": e(H), "dB": e(b, L, G, N),
+         "dC": e(b, L, G, N), "dD": e(H) if D is not None else None,
+         "dz": e(b, L, H, P) if z is not None else None,
+         "ddt_bias": e(H) if dt_bias is not None else None,
+         "dinitial_states": e(b, H, P, N) if return_dinitial_states else None}
+    ws_bytes = bwd_workspace_size(b, L, H, P, N, G, chunk_size, SSD_F32)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(scan_bwd_raw(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+        dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(dout),
+        _ptr(dfinal_states), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]),
+        _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
+        _ptr(g["dinitial_states"]), b, L, H, P, N, SSD_F32, _ptr(workspace), workspace.numel(),
+        stream))
+    return {k: v for k, v in g.items() if v is not None}
 
 
 def split_conv1d_scan_fwd_raw(zx_ptr, cw_ptr, cb_ptr, dt_bias_ptr, A_ptr, D_ptr, chunk_size,

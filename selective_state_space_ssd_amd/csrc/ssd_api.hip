@@ -207,6 +207,47 @@ int block_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
   return SSD_OK;
 }
 
+// Backward workspace (fp32, each region on a 256-byte boundary), blocks of 64:
+// dt, cum [b, H, nb, 64]; chunk-local states (then P_c) and entering states
+// [b, nb, H, P N]; y / dY [b, L, H, P]; G [b, nb, H, P N]; per-head dB and dC
+// parts [b, L, H, N]; dA and dD parts [b, nb, H].
+struct BwdLayout {
+  int64_t nb = 0;
+  size_t off_dt = 0, off_cum = 0, off_s = 0, off_in = 0, off_y = 0, off_g = 0, off_db = 0,
+         off_dc = 0, off_da = 0, off_dd = 0, total = 0;
+};
+
+int bwd_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+               int ngroups, int chunk_size, int dtype, BwdLayout* bl) {
+  Layout lay;
+  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
+                        &lay);
+  if (st != SSD_OK) return st;
+  if (dtype != SSD_F32) return SSD_ERR_UNSUPPORTED;
+  if (!ssd::config_supported(headdim, dstate, 64)) return SSD_ERR_UNSUPPORTED;
+  const int64_t nb = ssd::bwd_blocks(seqlen);
+  int64_t units, blkn, stn, xn, bcn;
+  if (!mul_ok(batch * nb, nheads, &units) || !mul_ok(units, 64, &blkn) ||
+      !mul_ok(units, headdim * dstate, &stn) || !mul_ok(batch * seqlen * nheads, headdim, &xn) ||
+      !mul_ok(batch * seqlen * nheads, dstate, &bcn))
+    return SSD_ERR_INVALID_ARG;
+  if (units > INT32_MAX || nb > 65535) return SSD_ERR_UNSUPPORTED;
+  bl->nb = nb;
+  bl->off_dt = 0;
+  bl->off_cum = round_up((size_t)blkn * 4);
+  bl->off_s = bl->off_cum + round_up((size_t)blkn * 4);
+  bl->off_in = bl->off_s + round_up((size_t)stn * 4);
+  bl->off_y = bl->off_in + round_up((size_t)stn * 4);
+  bl->off_g = bl->off_y + round_up((size_t)xn * 4);
+  bl->off_db = bl->off_g + round_up((size_t)stn * 4);
+  bl->off_dc = bl->off_db + round_up((size_t)bcn * 4);
+  bl->off_da = bl->off_dc + round_up((size_t)bcn * 4);
+  bl->off_dd = bl->off_da + round_up((size_t)units * 4);
+  bl->total = bl->off_dd + round_up((size_t)units * 4);
+  if (batch == 0 || seqlen == 0) bl->total = 0;
+  return SSD_OK;
+}
+
 }  // namespace
 
 struct ssd_timing {
@@ -398,6 +439,110 @@ int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
   if (st != SSD_OK) return st;
   if (nonempty && ssd::launch_gated_rmsnorm(q, stream) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
+}
+
+int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                 const float* D, const float* z, const float* dt_bias, float dt_min, float dt_max,
+                 int chunk_size, int ngroups, const float* initial_states, const float* dout,
+                 const float* dfinal_states, float* dx, float* ddt, float* dA, float* dB,
+                 float* dC, float* dD, float* dz, float* ddt_bias, float* dinitial_states,
+                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  BwdLayout bl;
+  int st = bwd_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, &bl);
+  if (st != SSD_OK) return st;
+  if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return SSD_ERR_INVALID_ARG;
+  if (!A || !dA) return SSD_ERR_INVALID_ARG;
+  if ((D != nullptr) != (dD != nullptr) || (z != nullptr) != (dz != nullptr) ||
+      (dt_bias != nullptr) != (ddt_bias != nullptr))
+    return SSD_ERR_INVALID_ARG;
+  const bool nonempty = batch > 0 && seqlen > 0;
+  if (nonempty && (!x || !dt || !B || !C || !dout || !dx || !ddt || !dB || !dC))
+    return SSD_ERR_INVALID_ARG;
+  const void* v16[] = {x, B, C, z, dout, dx, dz, dB, dC, initial_states, dfinal_states,
+                       dinitial_states};
+  for (const void* q : v16)
+    if (!aligned(q, 16)) return SSD_ERR_ALIGNMENT;
+  const void* v4[] = {dt, A, D, dt_bias, ddt, dA, dD, ddt_bias};
+  for (const void* q : v4)
+    if (!aligned(q, 4)) return SSD_ERR_ALIGNMENT;
+  // outputs must not overlap any input, each other or the workspace
+  const int64_t nx = batch * seqlen * nheads * headdim, nbc = batch * seqlen * ngroups * dstate;
+  const int64_t nst = batch * nheads * headdim * dstate, ndt = batch * seqlen * nheads;
+  const Span ins[] = {span(x, nx * 4), span(dt, ndt * 4), span(A, nheads * 4),
+                      span(B, nbc * 4), span(C, nbc * 4), span(D, D ? nheads * 4 : 0),
+                      span(z, z ? nx * 4 : 0), span(dt_bias, dt_bias ? nheads * 4 : 0),
+                      span(initial_states, initial_states ? nst * 4 : 0), span(dout, nx * 4),
+                      span(dfinal_states, dfinal_states ? nst * 4 : 0),
+                      span(workspace, (int64_t)bl.total)};
+  const Span outs[] = {span(dx, nx * 4), span(ddt, ndt * 4), span(dA, nheads * 4),
+                       span(dB, nbc * 4), span(dC, nbc * 4), span(dD, dD ? nheads * 4 : 0),
+                       span(dz, dz ? nx * 4 : 0), span(ddt_bias, ddt_bias ? nheads * 4 : 0),
+                       span(dinitial_states, dinitial_states ? nst * 4 : 0)};
+  for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+    if (outs[a].hi <= outs[a].lo) continue;
+    for (const Span& s2 : ins)
+      if (s2.hi > s2.lo && overlap(outs[a], s2)) return SSD_ERR_INVALID_ARG;
+    for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
+      if (outs[c].hi > outs[c].lo && overlap(outs[a], outs[c])) return SSD_ERR_INVALID_ARG;
+  }
+  if (bl.total > 0) {
+    if (!workspace || workspace_bytes < bl.total) return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, kAlign)) return SSD_ERR_ALIGNMENT;
+  }
+  if (batch == 0) return SSD_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  ssd::Problem p;
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = nullptr; p.dt_bias = dt_bias;
+  p.dt_min = dt_min; p.dt_max = dt_max; p.init = initial_states;
+  p.out = nonempty ? ws + bl.off_y : nullptr;
+  p.final_states = nullptr;
+  p.seq_idx = nullptr;
+  p.b = batch; p.L = seqlen; p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups;
+  p.Q = 64; p.nc = bl.nb; p.bf16 = false;
+  p.ws_dt = nonempty ? reinterpret_cast<float*>(ws + bl.off_dt) : nullptr;
+  p.ws_cum = nonempty ? reinterpret_cast<float*>(ws + bl.off_cum) : nullptr;
+  p.ws_states = nonempty ? reinterpret_cast<float*>(ws + bl.off_s) : nullptr;
+  p.ws_states_in = nonempty ? reinterpret_cast<float*>(ws + bl.off_in) : nullptr;
+  p.ws_bt = nullptr;
+  p.ws_seg = nullptr;
+  p.fs_ring = nullptr; p.fs_flags = nullptr; p.fs_ctl = nullptr;
+  p.fused_kind = 0;
+  if (nonempty) {
+    // the forward again (64-step blocks, no gate): dt, cum, states, y
+    if (!ssd::chunk_state_fuses_dt(p) && ssd::launch_dt_cumsum(p, stream) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (ssd::launch_chunk_state(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
+  }
+  ssd::BwdProblem q;
+  q.fwd = p;
+  q.fwd.z = z;
+  q.dout = dout;
+  q.dfinal = dfinal_states;
+  q.dy = nonempty ? reinterpret_cast<float*>(ws + bl.off_y) : nullptr;
+  q.pc = nonempty ? reinterpret_cast<float*>(ws + bl.off_s) : nullptr;
+  q.gst = nonempty ? reinterpret_cast<float*>(ws + bl.off_g) : nullptr;
+  q.dBh = nonempty ? reinterpret_cast<float*>(ws + bl.off_db) : nullptr;
+  q.dCh = nonempty ? reinterpret_cast<float*>(ws + bl.off_dc) : nullptr;
+  q.dA_p = nonempty ? reinterpret_cast<float*>(ws + bl.off_da) : nullptr;
+  q.dD_p = nonempty ? reinterpret_cast<float*>(ws + bl.off_dd) : nullptr;
+  q.dx = dx; q.dz = dz; q.ddt = ddt; q.dA = dA; q.dB = dB; q.dC = dC; q.dD = dD;
+  q.ddt_bias = ddt_bias; q.dinit = dinitial_states;
+  if (ssd::launch_bwd(q, stream) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
+}
+
+size_t ssd_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                   int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
+                                   int dtype) {
+  BwdLayout bl;
+  if (bwd_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, &bl) !=
+      SSD_OK)
+    return 0;
+  return bl.total;
 }
 
 size_t ssd_split_conv1d_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,

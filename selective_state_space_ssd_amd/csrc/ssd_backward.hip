@@ -1,0 +1,461 @@
+// Backward of the scan (fp32): gradients of l = sum(dout * out) + sum(dfinal *
+// final) with respect to x, dt_raw, A, B, C, D, z, dt_bias and the initial
+// state.  The chunked form, with blocks of T = 64 steps (the gradient, like
+// the forward result, does not depend on the block length):
+//
+// Inside a block, with cum_t the running sum of dt A from the block start,
+// cl = cum_{T-1}, H_in the state entering the block, G the gradient of the
+// state leaving it, dY = dout * silu(z) and
+//     M[t][s] = exp(cum_t - cum_s) [s <= t],  K[t][s] = C_t . B_s,
+//     R[t][s] = dY_t . x_s,  w_s = exp(cl - cum_s) dt_s,
+// the forward pieces  Y = exp(cum) (C H_in^T) + (M o K) diag(dt) X + D X  and
+// H_out = exp(cl) H_in + X^T diag(w) B  give
+//     dX = D dY + (M o K diag(dt))^T dY + diag(w) B G^T
+//     dB = diag(dt) (M o R)^T C + diag(w) X G
+//     dC = diag(exp(cum)) dY H_in + (M o R) diag(dt) B
+//     dH_in = dY^T diag(exp(cum)) C + exp(cl) G                 (state passing)
+// and for the log-decays, with v[t][s] = M K R dt_s:
+//     dcum_t += sum_s v[t][s] + exp(cum_t) dY_t . (H_in C_t)
+//     dcum_s -= sum_t v[t][s] + w_s x_s . (G B_s)
+//     dcum_cl += sum_s w_s x_s . (G B_s) + exp(cl) <G, H_in>
+//     ddt_t = sum_{t'} M K R [t'][t] + exp(cl - cum_t) x_t . (G B_t)
+//             + A sum_{t' >= t} dcum_t'        (cum_t = A * running sum of dt)
+//     dA   += sum_t dt_t sum_{t' >= t} dcum_t'
+// The pairs (t, s) that straddle blocks reach the gradients through H_in and
+// G, which the reverse state passing provides: G_{c-1} = exp(cl_c) G_c + P_c
+// with P_c = sum_t exp(cum_t) dY_t C_t^T, and dinit = G_{-1}.
+//
+// Kernels: the forward is re-run (64-step blocks) for dt, cum, the states
+// entering each block and the ungated y; then gate_bwd_kernel (dY, dz),
+// bwd_dstate_kernel (P_c), bwd_state_passing_kernel (G_c, dinit),
+// block_bwd_kernel (dX, per-head dB and dC, ddt_raw, per-block dA and dD
+// parts) and the reductions over heads, batch and blocks.  The products are
+// on v_mfma_f32_16x16x4_f32 from LDS tiles; masks and decays are applied to
+// the 64 x 64 in-block matrices in between.
+#include "ssd_dt.h"
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+namespace {
+constexpr int kBT = 64;   // block length of the backward
+constexpr int kXP = 65;   // padded row stride of 64-wide LDS tiles
+
+// acc (one 16 x 16 tile) += sum_{k < K} a(i, k) * b(k, j) for the wave:
+// lane l supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane
+// l holds the element (row 4 (l/16) + r, column l%16).
+template <typename FA, typename FB>
+__device__ __forceinline__ f4 tile16(FA a, FB b, int K, f4 acc) {
+  const int lane = threadIdx.x % kWave, i = lane % 16, kk = lane / 16;
+  for (int k = 0; k < K; k += 4) acc = mfma16x16x4(a(i, k + kk), b(k + kk, i), acc);
+  return acc;
+}
+}  // namespace
+
+// dY = dout * silu(z) (in place of y), dz = dout * y * silu'(z); without z,
+// dY = dout.  Four elements per thread.
+__global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dout,
+                                                       const float* __restrict__ z, float* y_dy,
+                                                       float* __restrict__ dz, int64_t n4) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= n4) return;
+  const f4 d = ld4(dout + 4 * k);
+  if (!z) {
+    st4(y_dy + 4 * k, d);
+    return;
+  }
+  const f4 y = ld4(y_dy + 4 * k), zv = ld4(z + 4 * k);
+  f4 dyv, dzv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float sg = 1.0f / (1.0f + expf(-zv[e]));
+    dyv[e] = d[e] * zv[e] * sg;
+    dzv[e] = d[e] * y[e] * sg * (1.0f + zv[e] * (1.0f - sg));
+  }
+  st4(y_dy + 4 * k, dyv);
+  st4(dz + 4 * k, dzv);
+}
+
+// P_c[p][n] = sum_t exp(cum_t) dY_t[p] C_t[n] per (batch, block, head), row-major
+// [P][N].  Wave w owns rows p in [16w, 16w+16) and all N/16 column tiles.
+template <int N>
+__global__ __launch_bounds__(256) void bwd_dstate_kernel(
+    const float* __restrict__ dy, const float* __restrict__ Cm, const float* __restrict__ ws_cum,
+    float* __restrict__ pc, int64_t L, int64_t H, int64_t G, int64_t nb) {
+  constexpr int P = 64, NJ = N / 16;
+  __shared__ float dy_l[kBT][kXP];
+  __shared__ float c_l[kBT][N + 1];
+  __shared__ float e_l[kBT];
+  const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
+  const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
+  const int64_t g = h / (H / G), t0 = blk * kBT;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  for (int e = tid; e < kBT * P; e += 256) {
+    const int t = e / P, p = e % P;
+    dy_l[t][p] = t0 + t < L ? dy[((b * L + t0 + t) * H + h) * P + p] : 0.0f;
+  }
+  for (int e = tid; e < kBT * N; e += 256) {
+    const int t = e / N, n = e % N;
+    c_l[t][n] = t0 + t < L ? Cm[((b * L + t0 + t) * G + g) * N + n] : 0.0f;
+  }
+  if (tid < kBT) e_l[tid] = expf(ws_cum[((b * H + h) * nb + blk) * kBT + tid]);
+  __syncthreads();
+  float* dst = pc + u * (int64_t)(P * N);
+  const int i = lane % 16, kk = lane / 16;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    acc = tile16([&](int r, int k) { return dy_l[k][16 * wave + r] * e_l[k]; },
+                 [&](int k, int c) { return c_l[k][16 * j + c]; }, kBT, acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * kk + r) * N + 16 * j + i] = acc[r];
+  }
+}
+
+// Reverse state passing: G_c (gradient of the state leaving block c, stored
+// row-major per block), G_{nb-1} = dfinal (or 0), G_{c-1} = exp(cl_c) G_c + P_c;
+// dinit = G_{-1}.  Four state elements per thread.
+__global__ __launch_bounds__(256) void bwd_state_passing_kernel(
+    const float* __restrict__ pc, const float* __restrict__ ws_cum, const float* dfinal,
+    float* __restrict__ gst, float* dinit, int64_t H, int64_t nb, int64_t PN) {
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  if (k >= PN / 4) return;
+  f4 gv = dfinal ? ld4(dfinal + (b * H + h) * PN + 4 * k) : f4{0.f, 0.f, 0.f, 0.f};
+  const float* cl = ws_cum + (b * H + h) * nb * kBT + (kBT - 1);
+  for (int64_t c = nb - 1; c >= 0; --c) {
+    const int64_t o = ((b * nb + c) * H + h) * PN + 4 * k;
+    st4(gst + o, gv);
+    gv = expf(cl[c * kBT]) * gv + ld4(pc + o);
+  }
+  if (dinit) st4(dinit + (b * H + h) * PN + 4 * k, gv);
+}
+
+// One workgroup (four waves) per (batch, block, head).
+template <int N>
+__global__ __launch_bounds__(256) void block_bwd_kernel(
+    const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
+    const float* __restrict__ dt_raw, const float* __restrict__ dt_bias, float dt_min,
+    float dt_max, const float* __restrict__ A, const float* __restrict__ Dv,
+    const float* __restrict__ ws_dt, const float* __restrict__ ws_cum,
+    const float* __restrict__ states_in, const float* __restrict__ gst,
+    const float* __restrict__ dy, float* __restrict__ dx, float* __restrict__ dBh,
+    float* __restrict__ dCh, float* __restrict__ ddt_raw, float* __restrict__ dA_p,
+    float* __restrict__ dD_p, int64_t L, int64_t H, int64_t G, int64_t nb) {
+  constexpr int P = 64, T = kBT, NJ = N / 16, NS = N + 1;
+  __shared__ float x_l[T][kXP], dy_l[T][kXP];
+  __shared__ float b_l[T][NS], c_l[T][NS];
+  __shared__ float km[T][kXP];  // K, then V = M o K diag(dt)
+  __shared__ float rm[T][kXP];  // R, then W = M o R
+  __shared__ float cum_l[T], dt_l[T];
+  __shared__ float rowv[T], xgb[T], yod[T], red[8];
+  __shared__ float colw[4][T], col0w[4][T];  // per-wave column sums, added in order
+
+  const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
+  const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
+  const int64_t g = h / (H / G), t0 = blk * T;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int i = lane % 16, kk = lane / 16;
+  const int64_t PN = (int64_t)P * N;
+  const float* hin = states_in + u * PN;  // tiled layout
+  const float* gc = gst + u * PN;         // row-major [P][N]
+
+  // ---- stage x, dY, B, C, cum, dt (rows past the end are zero) --------------
+  for (int e = tid; e < T * P; e += 256) {
+    const int t = e / P, p = e % P;
+    const bool ok = t0 + t < L;
+    const int64_t o = ((b * L + t0 + t) * H + h) * P + p;
+    x_l[t][p] = ok ? x[o] : 0.0f;
+    dy_l[t][p] = ok ? dy[o] : 0.0f;
+  }
+  for (int e = tid; e < T * N; e += 256) {
+    const int t = e / N, n = e % N;
+    const bool ok = t0 + t < L;
+    const int64_t o = ((b * L + t0 + t) * G + g) * N + n;
+    b_l[t][n] = ok ? Bm[o] : 0.0f;
+    c_l[t][n] = ok ? Cm[o] : 0.0f;
+  }
+  if (tid < T) {
+    const int64_t o = ((b * H + h) * nb + blk) * T + tid;
+    cum_l[tid] = ws_cum[o];
+    dt_l[tid] = ws_dt[o];
+  }
+  __syncthreads();
+  const float cl = cum_l[T - 1];
+  const float Dh = Dv ? Dv[h] : 0.0f;
+
+  // Sums over a row of a wave's 16 x 64 strip (16 lanes x 4 tiles) or a column
+  // (4 lane groups x 4 registers x 4 waves) are taken in a fixed order: lane
+  // shuffles within the wave, then the per-wave parts in wave order, so the
+  // gradients are identical from run to run.
+  auto sum16 = [](float v) {  // over the 16 lanes of a row group
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+  };
+  auto sum4g = [](float v) {  // over the four 16-lane groups
+    v += __shfl_xor(v, 16, kWave);
+    return v + __shfl_xor(v, 32, kWave);
+  };
+
+  // ---- K = C B^T and R = dY X^T; masks, decays and the dcum sums -------------
+  // wave w: rows t in [16w, 16w+16), four column tiles of s
+  float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f4 kacc = tile16([&](int r, int k) { return c_l[16 * wave + r][k]; },
+                     [&](int k, int c) { return b_l[16 * j + c][k]; }, N, f4{0.f, 0.f, 0.f, 0.f});
+    f4 racc = tile16([&](int r, int k) { return dy_l[16 * wave + r][k]; },
+                     [&](int k, int c) { return x_l[16 * j + c][k]; }, P, f4{0.f, 0.f, 0.f, 0.f});
+    const int s = 16 * j + i;
+    float cs = 0.0f, cs0 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * kk + r;
+      const float m = s <= t ? expf(cum_l[t] - cum_l[s]) : 0.0f;
+      const float v0 = m * kacc[r] * racc[r];
+      const float v = v0 * dt_l[s];
+      km[t][s] = m * kacc[r] * dt_l[s];
+      rm[t][s] = m * racc[r];
+      rsum[r] += v;
+      cs += v;
+      cs0 += v0;
+    }
+    cs = sum4g(cs);
+    cs0 = sum4g(cs0);
+    if (kk == 0) {
+      colw[wave][s] = cs;
+      col0w[wave][s] = cs0;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float v = sum16(rsum[r]);
+    if (i == 0) rowv[16 * wave + 4 * kk + r] = v;
+  }
+  __syncthreads();
+
+  // ---- dX = D dY + V^T dY + diag(w) B G^T; x . (G B) per row ----------------
+  float xs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f4 vdy = tile16([&](int r, int k) { return km[k][16 * wave + r]; },
+                          [&](int k, int c) { return dy_l[k][16 * j + c]; }, T,
+                          f4{0.f, 0.f, 0.f, 0.f});
+    const f4 gb = tile16([&](int r, int k) { return b_l[16 * wave + r][k]; },
+                         [&](int k, int c) { return gc[(16 * j + c) * N + k]; }, N,
+                         f4{0.f, 0.f, 0.f, 0.f});
+    const int p = 16 * j + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = 16 * wave + 4 * kk + r;
+      const float w = expf(cl - cum_l[s]) * dt_l[s];
+      if (t0 + s < L) dx[((b * L + t0 + s) * H + h) * P + p] = Dh * dy_l[s][p] + vdy[r] + w * gb[r];
+      xs[r] += x_l[s][p] * gb[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float v = sum16(xs[r]);
+    if (i == 0) xgb[16 * wave + 4 * kk + r] = v;
+  }
+
+  // ---- dB = diag(dt) W^T C + diag(w) X G --------------------------------------
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const f4 a1 = tile16([&](int r, int k) { return rm[k][16 * wave + r]; },
+                         [&](int k, int c) { return c_l[k][16 * j + c]; }, T,
+                         f4{0.f, 0.f, 0.f, 0.f});
+    const f4 a2 = tile16([&](int r, int k) { return x_l[16 * wave + r][k]; },
+                         [&](int k, int c) { return gc[k * N + 16 * j + c]; }, P,
+                         f4{0.f, 0.f, 0.f, 0.f});
+    const int n = 16 * j + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s = 16 * wave + 4 * kk + r;
+      const float w = expf(cl - cum_l[s]) * dt_l[s];
+      if (t0 + s < L) dBh[((b * L + t0 + s) * H + h) * N + n] = dt_l[s] * a1[r] + w * a2[r];
+    }
+  }
+
+  // ---- dC = diag(exp(cum)) dY H_in + W diag(dt) B; dY_t . (H_in C_t) ----------
+  float ys[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const f4 a1 = tile16([&](int r, int k) { return dy_l[16 * wave + r][k]; },
+                         [&](int k, int c) { return hin[state_tile_offset(k, 16 * j + c, N)]; },
+                         P, f4{0.f, 0.f, 0.f, 0.f});
+    const f4 a2 = tile16([&](int r, int k) { return rm[16 * wave + r][k] * dt_l[k]; },
+                         [&](int k, int c) { return b_l[k][16 * j + c]; }, T,
+                         f4{0.f, 0.f, 0.f, 0.f});
+    const int n = 16 * j + i;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * wave + 4 * kk + r;
+      const float e = expf(cum_l[t]) * a1[r];
+      if (t0 + t < L) dCh[((b * L + t0 + t) * H + h) * N + n] = e + a2[r];
+      ys[r] += e * c_l[t][n];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float v = sum16(ys[r]);
+    if (i == 0) yod[16 * wave + 4 * kk + r] = v;
+  }
+
+  // ---- <G, H_in> and dY . x ----------------------------------------------------
+  float gh = 0.0f, dd = 0.0f;
+  for (int64_t e = tid; e < PN; e += 256) {
+    const int p = (int)(e / N), n = (int)(e % N);
+    gh += gc[e] * hin[state_tile_offset(p, n, N)];
+  }
+  for (int e = tid; e < T * P; e += 256) dd += dy_l[e / P][e % P] * x_l[e / P][e % P];
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    gh += __shfl_xor(gh, off, kWave);
+    dd += __shfl_xor(dd, off, kWave);
+  }
+  if (lane == 0) {
+    red[wave] = gh;
+    red[4 + wave] = dd;
+  }
+  __syncthreads();
+
+  // ---- dcum, its reverse running sum, ddt_raw, the dA and dD parts -----------
+  if (wave == 0) {
+    const int t = lane;
+    const float w = expf(cl - cum_l[t]) * dt_l[t];
+    const float us = w * xgb[t];
+    float usum = us;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) usum += __shfl_xor(usum, off, kWave);
+    const float ghs = red[0] + red[1] + red[2] + red[3];
+    const float colv = colw[0][t] + colw[1][t] + colw[2][t] + colw[3][t];
+    const float col0 = col0w[0][t] + col0w[1][t] + col0w[2][t] + col0w[3][t];
+    float dc = rowv[t] + yod[t] - colv - us;
+    if (t == T - 1) dc += usum + expf(cl) * ghs;
+    // suffix sum over t
+    float rc = dc;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float o = __shfl_down(rc, off, kWave);
+      if (t + off < kWave) rc += o;
+    }
+    const float Ah = A[h];
+    const float ddt = col0 + expf(cl - cum_l[t]) * xgb[t] + Ah * rc;
+    float da = dt_l[t] * rc;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) da += __shfl_xor(da, off, kWave);
+    if (t0 + t < L) {
+      const int64_t o = (b * L + t0 + t) * H + h;
+      const float uu = dt_raw[o] + (dt_bias ? dt_bias[h] : 0.0f);
+      const float sp = softplus(uu);
+      const bool pass = sp >= dt_min && sp <= dt_max;
+      ddt_raw[o] = pass ? ddt / (1.0f + expf(-uu)) : 0.0f;
+    }
+    if (t == 0) {
+      dA_p[u] = da;
+      dD_p[u] = red[4] + red[5] + red[6] + red[7];
+    }
+  }
+}
+
+// dB and dC: sum the per-head parts over the heads of each group.
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ dBh,
+                                                            const float* __restrict__ dCh,
+                                                            float* __restrict__ dB,
+                                                            float* __restrict__ dC, int64_t n,
+                                                            int64_t H, int64_t G, int64_t N) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;  // ((b*L + t) * G + g) * N + c
+  if (k >= n) return;
+  const int64_t c = k % N, g = (k / N) % G, bt = k / (N * G);
+  const int64_t hpg = H / G;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t j = 0; j < hpg; ++j) {
+    const int64_t o = (bt * H + g * hpg + j) * N + c;
+    sb += dBh[o];
+    sc += dCh[o];
+  }
+  dB[k] = sb;
+  dC[k] = sc;
+}
+
+// dA, dD, ddt_bias: one workgroup per head, fixed summation order.
+__global__ __launch_bounds__(256) void bwd_head_sum_kernel(
+    const float* __restrict__ dA_p, const float* __restrict__ dD_p,
+    const float* __restrict__ ddt_raw, float* __restrict__ dA, float* dD, float* ddt_bias,
+    int64_t b, int64_t L, int64_t H, int64_t nb) {
+  __shared__ float red[3][4];
+  const int64_t h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  float sa = 0.0f, sd = 0.0f, sbias = 0.0f;
+  for (int64_t k = tid; k < b * nb; k += 256) {
+    sa += dA_p[k * H + h];
+    sd += dD_p[k * H + h];
+  }
+  for (int64_t k = tid; k < b * L; k += 256) sbias += ddt_raw[k * H + h];
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    sa += __shfl_xor(sa, off, kWave);
+    sd += __shfl_xor(sd, off, kWave);
+    sbias += __shfl_xor(sbias, off, kWave);
+  }
+  if (lane == 0) {
+    red[0][wave] = sa;
+    red[1][wave] = sd;
+    red[2][wave] = sbias;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dA[h] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    if (dD) dD[h] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    if (ddt_bias) ddt_bias[h] = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+  }
+}
+
+int64_t bwd_blocks(int64_t L) { return (L + kBT - 1) / kBT; }
+
+template <int N>
+static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
+  const Problem& p = q.fwd;
+  const int64_t units = p.b * p.nc * p.H;
+  hipLaunchKernelGGL((bwd_dstate_kernel<N>), dim3((unsigned)units), dim3(256), 0, s, q.dy,
+                     static_cast<const float*>(p.C), p.ws_cum, q.pc, p.L, p.H, p.G, p.nc);
+  const int64_t PN = 64 * N;
+  hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),
+                     (unsigned)p.H, (unsigned)p.b), dim3(256), 0, s, q.pc, p.ws_cum, q.dfinal,
+                     q.gst, q.dinit, p.H, p.nc, PN);
+  hipLaunchKernelGGL((block_bwd_kernel<N>), dim3((unsigned)units), dim3(256), 0, s,
+                     static_cast<const float*>(p.x), static_cast<const float*>(p.B),
+                     static_cast<const float*>(p.C), static_cast<const float*>(p.dt), p.dt_bias,
+                     p.dt_min, p.dt_max, p.A, p.D, p.ws_dt, p.ws_cum, p.ws_states_in, q.gst, q.dy,
+                     q.dx, q.dBh, q.dCh, q.ddt, q.dA_p, q.dD_p, p.L, p.H, p.G, p.nc);
+}
+
+hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
+  const Problem& p = q.fwd;
+  if (p.L > 0) {
+    const int64_t nx4 = p.b * p.L * p.H * p.P / 4;
+    hipLaunchKernelGGL(gate_bwd_kernel, dim3((unsigned)((nx4 + 255) / 256)), dim3(256), 0, s,
+                       q.dout, static_cast<const float*>(p.z), q.dy, q.dz, nx4);
+    switch (p.N) {
+      case 16: launch_bwd_n<16>(q, s); break;
+      case 32: launch_bwd_n<32>(q, s); break;
+      case 64: launch_bwd_n<64>(q, s); break;
+      case 128: launch_bwd_n<128>(q, s); break;
+    }
+    const int64_t nbc = p.b * p.L * p.G * p.N;
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
+                       s, q.dBh, q.dCh, q.dB, q.dC, nbc, p.H, p.G, p.N);
+  } else if (q.dinit) {  // no steps: the initial state's gradient is dfinal (or 0)
+    const int64_t PN = p.P * p.N;
+    hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),
+                       (unsigned)p.H, (unsigned)p.b), dim3(256), 0, s, nullptr, nullptr, q.dfinal,
+                       nullptr, q.dinit, p.H, (int64_t)0, PN);
+  }
+  hipLaunchKernelGGL(bwd_head_sum_kernel, dim3((unsigned)p.H), dim3(256), 0, s, q.dA_p, q.dD_p,
+                     q.ddt, q.dA, q.dD, q.ddt_bias, p.b, p.L, p.H, p.nc);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

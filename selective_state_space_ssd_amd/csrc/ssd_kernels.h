@@ -102,6 +102,34 @@ bool block_supported(int64_t dim, int norm_groups, int conv_width);
 hipError_t launch_conv_split(const BlockProblem& q, hipStream_t stream);
 hipError_t launch_gated_rmsnorm(const BlockProblem& q, hipStream_t stream);
 
+// Backward (ssd_backward.hip, fp32).  `fwd` is the forward problem re-run with
+// 64-step blocks (Q = 64, nc = bwd_blocks(L)) whose workspace regions hold dt,
+// cum, the chunk-local states (reused for P_c) and the states entering each
+// block; fwd.z is the gate input.
+struct BwdProblem {
+  Problem fwd;
+  const float* dout;     // [b, L, H, P]
+  const float* dfinal;   // [b, H, P, N], may be null
+  float* dy;             // [b, L, H, P]: the ungated y, then dY
+  float* pc;             // [b, nb, H] row-major P x N blocks
+  float* gst;            // [b, nb, H] row-major P x N blocks: gradient of each block's end state
+  float* dBh;            // [b, L, H, N] per-head parts of dB
+  float* dCh;            // [b, L, H, N] per-head parts of dC
+  float* dA_p;           // [b, nb, H]
+  float* dD_p;           // [b, nb, H]
+  float* dx;             // outputs
+  float* dz;             // may be null (no gate)
+  float* ddt;            // gradient of dt_raw
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;             // may be null
+  float* ddt_bias;       // may be null
+  float* dinit;          // may be null
+};
+int64_t bwd_blocks(int64_t L);
+hipError_t launch_bwd(const BwdProblem& q, hipStream_t stream);
+
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);
 

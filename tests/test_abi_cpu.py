@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
                  "ssd_timing_read", "ssd_timing_destroy", "ssd_set_option", "ssd_get_option",
                  "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size",
-                 "ssd_split_conv1d_scan_fwd", "ssd_split_conv1d_scan_fwd_workspace_size"):
+                 "ssd_split_conv1d_scan_fwd", "ssd_split_conv1d_scan_fwd_workspace_size",
+                 "ssd_scan_bwd", "ssd_scan_bwd_workspace_size"):
         assert want in names
 
 
@@ -304,6 +305,60 @@ BLOCK_CASES = [
 @pytest.mark.parametrize("desc,changes,want", BLOCK_CASES, ids=[c[0] for c in BLOCK_CASES])
 def test_block_rejected_before_launch(desc, changes, want):
     assert call_block(**changes) == want
+
+
+def test_workspace_size_backward():
+    """dt, cum [b, H, nb, 64]; two state arrays and G [b, nb, H, P N]; y/dY
+    [b, L, H, P]; dB and dC parts [b, L, H, N]; dA and dD parts [b, nb, H];
+    nb = ceil(L / 64) whatever the chunk size.  bf16 is not offered."""
+    for (b, L, H, P, N, G, Q) in SIZES:
+        nb = math.ceil(L / 64)
+        st = _r(b * nb * H * P * N * 4)
+        want = (2 * _r(b * H * nb * 64 * 4) + 3 * st + _r(b * L * H * P * 4) +
+                2 * _r(b * L * H * N * 4) + 2 * _r(b * nb * H * 4))
+        assert ssd.bwd_workspace_size(b, L, H, P, N, G, Q, 0) == want
+        assert ssd.bwd_workspace_size(b, L, H, P, N, G, Q, 1) == 0
+
+
+BWD = dict(x=0x10000000, dt=0x11000000, A=0x12000000, B=0x13000000, C=0x14000000,
+           D=0x15000000, z=0x16000000, dt_bias=0x17000000, init=None, dout=0x18000000,
+           dfinal=None, dx=0x20000000, ddt=0x21000000, dA=0x22000000, dB=0x23000000,
+           dC=0x24000000, dD=0x25000000, dz=0x26000000, ddt_bias=0x27000000, dinit=None,
+           b=1, L=100, H=4, P=64, N=16, G=1, Q=64, dtype=0, ws=None, ws_bytes=0)
+
+
+def call_bwd(**changes):
+    a = dict(BWD)
+    a.update(changes)
+    return ssd.scan_bwd_raw(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["dt_bias"],
+                            0.0, math.inf, a["Q"], a["G"], a["init"], a["dout"], a["dfinal"],
+                            a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                            a["ddt_bias"], a["dinit"], a["b"], a["L"], a["H"], a["P"], a["N"],
+                            a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+BWD_CASES = [
+    ("bf16", dict(dtype=1), UNSUPPORTED),
+    ("D given without dD", dict(dD=None), INVALID),
+    ("dz without z", dict(z=None), INVALID),
+    ("dt_bias without ddt_bias", dict(ddt_bias=None), INVALID),
+    ("null dout", dict(dout=None), INVALID),
+    ("null dA", dict(dA=None), INVALID),
+    ("dx misaligned", dict(dx=0x20000004), ALIGN),
+    ("dB misaligned", dict(dB=0x23000008), ALIGN),
+    ("dx overlaps x", dict(dx=0x10000000 + 1024), INVALID),
+    ("dB overlaps dC", dict(dB=0x24000000 - 256), INVALID),
+    ("ddt overlaps dout", dict(ddt=0x18000000 + 64), INVALID),
+    ("headdim 32", dict(P=32), UNSUPPORTED),
+    ("no workspace", dict(), WORKSPACE),
+    ("options absent (stops at workspace)",
+     dict(D=None, dD=None, z=None, dz=None, dt_bias=None, ddt_bias=None), WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("desc,changes,want", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_rejected_before_launch(desc, changes, want):
+    assert call_bwd(**changes) == want
 
 
 def test_empty_batch_is_a_no_op():

@@ -17,7 +17,8 @@ more workloads: bf16 batch 8 x seqlen 4096 and a one-token bf16 decode step
 seqlen 2048 shape holding packed sequences (seq_idx), against the fp32
 matrix roofline, and the block around the scan (conv1d prologue, gated RMSNorm
 epilogue) at the fp32 2 x 2048 size, its prologue and epilogue against the HBM
-roofline.
+roofline, and the backward (every gradient) of the fp32 2 x 2048 workload
+against the fp32 matrix roofline.
 """
 import argparse
 import json
@@ -355,6 +356,94 @@ def block_workload(steps, warmup, ngroups=1, norm_groups=1):
     }
 
 
+def bwd_alg_flops(w, T=64):
+    """Algorithmic flops of one backward call: the forward re-run in T-step
+    blocks plus, per (block, head), the causal in-block products (C.B^T once
+    per group, dY.x^T, the masked products with dY, C and B: T(T+1)/2 pairs
+    each) and the five T x P x N products with the block's states (P_c, G.B,
+    X.G, dY.H_in and the state part of dC)."""
+    from dataclasses import replace
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    nb = math.ceil(L / T)
+    fwd = sum(alg_flops(replace(w, chunk_size=T)).values())
+    pairs = T * (T + 1) / 2
+    per = 2.0 * (pairs * (P + P + 2 * N) + 5 * T * P * N)
+    return fwd + b * nb * (H * per + G * 2.0 * pairs * N)
+
+
+def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128"):
+    """The backward (every gradient, dfinal zero, z, D and dt_bias on) of the
+    fp32 batch 2 x seqlen 2048 workload at ngroups 1, alternating two input
+    copies; the forward on the same inputs is timed alongside."""
+    import torch
+    import selective_state_space_ssd_amd as ssd
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    rng = np.random.default_rng(31)
+    copies = []
+    for _ in range(2):
+        t = {k: torch.from_numpy(v).to(dev) for k, v in make_inputs(w).items()
+             if isinstance(v, np.ndarray)}
+        t["dout"] = torch.from_numpy(rng.standard_normal((b, L, H, P)).astype(np.float32)).to(dev)
+        copies.append(t)
+    e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    gr = dict(dx=e(b, L, H, P), ddt=e(b, L, H), dA=e(H), dB=e(b, L, G, N), dC=e(b, L, G, N),
+              dD=e(H), dz=e(b, L, H, P), ddt_bias=e(H))
+    wsz = ssd.bwd_workspace_size(b, L, H, P, N, G, w.chunk_size)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    fsz = ssd.workspace_size(b, L, H, P, N, G, w.chunk_size, ssd.SSD_F32)
+    fws = torch.empty(fsz, dtype=torch.uint8, device=dev)
+    out = torch.empty((b, L, H, P), device=dev)
+    s = torch.cuda.current_stream(dev).cuda_stream
+
+    def bwd_call(k):
+        t = copies[k % 2]
+        st = ssd.scan_bwd_raw(
+            t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(),
+            t["C"].data_ptr(), t["D"].data_ptr(), t["z"].data_ptr(), t["dt_bias"].data_ptr(),
+            0.0, math.inf, w.chunk_size, G, None, t["dout"].data_ptr(), None,
+            gr["dx"].data_ptr(), gr["ddt"].data_ptr(), gr["dA"].data_ptr(), gr["dB"].data_ptr(),
+            gr["dC"].data_ptr(), gr["dD"].data_ptr(), gr["dz"].data_ptr(),
+            gr["ddt_bias"].data_ptr(), None, b, L, H, P, N, ssd.SSD_F32, ws.data_ptr(), wsz, s)
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    def fwd_call(k):
+        t = copies[k % 2]
+        st = ssd.scan_fwd_raw(t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(),
+                              t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(),
+                              t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0, math.inf,
+                              w.chunk_size, G, None, out.data_ptr(), None, b, L, H, P, N,
+                              ssd.SSD_F32, fws.data_ptr(), fsz, s)
+        if st != 0:
+            raise ssd.SsdError(st, ssd.status_string(st))
+
+    res = {}
+    for nm, fn in (("bwd", bwd_call), ("fwd", fwd_call)):
+        for k in range(warmup):
+            fn(k)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            fn(k)
+        torch.cuda.synchronize()
+        res[nm] = (time.perf_counter() - t0) / steps
+    fl = bwd_alg_flops(w)
+    el = res["bwd"]
+    return {
+        "workload": "ssd_scan_bwd f32 batch 2 x seqlen 2048, 32 heads x headdim 64, dstate 128, "
+                    "ngroups 1, z gate, D and dt_bias on: every gradient (forward re-run inside)",
+        "tokens_per_s": w.tokens / el,
+        "us_per_call": el * 1e6,
+        "forward_us_per_call": res["fwd"] * 1e6,
+        "calls": steps,
+        "roofline": {"bound": "mfma", "achieved": fl / el / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS,
+                     "alg_flops": fl},
+    }
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -538,7 +627,8 @@ def main():
         line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3),
                                    decode_workload(max(20, args.steps), 5),
                                    varlen_workload(max(20, args.steps), 5),
-                                   block_workload(max(20, args.steps), 5)]
+                                   block_workload(max(20, args.steps), 5),
+                                   bwd_workload(max(10, args.steps // 2), 3)]
     print(json.dumps(line), flush=True)
 
 

@@ -41,14 +41,28 @@ namespace {
 constexpr int kBT = 64;   // block length of the backward
 constexpr int kXP = 65;   // padded row stride of 64-wide LDS tiles
 
-// acc (one 16 x 16 tile) += sum_{k < K} a(i, k) * b(k, j) for the wave:
-// lane l supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane
-// l holds the element (row 4 (l/16) + r, column l%16).
-template <typename FA, typename FB>
-__device__ __forceinline__ f4 tile16(FA a, FB b, int K, f4 acc) {
+// One 16 x 16 output tile of a wave on v_mfma_f32_16x16x4_f32: lane l
+// supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane l holds
+// the element (row 4 (l/16) + r, column l%16).
+//
+// NJ tiles of one 16-row strip at once: acc[j] += sum_k a(i, k) * b(j, k, c).
+// The A value is shared by the NJ independent accumulators, so consecutive
+// MFMAs never wait on each other, and the unrolled k loop lets the operand
+// loads of later steps issue early.
+template <int NJ, int K, typename FA, typename FB>
+__device__ __forceinline__ void tiles16(FA a, FB b, f4 (&acc)[NJ]) {
   const int lane = threadIdx.x % kWave, i = lane % 16, kk = lane / 16;
-  for (int k = 0; k < K; k += 4) acc = mfma16x16x4(a(i, k + kk), b(k + kk, i), acc);
-  return acc;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = 0; k < K; k += 4) {
+    const float av = a(i, k + kk);
+    float bv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bv[j] = b(j, k + kk, i);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = mfma16x16x4(av, bv[j], acc[j]);
+  }
 }
 }  // namespace
 
@@ -90,26 +104,43 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(
   const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
   const int64_t g = h / (H / G), t0 = blk * kBT;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  for (int e = tid; e < kBT * P; e += 256) {
-    const int t = e / P, p = e % P;
-    dy_l[t][p] = t0 + t < L ? dy[((b * L + t0 + t) * H + h) * P + p] : 0.0f;
-  }
-  for (int e = tid; e < kBT * N; e += 256) {
-    const int t = e / N, n = e % N;
-    c_l[t][n] = t0 + t < L ? Cm[((b * L + t0 + t) * G + g) * N + n] : 0.0f;
+  const int last = (int)((L - 1 - t0) < (kBT - 1) ? (L - 1 - t0) : (kBT - 1));
+  {  // 16-byte loads, all in flight, from rows clamped to the last real one
+    f4 yv[kBT * P / 1024], cv[kBT * N / 1024];
+#pragma unroll
+    for (int q = 0; q < kBT * P / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
+      yv[q] = ld4(dy + ((b * L + t0 + (t < last ? t : last)) * H + h) * P + p);
+    }
+#pragma unroll
+    for (int q = 0; q < kBT * N / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
+      cv[q] = ld4(Cm + ((b * L + t0 + (t < last ? t : last)) * G + g) * N + n);
+    }
+#pragma unroll
+    for (int q = 0; q < kBT * P / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dy_l[t][p + c] = t <= last ? yv[q][c] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kBT * N / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) c_l[t][n + c] = t <= last ? cv[q][c] : 0.0f;
+    }
   }
   if (tid < kBT) e_l[tid] = expf(ws_cum[((b * H + h) * nb + blk) * kBT + tid]);
   __syncthreads();
   float* dst = pc + u * (int64_t)(P * N);
   const int i = lane % 16, kk = lane / 16;
+  f4 acc[NJ];
+  tiles16<NJ, kBT>([&](int r, int k) { return dy_l[k][16 * wave + r] * e_l[k]; },
+                   [&](int j, int k, int c) { return c_l[k][16 * j + c]; }, acc);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-    acc = tile16([&](int r, int k) { return dy_l[k][16 * wave + r] * e_l[k]; },
-                 [&](int k, int c) { return c_l[k][16 * j + c]; }, kBT, acc);
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * kk + r) * N + 16 * j + i] = acc[r];
-  }
+    for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * kk + r) * N + 16 * j + i] = acc[j][r];
 }
 
 // Reverse state passing: G_c (gradient of the state leaving block c, stored
@@ -131,7 +162,18 @@ __global__ __launch_bounds__(256) void bwd_state_passing_kernel(
   if (dinit) st4(dinit + (b * H + h) * PN + 4 * k, gv);
 }
 
-// One workgroup (four waves) per (batch, block, head).
+// One workgroup (four waves) per (batch, block, head).  Everything the products
+// read is staged in one LDS buffer with 16-byte global loads, regions reused
+// as they die (floats; rows padded by one against bank conflicts):
+//   [0, 4160)       x [64][65]                 | then H_in [64][129] over
+//   [4160, 8256)    V [64][64]  (K, then V)    |   x and V (dC phase)
+//   [8256, 12416)   W [64][65]  (R, then W)    G [64][129] over V and W
+//   [12416, 16576)  dY [64][65]                  (first phase)
+//   [16576, 24832)  B [64][129]
+//   [24832, 33088)  C [64][129]
+// Phases: the products with G (G.B for dX, X.G for dB, x . (G B)) with G in
+// LDS, kept in registers; K and R, then V and W in place of G; dX and dB;
+// H_in over x and V, then dC and dY_t . (H_in C_t); the decay gradients.
 template <int N>
 __global__ __launch_bounds__(256) void block_bwd_kernel(
     const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
@@ -143,10 +185,18 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     float* __restrict__ dCh, float* __restrict__ ddt_raw, float* __restrict__ dA_p,
     float* __restrict__ dD_p, int64_t L, int64_t H, int64_t G, int64_t nb) {
   constexpr int P = 64, T = kBT, NJ = N / 16, NS = N + 1;
-  __shared__ float x_l[T][kXP], dy_l[T][kXP];
-  __shared__ float b_l[T][NS], c_l[T][NS];
-  __shared__ float km[T][kXP];  // K, then V = M o K diag(dt)
-  __shared__ float rm[T][kXP];  // R, then W = M o R
+  constexpr int OX = 0, OV = 4160, OW = 8256, OY = 12416, OB = 16576, OC = OB + T * NS;
+  static_assert(T * kXP == 4160 && OV + T * 64 == OW && OW + T * kXP == OY &&
+                OY + T * kXP == OB && T * NS <= OV + T * 64 && T * NS <= OY - OV, "LDS map");
+  __shared__ __align__(16) float lds[OC + T * NS];
+  float* const xs_ = lds + OX;   // x[t][p]      stride 65
+  float* const vm = lds + OV;    // K, then V    stride 64
+  float* const wm = lds + OW;    // R, then W    stride 65
+  float* const ys_ = lds + OY;   // dY[t][p]     stride 65
+  float* const bs_ = lds + OB;   // B[t][n]      stride N+1
+  float* const cs_ = lds + OC;   // C[t][n]      stride N+1
+  float* const gs_ = lds + OV;   // G[p][n]      stride N+1 (first phase)
+  float* const hs_ = lds + OX;   // H_in[p][n]   stride N+1 (dC phase)
   __shared__ float cum_l[T], dt_l[T];
   __shared__ float rowv[T], xgb[T], yod[T], red[8];
   __shared__ float colw[4][T], col0w[4][T];  // per-wave column sums, added in order
@@ -159,21 +209,54 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   const int64_t PN = (int64_t)P * N;
   const float* hin = states_in + u * PN;  // tiled layout
   const float* gc = gst + u * PN;         // row-major [P][N]
+  const int last = (int)((L - 1 - t0) < (T - 1) ? (L - 1 - t0) : (T - 1));
 
-  // ---- stage x, dY, B, C, cum, dt (rows past the end are zero) --------------
-  for (int e = tid; e < T * P; e += 256) {
-    const int t = e / P, p = e % P;
-    const bool ok = t0 + t < L;
-    const int64_t o = ((b * L + t0 + t) * H + h) * P + p;
-    x_l[t][p] = ok ? x[o] : 0.0f;
-    dy_l[t][p] = ok ? dy[o] : 0.0f;
-  }
-  for (int e = tid; e < T * N; e += 256) {
-    const int t = e / N, n = e % N;
-    const bool ok = t0 + t < L;
-    const int64_t o = ((b * L + t0 + t) * G + g) * N + n;
-    b_l[t][n] = ok ? Bm[o] : 0.0f;
-    c_l[t][n] = ok ? Cm[o] : 0.0f;
+  // ---- stage x, dY, B, C, G, cum, dt (rows past the end are zero) -----------
+  // rows are read from the last real row (always in bounds) and zeroed after
+  {
+    f4 xv[T * P / 1024], yv[T * P / 1024], bv[T * N / 1024], cv[T * N / 1024], gv[P * N / 1024];
+#pragma unroll
+    for (int q = 0; q < T * P / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
+      const int64_t o = ((b * L + t0 + (t < last ? t : last)) * H + h) * P + p;
+      xv[q] = ld4(x + o);
+      yv[q] = ld4(dy + o);
+    }
+#pragma unroll
+    for (int q = 0; q < T * N / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
+      const int64_t o = ((b * L + t0 + (t < last ? t : last)) * G + g) * N + n;
+      bv[q] = ld4(Bm + o);
+      cv[q] = ld4(Cm + o);
+    }
+#pragma unroll
+    for (int q = 0; q < P * N / 1024; ++q) gv[q] = ld4(gc + 4 * (q * 256 + tid));
+#pragma unroll
+    for (int q = 0; q < T * P / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
+      const bool ok = t <= last;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        xs_[t * kXP + p + c] = ok ? xv[q][c] : 0.0f;
+        ys_[t * kXP + p + c] = ok ? yv[q][c] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < T * N / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
+      const bool ok = t <= last;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bs_[t * NS + n + c] = ok ? bv[q][c] : 0.0f;
+        cs_[t * NS + n + c] = ok ? cv[q][c] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < P * N / 1024; ++q) {
+      const int e = 4 * (q * 256 + tid), p = e / N, n = e % N;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gs_[p * NS + n + c] = gv[q][c];
+    }
   }
   if (tid < T) {
     const int64_t o = ((b * H + h) * nb + blk) * T + tid;
@@ -198,15 +281,39 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     return v + __shfl_xor(v, 32, kWave);
   };
 
+  // ---- products with G: GB[s][p] = B_s . G_p (dX), XG[s][n] = x_s^T G (dB) --
+  // wave w: rows s in [16w, 16w+16)
+  f4 gball[4], xgall[NJ];
+  tiles16<4, N>([&](int r, int k) { return bs_[(16 * wave + r) * NS + k]; },
+                [&](int j, int k, int c) { return gs_[(16 * j + c) * NS + k]; }, gball);
+  tiles16<NJ, P>([&](int r, int k) { return xs_[(16 * wave + r) * kXP + k]; },
+                 [&](int j, int k, int c) { return gs_[k * NS + 16 * j + c]; }, xgall);
+  {
+    float xsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        xsum[r] += xs_[(16 * wave + 4 * kk + r) * kXP + 16 * j + i] * gball[j][r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = sum16(xsum[r]);
+      if (i == 0) xgb[16 * wave + 4 * kk + r] = v;
+    }
+  }
+  __syncthreads();  // G is dead: V and W take its place
+
   // ---- K = C B^T and R = dY X^T; masks, decays and the dcum sums -------------
   // wave w: rows t in [16w, 16w+16), four column tiles of s
   float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+  f4 kall[4], rall[4];
+  tiles16<4, N>([&](int r, int k) { return cs_[(16 * wave + r) * NS + k]; },
+                [&](int j, int k, int c) { return bs_[(16 * j + c) * NS + k]; }, kall);
+  tiles16<4, P>([&](int r, int k) { return ys_[(16 * wave + r) * kXP + k]; },
+                [&](int j, int k, int c) { return xs_[(16 * j + c) * kXP + k]; }, rall);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f4 kacc = tile16([&](int r, int k) { return c_l[16 * wave + r][k]; },
-                     [&](int k, int c) { return b_l[16 * j + c][k]; }, N, f4{0.f, 0.f, 0.f, 0.f});
-    f4 racc = tile16([&](int r, int k) { return dy_l[16 * wave + r][k]; },
-                     [&](int k, int c) { return x_l[16 * j + c][k]; }, P, f4{0.f, 0.f, 0.f, 0.f});
+    const f4 kacc = kall[j], racc = rall[j];
     const int s = 16 * j + i;
     float cs = 0.0f, cs0 = 0.0f;
 #pragma unroll
@@ -215,8 +322,8 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
       const float m = s <= t ? expf(cum_l[t] - cum_l[s]) : 0.0f;
       const float v0 = m * kacc[r] * racc[r];
       const float v = v0 * dt_l[s];
-      km[t][s] = m * kacc[r] * dt_l[s];
-      rm[t][s] = m * racc[r];
+      vm[t * 64 + s] = m * kacc[r] * dt_l[s];
+      wm[t * kXP + s] = m * racc[r];
       rsum[r] += v;
       cs += v;
       cs0 += v0;
@@ -235,81 +342,92 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   }
   __syncthreads();
 
-  // ---- dX = D dY + V^T dY + diag(w) B G^T; x . (G B) per row ----------------
-  float xs[4] = {0.f, 0.f, 0.f, 0.f};
+  // ---- dX = D dY + V^T dY + diag(w) GB;  dB = diag(dt) W^T C + diag(w) XG ----
+  {
+    f4 vall[4];
+    tiles16<4, T>([&](int r, int k) { return vm[k * 64 + 16 * wave + r]; },
+                  [&](int j, int k, int c) { return ys_[k * kXP + 16 * j + c]; }, vall);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f4 vdy = tile16([&](int r, int k) { return km[k][16 * wave + r]; },
-                          [&](int k, int c) { return dy_l[k][16 * j + c]; }, T,
-                          f4{0.f, 0.f, 0.f, 0.f});
-    const f4 gb = tile16([&](int r, int k) { return b_l[16 * wave + r][k]; },
-                         [&](int k, int c) { return gc[(16 * j + c) * N + k]; }, N,
-                         f4{0.f, 0.f, 0.f, 0.f});
-    const int p = 16 * j + i;
+    for (int j = 0; j < 4; ++j) {
+      const int p = 16 * j + i;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = 16 * wave + 4 * kk + r;
-      const float w = expf(cl - cum_l[s]) * dt_l[s];
-      if (t0 + s < L) dx[((b * L + t0 + s) * H + h) * P + p] = Dh * dy_l[s][p] + vdy[r] + w * gb[r];
-      xs[r] += x_l[s][p] * gb[r];
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * wave + 4 * kk + r;
+        const float w = expf(cl - cum_l[s]) * dt_l[s];
+        if (s <= last)
+          dx[((b * L + t0 + s) * H + h) * P + p] = Dh * ys_[s * kXP + p] + vall[j][r] + w * gball[j][r];
+      }
+    }
+    f4 a1[NJ];
+    tiles16<NJ, T>([&](int r, int k) { return wm[k * kXP + 16 * wave + r]; },
+                   [&](int j, int k, int c) { return cs_[k * NS + 16 * j + c]; }, a1);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = 16 * j + i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * wave + 4 * kk + r;
+        const float w = expf(cl - cum_l[s]) * dt_l[s];
+        if (s <= last) dBh[((b * L + t0 + s) * H + h) * N + n] = dt_l[s] * a1[j][r] + w * xgall[j][r];
+      }
     }
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float v = sum16(xs[r]);
-    if (i == 0) xgb[16 * wave + 4 * kk + r] = v;
-  }
+  float dd = 0.0f;  // dY . x over the block
+  for (int e = tid; e < T * P; e += 256) dd += ys_[(e / P) * kXP + e % P] * xs_[(e / P) * kXP + e % P];
+  __syncthreads();  // x and V are dead: H_in takes their place
 
-  // ---- dB = diag(dt) W^T C + diag(w) X G --------------------------------------
+  // ---- H_in into LDS, with <G, H_in> on the way ------------------------------
+  float gh = 0.0f;
+  {
+    f4 hv[P * N / 1024], gv2[P * N / 1024];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const f4 a1 = tile16([&](int r, int k) { return rm[k][16 * wave + r]; },
-                         [&](int k, int c) { return c_l[k][16 * j + c]; }, T,
-                         f4{0.f, 0.f, 0.f, 0.f});
-    const f4 a2 = tile16([&](int r, int k) { return x_l[16 * wave + r][k]; },
-                         [&](int k, int c) { return gc[k * N + 16 * j + c]; }, P,
-                         f4{0.f, 0.f, 0.f, 0.f});
-    const int n = 16 * j + i;
+    for (int q = 0; q < P * N / 1024; ++q) {
+      const int k4 = q * 256 + tid;  // float4 index in the tiled block
+      int p, n;
+      state_tile_coords(k4, N, &p, &n);
+      hv[q] = ld4(hin + 4 * k4);
+      gv2[q] = ld4(gc + p * N + n);
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int s = 16 * wave + 4 * kk + r;
-      const float w = expf(cl - cum_l[s]) * dt_l[s];
-      if (t0 + s < L) dBh[((b * L + t0 + s) * H + h) * N + n] = dt_l[s] * a1[r] + w * a2[r];
+    for (int q = 0; q < P * N / 1024; ++q) {
+      int p, n;
+      state_tile_coords(q * 256 + tid, N, &p, &n);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        hs_[p * NS + n + c] = hv[q][c];
+        gh += hv[q][c] * gv2[q][c];
+      }
     }
   }
+  __syncthreads();
 
   // ---- dC = diag(exp(cum)) dY H_in + W diag(dt) B; dY_t . (H_in C_t) ----------
-  float ys[4] = {0.f, 0.f, 0.f, 0.f};
+  float ysum[4] = {0.f, 0.f, 0.f, 0.f};
+  {
+    f4 a1[NJ], a2[NJ];
+    tiles16<NJ, P>([&](int r, int k) { return ys_[(16 * wave + r) * kXP + k]; },
+                   [&](int j, int k, int c) { return hs_[k * NS + 16 * j + c]; }, a1);
+    tiles16<NJ, T>([&](int r, int k) { return wm[(16 * wave + r) * kXP + k] * dt_l[k]; },
+                   [&](int j, int k, int c) { return bs_[k * NS + 16 * j + c]; }, a2);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const f4 a1 = tile16([&](int r, int k) { return dy_l[16 * wave + r][k]; },
-                         [&](int k, int c) { return hin[state_tile_offset(k, 16 * j + c, N)]; },
-                         P, f4{0.f, 0.f, 0.f, 0.f});
-    const f4 a2 = tile16([&](int r, int k) { return rm[16 * wave + r][k] * dt_l[k]; },
-                         [&](int k, int c) { return b_l[k][16 * j + c]; }, T,
-                         f4{0.f, 0.f, 0.f, 0.f});
-    const int n = 16 * j + i;
+    for (int j = 0; j < NJ; ++j) {
+      const int n = 16 * j + i;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * kk + r;
-      const float e = expf(cum_l[t]) * a1[r];
-      if (t0 + t < L) dCh[((b * L + t0 + t) * H + h) * N + n] = e + a2[r];
-      ys[r] += e * c_l[t][n];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * wave + 4 * kk + r;
+        const float e = expf(cum_l[t]) * a1[j][r];
+        if (t <= last) dCh[((b * L + t0 + t) * H + h) * N + n] = e + a2[j][r];
+        ysum[r] += e * cs_[t * NS + n];
+      }
     }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float v = sum16(ys[r]);
+    const float v = sum16(ysum[r]);
     if (i == 0) yod[16 * wave + 4 * kk + r] = v;
   }
 
-  // ---- <G, H_in> and dY . x ----------------------------------------------------
-  float gh = 0.0f, dd = 0.0f;
-  for (int64_t e = tid; e < PN; e += 256) {
-    const int p = (int)(e / N), n = (int)(e % N);
-    gh += gc[e] * hin[state_tile_offset(p, n, N)];
-  }
-  for (int e = tid; e < T * P; e += 256) dd += dy_l[e / P][e % P] * x_l[e / P][e % P];
+  // ---- <G, H_in> and dY . x across the workgroup ------------------------------
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     gh += __shfl_xor(gh, off, kWave);
@@ -346,7 +464,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     float da = dt_l[t] * rc;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) da += __shfl_xor(da, off, kWave);
-    if (t0 + t < L) {
+    if (t <= last) {
       const int64_t o = (b * L + t0 + t) * H + h;
       const float uu = dt_raw[o] + (dt_bias ? dt_bias[h] : 0.0f);
       const float sp = softplus(uu);

@@ -198,6 +198,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   float* const gs_ = lds + OV;   // G[p][n]      stride N+1 (first phase)
   float* const hs_ = lds + OX;   // H_in[p][n]   stride N+1 (dC phase)
   __shared__ float cum_l[T], dt_l[T];
+  __shared__ float ecum[T], wdt[T];  // exp(cum_t); w_t = exp(cl - cum_t) dt_t
   __shared__ float rowv[T], xgb[T], yod[T], red[8];
   __shared__ float colw[4][T], col0w[4][T];  // per-wave column sums, added in order
 
@@ -260,8 +261,11 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   }
   if (tid < T) {
     const int64_t o = ((b * H + h) * nb + blk) * T + tid;
-    cum_l[tid] = ws_cum[o];
-    dt_l[tid] = ws_dt[o];
+    const float c = ws_cum[o], d = ws_dt[o];
+    cum_l[tid] = c;
+    dt_l[tid] = d;
+    ecum[tid] = expf(c);
+    wdt[tid] = expf(ws_cum[o - tid + T - 1] - c) * d;
   }
   __syncthreads();
   const float cl = cum_l[T - 1];
@@ -353,9 +357,8 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * wave + 4 * kk + r;
-        const float w = expf(cl - cum_l[s]) * dt_l[s];
         if (s <= last)
-          dx[((b * L + t0 + s) * H + h) * P + p] = Dh * ys_[s * kXP + p] + vall[j][r] + w * gball[j][r];
+          dx[((b * L + t0 + s) * H + h) * P + p] = Dh * ys_[s * kXP + p] + vall[j][r] + wdt[s] * gball[j][r];
       }
     }
     f4 a1[NJ];
@@ -367,8 +370,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * wave + 4 * kk + r;
-        const float w = expf(cl - cum_l[s]) * dt_l[s];
-        if (s <= last) dBh[((b * L + t0 + s) * H + h) * N + n] = dt_l[s] * a1[j][r] + w * xgall[j][r];
+        if (s <= last) dBh[((b * L + t0 + s) * H + h) * N + n] = dt_l[s] * a1[j][r] + wdt[s] * xgall[j][r];
       }
     }
   }
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wave + 4 * kk + r;
-        const float e = expf(cum_l[t]) * a1[j][r];
+        const float e = ecum[t] * a1[j][r];
         if (t <= last) dCh[((b * L + t0 + t) * H + h) * N + n] = e + a2[j][r];
         ysum[r] += e * cs_[t * NS + n];
       }
@@ -442,8 +444,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   // ---- dcum, its reverse running sum, ddt_raw, the dA and dD parts -----------
   if (wave == 0) {
     const int t = lane;
-    const float w = expf(cl - cum_l[t]) * dt_l[t];
-    const float us = w * xgb[t];
+    const float us = wdt[t] * xgb[t];
     float usum = us;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) usum += __shfl_xor(usum, off, kWave);

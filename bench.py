@@ -225,25 +225,33 @@ def varlen_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mea
     import selective_state_space_ssd_amd as ssd
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
-    ws_bytes = ssd.varlen_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                                         w.ngroups, w.chunk_size, ssd.SSD_F32)
+    code = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
+    ws_bytes = max(ssd.varlen_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                             w.ngroups, w.chunk_size, code),
+                   ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                      w.ngroups, w.chunk_size, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     seq = torch.from_numpy(make_seq_idx(w.batch, w.seqlen, mean_len, 77)).to(dev)
     keep, calls = [], []
-    for _ in range(2):
-        t = {k: torch.from_numpy(v).to(dev) for k, v in make_inputs(w).items()
+    for _ in range(2 if w.dtype == "f32" else 1):
+        inp = make_inputs(w)
+        t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items()
              if isinstance(v, np.ndarray)}
+        if w.dtype == "bf16":
+            for k in ("x", "z", "B", "C", "dt"):
+                t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
         out = torch.empty_like(t["x"])
-        keep.append((t, out))
+        fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), device=dev)
+        keep.append((t, out, fin))
         calls.append((t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(),
                       t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(),
                       t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0, math.inf, w.chunk_size,
-                      w.ngroups, None, out.data_ptr(), None))
-    tail = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, ssd.SSD_F32, ws.data_ptr(),
+                      w.ngroups, None, out.data_ptr(), fin.data_ptr() if w.final else None))
+    tail = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, code, ws.data_ptr(),
             ws_bytes, torch.cuda.current_stream(dev).cuda_stream)
 
     def run(k, packed):
-        a = calls[k % 2]
+        a = calls[k % len(calls)]
         st = (ssd.scan_fwd_varlen_raw(*a, seq.data_ptr(), *tail) if packed
               else ssd.scan_fwd_raw(*a, *tail))
         if st != 0:
@@ -260,20 +268,29 @@ def varlen_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mea
         torch.cuda.synchronize()
         res[packed] = (time.perf_counter() - t0) / steps
     el = res[True]
-    fl = sum(alg_flops(w).values())
     nseq = int((seq[:, 1:] != seq[:, :-1]).sum().item()) + w.batch
-    return {
-        "workload": f"ssd_scan_fwd_varlen f32 batch 2 x seqlen 2048 holding {nseq} packed "
-                    f"sequences (mean length {mean_len}), 32 heads x headdim 64, dstate 128, "
-                    "chunk 128, ngroups 1, z gate and D on",
+    line = {
+        "workload": f"ssd_scan_fwd_varlen {w.dtype} batch {w.batch} x seqlen {w.seqlen} holding "
+                    f"{nseq} packed sequences (mean length {mean_len}), {w.nheads} heads x "
+                    f"headdim 64, dstate {w.dstate}, chunk {w.chunk_size}, ngroups {w.ngroups}, "
+                    "z gate and D on",
+        "path": "staged" if w.dtype == "f32" else ssd.get_bf16_path(),
         "tokens_per_s": w.tokens / el,
         "us_per_call": el * 1e6,
         "plain_us_per_call": res[False] * 1e6,
         "calls": steps,
-        "roofline": {"bound": "mfma", "achieved": fl / el / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS,
-                     "alg_flops": fl},
     }
+    if w.dtype == "f32":  # matrix-bound, like the plain fp32 workload
+        fl = sum(alg_flops(w).values())
+        line["roofline"] = {"bound": "mfma", "achieved": fl / el / 1e12,
+                            "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                            "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS, "alg_flops": fl}
+    else:  # HBM-bound, like the plain bf16 workload
+        nbytes = alg_bytes(w) + w.batch * w.seqlen * 4
+        line["roofline"] = {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
+                            "alg_bytes": nbytes}
+    return line
 
 
 def block_workload(steps, warmup, ngroups=1, norm_groups=1):
@@ -627,6 +644,8 @@ def main():
         line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3),
                                    decode_workload(max(20, args.steps), 5),
                                    varlen_workload(max(20, args.steps), 5),
+                                   varlen_workload(max(5, args.steps // 5), 3,
+                                                   "bf16_b8_L4096_H64_P64_N128_G8_Q256", 512),
                                    block_workload(max(20, args.steps), 5),
                                    bwd_workload(max(10, args.steps // 2), 3)]
     print(json.dumps(line), flush=True)

@@ -183,9 +183,11 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
  * final_states the state after the row's last step (its last sequence).
  * Every other argument, the checks and the execution rules are those of
  * ssd_scan_fwd; `out` must not overlap seq_idx either.  The call takes the
- * staged path (or, for seqlen <= 16, the step kernel) whatever the bf16 path
- * option, and needs ssd_scan_fwd_varlen_workspace_size(...) bytes of
- * workspace: the staged layout above followed, on a 256-byte boundary, by
+ * same path as ssd_scan_fwd (the fused bf16 kernel counts the sequence
+ * starts itself; with SSD_BF16_PATH_FUSED_GROUP it runs the per-head form)
+ * and needs ssd_scan_fwd_varlen_workspace_size(...) bytes of workspace: on
+ * the fused path the fused layout, on the staged path the staged layout
+ * followed, on a 256-byte boundary, by
  *   seg [batch, nchunks, chunk_size] int32: for step q of chunk c the number
  *       of sequence starts at steps c*chunk_size .. c*chunk_size + q (steps
  *       past the sequence end repeat the last count).

@@ -61,8 +61,9 @@ bool fused_path(int dtype, int64_t headdim, int64_t dstate) {
 }
 
 // Shape checks shared by the workspace query and the entry point.
-// varlen: the call carries seq_idx (packed sequences); it takes the staged
-// path and its workspace ends with the per-chunk sequence-start counts.
+// varlen: the call carries seq_idx (packed sequences).  On the staged path its
+// workspace ends with the per-chunk sequence-start counts; the fused bf16
+// kernel counts the starts itself.
 int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                  int ngroups, int chunk_size, int dtype, bool varlen, Layout* lay) {
   if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
@@ -91,7 +92,7 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     lay->total = 0;
     return SSD_OK;
   }
-  if (!varlen && fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
+  if (fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
     const int64_t nblk = ssd::fused_blocks(seqlen);
     int64_t nchain, grid, ringn, flagn;
     if (!mul_ok(batch, nheads, &nchain) || !mul_ok(nchain, nblk, &grid) ||

@@ -27,6 +27,15 @@
 // when workgroups are dealt round-robin to the XCDs.  The wait is bounded:
 // past the limit the workgroup records an error word and carries on.
 //
+// Packed sequences (seq_idx): wave 0 counts the sequence starts k_t from the
+// block's first step to t alongside dt; the masks ride on the per-step
+// factors already held in LDS -- w_t (only the block's last sequence reaches
+// its end state), u_s and the per-lane decay of an s-tile (pairs of one
+// sequence; k is monotone in t, so [k_s = k_t] = [k_s = k_e][k_e = k_t] for
+// the tile's last step e), exp(cum_t) (only the first sequence sees the
+// entering state) -- plus a compare on the diagonal tile, and a block with a
+// start drops the carried state.
+//
 // Operand precision as in the staged bf16 kernels: x, B, C enter the matrix
 // cores as they are; the decay-weighted B^T, the entering state and the
 // decay-masked C B^T values are split into hi/lo bf16 pairs.
@@ -156,8 +165,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
     const bf16_t* __restrict__ dt_raw, const float* __restrict__ A,
     const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Dv,
     const bf16_t* __restrict__ z, bf16_t* __restrict__ out, float* __restrict__ final_states,
-    float* __restrict__ ring, unsigned* __restrict__ flags, unsigned* __restrict__ ctl, int64_t L,
-    int64_t H, int64_t G, int64_t nblk, int64_t nchain, int nclass, unsigned spin_limit) {
+    float* __restrict__ ring, unsigned* __restrict__ flags, unsigned* __restrict__ ctl,
+    const int32_t* __restrict__ seq, int64_t L, int64_t H, int64_t G, int64_t nblk,
+    int64_t nchain, int nclass, unsigned spin_limit) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
   constexpr int KS = N / 16;                // k-steps over n
   constexpr int NPT = N == 128 ? 2 : 1;     // p-halves of the block state per wave
@@ -169,6 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
   __shared__ __align__(16) float w_lds[FQ];           // exp(cum_last - cum_t) dt_t
   __shared__ __align__(16) float u_lds[FQ];           // exp(cum_end(tile of s) - cum_s) dt_s
   __shared__ __align__(16) float et_lds[FQ];          // exp(cum_t)
+  __shared__ __align__(16) int32_t kseq_lds[FQ];      // sequence starts from the block start
   __shared__ float dlast_lds;
   __shared__ unsigned ticket_lds;
 
@@ -203,16 +214,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
                                L, H, nblk, nullptr, nullptr, dtv, cum, &cum_last);
     // lane l holds t = 2l, 2l + 1; the last step of its 32-step tile is lane 16 (l/16) + 15
     const float cend = __shfl(cum[1], 16 * (lane / 16) + 15, kWave);
+    // packed sequences: running count of starts over the block (0 without seq)
+    int ks[E] = {0, 0};
+    if (seq) {
+      int run = 0;
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const int64_t tt = t0 + lane * E + k;
+        if (tt >= 1 && tt < L) run += seq[b * L + tt] != seq[b * L + tt - 1];
+        ks[k] = run;
+      }
+      int incl = run;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += v;
+      }
+#pragma unroll
+      for (int k = 0; k < E; ++k) ks[k] += incl - run;
+    }
+    const int kend = __shfl(ks[1], 16 * (lane / 16) + 15, kWave);
+    const int klast = __shfl(ks[1], kWave - 1, kWave);
 #pragma unroll
     for (int k = 0; k < E; ++k) {
       const int t = lane * E + k;
       cum2_lds[t] = cum[k] * kLog2e;
       dt_lds[t] = dtv[k];
-      w_lds[t] = __expf(cum_last - cum[k]) * dtv[k];
-      u_lds[t] = __expf(cend - cum[k]) * dtv[k];
-      et_lds[t] = __expf(cum[k]);
+      w_lds[t] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
+      u_lds[t] = ks[k] == kend ? __expf(cend - cum[k]) * dtv[k] : 0.0f;
+      et_lds[t] = ks[k] == 0 ? __expf(cum[k]) : 0.0f;
+      kseq_lds[t] = ks[k];
     }
-    if (lane == 0) dlast_lds = __expf(cum_last);
+    // a start inside the block drops the carried state (marked by -1)
+    if (lane == 0) dlast_lds = klast == 0 ? __expf(cum_last) : -1.0f;
   }
 #pragma unroll
   for (int k = 0; k < XTile<FQ>::ITER; ++k) {  // x tile, permuted columns, swizzled chunks
@@ -259,6 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
       }
     }
     const float ct = cum2_lds[32 * ti + i];
+    const int kt = kseq_lds[32 * ti + i];
     f16x acc = zero16();
     for (int si = 0; si <= ti; ++si) {
       f16x gt = zero16();
@@ -271,7 +306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
       // register r: s = 32 si + 8 (r/4) + 4 kk + r%4, t = 32 ti + i
       float mv[16];
       if (si < ti) {
-        const float rs = fexp2(ct - cum2_lds[32 * si + 31]);
+        const float rs = kt == kseq_lds[32 * si + 31] ? fexp2(ct - cum2_lds[32 * si + 31]) : 0.0f;
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
           const f4 u = *reinterpret_cast<const f4*>(u_lds + 32 * si + 8 * R + 4 * kk);
@@ -283,11 +318,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
         for (int R = 0; R < 4; ++R) {
           const f4 cs = *reinterpret_cast<const f4*>(cum2_lds + 32 * si + 8 * R + 4 * kk);
           const f4 ds = *reinterpret_cast<const f4*>(dt_lds + 32 * si + 8 * R + 4 * kk);
+          const int4 k4 = *reinterpret_cast<const int4*>(kseq_lds + 32 * si + 8 * R + 4 * kk);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int sl = 8 * R + 4 * kk + q;
+            const int kq = q == 0 ? k4.x : q == 1 ? k4.y : q == 2 ? k4.z : k4.w;
             const float v = gt[4 * R + q] * fexp2(ct - cs[q]) * ds[q];
-            mv[4 * R + q] = sl < i ? v : (sl == i ? v + Dh : 0.0f);
+            mv[4 * R + q] = sl < i ? (kq == kt ? v : 0.0f) : (sl == i ? v + Dh : 0.0f);
           }
         }
       }
@@ -391,7 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
         const f4 hv = hreg[j][R];
         f4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = dl * hv[e] + sacc[j][4 * R + e];
+        for (int e = 0; e < 4; ++e) v[e] = dl < 0.0f ? sacc[j][4 * R + e] : dl * hv[e] + sacc[j][4 * R + e];
         if (more)
           st4_agent(hout, kP * N * 4, 4 * state_tile_offset(p, n0, N), v);
         else if (final_states)
@@ -536,17 +573,20 @@ static void launch_fused_n(const Problem& p, hipStream_t s, int stage) {
   if (p.z)
     hipLaunchKernelGGL((fused_scan_bf16_kernel<N, true>), grid, dim3(256), 0, s, xb, Bb, Cb, db,
                        p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.final_states, p.fs_ring,
-                       p.fs_flags, p.fs_ctl, p.L, p.H, p.G, nblk, nchain, nclass, spin_limit);
+                       p.fs_flags, p.fs_ctl, p.seq_idx, p.L, p.H, p.G, nblk, nchain, nclass,
+                       spin_limit);
   else
     hipLaunchKernelGGL((fused_scan_bf16_kernel<N, false>), grid, dim3(256), 0, s, xb, Bb, Cb, db,
                        p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.final_states, p.fs_ring,
-                       p.fs_flags, p.fs_ctl, p.L, p.H, p.G, nblk, nchain, nclass, spin_limit);
+                       p.fs_flags, p.fs_ctl, p.seq_idx, p.L, p.H, p.G, nblk, nchain, nclass,
+                       spin_limit);
 }
 
 hipError_t launch_fused_bf16(const Problem& p, hipStream_t s, int stage) {
   // the group kernel runs only when asked for: on the measured workloads the
-  // per-head kernel is faster (its workgroups hide each other's latency)
-  const bool group = stage == 1 && p.fused_kind == 2;
+  // per-head kernel is faster (its workgroups hide each other's latency); it
+  // does not take packed sequences
+  const bool group = stage == 1 && p.fused_kind == 2 && !p.seq_idx;
   if (group) return launch_fused_group_bf16(p, s);
   if (p.N == 128)
     launch_fused_n<128>(p, s, stage);

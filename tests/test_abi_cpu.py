@@ -115,9 +115,9 @@ def test_workspace_size_fused_bf16():
 
 
 def test_workspace_size_varlen():
-    """Packed-sequence calls: the staged layout (also for bf16 shapes the fused
-    path would take) plus [b, nc, Q] int32 sequence-start counts; nothing for
-    seqlen <= 16."""
+    """Packed-sequence calls: on the staged path the staged layout plus
+    [b, nc, Q] int32 sequence-start counts; on the fused bf16 path (headdim 64,
+    dstate 64/128) the fused layout; nothing for seqlen <= 16."""
     for (b, L, H, P, N, G, Q) in SIZES:
         nc = math.ceil(L / Q)
         staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
@@ -126,6 +126,13 @@ def test_workspace_size_varlen():
             if L <= DECODE_MAX_L:
                 assert got == 0
                 continue
+            if dt and N in (64, 128):
+                assert got == _ws(b, L, H, P, N, G, Q, 1)  # fused layout, as the plain call
+                prev = ssd.set_bf16_path("staged")
+                try:
+                    got = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, dt)
+                finally:
+                    ssd.set_bf16_path(prev)
             bt = _r(b * nc * G * N * Q * 2) if (dt and Q in (128, 256) and N in (64, 128)) else 0
             assert got == staged + bt + _r(b * nc * Q * 4)
     assert ssd.varlen_workspace_size(2, 100, 4, 64, 16, 3, 64, 0) == 0  # rejected shapes
@@ -239,9 +246,8 @@ VARLEN_CASES = [
     ("out overlaps seq_idx", dict(seq=0xA0000000 + 64), INVALID),
     ("shape checks as ssd_scan_fwd", dict(ngroups=3), INVALID),
     ("valid, stops at workspace", dict(), WORKSPACE),
-    ("bf16 fused shape still needs the staged workspace", dict(dtype=1, dstate=128,
-     chunk_size=128, ws=0xC0000000, ws_bytes=ssd.workspace_size(1, 100, 4, 64, 128, 1, 128, 1)),
-     WORKSPACE),
+    ("bf16 fused shape, workspace one byte short", dict(dtype=1, dstate=128, chunk_size=128,
+     ws=0xC0000000, ws_bytes=ssd.workspace_size(1, 100, 4, 64, 128, 1, 128, 1) - 1), WORKSPACE),
 ]
 
 

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, compare, log, np64, run_gpu, upload, ws_regions
+from parity import TOL, bf16_path, compare, log, np64, paths_for, run_gpu, upload, ws_regions
 from ssd_workloads import WORKLOADS, Workload, make_inputs, make_seq_idx
 
 pytestmark = pytest.mark.gpu
@@ -61,11 +61,14 @@ def test_varlen_parity(dtype, Q, N, H, G):
     for i, m in enumerate(MEANS):
         mean = {"Q/2": Q / 2, "3Q": 3 * Q}.get(m, m)
         seq = make_seq_idx(b, L, mean, 40 + i)
-        log(f"test_varlen_parity {dtype} Q={Q} N={N} H={H} G={G} L={L} mean length {m}")
-        out, fin = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
         ref, rfin = _oracle(inp, seq, inp["initial_states"])
-        compare(f"out mean {m}", np64(out), ref, TOL[dtype])
-        compare(f"final mean {m}", np64(fin), rfin, TOL[dtype])
+        for path in paths_for(dtype):
+            log(f"test_varlen_parity {dtype} Q={Q} N={N} H={H} G={G} L={L} mean length {m} "
+                f"path={path}")
+            with bf16_path(path):
+                out, fin = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
+            compare(f"out mean {m} {path}", np64(out), ref, TOL[dtype])
+            compare(f"final mean {m} {path}", np64(fin), rfin, TOL[dtype])
 
 
 EDGES = [
@@ -85,11 +88,13 @@ def test_varlen_edges(dtype, Q, desc, lengths):
     inp = make_inputs(w)
     t = upload(inp, dtype)
     seq = _from_lengths(b, L, lengths(Q))
-    log(f"test_varlen_edges {dtype} Q={Q}: {desc}")
-    out, fin = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
     ref, rfin = _oracle(inp, seq, inp["initial_states"])
-    compare("out", np64(out), ref, TOL[dtype])
-    compare("final", np64(fin), rfin, TOL[dtype])
+    for path in paths_for(dtype):
+        log(f"test_varlen_edges {dtype} Q={Q}: {desc} path={path}")
+        with bf16_path(path):
+            out, fin = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
+        compare(f"out {path}", np64(out), ref, TOL[dtype])
+        compare(f"final {path}", np64(fin), rfin, TOL[dtype])
 
 
 def test_varlen_one_label_is_the_plain_scan():
@@ -115,12 +120,14 @@ def test_varlen_labels_only_changes_matter(dtype):
     t = upload(inp, dtype)
     seq = make_seq_idx(b, L, 30, 9)
     log(f"test_varlen_labels_only_changes_matter {dtype}")
-    o1, f1 = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
-    o2, f2 = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq % 2))
-    assert torch.equal(o1, o2) and torch.equal(f1, f2)
     ref, rfin = _oracle(inp, seq % 2, inp["initial_states"])
-    compare("out", np64(o2), ref, TOL[dtype])
-    compare("final", np64(f2), rfin, TOL[dtype])
+    for path in paths_for(dtype):
+        with bf16_path(path):
+            o1, f1 = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
+            o2, f2 = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq % 2))
+        assert torch.equal(o1, o2) and torch.equal(f1, f2), path
+        compare(f"out {path}", np64(o2), ref, TOL[dtype])
+        compare(f"final {path}", np64(f2), rfin, TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype,Q,N", [("f32", 128, 128), ("bf16", 256, 128), ("f32", 64, 16)])
@@ -134,10 +141,11 @@ def test_varlen_intermediates(dtype, Q, N):
     t = upload(inp, dtype)
     seq = make_seq_idx(b, L, Q / 3, 11)
     code = 1 if dtype == "bf16" else 0
-    total = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, code)
-    ws = torch.zeros(total, dtype=torch.uint8, device=t["x"].device)
     log(f"test_varlen_intermediates {dtype} Q={Q} N={N}")
-    run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq), workspace=ws)
+    with bf16_path("staged"):  # the intermediates live in the staged path's workspace
+        total = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, code)
+        ws = torch.zeros(total, dtype=torch.uint8, device=t["x"].device)
+        run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq), workspace=ws)
     nc = -(-L // Q)
     seg_bytes = (b * nc * Q * 4 + 255) // 256 * 256
     seg = ws[total - seg_bytes:total - seg_bytes + b * nc * Q * 4].view(torch.int32)
@@ -205,19 +213,23 @@ def test_varlen_workload(name, mean):
     inp = make_inputs(w)
     t = upload(inp, w.dtype)
     seq = make_seq_idx(w.batch, w.seqlen, mean, 77)
-    out, fin = run_gpu(t, w.chunk_size, seq_idx=_seq(seq))
-    got, gfin = np64(out), np64(fin)
-    del out, fin
+    results = {}
+    for path in paths_for(w.dtype):
+        with bf16_path(path):
+            out, fin = run_gpu(t, w.chunk_size, seq_idx=_seq(seq))
+        results[path] = (np64(out), np64(fin))
+        del out, fin
     big = w.batch * w.seqlen * w.nheads > 2 * 2048 * 32
     mask = _sample_mask(w.batch, w.nheads, 8, w.seed) if big else None
     log(f"test_varlen_workload {name}: oracle")
     ref, rfin = _oracle(inp, seq, head_mask=mask)
     tol = TOL[w.dtype]
-    if mask is None:
-        compare("out", got, ref, tol)
-        compare("final", gfin, rfin, tol)
-    else:
-        compare("out (sampled heads)", got, ref, tol,
-                mask=np.broadcast_to(mask[:, None, :, None], ref.shape))
-        compare("final (sampled heads)", gfin, rfin, tol,
-                mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))
+    for path, (got, gfin) in results.items():
+        if mask is None:
+            compare(f"out {path}", got, ref, tol)
+            compare(f"final {path}", gfin, rfin, tol)
+        else:
+            compare(f"out (sampled heads) {path}", got, ref, tol,
+                    mask=np.broadcast_to(mask[:, None, :, None], ref.shape))
+            compare(f"final (sampled heads) {path}", gfin, rfin, tol,
+                    mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))

@@ -107,6 +107,14 @@ def cpu_baseline(workloads, min_seconds=10.0):
             "cpu": _cpu_model()}
 
 
+def bf16_kernel(ssd, workspace_bytes):
+    """The kernel a bf16 call takes: the chain kernel needs no workspace."""
+    opt = ssd.get_bf16_path()
+    if workspace_bytes == 0:
+        return "chain"
+    return opt if opt != "auto" else "fused"
+
+
 def bf16_workload(steps, warmup, name="bf16_b8_L4096_H64_P64_N128_G8_Q256"):
     """The bf16 workload (batch 8 x seqlen 4096, 64 heads, 8 groups, chunk 256,
     z and D on, final states returned) on the default bf16 path: calls per
@@ -117,19 +125,22 @@ def bf16_workload(steps, warmup, name="bf16_b8_L4096_H64_P64_N128_G8_Q256"):
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     inp = make_inputs(w)
-    t = {}
+    t = {"z": None, "D": None}
     for k in ("x", "z", "B", "C", "dt"):
-        t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
+        if k in inp["bits"]:
+            t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
     for k in ("A", "D", "dt_bias"):
-        t[k] = torch.from_numpy(inp[k]).to(dev)
+        if inp.get(k) is not None:
+            t[k] = torch.from_numpy(inp[k]).to(dev)
     del inp
     out = torch.empty_like(t["x"])
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
     wsz = ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
                              w.chunk_size, ssd.SSD_BF16)
     ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    ptr = lambda v: None if v is None else v.data_ptr()
     a = (t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(),
-         t["C"].data_ptr(), t["D"].data_ptr(), t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0,
+         t["C"].data_ptr(), ptr(t["D"]), ptr(t["z"]), t["dt_bias"].data_ptr(), 0.0,
          math.inf, w.chunk_size, w.ngroups, None, out.data_ptr(), fin.data_ptr(), w.batch,
          w.seqlen, w.nheads, w.headdim, w.dstate, ssd.SSD_BF16, ws.data_ptr(), wsz)
     s = torch.cuda.current_stream(dev).cuda_stream
@@ -151,7 +162,7 @@ def bf16_workload(steps, warmup, name="bf16_b8_L4096_H64_P64_N128_G8_Q256"):
     return {
         "workload": "ssd_scan_fwd bf16 batch 8 x seqlen 4096, 64 heads x headdim 64, dstate "
                     "128, ngroups 8, chunk 256, z gate and D on, final states returned",
-        "path": ssd.get_bf16_path(),
+        "path": bf16_kernel(ssd, wsz),
         "tokens_per_s": w.tokens / el,
         "ms_per_call": el * 1e3,
         "calls": steps,
@@ -274,7 +285,7 @@ def varlen_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mea
                     f"{nseq} packed sequences (mean length {mean_len}), {w.nheads} heads x "
                     f"headdim 64, dstate {w.dstate}, chunk {w.chunk_size}, ngroups {w.ngroups}, "
                     "z gate and D on",
-        "path": "staged" if w.dtype == "f32" else ssd.get_bf16_path(),
+        "path": "staged" if w.dtype == "f32" else bf16_kernel(ssd, ws_bytes),
         "tokens_per_s": w.tokens / el,
         "us_per_call": el * 1e6,
         "plain_us_per_call": res[False] * 1e6,

@@ -112,14 +112,19 @@ extern "C" {
  * be NULL) and ignores chunk_size beyond checking it.  final_states may be
  * initial_states.
  *
- * Longer sequences take one of two kernel paths.  bf16 inputs with headdim 64
- * and dstate 64 or 128 take the fused path by default (see ssd_set_option):
- * one set-up kernel and one scan kernel, in which each workgroup handles 128 timesteps of one (batch,
- * head) and hands the state to the workgroup of the next 128 timesteps
- * through the workspace (the chunked form gives the same result for any block
- * length, up to rounding; chunk_size is still checked).  Every other case
- * takes the staged path: dt/cumsum, chunk state, state passing and chunk
- * scan kernels with their intermediates in the workspace.
+ * Longer sequences take one of three kernel paths.  bf16 inputs with headdim
+ * 64 and dstate 64 or 128 take, by default (see ssd_set_option), the chain
+ * path when each group holds an even number of heads and the head pairs fill
+ * the machine: one kernel in which each workgroup carries a pair of heads of one
+ * group through the whole sequence in 128-step blocks with the state held on
+ * chip (no workspace: ssd_scan_fwd_workspace_size returns 0).  Otherwise they
+ * take the fused path: one set-up kernel and one scan kernel, in which each
+ * workgroup handles 128 timesteps of one (batch, head) and hands the state to
+ * the workgroup of the next 128 timesteps through the workspace.  (The
+ * chunked form gives the same result for any block length, up to rounding;
+ * chunk_size is still checked.)  Every other case takes the staged path:
+ * dt/cumsum, chunk state, state passing and chunk scan kernels with their
+ * intermediates in the workspace.
  *
  * Staged path: after the enqueued work completes, the workspace holds the
  * intermediates (float32, in this order, each region starting on a 256-byte
@@ -183,10 +188,11 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
  * final_states the state after the row's last step (its last sequence).
  * Every other argument, the checks and the execution rules are those of
  * ssd_scan_fwd; `out` must not overlap seq_idx either.  The call takes the
- * same path as ssd_scan_fwd (the fused bf16 kernel counts the sequence
- * starts itself; with SSD_BF16_PATH_FUSED_GROUP it runs the per-head form)
- * and needs ssd_scan_fwd_varlen_workspace_size(...) bytes of workspace: on
- * the fused path the fused layout, on the staged path the staged layout
+ * same path as ssd_scan_fwd (the chain and fused bf16 kernels count the
+ * sequence starts themselves; with SSD_BF16_PATH_FUSED_GROUP the fused path
+ * runs its per-head form) and needs ssd_scan_fwd_varlen_workspace_size(...)
+ * bytes of workspace: none on the chain path, on the fused path the fused
+ * layout, on the staged path the staged layout
  * followed, on a 256-byte boundary, by
  *   seg [batch, nchunks, chunk_size] int32: for step q of chunk c the number
  *       of sequence starts at steps c*chunk_size .. c*chunk_size + q (steps
@@ -311,11 +317,17 @@ int ssd_abi_version(void);
 
 /*
  * Process-wide options.  SSD_OPT_BF16_PATH selects the kernel path of bf16
- * problems that the fused path covers: SSD_BF16_PATH_AUTO (default, fused),
- * SSD_BF16_PATH_STAGED, SSD_BF16_PATH_FUSED (fused, kernel form chosen from
- * the shape), SSD_BF16_PATH_FUSED_HEAD (one workgroup per 128-step block and
- * head) or SSD_BF16_PATH_FUSED_GROUP (one workgroup per 128-step block, B/C
- * group and set of up to 8 of its heads).  The workspace size depends on
+ * problems that the fused path covers: SSD_BF16_PATH_AUTO (default: the
+ * chain kernel when the heads of a group pair up and the pairs, n = batch *
+ * nheads / 2 workgroups, fill the 256 compute units: 4 n >= 3 * 256 *
+ * ceil(n / 256); else fused), SSD_BF16_PATH_STAGED,
+ * SSD_BF16_PATH_FUSED (fused, kernel form chosen from the shape),
+ * SSD_BF16_PATH_FUSED_HEAD (one workgroup per 128-step block and head),
+ * SSD_BF16_PATH_FUSED_GROUP (one workgroup per 128-step block, B/C group
+ * and set of up to 8 of its heads) or SSD_BF16_PATH_CHAIN (one workgroup
+ * per pair of heads of a group for the whole sequence, the state held on
+ * chip, no workspace; shapes whose groups hold an odd number of heads take
+ * the fused path).  The workspace size depends on
  * the path, so set options before querying it; do not change them while
  * another thread is between the query and the call.  ssd_set_option returns
  * SSD_OK or SSD_ERR_INVALID_ARG; ssd_get_option the value or
@@ -327,6 +339,7 @@ int ssd_abi_version(void);
 #define SSD_BF16_PATH_FUSED 2
 #define SSD_BF16_PATH_FUSED_HEAD 3
 #define SSD_BF16_PATH_FUSED_GROUP 4
+#define SSD_BF16_PATH_CHAIN 5
 int ssd_set_option(int option, int value);
 int ssd_get_option(int option);
 
@@ -339,7 +352,8 @@ int ssd_get_option(int option);
  * transpose of the bf16 kernels, empty when dt/cumsum is fused into the chunk
  * state --, chunk state, state passing, chunk scan).  On the fused path prep
  * is the set-up kernel, the scan kernel is reported as chunk scan and the two
- * middle stages are empty.  Returns SSD_OK or SSD_ERR_HIP /
+ * middle stages are empty; on the chain path its one kernel is reported as
+ * chunk scan and the other stages are empty.  Returns SSD_OK or SSD_ERR_HIP /
  * SSD_ERR_INVALID_ARG.
  */
 #define SSD_NUM_STAGES 4

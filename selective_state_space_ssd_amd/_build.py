@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libssd.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["ssd_api.hip", "ssd_dt_cumsum.hip", "ssd_chunk_state.hip", "ssd_state_passing.hip",
            "ssd_chunk_scan.hip", "ssd_bf16.hip", "ssd_fused_bf16.hip",
-           "ssd_fused_group_bf16.hip", "ssd_decode.hip", "ssd_block.hip",
+           "ssd_fused_group_bf16.hip", "ssd_chain_bf16.hip", "ssd_decode.hip", "ssd_block.hip",
            "ssd_backward.hip"]
 ARCH = "gfx950"
 CFLAGS = [

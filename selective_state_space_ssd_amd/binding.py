@@ -21,7 +21,8 @@ SSD_BF16 = 1
 SSD_NUM_STAGES = 4
 STAGES = ("prep", "chunk_state", "state_passing", "chunk_scan")
 SSD_OPT_BF16_PATH = 1
-BF16_PATHS = {"auto": 0, "staged": 1, "fused": 2, "fused_head": 3, "fused_group": 4}
+BF16_PATHS = {"auto": 0, "staged": 1, "fused": 2, "fused_head": 3, "fused_group": 4,
+              "chain": 5}
 
 _lib = None
 
@@ -100,7 +101,8 @@ def abi_version() -> int:
 
 def set_bf16_path(name: str) -> str:
     """Select the kernel path of bf16 problems ("auto", "staged", "fused",
-    "fused_head" or "fused_group", process-wide); returns the previous setting."""
+    "fused_head", "fused_group" or "chain", process-wide); returns the
+    previous setting."""
     lib = load_library()
     prev = {v: k for k, v in BF16_PATHS.items()}[lib.ssd_get_option(SSD_OPT_BF16_PATH)]
     _check(lib.ssd_set_option(SSD_OPT_BF16_PATH, BF16_PATHS[name]))

@@ -38,6 +38,7 @@ struct Layout {
   int64_t nc = 0;
   bool decode = false;  // seqlen <= kDecodeMaxL: step-by-step kernel, no workspace
   bool fused = false;
+  bool chain = false;  // chain bf16 kernel: no workspace
   // staged path (off_seg: packed-sequence counts, varlen calls only)
   size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0, off_seg = 0;
   // fused bf16 path
@@ -58,6 +59,17 @@ bool bf16_path(int dtype, int64_t dstate, int chunk_size) {
 bool fused_path(int dtype, int64_t headdim, int64_t dstate) {
   return dtype == SSD_BF16 && headdim == 64 && (dstate == 64 || dstate == 128) &&
          g_bf16_path != SSD_BF16_PATH_STAGED;
+}
+
+// The chain bf16 kernel: asked for, or chosen by default when the head pairs
+// fill the machine (same shape rule as ssd::use_chain_bf16, plus the option).
+bool chain_path(int dtype, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                int ngroups) {
+  const bool shape = dtype == SSD_BF16 && headdim == 64 && (dstate == 64 || dstate == 128) &&
+                     (nheads / ngroups) % 2 == 0;
+  if (!shape) return false;
+  if (g_bf16_path == SSD_BF16_PATH_CHAIN) return true;
+  return g_bf16_path == SSD_BF16_PATH_AUTO && ssd::chain_fills_machine(batch, nheads);
 }
 
 // Shape checks shared by the workspace query and the entry point.
@@ -89,6 +101,11 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
   lay->nc = nc;
   if (ssd::use_decode(seqlen)) {
     lay->decode = true;
+    lay->total = 0;
+    return SSD_OK;
+  }
+  if (chain_path(dtype, batch, nheads, headdim, dstate, ngroups) && seqlen > 0 && batch > 0) {
+    lay->chain = true;
     lay->total = 0;
     return SSD_OK;
   }
@@ -300,6 +317,12 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     if ((seqlen > 0 || final_states) && ssd::launch_decode(p, stream) != hipSuccess)
       return SSD_ERR_HIP;
     if (!mark(4)) return SSD_ERR_HIP;
+    if (timing) timing->recorded = true;
+    return SSD_OK;
+  }
+  if (lay.chain) {
+    if (!mark(1) || !mark(2) || !mark(3)) return SSD_ERR_HIP;
+    if (ssd::launch_chain_bf16(p, stream) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
     if (timing) timing->recorded = true;
     return SSD_OK;
   }
@@ -593,7 +616,7 @@ int ssd_abi_version(void) { return SSD_ABI_VERSION; }
 
 int ssd_set_option(int option, int value) {
   if (option != SSD_OPT_BF16_PATH) return SSD_ERR_INVALID_ARG;
-  if (value < SSD_BF16_PATH_AUTO || value > SSD_BF16_PATH_FUSED_GROUP) return SSD_ERR_INVALID_ARG;
+  if (value < SSD_BF16_PATH_AUTO || value > SSD_BF16_PATH_CHAIN) return SSD_ERR_INVALID_ARG;
   g_bf16_path = value;
   return SSD_OK;
 }

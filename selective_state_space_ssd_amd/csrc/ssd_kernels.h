@@ -65,6 +65,19 @@ bool use_fused_bf16(const Problem& p);
 int64_t fused_blocks(int64_t L);
 hipError_t launch_fused_bf16(const Problem& p, hipStream_t stream, int stage);
 
+// Chain bf16 kernel (bf16 inputs, P 64, N 64/128, an even number of heads
+// per group): one workgroup per pair of heads of one group for the whole
+// sequence, the state in registers; no workspace.  One workgroup fills one
+// of the 256 compute units for the whole call, so it is the default only
+// when the pairs fill the machine: each round of 256 workgroups at least 3/4
+// full (below that the fused kernel, which spreads the blocks of a chain
+// over workgroups, is faster).
+constexpr int64_t kChainCUs = 256;
+bool use_chain_bf16(const Problem& p);
+int64_t chain_workgroups(int64_t b, int64_t H);
+bool chain_fills_machine(int64_t b, int64_t H);
+hipError_t launch_chain_bf16(const Problem& p, hipStream_t stream);
+
 // Group form of the fused kernel: one workgroup per (block, group, head set).
 int64_t fused_group_units(const Problem& p);
 hipError_t launch_fused_group_bf16(const Problem& p, hipStream_t stream);

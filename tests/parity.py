@@ -15,8 +15,8 @@ TOL = {"f32": 1e-3, "bf16": 2e-2}
 
 @contextmanager
 def bf16_path(name):
-    """Run the enclosed calls with the bf16 kernel path `name` ("fused",
-    "staged" or "auto")."""
+    """Run the enclosed calls with the bf16 kernel path `name` ("chain",
+    "fused", "fused_head", "fused_group", "staged" or "auto")."""
     prev = ssd.set_bf16_path(name)
     try:
         yield
@@ -26,7 +26,7 @@ def bf16_path(name):
 
 def paths_for(dtype):
     """The kernel paths a problem of this dtype can take."""
-    return ("fused_head", "fused_group", "staged") if dtype == "bf16" else ("auto",)
+    return ("chain", "fused_head", "fused_group", "staged") if dtype == "bf16" else ("auto",)
 
 
 def log(msg):

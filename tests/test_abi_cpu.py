@@ -96,28 +96,69 @@ def test_workspace_size_formula():
         ssd.set_bf16_path(prev)
 
 
+def _fused_ws(b, L, H, P, N):
+    """Fused bf16 layout: ring of two states per (batch, head), one flag per
+    128-step block, one 256-byte control region."""
+    return _r(b * H * 2 * P * N * 4) + _r(b * H * math.ceil(L / 128) * 4) + 256
+
+
+def _chain_fills(b, H):
+    """The chain kernel is the default when its workgroups (head pairs) fill
+    each round of 256 compute units at least 3/4."""
+    n = b * H // 2
+    rounds = -(-n // 256)
+    return n > 0 and 4 * n >= 3 * 256 * rounds
+
+
 def test_workspace_size_fused_bf16():
-    """Fused bf16 path (dstate 64/128): ring of two states per (batch, head),
-    one flag per 128-step block, one 256-byte control region."""
+    """Fused bf16 path (dstate 64/128), asked for explicitly."""
+    prev = ssd.set_bf16_path("fused")
+    try:
+        for (b, L, H, P, N, G, Q) in SIZES:
+            nc = math.ceil(L / Q)
+            staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+            if L <= DECODE_MAX_L:  # short sequences: the step-by-step kernel, no workspace
+                assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
+                continue
+            assert _ws(b, L, H, P, N, G, Q) == staged  # fp32 is always staged
+            want = _fused_ws(b, L, H, P, N) if N in (64, 128) else staged  # dstate 16/32: staged
+            assert _ws(b, L, H, P, N, G, Q, 1) == want
+    finally:
+        ssd.set_bf16_path(prev)
+
+
+def test_workspace_size_default_bf16():
+    """Default bf16 path: the chain kernel (no workspace) when the heads of a
+    group pair up and the pairs fill the machine, else the fused layout; the
+    chain option takes the chain kernel whenever the heads pair up."""
     assert ssd.get_bf16_path() == "auto"
-    for (b, L, H, P, N, G, Q) in SIZES:
-        nc = math.ceil(L / Q)
-        staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
-        if L <= DECODE_MAX_L:  # short sequences: the step-by-step kernel, no workspace
-            assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
+    cases = SIZES + [(8, 4096, 64, 64, 128, 64, 256), (4, 1000, 64, 64, 64, 2, 128),
+                     (2, 1000, 6, 64, 128, 2, 128), (6, 1000, 64, 64, 128, 8, 128),
+                     (5, 1000, 64, 64, 128, 8, 128), (1, 65536, 128, 64, 128, 8, 256),
+                     (12, 500, 64, 64, 128, 8, 128), (13, 500, 64, 64, 128, 8, 128)]
+    for (b, L, H, P, N, G, Q) in cases:
+        if L <= DECODE_MAX_L or N not in (64, 128):
             continue
-        assert _ws(b, L, H, P, N, G, Q) == staged  # fp32 is always staged
-        if N in (64, 128):
-            want = _r(b * H * 2 * P * N * 4) + _r(b * H * math.ceil(L / 128) * 4) + 256
-        else:
-            want = staged  # dstate 16/32: staged
-        assert _ws(b, L, H, P, N, G, Q, 1) == want
+        pairs_up = (H // G) % 2 == 0
+        chain = pairs_up and _chain_fills(b, H)
+        assert _ws(b, L, H, P, N, G, Q, 1) == (0 if chain else _fused_ws(b, L, H, P, N))
+        prev = ssd.set_bf16_path("chain")
+        try:
+            assert _ws(b, L, H, P, N, G, Q, 1) == (0 if pairs_up else _fused_ws(b, L, H, P, N))
+            assert _ws(b, L, H, P, N, G, Q, 0) > 0  # fp32 stays staged
+        finally:
+            ssd.set_bf16_path(prev)
+    assert _ws(8, 4096, 64, 64, 128, 8, 256, 1) == 0  # the bf16 8 x 4096 workload: chain
+    assert _ws(1, 65536, 128, 64, 128, 8, 256, 1) > 0  # the 1 x 65536 one: 64 pairs, fused
+    assert _chain_fills(6, 64) and not _chain_fills(5, 64)  # 192 of 256 / 160 of 256
+    assert _chain_fills(12, 64) and not _chain_fills(11, 64)  # 384 of 512 (3/4) / 352
 
 
 def test_workspace_size_varlen():
     """Packed-sequence calls: on the staged path the staged layout plus
-    [b, nc, Q] int32 sequence-start counts; on the fused bf16 path (headdim 64,
-    dstate 64/128) the fused layout; nothing for seqlen <= 16."""
+    [b, nc, Q] int32 sequence-start counts; on the chain and fused bf16 paths
+    (headdim 64, dstate 64/128) the plain call's layout; nothing for seqlen
+    <= 16."""
     for (b, L, H, P, N, G, Q) in SIZES:
         nc = math.ceil(L / Q)
         staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
@@ -127,7 +168,7 @@ def test_workspace_size_varlen():
                 assert got == 0
                 continue
             if dt and N in (64, 128):
-                assert got == _ws(b, L, H, P, N, G, Q, 1)  # fused layout, as the plain call
+                assert got == _ws(b, L, H, P, N, G, Q, 1)  # as the plain call
                 prev = ssd.set_bf16_path("staged")
                 try:
                     got = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, dt)
@@ -141,7 +182,7 @@ def test_workspace_size_varlen():
 def test_options():
     lib = ssd.load_library()
     assert lib.ssd_get_option(1) == 0
-    assert lib.ssd_set_option(1, 7) == INVALID
+    assert lib.ssd_set_option(1, 6) == INVALID
     assert lib.ssd_set_option(1, -1) == INVALID
     assert lib.ssd_set_option(2, 0) == INVALID
     assert lib.ssd_get_option(2) == INVALID

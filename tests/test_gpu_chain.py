@@ -1,0 +1,121 @@
+"""GPU checks specific to the chain bf16 kernel (one workgroup carries a pair
+of heads of one group through the whole sequence, the state in registers):
+block edges, agreement with the staged bf16 kernels, in-place continuation,
+run-to-run determinism, and the fallback for groups with an odd number of
+heads.  Every bf16 parity test elsewhere also runs on this path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_ssd_amd as ssd
+from parity import TOL, bf16_path, compare, log, np64, run_gpu, upload
+from ssd_workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, b, L, H, N, G, init=True, gate=True, skip=True):
+    w = Workload(f"chain{seed}", b, L, H, 64, N, G, 256, "bf16", seed, init=init, gate=gate,
+                 skip=skip)
+    inp = make_inputs(w)
+    return w, inp, upload(inp, "bf16")
+
+
+def _oracle(inp, init=True):
+    return oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                          z=inp["z"], dt_bias=inp["dt_bias"],
+                          initial_states=inp["initial_states"] if init else None,
+                          return_final_states=True)
+
+
+# sequence lengths around the 128-step block of the kernel (L <= 16 takes the
+# step kernel), both state sizes, one to four head pairs per group
+EDGES = [(L, N, H, G) for L in (17, 127, 128, 129, 255, 257) for (N, H, G) in
+         ((128, 4, 2), (64, 8, 1))]
+
+
+@pytest.mark.parametrize("L,N,H,G", EDGES, ids=[f"L{e[0]}-N{e[1]}-H{e[2]}-G{e[3]}" for e in EDGES])
+def test_chain_block_edges(L, N, H, G):
+    w, inp, t = _inputs(700 + L + N, 2, L, H, N, G)
+    log(f"test_chain_block_edges L={L} N={N} H={H} G={G}")
+    with bf16_path("chain"):
+        assert ssd.workspace_size(2, L, H, 64, N, G, 256, ssd.SSD_BF16) == 0
+        out, fin = run_gpu(t, 256, init=t["initial_states"])
+    ref, rfin = _oracle(inp)
+    compare("out", np64(out), ref, TOL["bf16"])
+    compare("final", np64(fin), rfin, TOL["bf16"])
+
+
+@pytest.mark.parametrize("gate,skip,init", [(False, False, False), (True, False, True),
+                                            (False, True, False)])
+def test_chain_options(gate, skip, init):
+    """Without the z gate, the D skip or an initial state."""
+    w, inp, t = _inputs(710, 2, 600, 8, 128, 4, init=init, gate=gate, skip=skip)
+    log(f"test_chain_options gate={gate} skip={skip} init={init}")
+    with bf16_path("chain"):
+        out, fin = run_gpu(t, 256, init=t["initial_states"] if init else None)
+    ref, rfin = _oracle(inp, init=init)
+    compare("out", np64(out), ref, TOL["bf16"])
+    compare("final", np64(fin), rfin, TOL["bf16"])
+
+
+def test_chain_matches_staged():
+    """The two bf16 paths differ only in rounding order: outputs within two
+    bf16 ulps of each other, final states within 1e-4 (1 + |ref|)."""
+    w, inp, t = _inputs(720, 2, 1500, 16, 128, 2)
+    res = {}
+    for path in ("chain", "staged"):
+        with bf16_path(path):
+            res[path] = [np64(v) for v in run_gpu(t, 256, init=t["initial_states"])]
+    compare("chain vs staged out", res["chain"][0], res["staged"][0], 2 * 2.0 ** -8)
+    compare("chain vs staged final", res["chain"][1], res["staged"][1], 1e-4)
+
+
+def test_chain_inplace_continuation():
+    """final_states may be the initial_states buffer: the state is read at the
+    start and written at the end of each workgroup's own heads."""
+    w, inp, t = _inputs(730, 2, 2 * 300, 8, 128, 2)
+    with bf16_path("chain"):
+        full, ffin = run_gpu(t, 256, init=t["initial_states"])
+        state = t["initial_states"].clone()
+        outs = []
+        for lo, hi in ((0, 300), (300, 600)):
+            seg = {k: (v[:, lo:hi].contiguous() if k in ("x", "z", "B", "C", "dt") else v)
+                   for k, v in t.items()}
+            out, fin = run_gpu(seg, 256, init=state, final_states=state)
+            assert fin.data_ptr() == state.data_ptr()
+            outs.append(out)
+    compare("segments vs full", np64(torch.cat(outs, dim=1)), np64(full), TOL["bf16"])
+    compare("final in place", np64(state), np64(ffin), 1e-4)
+
+
+def test_chain_repeat_bitwise():
+    """Back-to-back calls of a problem with 256 workgroups give bitwise equal
+    outputs and final states (no atomics, fixed reduction orders)."""
+    w, inp, t = _inputs(740, 4, 1024, 64, 128, 8)
+    with bf16_path("chain"):
+        o0, f0 = run_gpu(t, 256, init=t["initial_states"])
+        for k in range(6):
+            o, f = run_gpu(t, 256, init=t["initial_states"])
+            assert torch.equal(o, o0) and torch.equal(f, f0), k
+    mask = np.zeros((4, 64), bool)
+    mask[[0, 1, 3], [0, 33, 63]] = True
+    ref, rfin = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                               z=inp["z"], dt_bias=inp["dt_bias"],
+                               initial_states=inp["initial_states"], return_final_states=True,
+                               head_mask=mask)
+    compare("out (sampled heads)", np64(o0), ref, TOL["bf16"],
+            mask=np.broadcast_to(mask[:, None, :, None], ref.shape))
+
+
+def test_chain_odd_heads_per_group_falls_back():
+    """Groups of 3 heads do not pair up: asking for the chain kernel takes the
+    fused path (with its workspace) and still matches the oracle."""
+    w, inp, t = _inputs(750, 2, 400, 6, 128, 2)
+    with bf16_path("chain"):
+        assert ssd.workspace_size(2, 400, 6, 64, 128, 2, 256, ssd.SSD_BF16) > 0
+        out, fin = run_gpu(t, 256, init=t["initial_states"])
+    ref, rfin = _oracle(inp)
+    compare("out", np64(out), ref, TOL["bf16"])
+    compare("final", np64(fin), rfin, TOL["bf16"])

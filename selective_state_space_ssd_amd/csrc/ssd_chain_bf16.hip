@@ -422,12 +422,14 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         }
         s16x8 mhi, mlo;
         split_bf16x8(mv, mhi, mlo);
+        s16x8 xo[4];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const s16x8 xo = cat8(tr_rows(Xl, kXP, sa, 16 * pt, m), tr_rows(Xl, kXP, sb, 16 * pt, m));
-          acc[pt] = mfma16(xo, mhi, acc[pt]);
-          acc[pt] = mfma16(xo, mlo, acc[pt]);
-        }
+        for (int pt = 0; pt < 4; ++pt)
+          xo[pt] = cat8(tr_rows(Xl, kXP, sa, 16 * pt, m), tr_rows(Xl, kXP, sb, 16 * pt, m));
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(xo[pt], mhi, acc[pt]);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(xo[pt], mlo, acc[pt]);
         g0 = n0;
         g1 = n1;
       }
@@ -448,14 +450,22 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
                            Hs[2 * kn + 1][3]};
       s16x8 hhi, hlo;
       split_bf16x8(hv, hhi, hlo);
+      // four tiles at a time: their operands first, then four independent
+      // products per half (reading, hi and lo tile by tile makes one long
+      // latency chain)
 #pragma unroll
-      for (int i = 0; i < CT; ++i) {
-        const int t = 16 * i + m;
-        const s16x4 c0 = *reinterpret_cast<const s16x4*>(Cl + t * CP + 32 * kn + 4 * g);
-        const s16x4 c1 = *reinterpret_cast<const s16x4*>(Cl + t * CP + 32 * kn + 16 + 4 * g);
-        const s16x8 cop = cat8(c0, c1);
-        ch[i] = mfma16(hhi, cop, ch[i]);
-        ch[i] = mfma16(hlo, cop, ch[i]);
+      for (int i0 = 0; i0 < CT; i0 += 4) {
+        s16x8 cops[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = 16 * (i0 + q) + m;
+          cops[q] = cat8(*reinterpret_cast<const s16x4*>(Cl + t * CP + 32 * kn + 4 * g),
+                         *reinterpret_cast<const s16x4*>(Cl + t * CP + 32 * kn + 16 + 4 * g));
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ch[i0 + q] = mfma16(hhi, cops[q], ch[i0 + q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ch[i0 + q] = mfma16(hlo, cops[q], ch[i0 + q]);
       }
     }
 
@@ -480,14 +490,36 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         s16x8 whi, wlo;
         split_bf16x8(xw, whi, wlo);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const s16x8 bop = cat8(tr_rows(Bl, BP, r0, 16 * j, m), tr_rows(Bl, BP, r1, 16 * j, m));
-          Hs[j] = mfma16(bop, whi, Hs[j]);
-          Hs[j] = mfma16(bop, wlo, Hs[j]);
+        for (int j0 = 0; j0 < NT; j0 += 4) {  // four n-tiles at a time, as in C.H
+          s16x8 bops[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            bops[q] = cat8(tr_rows(Bl, BP, r0, 16 * (j0 + q), m),
+                           tr_rows(Bl, BP, r1, 16 * (j0 + q), m));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Hs[j0 + q] = mfma16(bops[q], whi, Hs[j0 + q]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Hs[j0 + q] = mfma16(bops[q], wlo, Hs[j0 + q]);
         }
       }
     }
     __syncthreads();  // staging tiles dead: the output tiles take their space
+
+    // The next block's dt, then this block's z, are loaded here, once the
+    // output registers are free (held from earlier, they would be spilled, and
+    // the wait for a spilled value waits for every load issued before it); the
+    // barrier and the table work cover their latency.
+    if (c + 1 < nblk) load_dt(c + 1);
+    uint4 zr[PX];
+    if constexpr (GATE) {
+      const bf16_t* zsrc = z + ((b * L + t0) * H + h) * kP;
+#pragma unroll
+      for (int k = 0; k < PX; ++k) {
+        const int e = k * 256 + th;
+        const int row = e / 8, col = (e % 8) * 8;
+        zr[k] = ldg16(zsrc, (uint32_t)(row < last ? row : last) * xrow + (uint32_t)col * 2);
+      }
+    }
 
     // ---- both output parts into LDS ----
 #pragma unroll
@@ -502,22 +534,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     }
     __syncthreads();
 
-    // The tables are free until the next staging: fill them for block c + 1.
-    // The next block's dt, then this block's z, are loaded here (held from
-    // earlier, their registers would stall the vector loads issued after them
-    // or be spilled); the table work covers their latency.
-    if (c + 1 < nblk) load_dt(c + 1);
-    uint4 zr[PX];
-    if constexpr (GATE) {
-      const bf16_t* zsrc = z + ((b * L + t0) * H + h) * kP;
-#pragma unroll
-      for (int k = 0; k < PX; ++k) {
-        const int e = k * 256 + th;
-        const int row = e / 8, col = (e % 8) * 8;
-        zr[k] = ldg16(zsrc, (uint32_t)(row < last ? row : last) * xrow + (uint32_t)col * 2);
-      }
-    }
-
+    // the tables are free until the next staging: fill them for block c + 1
     if (c + 1 < nblk) tables(c + 1);
 
     // ---- epilogue: 8 consecutive p of one step per thread piece ----

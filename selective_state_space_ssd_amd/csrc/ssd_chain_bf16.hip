@@ -472,11 +472,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     // ---- state: H = exp(cum_last) H + B^T (w o x); slots t = 32 kt + 4 g + j
     // (j < 4) and 32 kt + 16 + 4 g + j - 4 ----
     {
-      const float dl = dl_l[hd];
+      const float dlv = dl_l[hd];
+      const float dl = dlv < 0.0f ? 0.0f : dlv;
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Hs[j][r] = dl < 0.0f ? 0.0f : dl * Hs[j][r];
+      for (int j = 0; j < NT; ++j) Hs[j] *= dl;
 #pragma unroll
       for (int kt = 0; kt < CQ / 32; ++kt) {
         const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;

@@ -399,30 +399,36 @@ def bwd_alg_flops(w, T=64):
     return fwd + b * nb * (H * per + G * 2.0 * pairs * N)
 
 
-def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128"):
+def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", dtype="f32"):
     """The backward (every gradient, dfinal zero, z, D and dt_bias on) of the
-    fp32 batch 2 x seqlen 2048 workload at ngroups 1, alternating two input
-    copies; the forward on the same inputs is timed alongside."""
+    batch 2 x seqlen 2048 workload at ngroups 1, alternating two input copies;
+    the forward on the same inputs is timed alongside.  dtype "bf16": x, dt,
+    B, C, z, dout and their gradients in bf16 (the inputs rounded)."""
     import torch
     import selective_state_space_ssd_amd as ssd
     w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    io = torch.bfloat16 if dtype == "bf16" else torch.float32
+    code = ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32
     rng = np.random.default_rng(31)
     copies = []
     for _ in range(2):
         t = {k: torch.from_numpy(v).to(dev) for k, v in make_inputs(w).items()
              if isinstance(v, np.ndarray)}
         t["dout"] = torch.from_numpy(rng.standard_normal((b, L, H, P)).astype(np.float32)).to(dev)
+        for k in ("x", "dt", "B", "C", "z", "dout"):
+            t[k] = t[k].to(io)
         copies.append(t)
     e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
-    gr = dict(dx=e(b, L, H, P), ddt=e(b, L, H), dA=e(H), dB=e(b, L, G, N), dC=e(b, L, G, N),
-              dD=e(H), dz=e(b, L, H, P), ddt_bias=e(H))
-    wsz = ssd.bwd_workspace_size(b, L, H, P, N, G, w.chunk_size)
+    eio = lambda *shape: torch.empty(shape, dtype=io, device=dev)
+    gr = dict(dx=eio(b, L, H, P), ddt=eio(b, L, H), dA=e(H), dB=eio(b, L, G, N),
+              dC=eio(b, L, G, N), dD=e(H), dz=eio(b, L, H, P), ddt_bias=e(H))
+    wsz = ssd.bwd_workspace_size(b, L, H, P, N, G, w.chunk_size, code)
     ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
-    fsz = ssd.workspace_size(b, L, H, P, N, G, w.chunk_size, ssd.SSD_F32)
-    fws = torch.empty(fsz, dtype=torch.uint8, device=dev)
-    out = torch.empty((b, L, H, P), device=dev)
+    fsz = ssd.workspace_size(b, L, H, P, N, G, w.chunk_size, code)
+    fws = torch.empty(max(fsz, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((b, L, H, P), dtype=io, device=dev)
     s = torch.cuda.current_stream(dev).cuda_stream
 
     def bwd_call(k):
@@ -433,7 +439,7 @@ def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128"):
             0.0, math.inf, w.chunk_size, G, None, t["dout"].data_ptr(), None,
             gr["dx"].data_ptr(), gr["ddt"].data_ptr(), gr["dA"].data_ptr(), gr["dB"].data_ptr(),
             gr["dC"].data_ptr(), gr["dD"].data_ptr(), gr["dz"].data_ptr(),
-            gr["ddt_bias"].data_ptr(), None, b, L, H, P, N, ssd.SSD_F32, ws.data_ptr(), wsz, s)
+            gr["ddt_bias"].data_ptr(), None, b, L, H, P, N, code, ws.data_ptr(), wsz, s)
         if st != 0:
             raise ssd.SsdError(st, ssd.status_string(st))
 
@@ -443,7 +449,7 @@ def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128"):
                               t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(),
                               t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0, math.inf,
                               w.chunk_size, G, None, out.data_ptr(), None, b, L, H, P, N,
-                              ssd.SSD_F32, fws.data_ptr(), fsz, s)
+                              code, fws.data_ptr(), fsz, s)
         if st != 0:
             raise ssd.SsdError(st, ssd.status_string(st))
 
@@ -460,8 +466,10 @@ def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128"):
     fl = bwd_alg_flops(w)
     el = res["bwd"]
     return {
-        "workload": "ssd_scan_bwd f32 batch 2 x seqlen 2048, 32 heads x headdim 64, dstate 128, "
-                    "ngroups 1, z gate, D and dt_bias on: every gradient (forward re-run inside)",
+        "workload": f"ssd_scan_bwd {dtype} batch 2 x seqlen 2048, 32 heads x headdim 64, "
+                    "dstate 128, ngroups 1, z gate, D and dt_bias on: every gradient (forward "
+                    "re-run inside" + (", inputs widened to fp32 and bf16 gradients rounded)"
+                                       if dtype == "bf16" else ")"),
         "tokens_per_s": w.tokens / el,
         "us_per_call": el * 1e6,
         "forward_us_per_call": res["fwd"] * 1e6,
@@ -658,7 +666,8 @@ def main():
                                    varlen_workload(max(5, args.steps // 5), 3,
                                                    "bf16_b8_L4096_H64_P64_N128_G8_Q256", 512),
                                    block_workload(max(20, args.steps), 5),
-                                   bwd_workload(max(10, args.steps // 2), 3)]
+                                   bwd_workload(max(10, args.steps // 2), 3),
+                                   bwd_workload(max(10, args.steps // 2), 3, dtype="bf16")]
     print(json.dumps(line), flush=True)
 
 

@@ -266,12 +266,18 @@ size_t ssd_split_conv1d_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, i
                                                 int norm_groups);
 
 /*
- * Backward of ssd_scan_fwd (float32 inputs, dtype SSD_F32): the gradients of
+ * Backward of ssd_scan_fwd: the gradients of
  *     l = sum(dout * out) + sum(dfinal_states * final_states)
  * with respect to every input, for training (the pages note the backward as
  * missing or separate).  Arguments x .. initial_states, the sizes and dtype are
  * those of the forward call; chunk_size is checked as there (the gradients do
  * not depend on it: the backward works in 64-step blocks).
+ *
+ * dtype SSD_F32: every tensor below is float32.  dtype SSD_BF16: x, dt, B, C,
+ * z and dout are bfloat16, and so are their gradients dx, ddt, dB, dC and dz
+ * (rounded to nearest even from fp32); A, D, dt_bias, the states and dA, dD,
+ * ddt_bias, dinitial_states stay float32.  bf16 inputs are widened to fp32
+ * (exactly) in the workspace and every step runs in fp32, as for SSD_F32.
  *
  *   dout            [batch, seqlen, nheads, headdim]  required
  *   dfinal_states   [batch, nheads, headdim, dstate]  NULL: zero
@@ -285,23 +291,25 @@ size_t ssd_split_conv1d_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, i
  *   dz              like x      exactly when z is given
  *   ddt_bias        [nheads]    exactly when dt_bias is given
  *   dinitial_states [batch, nheads, headdim, dstate]  NULL: not returned
- * All float32, contiguous; x, B, C, z, dout, dx, dz, dB, dC and the state
- * tensors 16-byte aligned, the others 4-byte aligned.  No output may overlap
- * an input, another output or the workspace.
+ * All contiguous; x, B, C, z, dout, dx, dz, dB, dC and the state tensors
+ * 16-byte aligned, dt and ddt aligned to their element, the float32 vectors
+ * 4-byte aligned.  No output may overlap an input, another output or the
+ * workspace.
  *
  * The forward is re-run inside (dt, running sums, the states entering each
  * block and the ungated output go to the workspace), then the reverse pass.
- * Workspace: ssd_scan_bwd_workspace_size(...) bytes, 256-byte aligned.  Like
- * the forward the call is asynchronous and deterministic.  Status codes as
- * for ssd_scan_fwd; SSD_ERR_UNSUPPORTED for bf16.
+ * Workspace: ssd_scan_bwd_workspace_size(...) bytes, 256-byte aligned (for
+ * bf16 it adds fp32 copies of x, dt, B, C, z, dout and fp32 buffers for their
+ * gradients).  Like the forward the call is asynchronous and deterministic.
+ * Status codes as for ssd_scan_fwd.
  */
-int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
-                 const float* D, const float* z, const float* dt_bias, float dt_min, float dt_max,
-                 int chunk_size, int ngroups, const float* initial_states, const float* dout,
-                 const float* dfinal_states, float* dx, float* ddt, float* dA, float* dB,
-                 float* dC, float* dD, float* dz, float* ddt_bias, float* dinitial_states,
-                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
+                 int chunk_size, int ngroups, const float* initial_states, const void* dout,
+                 const float* dfinal_states, void* dx, void* ddt, float* dA, void* dB, void* dC,
+                 float* dD, void* dz, float* ddt_bias, float* dinitial_states, int64_t batch,
+                 int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace ssd_scan_bwd needs (0 for an empty problem and for
  * rejected arguments); pure host computation. */

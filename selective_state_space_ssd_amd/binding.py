@@ -213,34 +213,41 @@ def scan_bwd(x, dt, A, B, C, dout, D=None, z=None, dt_bias=None, dt_limit=(0.0, 
              chunk_size: int = 128, initial_states=None, dfinal_states=None,
              return_dinitial_states: bool = True, workspace=None):
     """Gradients of sum(dout * out) + sum(dfinal_states * final_states) of
-    ``scan_fwd`` (float32 inputs) with respect to x, dt (raw), A, B, C, D, z,
-    dt_bias and the initial state.  Returns a dict of float32 tensors: dx, ddt,
+    ``scan_fwd`` with respect to x, dt (raw), A, B, C, D, z, dt_bias and the
+    initial state.  x, dt, B, C, z and dout are all float32 or all bfloat16;
+    their gradients dx, ddt, dB, dC, dz come back in that dtype, the others
+    (dA, dD, ddt_bias, dinitial_states) in float32.  Returns a dict: dx, ddt,
     dA, dB, dC, and dD / dz / ddt_bias when D / z / dt_bias are given,
     dinitial_states when asked for."""
     import torch
 
     load_library()
-    if x.dtype != torch.float32:
-        raise TypeError("the backward takes float32 inputs")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("the backward takes float32 or bfloat16 inputs")
+    io = x.dtype
+    code = SSD_BF16 if io == torch.bfloat16 else SSD_F32
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     dev = x.device
-    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("dout", dout),
-                    ("D", D), ("z", z), ("dt_bias", dt_bias), ("initial_states", initial_states),
-                    ("dfinal_states", dfinal_states)):
+    for name, t, want in (("x", x, io), ("dt", dt, io), ("A", A, torch.float32), ("B", B, io),
+                          ("C", C, io), ("dout", dout, io), ("D", D, torch.float32), ("z", z, io),
+                          ("dt_bias", dt_bias, torch.float32),
+                          ("initial_states", initial_states, torch.float32),
+                          ("dfinal_states", dfinal_states, torch.float32)):
         if t is None:
             continue
-        if t.device != dev or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 tensor on x's device")
+        if t.device != dev or t.dtype != want or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {want} tensor on x's device")
     if tuple(dout.shape) != (b, L, H, P):
         raise ValueError("dout must have x's shape")
     e = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
-    g = {"dx": e(b, L, H, P), "ddt": e(b, L, H), "dA": e(H), "dB": e(b, L, G, N),
-         "dC": e(b, L, G, N), "dD": e(H) if D is not None else None,
-         "dz": e(b, L, H, P) if z is not None else None,
+    eio = lambda *shape: torch.empty(shape, dtype=io, device=dev)
+    g = {"dx": eio(b, L, H, P), "ddt": eio(b, L, H), "dA": e(H), "dB": eio(b, L, G, N),
+         "dC": eio(b, L, G, N), "dD": e(H) if D is not None else None,
+         "dz": eio(b, L, H, P) if z is not None else None,
          "ddt_bias": e(H) if dt_bias is not None else None,
          "dinitial_states": e(b, H, P, N) if return_dinitial_states else None}
-    ws_bytes = bwd_workspace_size(b, L, H, P, N, G, chunk_size, SSD_F32)
+    ws_bytes = bwd_workspace_size(b, L, H, P, N, G, chunk_size, code)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -249,7 +256,7 @@ def scan_bwd(x, dt, A, B, C, dout, D=None, z=None, dt_bias=None, dt_limit=(0.0, 
         dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(dout),
         _ptr(dfinal_states), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]),
         _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
-        _ptr(g["dinitial_states"]), b, L, H, P, N, SSD_F32, _ptr(workspace), workspace.numel(),
+        _ptr(g["dinitial_states"]), b, L, H, P, N, code, _ptr(workspace), workspace.numel(),
         stream))
     return {k: v for k, v in g.items() if v is not None}
 

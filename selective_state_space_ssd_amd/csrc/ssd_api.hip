@@ -233,7 +233,13 @@ struct BwdLayout {
   int64_t nb = 0;
   size_t off_dt = 0, off_cum = 0, off_s = 0, off_in = 0, off_y = 0, off_g = 0, off_db = 0,
          off_dc = 0, off_da = 0, off_dd = 0, total = 0;
+  // bf16 calls: fp32 copies of the inputs x, dt, B, C, z, dout and fp32
+  // gradients dx, ddt, dB, dC, dz, in this order (kWide* index below)
+  bool bf16 = false;
+  size_t off_w[11] = {};
 };
+enum { kWideX, kWideDt, kWideB, kWideC, kWideZ, kWideDout, kWideDx, kWideDdt, kWideDb, kWideDc,
+       kWideDz };
 
 int bwd_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                int ngroups, int chunk_size, int dtype, BwdLayout* bl) {
@@ -241,7 +247,6 @@ int bwd_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, i
   int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
                         &lay);
   if (st != SSD_OK) return st;
-  if (dtype != SSD_F32) return SSD_ERR_UNSUPPORTED;
   if (!ssd::config_supported(headdim, dstate, 64)) return SSD_ERR_UNSUPPORTED;
   const int64_t nb = ssd::bwd_blocks(seqlen);
   int64_t units, blkn, stn, xn, bcn;
@@ -262,6 +267,17 @@ int bwd_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, i
   bl->off_da = bl->off_dc + round_up((size_t)bcn * 4);
   bl->off_dd = bl->off_da + round_up((size_t)units * 4);
   bl->total = bl->off_dd + round_up((size_t)units * 4);
+  if (dtype == SSD_BF16) {
+    int64_t gn;
+    if (!mul_ok(batch * seqlen * ngroups, dstate, &gn)) return SSD_ERR_INVALID_ARG;
+    const int64_t ndt = batch * seqlen * nheads;
+    const int64_t sizes[11] = {xn, ndt, gn, gn, xn, xn, xn, ndt, gn, gn, xn};
+    bl->bf16 = true;
+    for (int k = 0; k < 11; ++k) {
+      bl->off_w[k] = bl->total;
+      bl->total += round_up((size_t)sizes[k] * 4);
+    }
+  }
   if (batch == 0 || seqlen == 0) bl->total = 0;
   return SSD_OK;
 }
@@ -465,13 +481,13 @@ int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
   return SSD_OK;
 }
 
-int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B, const float* C,
-                 const float* D, const float* z, const float* dt_bias, float dt_min, float dt_max,
-                 int chunk_size, int ngroups, const float* initial_states, const float* dout,
-                 const float* dfinal_states, float* dx, float* ddt, float* dA, float* dB,
-                 float* dC, float* dD, float* dz, float* ddt_bias, float* dinitial_states,
-                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                 const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
+                 int chunk_size, int ngroups, const float* initial_states, const void* dout,
+                 const float* dfinal_states, void* dx, void* ddt, float* dA, void* dB, void* dC,
+                 float* dD, void* dz, float* ddt_bias, float* dinitial_states, int64_t batch,
+                 int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   BwdLayout bl;
   int st = bwd_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, &bl);
   if (st != SSD_OK) return st;
@@ -487,21 +503,23 @@ int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B
                        dinitial_states};
   for (const void* q : v16)
     if (!aligned(q, 16)) return SSD_ERR_ALIGNMENT;
-  const void* v4[] = {dt, A, D, dt_bias, ddt, dA, dD, ddt_bias};
+  const int es = dtype == SSD_BF16 ? 2 : 4;  // bytes per element of the dtype tensors
+  const void* v4[] = {A, D, dt_bias, dA, dD, ddt_bias};
   for (const void* q : v4)
     if (!aligned(q, 4)) return SSD_ERR_ALIGNMENT;
+  if (!aligned(dt, es) || !aligned(ddt, es)) return SSD_ERR_ALIGNMENT;
   // outputs must not overlap any input, each other or the workspace
   const int64_t nx = batch * seqlen * nheads * headdim, nbc = batch * seqlen * ngroups * dstate;
   const int64_t nst = batch * nheads * headdim * dstate, ndt = batch * seqlen * nheads;
-  const Span ins[] = {span(x, nx * 4), span(dt, ndt * 4), span(A, nheads * 4),
-                      span(B, nbc * 4), span(C, nbc * 4), span(D, D ? nheads * 4 : 0),
-                      span(z, z ? nx * 4 : 0), span(dt_bias, dt_bias ? nheads * 4 : 0),
-                      span(initial_states, initial_states ? nst * 4 : 0), span(dout, nx * 4),
+  const Span ins[] = {span(x, nx * es), span(dt, ndt * es), span(A, nheads * 4),
+                      span(B, nbc * es), span(C, nbc * es), span(D, D ? nheads * 4 : 0),
+                      span(z, z ? nx * es : 0), span(dt_bias, dt_bias ? nheads * 4 : 0),
+                      span(initial_states, initial_states ? nst * 4 : 0), span(dout, nx * es),
                       span(dfinal_states, dfinal_states ? nst * 4 : 0),
                       span(workspace, (int64_t)bl.total)};
-  const Span outs[] = {span(dx, nx * 4), span(ddt, ndt * 4), span(dA, nheads * 4),
-                       span(dB, nbc * 4), span(dC, nbc * 4), span(dD, dD ? nheads * 4 : 0),
-                       span(dz, dz ? nx * 4 : 0), span(ddt_bias, ddt_bias ? nheads * 4 : 0),
+  const Span outs[] = {span(dx, nx * es), span(ddt, ndt * es), span(dA, nheads * 4),
+                       span(dB, nbc * es), span(dC, nbc * es), span(dD, dD ? nheads * 4 : 0),
+                       span(dz, dz ? nx * es : 0), span(ddt_bias, ddt_bias ? nheads * 4 : 0),
                        span(dinitial_states, dinitial_states ? nst * 4 : 0)};
   for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
     if (outs[a].hi <= outs[a].lo) continue;
@@ -517,6 +535,22 @@ int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B
   if (batch == 0) return SSD_OK;
 
   char* ws = static_cast<char*>(workspace);
+  // bf16: every step below runs on fp32 copies; the gradients of the bf16
+  // tensors land in fp32 buffers and are rounded into the caller's at the end
+  const void* in[6] = {x, dt, B, C, z, dout};
+  void* grad[5] = {dx, ddt, dB, dC, dz};
+  if (bl.bf16 && nonempty) {
+    const int64_t nin[6] = {nx, ndt, nbc, nbc, nx, nx};
+    for (int k = 0; k < 6; ++k) {
+      if (!in[k]) continue;
+      float* w = reinterpret_cast<float*>(ws + bl.off_w[k]);
+      if (ssd::launch_widen_bf16(in[k], w, nin[k], stream) != hipSuccess) return SSD_ERR_HIP;
+      in[k] = w;
+    }
+    for (int k = 0; k < 5; ++k)
+      if (grad[k]) grad[k] = ws + bl.off_w[kWideDx + k];
+  }
+  x = in[0]; dt = in[1]; B = in[2]; C = in[3]; z = in[4]; dout = in[5];
   ssd::Problem p;
   p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.z = nullptr; p.dt_bias = dt_bias;
   p.dt_min = dt_min; p.dt_max = dt_max; p.init = initial_states;
@@ -544,7 +578,7 @@ int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B
   ssd::BwdProblem q;
   q.fwd = p;
   q.fwd.z = z;
-  q.dout = dout;
+  q.dout = static_cast<const float*>(dout);
   q.dfinal = dfinal_states;
   q.dy = nonempty ? reinterpret_cast<float*>(ws + bl.off_y) : nullptr;
   q.pc = nonempty ? reinterpret_cast<float*>(ws + bl.off_s) : nullptr;
@@ -553,9 +587,22 @@ int ssd_scan_bwd(const float* x, const float* dt, const float* A, const float* B
   q.dCh = nonempty ? reinterpret_cast<float*>(ws + bl.off_dc) : nullptr;
   q.dA_p = nonempty ? reinterpret_cast<float*>(ws + bl.off_da) : nullptr;
   q.dD_p = nonempty ? reinterpret_cast<float*>(ws + bl.off_dd) : nullptr;
-  q.dx = dx; q.dz = dz; q.ddt = ddt; q.dA = dA; q.dB = dB; q.dC = dC; q.dD = dD;
-  q.ddt_bias = ddt_bias; q.dinit = dinitial_states;
+  q.dx = static_cast<float*>(grad[0]);
+  q.ddt = static_cast<float*>(grad[1]);
+  q.dB = static_cast<float*>(grad[2]);
+  q.dC = static_cast<float*>(grad[3]);
+  q.dz = static_cast<float*>(grad[4]);
+  q.dA = dA; q.dD = dD; q.ddt_bias = ddt_bias; q.dinit = dinitial_states;
   if (ssd::launch_bwd(q, stream) != hipSuccess) return SSD_ERR_HIP;
+  if (bl.bf16 && nonempty) {
+    void* outs_bf16[5] = {dx, ddt, dB, dC, dz};
+    const int64_t nout[5] = {nx, ndt, nbc, nbc, nx};
+    for (int k = 0; k < 5; ++k)
+      if (outs_bf16[k] &&
+          ssd::launch_narrow_bf16(static_cast<const float*>(grad[k]), outs_bf16[k], nout[k],
+                                  stream) != hipSuccess)
+        return SSD_ERR_HIP;
+  }
   return SSD_OK;
 }
 

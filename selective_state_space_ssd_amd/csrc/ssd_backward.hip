@@ -577,4 +577,69 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- bf16 <-> fp32 for the backward of bf16 inputs --------------------------
+// The backward of bf16 inputs widens them to fp32 (exactly), runs the fp32
+// kernels and rounds the gradients of the bf16 tensors to bf16 (nearest
+// even).  Eight elements per thread; 16-byte accesses when both pointers are
+// 16-byte aligned (`vec`), element by element otherwise and in the tail.
+
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const bf16_t* __restrict__ src,
+                                                          float* __restrict__ dst, int64_t n,
+                                                          bool vec) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (vec && i + 8 <= n) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    f4 a, b;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      a[2 * k] = bf16_lo(w[k]);
+      a[2 * k + 1] = bf16_hi(w[k]);
+      b[2 * k] = bf16_lo(w[k + 2]);
+      b[2 * k + 1] = bf16_hi(w[k + 2]);
+    }
+    st4(dst + i, a);
+    st4(dst + i + 4, b);
+  } else {
+    for (int64_t k = i; k < n && k < i + 8; ++k) dst[k] = to_f32(src[k]);
+  }
+}
+
+__global__ __launch_bounds__(256) void narrow_bf16_kernel(const float* __restrict__ src,
+                                                           bf16_t* __restrict__ dst, int64_t n,
+                                                           bool vec) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (vec && i + 8 <= n) {
+    const f4 a = ld4(src + i), b = ld4(src + i + 4);
+    uint4 v;
+    v.x = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+    v.y = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+    v.z = f32_to_bf16_bits(b[0]) | (f32_to_bf16_bits(b[1]) << 16);
+    v.w = f32_to_bf16_bits(b[2]) | (f32_to_bf16_bits(b[3]) << 16);
+    *reinterpret_cast<uint4*>(dst + i) = v;
+  } else {
+    for (int64_t k = i; k < n && k < i + 8; ++k) dst[k] = (bf16_t)f32_to_bf16_bits(src[k]);
+  }
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 7) / 8;
+  hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(src), dst, n, aligned16(src) && aligned16(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 7) / 8;
+  hipLaunchKernelGGL(narrow_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     src, static_cast<bf16_t*>(dst), n, aligned16(src) && aligned16(dst));
+  return hipGetLastError();
+}
+
 }  // namespace ssd

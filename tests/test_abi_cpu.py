@@ -357,14 +357,17 @@ def test_block_rejected_before_launch(desc, changes, want):
 def test_workspace_size_backward():
     """dt, cum [b, H, nb, 64]; two state arrays and G [b, nb, H, P N]; y/dY
     [b, L, H, P]; dB and dC parts [b, L, H, N]; dA and dD parts [b, nb, H];
-    nb = ceil(L / 64) whatever the chunk size.  bf16 is not offered."""
+    nb = ceil(L / 64) whatever the chunk size.  bf16 adds fp32 copies of x,
+    dt, B, C, z, dout and fp32 buffers for dx, ddt, dB, dC, dz."""
     for (b, L, H, P, N, G, Q) in SIZES:
         nb = math.ceil(L / 64)
         st = _r(b * nb * H * P * N * 4)
         want = (2 * _r(b * H * nb * 64 * 4) + 3 * st + _r(b * L * H * P * 4) +
                 2 * _r(b * L * H * N * 4) + 2 * _r(b * nb * H * 4))
         assert ssd.bwd_workspace_size(b, L, H, P, N, G, Q, 0) == want
-        assert ssd.bwd_workspace_size(b, L, H, P, N, G, Q, 1) == 0
+        xn, ndt, gn = b * L * H * P, b * L * H, b * L * G * N
+        wide = 5 * _r(xn * 4) + 2 * _r(ndt * 4) + 4 * _r(gn * 4)
+        assert ssd.bwd_workspace_size(b, L, H, P, N, G, Q, 1) == want + wide
 
 
 BWD = dict(x=0x10000000, dt=0x11000000, A=0x12000000, B=0x13000000, C=0x14000000,
@@ -385,7 +388,10 @@ def call_bwd(**changes):
 
 
 BWD_CASES = [
-    ("bf16", dict(dtype=1), UNSUPPORTED),
+    ("bf16 (stops at workspace)", dict(dtype=1), WORKSPACE),
+    ("bf16 dt on an odd address", dict(dtype=1, dt=0x11000001), ALIGN),
+    ("f32 ddt 2-byte aligned", dict(ddt=0x21000002), ALIGN),
+    ("bf16 dx overlaps x", dict(dtype=1, dx=0x10000000 + 100 * 4 * 64 * 2 - 16), INVALID),
     ("D given without dD", dict(dD=None), INVALID),
     ("dz without z", dict(z=None), INVALID),
     ("dt_bias without ddt_bias", dict(ddt_bias=None), INVALID),

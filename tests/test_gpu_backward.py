@@ -133,3 +133,54 @@ def test_bwd_full_size():
     log("test_bwd_full_size: GPU and oracle")
     g, ref = _run(inp, t, dout, None, init=False)
     _compare_all(g, ref)
+
+
+# --------------------------------------------------------------------------
+# bf16 inputs: widened to fp32 in the workspace, the fp32 backward, gradients
+# of the bf16 tensors rounded to bf16
+# --------------------------------------------------------------------------
+
+BF16_OUT = ("dx", "ddt", "dB", "dC", "dz")
+F32_OUT = ("dA", "dD", "ddt_bias", "dinitial_states")
+
+
+def _bf16_bits(a):
+    """float32 -> (bf16 bit patterns as int16, the rounded values), nearest even."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bits.view(np.int16), (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("N,H,G,L", [(128, 4, 2, 2 * 64 + 37), (64, 8, 8, 300), (16, 6, 3, 1)])
+def test_bwd_bf16(N, H, G, L):
+    """Every gradient against the oracle on the bf16-rounded inputs (bf16
+    gradients to the bf16 bar, fp32 ones to the fp32 bar), and the call equal
+    bit for bit to the fp32 backward of the same values with the bf16
+    gradients rounded."""
+    rng = np.random.default_rng(7300 + N + L)
+    w = Workload("bwd16", 2, L, H, 64, N, G, 128, "bf16", 7300 + N + L, init=True)
+    inp = make_inputs(w)
+    t = upload(inp, "bf16")
+    dout_bits, dout = _bf16_bits(rng.standard_normal(inp["x"].shape).astype(np.float32))
+    dout16 = torch.from_numpy(dout_bits).to(DEV).view(torch.bfloat16)
+    dfin = torch.from_numpy(rng.standard_normal((2, H, 64, N)).astype(np.float32)).to(DEV)
+    log(f"test_bwd_bf16 N={N} H={H} G={G} L={L}")
+    kw = dict(D=t["D"], dt_bias=t["dt_bias"], chunk_size=128,
+              initial_states=t["initial_states"], dfinal_states=dfin)
+    g = ssd.scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], dout16, z=t["z"], **kw)
+    g32 = ssd.scan_bwd(t["x"].float(), t["dt"].float(), t["A"], t["B"].float(), t["C"].float(),
+                       dout16.float(), z=t["z"].float(), **kw)
+    torch.cuda.synchronize()
+    for k in BF16_OUT:
+        assert g[k].dtype == torch.bfloat16, k
+        assert torch.equal(g[k], g32[k].to(torch.bfloat16)), k
+    for k in F32_OUT:
+        assert g[k].dtype == torch.float32 and torch.equal(g[k], g32[k]), k
+    ref = oracle.ssd_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         dout.astype(np.float64), D=inp["D"], z=inp["z"],
+                         dt_bias=inp["dt_bias"], initial_states=inp["initial_states"],
+                         dfinal=dfin.cpu().numpy().astype(np.float64))
+    for k in BF16_OUT:
+        compare(k, np64(g[k]), ref[k], TOL["bf16"])
+    for k in F32_OUT:
+        compare(k, np64(g[k]), ref[k], TOL["f32"])

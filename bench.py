@@ -61,15 +61,20 @@ def measured_traffic(kernel_stage):
 def alg_flops(w):
     """Algorithmic flops of one call, by stage (chunked SSD, causal, C.B^T once
     per group): chunk state 2QPN per (chunk, head); state passing 2PN per
-    (chunk, head); chunk scan 2QPN + PQ(Q+1) per (chunk, head) plus NQ(Q+1)
-    per (chunk, group)."""
+    (chunk, head); chunk scan 2QPN + PQ(Q+1) per (chunk, head); C.B^T NQ(Q+1)
+    per (chunk, group), in the stage that forms it: the state-passing launch
+    when the four-heads chunk scan runs with two or more of its workgroups per
+    group (it reads the tiles from there), else the chunk scan."""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
     nc = math.ceil(L / Q)
+    gram = b * nc * G * N * Q * (Q + 1)
+    group_scan = (Q in (64, 128) and N in (64, 128) and (H // G) % 4 == 0 and H // G >= 8
+                  and not (w.dtype == "bf16" and Q == 128))
     return {
         "prep": b * L * H * 2.0,
         "chunk_state": b * nc * H * 2.0 * Q * P * N,
-        "state_passing": b * nc * H * 2.0 * P * N,
-        "chunk_scan": b * nc * (H * (2.0 * Q * P * N + P * Q * (Q + 1)) + G * N * Q * (Q + 1)),
+        "state_passing": b * nc * H * 2.0 * P * N + (gram if group_scan else 0),
+        "chunk_scan": b * nc * H * (2.0 * Q * P * N + P * Q * (Q + 1)) + (0 if group_scan else gram),
     }
 
 

@@ -139,6 +139,14 @@ extern "C" {
  *   B^T       [batch, nchunks, ngroups] blocks of dstate x chunk_size bf16
  *             (present only when dtype is SSD_BF16, chunk_size 128 or 256 and
  *             dstate 64 or 128: the bf16 matrix-core kernels' transposed B)
+ *   C.B^T     [batch, nchunks, ngroups] blocks of T(T+1)/2 x 1024 floats,
+ *             T = chunk_size/32: the causal 32 x 32 tiles of B C^T of each
+ *             chunk (tile s <= t numbered t(t+1)/2 + s; in each tile the
+ *             float4 at R*64 + lane holds the values lane `lane` of a
+ *             v_mfma_f32_32x32x2_f32 result keeps in registers 4R..4R+3).
+ *             Present only when chunk_size is 64 or 128, dstate 64 or 128,
+ *             nheads/ngroups a multiple of 4 and at least 8, and the inputs
+ *             are SSD_F32 or SSD_BF16 at chunk_size 64.
  * with nchunks = ceil(seqlen / chunk_size).  Inside a state block (headdim
  * 64) element (p, n) sits at float offset
  *   ((q*2 + p%2)*64 + 32*k + p/2)*4 + n%4,  k = n / (dstate/2),

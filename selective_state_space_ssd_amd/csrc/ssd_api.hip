@@ -40,7 +40,10 @@ struct Layout {
   bool fused = false;
   bool chain = false;  // chain bf16 kernel: no workspace
   // staged path (off_seg: packed-sequence counts, varlen calls only)
+  // (off_gram: tiles of B C^T for the four-heads chunk scan, ssd::use_gram)
   size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0, off_seg = 0;
+  size_t off_gram = 0;
+  bool gram = false;
   // fused bf16 path
   size_t off_ring = 0, off_flags = 0, off_ctl = 0;
   size_t total = 0;
@@ -133,6 +136,18 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     int64_t btn;
     if (!mul_ok(batch * nc * ngroups, dstate * chunk_size, &btn)) return SSD_ERR_INVALID_ARG;
     lay->total += round_up((size_t)btn * 2);
+  }
+  if (ssd::use_gram(nheads, dstate, ngroups, chunk_size, dtype == SSD_BF16)) {
+    int64_t gramn;
+    if (!mul_ok(batch * nc * ngroups, ssd::gram_tile_floats(chunk_size), &gramn))
+      return SSD_ERR_INVALID_ARG;
+    // the state-passing launch adds grid planes for the tiles; past the
+    // grid's limit the chunk scan forms them itself
+    if (ssd::gram_planes(batch, nc, nheads, dstate, ngroups, chunk_size) + batch <= 65535) {
+      lay->gram = true;
+      lay->off_gram = lay->total;
+      lay->total += round_up((size_t)gramn * 4);
+    }
   }
   if (varlen) {
     int64_t segn;
@@ -317,6 +332,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.ws_states_in = staged_ws ? reinterpret_cast<float*>(ws + lay.off_states_in) : nullptr;
   p.ws_bt = staged_ws ? reinterpret_cast<uint16_t*>(ws + lay.off_bt) : nullptr;
   p.ws_seg = staged_ws && varlen ? reinterpret_cast<int32_t*>(ws + lay.off_seg) : nullptr;
+  p.ws_gram = staged_ws && lay.gram ? reinterpret_cast<float*>(ws + lay.off_gram) : nullptr;
   p.fs_ring = lay.fused ? reinterpret_cast<float*>(ws + lay.off_ring) : nullptr;
   p.fs_flags = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_flags) : nullptr;
   p.fs_ctl = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_ctl) : nullptr;
@@ -565,6 +581,7 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   p.ws_states_in = nonempty ? reinterpret_cast<float*>(ws + bl.off_in) : nullptr;
   p.ws_bt = nullptr;
   p.ws_seg = nullptr;
+  p.ws_gram = nullptr;  // the chunk scan forms its tiles of B C^T itself
   p.fs_ring = nullptr; p.fs_flags = nullptr; p.fs_ctl = nullptr;
   p.fused_kind = 0;
   if (nonempty) {

@@ -205,10 +205,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 // Four heads of one group per workgroup, two waves per head (Q = 64 or 128,
 // N = 64 or 128, nheads / ngroups a multiple of 4).
 //
-// The group's C and B tiles of the chunk are staged in LDS once.  The four
-// waves first compute the causal 32 x 32 tiles of G^T = B C^T (G[t][s] =
-// C_t . B_s) on v_mfma_f32_32x32x2_f32, shared by the four heads, and park
-// them in LDS in register order.  Each wave then holds half of its head's
+// The group's C tile of the chunk is staged in LDS once, and so are the
+// causal 32 x 32 tiles of G^T = B C^T (G[t][s] = C_t . B_s), shared by the
+// four heads, in register order.  With PRE they come from the workspace,
+// formed once per (chunk, group) by the chunk-state launch; otherwise B is
+// staged too and the eight waves form them on v_mfma_f32_32x32x2_f32 first.
+// Each wave then holds half of its head's
 // Q x 64 output in accumulators (t-tiles {h, Q/32-1-h} of wave half h, x 2
 // p-tiles of 32 x 32, so both halves do the same causal work):
 //   1. acc = C . H_in^T        (A: C rows from LDS; B: H_in, tiled layout,
@@ -225,33 +227,24 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 // per lane, two full 256-byte rows per instruction.
 // ---------------------------------------------------------------------------
 
-template <int NT>
-__device__ __forceinline__ void tile_of(int tau, int* si, int* ti) {
-  // causal tiles numbered ti*(ti+1)/2 + si, si <= ti
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    if (tau >= t * (t + 1) / 2 && tau < (t + 1) * (t + 2) / 2) {
-      *ti = t;
-      *si = tau - t * (t + 1) / 2;
-    }
-}
-
-template <typename T, int Q, int N, bool GATE>
+template <typename T, int Q, int N, bool GATE, bool PRE>
 __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ Dv, const T* __restrict__ z, const float* __restrict__ ws_dt,
-    const float* __restrict__ ws_cum, const float* __restrict__ states_in, T* __restrict__ out,
+    const float* __restrict__ ws_cum, const float* __restrict__ states_in,
+    const float* __restrict__ gram, T* __restrict__ out,
     const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   constexpr int P = 64, NT = Q / 32, CS = N + 4, NG = NT * (NT + 1) / 2, KQ = N / 8;
   constexpr int NW = 8;                   // waves: two per head
   constexpr int GW = (NG + NW - 1) / NW;  // G tiles per wave, at most
   constexpr int NS = NT / 2;              // t-tiles per wave
-  constexpr int BGS = (Q * CS > NG * 1024) ? Q * CS : NG * 1024;
+  // B tile, then the G^T tiles; only the tiles when they are read in
+  constexpr int BGS = (!PRE && Q * CS > NG * 1024) ? Q * CS : NG * 1024;
   constexpr int HR = 3;                   // ring of state loads: two steps ahead
   constexpr float kLog2e = 1.4426950408889634f;
   static_assert((Q == 64 || Q == 128) && (N == 64 || N == 128), "tile");
   __shared__ float c_lds[Q * CS];
-  __shared__ float bg_lds[BGS];  // B tile, then the G^T tiles
+  __shared__ float bg_lds[BGS];
   __shared__ float cum_lds[4][Q];  // running sums in log2 units (cum * log2 e)
   __shared__ float dt_lds[4][Q];
   // u_s = 2^(cum_e - cum_s) dt_s, e = last step of s's 32-step tile (<= dt_s);
@@ -287,10 +280,22 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
       const int e = (k * 64 * NW + tid) * 4;
       const int row = e / N, col = e % N;
       const int r = row < last ? row : last;
-      f4 cv = ld4(cs + r * rs + col), bv = ld4(bs + r * rs + col);
-      if (row > last) cv = bv = f4{0.f, 0.f, 0.f, 0.f};
+      f4 cv = ld4(cs + r * rs + col);
+      if (row > last) cv = f4{0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f4*>(&c_lds[row * CS + col]) = cv;
-      *reinterpret_cast<f4*>(&bg_lds[row * CS + col]) = bv;
+      if constexpr (!PRE) {
+        f4 bv = ld4(bs + r * rs + col);
+        if (row > last) bv = f4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f4*>(&bg_lds[row * CS + col]) = bv;
+      }
+    }
+    if constexpr (PRE) {
+      const float* gs = gram + ((b * nc + c) * G + g) * (int64_t)(NG * 1024);
+#pragma unroll
+      for (int k0 = 0; k0 < NG * 256; k0 += 64 * NW) {
+        const int k = k0 + tid;
+        if (k < NG * 256) *reinterpret_cast<f4*>(&bg_lds[4 * k]) = ld4(gs + 4 * k);
+      }
     }
     const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
     for (int k = tid; k < 4 * Q; k += 64 * NW) {
@@ -305,9 +310,9 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
       if (w == 0) seg_lds[t] = sc ? sc[t] : 0;
     }
   }
-  __syncthreads();
 
-  // ---- first per-head loads, in flight during the shared G phase -------------
+  // ---- first per-head loads, in flight during the staging barrier (and the
+  // shared G phase) ----------------------------------------------------------
   const T* xh = x + ((b * L + t0) * H + h) * P + 2 * i;
   const T* zh = z + ((b * L + t0) * H + h) * P + 2 * i;  // read only when GATE
   T* oh = out + ((b * L + t0) * H + h) * P + 2 * i;
@@ -344,8 +349,10 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     }
   };
   if constexpr (GATE) load_z(own(0));
+  __syncthreads();
 
   // ---- 1. causal tiles of G^T = B C^T, shared by the four heads ---------------
+  if constexpr (!PRE) {
   f16x gt[GW];
 #pragma unroll
   for (int k = 0; k < GW; ++k) {
@@ -382,6 +389,7 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     }
   }
   __syncthreads();
+  }
 
   const float* cumw = cum_lds[slot];
   const float* dtw = dt_lds[slot];
@@ -535,23 +543,42 @@ static bool use_group_kernel(const Problem& p) {
   return (p.Q == 64 || p.Q == 128) && (p.N == 64 || p.N == 128) && ((p.H / p.G) % 4 == 0);
 }
 
+bool use_group_scan(int64_t H, int64_t N, int64_t G, int64_t Q, bool bf16) {
+  // bf16 inputs at chunk 128/256 take the bf16 matrix-core kernels instead
+  const bool bf16_kernels = bf16 && (Q == 128 || Q == 256) && (N == 64 || N == 128);
+  return (Q == 64 || Q == 128) && (N == 64 || N == 128) && (H / G) % 4 == 0 && !bf16_kernels;
+}
+
+bool use_gram(int64_t H, int64_t N, int64_t G, int64_t Q, bool bf16) {
+  return use_group_scan(H, N, G, Q, bf16) && H / G >= 8;
+}
+
+int64_t gram_tile_floats(int64_t Q) {
+  const int64_t nt = Q / 32;
+  return nt * (nt + 1) / 2 * 1024;
+}
+
+template <typename T, int Q, int N, bool GATE, bool PRE>
+static void launch_group(const Problem& p, hipStream_t s, int64_t nunits) {
+  hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, GATE, PRE>), dim3((unsigned)nunits),
+                     dim3(512), 0, s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
+                     static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.ws_dt,
+                     p.ws_cum, p.ws_states_in, p.ws_gram, static_cast<T*>(p.out), p.ws_seg, p.L,
+                     p.H, p.G, p.nc, nunits);
+}
+
 template <typename T, int Q, int N>
 static void launch_qn(const Problem& p, hipStream_t s) {
   if constexpr ((Q == 64 || Q == 128) && (N == 64 || N == 128)) {
     if (use_group_kernel(p)) {
       const int64_t nunits = p.b * p.nc * (p.H / 4);
-      if (p.z)
-        hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, true>), dim3((unsigned)nunits),
-                           dim3(512), 0, s, static_cast<const T*>(p.x),
-                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,
-                           static_cast<const T*>(p.z), p.ws_dt, p.ws_cum, p.ws_states_in,
-                           static_cast<T*>(p.out), p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
-      else
-        hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, false>), dim3((unsigned)nunits),
-                           dim3(512), 0, s, static_cast<const T*>(p.x),
-                           static_cast<const T*>(p.B), static_cast<const T*>(p.C), p.D,
-                           static_cast<const T*>(p.z), p.ws_dt, p.ws_cum, p.ws_states_in,
-                           static_cast<T*>(p.out), p.ws_seg, p.L, p.H, p.G, p.nc, nunits);
+      if (p.ws_gram) {
+        if (p.z) launch_group<T, Q, N, true, true>(p, s, nunits);
+        else launch_group<T, Q, N, false, true>(p, s, nunits);
+      } else {
+        if (p.z) launch_group<T, Q, N, true, false>(p, s, nunits);
+        else launch_group<T, Q, N, false, false>(p, s, nunits);
+      }
       return;
     }
   }

@@ -180,6 +180,21 @@ __device__ __forceinline__ void state_tile_coords(int k, int N, int* p, int* n) 
   *n = (N / 2) * (lane >> 5) + 4 * q;
 }
 
+// ---- tiles of G^T = B C^T (chunk scan) ------------------------------------------
+// The causal 32 x 32 tiles (s-tile si <= t-tile ti) of one chunk of one group
+// are numbered tau = ti*(ti+1)/2 + si.  A tile is stored in the register order
+// of v_mfma_f32_32x32x2_f32: the float4 at ((tau*4 + R)*64 + lane) holds
+// registers 4R..4R+3 of that lane, i.e. 1 KB per R, lane-contiguous.
+template <int NT>
+__device__ __forceinline__ void tile_of(int tau, int* si, int* ti) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (tau >= t * (t + 1) / 2 && tau < (t + 1) * (t + 2) / 2) {
+      *ti = t;
+      *si = tau - t * (t + 1) / 2;
+    }
+}
+
 // ---- math -------------------------------------------------------------------
 
 // 2^x on v_exp_f32 (results below the normal range flush to zero) and 1/x on

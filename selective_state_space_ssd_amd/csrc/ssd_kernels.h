@@ -33,6 +33,10 @@ struct Problem {
   uint16_t* ws_bt;       // [b, nc, G] blocks of N x Q bf16: B^T per chunk (bf16 kernels only)
   int32_t* ws_seg;       // [b, nc, Q] sequence starts counted from the chunk start
                          // (seq_idx only; null otherwise)
+  float* ws_gram;        // [b, nc, G] causal 32 x 32 tiles of G^T = B C^T per chunk
+                         // (gram_tile_floats(Q) floats each, ssd_device.h layout): formed
+                         // by the state-passing launch for the four-heads chunk-scan
+                         // kernel; null: that kernel forms them itself
   // fused bf16 kernel
   float* fs_ring;        // [b*H chains][2 slots] tiled P x N states
   unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
@@ -48,6 +52,22 @@ hipError_t launch_seq_count(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_passing(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
+
+// The four-heads-per-workgroup chunk-scan kernel (fp32 scan of fp32 inputs,
+// or of bf16 inputs at chunk 64; Q 64/128, N 64/128, nheads/ngroups a
+// multiple of 4).
+bool use_group_scan(int64_t H, int64_t N, int64_t G, int64_t Q, bool bf16);
+// When that kernel runs with at least two of its workgroups per group and
+// chunk (nheads/ngroups >= 8), the state-passing launch forms each chunk's
+// tiles of B C^T once per group (ws_gram) and the chunk scan reads them
+// instead of forming them in every workgroup of four heads.
+bool use_gram(int64_t H, int64_t N, int64_t G, int64_t Q, bool bf16);
+// Grid planes (z) of G^T tiles that the state-passing launch adds in front of
+// its b planes; the grid's z extent gram_planes + b must stay within 65535.
+int64_t gram_planes(int64_t b, int64_t nc, int64_t H, int64_t N, int64_t G, int64_t Q);
+// Floats of one (batch, chunk, group) block of ws_gram: the Q/32 (Q/32 + 1) / 2
+// causal tiles of 32 x 32.
+int64_t gram_tile_floats(int64_t Q);
 
 // True when the chunk-state kernel chosen for this problem also computes dt
 // and its in-chunk cumsum (stage 1), so no separate stage-1 launch is needed.

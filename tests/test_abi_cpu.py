@@ -74,9 +74,24 @@ def _r(v):
     return (v + 255) // 256 * 256
 
 
+def _gram(b, L, H, N, G, Q, bf16):
+    """Tiles of B C^T per (chunk, group) for the four-heads chunk scan (chunk
+    64/128, dstate 64/128, nheads/ngroups a multiple of 4; bf16 inputs at chunk
+    128 take the bf16 kernels instead), formed once per group when at least
+    two of its workgroups share them (nheads/ngroups >= 8): Q/32 (Q/32 + 1)/2
+    tiles of 32 x 32 fp32."""
+    if Q not in (64, 128) or N not in (64, 128) or (H // G) % 4 or (bf16 and Q == 128):
+        return 0
+    if H // G < 8:
+        return 0
+    nt = Q // 32
+    return _r(b * math.ceil(L / Q) * G * nt * (nt + 1) // 2 * 1024 * 4)
+
+
 SIZES = [(2, 2048, 32, 64, 128, 1, 128), (1, 300, 4, 64, 16, 1, 64),
          (8, 4096, 64, 64, 128, 8, 256), (3, 1, 2, 64, 32, 2, 128), (1, 200, 4, 64, 64, 2, 64),
-         (2, 17, 4, 64, 128, 2, 128)]
+         (2, 17, 4, 64, 128, 2, 128), (1, 200, 16, 64, 64, 2, 64),
+         (1, 300, 8, 64, 128, 2, 128)]
 
 
 def test_workspace_size_formula():
@@ -86,12 +101,13 @@ def test_workspace_size_formula():
             nc = math.ceil(L / Q)
             want = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
             if L <= DECODE_MAX_L:
-                want = 0
-            assert _ws(b, L, H, P, N, G, Q) == want
+                assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
+                continue
+            assert _ws(b, L, H, P, N, G, Q) == want + _gram(b, L, H, N, G, Q, False)
             # intermediates are fp32 for bf16 too; the staged bf16 matrix-core
             # kernels (chunk 128/256, dstate 64/128) add B^T per (chunk, group)
             bt = _r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
-            assert _ws(b, L, H, P, N, G, Q, 1) == (want + bt if want else 0)
+            assert _ws(b, L, H, P, N, G, Q, 1) == want + bt + _gram(b, L, H, N, G, Q, True)
     finally:
         ssd.set_bf16_path(prev)
 
@@ -120,7 +136,8 @@ def test_workspace_size_fused_bf16():
             if L <= DECODE_MAX_L:  # short sequences: the step-by-step kernel, no workspace
                 assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
                 continue
-            assert _ws(b, L, H, P, N, G, Q) == staged  # fp32 is always staged
+            # fp32 is always staged
+            assert _ws(b, L, H, P, N, G, Q) == staged + _gram(b, L, H, N, G, Q, False)
             want = _fused_ws(b, L, H, P, N) if N in (64, 128) else staged  # dstate 16/32: staged
             assert _ws(b, L, H, P, N, G, Q, 1) == want
     finally:
@@ -175,7 +192,7 @@ def test_workspace_size_varlen():
                 finally:
                     ssd.set_bf16_path(prev)
             bt = _r(b * nc * G * N * Q * 2) if (dt and Q in (128, 256) and N in (64, 128)) else 0
-            assert got == staged + bt + _r(b * nc * Q * 4)
+            assert got == staged + bt + _gram(b, L, H, N, G, Q, dt) + _r(b * nc * Q * 4)
     assert ssd.varlen_workspace_size(2, 100, 4, 64, 16, 3, 64, 0) == 0  # rejected shapes
 
 

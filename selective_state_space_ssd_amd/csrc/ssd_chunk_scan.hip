@@ -270,49 +270,52 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   auto own = [&](int j) { return j == 0 ? half : NT - 1 - half; };
   const int smax = own(NS - 1) > own(0) ? own(NS - 1) : own(0);  // last s-tile needed
 
-  // ---- 0. stage C, B, cum, dt ------------------------------------------------
-  {
-    const T* cs = Cm + ((b * L + t0) * G + g) * N;
-    const T* bs = Bm + ((b * L + t0) * G + g) * N;
-    const int64_t rs = G * N;
+  // ---- 0. stage C (and B, or the G^T tiles), cum, dt ---------------------------
+  // Every global load of the set-up -- the tiles, the step tables and this
+  // wave's first per-head operands -- is issued before the first LDS write,
+  // so the set-up waits for one memory latency rather than one per group of
+  // loads.
+  constexpr int KC = Q * N / (4 * 64 * NW);             // float4 per thread per tile
+  constexpr int KG = (NG * 256 + 64 * NW - 1) / (64 * NW);  // float4 of G^T per thread
+  const T* cs = Cm + ((b * L + t0) * G + g) * N;
+  const T* bs = Bm + ((b * L + t0) * G + g) * N;
+  const int64_t rs = G * N;
+  f4 cst[KC], bst[PRE ? 1 : KC], gst[PRE ? KG : 1];
 #pragma unroll
-    for (int k = 0; k < Q * N / (4 * 64 * NW); ++k) {
-      const int e = (k * 64 * NW + tid) * 4;
-      const int row = e / N, col = e % N;
-      const int r = row < last ? row : last;
-      f4 cv = ld4(cs + r * rs + col);
-      if (row > last) cv = f4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f4*>(&c_lds[row * CS + col]) = cv;
-      if constexpr (!PRE) {
-        f4 bv = ld4(bs + r * rs + col);
-        if (row > last) bv = f4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f4*>(&bg_lds[row * CS + col]) = bv;
-      }
-    }
-    if constexpr (PRE) {
-      const float* gs = gram + ((b * nc + c) * G + g) * (int64_t)(NG * 1024);
+  for (int k = 0; k < KC; ++k) {
+    const int e = (k * 64 * NW + tid) * 4;
+    const int row = e / N, col = e % N;
+    const int r = row < last ? row : last;
+    cst[k] = ld4(cs + r * rs + col);
+    if constexpr (!PRE) bst[k] = ld4(bs + r * rs + col);
+  }
+  if constexpr (PRE) {
+    const float* gs = gram + ((b * nc + c) * G + g) * (int64_t)(NG * 1024);
 #pragma unroll
-      for (int k0 = 0; k0 < NG * 256; k0 += 64 * NW) {
-        const int k = k0 + tid;
-        if (k < NG * 256) *reinterpret_cast<f4*>(&bg_lds[4 * k]) = ld4(gs + 4 * k);
-      }
+    for (int k = 0; k < KG; ++k) {
+      const int q = k * 64 * NW + tid;
+      if (q < NG * 256) gst[k] = ld4(gs + 4 * q);
     }
-    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
-    for (int k = tid; k < 4 * Q; k += 64 * NW) {
-      const int w = k / Q, t = k % Q;
-      const int64_t o = ((b * H + h0 + w) * nc + c) * Q + t;
-      const float cum2 = ws_cum[o] * kLog2e, dtv = ws_dt[o];
-      const float cend2 = ws_cum[o - t + (t | 31)] * kLog2e;
-      const bool keep = !sc || sc[t] == sc[t | 31];
-      cum_lds[w][t] = cum2;
-      dt_lds[w][t] = dtv;
-      u_lds[w][t] = keep ? fast_exp2(cend2 - cum2) * dtv : 0.0f;
-      if (w == 0) seg_lds[t] = sc ? sc[t] : 0;
+  }
+  // step tables: step t of head slot w per thread (4 Q <= 512 threads)
+  const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
+  const int tw = tid / Q, tt = tid % Q;
+  const bool tab = tid < 4 * Q;
+  float cum_a = 0.f, dt_a = 0.f, cend_a = 0.f;
+  int32_t seg_a = 0, seg_e = 0;
+  if (tab) {
+    const int64_t o = ((b * H + h0 + tw) * nc + c) * Q + tt;
+    cum_a = ws_cum[o];
+    dt_a = ws_dt[o];
+    cend_a = ws_cum[o - tt + (tt | 31)];
+    if (sc) {
+      seg_a = sc[tt];
+      seg_e = sc[tt | 31];
     }
   }
 
-  // ---- first per-head loads, in flight during the staging barrier (and the
-  // shared G phase) ----------------------------------------------------------
+  // ---- first per-head loads, in flight during the set-up (and the shared G
+  // phase) --------------------------------------------------------------------
   const T* xh = x + ((b * L + t0) * H + h) * P + 2 * i;
   const T* zh = z + ((b * L + t0) * H + h) * P + 2 * i;  // read only when GATE
   T* oh = out + ((b * L + t0) * H + h) * P + 2 * i;
@@ -336,8 +339,6 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
       xv[4 * R + e] = srow <= last ? v : f2{0.f, 0.f};
     }
   };
-#pragma unroll
-  for (int R = 0; R < 4; ++R) load_x(0, R);
   // z rows of the t-tile this wave emits next (its first owned tile now; the
   // second one is loaded as soon as the first has been emitted)
   f2 zv[16];
@@ -348,8 +349,36 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
       zv[m] = ld2(zh + (srow < last ? srow : last) * xs);
     }
   };
-  if constexpr (GATE) load_z(own(0));
+  __builtin_amdgcn_sched_barrier(0);  // every set-up load is issued above
+
+#pragma unroll
+  for (int k = 0; k < KC; ++k) {
+    const int e = (k * 64 * NW + tid) * 4;
+    const int row = e / N, col = e % N;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f4*>(&c_lds[row * CS + col]) = row > last ? zero : cst[k];
+    if constexpr (!PRE) *reinterpret_cast<f4*>(&bg_lds[row * CS + col]) = row > last ? zero : bst[k];
+  }
+  if constexpr (PRE) {
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int q = k * 64 * NW + tid;
+      if (q < NG * 256) *reinterpret_cast<f4*>(&bg_lds[4 * q]) = gst[k];
+    }
+  }
+  if (tab) {
+    const float cum2 = cum_a * kLog2e, cend2 = cend_a * kLog2e;
+    cum_lds[tw][tt] = cum2;
+    dt_lds[tw][tt] = dt_a;
+    u_lds[tw][tt] = seg_a == seg_e ? fast_exp2(cend2 - cum2) * dt_a : 0.0f;
+    if (tw == 0) seg_lds[tt] = seg_a;
+  }
   __syncthreads();
+  // x of the first s-tile and z of the first t-tile stream in under the
+  // state part, which is bound by the matrix cores
+#pragma unroll
+  for (int R = 0; R < 4; ++R) load_x(0, R);
+  if constexpr (GATE) load_z(own(0));
 
   // ---- 1. causal tiles of G^T = B C^T, shared by the four heads ---------------
   if constexpr (!PRE) {

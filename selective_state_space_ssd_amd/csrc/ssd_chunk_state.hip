@@ -14,7 +14,9 @@
 //
 // Two kernels:
 //  * chunk_state_wave_kernel (N = 64 or 128): WPH waves per (chunk, head)
-//    (two as launched), 8 waves per workgroup.  The first wave of a head
+//    (two as launched), 4 waves (two heads) per workgroup: two workgroups
+//    per compute unit in the same round measured 0.5 us faster than one of
+//    four heads on batch 2 x 2048.  The first wave of a head
 //    computes dt and the in-chunk cumsum (stage 1, fused here); then each wave
 //    holds 32-column n-tiles of the state tile in accumulators of v_mfma_f32_32x32x2_f32
 //    while it walks the chunk two timesteps per MFMA.  It computes
@@ -24,6 +26,8 @@
 //    consecutive n of one p -- one float4 of the tiled layout.
 //  * chunk_state_kernel (any N): four waves per (chunk, head) on
 //    v_mfma_f32_16x16x4_f32, after a separate stage-1 launch.
+#include <type_traits>
+
 #include "ssd_dt.h"
 #include "ssd_kernels.h"
 
@@ -34,21 +38,22 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 
 template <typename T, int Q, int N, int WPH>
-__global__ __launch_bounds__(512) void chunk_state_wave_kernel(
+__global__ __launch_bounds__(256) void chunk_state_wave_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ dt_raw,
     const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
     float* __restrict__ ws_dt, float* __restrict__ ws_cum, float* __restrict__ states,
     const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
   // WPH waves per head, each owning NTW n-tiles (both p-halves); HPW heads per
-  // workgroup of 8 waves
-  constexpr int P = 64, NTN = N / 32, NTW = NTN / WPH, HPW = 8 / WPH, E = Q / kWave;
+  // workgroup of 4 waves
+  constexpr int P = 64, NTN = N / 32, NTW = NTN / WPH, HPW = 4 / WPH, E = Q / kWave;
   static_assert((N == 64 || N == 128) && NTW >= 1 && NTW * WPH == NTN, "tile");
   __shared__ float w_lds[HPW][2][Q / 2];  // [head][t % 2][t / 2]
 
   const int64_t HQ = (H + HPW - 1) / HPW;
   const int64_t u = xcd_remap(blockIdx.x, nunits);  // ((b*nc + c)*HQ + hq)
   const int64_t hq = u % HQ, c = (u / HQ) % nc, b = u / (HQ * nc);
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int slot = wave / WPH, half = wave % WPH;  // head within the workgroup, wave within the head
   const int64_t h = hq * HPW + slot;
   const bool active = h < H;
@@ -71,67 +76,77 @@ __global__ __launch_bounds__(512) void chunk_state_wave_kernel(
   const int64_t g = h / (H / G);
   const int i = lane % 32, kk = lane / 32;
   const int64_t t0 = c * Q;
-  const T* xb = x + ((b * L + t0) * H + h) * P + 2 * i;
-  const T* bb = Bm + ((b * L + t0) * G + g) * N + 32 * NTW * half + i;
-  const int64_t xs = H * P, bs = G * N;
   const float* wrow = w_lds[slot][kk];  // w of timesteps 2m + kk, m = 0 .. Q/2-1
 
   f16x acc[NTW][2];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) acc[nt][0] = acc[nt][1] = zero16();
 
-  // Loads run PF steps ahead of the MFMAs through a ring of registers.  Rows
-  // past the sequence end are clamped to the last row (always readable) and
-  // their operands replaced by zeros, so the loop body has no divergent
-  // branch and every load can be in flight while earlier steps compute.
+  // Loads run PF steps ahead of the MFMAs through a ring of registers.  Each
+  // lane addresses its rows as a 32-bit element offset from the wave's base
+  // (a chunk spans fewer than 2^32 elements of x and of B: rows < 256 of
+  // H*P <= 2^22 and G*N <= 2^23 elements).  A chunk that ends early takes a
+  // second copy of the loop in which rows past the end are clamped to the
+  // last row (always readable) and their operands replaced by zeros; full
+  // chunks (all but a ragged last one) skip the clamps and selects.
   constexpr int PF = 8, KS = Q / 2;
   static_assert(KS % PF == 0, "ring");
-  const int64_t last = L - 1 - t0;  // last readable row of this chunk
-  auto row = [&](int m) -> int64_t {
-    const int64_t t = 2 * m + kk;
-    return t < last ? t : last;
-  };
-  f2 xr[PF];
-  float br[PF][NTW];
-#pragma unroll
-  for (int d = 0; d < PF; ++d) {
-    const int64_t t = row(d);
-    xr[d] = ld2(xb + t * xs);
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bb + t * bs + 32 * nt);
-  }
-  for (int m0 = 0; m0 < KS; m0 += PF) {
-    f4 wv[PF / 4];
-#pragma unroll
-    for (int k = 0; k < PF / 4; ++k) wv[k] = *reinterpret_cast<const f4*>(wrow + m0 + 4 * k);
+  const int last = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
+  const T* xw = x + ((b * L + t0) * H + h) * P;
+  const T* bw = Bm + ((b * L + t0) * G + g) * N + 32 * NTW * half;
+  const uint32_t xs = (uint32_t)(H * P), bs = (uint32_t)(G * N);
+  auto main_loop = [&](auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    auto row = [&](int m) -> uint32_t {
+      const int t = 2 * m + kk;
+      return (uint32_t)(FULL || t < last ? t : last);
+    };
+    f2 xr[PF];
+    float br[PF][NTW];
 #pragma unroll
     for (int d = 0; d < PF; ++d) {
-      const int m = m0 + d;
-      // rows past the end contribute exactly zero (selects, not branches)
-      const bool ok = 2 * m + kk <= last;
-      const float w = wv[d / 4][d % 4];
-      const float x0 = ok ? xr[d][0] * w : 0.0f, x1 = ok ? xr[d][1] * w : 0.0f;
-      float bv[NTW];
+      const uint32_t t = row(d);
+      xr[d] = ld2(xw + (t * xs + 2 * i));
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) bv[nt] = ok ? br[d][nt] : 0.0f;
-      {  // refill the slot for step m + PF; past the chunk end it re-reads a
-         // valid row (unused), so the loads are issued unconditionally and
-         // the compiler's count of loads in flight stays exact across steps
-        const int64_t t = row(m + PF < KS ? m + PF : KS - 1);
-        xr[d] = ld2(xb + t * xs);
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bb + t * bs + 32 * nt);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        acc[nt][0] = mfma32x32x2(bv[nt], x0, acc[nt][0]);
-        acc[nt][1] = mfma32x32x2(bv[nt], x1, acc[nt][1]);
-      }
-      // keep each step's loads and MFMAs in program order: the scheduler
-      // would otherwise sink the refills next to their uses
-      __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bw + (t * bs + 32 * nt + i));
     }
-  }
+    for (int m0 = 0; m0 < KS; m0 += PF) {
+      f4 wv[PF / 4];
+#pragma unroll
+      for (int k = 0; k < PF / 4; ++k) wv[k] = *reinterpret_cast<const f4*>(wrow + m0 + 4 * k);
+#pragma unroll
+      for (int d = 0; d < PF; ++d) {
+        const int m = m0 + d;
+        // rows past the end contribute exactly zero (selects, not branches)
+        const bool ok = FULL || 2 * m + kk <= last;
+        const float w = wv[d / 4][d % 4];
+        const float x0 = ok ? xr[d][0] * w : 0.0f, x1 = ok ? xr[d][1] * w : 0.0f;
+        float bv[NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) bv[nt] = ok ? br[d][nt] : 0.0f;
+        {  // refill the slot for step m + PF; past the chunk end it re-reads a
+           // valid row (unused), so the loads are issued unconditionally and
+           // the compiler's count of loads in flight stays exact across steps
+          const uint32_t t = row(m + PF < KS ? m + PF : KS - 1);
+          xr[d] = ld2(xw + (t * xs + 2 * i));
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bw + (t * bs + 32 * nt + i));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          acc[nt][0] = mfma32x32x2(bv[nt], x0, acc[nt][0]);
+          acc[nt][1] = mfma32x32x2(bv[nt], x1, acc[nt][1]);
+        }
+        // keep each step's loads and MFMAs in program order: the scheduler
+        // would otherwise sink the refills next to their uses
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (last == Q - 1)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
 
   // register 4R+e of tile (nt, pt): n = 32*(NTW*half + nt) + 8*R + 4*kk + e, p = 2*i + pt
   float* dst = states + ((b * nc + c) * H + h) * (int64_t)(P * N);
@@ -262,8 +277,8 @@ static void launch_qn(const Problem& p, hipStream_t s) {
     // but load every x row four times, and measured slower (48 vs 39 us on
     // batch 2 x seqlen 2048, 32 heads, dstate 128)
     constexpr int WPH = 2;
-    const int64_t nunits = p.b * p.nc * ((p.H + (8 / WPH) - 1) / (8 / WPH));
-    hipLaunchKernelGGL((chunk_state_wave_kernel<T, Q, N, WPH>), dim3((unsigned)nunits), dim3(512), 0,
+    const int64_t nunits = p.b * p.nc * ((p.H + (4 / WPH) - 1) / (4 / WPH));
+    hipLaunchKernelGGL((chunk_state_wave_kernel<T, Q, N, WPH>), dim3((unsigned)nunits), dim3(256), 0,
                        s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
                        static_cast<const T*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.ws_dt,
                        p.ws_cum, p.ws_states, p.ws_seg, p.L, p.H, p.G, p.nc, nunits);

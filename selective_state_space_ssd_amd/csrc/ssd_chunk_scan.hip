@@ -257,7 +257,9 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   const int64_t hq = u % HQ, c = (u / HQ) % nc, b = u / (HQ * nc);
   const int64_t h0 = 4 * hq;
   const int64_t g = h0 / (H / G);
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  // wave-uniform (the buffer resources below and the per-wave branches need it)
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int slot = wave >> 1, half = wave & 1;
   const int i = lane % 32, kk = lane / 32;
   const int64_t h = h0 + slot;
@@ -316,9 +318,15 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
 
   // ---- first per-head loads, in flight during the set-up (and the shared G
   // phase) --------------------------------------------------------------------
-  const T* xh = x + ((b * L + t0) * H + h) * P + 2 * i;
-  const T* zh = z + ((b * L + t0) * H + h) * P + 2 * i;  // read only when GATE
-  T* oh = out + ((b * L + t0) * H + h) * P + 2 * i;
+  // x, z and out rows of this head in the chunk through buffer resources that
+  // end after row `last`: padding rows read as zero and are never written
+  const int64_t hoff = ((b * L + t0) * H + h) * P;
+  const uint32_t rowb = (uint32_t)(xs * sizeof(T));  // bytes from one step to the next
+  const uint32_t nbytes = (uint32_t)((last * xs + P) * sizeof(T));
+  const auto xr = row_rsrc(x + hoff, nbytes);
+  const auto zr = row_rsrc(GATE ? z + hoff : x + hoff, nbytes);  // read only when GATE
+  const auto orr = row_rsrc(out + hoff, nbytes);
+  const uint32_t lane_b = (uint32_t)((4 * kk * xs + 2 * i) * sizeof(T));  // row 4 kk, column 2 i
   const float* hs = states_in + ((b * nc + c) * H + h) * (int64_t)(P * N) + 4 * lane;
   f4 hv[HR][2];
 #pragma unroll
@@ -328,26 +336,18 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   }
   // x rows of s-tile si held by this lane: 32*si + 8*(m/4) + 4*kk + m%4.  One
   // rolling buffer: slots 4R..4R+3 are refilled with the next s-tile's rows as
-  // soon as the MFMAs of step R have consumed them.  Padding rows read the last
-  // real row and are zeroed.
+  // soon as the MFMAs of step R have consumed them.  Padding rows read as zero.
   f2 xv[16];
   auto load_x = [&](int si, int R) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int srow = 32 * si + 8 * R + 4 * kk + e;
-      const f2 v = ld2(xh + (srow < last ? srow : last) * xs);
-      xv[4 * R + e] = srow <= last ? v : f2{0.f, 0.f};
-    }
+    for (int e = 0; e < 4; ++e) xv[4 * R + e] = bld2(xr, lane_b + (32 * si + 8 * R + e) * rowb, T{});
   };
   // z rows of the t-tile this wave emits next (its first owned tile now; the
   // second one is loaded as soon as the first has been emitted)
   f2 zv[16];
   auto load_z = [&](int ti) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int srow = 32 * ti + 8 * (m / 4) + 4 * kk + (m % 4);
-      zv[m] = ld2(zh + (srow < last ? srow : last) * xs);
-    }
+    for (int m = 0; m < 16; ++m) zv[m] = bld2(zr, lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb, T{});
   };
   __builtin_amdgcn_sched_barrier(0);  // every set-up load is issued above
 
@@ -471,7 +471,6 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   // + D_h, so the epilogue needs no x.  The four masked values of step R+1 are
   // computed while the MFMAs of step R run.
   const float Dh = Dv ? Dv[h] : 0.0f;
-  const bool full = last == Q - 1;  // uniform: no padding rows in this chunk
 #pragma unroll
   for (int si = 0; si < NT; ++si) {
     if (si > smax) break;  // uniform per wave
@@ -542,7 +541,6 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     for (int j = 0; j < NS; ++j) {
       if (own(j) != si) continue;  // uniform
       auto emit = [&](int r) {
-        const int trow = 32 * si + 8 * (r / 4) + 4 * kk + (r % 4);
         f2 y;
         y[0] = acc[j][0][r];
         y[1] = acc[j][1][r];
@@ -550,16 +548,11 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
           y[0] *= silu(zv[r][0]);
           y[1] *= silu(zv[r][1]);
         }
-        st2(oh + trow * xs, y);
+        // rows past `last` fall outside the buffer and are dropped
+        bst2(orr, lane_b + (32 * si + 8 * (r / 4) + r % 4) * rowb, y, T{});
       };
-      if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) emit(r);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * si + 8 * (r / 4) + 4 * kk + (r % 4) <= last) emit(r);
-      }
+      for (int r = 0; r < 16; ++r) emit(r);
       if constexpr (GATE) {
         if (j + 1 < NS) load_z(own(j + 1));
       }

@@ -68,6 +68,36 @@ __device__ __forceinline__ void st4(bf16_t* p, f4 v) {
   *reinterpret_cast<uint2*>(p) = w;
 }
 
+// ---- buffer-addressed rows ------------------------------------------------------
+// A raw buffer resource over [base, base + bytes): loads at byte offsets past
+// the end return 0 and stores there are dropped by the hardware's range check
+// (the whole access lies either inside or outside in the uses here).  The
+// offset is a 32-bit per-lane value, so a row walk costs one add instead of
+// 64-bit address arithmetic, and rows past a sequence's end need no clamp,
+// select or branch.  base and bytes must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// two consecutive elements at byte offset off, as fp32
+__device__ __forceinline__ f2 bld2(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
+  return __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ f2 bld2(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16_t) {
+  const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  f2 v;
+  v[0] = bf16_lo(w);
+  v[1] = bf16_hi(w);
+  return v;
+}
+__device__ __forceinline__ void bst2(__amdgpu_buffer_rsrc_t r, uint32_t off, f2 v, float) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v),
+                                        r, off, 0, 0);
+}
+__device__ __forceinline__ void bst2(__amdgpu_buffer_rsrc_t r, uint32_t off, f2 v, bf16_t) {
+  __builtin_amdgcn_raw_buffer_store_b32(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16), r,
+                                        off, 0, 0);
+}
+
 // ---- matrix core ------------------------------------------------------------
 // v_mfma_f32_16x16x4_f32: D[16x16] += A[16x4] * B[4x16].  Lane l supplies
 // A[l%16][l/16] and B[l/16][l%16]; D element (row 4*(l/16)+r, col l%16) is

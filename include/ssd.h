@@ -62,7 +62,9 @@ extern "C" {
                                     initial_states */
 #define SSD_ERR_UNSUPPORTED (-2) /* a (headdim, dstate, chunk_size) combination not compiled:
                                     headdim must be 64, dstate one of 16/32/64/128, chunk_size
-                                    one of 64/128/256 */
+                                    one of 64/128/256; or sizes past the kernels' limits
+                                    (nheads*headdim or ngroups*dstate above 2^22, batch, nheads
+                                    or chunks above 65535) */
 #define SSD_ERR_ALIGNMENT (-3)   /* x, z, out, B, C, states not 16-byte aligned; dt, A, D,
                                     dt_bias not aligned to their element; workspace not
                                     256-byte aligned */

@@ -49,6 +49,8 @@ struct Layout {
   size_t total = 0;
 };
 
+constexpr int64_t kMaxRowElems = ((int64_t)1 << 32) / (256 * 4);
+
 // Process-wide options (ssd_set_option).
 int g_bf16_path = SSD_BF16_PATH_AUTO;
 
@@ -97,6 +99,11 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
   int64_t units;
   if (!mul_ok(batch, nc, &t1) || !mul_ok(t1, nheads, &units)) return SSD_ERR_INVALID_ARG;
   if (units > INT32_MAX || nc > 65535 || batch > 65535 || nheads > 65535)
+    return SSD_ERR_UNSUPPORTED;
+  // the kernels address a chunk's (or 256-step block's) rows of x, z, out and
+  // of B, C with 32-bit byte offsets: a row may hold at most 2^32 / (256 * 4)
+  // elements
+  if (nheads * headdim > kMaxRowElems || (int64_t)ngroups * dstate > kMaxRowElems)
     return SSD_ERR_UNSUPPORTED;
   int64_t dtn, stn;
   if (!mul_ok(units, chunk_size, &dtn) || !mul_ok(units, pn, &stn)) return SSD_ERR_INVALID_ARG;

@@ -26,8 +26,6 @@
 //    consecutive n of one p -- one float4 of the tiled layout.
 //  * chunk_state_kernel (any N): four waves per (chunk, head) on
 //    v_mfma_f32_16x16x4_f32, after a separate stage-1 launch.
-#include <type_traits>
-
 #include "ssd_dt.h"
 #include "ssd_kernels.h"
 
@@ -73,7 +71,8 @@ __global__ __launch_bounds__(256) void chunk_state_wave_kernel(
   __syncthreads();
   if (!active) return;  // after the only barrier
 
-  const int64_t g = h / (H / G);
+  // 32-bit and wave-uniform (the B buffer resource needs a scalar base)
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G));
   const int i = lane % 32, kk = lane / 32;
   const int64_t t0 = c * Q;
   const float* wrow = w_lds[slot][kk];  // w of timesteps 2m + kk, m = 0 .. Q/2-1
@@ -82,71 +81,57 @@ __global__ __launch_bounds__(256) void chunk_state_wave_kernel(
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) acc[nt][0] = acc[nt][1] = zero16();
 
-  // Loads run PF steps ahead of the MFMAs through a ring of registers.  Each
-  // lane addresses its rows as a 32-bit element offset from the wave's base
-  // (a chunk spans fewer than 2^32 elements of x and of B: rows < 256 of
-  // H*P <= 2^22 and G*N <= 2^23 elements).  A chunk that ends early takes a
-  // second copy of the loop in which rows past the end are clamped to the
-  // last row (always readable) and their operands replaced by zeros; full
-  // chunks (all but a ragged last one) skip the clamps and selects.
+  // Loads run PF steps ahead of the MFMAs through a ring of registers.  x and
+  // B rows of the chunk are read through buffer resources that end after the
+  // chunk's last row: rows past it (a ragged last chunk, and the refills past
+  // the chunk's end) read as zero, which is their exact contribution (their
+  // w is 0 too), so the loop has no clamp, select or branch.  Offsets are
+  // 32-bit (a chunk spans < 2^32 bytes of x and of B).
   constexpr int PF = 8, KS = Q / 2;
   static_assert(KS % PF == 0, "ring");
   const int last = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
-  const T* xw = x + ((b * L + t0) * H + h) * P;
-  const T* bw = Bm + ((b * L + t0) * G + g) * N + 32 * NTW * half;
-  const uint32_t xs = (uint32_t)(H * P), bs = (uint32_t)(G * N);
-  auto main_loop = [&](auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    auto row = [&](int m) -> uint32_t {
-      const int t = 2 * m + kk;
-      return (uint32_t)(FULL || t < last ? t : last);
-    };
-    f2 xr[PF];
-    float br[PF][NTW];
+  const int64_t xs = H * P, bs = G * N;
+  const auto xr = row_rsrc(x + ((b * L + t0) * H + h) * P, (uint32_t)((last * xs + P) * sizeof(T)));
+  const auto br_ = row_rsrc(Bm + ((b * L + t0) * G + g) * N,
+                            (uint32_t)((last * bs + N) * sizeof(T)));
+  const uint32_t xrow = (uint32_t)(xs * sizeof(T)), brow = (uint32_t)(bs * sizeof(T));
+  // step m reads row t = 2m + kk: x at column 2i, B at columns 32 (NTW half + nt) + i
+  const uint32_t xl = kk * xrow + 2 * i * sizeof(T);
+  const uint32_t bl = kk * brow + (32 * NTW * half + i) * sizeof(T);
+  f2 xr_[PF];
+  float bq[PF][NTW];
+#pragma unroll
+  for (int d = 0; d < PF; ++d) {
+    xr_[d] = bld2(xr, xl + 2 * d * xrow, T{});
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) bq[d][nt] = bld1(br_, bl + 2 * d * brow + 32 * nt * sizeof(T), T{});
+  }
+  for (int m0 = 0; m0 < KS; m0 += PF) {
+    f4 wv[PF / 4];
+#pragma unroll
+    for (int k = 0; k < PF / 4; ++k) wv[k] = *reinterpret_cast<const f4*>(wrow + m0 + 4 * k);
+    const uint32_t xn = xl + 2 * (m0 + PF) * xrow, bn = bl + 2 * (m0 + PF) * brow;
 #pragma unroll
     for (int d = 0; d < PF; ++d) {
-      const uint32_t t = row(d);
-      xr[d] = ld2(xw + (t * xs + 2 * i));
+      const float w = wv[d / 4][d % 4];
+      const float x0 = xr_[d][0] * w, x1 = xr_[d][1] * w;
+      float bv[NTW];
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bw + (t * bs + 32 * nt + i));
-    }
-    for (int m0 = 0; m0 < KS; m0 += PF) {
-      f4 wv[PF / 4];
+      for (int nt = 0; nt < NTW; ++nt) bv[nt] = bq[d][nt];
+      // refill the slot for step m0 + d + PF (past the chunk: zeros, unused)
+      xr_[d] = bld2(xr, xn + 2 * d * xrow, T{});
 #pragma unroll
-      for (int k = 0; k < PF / 4; ++k) wv[k] = *reinterpret_cast<const f4*>(wrow + m0 + 4 * k);
+      for (int nt = 0; nt < NTW; ++nt) bq[d][nt] = bld1(br_, bn + 2 * d * brow + 32 * nt * sizeof(T), T{});
 #pragma unroll
-      for (int d = 0; d < PF; ++d) {
-        const int m = m0 + d;
-        // rows past the end contribute exactly zero (selects, not branches)
-        const bool ok = FULL || 2 * m + kk <= last;
-        const float w = wv[d / 4][d % 4];
-        const float x0 = ok ? xr[d][0] * w : 0.0f, x1 = ok ? xr[d][1] * w : 0.0f;
-        float bv[NTW];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) bv[nt] = ok ? br[d][nt] : 0.0f;
-        {  // refill the slot for step m + PF; past the chunk end it re-reads a
-           // valid row (unused), so the loads are issued unconditionally and
-           // the compiler's count of loads in flight stays exact across steps
-          const uint32_t t = row(m + PF < KS ? m + PF : KS - 1);
-          xr[d] = ld2(xw + (t * xs + 2 * i));
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) br[d][nt] = ld1(bw + (t * bs + 32 * nt + i));
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          acc[nt][0] = mfma32x32x2(bv[nt], x0, acc[nt][0]);
-          acc[nt][1] = mfma32x32x2(bv[nt], x1, acc[nt][1]);
-        }
-        // keep each step's loads and MFMAs in program order: the scheduler
-        // would otherwise sink the refills next to their uses
-        __builtin_amdgcn_sched_barrier(0);
+      for (int nt = 0; nt < NTW; ++nt) {
+        acc[nt][0] = mfma32x32x2(bv[nt], x0, acc[nt][0]);
+        acc[nt][1] = mfma32x32x2(bv[nt], x1, acc[nt][1]);
       }
+      // keep each step's loads and MFMAs in program order: the scheduler
+      // would otherwise sink the refills next to their uses
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  if (last == Q - 1)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
+  }
 
   // register 4R+e of tile (nt, pt): n = 32*(NTW*half + nt) + 8*R + 4*kk + e, p = 2*i + pt
   float* dst = states + ((b * nc + c) * H + h) * (int64_t)(P * N);

@@ -78,6 +78,13 @@ __device__ __forceinline__ void st4(bf16_t* p, f4 v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
+// one element at byte offset off, as fp32
+__device__ __forceinline__ float bld1(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float bld1(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16_t) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
+}
 // two consecutive elements at byte offset off, as fp32
 __device__ __forceinline__ f2 bld2(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
   return __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));

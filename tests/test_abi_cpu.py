@@ -256,6 +256,8 @@ CASES = [
     ("chunk 32", dict(chunk_size=32), UNSUPPORTED),
     ("chunk 100", dict(chunk_size=100), UNSUPPORTED),
     ("too many chunks", dict(seqlen=64 * 65536), UNSUPPORTED),
+    # rows of B/C wider than 2^22 elements (32-bit byte offsets over 256 steps)
+    ("B row too wide", dict(nheads=65535, ngroups=65535, dstate=128), UNSUPPORTED),
     ("x misaligned", dict(x=0x10000004), ALIGN),
     ("out misaligned", dict(out=0xA0000008), ALIGN),
     ("B misaligned", dict(B=0x40000002), ALIGN),

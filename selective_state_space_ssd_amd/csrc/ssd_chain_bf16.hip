@@ -101,10 +101,10 @@ __device__ __forceinline__ s16x4 tr_rows(const bf16_t* t, int ld, int r0, int c0
   return tr4(t + (r0 + (m >> 2)) * ld + c0 + 4 * (m & 3));
 }
 
-// 16 bytes at a wave-uniform base plus a per-lane 32-bit byte offset (the
-// scalar-base addressing form: one VGPR per address instead of two).
-__device__ __forceinline__ uint4 ldg16(const void* base, uint32_t off) {
-  return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + off);
+// 16 bytes at a per-lane 32-bit byte offset into a buffer resource (zero past
+// its end, ssd_device.h).
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 __device__ __forceinline__ float fexp2(float v) { return __builtin_amdgcn_exp2f(v); }
@@ -192,25 +192,29 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
   // ---- prefetch registers: the next block's B, C and x tiles ----
   uint4 pb[PB], pc[PB], px[PX];
   bf16_t pdt[2] = {0, 0};
+  // Rows of a block go through buffer resources that end after the block's
+  // last row: rows past the sequence end read as zero (and the epilogue's
+  // stores there are dropped), with no clamp, mask or branch.
   auto prefetch = [&](int64_t c) {
     const int64_t t0 = c * CQ;
-    const int last = (int)((L - 1 - t0) < (CQ - 1) ? (L - 1 - t0) : (CQ - 1));
-    const bf16_t* bsrc = Bm + ((b * L + t0) * G + grp) * N;
-    const bf16_t* csrc = Cm + ((b * L + t0) * G + grp) * N;
+    const uint32_t last = (uint32_t)((L - 1 - t0) < (CQ - 1) ? (L - 1 - t0) : (CQ - 1));
+    const uint32_t nb = last * brow + N * 2;
+    const auto brs = row_rsrc(Bm + ((b * L + t0) * G + grp) * N, nb);
+    const auto crs = row_rsrc(Cm + ((b * L + t0) * G + grp) * N, nb);
 #pragma unroll
     for (int k = 0; k < PB; ++k) {
       const int e = k * kChainThreads + tid;
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
-      const uint32_t o = (uint32_t)(row < last ? row : last) * brow + (uint32_t)col * 2;
-      pb[k] = ldg16(bsrc, o);
-      pc[k] = ldg16(csrc, o);
+      const uint32_t o = (uint32_t)row * brow + (uint32_t)col * 2;
+      pb[k] = bld16(brs, o);
+      pc[k] = bld16(crs, o);
     }
-    const bf16_t* xsrc = x + ((b * L + t0) * H + h) * kP;
+    const auto xrs = row_rsrc(x + ((b * L + t0) * H + h) * kP, last * xrow + kP * 2);
 #pragma unroll
     for (int k = 0; k < PX; ++k) {
       const int e = k * 256 + th;
       const int row = e / 8, col = (e % 8) * 8;
-      px[k] = ldg16(xsrc, (uint32_t)(row < last ? row : last) * xrow + (uint32_t)col * 2);
+      px[k] = bld16(xrs, (uint32_t)row * xrow + (uint32_t)col * 2);
     }
   };
   // dt_raw of block c (lane l: steps 2l, 2l+1), loaded where it is used: held
@@ -328,23 +332,19 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const int64_t t0 = c * CQ;
     const int last = (int)((L - 1 - t0) < (CQ - 1) ? (L - 1 - t0) : (CQ - 1));
 
-    // ---- stage: tiles into LDS (rows past the end zeroed) ----
-    // (a bit mask rather than a select between tiles: selecting between the
-    // prefetch registers and a zero constant would put them in memory)
-    auto masked = [](uint4 v, uint32_t mk) { return uint4{v.x & mk, v.y & mk, v.z & mk, v.w & mk}; };
+    // ---- stage: tiles into LDS (rows past the end arrived as zeros) ----
 #pragma unroll
     for (int k = 0; k < PB; ++k) {
       const int e = k * kChainThreads + tid;
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
-      const uint32_t mk = row > last ? 0u : 0xffffffffu;
-      *reinterpret_cast<uint4*>(Bl + row * BP + col) = masked(pb[k], mk);
-      *reinterpret_cast<uint4*>(Cl + row * CP + col) = masked(pc[k], mk);
+      *reinterpret_cast<uint4*>(Bl + row * BP + col) = pb[k];
+      *reinterpret_cast<uint4*>(Cl + row * CP + col) = pc[k];
     }
 #pragma unroll
     for (int k = 0; k < PX; ++k) {
       const int e = k * 256 + th;
       const int row = e / 8, col = (e % 8) * 8;
-      *reinterpret_cast<uint4*>(Xl + row * kXP + col) = masked(px[k], row > last ? 0u : 0xffffffffu);
+      *reinterpret_cast<uint4*>(Xl + row * kXP + col) = px[k];
     }
     __syncthreads();
 
@@ -509,14 +509,16 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     // the wait for a spilled value waits for every load issued before it); the
     // barrier and the table work cover their latency.
     if (c + 1 < nblk) load_dt(c + 1);
+    // x, z and out rows of this head in the block: the same range
+    const uint32_t nxb = (uint32_t)last * xrow + kP * 2;
     uint4 zr[PX];
     if constexpr (GATE) {
-      const bf16_t* zsrc = z + ((b * L + t0) * H + h) * kP;
+      const auto zrs = row_rsrc(z + ((b * L + t0) * H + h) * kP, nxb);
 #pragma unroll
       for (int k = 0; k < PX; ++k) {
         const int e = k * 256 + th;
         const int row = e / 8, col = (e % 8) * 8;
-        zr[k] = ldg16(zsrc, (uint32_t)(row < last ? row : last) * xrow + (uint32_t)col * 2);
+        zr[k] = bld16(zrs, (uint32_t)row * xrow + (uint32_t)col * 2);
       }
     }
 
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     if (c + 1 < nblk) tables(c + 1);
 
     // ---- epilogue: 8 consecutive p of one step per thread piece ----
-    bf16_t* obase = out + ((b * L + t0) * H + h) * kP;
+    const auto ors = row_rsrc(out + ((b * L + t0) * H + h) * kP, nxb);
 #pragma unroll
     for (int k = 0; k < PX; ++k) {
       const int e = k * 256 + th;
@@ -555,12 +557,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
           yv[2 * q + 1] *= fsilu(bf16_hi(zw[q]));
         }
       }
-      if (row <= last) {
-        const uint4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
-                         pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])};
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(obase) + (uint32_t)row * xrow +
-                                  (uint32_t)col * 2) = o;
-      }
+      // rows past the end fall outside the resource and are dropped
+      const uint4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
+                       pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, o),
+                                             ors, (uint32_t)row * xrow + (uint32_t)col * 2, 0, 0);
     }
     __syncthreads();  // the output tiles are read before the next staging
   }

@@ -56,23 +56,12 @@ __global__ __launch_bounds__(256) void chunk_state_wave_kernel(
   const int64_t h = hq * HPW + slot;
   const bool active = h < H;
 
-  if (active && half == 0) {
-    float dtv[E], cum[E], cum_last;
-    wave_dt_cumsum<T, Q>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c, h, L,
-                         H, nc, ws_dt, ws_cum, dtv, cum, &cum_last);
-    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
-#pragma unroll
-    for (int k = 0; k < E; ++k) {
-      const int t = lane * E + k;
-      const bool keep = !sc || sc[t] == sc[Q - 1];
-      w_lds[slot][t & 1][t >> 1] = keep ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
-    }
-  }
-  __syncthreads();
-  if (!active) return;  // after the only barrier
-
+  // The ring's first loads are issued before the dt phase and its barrier,
+  // whose latency they overlap.  A wave past the last head (H odd) reads
+  // head H-1's rows and returns after the barrier.
+  const int64_t ha = active ? h : H - 1;
   // 32-bit and wave-uniform (the B buffer resource needs a scalar base)
-  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G));
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)ha / (int)(H / G));
   const int i = lane % 32, kk = lane / 32;
   const int64_t t0 = c * Q;
   const float* wrow = w_lds[slot][kk];  // w of timesteps 2m + kk, m = 0 .. Q/2-1
@@ -91,7 +80,7 @@ __global__ __launch_bounds__(256) void chunk_state_wave_kernel(
   static_assert(KS % PF == 0, "ring");
   const int last = (int)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
   const int64_t xs = H * P, bs = G * N;
-  const auto xr = row_rsrc(x + ((b * L + t0) * H + h) * P, (uint32_t)((last * xs + P) * sizeof(T)));
+  const auto xr = row_rsrc(x + ((b * L + t0) * H + ha) * P, (uint32_t)((last * xs + P) * sizeof(T)));
   const auto br_ = row_rsrc(Bm + ((b * L + t0) * G + g) * N,
                             (uint32_t)((last * bs + N) * sizeof(T)));
   const uint32_t xrow = (uint32_t)(xs * sizeof(T)), brow = (uint32_t)(bs * sizeof(T));
@@ -106,6 +95,21 @@ __global__ __launch_bounds__(256) void chunk_state_wave_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) bq[d][nt] = bld1(br_, bl + 2 * d * brow + 32 * nt * sizeof(T), T{});
   }
+  if (active && half == 0) {
+    float dtv[E], cum[E], cum_last;
+    wave_dt_cumsum<T, Q>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c, h, L,
+                         H, nc, ws_dt, ws_cum, dtv, cum, &cum_last);
+    const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const int t = lane * E + k;
+      const bool keep = !sc || sc[t] == sc[Q - 1];
+      w_lds[slot][t & 1][t >> 1] = keep ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (!active) return;  // after the only barrier
+
   for (int m0 = 0; m0 < KS; m0 += PF) {
     f4 wv[PF / 4];
 #pragma unroll

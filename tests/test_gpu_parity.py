@@ -44,6 +44,9 @@ SMALL += [("f32", 128, 32, 4, 2), ("f32", 128, 64, 4, 2), ("bf16", 64, 32, 4, 2)
 SMALL += [(dt, Q, N, 8, G) for dt in ("f32", "bf16") for Q in (64, 128) for N in (64, 128)
           for G in (1, 2)]
 SMALL += [("f32", 128, 128, 6, 3), ("f32", 64, 64, 12, 3), ("bf16", 128, 128, 16, 1)]
+# an odd number of heads leaves the last chunk-state workgroup (two heads) with
+# one idle head
+SMALL += [("f32", 128, 128, 5, 1), ("bf16", 64, 64, 3, 1)]
 # batch * ngroups a multiple of 8: the fused bf16 kernel deals its chains to
 # eight ticket classes (one group per class here)
 SMALL += [("bf16", 256, 128, 8, 4), ("bf16", 128, 64, 8, 8)]

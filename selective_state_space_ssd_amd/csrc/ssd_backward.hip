@@ -204,7 +204,8 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 
   const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
   const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
-  const int64_t g = h / (H / G), t0 = blk * T;
+  // 32-bit and wave-uniform: the B and C buffer resources need a scalar base
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G)), t0 = blk * T;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int i = lane % 16, kk = lane / 16;
   const int64_t PN = (int64_t)P * N;
@@ -212,44 +213,54 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   const float* gc = gst + u * PN;         // row-major [P][N]
   const int last = (int)((L - 1 - t0) < (T - 1) ? (L - 1 - t0) : (T - 1));
 
+  // Rows of this block (head h, or its group for B and C) through buffer
+  // resources that end after row `last`: rows past it read as zero and the
+  // gradient stores there are dropped, with 32-bit offsets and no clamps,
+  // selects or branches.
+  const uint32_t xrow = (uint32_t)(H * P * 4), brow = (uint32_t)(G * N * 4);
+  const uint32_t hrow = (uint32_t)(H * N * 4);  // per-head dB / dC parts
+  const int64_t xo = ((b * L + t0) * H + h) * P, bo = ((b * L + t0) * G + g) * N;
+  const int64_t ho = ((b * L + t0) * H + h) * N;
+  const uint32_t xbytes = (uint32_t)last * xrow + P * 4, bbytes = (uint32_t)last * brow + N * 4;
+  const uint32_t hbytes = (uint32_t)last * hrow + N * 4;
+
   // ---- stage x, dY, B, C, G, cum, dt (rows past the end are zero) -----------
-  // rows are read from the last real row (always in bounds) and zeroed after
   {
+    const auto xr = row_rsrc(x + xo, xbytes), yr = row_rsrc(dy + xo, xbytes);
+    const auto br = row_rsrc(Bm + bo, bbytes), cr = row_rsrc(Cm + bo, bbytes);
     f4 xv[T * P / 1024], yv[T * P / 1024], bv[T * N / 1024], cv[T * N / 1024], gv[P * N / 1024];
 #pragma unroll
     for (int q = 0; q < T * P / 1024; ++q) {
       const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
-      const int64_t o = ((b * L + t0 + (t < last ? t : last)) * H + h) * P + p;
-      xv[q] = ld4(x + o);
-      yv[q] = ld4(dy + o);
+      const uint32_t o = (uint32_t)t * xrow + (uint32_t)p * 4;
+      xv[q] = bld4(xr, o);
+      yv[q] = bld4(yr, o);
     }
 #pragma unroll
     for (int q = 0; q < T * N / 1024; ++q) {
       const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
-      const int64_t o = ((b * L + t0 + (t < last ? t : last)) * G + g) * N + n;
-      bv[q] = ld4(Bm + o);
-      cv[q] = ld4(Cm + o);
+      const uint32_t o = (uint32_t)t * brow + (uint32_t)n * 4;
+      bv[q] = bld4(br, o);
+      cv[q] = bld4(cr, o);
     }
 #pragma unroll
     for (int q = 0; q < P * N / 1024; ++q) gv[q] = ld4(gc + 4 * (q * 256 + tid));
 #pragma unroll
     for (int q = 0; q < T * P / 1024; ++q) {
       const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
-      const bool ok = t <= last;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        xs_[t * kXP + p + c] = ok ? xv[q][c] : 0.0f;
-        ys_[t * kXP + p + c] = ok ? yv[q][c] : 0.0f;
+        xs_[t * kXP + p + c] = xv[q][c];
+        ys_[t * kXP + p + c] = yv[q][c];
       }
     }
 #pragma unroll
     for (int q = 0; q < T * N / 1024; ++q) {
       const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
-      const bool ok = t <= last;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        bs_[t * NS + n + c] = ok ? bv[q][c] : 0.0f;
-        cs_[t * NS + n + c] = ok ? cv[q][c] : 0.0f;
+        bs_[t * NS + n + c] = bv[q][c];
+        cs_[t * NS + n + c] = cv[q][c];
       }
     }
 #pragma unroll
@@ -348,6 +359,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 
   // ---- dX = D dY + V^T dY + diag(w) GB;  dB = diag(dt) W^T C + diag(w) XG ----
   {
+    const auto dxr = row_rsrc(dx + xo, xbytes), dbr = row_rsrc(dBh + ho, hbytes);
     f4 vall[4];
     tiles16<4, T>([&](int r, int k) { return vm[k * 64 + 16 * wave + r]; },
                   [&](int j, int k, int c) { return ys_[k * kXP + 16 * j + c]; }, vall);
@@ -357,8 +369,8 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * wave + 4 * kk + r;
-        if (s <= last)
-          dx[((b * L + t0 + s) * H + h) * P + p] = Dh * ys_[s * kXP + p] + vall[j][r] + wdt[s] * gball[j][r];
+        bst1(dxr, (uint32_t)s * xrow + (uint32_t)p * 4,
+             Dh * ys_[s * kXP + p] + vall[j][r] + wdt[s] * gball[j][r]);
       }
     }
     f4 a1[NJ];
@@ -370,7 +382,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * wave + 4 * kk + r;
-        if (s <= last) dBh[((b * L + t0 + s) * H + h) * N + n] = dt_l[s] * a1[j][r] + wdt[s] * xgall[j][r];
+        bst1(dbr, (uint32_t)s * hrow + (uint32_t)n * 4, dt_l[s] * a1[j][r] + wdt[s] * xgall[j][r]);
       }
     }
   }
@@ -406,6 +418,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   // ---- dC = diag(exp(cum)) dY H_in + W diag(dt) B; dY_t . (H_in C_t) ----------
   float ysum[4] = {0.f, 0.f, 0.f, 0.f};
   {
+    const auto dcr = row_rsrc(dCh + ho, hbytes);
     f4 a1[NJ], a2[NJ];
     tiles16<NJ, P>([&](int r, int k) { return ys_[(16 * wave + r) * kXP + k]; },
                    [&](int j, int k, int c) { return hs_[k * NS + 16 * j + c]; }, a1);
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * wave + 4 * kk + r;
         const float e = ecum[t] * a1[j][r];
-        if (t <= last) dCh[((b * L + t0 + t) * H + h) * N + n] = e + a2[j][r];
+        bst1(dcr, (uint32_t)t * hrow + (uint32_t)n * 4, e + a2[j][r]);
         ysum[r] += e * cs_[t * NS + n];
       }
     }

@@ -85,6 +85,14 @@ __device__ __forceinline__ float bld1(__amdgpu_buffer_rsrc_t r, uint32_t off, fl
 __device__ __forceinline__ float bld1(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16_t) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
 }
+// four consecutive fp32 elements at byte offset off
+__device__ __forceinline__ f4 bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// one fp32 element stored at byte offset off
+__device__ __forceinline__ void bst1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
 // two consecutive elements at byte offset off, as fp32
 __device__ __forceinline__ f2 bld2(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
   return __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));

@@ -40,6 +40,7 @@ namespace ssd {
 namespace {
 constexpr int kBT = 64;   // block length of the backward
 constexpr int kXP = 65;   // padded row stride of 64-wide LDS tiles
+constexpr int kBwdThreads = 512;  // block backward kernel: eight waves
 
 // One 16 x 16 output tile of a wave on v_mfma_f32_16x16x4_f32: lane l
 // supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane l holds
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256) void bwd_state_passing_kernel(
 // LDS, kept in registers; K and R, then V and W in place of G; dX and dB;
 // H_in over x and V, then dC and dY_t . (H_in C_t); the decay gradients.
 template <int N>
-__global__ __launch_bounds__(256) void block_bwd_kernel(
+__global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
     const float* __restrict__ dt_raw, const float* __restrict__ dt_bias, float dt_min,
     float dt_max, const float* __restrict__ A, const float* __restrict__ Dv,
@@ -185,6 +186,12 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     float* __restrict__ dCh, float* __restrict__ ddt_raw, float* __restrict__ dA_p,
     float* __restrict__ dD_p, int64_t L, int64_t H, int64_t G, int64_t nb) {
   constexpr int P = 64, T = kBT, NJ = N / 16, NS = N + 1;
+  // Eight waves: wave w takes the 16-row strip w % 4 of every product and
+  // half w / 4 of its column tiles (two waves per SIMD hide each other's
+  // LDS and memory latency; with four waves, one per SIMD, they did not).
+  // A product with a single column tile (N = 16) is done by the first half.
+  constexpr int NW = kBwdThreads / kWave, NTH = kBwdThreads;
+  constexpr int NJW = NJ >= 2 ? NJ / 2 : 1;  // column tiles of N per wave
   constexpr int OX = 0, OV = 4160, OW = 8256, OY = 12416, OB = 16576, OC = OB + T * NS;
   static_assert(T * kXP == 4160 && OV + T * 64 == OW && OW + T * kXP == OY &&
                 OY + T * kXP == OB && T * NS <= OV + T * 64 && T * NS <= OY - OV, "LDS map");
@@ -199,14 +206,16 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   float* const hs_ = lds + OX;   // H_in[p][n]   stride N+1 (dC phase)
   __shared__ float cum_l[T], dt_l[T];
   __shared__ float ecum[T], wdt[T];  // exp(cum_t); w_t = exp(cl - cum_t) dt_t
-  __shared__ float rowv[T], xgb[T], yod[T], red[8];
-  __shared__ float colw[4][T], col0w[4][T];  // per-wave column sums, added in order
+  // per-half row sums and per-strip column sums, added in a fixed order
+  __shared__ float rowv[2][T], xgb[2][T], yod[2][T], red[2 * NW];
+  __shared__ float colw[4][T], col0w[4][T];
 
   const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
   const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
   // 32-bit and wave-uniform: the B and C buffer resources need a scalar base
   const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G)), t0 = blk * T;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int strip = wave & 3, colh = wave >> 2;  // row strip, column half
   const int i = lane % 16, kk = lane / 16;
   const int64_t PN = (int64_t)P * N;
   const float* hin = states_in + u * PN;  // tiled layout
@@ -228,26 +237,32 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   {
     const auto xr = row_rsrc(x + xo, xbytes), yr = row_rsrc(dy + xo, xbytes);
     const auto br = row_rsrc(Bm + bo, bbytes), cr = row_rsrc(Cm + bo, bbytes);
-    f4 xv[T * P / 1024], yv[T * P / 1024], bv[T * N / 1024], cv[T * N / 1024], gv[P * N / 1024];
+    // float4 per thread (the last may be partial for N = 16: guarded)
+    constexpr int QX = T * P / (4 * NTH), QB = (T * N / 4 + NTH - 1) / NTH, QG = QB;
+    static_assert(T * P % (4 * NTH) == 0 && T == P, "staging");
+    f4 xv[QX], yv[QX], bv[QB], cv[QB], gv[QG];
 #pragma unroll
-    for (int q = 0; q < T * P / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
+    for (int q = 0; q < QX; ++q) {
+      const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
       const uint32_t o = (uint32_t)t * xrow + (uint32_t)p * 4;
       xv[q] = bld4(xr, o);
       yv[q] = bld4(yr, o);
     }
 #pragma unroll
-    for (int q = 0; q < T * N / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
+    for (int q = 0; q < QB; ++q) {
+      const int e = 4 * (q * NTH + tid), t = e / N, n = e % N;
       const uint32_t o = (uint32_t)t * brow + (uint32_t)n * 4;
-      bv[q] = bld4(br, o);
-      cv[q] = bld4(cr, o);
+      if (e < T * N) {
+        bv[q] = bld4(br, o);
+        cv[q] = bld4(cr, o);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < P * N / 1024; ++q) gv[q] = ld4(gc + 4 * (q * 256 + tid));
+    for (int q = 0; q < QG; ++q)
+      if (4 * (q * NTH + tid) < P * N) gv[q] = ld4(gc + 4 * (q * NTH + tid));
 #pragma unroll
-    for (int q = 0; q < T * P / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
+    for (int q = 0; q < QX; ++q) {
+      const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         xs_[t * kXP + p + c] = xv[q][c];
@@ -255,19 +270,23 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
       }
     }
 #pragma unroll
-    for (int q = 0; q < T * N / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
+    for (int q = 0; q < QB; ++q) {
+      const int e = 4 * (q * NTH + tid), t = e / N, n = e % N;
+      if (e < T * N) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bs_[t * NS + n + c] = bv[q][c];
-        cs_[t * NS + n + c] = cv[q][c];
+        for (int c = 0; c < 4; ++c) {
+          bs_[t * NS + n + c] = bv[q][c];
+          cs_[t * NS + n + c] = cv[q][c];
+        }
       }
     }
 #pragma unroll
-    for (int q = 0; q < P * N / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), p = e / N, n = e % N;
+    for (int q = 0; q < QG; ++q) {
+      const int e = 4 * (q * NTH + tid), p = e / N, n = e % N;
+      if (e < P * N) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) gs_[p * NS + n + c] = gv[q][c];
+        for (int c = 0; c < 4; ++c) gs_[p * NS + n + c] = gv[q][c];
+      }
     }
   }
   if (tid < T) {
@@ -296,44 +315,51 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     return v + __shfl_xor(v, 32, kWave);
   };
 
+  // Column tiles of this wave: 64-wide products (over p or s) tiles
+  // 2 colh, 2 colh + 1; N-wide ones NJW tiles from jn (none when N = 16 and
+  // colh = 1).
+  const int j4 = 2 * colh, jn = colh * NJW;
+  const bool hasn = jn < NJ;  // wave-uniform
+
   // ---- products with G: GB[s][p] = B_s . G_p (dX), XG[s][n] = x_s^T G (dB) --
-  // wave w: rows s in [16w, 16w+16)
-  f4 gball[4], xgall[NJ];
-  tiles16<4, N>([&](int r, int k) { return bs_[(16 * wave + r) * NS + k]; },
-                [&](int j, int k, int c) { return gs_[(16 * j + c) * NS + k]; }, gball);
-  tiles16<NJ, P>([&](int r, int k) { return xs_[(16 * wave + r) * kXP + k]; },
-                 [&](int j, int k, int c) { return gs_[k * NS + 16 * j + c]; }, xgall);
+  // rows s in [16 strip, 16 strip + 16)
+  f4 gball[2], xgall[NJW];
+  tiles16<2, N>([&](int r, int k) { return bs_[(16 * strip + r) * NS + k]; },
+                [&](int j, int k, int c) { return gs_[(16 * (j4 + j) + c) * NS + k]; }, gball);
+  if (hasn)
+    tiles16<NJW, P>([&](int r, int k) { return xs_[(16 * strip + r) * kXP + k]; },
+                    [&](int j, int k, int c) { return gs_[k * NS + 16 * (jn + j) + c]; }, xgall);
   {
     float xsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        xsum[r] += xs_[(16 * wave + 4 * kk + r) * kXP + 16 * j + i] * gball[j][r];
+        xsum[r] += xs_[(16 * strip + 4 * kk + r) * kXP + 16 * (j4 + j) + i] * gball[j][r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float v = sum16(xsum[r]);
-      if (i == 0) xgb[16 * wave + 4 * kk + r] = v;
+      if (i == 0) xgb[colh][16 * strip + 4 * kk + r] = v;
     }
   }
   __syncthreads();  // G is dead: V and W take its place
 
   // ---- K = C B^T and R = dY X^T; masks, decays and the dcum sums -------------
-  // wave w: rows t in [16w, 16w+16), four column tiles of s
+  // rows t in [16 strip, 16 strip + 16), two column tiles of s
   float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-  f4 kall[4], rall[4];
-  tiles16<4, N>([&](int r, int k) { return cs_[(16 * wave + r) * NS + k]; },
-                [&](int j, int k, int c) { return bs_[(16 * j + c) * NS + k]; }, kall);
-  tiles16<4, P>([&](int r, int k) { return ys_[(16 * wave + r) * kXP + k]; },
-                [&](int j, int k, int c) { return xs_[(16 * j + c) * kXP + k]; }, rall);
+  f4 kall[2], rall[2];
+  tiles16<2, N>([&](int r, int k) { return cs_[(16 * strip + r) * NS + k]; },
+                [&](int j, int k, int c) { return bs_[(16 * (j4 + j) + c) * NS + k]; }, kall);
+  tiles16<2, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
+                [&](int j, int k, int c) { return xs_[(16 * (j4 + j) + c) * kXP + k]; }, rall);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const f4 kacc = kall[j], racc = rall[j];
-    const int s = 16 * j + i;
+    const int s = 16 * (j4 + j) + i;
     float cs = 0.0f, cs0 = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * wave + 4 * kk + r;
+      const int t = 16 * strip + 4 * kk + r;
       const float m = s <= t ? expf(cum_l[t] - cum_l[s]) : 0.0f;
       const float v0 = m * kacc[r] * racc[r];
       const float v = v0 * dt_l[s];
@@ -346,66 +372,71 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     cs = sum4g(cs);
     cs0 = sum4g(cs0);
     if (kk == 0) {
-      colw[wave][s] = cs;
-      col0w[wave][s] = cs0;
+      colw[strip][s] = cs;
+      col0w[strip][s] = cs0;
     }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float v = sum16(rsum[r]);
-    if (i == 0) rowv[16 * wave + 4 * kk + r] = v;
+    if (i == 0) rowv[colh][16 * strip + 4 * kk + r] = v;
   }
   __syncthreads();
 
   // ---- dX = D dY + V^T dY + diag(w) GB;  dB = diag(dt) W^T C + diag(w) XG ----
   {
     const auto dxr = row_rsrc(dx + xo, xbytes), dbr = row_rsrc(dBh + ho, hbytes);
-    f4 vall[4];
-    tiles16<4, T>([&](int r, int k) { return vm[k * 64 + 16 * wave + r]; },
-                  [&](int j, int k, int c) { return ys_[k * kXP + 16 * j + c]; }, vall);
+    f4 vall[2];
+    tiles16<2, T>([&](int r, int k) { return vm[k * 64 + 16 * strip + r]; },
+                  [&](int j, int k, int c) { return ys_[k * kXP + 16 * (j4 + j) + c]; }, vall);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = 16 * j + i;
+    for (int j = 0; j < 2; ++j) {
+      const int p = 16 * (j4 + j) + i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = 16 * wave + 4 * kk + r;
+        const int s = 16 * strip + 4 * kk + r;
         bst1(dxr, (uint32_t)s * xrow + (uint32_t)p * 4,
              Dh * ys_[s * kXP + p] + vall[j][r] + wdt[s] * gball[j][r]);
       }
     }
-    f4 a1[NJ];
-    tiles16<NJ, T>([&](int r, int k) { return wm[k * kXP + 16 * wave + r]; },
-                   [&](int j, int k, int c) { return cs_[k * NS + 16 * j + c]; }, a1);
+    if (hasn) {
+    f4 a1[NJW];
+    tiles16<NJW, T>([&](int r, int k) { return wm[k * kXP + 16 * strip + r]; },
+                    [&](int j, int k, int c) { return cs_[k * NS + 16 * (jn + j) + c]; }, a1);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = 16 * j + i;
+    for (int j = 0; j < NJW; ++j) {
+      const int n = 16 * (jn + j) + i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int s = 16 * wave + 4 * kk + r;
+        const int s = 16 * strip + 4 * kk + r;
         bst1(dbr, (uint32_t)s * hrow + (uint32_t)n * 4, dt_l[s] * a1[j][r] + wdt[s] * xgall[j][r]);
       }
     }
+    }
   }
   float dd = 0.0f;  // dY . x over the block
-  for (int e = tid; e < T * P; e += 256) dd += ys_[(e / P) * kXP + e % P] * xs_[(e / P) * kXP + e % P];
+  for (int e = tid; e < T * P; e += NTH) dd += ys_[(e / P) * kXP + e % P] * xs_[(e / P) * kXP + e % P];
   __syncthreads();  // x and V are dead: H_in takes their place
 
   // ---- H_in into LDS, with <G, H_in> on the way ------------------------------
   float gh = 0.0f;
   {
-    f4 hv[P * N / 1024], gv2[P * N / 1024];
+    constexpr int QH = (P * N / 4 + NTH - 1) / NTH;
+    f4 hv[QH], gv2[QH];
 #pragma unroll
-    for (int q = 0; q < P * N / 1024; ++q) {
-      const int k4 = q * 256 + tid;  // float4 index in the tiled block
+    for (int q = 0; q < QH; ++q) {
+      const int k4 = q * NTH + tid;  // float4 index in the tiled block
+      if (k4 >= P * N / 4) break;
       int p, n;
       state_tile_coords(k4, N, &p, &n);
       hv[q] = ld4(hin + 4 * k4);
       gv2[q] = ld4(gc + p * N + n);
     }
 #pragma unroll
-    for (int q = 0; q < P * N / 1024; ++q) {
+    for (int q = 0; q < QH; ++q) {
+      if (q * NTH + tid >= P * N / 4) break;
       int p, n;
-      state_tile_coords(q * 256 + tid, N, &p, &n);
+      state_tile_coords(q * NTH + tid, N, &p, &n);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         hs_[p * NS + n + c] = hv[q][c];
@@ -417,19 +448,19 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
 
   // ---- dC = diag(exp(cum)) dY H_in + W diag(dt) B; dY_t . (H_in C_t) ----------
   float ysum[4] = {0.f, 0.f, 0.f, 0.f};
-  {
+  if (hasn) {
     const auto dcr = row_rsrc(dCh + ho, hbytes);
-    f4 a1[NJ], a2[NJ];
-    tiles16<NJ, P>([&](int r, int k) { return ys_[(16 * wave + r) * kXP + k]; },
-                   [&](int j, int k, int c) { return hs_[k * NS + 16 * j + c]; }, a1);
-    tiles16<NJ, T>([&](int r, int k) { return wm[(16 * wave + r) * kXP + k] * dt_l[k]; },
-                   [&](int j, int k, int c) { return bs_[k * NS + 16 * j + c]; }, a2);
+    f4 a1[NJW], a2[NJW];
+    tiles16<NJW, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
+                    [&](int j, int k, int c) { return hs_[k * NS + 16 * (jn + j) + c]; }, a1);
+    tiles16<NJW, T>([&](int r, int k) { return wm[(16 * strip + r) * kXP + k] * dt_l[k]; },
+                    [&](int j, int k, int c) { return bs_[k * NS + 16 * (jn + j) + c]; }, a2);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = 16 * j + i;
+    for (int j = 0; j < NJW; ++j) {
+      const int n = 16 * (jn + j) + i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * wave + 4 * kk + r;
+        const int t = 16 * strip + 4 * kk + r;
         const float e = ecum[t] * a1[j][r];
         bst1(dcr, (uint32_t)t * hrow + (uint32_t)n * 4, e + a2[j][r]);
         ysum[r] += e * cs_[t * NS + n];
@@ -437,9 +468,9 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < 4; ++r) {  // zero partials from a wave without N tiles
     const float v = sum16(ysum[r]);
-    if (i == 0) yod[16 * wave + 4 * kk + r] = v;
+    if (i == 0) yod[colh][16 * strip + 4 * kk + r] = v;
   }
 
   // ---- <G, H_in> and dY . x across the workgroup ------------------------------
@@ -450,21 +481,27 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
   }
   if (lane == 0) {
     red[wave] = gh;
-    red[4 + wave] = dd;
+    red[NW + wave] = dd;
   }
   __syncthreads();
 
   // ---- dcum, its reverse running sum, ddt_raw, the dA and dD parts -----------
   if (wave == 0) {
     const int t = lane;
-    const float us = wdt[t] * xgb[t];
+    const float xg = xgb[0][t] + xgb[1][t];
+    const float us = wdt[t] * xg;
     float usum = us;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) usum += __shfl_xor(usum, off, kWave);
-    const float ghs = red[0] + red[1] + red[2] + red[3];
+    float ghs = 0.0f, dds = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      ghs += red[w];
+      dds += red[NW + w];
+    }
     const float colv = colw[0][t] + colw[1][t] + colw[2][t] + colw[3][t];
     const float col0 = col0w[0][t] + col0w[1][t] + col0w[2][t] + col0w[3][t];
-    float dc = rowv[t] + yod[t] - colv - us;
+    float dc = (rowv[0][t] + rowv[1][t]) + (yod[0][t] + yod[1][t]) - colv - us;
     if (t == T - 1) dc += usum + expf(cl) * ghs;
     // suffix sum over t
     float rc = dc;
@@ -474,7 +511,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
       if (t + off < kWave) rc += o;
     }
     const float Ah = A[h];
-    const float ddt = col0 + expf(cl - cum_l[t]) * xgb[t] + Ah * rc;
+    const float ddt = col0 + expf(cl - cum_l[t]) * xg + Ah * rc;
     float da = dt_l[t] * rc;
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) da += __shfl_xor(da, off, kWave);
@@ -487,7 +524,7 @@ __global__ __launch_bounds__(256) void block_bwd_kernel(
     }
     if (t == 0) {
       dA_p[u] = da;
-      dD_p[u] = red[4] + red[5] + red[6] + red[7];
+      dD_p[u] = dds;
     }
   }
 }
@@ -557,7 +594,7 @@ static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
   hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),
                      (unsigned)p.H, (unsigned)p.b), dim3(256), 0, s, q.pc, p.ws_cum, q.dfinal,
                      q.gst, q.dinit, p.H, p.nc, PN);
-  hipLaunchKernelGGL((block_bwd_kernel<N>), dim3((unsigned)units), dim3(256), 0, s,
+  hipLaunchKernelGGL((block_bwd_kernel<N>), dim3((unsigned)units), dim3(kBwdThreads), 0, s,
                      static_cast<const float*>(p.x), static_cast<const float*>(p.B),
                      static_cast<const float*>(p.C), static_cast<const float*>(p.dt), p.dt_bias,
                      p.dt_min, p.dt_max, p.A, p.D, p.ws_dt, p.ws_cum, p.ws_states_in, q.gst, q.dy,

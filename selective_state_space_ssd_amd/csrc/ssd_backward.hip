@@ -40,7 +40,7 @@ namespace ssd {
 namespace {
 constexpr int kBT = 64;   // block length of the backward
 constexpr int kXP = 65;   // padded row stride of 64-wide LDS tiles
-constexpr int kBwdThreads = 512;  // block backward kernel: eight waves
+constexpr int kBwdThreads = 512;  // block backward kernel: eight waves (sixteen measured the same)
 
 // One 16 x 16 output tile of a wave on v_mfma_f32_16x16x4_f32: lane l
 // supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane l holds
@@ -186,12 +186,15 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     float* __restrict__ dCh, float* __restrict__ ddt_raw, float* __restrict__ dA_p,
     float* __restrict__ dD_p, int64_t L, int64_t H, int64_t G, int64_t nb) {
   constexpr int P = 64, T = kBT, NJ = N / 16, NS = N + 1;
-  // Eight waves: wave w takes the 16-row strip w % 4 of every product and
-  // half w / 4 of its column tiles (two waves per SIMD hide each other's
-  // LDS and memory latency; with four waves, one per SIMD, they did not).
-  // A product with a single column tile (N = 16) is done by the first half.
+  // NW waves: wave w takes the 16-row strip w % 4 of every product and
+  // column group w / 4 of its column tiles (several waves per SIMD hide each
+  // other's LDS and memory latency; with four waves, one per SIMD, they did
+  // not).  N-wide products with fewer column tiles than groups are done by
+  // the first groups.
   constexpr int NW = kBwdThreads / kWave, NTH = kBwdThreads;
-  constexpr int NJW = NJ >= 2 ? NJ / 2 : 1;  // column tiles of N per wave
+  constexpr int NCG = NW / 4;                      // column groups
+  constexpr int NJ4 = 4 / NCG;                     // 64-wide column tiles per wave
+  constexpr int NJW = NJ >= NCG ? NJ / NCG : 1;    // N-wide column tiles per wave
   constexpr int OX = 0, OV = 4160, OW = 8256, OY = 12416, OB = 16576, OC = OB + T * NS;
   static_assert(T * kXP == 4160 && OV + T * 64 == OW && OW + T * kXP == OY &&
                 OY + T * kXP == OB && T * NS <= OV + T * 64 && T * NS <= OY - OV, "LDS map");
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   __shared__ float cum_l[T], dt_l[T];
   __shared__ float ecum[T], wdt[T];  // exp(cum_t); w_t = exp(cl - cum_t) dt_t
   // per-half row sums and per-strip column sums, added in a fixed order
-  __shared__ float rowv[2][T], xgb[2][T], yod[2][T], red[2 * NW];
+  __shared__ float rowv[NCG][T], xgb[NCG][T], yod[NCG][T], red[2 * NW];
   __shared__ float colw[4][T], col0w[4][T];
 
   const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // 32-bit and wave-uniform: the B and C buffer resources need a scalar base
   const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G)), t0 = blk * T;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int strip = wave & 3, colh = wave >> 2;  // row strip, column half
+  const int strip = wave & 3, colh = wave >> 2;  // row strip, column group
   const int i = lane % 16, kk = lane / 16;
   const int64_t PN = (int64_t)P * N;
   const float* hin = states_in + u * PN;  // tiled layout
@@ -318,13 +321,13 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // Column tiles of this wave: 64-wide products (over p or s) tiles
   // 2 colh, 2 colh + 1; N-wide ones NJW tiles from jn (none when N = 16 and
   // colh = 1).
-  const int j4 = 2 * colh, jn = colh * NJW;
+  const int j4 = NJ4 * colh, jn = colh * NJW;
   const bool hasn = jn < NJ;  // wave-uniform
 
   // ---- products with G: GB[s][p] = B_s . G_p (dX), XG[s][n] = x_s^T G (dB) --
   // rows s in [16 strip, 16 strip + 16)
-  f4 gball[2], xgall[NJW];
-  tiles16<2, N>([&](int r, int k) { return bs_[(16 * strip + r) * NS + k]; },
+  f4 gball[NJ4], xgall[NJW];
+  tiles16<NJ4, N>([&](int r, int k) { return bs_[(16 * strip + r) * NS + k]; },
                 [&](int j, int k, int c) { return gs_[(16 * (j4 + j) + c) * NS + k]; }, gball);
   if (hasn)
     tiles16<NJW, P>([&](int r, int k) { return xs_[(16 * strip + r) * kXP + k]; },
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   {
     float xsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         xsum[r] += xs_[(16 * strip + 4 * kk + r) * kXP + 16 * (j4 + j) + i] * gball[j][r];
@@ -347,13 +350,13 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // ---- K = C B^T and R = dY X^T; masks, decays and the dcum sums -------------
   // rows t in [16 strip, 16 strip + 16), two column tiles of s
   float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-  f4 kall[2], rall[2];
-  tiles16<2, N>([&](int r, int k) { return cs_[(16 * strip + r) * NS + k]; },
+  f4 kall[NJ4], rall[NJ4];
+  tiles16<NJ4, N>([&](int r, int k) { return cs_[(16 * strip + r) * NS + k]; },
                 [&](int j, int k, int c) { return bs_[(16 * (j4 + j) + c) * NS + k]; }, kall);
-  tiles16<2, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
-                [&](int j, int k, int c) { return xs_[(16 * (j4 + j) + c) * kXP + k]; }, rall);
+  tiles16<NJ4, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
+                  [&](int j, int k, int c) { return xs_[(16 * (j4 + j) + c) * kXP + k]; }, rall);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ4; ++j) {
     const f4 kacc = kall[j], racc = rall[j];
     const int s = 16 * (j4 + j) + i;
     float cs = 0.0f, cs0 = 0.0f;
@@ -386,11 +389,11 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // ---- dX = D dY + V^T dY + diag(w) GB;  dB = diag(dt) W^T C + diag(w) XG ----
   {
     const auto dxr = row_rsrc(dx + xo, xbytes), dbr = row_rsrc(dBh + ho, hbytes);
-    f4 vall[2];
-    tiles16<2, T>([&](int r, int k) { return vm[k * 64 + 16 * strip + r]; },
+    f4 vall[NJ4];
+    tiles16<NJ4, T>([&](int r, int k) { return vm[k * 64 + 16 * strip + r]; },
                   [&](int j, int k, int c) { return ys_[k * kXP + 16 * (j4 + j) + c]; }, vall);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ4; ++j) {
       const int p = 16 * (j4 + j) + i;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -488,7 +491,13 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // ---- dcum, its reverse running sum, ddt_raw, the dA and dD parts -----------
   if (wave == 0) {
     const int t = lane;
-    const float xg = xgb[0][t] + xgb[1][t];
+    float xg = 0.0f, rv = 0.0f, yo = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NCG; ++q) {
+      xg += xgb[q][t];
+      rv += rowv[q][t];
+      yo += yod[q][t];
+    }
     const float us = wdt[t] * xg;
     float usum = us;
 #pragma unroll
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     }
     const float colv = colw[0][t] + colw[1][t] + colw[2][t] + colw[3][t];
     const float col0 = col0w[0][t] + col0w[1][t] + col0w[2][t] + col0w[3][t];
-    float dc = (rowv[0][t] + rowv[1][t]) + (yod[0][t] + yod[1][t]) - colv - us;
+    float dc = rv + yo - colv - us;
     if (t == T - 1) dc += usum + expf(cl) * ghs;
     // suffix sum over t
     float rc = dc;

@@ -122,6 +122,19 @@ __device__ __forceinline__ void st4_agent(float* slot, int slot_bytes, int byte_
                                          r, byte_off, 0, kCachePolicySc1);
 }
 
+// 16 bytes read with system-scope coherence (sc0 sc1): past this CU's L1 and
+// this XCD's L2, from the memory side where the producer's write-through
+// stores landed.  Reading the entering state this way replaces an agent-scope
+// acquire, which would invalidate the whole L2 of the XCD (the B, C and x
+// tiles other workgroups there are about to reuse) on every hand-off.
+constexpr int kCachePolicySc0 = 1;
+__device__ __forceinline__ f4 ld4_agent(const float* slot, int slot_bytes, int byte_off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(slot), 0, slot_bytes, 0x00020000);
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0,
+                                                                      kCachePolicySc0 | kCachePolicySc1));
+}
+
 // s_waitcnt vmcnt(0): this wave's vector memory operations, stores included,
 // have completed (gfx9 encoding: vmcnt 0, expcnt and lgkmcnt at their maxima).
 __device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -382,10 +395,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
         break;
       }
     }
-    // the other waves of this workgroup run on the same CU: one acquire (L1
-    // and L2 invalidation) before the barrier covers their loads as well
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
+  // the barrier orders every wave's state loads after thread 0 saw the flag;
+  // the loads themselves bypass the caches (ld4_agent)
   __syncthreads();
 
   // Each thread loads the entering state at the elements of its own S tiles,
@@ -398,7 +410,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
   for (int j = 0; j < NPT; ++j)
 #pragma unroll
     for (int R = 0; R < 4; ++R)
-      hreg[j][R] = ld4(hin + state_tile_offset(2 * i + spt0 + j, 32 * snt + 8 * R + 4 * kk, N));
+      hreg[j][R] = ld4_agent(hin, kP * N * 4,
+                             4 * state_tile_offset(2 * i + spt0 + j, 32 * snt + 8 * R + 4 * kk, N));
   // C rows 64..127 of the block (t-tiles 2 and 3, i.e. ti0 of every wave;
   // ti1's rows are still in creg) go to the x tile's space, swizzled like the
   // B tile; loads now, LDS stores after the state update

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void bwd_state_passing_kernel(
 // Phases: the products with G (G.B for dX, X.G for dB, x . (G B)) with G in
 // LDS, kept in registers; K and R, then V and W in place of G; dX and dB;
 // H_in over x and V, then dC and dY_t . (H_in C_t); the decay gradients.
-template <int N>
+template <int N, int HPW>
 __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
     const float* __restrict__ dt_raw, const float* __restrict__ dt_bias, float dt_min,
@@ -213,44 +213,38 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   __shared__ float rowv[NCG][T], xgb[NCG][T], yod[NCG][T], red[2 * NW];
   __shared__ float colw[4][T], col0w[4][T];
 
-  const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
-  const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
+  // HPW heads of one group per workgroup, one after the other: B and C are
+  // staged once for all of them, and their dB and dC parts are summed in
+  // registers, so one part per HPW heads goes to memory (the group sum then
+  // reads H/HPW parts per step instead of H).
+  const int64_t HQ = H / HPW;
+  const int64_t uq = blockIdx.x;  // (b * nb + blk) * HQ + hq
+  const int64_t hq = uq % HQ, blk = (uq / HQ) % nb, b = uq / (HQ * nb);
   // 32-bit and wave-uniform: the B and C buffer resources need a scalar base
-  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G)), t0 = blk * T;
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)(hq * HPW) / (int)(H / G)), t0 = blk * T;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int strip = wave & 3, colh = wave >> 2;  // row strip, column group
   const int i = lane % 16, kk = lane / 16;
   const int64_t PN = (int64_t)P * N;
-  const float* hin = states_in + u * PN;  // tiled layout
-  const float* gc = gst + u * PN;         // row-major [P][N]
   const int last = (int)((L - 1 - t0) < (T - 1) ? (L - 1 - t0) : (T - 1));
 
-  // Rows of this block (head h, or its group for B and C) through buffer
-  // resources that end after row `last`: rows past it read as zero and the
-  // gradient stores there are dropped, with 32-bit offsets and no clamps,
-  // selects or branches.
+  // Rows of this block (a head's x, dY and dX; the group's B and C; the dB
+  // and dC parts of the HPW heads) through buffer resources that end after
+  // row `last`: rows past it read as zero and the gradient stores there are
+  // dropped, with 32-bit offsets and no clamps, selects or branches.
   const uint32_t xrow = (uint32_t)(H * P * 4), brow = (uint32_t)(G * N * 4);
-  const uint32_t hrow = (uint32_t)(H * N * 4);  // per-head dB / dC parts
-  const int64_t xo = ((b * L + t0) * H + h) * P, bo = ((b * L + t0) * G + g) * N;
-  const int64_t ho = ((b * L + t0) * H + h) * N;
+  const uint32_t prow = (uint32_t)(HQ * N * 4);  // dB / dC parts, one per HPW heads
+  const int64_t bo = ((b * L + t0) * G + g) * N, po = ((b * L + t0) * HQ + hq) * N;
   const uint32_t xbytes = (uint32_t)last * xrow + P * 4, bbytes = (uint32_t)last * brow + N * 4;
-  const uint32_t hbytes = (uint32_t)last * hrow + N * 4;
+  const uint32_t pbytes = (uint32_t)last * prow + N * 4;
+  // float4 per thread (the last may be partial for N = 16: guarded)
+  constexpr int QX = T * P / (4 * NTH), QB = (T * N / 4 + NTH - 1) / NTH, QG = QB;
+  static_assert(T * P % (4 * NTH) == 0 && T == P, "staging");
 
-  // ---- stage x, dY, B, C, G, cum, dt (rows past the end are zero) -----------
+  // ---- stage B and C once (rows past the end are zero) -----------------------
   {
-    const auto xr = row_rsrc(x + xo, xbytes), yr = row_rsrc(dy + xo, xbytes);
     const auto br = row_rsrc(Bm + bo, bbytes), cr = row_rsrc(Cm + bo, bbytes);
-    // float4 per thread (the last may be partial for N = 16: guarded)
-    constexpr int QX = T * P / (4 * NTH), QB = (T * N / 4 + NTH - 1) / NTH, QG = QB;
-    static_assert(T * P % (4 * NTH) == 0 && T == P, "staging");
-    f4 xv[QX], yv[QX], bv[QB], cv[QB], gv[QG];
-#pragma unroll
-    for (int q = 0; q < QX; ++q) {
-      const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
-      const uint32_t o = (uint32_t)t * xrow + (uint32_t)p * 4;
-      xv[q] = bld4(xr, o);
-      yv[q] = bld4(yr, o);
-    }
+    f4 bv[QB], cv[QB];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const int e = 4 * (q * NTH + tid), t = e / N, n = e % N;
@@ -258,18 +252,6 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
       if (e < T * N) {
         bv[q] = bld4(br, o);
         cv[q] = bld4(cr, o);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < QG; ++q)
-      if (4 * (q * NTH + tid) < P * N) gv[q] = ld4(gc + 4 * (q * NTH + tid));
-#pragma unroll
-    for (int q = 0; q < QX; ++q) {
-      const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        xs_[t * kXP + p + c] = xv[q][c];
-        ys_[t * kXP + p + c] = yv[q][c];
       }
     }
 #pragma unroll
@@ -281,6 +263,47 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
           bs_[t * NS + n + c] = bv[q][c];
           cs_[t * NS + n + c] = cv[q][c];
         }
+      }
+    }
+  }
+
+  // Column tiles of this wave: 64-wide products (over p or s) tiles
+  // NJ4 colh ...; N-wide ones NJW tiles from jn (none for the later column
+  // groups when N has fewer tiles than groups).
+  const int j4 = NJ4 * colh, jn = colh * NJW;
+  const bool hasn = jn < NJ;  // wave-uniform
+  f4 dbacc[NJW], dcacc[NJW];  // dB and dC parts summed over the HPW heads
+#pragma unroll
+  for (int j = 0; j < NJW; ++j) dbacc[j] = dcacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int hk = 0; hk < HPW; ++hk) {
+  const int64_t h = hq * HPW + hk;
+  const int64_t u = (b * nb + blk) * H + h;  // this head's block
+  const float* hin = states_in + u * PN;  // tiled layout
+  const float* gc = gst + u * PN;         // row-major [P][N]
+  const int64_t xo = ((b * L + t0) * H + h) * P;
+
+  // ---- stage x, dY, G, cum, dt of this head (rows past the end are zero) -----
+  {
+    const auto xr = row_rsrc(x + xo, xbytes), yr = row_rsrc(dy + xo, xbytes);
+    f4 xv[QX], yv[QX], gv[QG];
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+      const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
+      const uint32_t o = (uint32_t)t * xrow + (uint32_t)p * 4;
+      xv[q] = bld4(xr, o);
+      yv[q] = bld4(yr, o);
+    }
+#pragma unroll
+    for (int q = 0; q < QG; ++q)
+      if (4 * (q * NTH + tid) < P * N) gv[q] = ld4(gc + 4 * (q * NTH + tid));
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+      const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        xs_[t * kXP + p + c] = xv[q][c];
+        ys_[t * kXP + p + c] = yv[q][c];
       }
     }
 #pragma unroll
@@ -317,12 +340,6 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     v += __shfl_xor(v, 16, kWave);
     return v + __shfl_xor(v, 32, kWave);
   };
-
-  // Column tiles of this wave: 64-wide products (over p or s) tiles
-  // 2 colh, 2 colh + 1; N-wide ones NJW tiles from jn (none when N = 16 and
-  // colh = 1).
-  const int j4 = NJ4 * colh, jn = colh * NJW;
-  const bool hasn = jn < NJ;  // wave-uniform
 
   // ---- products with G: GB[s][p] = B_s . G_p (dX), XG[s][n] = x_s^T G (dB) --
   // rows s in [16 strip, 16 strip + 16)
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
 
   // ---- dX = D dY + V^T dY + diag(w) GB;  dB = diag(dt) W^T C + diag(w) XG ----
   {
-    const auto dxr = row_rsrc(dx + xo, xbytes), dbr = row_rsrc(dBh + ho, hbytes);
+    const auto dxr = row_rsrc(dx + xo, xbytes);
     f4 vall[NJ4];
     tiles16<NJ4, T>([&](int r, int k) { return vm[k * 64 + 16 * strip + r]; },
                   [&](int j, int k, int c) { return ys_[k * kXP + 16 * (j4 + j) + c]; }, vall);
@@ -407,14 +424,12 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     tiles16<NJW, T>([&](int r, int k) { return wm[k * kXP + 16 * strip + r]; },
                     [&](int j, int k, int c) { return cs_[k * NS + 16 * (jn + j) + c]; }, a1);
 #pragma unroll
-    for (int j = 0; j < NJW; ++j) {
-      const int n = 16 * (jn + j) + i;
+    for (int j = 0; j < NJW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * strip + 4 * kk + r;
-        bst1(dbr, (uint32_t)s * hrow + (uint32_t)n * 4, dt_l[s] * a1[j][r] + wdt[s] * xgall[j][r]);
+        dbacc[j][r] += dt_l[s] * a1[j][r] + wdt[s] * xgall[j][r];
       }
-    }
     }
   }
   float dd = 0.0f;  // dY . x over the block
@@ -452,7 +467,6 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // ---- dC = diag(exp(cum)) dY H_in + W diag(dt) B; dY_t . (H_in C_t) ----------
   float ysum[4] = {0.f, 0.f, 0.f, 0.f};
   if (hasn) {
-    const auto dcr = row_rsrc(dCh + ho, hbytes);
     f4 a1[NJW], a2[NJW];
     tiles16<NJW, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
                     [&](int j, int k, int c) { return hs_[k * NS + 16 * (jn + j) + c]; }, a1);
@@ -465,7 +479,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * strip + 4 * kk + r;
         const float e = ecum[t] * a1[j][r];
-        bst1(dcr, (uint32_t)t * hrow + (uint32_t)n * 4, e + a2[j][r]);
+        dcacc[j][r] += e + a2[j][r];
         ysum[r] += e * cs_[t * NS + n];
       }
     }
@@ -536,21 +550,39 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
       dD_p[u] = dds;
     }
   }
+  __syncthreads();  // every LDS region of this head is read before the next
+  }
+
+  // ---- dB and dC parts of the HPW heads ---------------------------------------
+  if (hasn) {
+    const auto dbr = row_rsrc(dBh + po, pbytes), dcr = row_rsrc(dCh + po, pbytes);
+#pragma unroll
+    for (int j = 0; j < NJW; ++j) {
+      const int n = 16 * (jn + j) + i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t o = (uint32_t)(16 * strip + 4 * kk + r) * prow + (uint32_t)n * 4;
+        bst1(dbr, o, dbacc[j][r]);
+        bst1(dcr, o, dcacc[j][r]);
+      }
+    }
+  }
 }
 
-// dB and dC: sum the per-head parts over the heads of each group.
+// dB and dC: sum the parts (one per HPW heads, HQ = H / HPW per step) over the
+// heads of each group.
 __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ dBh,
                                                             const float* __restrict__ dCh,
                                                             float* __restrict__ dB,
                                                             float* __restrict__ dC, int64_t n,
-                                                            int64_t H, int64_t G, int64_t N) {
+                                                            int64_t HQ, int64_t G, int64_t N) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;  // ((b*L + t) * G + g) * N + c
   if (k >= n) return;
   const int64_t c = k % N, g = (k / N) % G, bt = k / (N * G);
-  const int64_t hpg = H / G;
+  const int64_t ppg = HQ / G;  // parts per group
   float sb = 0.0f, sc = 0.0f;
-  for (int64_t j = 0; j < hpg; ++j) {
-    const int64_t o = (bt * H + g * hpg + j) * N + c;
+  for (int64_t j = 0; j < ppg; ++j) {
+    const int64_t o = (bt * HQ + g * ppg + j) * N + c;
     sb += dBh[o];
     sc += dCh[o];
   }
@@ -593,6 +625,12 @@ __global__ __launch_bounds__(256) void bwd_head_sum_kernel(
 
 int64_t bwd_blocks(int64_t L) { return (L + kBT - 1) / kBT; }
 
+// Heads of one group the block kernel handles per workgroup: 4, else 2, else 1.
+static int bwd_heads_per_workgroup(int64_t H, int64_t G) {
+  const int64_t hpg = H / G;
+  return hpg % 4 == 0 ? 4 : hpg % 2 == 0 ? 2 : 1;
+}
+
 template <int N>
 static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
   const Problem& p = q.fwd;
@@ -603,11 +641,20 @@ static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
   hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),
                      (unsigned)p.H, (unsigned)p.b), dim3(256), 0, s, q.pc, p.ws_cum, q.dfinal,
                      q.gst, q.dinit, p.H, p.nc, PN);
-  hipLaunchKernelGGL((block_bwd_kernel<N>), dim3((unsigned)units), dim3(kBwdThreads), 0, s,
-                     static_cast<const float*>(p.x), static_cast<const float*>(p.B),
-                     static_cast<const float*>(p.C), static_cast<const float*>(p.dt), p.dt_bias,
-                     p.dt_min, p.dt_max, p.A, p.D, p.ws_dt, p.ws_cum, p.ws_states_in, q.gst, q.dy,
-                     q.dx, q.dBh, q.dCh, q.ddt, q.dA_p, q.dD_p, p.L, p.H, p.G, p.nc);
+  const int hpw = bwd_heads_per_workgroup(p.H, p.G);
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)(units / hpw)), dim3(kBwdThreads), 0, s,
+                       static_cast<const float*>(p.x), static_cast<const float*>(p.B),
+                       static_cast<const float*>(p.C), static_cast<const float*>(p.dt), p.dt_bias,
+                       p.dt_min, p.dt_max, p.A, p.D, p.ws_dt, p.ws_cum, p.ws_states_in, q.gst,
+                       q.dy, q.dx, q.dBh, q.dCh, q.ddt, q.dA_p, q.dD_p, p.L, p.H, p.G, p.nc);
+  };
+  if (hpw == 4)
+    launch(block_bwd_kernel<N, 4>);
+  else if (hpw == 2)
+    launch(block_bwd_kernel<N, 2>);
+  else
+    launch(block_bwd_kernel<N, 1>);
 }
 
 hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
@@ -624,7 +671,8 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
     }
     const int64_t nbc = p.b * p.L * p.G * p.N;
     hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
-                       s, q.dBh, q.dCh, q.dB, q.dC, nbc, p.H, p.G, p.N);
+                       s, q.dBh, q.dCh, q.dB, q.dC, nbc, p.H / bwd_heads_per_workgroup(p.H, p.G),
+                       p.G, p.N);
   } else if (q.dinit) {  // no steps: the initial state's gradient is dfinal (or 0)
     const int64_t PN = p.P * p.N;
     hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),

@@ -275,6 +275,13 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   f4 dbacc[NJW], dcacc[NJW];  // dB and dC parts summed over the HPW heads
 #pragma unroll
   for (int j = 0; j < NJW; ++j) dbacc[j] = dcacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  // K = C B^T is the same for every head of the group: formed once, kept in
+  // registers (rows t in [16 strip, 16 strip + 16), this wave's s tiles).
+  f4 kall[NJ4];
+  tiles16<NJ4, N>([&](int r, int k) { return cs_[(16 * strip + r) * NS + k]; },
+                [&](int j, int k, int c) { return bs_[(16 * (j4 + j) + c) * NS + k]; }, kall);
 
   for (int hk = 0; hk < HPW; ++hk) {
   const int64_t h = hq * HPW + hk;
@@ -364,12 +371,10 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   }
   __syncthreads();  // G is dead: V and W take its place
 
-  // ---- K = C B^T and R = dY X^T; masks, decays and the dcum sums -------------
-  // rows t in [16 strip, 16 strip + 16), two column tiles of s
+  // ---- R = dY X^T; masks, decays and the dcum sums with K --------------------
+  // rows t in [16 strip, 16 strip + 16), this wave's column tiles of s
   float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-  f4 kall[NJ4], rall[NJ4];
-  tiles16<NJ4, N>([&](int r, int k) { return cs_[(16 * strip + r) * NS + k]; },
-                [&](int j, int k, int c) { return bs_[(16 * (j4 + j) + c) * NS + k]; }, kall);
+  f4 rall[NJ4];
   tiles16<NJ4, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
                   [&](int j, int k, int c) { return xs_[(16 * (j4 + j) + c) * kXP + k]; }, rall);
 #pragma unroll

@@ -605,7 +605,6 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   q.dout = static_cast<const float*>(dout);
   q.dfinal = dfinal_states;
   q.dy = nonempty ? reinterpret_cast<float*>(ws + bl.off_y) : nullptr;
-  q.pc = nonempty ? reinterpret_cast<float*>(ws + bl.off_s) : nullptr;
   q.gst = nonempty ? reinterpret_cast<float*>(ws + bl.off_g) : nullptr;
   q.dBh = nonempty ? reinterpret_cast<float*>(ws + bl.off_db) : nullptr;
   q.dCh = nonempty ? reinterpret_cast<float*>(ws + bl.off_dc) : nullptr;

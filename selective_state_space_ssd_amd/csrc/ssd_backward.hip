@@ -27,7 +27,7 @@
 //
 // Kernels: the forward is re-run (64-step blocks) for dt, cum, the states
 // entering each block and the ungated y; then gate_bwd_kernel (dY, dz),
-// bwd_dstate_kernel (P_c), bwd_state_passing_kernel (G_c, dinit),
+// bwd_state_scan_kernel (P_c and the reverse scan: G_c, dinit),
 // block_bwd_kernel (dX, per-head dB and dC, ddt_raw, per-block dA and dD
 // parts) and the reductions over heads, batch and blocks.  The products are
 // on v_mfma_f32_16x16x4_f32 from LDS tiles; masks and decays are applied to
@@ -41,6 +41,9 @@ namespace {
 constexpr int kBT = 64;   // block length of the backward
 constexpr int kXP = 65;   // padded row stride of 64-wide LDS tiles
 constexpr int kBwdThreads = 512;  // block backward kernel: eight waves (sixteen measured the same)
+// reverse state scan: up to 32 state columns, four waves per 16, per workgroup
+template <int N>
+constexpr int kScanThreads = 4 * ((N < 32 ? N : 32) / 16) * kWave;
 
 // One 16 x 16 output tile of a wave on v_mfma_f32_16x16x4_f32: lane l
 // supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane l holds
@@ -91,76 +94,117 @@ __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__
   st4(dz + 4 * k, dzv);
 }
 
-// P_c[p][n] = sum_t exp(cum_t) dY_t[p] C_t[n] per (batch, block, head), row-major
-// [P][N].  Wave w owns rows p in [16w, 16w+16) and all N/16 column tiles.
+// Gradient of the state leaving each block, by a reverse scan over the
+// blocks: G_{nb-1} = dfinal (or 0), G_{c-1} = exp(cl_c) G_c + P_c with
+// P_c = sum_t exp(cum_t) dY_t C_t^T over block c (cum the running sum of
+// dt A inside the block, cl its last value); dinit = G_{-1}.  G_c is stored
+// row-major [P][N] per block.
+//
+// One workgroup per (batch, head, NCOL state columns), four waves per 16
+// columns; wave w holds the 16 x 16 tile (columns 16 (w % NS16) ..., rows
+// 16 (w / NS16) ...) of G^T in registers.  P_c needs no carry, so the blocks
+// go in groups of KD: a group's dY and C rows are staged into KD LDS buffers
+// at once, the next group's rows are loaded into registers, and the KD
+// products and updates of G run without waiting on memory (a wait for loads
+// issued a whole group earlier, not one block earlier).  C is staged already
+// scaled by exp(cum_t).  Rows past the sequence end, and blocks before the
+// first, read as zero through empty buffer ranges; such blocks leave G as it
+// is (exp(0) G + 0) and their stores are dropped.
 template <int N>
-__global__ __launch_bounds__(256) void bwd_dstate_kernel(
+__global__ __launch_bounds__(kScanThreads<N>) void bwd_state_scan_kernel(
     const float* __restrict__ dy, const float* __restrict__ Cm, const float* __restrict__ ws_cum,
-    float* __restrict__ pc, int64_t L, int64_t H, int64_t G, int64_t nb) {
-  constexpr int P = 64, NJ = N / 16;
-  __shared__ float dy_l[kBT][kXP];
-  __shared__ float c_l[kBT][N + 1];
-  __shared__ float e_l[kBT];
-  const int64_t u = blockIdx.x;  // (b * nb + blk) * H + h
-  const int64_t h = u % H, blk = (u / H) % nb, b = u / (H * nb);
-  const int64_t g = h / (H / G), t0 = blk * kBT;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int last = (int)((L - 1 - t0) < (kBT - 1) ? (L - 1 - t0) : (kBT - 1));
-  {  // 16-byte loads, all in flight, from rows clamped to the last real one
-    f4 yv[kBT * P / 1024], cv[kBT * N / 1024];
-#pragma unroll
-    for (int q = 0; q < kBT * P / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
-      yv[q] = ld4(dy + ((b * L + t0 + (t < last ? t : last)) * H + h) * P + p);
-    }
-#pragma unroll
-    for (int q = 0; q < kBT * N / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
-      cv[q] = ld4(Cm + ((b * L + t0 + (t < last ? t : last)) * G + g) * N + n);
-    }
-#pragma unroll
-    for (int q = 0; q < kBT * P / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / P, p = e % P;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) dy_l[t][p + c] = t <= last ? yv[q][c] : 0.0f;
-    }
-#pragma unroll
-    for (int q = 0; q < kBT * N / 1024; ++q) {
-      const int e = 4 * (q * 256 + tid), t = e / N, n = e % N;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) c_l[t][n + c] = t <= last ? cv[q][c] : 0.0f;
-    }
-  }
-  if (tid < kBT) e_l[tid] = expf(ws_cum[((b * H + h) * nb + blk) * kBT + tid]);
-  __syncthreads();
-  float* dst = pc + u * (int64_t)(P * N);
-  const int i = lane % 16, kk = lane / 16;
-  f4 acc[NJ];
-  tiles16<NJ, kBT>([&](int r, int k) { return dy_l[k][16 * wave + r] * e_l[k]; },
-                   [&](int j, int k, int c) { return c_l[k][16 * j + c]; }, acc);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(16 * wave + 4 * kk + r) * N + 16 * j + i] = acc[j][r];
-}
+    const float* dfinal, float* __restrict__ gst, float* dinit, int64_t L, int64_t H,
+    int64_t G, int64_t nb) {
+  constexpr int P = 64, T = kBT, NCOL = N < 32 ? N : 32, NS16 = NCOL / 16;
+  constexpr int NT = kScanThreads<N>;
+  constexpr int CS = NCOL == 32 ? 48 : 16, YS = 80;  // padded LDS row strides
+  constexpr int QY = T * P / (4 * NT);               // dY float4 per thread
+  constexpr int KD = 4;                              // blocks per group
+  static_assert(T * NCOL == 4 * NT && T * P % (4 * NT) == 0, "staging");
+  __shared__ __align__(16) float cl_[KD][T * CS];
+  __shared__ __align__(16) float yl_[KD][T * YS];
 
-// Reverse state passing: G_c (gradient of the state leaving block c, stored
-// row-major per block), G_{nb-1} = dfinal (or 0), G_{c-1} = exp(cl_c) G_c + P_c;
-// dinit = G_{-1}.  Four state elements per thread.
-__global__ __launch_bounds__(256) void bwd_state_passing_kernel(
-    const float* __restrict__ pc, const float* __restrict__ ws_cum, const float* dfinal,
-    float* __restrict__ gst, float* dinit, int64_t H, int64_t nb, int64_t PN) {
-  const int64_t h = blockIdx.y, b = blockIdx.z;
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
-  if (k >= PN / 4) return;
-  f4 gv = dfinal ? ld4(dfinal + (b * H + h) * PN + 4 * k) : f4{0.f, 0.f, 0.f, 0.f};
-  const float* cl = ws_cum + (b * H + h) * nb * kBT + (kBT - 1);
-  for (int64_t c = nb - 1; c >= 0; --c) {
-    const int64_t o = ((b * nb + c) * H + h) * PN + 4 * k;
-    st4(gst + o, gv);
-    gv = expf(cl[c * kBT]) * gv + ld4(pc + o);
+  // blockIdx.x = ncs * (b H) + (b H index): the column slices of one head
+  // are b H apart, on one XCD when b H is a multiple of 8
+  const int64_t BH = (int64_t)gridDim.x / (N / NCOL);
+  const int64_t bh = blockIdx.x % BH, ncs = blockIdx.x / BH;
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G));
+  const int n0 = (int)ncs * NCOL;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int ns = wave % NS16, pt = wave / NS16, i = lane % 16, kk = lane / 16;
+  const uint32_t xrow = (uint32_t)(H * P * 4), brow = (uint32_t)(G * N * 4);
+  const int64_t PN = (int64_t)P * N;
+
+  // this thread's staging slots: C row tc, columns nc..nc+3; QY dY float4s
+  const int tc = tid / (NCOL / 4), nc = 4 * (tid % (NCOL / 4));
+  f4 cv[KD], yv[KD][QY];
+  float cumv[KD], clv[KD];
+  auto load = [&](int j, int64_t c) {  // block c < 0: nothing is read
+    const int64_t t0 = c * T;
+    const int last = (int)((L - 1 - t0) < (T - 1) ? (L - 1 - t0) : (T - 1));
+    const uint32_t yb = c >= 0 ? (uint32_t)last * xrow + P * 4 : 0u;
+    const uint32_t cb = c >= 0 ? (uint32_t)last * brow + NCOL * 4 : 0u;
+    const auto yr = row_rsrc(dy + ((b * L + t0) * H + h) * P, yb);
+    const auto cr = row_rsrc(Cm + ((b * L + t0) * G + g) * N + n0, cb);
+    const auto ur = row_rsrc(ws_cum + (bh * nb + (c >= 0 ? c : 0)) * T, c >= 0 ? T * 4 : 0u);
+#pragma unroll
+    for (int q = 0; q < QY; ++q) {
+      const int e = 4 * (q * NT + tid);
+      yv[j][q] = bld4(yr, (uint32_t)(e / P) * xrow + (uint32_t)(e % P) * 4);
+    }
+    cv[j] = bld4(cr, (uint32_t)tc * brow + (uint32_t)nc * 4);
+    cumv[j] = bld1(ur, (uint32_t)tc * 4, 0.0f);
+    clv[j] = bld1(ur, (T - 1) * 4, 0.0f);
+  };
+  auto stage = [&](int j) {
+    const float e = expf(cumv[j]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cl_[j][tc * CS + nc + c] = e * cv[j][c];
+#pragma unroll
+    for (int q = 0; q < QY; ++q) {
+      const int e4 = 4 * (q * NT + tid);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) yl_[j][(e4 / P) * YS + e4 % P + c] = yv[j][q][c];
+    }
+  };
+
+  // G^T tile: register r of lane (i, kk) is column n = n0 + 16 ns + 4 kk + r
+  // of row p = 16 pt + i, i.e. four consecutive floats of the row-major block
+  const int64_t toff = (int64_t)(16 * pt + i) * N + n0 + 16 * ns + 4 * kk;
+  f4 gv = dfinal ? ld4(dfinal + bh * PN + toff) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KD; ++j) load(j, nb - 1 - j);
+  for (int64_t c0 = nb - 1; c0 >= 0; c0 -= KD) {
+#pragma unroll
+    for (int j = 0; j < KD; ++j) stage(j);
+    float ecl[KD];
+#pragma unroll
+    for (int j = 0; j < KD; ++j) ecl[j] = expf(clv[j]);
+#pragma unroll
+    for (int j = 0; j < KD; ++j) load(j, c0 - KD - j);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KD; ++j) {
+      const int64_t c = c0 - j;
+      const auto gr = row_rsrc(gst + ((b * nb + c) * H + h) * PN, c >= 0 ? (uint32_t)PN * 4 : 0u);
+      bst4(gr, (uint32_t)toff * 4, gv);
+      // P_c^T tile = sum_t (e_t C_t)[n] dY_t[p], two accumulators over t
+      f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+      const float* ca = &cl_[j][16 * ns + i];
+      const float* yb = &yl_[j][16 * pt + i];
+#pragma unroll
+      for (int k = 0; k < T; k += 8) {
+        a0 = mfma16x16x4(ca[(k + kk) * CS], yb[(k + kk) * YS], a0);
+        a1 = mfma16x16x4(ca[(k + 4 + kk) * CS], yb[(k + 4 + kk) * YS], a1);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gv[r] = ecl[j] * gv[r] + (a0[r] + a1[r]);
+    }
+    __syncthreads();  // the buffers are rewritten by the next group
   }
-  if (dinit) st4(dinit + (b * H + h) * PN + 4 * k, gv);
+  if (dinit) st4(dinit + bh * PN + toff, gv);
 }
 
 // One workgroup (four waves) per (batch, block, head).  Everything the products
@@ -636,16 +680,21 @@ static int bwd_heads_per_workgroup(int64_t H, int64_t G) {
   return hpg % 4 == 0 ? 4 : hpg % 2 == 0 ? 2 : 1;
 }
 
+// The reverse state scan over nb blocks (nb = 0: dinit = dfinal, or 0).
+template <int N>
+static void launch_state_scan(const BwdProblem& q, hipStream_t s, int64_t nb) {
+  const Problem& p = q.fwd;
+  constexpr int NCOL = N < 32 ? N : 32, NT = kScanThreads<N>;
+  hipLaunchKernelGGL((bwd_state_scan_kernel<N>), dim3((unsigned)(N / NCOL * p.b * p.H)),
+                     dim3(NT), 0, s, q.dy, static_cast<const float*>(p.C), p.ws_cum, q.dfinal,
+                     q.gst, q.dinit, p.L, p.H, p.G, nb);
+}
+
 template <int N>
 static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
   const Problem& p = q.fwd;
   const int64_t units = p.b * p.nc * p.H;
-  hipLaunchKernelGGL((bwd_dstate_kernel<N>), dim3((unsigned)units), dim3(256), 0, s, q.dy,
-                     static_cast<const float*>(p.C), p.ws_cum, q.pc, p.L, p.H, p.G, p.nc);
-  const int64_t PN = 64 * N;
-  hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),
-                     (unsigned)p.H, (unsigned)p.b), dim3(256), 0, s, q.pc, p.ws_cum, q.dfinal,
-                     q.gst, q.dinit, p.H, p.nc, PN);
+  launch_state_scan<N>(q, s, p.nc);
   const int hpw = bwd_heads_per_workgroup(p.H, p.G);
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(units / hpw)), dim3(kBwdThreads), 0, s,
@@ -679,10 +728,12 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
                        s, q.dBh, q.dCh, q.dB, q.dC, nbc, p.H / bwd_heads_per_workgroup(p.H, p.G),
                        p.G, p.N);
   } else if (q.dinit) {  // no steps: the initial state's gradient is dfinal (or 0)
-    const int64_t PN = p.P * p.N;
-    hipLaunchKernelGGL(bwd_state_passing_kernel, dim3((unsigned)((PN / 4 + 255) / 256),
-                       (unsigned)p.H, (unsigned)p.b), dim3(256), 0, s, nullptr, nullptr, q.dfinal,
-                       nullptr, q.dinit, p.H, (int64_t)0, PN);
+    switch (p.N) {
+      case 16: launch_state_scan<16>(q, s, 0); break;
+      case 32: launch_state_scan<32>(q, s, 0); break;
+      case 64: launch_state_scan<64>(q, s, 0); break;
+      case 128: launch_state_scan<128>(q, s, 0); break;
+    }
   }
   hipLaunchKernelGGL(bwd_head_sum_kernel, dim3((unsigned)p.H), dim3(256), 0, s, q.dA_p, q.dD_p,
                      q.ddt, q.dA, q.dD, q.ddt_bias, p.b, p.L, p.H, p.nc);

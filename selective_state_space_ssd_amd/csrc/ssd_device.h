@@ -93,6 +93,11 @@ __device__ __forceinline__ f4 bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bst1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
+// four consecutive fp32 elements stored at byte offset off
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v),
+                                         r, off, 0, 0);
+}
 // two consecutive elements at byte offset off, as fp32
 __device__ __forceinline__ f2 bld2(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
   return __builtin_bit_cast(f2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));

@@ -137,17 +137,16 @@ hipError_t launch_gated_rmsnorm(const BlockProblem& q, hipStream_t stream);
 
 // Backward (ssd_backward.hip, fp32).  `fwd` is the forward problem re-run with
 // 64-step blocks (Q = 64, nc = bwd_blocks(L)) whose workspace regions hold dt,
-// cum, the chunk-local states (reused for P_c) and the states entering each
+// cum, the chunk-local states and the states entering each
 // block; fwd.z is the gate input.
 struct BwdProblem {
   Problem fwd;
   const float* dout;     // [b, L, H, P]
   const float* dfinal;   // [b, H, P, N], may be null
   float* dy;             // [b, L, H, P]: the ungated y, then dY
-  float* pc;             // [b, nb, H] row-major P x N blocks
   float* gst;            // [b, nb, H] row-major P x N blocks: gradient of each block's end state
-  float* dBh;            // [b, L, H, N] per-head parts of dB
-  float* dCh;            // [b, L, H, N] per-head parts of dC
+  float* dBh;            // [b, L, H, N]: dB parts, one per 1, 2 or 4 heads (H/HPW used)
+  float* dCh;            // [b, L, H, N]: parts of dC, the same
   float* dA_p;           // [b, nb, H]
   float* dD_p;           // [b, nb, H]
   float* dx;             // outputs

@@ -207,17 +207,19 @@ __global__ __launch_bounds__(kScanThreads<N>) void bwd_state_scan_kernel(
   if (dinit) st4(dinit + bh * PN + toff, gv);
 }
 
-// One workgroup (four waves) per (batch, block, head).  Everything the products
-// read is staged in one LDS buffer with 16-byte global loads, regions reused
-// as they die (floats; rows padded by one against bank conflicts):
+// One workgroup (eight waves) per (batch, block, up to four heads of one
+// group).  Everything the products read is staged in one LDS buffer with
+// 16-byte global loads, regions reused as they die (floats; rows padded by
+// one against bank conflicts; B and C once, the rest per head):
 //   [0, 4160)       x [64][65]                 | then H_in [64][129] over
-//   [4160, 8256)    V [64][64]  (K, then V)    |   x and V (dC phase)
-//   [8256, 12416)   W [64][65]  (R, then W)    G [64][129] over V and W
+//   [4160, 8256)    V [64][64]                 |   x and V (dC phase)
+//   [8256, 12416)   W [64][65]                 G [64][129] over V and W
 //   [12416, 16576)  dY [64][65]                  (first phase)
 //   [16576, 24832)  B [64][129]
 //   [24832, 33088)  C [64][129]
-// Phases: the products with G (G.B for dX, X.G for dB, x . (G B)) with G in
-// LDS, kept in registers; K and R, then V and W in place of G; dX and dB;
+// Phases per head: the products with G (G.B for dX, X.G for dB, x . (G B))
+// with G in LDS, kept in registers; R, and with K = C B^T (formed once per
+// workgroup, in registers) V and W in place of G; dX and dB;
 // H_in over x and V, then dC and dY_t . (H_in C_t); the decay gradients.
 template <int N, int HPW>
 __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     int64_t H, int64_t nc, int64_t Q, const T* __restrict__ Bm, const T* __restrict__ Cm,
     float* __restrict__ gram, int64_t gz, int64_t gram_jobs, int64_t L, int64_t G) {
   constexpr int PN = 64 * N;
-  constexpr int U = 4;  // chunks in flight
+  constexpr int U = 16;  // chunks in flight
   if constexpr (QG > 0) {
     if (blockIdx.z < gz) {  // whole workgroup
       const int64_t job =

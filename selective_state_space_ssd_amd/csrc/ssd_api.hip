@@ -592,19 +592,23 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   p.fs_ring = nullptr; p.fs_flags = nullptr; p.fs_ctl = nullptr;
   p.fused_kind = 0;
   if (nonempty) {
-    // the forward again (64-step blocks, no gate): dt, cum, states, y
+    // the forward again (64-step blocks, no gate): dt, cum, states, and the
+    // ungated y, which only dz needs (no gate: no y)
     if (!ssd::chunk_state_fuses_dt(p) && ssd::launch_dt_cumsum(p, stream) != hipSuccess)
       return SSD_ERR_HIP;
     if (ssd::launch_chunk_state(p, stream) != hipSuccess) return SSD_ERR_HIP;
     if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
-    if (ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (z && ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
   }
   ssd::BwdProblem q;
   q.fwd = p;
   q.fwd.z = z;
   q.dout = static_cast<const float*>(dout);
   q.dfinal = dfinal_states;
-  q.dy = nonempty ? reinterpret_cast<float*>(ws + bl.off_y) : nullptr;
+  // dY: formed over y when there is a gate, else dout itself (only read)
+  q.dy = !nonempty ? nullptr
+         : z       ? reinterpret_cast<float*>(ws + bl.off_y)
+                   : const_cast<float*>(static_cast<const float*>(dout));
   q.gst = nonempty ? reinterpret_cast<float*>(ws + bl.off_g) : nullptr;
   q.dBh = nonempty ? reinterpret_cast<float*>(ws + bl.off_db) : nullptr;
   q.dCh = nonempty ? reinterpret_cast<float*>(ws + bl.off_dc) : nullptr;

@@ -26,7 +26,7 @@
 // with P_c = sum_t exp(cum_t) dY_t C_t^T, and dinit = G_{-1}.
 //
 // Kernels: the forward is re-run (64-step blocks) for dt, cum, the states
-// entering each block and the ungated y; then gate_bwd_kernel (dY, dz),
+// entering each block and the ungated y (with a gate); then gate_bwd_kernel (dY, dz),
 // bwd_state_scan_kernel (P_c and the reverse scan: G_c, dinit),
 // block_bwd_kernel (dX, per-head dB and dC, ddt_raw, per-block dA and dD
 // parts) and the reductions over heads, batch and blocks.  The products are
@@ -70,18 +70,14 @@ __device__ __forceinline__ void tiles16(FA a, FB b, f4 (&acc)[NJ]) {
 }
 }  // namespace
 
-// dY = dout * silu(z) (in place of y), dz = dout * y * silu'(z); without z,
-// dY = dout.  Four elements per thread.
+// dY = dout * silu(z) (in place of y), dz = dout * y * silu'(z); launched
+// only with a gate.  Four elements per thread.
 __global__ __launch_bounds__(256) void gate_bwd_kernel(const float* __restrict__ dout,
                                                        const float* __restrict__ z, float* y_dy,
                                                        float* __restrict__ dz, int64_t n4) {
   const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (k >= n4) return;
   const f4 d = ld4(dout + 4 * k);
-  if (!z) {
-    st4(y_dy + 4 * k, d);
-    return;
-  }
   const f4 y = ld4(y_dy + 4 * k), zv = ld4(z + 4 * k);
   f4 dyv, dzv;
 #pragma unroll
@@ -717,8 +713,9 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
   const Problem& p = q.fwd;
   if (p.L > 0) {
     const int64_t nx4 = p.b * p.L * p.H * p.P / 4;
-    hipLaunchKernelGGL(gate_bwd_kernel, dim3((unsigned)((nx4 + 255) / 256)), dim3(256), 0, s,
-                       q.dout, static_cast<const float*>(p.z), q.dy, q.dz, nx4);
+    if (p.z)  // without a gate dY is dout, which q.dy then points at
+      hipLaunchKernelGGL(gate_bwd_kernel, dim3((unsigned)((nx4 + 255) / 256)), dim3(256), 0, s,
+                         q.dout, static_cast<const float*>(p.z), q.dy, q.dz, nx4);
     switch (p.N) {
       case 16: launch_bwd_n<16>(q, s); break;
       case 32: launch_bwd_n<32>(q, s); break;

@@ -143,7 +143,7 @@ struct BwdProblem {
   Problem fwd;
   const float* dout;     // [b, L, H, P]
   const float* dfinal;   // [b, H, P, N], may be null
-  float* dy;             // [b, L, H, P]: the ungated y, then dY
+  float* dy;             // [b, L, H, P]: the ungated y, then dY (without a gate: dout, read only)
   float* gst;            // [b, nb, H] row-major P x N blocks: gradient of each block's end state
   float* dBh;            // [b, L, H, N]: dB parts, one per 1, 2 or 4 heads (H/HPW used)
   float* dCh;            // [b, L, H, N]: parts of dC, the same

@@ -184,3 +184,30 @@ def test_bwd_bf16(N, H, G, L):
         compare(k, np64(g[k]), ref[k], TOL["bf16"])
     for k in F32_OUT:
         compare(k, np64(g[k]), ref[k], TOL["f32"])
+
+
+@pytest.mark.parametrize("gate", [True, False], ids=["gate", "nogate"])
+def test_bwd_leaves_inputs_unchanged(gate):
+    """Without a gate dY is dout itself, read in place by the reverse pass;
+    with one it is formed in the workspace.  Either way every input, dout
+    included, must be bitwise what the caller passed."""
+    w = Workload("bwd_inputs", 2, 3 * 64 + 11, 8, 64, 128, 2, 128, "f32", 7300 + gate, gate=gate,
+                 skip=True, init=True)
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    log(f"test_bwd_leaves_inputs_unchanged gate={gate}")
+    rng = np.random.default_rng(7301)
+    dout = torch.from_numpy(rng.standard_normal(t["x"].shape).astype(np.float32)).to(DEV)
+    dfin = torch.from_numpy(
+        rng.standard_normal(t["initial_states"].shape).astype(np.float32)).to(DEV)
+    args = {k: v for k, v in t.items() if isinstance(v, torch.Tensor)}
+    before = {k: v.clone() for k, v in args.items()}
+    dout0, dfin0 = dout.clone(), dfin.clone()
+    g = ssd.scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], dout, D=t["D"], z=t["z"],
+                     dt_bias=t["dt_bias"], initial_states=t["initial_states"], dfinal_states=dfin)
+    torch.cuda.synchronize()
+    for k, v in args.items():
+        assert torch.equal(v, before[k]), k
+    assert torch.equal(dout, dout0)
+    assert torch.equal(dfin, dfin0)
+    assert torch.isfinite(g["dx"]).all()

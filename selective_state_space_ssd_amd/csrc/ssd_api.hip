@@ -591,6 +591,7 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   p.ws_gram = nullptr;  // the chunk scan forms its tiles of B C^T itself
   p.fs_ring = nullptr; p.fs_flags = nullptr; p.fs_ctl = nullptr;
   p.fused_kind = 0;
+  const bool fuse_gate = nonempty && z && ssd::use_group_scan(nheads, dstate, ngroups, 64, false);
   if (nonempty) {
     // the forward again (64-step blocks, no gate): dt, cum, states, and the
     // ungated y, which only dz needs (no gate: no y)
@@ -598,7 +599,17 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
       return SSD_ERR_HIP;
     if (ssd::launch_chunk_state(p, stream) != hipSuccess) return SSD_ERR_HIP;
     if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    // With a gate and the four-heads chunk scan, its epilogue forms dY and dz
+    // from y directly (no y round trip, no gate kernel)
+    if (fuse_gate) {
+      p.z = z;
+      p.gate_dout = static_cast<const float*>(dout);
+      p.gate_dz = static_cast<float*>(grad[4]);
+    }
     if (z && ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    p.z = nullptr;
+    p.gate_dout = nullptr;
+    p.gate_dz = nullptr;
   }
   ssd::BwdProblem q;
   q.fwd = p;
@@ -620,6 +631,7 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   q.dC = static_cast<float*>(grad[3]);
   q.dz = static_cast<float*>(grad[4]);
   q.dA = dA; q.dD = dD; q.ddt_bias = ddt_bias; q.dinit = dinitial_states;
+  q.dy_formed = fuse_gate;
   if (ssd::launch_bwd(q, stream) != hipSuccess) return SSD_ERR_HIP;
   if (bl.bf16 && nonempty) {
     void* outs_bf16[5] = {dx, ddt, dB, dC, dz};

@@ -713,7 +713,9 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
   const Problem& p = q.fwd;
   if (p.L > 0) {
     const int64_t nx4 = p.b * p.L * p.H * p.P / 4;
-    if (p.z)  // without a gate dY is dout, which q.dy then points at
+    // without a gate dY is dout, which q.dy then points at; dy_formed: the
+    // re-run's chunk scan has written dY and dz already
+    if (p.z && !q.dy_formed)
       hipLaunchKernelGGL(gate_bwd_kernel, dim3((unsigned)((nx4 + 255) / 256)), dim3(256), 0, s,
                          q.dout, static_cast<const float*>(p.z), q.dy, q.dz, nx4);
     switch (p.N) {

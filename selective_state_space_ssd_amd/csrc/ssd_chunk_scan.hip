@@ -36,6 +36,7 @@
 // read hit 16 consecutive padded rows.
 #include "ssd_device.h"
 #include "ssd_kernels.h"
+#include <type_traits>
 
 namespace ssd {
 
@@ -227,14 +228,16 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 // per lane, two full 256-byte rows per instruction.
 // ---------------------------------------------------------------------------
 
-template <typename T, int Q, int N, bool GATE, bool PRE>
+template <typename T, int Q, int N, bool GATE, bool PRE, bool GB = false>
 __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ Dv, const T* __restrict__ z, const float* __restrict__ ws_dt,
     const float* __restrict__ ws_cum, const float* __restrict__ states_in,
     const float* __restrict__ gram, T* __restrict__ out,
-    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits) {
+    const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits,
+    const T* __restrict__ gd, T* __restrict__ gdz) {
   constexpr int P = 64, NT = Q / 32, CS = N + 4, NG = NT * (NT + 1) / 2, KQ = N / 8;
+  static_assert(!(GB && GATE), "the gate gradient epilogue takes the ungated y");
   constexpr int NW = 8;                   // waves: two per head
   constexpr int GW = (NG + NW - 1) / NW;  // G tiles per wave, at most
   constexpr int NS = NT / 2;              // t-tiles per wave
@@ -324,8 +327,11 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   const uint32_t rowb = (uint32_t)(xs * sizeof(T));  // bytes from one step to the next
   const uint32_t nbytes = (uint32_t)((last * xs + P) * sizeof(T));
   const auto xr = row_rsrc(x + hoff, nbytes);
-  const auto zr = row_rsrc(GATE ? z + hoff : x + hoff, nbytes);  // read only when GATE
+  const auto zr = row_rsrc(GATE || GB ? z + hoff : x + hoff, nbytes);  // read only when GATE or GB
   const auto orr = row_rsrc(out + hoff, nbytes);
+  // gate gradient epilogue: dout in, dz out (same rows)
+  const auto dr = row_rsrc(GB ? gd + hoff : x + hoff, nbytes);
+  const auto dzr = row_rsrc(GB ? gdz + hoff : out + hoff, nbytes);
   const uint32_t lane_b = (uint32_t)((4 * kk * xs + 2 * i) * sizeof(T));  // row 4 kk, column 2 i
   const float* hs = states_in + ((b * nc + c) * H + h) * (int64_t)(P * N) + 4 * lane;
   f4 hv[HR][2];
@@ -348,6 +354,12 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   auto load_z = [&](int ti) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) zv[m] = bld2(zr, lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb, T{});
+  };
+  f2 dv[GB ? 16 : 1];  // dout rows of that t-tile (gate gradient epilogue)
+  auto load_d = [&](int ti) {
+#pragma unroll
+    for (int m = 0; m < (GB ? 16 : 1); ++m)
+      dv[m] = bld2(dr, lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb, T{});
   };
   __builtin_amdgcn_sched_barrier(0);  // every set-up load is issued above
 
@@ -378,7 +390,8 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   // state part, which is bound by the matrix cores
 #pragma unroll
   for (int R = 0; R < 4; ++R) load_x(0, R);
-  if constexpr (GATE) load_z(own(0));
+  if constexpr (GATE || GB) load_z(own(0));
+  if constexpr (GB) load_d(own(0));
 
   // ---- 1. causal tiles of G^T = B C^T, shared by the four heads ---------------
   if constexpr (!PRE) {
@@ -544,17 +557,35 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
         f2 y;
         y[0] = acc[j][0][r];
         y[1] = acc[j][1][r];
-        if constexpr (GATE) {
-          y[0] *= silu(zv[r][0]);
-          y[1] *= silu(zv[r][1]);
-        }
         // rows past `last` fall outside the buffer and are dropped
-        bst2(orr, lane_b + (32 * si + 8 * (r / 4) + r % 4) * rowb, y, T{});
+        const uint32_t off = lane_b + (32 * si + 8 * (r / 4) + r % 4) * rowb;
+        if constexpr (GB) {
+          // dY = dout silu(z), dz = dout y sigmoid(z) (1 + z (1 - sigmoid(z)))
+          f2 dyv, dzv;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float zz = zv[r][e], d = dv[r][e];
+            const float sg = fast_rcp(1.0f + fast_exp2(-zz * kLog2e));
+            dyv[e] = d * zz * sg;
+            dzv[e] = d * y[e] * sg * (1.0f + zz * (1.0f - sg));
+          }
+          bst2(orr, off, dyv, T{});
+          bst2(dzr, off, dzv, T{});
+        } else {
+          if constexpr (GATE) {
+            y[0] *= silu(zv[r][0]);
+            y[1] *= silu(zv[r][1]);
+          }
+          bst2(orr, off, y, T{});
+        }
       };
 #pragma unroll
       for (int r = 0; r < 16; ++r) emit(r);
-      if constexpr (GATE) {
+      if constexpr (GATE || GB) {
         if (j + 1 < NS) load_z(own(j + 1));
+      }
+      if constexpr (GB) {
+        if (j + 1 < NS) load_d(own(j + 1));
       }
     }
   }
@@ -580,13 +611,15 @@ int64_t gram_tile_floats(int64_t Q) {
   return nt * (nt + 1) / 2 * 1024;
 }
 
-template <typename T, int Q, int N, bool GATE, bool PRE>
+template <typename T, int Q, int N, bool GATE, bool PRE, bool GB = false>
 static void launch_group(const Problem& p, hipStream_t s, int64_t nunits) {
-  hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, GATE, PRE>), dim3((unsigned)nunits),
+  hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, GATE, PRE, GB>), dim3((unsigned)nunits),
                      dim3(512), 0, s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
                      static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.ws_dt,
                      p.ws_cum, p.ws_states_in, p.ws_gram, static_cast<T*>(p.out), p.ws_seg, p.L,
-                     p.H, p.G, p.nc, nunits);
+                     p.H, p.G, p.nc, nunits,
+                     static_cast<const T*>(static_cast<const void*>(p.gate_dout)),
+                     static_cast<T*>(static_cast<void*>(p.gate_dz)));
 }
 
 template <typename T, int Q, int N>
@@ -594,6 +627,12 @@ static void launch_qn(const Problem& p, hipStream_t s) {
   if constexpr ((Q == 64 || Q == 128) && (N == 64 || N == 128)) {
     if (use_group_kernel(p)) {
       const int64_t nunits = p.b * p.nc * (p.H / 4);
+      if constexpr (std::is_same<T, float>::value && Q == 64) {
+        if (p.gate_dout) {  // the backward's re-run: the gate gradient epilogue
+          launch_group<T, Q, N, false, false, true>(p, s, nunits);
+          return;
+        }
+      }
       if (p.ws_gram) {
         if (p.z) launch_group<T, Q, N, true, true>(p, s, nunits);
         else launch_group<T, Q, N, false, true>(p, s, nunits);

@@ -42,6 +42,11 @@ struct Problem {
   unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
   unsigned* fs_ctl;      // 8 ticket counters, then the error word
   int fused_kind;        // 0: choose, 1: per-head kernel, 2: group kernel
+  // Backward re-run only (fp32, four-heads chunk scan): with gate_dout set the
+  // chunk scan's epilogue writes dY = dout silu(z) to out and dz = dout y
+  // silu'(z) to gate_dz in place of y (z is then the gate input).
+  const float* gate_dout = nullptr;
+  float* gate_dz = nullptr;
 };
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().
@@ -158,6 +163,7 @@ struct BwdProblem {
   float* dD;             // may be null
   float* ddt_bias;       // may be null
   float* dinit;          // may be null
+  bool dy_formed = false;  // dY and dz already written by the re-run's chunk scan
 };
 int64_t bwd_blocks(int64_t L);
 hipError_t launch_bwd(const BwdProblem& q, hipStream_t stream);

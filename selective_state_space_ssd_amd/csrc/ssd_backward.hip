@@ -26,7 +26,8 @@
 // with P_c = sum_t exp(cum_t) dY_t C_t^T, and dinit = G_{-1}.
 //
 // Kernels: the forward is re-run (64-step blocks) for dt, cum, the states
-// entering each block and the ungated y (with a gate); then gate_bwd_kernel (dY, dz),
+// entering each block and, with a gate, dY and dz (formed from the ungated y
+// by the four-heads chunk scan's epilogue, else by gate_bwd_kernel); then
 // bwd_state_scan_kernel (P_c and the reverse scan: G_c, dinit),
 // block_bwd_kernel (dX, per-head dB and dC, ddt_raw, per-block dA and dD
 // parts) and the reductions over heads, batch and blocks.  The products are

@@ -638,20 +638,23 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restr
   dC[k] = sc;
 }
 
-// dA, dD, ddt_bias: one workgroup per head, fixed summation order.
-__global__ __launch_bounds__(256) void bwd_head_sum_kernel(
+// dA, dD, ddt_bias: one workgroup per head, fixed summation order.  1024
+// threads, so each walks few rows of the [b L, H] and [b nb, H] parts.
+constexpr int kHeadSumThreads = 1024;
+__global__ __launch_bounds__(kHeadSumThreads) void bwd_head_sum_kernel(
     const float* __restrict__ dA_p, const float* __restrict__ dD_p,
     const float* __restrict__ ddt_raw, float* __restrict__ dA, float* dD, float* ddt_bias,
     int64_t b, int64_t L, int64_t H, int64_t nb) {
-  __shared__ float red[3][4];
+  constexpr int NW = kHeadSumThreads / kWave;
+  __shared__ float red[3][NW];
   const int64_t h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   float sa = 0.0f, sd = 0.0f, sbias = 0.0f;
-  for (int64_t k = tid; k < b * nb; k += 256) {
+  for (int64_t k = tid; k < b * nb; k += kHeadSumThreads) {
     sa += dA_p[k * H + h];
     sd += dD_p[k * H + h];
   }
-  for (int64_t k = tid; k < b * L; k += 256) sbias += ddt_raw[k * H + h];
+  for (int64_t k = tid; k < b * L; k += kHeadSumThreads) sbias += ddt_raw[k * H + h];
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     sa += __shfl_xor(sa, off, kWave);
@@ -665,9 +668,15 @@ __global__ __launch_bounds__(256) void bwd_head_sum_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    dA[h] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    if (dD) dD[h] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    if (ddt_bias) ddt_bias[h] = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+    float ta = 0.0f, td = 0.0f, tb = 0.0f;
+    for (int w = 0; w < NW; ++w) {
+      ta += red[0][w];
+      td += red[1][w];
+      tb += red[2][w];
+    }
+    dA[h] = ta;
+    if (dD) dD[h] = td;
+    if (ddt_bias) ddt_bias[h] = tb;
   }
 }
 
@@ -737,8 +746,8 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
       case 128: launch_state_scan<128>(q, s, 0); break;
     }
   }
-  hipLaunchKernelGGL(bwd_head_sum_kernel, dim3((unsigned)p.H), dim3(256), 0, s, q.dA_p, q.dD_p,
-                     q.ddt, q.dA, q.dD, q.ddt_bias, p.b, p.L, p.H, p.nc);
+  hipLaunchKernelGGL(bwd_head_sum_kernel, dim3((unsigned)p.H), dim3(kHeadSumThreads), 0, s,
+                     q.dA_p, q.dD_p, q.ddt, q.dA, q.dD, q.ddt_bias, p.b, p.L, p.H, p.nc);
   return hipGetLastError();
 }
 

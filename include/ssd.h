@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 /* Element type of x, dt, B, C, z and out.  A, D, dt_bias, dt_limit and both
  * state tensors are always float32; accumulation is always float32. */
@@ -69,7 +69,11 @@ extern "C" {
                                     dt_bias not aligned to their element; workspace not
                                     256-byte aligned */
 #define SSD_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than ssd_scan_fwd_workspace_size */
-#define SSD_ERR_HIP (-5)         /* a kernel launch failed (hipGetLastError) */
+#define SSD_ERR_HIP (-5)         /* a kernel launch failed (hipGetLastError), or a HIP call of
+                                    ssd_scan_fwd_wait_status failed */
+#define SSD_ERR_WAIT (-6)        /* ssd_scan_fwd_wait_status only: on the fused path a
+                                    workgroup gave up its bounded wait for the state entering
+                                    its block; out and final_states of that call are invalid */
 
 /*
  * ssd_scan_fwd -- enqueue the forward on `stream`.
@@ -115,7 +119,8 @@ extern "C" {
  * initial_states.
  *
  * Longer sequences take one of three kernel paths.  bf16 inputs with headdim
- * 64 and dstate 64 or 128 take, by default (see ssd_set_option), the chain
+ * 64 and dstate 64 or 128 take, by default (ssd_scan_fwd_path selects a path
+ * explicitly), the chain
  * path when each group holds an even number of heads and the head pairs fill
  * the machine: one kernel in which each workgroup carries a pair of heads of one
  * group through the whole sequence in 128-step blocks with the state held on
@@ -163,8 +168,7 @@ extern "C" {
  *   control 9 uint32: eight ticket counters, then an error word that is
  *          non-zero if a workgroup gave up waiting for its entering state
  *          (outputs are then invalid; it cannot happen unless the device
- *          stops making progress).  Its byte offset is
- *          ssd_scan_fwd_workspace_size(...) - 256 + 32.
+ *          stops making progress).  ssd_scan_fwd_wait_status reads it.
  * The workspace of one call must not be in use by another call at the same
  * time (true of both paths).
  */
@@ -176,11 +180,81 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
                  size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace ssd_scan_fwd needs for these sizes (0 for an empty
- * problem and for seqlen <= 16).  Returns 0 as well for arguments ssd_scan_fwd would reject;
- * pure host computation, no HIP call. */
+ * problem, for seqlen <= 16, on the chain path, and for arguments ssd_scan_fwd
+ * would reject); pure host computation, no HIP call.  The workspace holds
+ * the chunked form's intermediates: per-chunk states and the states entering
+ * each chunk, as the Mamba-1 CUDA forward on mamba issue #488 keeps its
+ * per-chunk scan intermediates in a buffer the caller receives. */
 size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
                                    int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
                                    int dtype);
+
+/*
+ * Kernel paths of ssd_scan_fwd_path (the path ssd_scan_fwd takes is
+ * SSD_PATH_AUTO).  They compute the same operation and differ only in
+ * rounding order; testing and measuring each path needs a way to ask for it
+ * by name, per call:
+ *   SSD_PATH_AUTO        the choice described at ssd_scan_fwd
+ *   SSD_PATH_STAGED      dt/cumsum, chunk state, state passing, chunk scan
+ *   SSD_PATH_FUSED       the fused bf16 path, kernel form chosen from the shape
+ *   SSD_PATH_FUSED_HEAD  fused, one workgroup per 128-step block and head
+ *   SSD_PATH_FUSED_GROUP fused, one workgroup per 128-step block, B/C group
+ *                        and set of up to 8 of its heads (packed-sequence
+ *                        calls run the per-head form)
+ *   SSD_PATH_CHAIN       the chain bf16 kernel (one workgroup per pair of
+ *                        heads of a group for the whole sequence)
+ * A path the shape cannot take falls back, always the same way: SSD_PATH_CHAIN
+ * with an odd number of heads per group takes the fused path; every fused or
+ * chain path takes the staged path unless the inputs are bf16 with headdim 64
+ * and dstate 64 or 128; seqlen <= 16 always takes the step kernel.  Any other
+ * value is SSD_ERR_INVALID_ARG.
+ */
+#define SSD_PATH_AUTO 0
+#define SSD_PATH_STAGED 1
+#define SSD_PATH_FUSED 2
+#define SSD_PATH_FUSED_HEAD 3
+#define SSD_PATH_FUSED_GROUP 4
+#define SSD_PATH_CHAIN 5
+
+/*
+ * ssd_scan_fwd_path -- ssd_scan_fwd on an explicitly chosen kernel path.
+ * Arguments as for ssd_scan_fwd_varlen, except that seq_idx may be NULL (one
+ * sequence per row, exactly ssd_scan_fwd), plus kernel_path (SSD_PATH_*).  The
+ * workspace is ssd_scan_fwd_path_workspace_size(..., varlen = seq_idx != NULL,
+ * kernel_path) bytes.  Stateless: the path is an argument, nothing is kept
+ * between calls.
+ */
+int ssd_scan_fwd_path(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                      const float* D, const void* z, const float* dt_bias, float dt_min,
+                      float dt_max, int chunk_size, int ngroups, const float* initial_states,
+                      void* out, float* final_states, const int32_t* seq_idx, int64_t batch,
+                      int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+                      int kernel_path, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Workspace bytes of ssd_scan_fwd_path (varlen: non-zero when seq_idx will
+ * be given).  0 for arguments the call would reject; pure host computation. */
+size_t ssd_scan_fwd_path_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                        int64_t headdim, int64_t dstate, int ngroups,
+                                        int chunk_size, int dtype, int varlen, int kernel_path);
+
+/*
+ * ssd_scan_fwd_wait_status -- whether the last call enqueued on `stream` with
+ * this workspace and these arguments (the sizes, dtype, varlen and path of
+ * that call; ssd_scan_fwd, ssd_scan_fwd_varlen and ssd_scan_fwd_timed are
+ * SSD_PATH_AUTO) completed its hand-offs.  It synchronizes `stream`.  On the
+ * fused path it reads the error word of the workspace's control region:
+ * SSD_OK, or SSD_ERR_WAIT when a workgroup gave up its bounded wait (then
+ * out and final_states of that call are invalid).  Other paths have no
+ * bounded wait and return SSD_OK after the synchronization.  SSD_ERR_HIP if
+ * the synchronization or the read fails; the shape checks of ssd_scan_fwd
+ * otherwise.  The word is cleared by the next call's set-up kernel, so
+ * query before enqueueing another call on the same workspace.
+ */
+int ssd_scan_fwd_wait_status(const void* workspace, size_t workspace_bytes, int64_t batch,
+                             int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                             int ngroups, int chunk_size, int dtype, int varlen, int kernel_path,
+                             hipStream_t stream);
 
 /*
  * Packed sequences: ssd_scan_fwd over batch rows that each hold several
@@ -199,7 +273,7 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
  * Every other argument, the checks and the execution rules are those of
  * ssd_scan_fwd; `out` must not overlap seq_idx either.  The call takes the
  * same path as ssd_scan_fwd (the chain and fused bf16 kernels count the
- * sequence starts themselves; with SSD_BF16_PATH_FUSED_GROUP the fused path
+ * sequence starts themselves; asked for SSD_PATH_FUSED_GROUP the fused path
  * runs its per-head form) and needs ssd_scan_fwd_varlen_workspace_size(...)
  * bytes of workspace: none on the chain path, on the fused path the fused
  * layout, on the staged path the staged layout
@@ -327,39 +401,17 @@ size_t ssd_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
                                    int64_t headdim, int64_t dstate, int ngroups, int chunk_size,
                                    int dtype);
 
-/* Static text for a status code ("unknown status" for others). */
+/* Static text for a status code ("unknown status" for others).  Every case
+ * the kernels do not cover gets a code of its own instead of a different
+ * result: mamba issue #647 shows a fused kernel that silently diverged for
+ * ngroups > 1 and asks whether that was "a not supported feature". */
 const char* ssd_status_string(int status);
 
-/* SSD_ABI_VERSION of the loaded library. */
+/* SSD_ABI_VERSION of the loaded library.  Mamba issue #488 shows a change of
+ * the positional signature of the CUDA forward breaking a second caller
+ * (MambaInnerFn); a caller checks this number against the header it was
+ * built with. */
 int ssd_abi_version(void);
-
-/*
- * Process-wide options.  SSD_OPT_BF16_PATH selects the kernel path of bf16
- * problems that the fused path covers: SSD_BF16_PATH_AUTO (default: the
- * chain kernel when the heads of a group pair up and the pairs, n = batch *
- * nheads / 2 workgroups, fill the 256 compute units: 4 n >= 3 * 256 *
- * ceil(n / 256); else fused), SSD_BF16_PATH_STAGED,
- * SSD_BF16_PATH_FUSED (fused, kernel form chosen from the shape),
- * SSD_BF16_PATH_FUSED_HEAD (one workgroup per 128-step block and head),
- * SSD_BF16_PATH_FUSED_GROUP (one workgroup per 128-step block, B/C group
- * and set of up to 8 of its heads) or SSD_BF16_PATH_CHAIN (one workgroup
- * per pair of heads of a group for the whole sequence, the state held on
- * chip, no workspace; shapes whose groups hold an odd number of heads take
- * the fused path).  The workspace size depends on
- * the path, so set options before querying it; do not change them while
- * another thread is between the query and the call.  ssd_set_option returns
- * SSD_OK or SSD_ERR_INVALID_ARG; ssd_get_option the value or
- * SSD_ERR_INVALID_ARG.  Host only, no HIP call.
- */
-#define SSD_OPT_BF16_PATH 1
-#define SSD_BF16_PATH_AUTO 0
-#define SSD_BF16_PATH_STAGED 1
-#define SSD_BF16_PATH_FUSED 2
-#define SSD_BF16_PATH_FUSED_HEAD 3
-#define SSD_BF16_PATH_FUSED_GROUP 4
-#define SSD_BF16_PATH_CHAIN 5
-int ssd_set_option(int option, int value);
-int ssd_get_option(int option);
 
 /*
  * Per-stage timing, for measurement.  A timing object holds HIP events;

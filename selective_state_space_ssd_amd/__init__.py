@@ -4,15 +4,16 @@ The scan runs in hand-written HIP kernels for gfx950 behind the C ABI of
 ``include/ssd.h`` (``libssd.so``, built in-tree); ``binding`` marshals torch
 tensors to it.
 """
-from .binding import (SSD_BF16, SSD_F32, STAGES, SsdError, Timing, abi_version,
-                      block_workspace_size, bwd_workspace_size, get_bf16_path, load_library,
-                      scan_bwd, scan_bwd_raw, scan_fwd, scan_fwd_raw, scan_fwd_varlen_raw,
-                      set_bf16_path, split_conv1d_scan_fwd, split_conv1d_scan_fwd_raw,
-                      status_string, varlen_workspace_size, workspace_size)
+from .binding import (KERNEL_PATHS, SSD_BF16, SSD_ERR_WAIT, SSD_F32, STAGES, SsdError, Timing,
+                      abi_version, block_workspace_size, bwd_workspace_size, load_library,
+                      path_code, scan_bwd, scan_bwd_raw, scan_fwd, scan_fwd_path_raw,
+                      scan_fwd_raw, scan_fwd_varlen_raw, split_conv1d_scan_fwd,
+                      split_conv1d_scan_fwd_raw, status_string, varlen_workspace_size,
+                      wait_status, workspace_size)
 
-__all__ = ["scan_fwd", "scan_fwd_raw", "scan_fwd_varlen_raw", "scan_bwd", "scan_bwd_raw",
-           "bwd_workspace_size", "split_conv1d_scan_fwd",
+__all__ = ["scan_fwd", "scan_fwd_raw", "scan_fwd_path_raw", "scan_fwd_varlen_raw", "scan_bwd",
+           "scan_bwd_raw", "bwd_workspace_size", "split_conv1d_scan_fwd",
            "split_conv1d_scan_fwd_raw", "workspace_size", "varlen_workspace_size",
-           "block_workspace_size", "status_string", "abi_version", "load_library",
-           "set_bf16_path", "get_bf16_path", "Timing", "SsdError", "SSD_F32", "SSD_BF16",
-           "STAGES"]
+           "block_workspace_size", "wait_status", "status_string", "abi_version",
+           "load_library", "path_code", "KERNEL_PATHS", "Timing", "SsdError", "SSD_F32",
+           "SSD_BF16", "SSD_ERR_WAIT", "STAGES"]

@@ -20,9 +20,10 @@ SSD_F32 = 0
 SSD_BF16 = 1
 SSD_NUM_STAGES = 4
 STAGES = ("prep", "chunk_state", "state_passing", "chunk_scan")
-SSD_OPT_BF16_PATH = 1
-BF16_PATHS = {"auto": 0, "staged": 1, "fused": 2, "fused_head": 3, "fused_group": 4,
-              "chain": 5}
+# Kernel paths of ssd_scan_fwd_path (SSD_PATH_* in include/ssd.h)
+KERNEL_PATHS = {"auto": 0, "staged": 1, "fused": 2, "fused_head": 3, "fused_group": 4,
+                "chain": 5}
+SSD_ERR_WAIT = -6
 
 _lib = None
 
@@ -59,6 +60,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_scan_fwd_varlen.restype = i
     lib.ssd_scan_fwd_varlen_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i]
     lib.ssd_scan_fwd_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_scan_fwd_path.argtypes = fwd_args[:15] + [p] + fwd_args[15:21] + [i] + fwd_args[21:]
+    lib.ssd_scan_fwd_path.restype = i
+    lib.ssd_scan_fwd_path_workspace_size.argtypes = [i64, i64, i64, i64, i64, i, i, i, i, i]
+    lib.ssd_scan_fwd_path_workspace_size.restype = ctypes.c_size_t
+    lib.ssd_scan_fwd_wait_status.argtypes = [p, ctypes.c_size_t, i64, i64, i64, i64, i64, i, i,
+                                             i, i, i, p]
+    lib.ssd_scan_fwd_wait_status.restype = i
     lib.ssd_split_conv1d_scan_fwd.argtypes = (
         [p, p, p, p, p, p, i, p, f, f, p, f, i64, i, i, p, p, i64, i64, i64, i64, i, i, p,
          ctypes.c_size_t, p])
@@ -77,10 +85,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
     lib.ssd_abi_version.restype = i
-    lib.ssd_set_option.argtypes = [i, i]
-    lib.ssd_set_option.restype = i
-    lib.ssd_get_option.argtypes = [i]
-    lib.ssd_get_option.restype = i
     lib.ssd_timing_create.argtypes = [ctypes.POINTER(p)]
     lib.ssd_timing_create.restype = i
     lib.ssd_timing_destroy.argtypes = [p]
@@ -99,30 +103,50 @@ def abi_version() -> int:
     return int(load_library().ssd_abi_version())
 
 
-def set_bf16_path(name: str) -> str:
-    """Select the kernel path of bf16 problems ("auto", "staged", "fused",
-    "fused_head", "fused_group" or "chain", process-wide); returns the
-    previous setting."""
+def path_code(name: str) -> int:
+    """SSD_PATH_* code of a kernel path name ("auto", "staged", "fused",
+    "fused_head", "fused_group" or "chain")."""
+    if name not in KERNEL_PATHS:
+        raise ValueError(f"unknown kernel path {name!r}; one of {sorted(KERNEL_PATHS)}")
+    return KERNEL_PATHS[name]
+
+
+def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
+                   kernel_path: str = "auto") -> int:
+    """Workspace bytes of a call on kernel path ``kernel_path``."""
     lib = load_library()
-    prev = {v: k for k, v in BF16_PATHS.items()}[lib.ssd_get_option(SSD_OPT_BF16_PATH)]
-    _check(lib.ssd_set_option(SSD_OPT_BF16_PATH, BF16_PATHS[name]))
-    return prev
-
-
-def get_bf16_path() -> str:
-    return {v: k for k, v in BF16_PATHS.items()}[load_library().ssd_get_option(SSD_OPT_BF16_PATH)]
-
-
-def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype) -> int:
-    return int(load_library().ssd_scan_fwd_workspace_size(
-        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+    if kernel_path == "auto":
+        return int(lib.ssd_scan_fwd_workspace_size(
+            batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+    return int(lib.ssd_scan_fwd_path_workspace_size(
+        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, 0,
+        path_code(kernel_path)))
 
 
 def varlen_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
-                          dtype) -> int:
+                          dtype, kernel_path: str = "auto") -> int:
     """Workspace bytes of a packed-sequence (seq_idx) call."""
-    return int(load_library().ssd_scan_fwd_varlen_workspace_size(
-        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+    lib = load_library()
+    if kernel_path == "auto":
+        return int(lib.ssd_scan_fwd_varlen_workspace_size(
+            batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype))
+    return int(lib.ssd_scan_fwd_path_workspace_size(
+        batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, 1,
+        path_code(kernel_path)))
+
+
+def wait_status(workspace_ptr, workspace_bytes, batch, seqlen, nheads, headdim, dstate, ngroups,
+                chunk_size, dtype, varlen=False, kernel_path: str = "auto", stream=None) -> int:
+    """ssd_scan_fwd_wait_status: synchronizes ``stream`` (torch's current one by
+    default) and returns SSD_OK (0) or SSD_ERR_WAIT when a fused-path
+    workgroup of the last call on this workspace gave up waiting."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().ssd_scan_fwd_wait_status(
+        workspace_ptr, int(workspace_bytes), int(batch), int(seqlen), int(nheads), int(headdim),
+        int(dstate), int(ngroups), int(chunk_size), int(dtype), 1 if varlen else 0,
+        path_code(kernel_path), stream))
 
 
 def block_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
@@ -179,6 +203,20 @@ def scan_fwd_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, 
     if timing is None:
         return int(lib.ssd_scan_fwd(*args))
     return int(lib.ssd_scan_fwd_timed(*args, timing.handle))
+
+
+def scan_fwd_path_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min,
+                      dt_max, chunk_size, ngroups, init_ptr, out_ptr, final_ptr, seq_ptr, batch,
+                      seqlen, nheads, headdim, dstate, dtype, kernel_path, ws_ptr, ws_bytes,
+                      stream) -> int:
+    """Direct call of ``ssd_scan_fwd_path`` (``kernel_path`` a name or an
+    SSD_PATH_* code; ``seq_ptr`` may be None); returns the status."""
+    code = path_code(kernel_path) if isinstance(kernel_path, str) else int(kernel_path)
+    return int(load_library().ssd_scan_fwd_path(
+        x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, float(dt_min),
+        float(dt_max), int(chunk_size), int(ngroups), init_ptr, out_ptr, final_ptr, seq_ptr,
+        int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(dtype), code, ws_ptr,
+        int(ws_bytes), stream))
 
 
 def scan_fwd_varlen_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min,
@@ -336,7 +374,7 @@ def split_conv1d_scan_fwd(zxbcdt, conv1d_weight, conv1d_bias, dt_bias, A, D, chu
 def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.inf),
              chunk_size: int = 128, initial_states=None, return_final_states: bool = False,
              out=None, final_states=None, workspace=None, timing: Optional[Timing] = None,
-             seq_idx=None):
+             seq_idx=None, kernel_path: str = "auto"):
     """SSD chunked selective-scan forward on the GPU.
 
     x [b, L, H, P], dt [b, L, H], B/C [b, L, G, N], z like x: float32 or
@@ -346,7 +384,8 @@ def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.i
     (uint8) may be given to avoid allocations; ``final_states`` may be the
     ``initial_states`` tensor itself (in-place continuation).  ``seq_idx``
     [b, L] int32 packs several sequences per row (the state resets where the
-    label changes; ``ssd_scan_fwd_varlen``)."""
+    label changes; ``ssd_scan_fwd_varlen``).  ``kernel_path`` names the
+    kernel path ("auto" is ssd_scan_fwd's own choice; ``ssd_scan_fwd_path``)."""
     import torch
 
     load_library()
@@ -393,16 +432,26 @@ def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.i
             raise ValueError("seq_idx must be a contiguous tensor on x's device")
         if timing is not None:
             raise ValueError("per-stage timing is not offered for seq_idx calls")
+    code = path_code(kernel_path)
+    if code != 0 and timing is not None:
+        raise ValueError("per-stage timing is offered on the automatic path only")
 
     if out is None:
         out = torch.empty_like(x)
     if return_final_states and final_states is None:
         final_states = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
     size_fn = workspace_size if seq_idx is None else varlen_workspace_size
-    ws_bytes = size_fn(b, L, H, P, N, G, chunk_size, dtype)
+    ws_bytes = size_fn(b, L, H, P, N, G, chunk_size, dtype, kernel_path)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if code != 0:
+        _check(scan_fwd_path_raw(
+            _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+            dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),
+            _ptr(final_states) if return_final_states else None, _ptr(seq_idx), b, L, H, P, N,
+            dtype, code, _ptr(workspace), workspace.numel(), stream))
+        return (out, final_states) if return_final_states else out
     if seq_idx is not None:
         _check(scan_fwd_varlen_raw(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),

@@ -47,12 +47,10 @@ struct Layout {
   // fused bf16 path
   size_t off_ring = 0, off_flags = 0, off_ctl = 0;
   size_t total = 0;
+  int path = SSD_PATH_AUTO;  // the kernel path the call asked for (SSD_PATH_*)
 };
 
 constexpr int64_t kMaxRowElems = ((int64_t)1 << 32) / (256 * 4);
-
-// Process-wide options (ssd_set_option).
-int g_bf16_path = SSD_BF16_PATH_AUTO;
 
 // The staged bf16 matrix-core kernels (same rule as ssd::use_bf16_kernels).
 bool bf16_path(int dtype, int64_t dstate, int chunk_size) {
@@ -60,29 +58,34 @@ bool bf16_path(int dtype, int64_t dstate, int chunk_size) {
          (dstate == 64 || dstate == 128);
 }
 
-// The fused bf16 kernel (same rule as ssd::use_fused_bf16, plus the option).
-bool fused_path(int dtype, int64_t headdim, int64_t dstate) {
+// The fused bf16 kernel (same rule as ssd::use_fused_bf16), unless the call
+// asks for the staged path.
+bool fused_path(int dtype, int64_t headdim, int64_t dstate, int path) {
   return dtype == SSD_BF16 && headdim == 64 && (dstate == 64 || dstate == 128) &&
-         g_bf16_path != SSD_BF16_PATH_STAGED;
+         path != SSD_PATH_STAGED;
 }
 
-// The chain bf16 kernel: asked for, or chosen by default when the head pairs
-// fill the machine (same shape rule as ssd::use_chain_bf16, plus the option).
+// The chain bf16 kernel: asked for, or chosen by SSD_PATH_AUTO when the head
+// pairs fill the machine (same shape rule as ssd::use_chain_bf16).
 bool chain_path(int dtype, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
-                int ngroups) {
+                int ngroups, int path) {
   const bool shape = dtype == SSD_BF16 && headdim == 64 && (dstate == 64 || dstate == 128) &&
                      (nheads / ngroups) % 2 == 0;
   if (!shape) return false;
-  if (g_bf16_path == SSD_BF16_PATH_CHAIN) return true;
-  return g_bf16_path == SSD_BF16_PATH_AUTO && ssd::chain_fills_machine(batch, nheads);
+  if (path == SSD_PATH_CHAIN) return true;
+  return path == SSD_PATH_AUTO && ssd::chain_fills_machine(batch, nheads);
 }
+
+bool path_valid(int path) { return path >= SSD_PATH_AUTO && path <= SSD_PATH_CHAIN; }
 
 // Shape checks shared by the workspace query and the entry point.
 // varlen: the call carries seq_idx (packed sequences).  On the staged path its
 // workspace ends with the per-chunk sequence-start counts; the fused bf16
 // kernel counts the starts itself.
 int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
-                 int ngroups, int chunk_size, int dtype, bool varlen, Layout* lay) {
+                 int ngroups, int chunk_size, int dtype, bool varlen, int path, Layout* lay) {
+  if (!path_valid(path)) return SSD_ERR_INVALID_ARG;
+  lay->path = path;
   if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
       chunk_size <= 0)
     return SSD_ERR_INVALID_ARG;
@@ -114,12 +117,12 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     lay->total = 0;
     return SSD_OK;
   }
-  if (chain_path(dtype, batch, nheads, headdim, dstate, ngroups) && seqlen > 0 && batch > 0) {
+  if (chain_path(dtype, batch, nheads, headdim, dstate, ngroups, path) && seqlen > 0 && batch > 0) {
     lay->chain = true;
     lay->total = 0;
     return SSD_OK;
   }
-  if (fused_path(dtype, headdim, dstate) && seqlen > 0 && batch > 0) {
+  if (fused_path(dtype, headdim, dstate, path) && seqlen > 0 && batch > 0) {
     const int64_t nblk = ssd::fused_blocks(seqlen);
     int64_t nchain, grid, ringn, flagn;
     if (!mul_ok(batch, nheads, &nchain) || !mul_ok(nchain, nblk, &grid) ||
@@ -170,10 +173,10 @@ int validate(const void* x, const void* dt, const float* A, const void* B, const
              const float* D, const void* z, const float* dt_bias, float dt_min, float dt_max,
              int chunk_size, int ngroups, const float* initial_states, void* out,
              float* final_states, const int32_t* seq_idx, bool varlen, int64_t batch,
-             int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+             int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype, int path,
              void* workspace, size_t workspace_bytes, Layout* lay) {
   int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, varlen,
-                        lay);
+                        path, lay);
   if (st != SSD_OK) return st;
   if (std::isnan(dt_min) || std::isnan(dt_max) || dt_min > dt_max) return SSD_ERR_INVALID_ARG;
   if (!A) return SSD_ERR_INVALID_ARG;
@@ -188,25 +191,34 @@ int validate(const void* x, const void* dt, const float* A, const void* B, const
       !aligned(C, 16) || !aligned(dt, es) || !aligned(initial_states, 16) ||
       !aligned(final_states, 16))
     return SSD_ERR_ALIGNMENT;
-  // overlap rules: out against every input; final against init (equal is fine)
+  // Overlap rules: out and final_states are written while inputs are still
+  // being read (a later workgroup may read a row or an initial state that an
+  // earlier one has already overwritten), so neither may overlap any input,
+  // the other output or the workspace -- except that final_states may be
+  // exactly initial_states (each element is read before it is written).
   const int64_t nx = batch * seqlen * nheads * headdim;
   const int64_t nbc = batch * seqlen * ngroups * dstate;
   const int64_t nst = batch * nheads * headdim * dstate;
-  if (nonempty) {
-    const Span so = span(out, nx * (int64_t)es);
-    const Span ins[] = {span(x, nx * (int64_t)es), span(dt, batch * seqlen * nheads * (int64_t)es),
-                        span(B, nbc * (int64_t)es), span(C, nbc * (int64_t)es),
-                        z ? span(z, nx * (int64_t)es) : Span{0, 0},
-                        seq_idx ? span(seq_idx, batch * seqlen * 4) : Span{0, 0}};
-    for (const Span& s : ins)
-      if (s.hi > s.lo && overlap(so, s)) return SSD_ERR_INVALID_ARG;
-    if (final_states && overlap(so, span(final_states, nst * 4))) return SSD_ERR_INVALID_ARG;
-    if (lay->total > 0 && overlap(so, span(workspace, (int64_t)lay->total)))
-      return SSD_ERR_INVALID_ARG;
-  }
-  if (final_states && initial_states && final_states != initial_states &&
-      overlap(span(final_states, nst * 4), span(initial_states, nst * 4)))
-    return SSD_ERR_INVALID_ARG;
+  const Span none{0, 0};
+  const Span sx = nonempty ? span(x, nx * (int64_t)es) : none;
+  const Span sdt = nonempty ? span(dt, batch * seqlen * nheads * (int64_t)es) : none;
+  const Span sB = nonempty ? span(B, nbc * (int64_t)es) : none;
+  const Span sC = nonempty ? span(C, nbc * (int64_t)es) : none;
+  const Span sz = nonempty && z ? span(z, nx * (int64_t)es) : none;
+  const Span sseq = nonempty && seq_idx ? span(seq_idx, batch * seqlen * 4) : none;
+  const Span sA = span(A, nheads * 4);
+  const Span sD = D ? span(D, nheads * 4) : none;
+  const Span sbias = dt_bias ? span(dt_bias, nheads * 4) : none;
+  const Span sinit = initial_states ? span(initial_states, nst * 4) : none;
+  const Span sws = lay->total > 0 && workspace ? span(workspace, (int64_t)lay->total) : none;
+  const Span so = nonempty ? span(out, nx * (int64_t)es) : none;
+  const Span sfin = final_states ? span(final_states, nst * 4) : none;
+  auto hits = [](Span a, Span b) { return a.hi > a.lo && b.hi > b.lo && overlap(a, b); };
+  for (const Span& s : {sx, sdt, sB, sC, sz, sseq, sA, sD, sbias, sinit, sws, sfin})
+    if (hits(so, s)) return SSD_ERR_INVALID_ARG;
+  for (const Span& s : {sx, sdt, sB, sC, sz, sseq, sA, sD, sbias, sws})
+    if (hits(sfin, s)) return SSD_ERR_INVALID_ARG;
+  if (final_states != initial_states && hits(sfin, sinit)) return SSD_ERR_INVALID_ARG;
   // the workspace is checked last: a call that gets past it launches kernels
   if (lay->total > 0) {
     if (!workspace || workspace_bytes < lay->total) return SSD_ERR_WORKSPACE;
@@ -226,7 +238,7 @@ int block_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                  int ngroups, int chunk_size, int dtype, int conv_width, int norm_groups,
                  BlockLayout* bl) {
   int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
-                        &bl->scan);
+                        SSD_PATH_AUTO, &bl->scan);
   if (st != SSD_OK) return st;
   if (!ssd::block_supported(nheads * headdim, norm_groups, conv_width)) return SSD_ERR_UNSUPPORTED;
   // grids: the prologue tiles time by 32 steps (y dimension <= 65535), the
@@ -267,7 +279,7 @@ int bwd_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, i
                int ngroups, int chunk_size, int dtype, BwdLayout* bl) {
   Layout lay;
   int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
-                        &lay);
+                        SSD_PATH_AUTO, &lay);
   if (st != SSD_OK) return st;
   if (!ssd::config_supported(headdim, dstate, 64)) return SSD_ERR_UNSUPPORTED;
   const int64_t nb = ssd::bwd_blocks(seqlen);
@@ -316,11 +328,12 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
                int chunk_size, int ngroups, const float* initial_states, void* out,
                float* final_states, const int32_t* seq_idx, bool varlen, int64_t batch,
                int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
-               void* workspace, size_t workspace_bytes, hipStream_t stream, ssd_timing* timing) {
+               int path, void* workspace, size_t workspace_bytes, hipStream_t stream,
+               ssd_timing* timing) {
   Layout lay;
   int st = validate(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups,
                     initial_states, out, final_states, seq_idx, varlen, batch, seqlen, nheads,
-                    headdim, dstate, dtype, workspace, workspace_bytes, &lay);
+                    headdim, dstate, dtype, path, workspace, workspace_bytes, &lay);
   if (st != SSD_OK) return st;
   if (batch == 0) return SSD_OK;
 
@@ -343,9 +356,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.fs_ring = lay.fused ? reinterpret_cast<float*>(ws + lay.off_ring) : nullptr;
   p.fs_flags = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_flags) : nullptr;
   p.fs_ctl = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_ctl) : nullptr;
-  p.fused_kind = g_bf16_path == SSD_BF16_PATH_FUSED_HEAD    ? 1
-                 : g_bf16_path == SSD_BF16_PATH_FUSED_GROUP ? 2
-                                                            : 0;
+  p.fused_kind = path == SSD_PATH_FUSED_HEAD ? 1 : path == SSD_PATH_FUSED_GROUP ? 2 : 0;
 
   auto mark = [&](int i) -> bool {
     return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
@@ -411,7 +422,7 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
                  size_t workspace_bytes, hipStream_t stream) {
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
              out, final_states, nullptr, false, batch, seqlen, nheads, headdim, dstate, dtype,
-             workspace, workspace_bytes, stream, nullptr);
+             SSD_PATH_AUTO, workspace, workspace_bytes, stream, nullptr);
 }
 
 int ssd_scan_fwd_varlen(const void* x, const void* dt, const float* A, const void* B,
@@ -423,7 +434,48 @@ int ssd_scan_fwd_varlen(const void* x, const void* dt, const float* A, const voi
                         size_t workspace_bytes, hipStream_t stream) {
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
              out, final_states, seq_idx, true, batch, seqlen, nheads, headdim, dstate, dtype,
-             workspace, workspace_bytes, stream, nullptr);
+             SSD_PATH_AUTO, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssd_scan_fwd_path(const void* x, const void* dt, const float* A, const void* B, const void* C,
+                      const float* D, const void* z, const float* dt_bias, float dt_min,
+                      float dt_max, int chunk_size, int ngroups, const float* initial_states,
+                      void* out, float* final_states, const int32_t* seq_idx, int64_t batch,
+                      int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype,
+                      int kernel_path, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
+             out, final_states, seq_idx, seq_idx != nullptr, batch, seqlen, nheads, headdim,
+             dstate, dtype, kernel_path, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t ssd_scan_fwd_path_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                        int64_t headdim, int64_t dstate, int ngroups,
+                                        int chunk_size, int dtype, int varlen, int kernel_path) {
+  Layout lay;
+  if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
+                   varlen != 0, kernel_path, &lay) != SSD_OK)
+    return 0;
+  return lay.total;
+}
+
+int ssd_scan_fwd_wait_status(const void* workspace, size_t workspace_bytes, int64_t batch,
+                             int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                             int ngroups, int chunk_size, int dtype, int varlen, int kernel_path,
+                             hipStream_t stream) {
+  Layout lay;
+  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
+                        varlen != 0, kernel_path, &lay);
+  if (st != SSD_OK) return st;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SSD_ERR_HIP;
+  if (!lay.fused || lay.total == 0) return SSD_OK;  // no bounded wait on this path
+  if (!workspace || workspace_bytes < lay.total) return SSD_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SSD_ERR_ALIGNMENT;
+  unsigned word = 0;
+  const char* src = static_cast<const char*>(workspace) + lay.off_ctl + ssd::kFusedErrorWordByte;
+  if (hipMemcpy(&word, src, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return SSD_ERR_HIP;
+  return word == 0 ? SSD_OK : SSD_ERR_WAIT;
 }
 
 int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void* B,
@@ -436,7 +488,7 @@ int ssd_scan_fwd_timed(const void* x, const void* dt, const float* A, const void
   if (!timing) return SSD_ERR_INVALID_ARG;
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
              out, final_states, nullptr, false, batch, seqlen, nheads, headdim, dstate, dtype,
-             workspace, workspace_bytes, stream, timing);
+             SSD_PATH_AUTO, workspace, workspace_bytes, stream, timing);
 }
 
 int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
@@ -497,7 +549,7 @@ int ssd_split_conv1d_scan_fwd(const void* zxbcdt, const float* conv1d_weight,
   // normalises it in place
   st = run(q.x, q.dt, A, q.B, q.C, D, nullptr, dt_bias, dt_min, dt_max, chunk_size, ngroups,
            initial_states, out, final_states, nullptr, false, batch, seqlen, nheads, headdim,
-           dstate, dtype, nonempty ? ws + bl.off_scan : nullptr,
+           dstate, dtype, SSD_PATH_AUTO, nonempty ? ws + bl.off_scan : nullptr,
            nonempty ? workspace_bytes - bl.off_scan : 0, stream, nullptr);
   if (st != SSD_OK) return st;
   if (nonempty && ssd::launch_gated_rmsnorm(q, stream) != hipSuccess) return SSD_ERR_HIP;
@@ -671,7 +723,7 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
                                    int dtype) {
   Layout lay;
   if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
-                   &lay) != SSD_OK)
+                   SSD_PATH_AUTO, &lay) != SSD_OK)
     return 0;
   return lay.total;
 }
@@ -681,7 +733,7 @@ size_t ssd_scan_fwd_varlen_workspace_size(int64_t batch, int64_t seqlen, int64_t
                                           int chunk_size, int dtype) {
   Layout lay;
   if (check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, true,
-                   &lay) != SSD_OK)
+                   SSD_PATH_AUTO, &lay) != SSD_OK)
     return 0;
   return lay.total;
 }
@@ -694,23 +746,12 @@ const char* ssd_status_string(int status) {
     case SSD_ERR_ALIGNMENT: return "misaligned pointer";
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_HIP: return "HIP launch failure";
+    case SSD_ERR_WAIT: return "a workgroup gave up waiting for its entering state";
     default: return "unknown status";
   }
 }
 
 int ssd_abi_version(void) { return SSD_ABI_VERSION; }
-
-int ssd_set_option(int option, int value) {
-  if (option != SSD_OPT_BF16_PATH) return SSD_ERR_INVALID_ARG;
-  if (value < SSD_BF16_PATH_AUTO || value > SSD_BF16_PATH_CHAIN) return SSD_ERR_INVALID_ARG;
-  g_bf16_path = value;
-  return SSD_OK;
-}
-
-int ssd_get_option(int option) {
-  if (option != SSD_OPT_BF16_PATH) return SSD_ERR_INVALID_ARG;
-  return g_bf16_path;
-}
 
 int ssd_timing_create(ssd_timing** out) {
   if (!out) return SSD_ERR_INVALID_ARG;

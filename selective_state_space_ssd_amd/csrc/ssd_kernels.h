@@ -88,6 +88,10 @@ hipError_t launch_bf16_stage(const Problem& p, hipStream_t stream, int stage);
 // kernel, stage 1 the scan.  Blocks of 128 timesteps whatever Q is.
 bool use_fused_bf16(const Problem& p);
 int64_t fused_blocks(int64_t L);
+// Byte offset, inside fs_ctl, of the error word both fused kernels set when a
+// workgroup gives up its bounded wait (after the eight ticket counters); the
+// set-up kernel clears it on every call.
+constexpr size_t kFusedErrorWordByte = 8 * sizeof(unsigned);
 hipError_t launch_fused_bf16(const Problem& p, hipStream_t stream, int stage);
 
 // Chain bf16 kernel (bf16 inputs, P 64, N 64/128, an even number of heads

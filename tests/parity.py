@@ -13,15 +13,28 @@ import selective_state_space_ssd_amd as ssd
 TOL = {"f32": 1e-3, "bf16": 2e-2}
 
 
+# The kernel path the enclosed test calls ask for: a setting of these test
+# helpers, passed to every call as its kernel_path argument (the library keeps
+# no state).
+_PATH = ["auto"]
+
+
 @contextmanager
 def bf16_path(name):
-    """Run the enclosed calls with the bf16 kernel path `name` ("chain",
-    "fused", "fused_head", "fused_group", "staged" or "auto")."""
-    prev = ssd.set_bf16_path(name)
+    """Run the enclosed run_gpu calls on kernel path `name` ("chain", "fused",
+    "fused_head", "fused_group", "staged" or "auto")."""
+    ssd.path_code(name)  # reject unknown names here
+    prev = _PATH[0]
+    _PATH[0] = name
     try:
         yield
     finally:
-        ssd.set_bf16_path(prev)
+        _PATH[0] = prev
+
+
+def current_path():
+    """The kernel path bf16_path set for the enclosing block."""
+    return _PATH[0]
 
 
 def paths_for(dtype):
@@ -58,6 +71,7 @@ def upload(inp, dtype):
 
 
 def run_gpu(t, chunk_size, dt_limit=(0.0, float("inf")), init=None, final=True, **kw):
+    kw.setdefault("kernel_path", current_path())
     res = ssd.scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                        dt_bias=t["dt_bias"], dt_limit=dt_limit, chunk_size=chunk_size,
                        initial_states=init, return_final_states=final, **kw)

@@ -19,7 +19,7 @@ import selective_state_space_ssd_amd as ssd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP, WAIT = 0, -1, -2, -3, -4, -5, -6
 
 
 def declared_functions():
@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("ssd_scan_fwd", "ssd_scan_fwd_workspace_size", "ssd_status_string",
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
-                 "ssd_timing_read", "ssd_timing_destroy", "ssd_set_option", "ssd_get_option",
+                 "ssd_timing_read", "ssd_timing_destroy", "ssd_scan_fwd_path",
+                 "ssd_scan_fwd_path_workspace_size", "ssd_scan_fwd_wait_status",
                  "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size",
                  "ssd_split_conv1d_scan_fwd", "ssd_split_conv1d_scan_fwd_workspace_size",
                  "ssd_scan_bwd", "ssd_scan_bwd_workspace_size"):
@@ -50,15 +51,15 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ssd.abi_version() == 1
+    assert ssd.abi_version() == 2
     assert ssd.status_string(0) == "ok"
-    seen = {ssd.status_string(s) for s in (INVALID, UNSUPPORTED, ALIGN, WORKSPACE, -5)}
-    assert len(seen) == 5 and "unknown status" not in seen
+    seen = {ssd.status_string(s) for s in (INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP, WAIT)}
+    assert len(seen) == 6 and "unknown status" not in seen
     assert ssd.status_string(12345) == "unknown status"
 
 
-def _ws(b, L, H, P, N, G, Q, dt=0):
-    return ssd.workspace_size(b, L, H, P, N, G, Q, dt)
+def _ws(b, L, H, P, N, G, Q, dt=0, path="auto"):
+    return ssd.workspace_size(b, L, H, P, N, G, Q, dt, path)
 
 
 DECODE_MAX_L = 16  # sequences this short take the step-by-step kernel
@@ -95,21 +96,18 @@ SIZES = [(2, 2048, 32, 64, 128, 1, 128), (1, 300, 4, 64, 16, 1, 64),
 
 
 def test_workspace_size_formula():
-    prev = ssd.set_bf16_path("staged")
-    try:
-        for (b, L, H, P, N, G, Q) in SIZES:
-            nc = math.ceil(L / Q)
-            want = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
-            if L <= DECODE_MAX_L:
-                assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
-                continue
-            assert _ws(b, L, H, P, N, G, Q) == want + _gram(b, L, H, N, G, Q, False)
-            # intermediates are fp32 for bf16 too; the staged bf16 matrix-core
-            # kernels (chunk 128/256, dstate 64/128) add B^T per (chunk, group)
-            bt = _r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
-            assert _ws(b, L, H, P, N, G, Q, 1) == want + bt + _gram(b, L, H, N, G, Q, True)
-    finally:
-        ssd.set_bf16_path(prev)
+    for (b, L, H, P, N, G, Q) in SIZES:
+        nc = math.ceil(L / Q)
+        want = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
+        if L <= DECODE_MAX_L:
+            assert _ws(b, L, H, P, N, G, Q, 0, "staged") == 0
+            assert _ws(b, L, H, P, N, G, Q, 1, "staged") == 0
+            continue
+        assert _ws(b, L, H, P, N, G, Q, 0, "staged") == want + _gram(b, L, H, N, G, Q, False)
+        # intermediates are fp32 for bf16 too; the staged bf16 matrix-core
+        # kernels (chunk 128/256, dstate 64/128) add B^T per (chunk, group)
+        bt = _r(b * nc * G * N * Q * 2) if (Q in (128, 256) and N in (64, 128)) else 0
+        assert _ws(b, L, H, P, N, G, Q, 1, "staged") == want + bt + _gram(b, L, H, N, G, Q, True)
 
 
 def _fused_ws(b, L, H, P, N):
@@ -128,27 +126,27 @@ def _chain_fills(b, H):
 
 def test_workspace_size_fused_bf16():
     """Fused bf16 path (dstate 64/128), asked for explicitly."""
-    prev = ssd.set_bf16_path("fused")
-    try:
+    for path in ("fused", "fused_head", "fused_group"):
         for (b, L, H, P, N, G, Q) in SIZES:
             nc = math.ceil(L / Q)
             staged = 2 * _r(b * H * nc * Q * 4) + 2 * _r(b * nc * H * P * N * 4)
             if L <= DECODE_MAX_L:  # short sequences: the step-by-step kernel, no workspace
-                assert _ws(b, L, H, P, N, G, Q) == 0 and _ws(b, L, H, P, N, G, Q, 1) == 0
+                assert _ws(b, L, H, P, N, G, Q, 0, path) == 0
+                assert _ws(b, L, H, P, N, G, Q, 1, path) == 0
                 continue
             # fp32 is always staged
-            assert _ws(b, L, H, P, N, G, Q) == staged + _gram(b, L, H, N, G, Q, False)
+            assert _ws(b, L, H, P, N, G, Q, 0, path) == staged + _gram(b, L, H, N, G, Q, False)
             want = _fused_ws(b, L, H, P, N) if N in (64, 128) else staged  # dstate 16/32: staged
-            assert _ws(b, L, H, P, N, G, Q, 1) == want
-    finally:
-        ssd.set_bf16_path(prev)
+            if want == staged:
+                bt = _r(b * nc * G * N * Q * 2) if Q in (128, 256) else 0
+                want += bt + _gram(b, L, H, N, G, Q, True)
+            assert _ws(b, L, H, P, N, G, Q, 1, path) == want
 
 
 def test_workspace_size_default_bf16():
     """Default bf16 path: the chain kernel (no workspace) when the heads of a
     group pair up and the pairs fill the machine, else the fused layout; the
     chain option takes the chain kernel whenever the heads pair up."""
-    assert ssd.get_bf16_path() == "auto"
     cases = SIZES + [(8, 4096, 64, 64, 128, 64, 256), (4, 1000, 64, 64, 64, 2, 128),
                      (2, 1000, 6, 64, 128, 2, 128), (6, 1000, 64, 64, 128, 8, 128),
                      (5, 1000, 64, 64, 128, 8, 128), (1, 65536, 128, 64, 128, 8, 256),
@@ -159,12 +157,10 @@ def test_workspace_size_default_bf16():
         pairs_up = (H // G) % 2 == 0
         chain = pairs_up and _chain_fills(b, H)
         assert _ws(b, L, H, P, N, G, Q, 1) == (0 if chain else _fused_ws(b, L, H, P, N))
-        prev = ssd.set_bf16_path("chain")
-        try:
-            assert _ws(b, L, H, P, N, G, Q, 1) == (0 if pairs_up else _fused_ws(b, L, H, P, N))
-            assert _ws(b, L, H, P, N, G, Q, 0) > 0  # fp32 stays staged
-        finally:
-            ssd.set_bf16_path(prev)
+        assert _ws(b, L, H, P, N, G, Q, 1, "auto") == _ws(b, L, H, P, N, G, Q, 1)
+        assert (_ws(b, L, H, P, N, G, Q, 1, "chain")
+                == (0 if pairs_up else _fused_ws(b, L, H, P, N)))
+        assert _ws(b, L, H, P, N, G, Q, 0, "chain") > 0  # fp32 stays staged
     assert _ws(8, 4096, 64, 64, 128, 8, 256, 1) == 0  # the bf16 8 x 4096 workload: chain
     assert _ws(1, 65536, 128, 64, 128, 8, 256, 1) > 0  # the 1 x 65536 one: 64 pairs, fused
     assert _chain_fills(6, 64) and not _chain_fills(5, 64)  # 192 of 256 / 160 of 256
@@ -186,30 +182,54 @@ def test_workspace_size_varlen():
                 continue
             if dt and N in (64, 128):
                 assert got == _ws(b, L, H, P, N, G, Q, 1)  # as the plain call
-                prev = ssd.set_bf16_path("staged")
-                try:
-                    got = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, dt)
-                finally:
-                    ssd.set_bf16_path(prev)
+                got = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, dt, "staged")
             bt = _r(b * nc * G * N * Q * 2) if (dt and Q in (128, 256) and N in (64, 128)) else 0
             assert got == staged + bt + _gram(b, L, H, N, G, Q, dt) + _r(b * nc * Q * 4)
     assert ssd.varlen_workspace_size(2, 100, 4, 64, 16, 3, 64, 0) == 0  # rejected shapes
 
 
-def test_options():
+def test_kernel_path_argument():
+    """The path is an argument of each call: out-of-range codes are rejected,
+    and asking for one path leaves every later query unchanged."""
     lib = ssd.load_library()
-    assert lib.ssd_get_option(1) == 0
-    assert lib.ssd_set_option(1, 6) == INVALID
-    assert lib.ssd_set_option(1, -1) == INVALID
-    assert lib.ssd_set_option(2, 0) == INVALID
-    assert lib.ssd_get_option(2) == INVALID
-    prev = ssd.set_bf16_path("fused")
-    assert prev == "auto" and ssd.get_bf16_path() == "fused"
-    assert ssd.set_bf16_path(prev) == "fused" and ssd.get_bf16_path() == "auto"
+    for bad in (-1, 6, 99):
+        assert lib.ssd_scan_fwd_path_workspace_size(2, 300, 8, 64, 128, 2, 128, 1, 0, bad) == 0
+    before = _ws(1, 65536, 128, 64, 128, 8, 256, 1)
+    assert _ws(1, 65536, 128, 64, 128, 8, 256, 1, "chain") == 0
+    assert _ws(1, 65536, 128, 64, 128, 8, 256, 1, "staged") > before
+    assert _ws(1, 65536, 128, 64, 128, 8, 256, 1) == before
+    with pytest.raises(ValueError):
+        ssd.path_code("fastest")
     assert _ws(0, 100, 4, 64, 16, 1, 64) == 0
     assert _ws(2, 0, 4, 64, 16, 1, 64) == 0
     assert _ws(2, 100, 4, 64, 16, 3, 64) == 0       # rejected: 3 does not divide 4
     assert _ws(2, 100, 4, 32, 16, 1, 64) == 0       # rejected: headdim 32 not compiled
+
+
+def test_no_mutable_globals_in_the_abi(tmp_path):
+    """The C ABI keeps no state between calls: compiled on its own,
+    ssd_api.hip defines no writable data symbol besides the HIP runtime's
+    registration handles and the scratch of the allocation-free entry point
+    (the array itself and its per-device address table, filled once per
+    device)."""
+    import shutil
+    import subprocess
+    from selective_state_space_ssd_amd import _build
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    obj = tmp_path / "ssd_api.o"
+    subprocess.run([_build.hipcc(), *_build.CFLAGS, "-c",
+                    os.path.join(_build.CSRC, "ssd_api.hip"), "-o", str(obj)], check=True,
+                   capture_output=True)
+    out = subprocess.run(["nm", "-C", str(obj)], check=True, capture_output=True,
+                         text=True).stdout
+    data = []
+    for line in out.splitlines():
+        parts = line.split(None, 2)
+        if len(parts) == 3 and parts[1] in "bBdDcCgGsS":
+            data.append(parts[2])
+    mutable = [d for d in data if not d.startswith("__hip_") and "scratch" not in d]
+    assert mutable == [], mutable
 
 
 # A base argument set with distinct, 256-byte-aligned fake addresses.
@@ -273,6 +293,18 @@ CASES = [
     ("out overlaps B", dict(out=0x40000000), INVALID),
     ("out overlaps final", dict(final=0xA0000000 + 1024), INVALID),
     ("final partially overlaps init", dict(final=0x90000000 + 4096), INVALID),
+    ("out overlaps initial_states", dict(out=0x90000000 + 512), INVALID),
+    ("out overlaps A", dict(out=0x30000000 - 256), INVALID),
+    ("out overlaps D", dict(out=0x60000000 - 64), INVALID),
+    ("out overlaps dt_bias", dict(out=0x80000000 - 16), INVALID),
+    ("out overlaps workspace", dict(ws=0xA0000000 + 4096, ws_bytes=16), INVALID),
+    ("final overlaps x", dict(final=0x10000000 + 1024), INVALID),
+    ("final overlaps dt", dict(final=0x20000000 - 256), INVALID),
+    ("final overlaps B", dict(final=0x40000000), INVALID),
+    ("final overlaps C", dict(final=0x50000000 + 16), INVALID),
+    ("final overlaps z", dict(final=0x70000000 + 4096), INVALID),
+    ("final overlaps A", dict(final=0x30000000 - 16), INVALID),
+    ("final overlaps workspace", dict(ws=0xB0000000 - 256, ws_bytes=512), INVALID),
     ("no workspace", dict(), WORKSPACE),
     ("workspace too small", dict(ws=0xC0000000, ws_bytes=1024), WORKSPACE),
     ("final aliases init exactly (valid, stops at workspace)", dict(final=0x90000000),
@@ -288,6 +320,41 @@ CASES = [
 def test_rejected_before_launch(desc, changes, want):
     assert want != OK
     assert call(**changes) == want
+
+
+def call_path(path, seq=None, **changes):
+    a = dict(BASE)
+    a.update(changes)
+    return ssd.scan_fwd_path_raw(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                 a["dt_bias"], a["dt_min"], a["dt_max"], a["chunk_size"],
+                                 a["ngroups"], a["init"], a["out"], a["final"], seq, a["batch"],
+                                 a["seqlen"], a["nheads"], a["headdim"], a["dstate"], a["dtype"],
+                                 path, a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_path_entry_point_rejections():
+    """ssd_scan_fwd_path validates like ssd_scan_fwd, and the path code too."""
+    for bad in (-1, 6, 1000):
+        assert call_path(bad) == INVALID
+    for name, code in ssd.KERNEL_PATHS.items():
+        assert call_path(code) == WORKSPACE, name            # valid, stops at workspace
+        assert call_path(code, ngroups=3) == INVALID, name
+        assert call_path(code, x=0x10000004) == ALIGN, name
+    bf = dict(dtype=1, dstate=128, chunk_size=256, seqlen=1000, nheads=8, ngroups=2)
+    need = ssd.workspace_size(1, 1000, 8, 64, 128, 2, 256, 1, "fused_head")
+    assert need > 0
+    assert call_path(3, ws=0xC0000000, ws_bytes=need - 1, **bf) == WORKSPACE
+    # seq_idx on the path entry point: packed-sequence rules apply
+    assert call_path(0, seq=0xD0000002) == ALIGN
+
+
+def test_wait_status_rejections_without_gpu():
+    """Shape and path checks come before any HIP call."""
+    lib = ssd.load_library()
+    assert lib.ssd_scan_fwd_wait_status(None, 0, 1, 100, 4, 64, 16, 3, 64, 0, 0, 0, None) == INVALID
+    assert lib.ssd_scan_fwd_wait_status(None, 0, 1, 100, 4, 64, 16, 1, 64, 0, 0, 9, None) == INVALID
+    assert lib.ssd_scan_fwd_wait_status(None, 0, 1, 100, 4, 32, 16, 1, 64, 0, 0, 0, None) == \
+        UNSUPPORTED
 
 
 def call_varlen(seq=0xD0000000, **changes):

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, bf16_path, compare, log, np64, run_gpu, upload
+from parity import TOL, bf16_path, compare, current_path, log, np64, run_gpu, upload
 from ssd_workloads import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def test_chain_block_edges(L, N, H, G):
     w, inp, t = _inputs(700 + L + N, 2, L, H, N, G)
     log(f"test_chain_block_edges L={L} N={N} H={H} G={G}")
     with bf16_path("chain"):
-        assert ssd.workspace_size(2, L, H, 64, N, G, 256, ssd.SSD_BF16) == 0
+        assert ssd.workspace_size(2, L, H, 64, N, G, 256, ssd.SSD_BF16, current_path()) == 0
         out, fin = run_gpu(t, 256, init=t["initial_states"])
     ref, rfin = _oracle(inp)
     compare("out", np64(out), ref, TOL["bf16"])
@@ -114,7 +114,7 @@ def test_chain_odd_heads_per_group_falls_back():
     fused path (with its workspace) and still matches the oracle."""
     w, inp, t = _inputs(750, 2, 400, 6, 128, 2)
     with bf16_path("chain"):
-        assert ssd.workspace_size(2, 400, 6, 64, 128, 2, 256, ssd.SSD_BF16) > 0
+        assert ssd.workspace_size(2, 400, 6, 64, 128, 2, 256, ssd.SSD_BF16, current_path()) > 0
         out, fin = run_gpu(t, 256, init=t["initial_states"])
     ref, rfin = _oracle(inp)
     compare("out", np64(out), ref, TOL["bf16"])

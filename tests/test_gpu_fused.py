@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, bf16_path, compare, log, np64, run_gpu, upload
+from parity import TOL, bf16_path, compare, current_path, log, np64, run_gpu, upload
 from ssd_workloads import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -18,9 +18,11 @@ pytestmark = pytest.mark.gpu
 KINDS = ("fused_head", "fused_group")
 
 
-def _error_word(ws):
-    # control region = the last 256 bytes: 8 ticket counters, then the error word
-    return int(ws[ws.numel() - 256 + 32:ws.numel() - 256 + 36].view(torch.int32).item())
+def _wait_status(ws, b, L, H, N, G):
+    """The fused path's bounded-wait status of the last call on `ws`, read
+    through the C ABI (ssd_scan_fwd_wait_status)."""
+    return ssd.wait_status(ws.data_ptr(), ws.numel(), b, L, H, 64, N, G, 256, ssd.SSD_BF16,
+                           kernel_path=current_path())
 
 
 def _inputs(seed, b=2, L=700, H=8, N=128, G=4, init=True):
@@ -38,12 +40,12 @@ def test_fused_reuse_and_error_word(kind, b, L, H, N, G):
     w, inp, t = _inputs(600 + L, b, L, H, N, G)
     log(f"test_fused_reuse {kind} b={b} L={L} H={H} N={N} G={G}")
     with bf16_path(kind):
-        ws = torch.empty(ssd.workspace_size(b, L, H, 64, N, G, 256, 1), dtype=torch.uint8,
-                         device=t["x"].device)
+        ws = torch.empty(ssd.workspace_size(b, L, H, 64, N, G, 256, 1, current_path()),
+                         dtype=torch.uint8, device=t["x"].device)
         o1, f1 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
-        assert _error_word(ws) == 0
+        assert _wait_status(ws, b, L, H, N, G) == 0
         o2, f2 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
-        assert _error_word(ws) == 0
+        assert _wait_status(ws, b, L, H, N, G) == 0
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
     ref, rfin = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
                                z=inp["z"], dt_bias=inp["dt_bias"],
@@ -93,12 +95,12 @@ def test_fused_repeat_bitwise(kind):
     visible would make a call differ."""
     w, inp, t = _inputs(630, b=4, L=2048, H=32, N=128, G=8)
     with bf16_path(kind):
-        ws = torch.empty(ssd.workspace_size(4, 2048, 32, 64, 128, 8, 256, 1), dtype=torch.uint8,
-                         device=t["x"].device)
+        ws = torch.empty(ssd.workspace_size(4, 2048, 32, 64, 128, 8, 256, 1, current_path()),
+                         dtype=torch.uint8, device=t["x"].device)
         o0, f0 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
         for k in range(12):
             o, f = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
-            assert _error_word(ws) == 0
+            assert _wait_status(ws, 4, 2048, 32, 128, 8) == 0
             assert torch.equal(o, o0) and torch.equal(f, f0), k
     mask = np.zeros((4, 32), bool)
     mask[[0, 1, 3], [5, 17, 31]] = True

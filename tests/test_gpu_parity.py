@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, bf16_path, compare, log, np64, paths_for, run_gpu, upload, ws_regions
+from parity import (TOL, bf16_path, compare, current_path, log, np64, paths_for, run_gpu, upload,
+                    ws_regions)
 from ssd_workloads import WORKLOADS, Workload, make_inputs, small
 
 pytestmark = pytest.mark.gpu
@@ -83,7 +84,8 @@ def test_stage_intermediates(dtype, Q, N):
     inp = make_inputs(w)
     t = upload(inp, dtype)
     with bf16_path("staged"):  # the intermediates live in the staged path's workspace
-        ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0),
+        ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0,
+                                           current_path()),
                          dtype=torch.uint8, device=t["x"].device)
         run_gpu(t, Q, init=t["initial_states"], workspace=ws)
     got = {k: np64(v) for k, v in ws_regions(ws, b, L, H, P, N, Q).items()}

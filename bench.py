@@ -1,26 +1,26 @@
 """Throughput of the SSD scan forward on one MI355X.
 
-One step = one pass of the whole scan (dt/cumsum, chunk state, state passing,
-chunk scan with the D/z epilogue) over the fp32 workload batch 2 x seqlen
-2048, 32 heads of 64, dstate 128, chunk 128, at ngroups 1, 2 and 4: three
-ssd_scan_fwd calls, 3 x 4096 tokens.  Inputs are seeded, synthetic and
-resident in HBM before timing starts; two copies of every input rotate across
-steps so that consecutive steps touch more memory than the 256 MB Infinity
-Cache holds.
+One step = one ssd_scan_fwd call (the whole hot path: dt/cumsum, chunk state,
+state passing, chunk scan with the D/z epilogue) over the long bf16 workload:
+batch 1 x seqlen 65536, 128 heads of 64, dstate 128, 8 B/C groups, chunk
+256, D on, z off (65536 tokens per step).  Inputs are seeded, synthetic and
+resident in HBM before timing starts (one call touches 2.4 GB, ten times the
+256 MB Infinity Cache).
 
-Prints one JSON line: tokens/s over the timed steps, the roofline of the
-dominant kernel (its algorithmic flops per launch over its mean launch time,
-measured with HIP events recorded by the library on the launch stream), the
-CPU oracle's throughput on the same workload, and (unless --no-bf16) three
-more workloads: bf16 batch 8 x seqlen 4096 and a one-token bf16 decode step
-(batch 128, state in place), against the HBM roofline, and the fp32 batch 2 x
-seqlen 2048 shape holding packed sequences (seq_idx), against the fp32
-matrix roofline, and the block around the scan (conv1d prologue, gated RMSNorm
-epilogue) at the fp32 2 x 2048 size, its prologue and epilogue against the HBM
-roofline, and the backward (every gradient) of the fp32 2 x 2048 workload
-against the fp32 matrix roofline.
+Prints one JSON line: tokens/s over exactly `--steps` back-to-back calls, the
+per-call median and minimum from HIP events (a second pass), the roofline of
+the dominant kernel (its algorithmic bytes per launch over its mean launch
+time, from events the library records around each stage on the launch
+stream -- a third pass), its HBM traffic from committed rocprofv3 counter
+summaries, the machine's measured peaks next to the datasheet ones, the CPU
+oracle on a bounded sample of the same workload, and (unless --no-others) a
+line per further workload: the other four scan configurations (fp32 1 x 256;
+fp32 2 x 2048 at ngroups 1, 2, 4; bf16 8 x 4096; fp32 4 x 8192 as four
+chained 2048-step segments), packed sequences, one-token decode, the block
+around the scan and the backward.
 """
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -32,44 +32,37 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from ssd_workloads import BENCH_WORKLOADS, WORKLOADS, make_inputs, make_seq_idx  # noqa: E402
+from ssd_workloads import WORKLOADS, make_inputs, make_seq_idx  # noqa: E402
 
-PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
-PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak (datasheet)
+PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (datasheet)
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E (datasheet)
+
+HEADLINE = "bf16_b1_L65536_H128_P64_N128_G8_Q256"
+TRAFFIC_DIR = os.path.join(ROOT, "profiles", "traffic")
+CSRC = os.path.join(ROOT, "selective_state_space_ssd_amd", "csrc")
+MIN_CALLS = 30
 
 
-# Kernel sources whose counters the committed traffic summary describes.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_scan_group_f32_b2_L2048_traffic.json")
-
-
-def measured_traffic(kernel_stage):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None when there is none or the kernel's
-    sources have changed since the counters were taken."""
-    import json
-    if kernel_stage != "chunk_scan" or not os.path.exists(TRAFFIC_FILE):
-        return None
-    from rocprof_summary import sources_hash
-    t = json.load(open(TRAFFIC_FILE))
-    csrc = os.path.join(ROOT, "selective_state_space_ssd_amd", "csrc")
-    if sources_hash([os.path.join(csrc, n) for n in t["sources"]]) != t["sources_sha256_16"]:
-        return None
-    return t["bytes_per_dispatch"]
-
+# --------------------------------------------------------------------------
+# algorithmic work
+# --------------------------------------------------------------------------
 
 def alg_flops(w):
     """Algorithmic flops of one call, by stage (chunked SSD, causal, C.B^T once
     per group): chunk state 2QPN per (chunk, head); state passing 2PN per
     (chunk, head); chunk scan 2QPN + PQ(Q+1) per (chunk, head); C.B^T NQ(Q+1)
     per (chunk, group), in the stage that forms it: the state-passing launch
-    when the four-heads chunk scan runs with two or more of its workgroups per
-    group (it reads the tiles from there), else the chunk scan."""
+    when the fp32 four-heads chunk scan runs with two or more of its
+    workgroups per group (it reads the tiles from there), else the chunk
+    scan."""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    if w.segments > 1:
+        L //= w.segments
     nc = math.ceil(L / Q)
     gram = b * nc * G * N * Q * (Q + 1)
     group_scan = (Q in (64, 128) and N in (64, 128) and (H // G) % 4 == 0 and H // G >= 8
-                  and not (w.dtype == "bf16" and Q == 128))
+                  and w.dtype == "f32")
     return {
         "prep": b * L * H * 2.0,
         "chunk_state": b * nc * H * 2.0 * Q * P * N,
@@ -79,111 +72,321 @@ def alg_flops(w):
 
 
 def alg_bytes(w):
-    """Bytes the method must move: read x, dt, B, C, (z), (init), A, D, dt_bias;
-    write out, (final).  Intermediates are not counted."""
+    """Bytes one call must move: read x, dt, B, C, (z), (init), A, D, dt_bias;
+    write out, (final).  Intermediates are not counted.  For a continuation
+    workload, one segment call."""
     b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    if w.segments > 1:
+        L //= w.segments
     es = 2 if w.dtype == "bf16" else 4
     n = b * L * H * P * es * (2 + (1 if w.gate else 0))     # x, out, z
     n += b * L * H * es + 2 * b * L * G * N * es              # dt, B, C
     n += 3 * H * 4
     st = b * H * P * N * 4
-    n += st * ((1 if w.init else 0) + (1 if w.final else 0))
+    n += st * ((1 if (w.init or w.segments > 1) else 0) + (1 if w.final else 0))
     return n
 
 
-def cpu_baseline(workloads, min_seconds=10.0):
-    """The oracle (untuned fp64 recurrence, OpenMP over batch x heads) on the
-    whole step, repeated until at least `min_seconds` have passed."""
-    import oracle
-    inputs = [make_inputs(w) for w in workloads]
-    threads = oracle.max_threads()
-    tokens, elapsed, passes = 0, 0.0, 0
-    while elapsed < min_seconds:
-        for w, inp in zip(workloads, inputs):
-            t0 = time.perf_counter()
-            oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
-                           z=inp["z"], dt_bias=inp["dt_bias"])
-            elapsed += time.perf_counter() - t0
-            tokens += w.tokens
-        passes += 1
-    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} full step(s): ngroups 1, 2, 4 at batch 2 x seqlen 2048 "
-                      f"({tokens} tokens, {elapsed:.1f} s, fp64 recurrence)",
-            "cpu": _cpu_model()}
+# --------------------------------------------------------------------------
+# measured peaks and counter summaries
+# --------------------------------------------------------------------------
 
-
-def bf16_kernel(ssd, workspace_bytes):
-    """The kernel a bf16 call takes: the chain kernel needs no workspace."""
-    opt = ssd.get_bf16_path()
-    if workspace_bytes == 0:
-        return "chain"
-    return opt if opt != "auto" else "fused"
-
-
-def bf16_workload(steps, warmup, name="bf16_b8_L4096_H64_P64_N128_G8_Q256"):
-    """The bf16 workload (batch 8 x seqlen 4096, 64 heads, 8 groups, chunk 256,
-    z and D on, final states returned) on the default bf16 path: calls per
-    second over `steps` calls after `warmup`, with the algorithmic bytes of a
-    call over its mean duration against the HBM peak."""
+def measured_peaks(dev):
+    """Streaming-copy HBM rate and matrix-core rates, from libssd_peaks.so
+    (selective_state_space_ssd_amd/csrc/ssd_peaks.hip), timed with events."""
     import torch
-    import selective_state_space_ssd_amd as ssd
-    w = WORKLOADS[name]
-    dev = torch.device("cuda:0")
-    inp = make_inputs(w)
-    t = {"z": None, "D": None}
-    for k in ("x", "z", "B", "C", "dt"):
-        if k in inp["bits"]:
-            t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
-    for k in ("A", "D", "dt_bias"):
-        if inp.get(k) is not None:
-            t[k] = torch.from_numpy(inp[k]).to(dev)
-    del inp
-    out = torch.empty_like(t["x"])
-    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
-    wsz = ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
-                             w.chunk_size, ssd.SSD_BF16)
-    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
-    ptr = lambda v: None if v is None else v.data_ptr()
-    a = (t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(),
-         t["C"].data_ptr(), ptr(t["D"]), ptr(t["z"]), t["dt_bias"].data_ptr(), 0.0,
-         math.inf, w.chunk_size, w.ngroups, None, out.data_ptr(), fin.data_ptr(), w.batch,
-         w.seqlen, w.nheads, w.headdim, w.dstate, ssd.SSD_BF16, ws.data_ptr(), wsz)
-    s = torch.cuda.current_stream(dev).cuda_stream
+    from selective_state_space_ssd_amd import _build
+    lib = ctypes.CDLL(_build.PEAKS_LIB_PATH)
+    p = ctypes.c_void_p
+    lib.ssd_peak_copy.argtypes = [p, p, ctypes.c_size_t, p]
+    lib.ssd_peak_copy.restype = ctypes.c_int
+    lib.ssd_peak_mfma.argtypes = [p, ctypes.c_int, ctypes.c_int, ctypes.c_int, p]
+    lib.ssd_peak_mfma.restype = ctypes.c_int
+    lib.ssd_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.ssd_peak_mfma_flops.restype = ctypes.c_double
+    s = torch.cuda.current_stream(dev)
 
-    def call():
-        st = ssd.scan_fwd_raw(*a, s)
-        if st != 0:
-            raise ssd.SsdError(st, ssd.status_string(st))
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        best = math.inf
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            fn()
+            b.record(s)
+            b.synchronize()
+            best = min(best, a.elapsed_time(b) / 1e3)
+        return best
 
-    for _ in range(warmup):
-        call()
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def copy():
+        if lib.ssd_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, s.cuda_stream) != 0:
+            raise RuntimeError("ssd_peak_copy failed")
+
+    t = timed(copy, 5)
+    assert torch.equal(dst[:1024], src[:1024])
+    del src, dst
+    res = {"hbm_copy_GBs": 2 * nbytes / t / 1e9,
+           "hbm_copy_note": "1 GiB read + 1 GiB written per launch, best of 5"}
+    wgs, iters = 256 * 8, 2000
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    for kind, name in ((0, "fp32_32x32x2"), (3, "fp32_16x16x4"), (1, "bf16_32x32x16"),
+                       (2, "bf16_16x16x32")):
+        def run():
+            if lib.ssd_peak_mfma(sink.data_ptr(), kind, wgs, iters, s.cuda_stream) != 0:
+                raise RuntimeError("ssd_peak_mfma failed")
+        t = timed(run, 3)
+        res[f"mfma_{name}_TFLOPs"] = lib.ssd_peak_mfma_flops(kind, wgs, iters) / t / 1e12
+    return res
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of the kernel of `stage` on `workload`, from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
+    (profiles/traffic/<workload>.<stage>.json, written by rocprof_summary.py
+    --traffic), or None when there is none or the kernel's sources have
+    changed since the counters were taken."""
+    path = os.path.join(TRAFFIC_DIR, f"{workload}.{stage}.json")
+    if not os.path.exists(path):
+        return None
+    from rocprof_summary import sources_hash
+    t = json.load(open(path))
+    if sources_hash([os.path.join(CSRC, n) for n in t["sources"]]) != t["sources_sha256_16"]:
+        return None
+    return {"bytes_per_launch": t["bytes_per_dispatch"], "kernel": t["kernel"],
+            "fetch_factor": t["fetch_factor"], "write_factor": t["write_factor"]}
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+
+def time_calls(call, n, warmup, dev, n_events=None):
+    """`warmup` untimed calls, then exactly `n` back-to-back calls timed by the
+    host clock between two synchronizations, then `n_events` (default: `n`,
+    at least 30) more calls each bracketed by HIP events on the launch stream.
+    Returns wall seconds per call and the events' median, min and mean in ms."""
+    import torch
+    s = torch.cuda.current_stream(dev)
+    for k in range(warmup):
+        call(k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
+    for k in range(n):
+        call(k)
     torch.cuda.synchronize()
-    el = (time.perf_counter() - t0) / steps
-    nbytes = alg_bytes(w)
+    wall = (time.perf_counter() - t0) / n
+    ne = max(n if n_events is None else n_events, MIN_CALLS)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(ne)]
+    for k in range(ne):
+        evs[k][0].record(s)
+        call(k)
+        evs[k][1].record(s)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"wall_s_per_call": wall, "median_ms": float(np.median(ms)),
+            "min_ms": float(ms.min()), "mean_ms": float(ms.mean()), "calls": n,
+            "event_calls": ne}
+
+
+# --------------------------------------------------------------------------
+# the scan workloads
+# --------------------------------------------------------------------------
+
+class ScanWorkload:
+    """Device copies of a workload's inputs (`copies` of them, rotated call by
+    call) and the calls of the scan on the automatic path."""
+
+    def __init__(self, w, dev, copies=1, inp=None):
+        import torch
+        import selective_state_space_ssd_amd as ssd
+        self.w, self.dev = w, dev
+        self.code = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
+        L = w.seqlen // w.segments
+        self.seg_len = L
+        self.path = ssd.taken_path(w.batch, L, w.nheads, w.headdim, w.dstate, w.ngroups,
+                                   w.chunk_size, self.code)
+        self.ws_bytes = ssd.workspace_size(w.batch, L, w.nheads, w.headdim, w.dstate,
+                                           w.ngroups, w.chunk_size, self.code)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.sets = []
+        for c in range(copies):
+            src = inp if (inp is not None and c == 0) else make_inputs(w)
+            t = {}
+            for k in ("x", "z", "B", "C", "dt"):
+                if src.get(k) is None:
+                    t[k] = None
+                elif w.dtype == "bf16":
+                    t[k] = torch.from_numpy(src["bits"][k].view(np.int16)).to(dev).view(
+                        torch.bfloat16)
+                else:
+                    t[k] = torch.from_numpy(src[k]).to(dev)
+            for k in ("A", "D", "dt_bias", "initial_states"):
+                t[k] = None if src.get(k) is None else torch.from_numpy(src[k]).to(dev)
+            t["out"] = torch.empty_like(t["x"])
+            st_shape = (w.batch, w.nheads, w.headdim, w.dstate)
+            t["state"] = (torch.zeros(st_shape, dtype=torch.float32, device=dev)
+                          if (w.final or w.segments > 1) else None)
+            self.sets.append(t)
+
+    def _args(self, t, seg):
+        w, ptr = self.w, (lambda v: None if v is None else v.data_ptr())
+        L = self.seg_len
+        lo = seg * L
+
+        def sl(v):
+            return None if v is None else v[:, lo:lo + L] if w.segments > 1 else v
+
+        x, dt, B, C, z, out = (sl(t[k]) for k in ("x", "dt", "B", "C", "z", "out"))
+        if w.segments > 1:  # a segment's slice of [b, L, ...] is not contiguous: use copies
+            x, dt, B, C, out = (t.setdefault(f"seg{seg}_{k}", v.contiguous())
+                                for k, v in (("x", x), ("dt", dt), ("B", B), ("C", C),
+                                             ("out", out)))
+            z = None if z is None else t.setdefault(f"seg{seg}_z", z.contiguous())
+        init = t["state"] if (w.segments > 1 and seg > 0) else t["initial_states"]
+        return (ptr(x), ptr(dt), ptr(t["A"]), ptr(B), ptr(C), ptr(t["D"]), ptr(z),
+                ptr(t["dt_bias"]), 0.0, math.inf, w.chunk_size, w.ngroups, ptr(init), ptr(out),
+                ptr(t["state"]), w.batch, L, w.nheads, w.headdim, w.dstate, self.code,
+                self.ws.data_ptr(), self.ws_bytes)
+
+    def prepare(self):
+        """Argument tuples per (copy, segment)."""
+        self.argv = [[self._args(t, s) for s in range(self.w.segments)] for t in self.sets]
+
+    def call(self, k, timing=None):
+        import torch
+        import selective_state_space_ssd_amd as ssd
+        s = torch.cuda.current_stream(self.dev).cuda_stream
+        for seg, a in enumerate(self.argv[k % len(self.argv)]):
+            st = ssd.scan_fwd_raw(*a, s, timing=None if timing is None else timing[seg])
+            if st != 0:
+                raise ssd.SsdError(st, ssd.status_string(st))
+
+
+def describe(w):
+    opts = []
+    opts.append("z gate on" if w.gate else "z off")
+    opts.append("D on" if w.skip else "D off")
+    if w.final:
+        opts.append("final states returned")
+    seg = (f" as {w.segments} chained segments of {w.seqlen // w.segments} (initial state = "
+           "the previous segment's final state, in place)" if w.segments > 1 else "")
+    return (f"ssd_scan_fwd {w.dtype} batch {w.batch} x seqlen {w.seqlen}{seg}, {w.nheads} heads "
+            f"x headdim {w.headdim}, dstate {w.dstate}, ngroups {w.ngroups}, chunk "
+            f"{w.chunk_size}, {', '.join(opts)}")
+
+
+STAGE_KERNELS = {
+    "staged": {"prep": "dt_cumsum_kernel", "chunk_state": "chunk_state kernel",
+               "state_passing": "state_passing_kernel", "chunk_scan": "chunk scan kernel"},
+    "chain": {"chunk_scan": "chain_scan_bf16_kernel"},
+    "fused_head": {"prep": "fused set-up kernel", "chunk_scan": "fused_scan_bf16_kernel"},
+    "fused_group": {"prep": "fused set-up kernel", "chunk_scan": "fused_group_bf16_kernel"},
+}
+
+
+def scan_line(names, dev, steps, warmup, peaks, copies=1, inp=None):
+    """One line for a step made of the scan calls of `names` (one workload,
+    or several run back to back as one step): tokens/s, per-step median and
+    min, the dominant kernel's roofline and the whole call's fractions of
+    both rooflines."""
+    import selective_state_space_ssd_amd as ssd
+    works = [ScanWorkload(WORKLOADS[n], dev, copies, inp if i == 0 else None)
+             for i, n in enumerate(names)]
+    for sw in works:
+        sw.prepare()
+    import torch
+    step = lambda k: [sw.call(k) for sw in works]
+    tm = time_calls(step, steps, warmup, dev)
+    n = tm["event_calls"]
+    # per-stage launch times: a third pass with events the library records
+    # around each stage on the launch stream
+    launches_per_step = sum(sw.w.segments for sw in works)
+    stage_ms = np.zeros(len(ssd.STAGES))
+    for k in range(n):
+        tms = [[ssd.Timing() for _ in range(sw.w.segments)] for sw in works]
+        for sw, t in zip(works, tms):
+            sw.call(k, t)
+        torch.cuda.synchronize()
+        stage_ms += np.sum([t.read() for row in tms for t in row], axis=0) / n
+    dom = int(np.argmax(stage_ms))
+    stage = ssd.STAGES[dom]
+    w0 = works[0].w
+    bf16 = w0.dtype == "bf16"
+    tokens = sum(sw.w.tokens for sw in works)
+    step_s = tm["wall_s_per_call"]
+    fl = [alg_flops(sw.w) for sw in works]
+    segs = [sw.w.segments for sw in works]
+    dom_flops = sum(f[stage] * s for f, s in zip(fl, segs))
+    path_flops = sum(sum(f.values()) * s for f, s in zip(fl, segs))
+    path_bytes = sum(alg_bytes(sw.w) * sw.w.segments for sw in works)
+    dom_s = stage_ms[dom] / 1e3
+    mean_launch_s = dom_s / launches_per_step
+    if bf16:  # HBM-bound (flop per byte below the bf16 ridge): the call's bytes
+        ach = path_bytes / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS,
+                "frac_of_measured_peak": ach / peaks["hbm_copy_GBs"] if peaks else None,
+                "alg_bytes_per_launch": path_bytes / launches_per_step}
+    else:     # fp32 matrix-bound: the stage's flops
+        ach = dom_flops / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_FP32_MFMA_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_FP32_MFMA_TFLOPS,
+                "frac_of_measured_peak": (ach / peaks["mfma_fp32_32x32x2_TFLOPs"]
+                                          if peaks else None),
+                "alg_flops_per_launch": dom_flops / launches_per_step}
+    traffic = measured_traffic(names[0], stage) if len(names) == 1 else None
+    roof.update({"kernel": STAGE_KERNELS.get(works[0].path, {}).get(stage, stage),
+                 "stage": stage, "path": works[0].path,
+                 "traffic": traffic["bytes_per_launch"] if traffic else None,
+                 "traffic_source": (f"profiles/traffic/{names[0]}.{stage}.json" if traffic
+                                    else None),
+                 "launches_timed": n * launches_per_step,
+                 "mean_launch_us": mean_launch_s * 1e6})
+    peak_fl = (PEAK_BF16_MFMA_TFLOPS if bf16 else PEAK_FP32_MFMA_TFLOPS) * 1e12
+    t_hbm, t_mfma = path_bytes / (PEAK_HBM_GBS * 1e9), path_flops / peak_fl
     return {
-        "workload": "ssd_scan_fwd bf16 batch 8 x seqlen 4096, 64 heads x headdim 64, dstate "
-                    "128, ngroups 8, chunk 256, z gate and D on, final states returned",
-        "path": bf16_kernel(ssd, wsz),
-        "tokens_per_s": w.tokens / el,
-        "ms_per_call": el * 1e3,
-        "calls": steps,
-        "roofline": {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
-                     "alg_bytes": nbytes},
+        "workload": " + ".join(describe(sw.w) for sw in works),
+        "names": list(names),
+        "path": works[0].path,
+        "tokens_per_step": tokens,
+        "tokens_per_s": tokens / step_s,
+        "ms_per_step": step_s * 1e3,
+        "ms_per_step_events": {k: tm[k] for k in ("median_ms", "min_ms", "mean_ms")},
+        "steps_timed": tm["calls"],
+        "steps_timed_events": n,
+        "roofline": roof,
+        "call": {"alg_bytes": path_bytes, "alg_flops": path_flops,
+                 "hbm_frac": t_hbm / step_s, "mfma_frac": t_mfma / step_s,
+                 "binding": "hbm" if t_hbm >= t_mfma else "mfma",
+                 "binding_frac": max(t_hbm, t_mfma) / step_s,
+                 "stage_us_per_step": {s: float(stage_ms[i] * 1e3)
+                                       for i, s in enumerate(ssd.STAGES)}},
     }
 
 
-def decode_workload(steps, warmup, batch=128, nheads=64, dstate=128, ngroups=8):
+# --------------------------------------------------------------------------
+# further workloads (packed sequences, decode, block, backward)
+# --------------------------------------------------------------------------
+
+def _line_timing(tm):
+    return {"us_per_call": tm["wall_s_per_call"] * 1e6,
+            "us_per_call_events": {k.replace("_ms", "_us"): tm[k] * 1e3
+                                   for k in ("median_ms", "min_ms", "mean_ms")},
+            "calls": tm["calls"]}
+
+
+def decode_workload(dev, warmup, batch=128, nheads=64, dstate=128, ngroups=8):
     """One-token decode steps (bf16 inputs, fp32 state updated in place, z and D
     on): the short-sequence kernel.  Bound by reading and writing the state, so
     the roofline is HBM on the state bytes plus the token's inputs."""
     import torch
     import selective_state_space_ssd_amd as ssd
-    dev = torch.device("cuda:0")
     P = 64
     g = torch.Generator(device="cpu").manual_seed(11)
 
@@ -203,113 +406,78 @@ def decode_workload(steps, warmup, batch=128, nheads=64, dstate=128, ngroups=8):
          out.data_ptr(), state.data_ptr(), batch, 1, nheads, P, dstate, ssd.SSD_BF16, None, 0)
     s = torch.cuda.current_stream(dev).cuda_stream
 
-    def call():
+    def call(k):
         st = ssd.scan_fwd_raw(*a, s)
         if st != 0:
             raise ssd.SsdError(st, ssd.status_string(st))
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    el = (time.perf_counter() - t0) / steps
+    tm = time_calls(call, 100, warmup, dev)
+    el = tm["median_ms"] / 1e3
     nbytes = 2 * batch * nheads * P * dstate * 4 + batch * (
         3 * nheads * P * 2 + nheads * 2 + 2 * ngroups * dstate * 2)
     return {
         "workload": f"one-token decode, bf16 inputs, batch {batch}, {nheads} heads x headdim 64, "
                     f"dstate {dstate}, ngroups {ngroups}, z and D on, fp32 state in place",
-        "tokens_per_s": batch / el,
-        "us_per_call": el * 1e6,
-        "calls": steps,
-        "roofline": {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
-                     "alg_bytes": nbytes},
+        "path": "step", "tokens_per_s": batch / tm["wall_s_per_call"], **_line_timing(tm),
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": nbytes / el / 1e9,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
+                     "alg_bytes": nbytes, "time": "median of the per-call events"},
     }
 
 
-def varlen_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mean_len=256):
-    """Packed sequences (seq_idx) on the fp32 batch 2 x seqlen 2048 shape: each row
-    holds sequences of mean length `mean_len` (uniform lengths 1 .. 2*mean-1).
-    Calls alternate between two input copies, like the main measurement; the
-    same calls without seq_idx are timed alongside.  The chunked form does the
-    same work with or without sequence starts, so the roofline is the whole
-    call's algorithmic flops over its time against the fp32 matrix peak."""
+def varlen_workload(dev, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", mean_len=256):
+    """Packed sequences (seq_idx) on a workload's shape: each row holds
+    sequences of mean length `mean_len` (uniform lengths 1 .. 2*mean-1).  The
+    same calls without seq_idx are timed alongside."""
     import torch
     import selective_state_space_ssd_amd as ssd
     w = WORKLOADS[name]
-    dev = torch.device("cuda:0")
-    code = ssd.SSD_BF16 if w.dtype == "bf16" else ssd.SSD_F32
+    sw = ScanWorkload(w, dev, copies=2 if w.dtype == "f32" else 1)
+    sw.prepare()
     ws_bytes = max(ssd.varlen_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                                             w.ngroups, w.chunk_size, code),
-                   ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                                      w.ngroups, w.chunk_size, code))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+                                             w.ngroups, w.chunk_size, sw.code), sw.ws_bytes)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     seq = torch.from_numpy(make_seq_idx(w.batch, w.seqlen, mean_len, 77)).to(dev)
-    keep, calls = [], []
-    for _ in range(2 if w.dtype == "f32" else 1):
-        inp = make_inputs(w)
-        t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items()
-             if isinstance(v, np.ndarray)}
-        if w.dtype == "bf16":
-            for k in ("x", "z", "B", "C", "dt"):
-                t[k] = torch.from_numpy(inp["bits"][k].view(np.int16)).to(dev).view(torch.bfloat16)
-        out = torch.empty_like(t["x"])
-        fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), device=dev)
-        keep.append((t, out, fin))
-        calls.append((t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(),
-                      t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(),
-                      t["z"].data_ptr(), t["dt_bias"].data_ptr(), 0.0, math.inf, w.chunk_size,
-                      w.ngroups, None, out.data_ptr(), fin.data_ptr() if w.final else None))
-    tail = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, code, ws.data_ptr(),
-            ws_bytes, torch.cuda.current_stream(dev).cuda_stream)
+    s = torch.cuda.current_stream(dev).cuda_stream
 
     def run(k, packed):
-        a = calls[k % len(calls)]
-        st = (ssd.scan_fwd_varlen_raw(*a, seq.data_ptr(), *tail) if packed
-              else ssd.scan_fwd_raw(*a, *tail))
+        a = list(sw.argv[k % len(sw.argv)][0])
+        a[-2], a[-1] = ws.data_ptr(), ws_bytes
+        st = (ssd.scan_fwd_varlen_raw(*a[:15], seq.data_ptr(), *a[15:], s) if packed
+              else ssd.scan_fwd_raw(*a, s))
         if st != 0:
             raise ssd.SsdError(st, ssd.status_string(st))
 
-    res = {}
-    for packed in (True, False):
-        for k in range(warmup):
-            run(k, packed)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(steps):
-            run(k, packed)
-        torch.cuda.synchronize()
-        res[packed] = (time.perf_counter() - t0) / steps
-    el = res[True]
+    tp = time_calls(lambda k: run(k, True), MIN_CALLS, warmup, dev)
+    tu = time_calls(lambda k: run(k, False), MIN_CALLS, warmup, dev)
+    el = tp["median_ms"] / 1e3
     nseq = int((seq[:, 1:] != seq[:, :-1]).sum().item()) + w.batch
     line = {
         "workload": f"ssd_scan_fwd_varlen {w.dtype} batch {w.batch} x seqlen {w.seqlen} holding "
                     f"{nseq} packed sequences (mean length {mean_len}), {w.nheads} heads x "
-                    f"headdim 64, dstate {w.dstate}, chunk {w.chunk_size}, ngroups {w.ngroups}, "
-                    "z gate and D on",
-        "path": "staged" if w.dtype == "f32" else bf16_kernel(ssd, ws_bytes),
-        "tokens_per_s": w.tokens / el,
-        "us_per_call": el * 1e6,
-        "plain_us_per_call": res[False] * 1e6,
-        "calls": steps,
+                    f"headdim 64, dstate {w.dstate}, chunk {w.chunk_size}, ngroups {w.ngroups}",
+        "path": ssd.taken_path(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+                               w.chunk_size, sw.code, varlen=True),
+        "tokens_per_s": w.tokens / tp["wall_s_per_call"], **_line_timing(tp),
+        "plain_us_per_call_events": {"median_us": tu["median_ms"] * 1e3,
+                                     "min_us": tu["min_ms"] * 1e3},
     }
-    if w.dtype == "f32":  # matrix-bound, like the plain fp32 workload
+    if w.dtype == "f32":
         fl = sum(alg_flops(w).values())
         line["roofline"] = {"bound": "mfma", "achieved": fl / el / 1e12,
                             "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                            "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS, "alg_flops": fl}
-    else:  # HBM-bound, like the plain bf16 workload
+                            "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS, "alg_flops": fl,
+                            "kernels": "whole call", "time": "median of the per-call events"}
+    else:
         nbytes = alg_bytes(w) + w.batch * w.seqlen * 4
         line["roofline"] = {"bound": "hbm", "achieved": nbytes / el / 1e9, "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": nbytes / el / 1e9 / PEAK_HBM_GBS,
-                            "alg_bytes": nbytes}
+                            "alg_bytes": nbytes, "kernels": "whole call",
+                            "time": "median of the per-call events"}
     return line
 
 
-def block_workload(steps, warmup, ngroups=1, norm_groups=1):
+def block_workload(dev, warmup, ngroups=1, norm_groups=1):
     """The block around the scan (split + conv1d + SiLU prologue, scan, gated
     RMSNorm epilogue) at mamba issue #647's repro size: fp32, batch 2 x seqlen
     2048, dim 2048 (32 heads of 64), dstate 128, conv width 4, chunk 128, with
@@ -323,7 +491,6 @@ def block_workload(steps, warmup, ngroups=1, norm_groups=1):
     G = ngroups
     dim, gn = H * P, G * N
     width = 2 * dim + 2 * gn + H
-    dev = torch.device("cuda:0")
     rng = np.random.default_rng(21)
     f = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev)
     zx = [f(b, L, width) for _ in range(2)]
@@ -335,7 +502,6 @@ def block_workload(steps, warmup, ngroups=1, norm_groups=1):
     wsz = ssd.block_workspace_size(b, L, H, P, N, G, Q, ssd.SSD_F32, W, norm_groups)
     ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
     s = torch.cuda.current_stream(dev).cuda_stream
-    # the scan alone on same-shaped inputs, no gate (the scan inside the block)
     xs = [f(b, L, H, P) for _ in range(2)]
     Bs, Cs, dts = f(b, L, G, N), f(b, L, G, N), f(b, L, H)
     y = torch.empty_like(xs[0])
@@ -358,30 +524,19 @@ def block_workload(steps, warmup, ngroups=1, norm_groups=1):
         if st != 0:
             raise ssd.SsdError(st, ssd.status_string(st))
 
-    res = {}
-    for name, fn in (("block", block_call), ("scan", scan_call)):
-        for k in range(warmup):
-            fn(k)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(steps):
-            fn(k)
-        torch.cuda.synchronize()
-        res[name] = (time.perf_counter() - t0) / steps
-    extra = res["block"] - res["scan"]
-    # prologue: read the xBC and dt columns (plus a 3-step halo per 32-step
-    # tile) and write x, B, C, dt; epilogue: read y and z, write out
+    tb = time_calls(block_call, MIN_CALLS, warmup, dev)
+    ts = time_calls(scan_call, MIN_CALLS, warmup, dev)
+    extra = (tb["median_ms"] - ts["median_ms"]) / 1e3
     halo = 1.0 + (W - 1) / 32.0
     nbytes = b * L * 4 * ((dim + 2 * gn + H) * (1.0 + halo) + 3 * dim)
     return {
         "workload": f"ssd_split_conv1d_scan_fwd f32 batch 2 x seqlen 2048, dim 2048 (32 heads x "
                     f"headdim 64), dstate 128, ngroups {G}, conv width 4, chunk 128, gated "
                     f"RMSNorm over {'the whole width' if norm_groups == 1 else 'each group'}",
-        "tokens_per_s": b * L / res["block"],
-        "us_per_call": res["block"] * 1e6,
-        "scan_alone_us_per_call": res["scan"] * 1e6,
-        "calls": steps,
-        "roofline": {"kernels": "prologue + epilogue (block time minus scan time)",
+        "tokens_per_s": b * L / tb["wall_s_per_call"], **_line_timing(tb),
+        "scan_alone_us_per_call_events": {"median_us": ts["median_ms"] * 1e3,
+                                          "min_us": ts["min_ms"] * 1e3},
+        "roofline": {"kernels": "prologue + epilogue (block median minus scan median)",
                      "bound": "hbm", "achieved": nbytes / extra / 1e9 if extra > 0 else None,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": nbytes / extra / 1e9 / PEAK_HBM_GBS if extra > 0 else None,
@@ -404,7 +559,7 @@ def bwd_alg_flops(w, T=64):
     return fwd + b * nb * (H * per + G * 2.0 * pairs * N)
 
 
-def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", dtype="f32"):
+def bwd_workload(dev, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", dtype="f32"):
     """The backward (every gradient, dfinal zero, z, D and dt_bias on) of the
     batch 2 x seqlen 2048 workload at ngroups 1, alternating two input copies;
     the forward on the same inputs is timed alongside.  dtype "bf16": x, dt,
@@ -412,7 +567,6 @@ def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", dtype=
     import torch
     import selective_state_space_ssd_amd as ssd
     w = WORKLOADS[name]
-    dev = torch.device("cuda:0")
     b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
     io = torch.bfloat16 if dtype == "bf16" else torch.float32
     code = ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32
@@ -458,32 +612,28 @@ def bwd_workload(steps, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", dtype=
         if st != 0:
             raise ssd.SsdError(st, ssd.status_string(st))
 
-    res = {}
-    for nm, fn in (("bwd", bwd_call), ("fwd", fwd_call)):
-        for k in range(warmup):
-            fn(k)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(steps):
-            fn(k)
-        torch.cuda.synchronize()
-        res[nm] = (time.perf_counter() - t0) / steps
+    tb = time_calls(bwd_call, MIN_CALLS, warmup, dev)
+    tf = time_calls(fwd_call, MIN_CALLS, warmup, dev)
     fl = bwd_alg_flops(w)
-    el = res["bwd"]
+    el = tb["median_ms"] / 1e3
     return {
         "workload": f"ssd_scan_bwd {dtype} batch 2 x seqlen 2048, 32 heads x headdim 64, "
                     "dstate 128, ngroups 1, z gate, D and dt_bias on: every gradient (forward "
                     "re-run inside" + (", inputs widened to fp32 and bf16 gradients rounded)"
                                        if dtype == "bf16" else ")"),
-        "tokens_per_s": w.tokens / el,
-        "us_per_call": el * 1e6,
-        "forward_us_per_call": res["fwd"] * 1e6,
-        "calls": steps,
-        "roofline": {"bound": "mfma", "achieved": fl / el / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
-                     "unit": "TFLOP/s", "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS,
-                     "alg_flops": fl},
+        "tokens_per_s": w.tokens / tb["wall_s_per_call"], **_line_timing(tb),
+        "forward_us_per_call_events": {"median_us": tf["median_ms"] * 1e3,
+                                       "min_us": tf["min_ms"] * 1e3},
+        "roofline": {"kernels": "whole call", "bound": "mfma", "achieved": fl / el / 1e12,
+                     "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fl / el / 1e12 / PEAK_FP32_MFMA_TFLOPS, "alg_flops": fl,
+                     "time": "median of the per-call events"},
     }
 
+
+# --------------------------------------------------------------------------
+# CPU baseline
+# --------------------------------------------------------------------------
 
 def _cpu_model():
     try:
@@ -495,20 +645,80 @@ def _cpu_model():
     return "unknown"
 
 
+def cpu_baseline(w, inp, min_seconds=10.0, heads_per_pass=16):
+    """The oracle (untuned fp64 recurrence, OpenMP over batch x heads) on a
+    bounded sample of workload `w`: passes of `heads_per_pass` whole heads
+    (every timestep) until `min_seconds` have passed or every head is done,
+    scaled to tokens/s of the whole workload (tokens x heads done / heads)."""
+    import oracle
+    threads = oracle.max_threads()
+    H = w.nheads
+    done, elapsed, h0 = 0, 0.0, 0
+    while elapsed < min_seconds and done < w.batch * H:
+        mask = np.zeros((w.batch, H), bool)
+        hs = [(h0 + j) % H for j in range(min(heads_per_pass, H))]
+        mask[:, hs] = True
+        t0 = time.perf_counter()
+        oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                       dt_bias=inp["dt_bias"], head_mask=mask)
+        elapsed += time.perf_counter() - t0
+        done += int(mask.sum())
+        h0 += len(hs)
+    frac = done / (w.batch * H)
+    return {"value": w.tokens * frac / elapsed, "unit": "tokens/s",
+            "cores": min(threads, heads_per_pass * w.batch), "kind": "oracle",
+            "sample": f"{done} of {w.batch * H} (batch, head) pairs of the {w.name} workload, "
+                      f"every timestep ({elapsed:.1f} s of fp64 recurrence, OpenMP over the "
+                      f"pairs of a pass, {heads_per_pass} per pass); value = tokens x "
+                      f"{frac:.4f} / time",
+            "cpu": _cpu_model(), "threads_available": threads}
+
+
+def cpu_baseline_single_thread(name="f32_b1_L256_H4_P64_N16_G1_Q64", min_seconds=2.0):
+    """The oracle with one thread on the small fp32 workload."""
+    import oracle
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                       dt_bias=inp["dt_bias"], nthreads=1)
+        n += 1
+    el = time.perf_counter() - t0
+    return {"value": w.tokens * n / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole calls of {w.name} in {el:.1f} s, one thread"}
+
+
+# --------------------------------------------------------------------------
+
+OTHER_SCAN_LINES = (
+    ("f32_b1_L256_H4_P64_N16_G1_Q64",),
+    ("f32_b2_L2048_H32_P64_N128_G1_Q128",),
+    ("f32_b2_L2048_H32_P64_N128_G2_Q128",),
+    ("f32_b2_L2048_H32_P64_N128_G4_Q128",),
+    ("bf16_b8_L4096_H64_P64_N128_G8_Q256",),
+    ("f32_b4_L8192x4seg_H32_P64_N128_G1_Q128",),
+)
+
+
 def main():
+    global MIN_CALLS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-bf16", action="store_true",
-                    help="skip the second measured workload (bf16, batch 8 x seqlen 4096)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also capture the step once as a HIP graph per input copy, replay "
-                         "it, and report the replay rate as the value")
+    ap.add_argument("--no-others", action="store_true",
+                    help="measure the headline workload only")
+    ap.add_argument("--only", default=None,
+                    help="measure only this workload (a name of ssd_workloads.WORKLOADS) and "
+                         "print its line (for counter runs)")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--min-calls", type=int, default=MIN_CALLS,
+                    help="least number of event-timed calls per line (counter runs use fewer)")
     ap.add_argument("--copy-mb", type=int, default=0,
-                    help="before the steps, run 3 plain device copies of this many MiB "
-                         "(reference kernel for calibrating HBM byte counters)")
+                    help="before the measurements, run 3 streaming device copies of this many "
+                         "MiB (the reference kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -516,163 +726,85 @@ def main():
         sys.exit(2)
 
     import torch
-    import selective_state_space_ssd_amd as ssd
+    import selective_state_space_ssd_amd as ssd  # noqa: F401
 
+    MIN_CALLS = max(1, args.min_calls)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    workloads = [WORKLOADS[n] for n in BENCH_WORKLOADS]
-    stream = torch.cuda.current_stream(dev)
-
-    # inputs, two copies of each, plus outputs and one shared workspace
-    calls = []   # per rotation copy: list of argument tuples for ssd_scan_fwd
-    keep = []
-    ws_bytes = max(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                                      w.ngroups, w.chunk_size, 0) for w in workloads)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    for copy in range(2):
-        args_copy = []
-        for w in workloads:
-            inp = make_inputs(w)
-            t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items()
-                 if isinstance(v, np.ndarray)}
-            out = torch.empty_like(t["x"])
-            keep.append((t, out))
-            args_copy.append((
-                t["x"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(),
-                t["C"].data_ptr(), t["D"].data_ptr(), t["z"].data_ptr(),
-                t["dt_bias"].data_ptr(), 0.0, math.inf, w.chunk_size, w.ngroups, None,
-                out.data_ptr(), None, w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                ssd.SSD_F32, ws.data_ptr(), ws_bytes))
-        calls.append(args_copy)
-
-    def step(k, timings=None):
-        s = torch.cuda.current_stream(dev).cuda_stream
-        for i, a in enumerate(calls[k % 2]):
-            st = ssd.scan_fwd_raw(*a, s, timing=None if timings is None else timings[i])
-            if st != 0:
-                raise ssd.SsdError(st, ssd.status_string(st))
-
     if args.copy_mb > 0:
-        n = args.copy_mb * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
+        from selective_state_space_ssd_amd import _build
+        lib = ctypes.CDLL(_build.PEAKS_LIB_PATH)
+        lib.ssd_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]
+        nb = args.copy_mb << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            assert lib.ssd_peak_copy(src.data_ptr(), dst.data_ptr(), nb,
+                                     torch.cuda.current_stream(dev).cuda_stream) == 0
         torch.cuda.synchronize()
         del src, dst
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    if args.only:
+        w1 = WORKLOADS[args.only]
+        line = scan_line((args.only,), dev, args.steps, args.warmup, peaks,
+                         copies=2 if (w1.dtype == "f32" and w1.segments == 1) else 1)
+        line["peaks_measured"] = peaks
+        print(json.dumps(line), flush=True)
+        return
 
-    # eager launches: exactly `steps` steps
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    elapsed_eager = time.perf_counter() - t0
-
-    # the same step captured as one HIP graph per input copy (three calls,
-    # nine kernels, no allocation or memset inside), replayed
-    elapsed_graph = None
-    if args.graph:
-        graphs = []
-        for k in range(2):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(k)
-            graphs.append(g)
-        for k in range(args.warmup):
-            graphs[k % 2].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(args.steps):
-            graphs[k % 2].replay()
-        torch.cuda.synchronize()
-        elapsed_graph = time.perf_counter() - t0
-    elapsed = elapsed_graph if elapsed_graph is not None else elapsed_eager
-
-    # per-stage durations: the same steps again, with the library recording a
-    # HIP event around each stage on the launch stream
-    timings = [[ssd.Timing() for _ in workloads] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for k in range(args.steps):
-        step(k, timings[k])
-    torch.cuda.synchronize()
-    elapsed_ev = time.perf_counter() - t1
-    stage_ms = np.array([[tm.read() for tm in row] for row in timings])  # [steps, calls, stages]
-    mean_ms = stage_ms.mean(axis=0)                                        # [calls, stages]
-
-    tokens = sum(w.tokens for w in workloads)
-    value = tokens * args.steps / elapsed
-    flops = [alg_flops(w) for w in workloads]
-    per_stage_total = mean_ms.sum(axis=0)
-    dom = int(np.argmax(per_stage_total))
-    dom_name = ssd.STAGES[dom]
-    dom_flops = sum(f[dom_name] for f in flops)
-    dom_s = per_stage_total[dom] / 1e3
-    achieved = dom_flops / dom_s / 1e12
-    path_flops = sum(sum(f.values()) for f in flops)
-    step_s = elapsed / args.steps
-    path_bytes = sum(alg_bytes(w) for w in workloads)
-
+    w = WORKLOADS[HEADLINE]
+    inp = make_inputs(w)
+    head = scan_line((HEADLINE,), dev, args.steps, args.warmup, peaks, inp=inp)
+    torch.cuda.empty_cache()
     line = {
         "metric": "SSD scan fwd tokens/sec at 1 MI355X; % of MFMA/HBM roofline",
-        "value": value,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps_timed"],
         "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_events": head["ms_per_step_events"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "ssd_scan_fwd f32 batch 2 x seqlen 2048, 32 heads x headdim 64, "
-                        "dstate 128, chunk 128, ngroups 1/2/4 (3 calls per step), "
-                        "z gate and D skip on, dt_limit (0, inf)",
-            "batch": 2, "seqlen": 2048, "nheads": 32, "headdim": 64, "dstate": 128,
-            "chunk_size": 128, "ngroups": [1, 2, 4], "tokens_per_step": tokens,
-            "launch": "hip graph replay" if elapsed_graph is not None else "eager",
+            "workload": describe(w) + " (one ssd_scan_fwd call per step)",
+            "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+            "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
+            "tokens_per_step": w.tokens, "path": head["path"], "launch": "eager",
         },
-        "roofline": {
-            "kernel": dom_name,
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_FP32_MFMA_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_FP32_MFMA_TFLOPS,
-            "traffic": measured_traffic(dom_name),
-            "launches_timed": args.steps * len(workloads),
-            "mean_launch_us": dom_s / len(workloads) * 1e6,
-        },
-        "path": {
-            "alg_tflops_per_s": path_flops / step_s / 1e12,
-            "mfma_frac": path_flops / step_s / 1e12 / PEAK_FP32_MFMA_TFLOPS,
-            "alg_gbytes_per_s": path_bytes / step_s / 1e9,
-            "hbm_frac": path_bytes / step_s / 1e9 / PEAK_HBM_GBS,
-            "stage_us_per_call": {s: float(per_stage_total[i] / len(workloads) * 1e3)
-                                  for i, s in enumerate(ssd.STAGES)},
-            "event_pass_ms_per_step": elapsed_ev / args.steps * 1e3,
-            "eager_ms_per_step": elapsed_eager / args.steps * 1e3,
-            "eager_tokens_per_s": tokens * args.steps / elapsed_eager,
-        },
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(workloads),
+        "roofline": head["roofline"],
+        "call": head["call"],
+        "peaks": {"datasheet": {"hbm_GBs": PEAK_HBM_GBS, "mfma_fp32_TFLOPs": PEAK_FP32_MFMA_TFLOPS,
+                                "mfma_bf16_TFLOPs": PEAK_BF16_MFMA_TFLOPS},
+                  "measured": peaks},
+        "cpu_baseline": None,
     }
-    if not args.no_bf16:
-        del keep, calls, ws
-        torch.cuda.empty_cache()
-        line["other_workloads"] = [bf16_workload(max(5, args.steps // 5), 3),
-                                   decode_workload(max(20, args.steps), 5),
-                                   varlen_workload(max(20, args.steps), 5),
-                                   varlen_workload(max(5, args.steps // 5), 3,
-                                                   "bf16_b8_L4096_H64_P64_N128_G8_Q256", 512),
-                                   block_workload(max(20, args.steps), 5),
-                                   bwd_workload(max(10, args.steps // 2), 3),
-                                   bwd_workload(max(10, args.steps // 2), 3, dtype="bf16")]
+    if not args.no_others:
+        others = []
+        for names in OTHER_SCAN_LINES:
+            w2 = WORKLOADS[names[0]]
+            others.append(scan_line(names, dev, args.steps, args.warmup, peaks,
+                                    copies=2 if (w2.dtype == "f32" and w2.segments == 1) else 1))
+            torch.cuda.empty_cache()
+        for fn in (lambda: varlen_workload(dev, args.warmup),
+                   lambda: varlen_workload(dev, args.warmup, "bf16_b8_L4096_H64_P64_N128_G8_Q256",
+                                           512),
+                   lambda: decode_workload(dev, args.warmup),
+                   lambda: block_workload(dev, args.warmup),
+                   lambda: bwd_workload(dev, args.warmup),
+                   lambda: bwd_workload(dev, args.warmup, dtype="bf16")):
+            others.append(fn())
+            torch.cuda.empty_cache()
+        line["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, inp)
+        line["cpu_baseline_single_thread"] = cpu_baseline_single_thread()
     print(json.dumps(line), flush=True)
 
 

@@ -215,6 +215,7 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
 #define SSD_PATH_FUSED_HEAD 3
 #define SSD_PATH_FUSED_GROUP 4
 #define SSD_PATH_CHAIN 5
+#define SSD_PATH_STEP 6 /* reported by ssd_scan_fwd_taken_path only (seqlen <= 16) */
 
 /*
  * ssd_scan_fwd_path -- ssd_scan_fwd on an explicitly chosen kernel path.
@@ -237,6 +238,15 @@ int ssd_scan_fwd_path(const void* x, const void* dt, const float* A, const void*
 size_t ssd_scan_fwd_path_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
                                         int64_t headdim, int64_t dstate, int ngroups,
                                         int chunk_size, int dtype, int varlen, int kernel_path);
+
+/* The kernel path a call with these arguments takes: SSD_PATH_STAGED,
+ * SSD_PATH_FUSED_HEAD, SSD_PATH_FUSED_GROUP, SSD_PATH_CHAIN or SSD_PATH_STEP
+ * (the step kernel of seqlen <= 16), after the fallbacks above; kernel_path
+ * is what the call asks for (SSD_PATH_AUTO for ssd_scan_fwd).  A negative
+ * status for arguments the call would reject.  Pure host computation. */
+int ssd_scan_fwd_taken_path(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int ngroups, int chunk_size, int dtype, int varlen,
+                            int kernel_path);
 
 /*
  * ssd_scan_fwd_wait_status -- whether the last call enqueued on `stream` with

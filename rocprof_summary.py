@@ -30,6 +30,7 @@ def _db(path):
 
 
 def short(name):
+    name = name.replace("(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "")
 
 
@@ -75,12 +76,12 @@ def traffic(fetch_dir, write_dir, kernel, copy_mib, sources):
             raise SystemExit(f"{counter}: {len(hits)} kernels match {sub!r}: {[h[0] for h in hits]}")
         return hits[0]
 
-    # the calibration copy: the largest single dispatch of a copy kernel (the
-    # COPY_MIB device-to-device copy; small uploads use the same kernel)
+    # the calibration copy: the largest dispatch of the streaming copy kernel
+    # of libssd_peaks.so (bench.py --copy-mb COPY_MIB runs three of them)
     def copy_reading(path, counter):
         con = sqlite3.connect(_db(path))
         v = con.execute("select max(value) from counters_collection where counter_name = ? and "
-                        "lower(kernel_name) like '%copy%'", (counter,)).fetchone()[0]
+                        "kernel_name like '%copy_kernel%'", (counter,)).fetchone()[0]
         if not v:
             raise SystemExit(f"{counter}: no copy kernel in the run")
         return float(v)

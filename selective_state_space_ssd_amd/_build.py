@@ -14,6 +14,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libssd.so")
+# measured peaks (streaming copy, matrix-core loops) for the benchmark's
+# roofline lines: a library of its own, not part of the scan's
+PEAKS_LIB_PATH = os.path.join(PKG, "libssd_peaks.so")
+PEAKS_SOURCES = ["ssd_peaks.hip"]
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["ssd_api.hip", "ssd_dt_cumsum.hip", "ssd_chunk_state.hip", "ssd_state_passing.hip",
            "ssd_chunk_scan.hip", "ssd_bf16.hip", "ssd_fused_bf16.hip",
@@ -36,7 +40,8 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libssd.so``; returns its path."""
+    """Compile every source and link ``libssd.so`` and ``libssd_peaks.so``;
+    returns the path of ``libssd.so``."""
     cc = hipcc()
     os.makedirs(OBJ_DIR, exist_ok=True)
 
@@ -50,14 +55,17 @@ def build(verbose: bool = False) -> str:
             print(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    every = SOURCES + PEAKS_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(every), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(every, ex.map(compile_one, every)))
+    for path, srcs in ((LIB_PATH, SOURCES), (PEAKS_LIB_PATH, PEAKS_SOURCES)):
+        tmp = path + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[objs[s] for s in srcs],
+               "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_scan_fwd_wait_status.argtypes = [p, ctypes.c_size_t, i64, i64, i64, i64, i64, i, i,
                                              i, i, i, p]
     lib.ssd_scan_fwd_wait_status.restype = i
+    lib.ssd_scan_fwd_taken_path.argtypes = [i64, i64, i64, i64, i64, i, i, i, i, i]
+    lib.ssd_scan_fwd_taken_path.restype = i
     lib.ssd_split_conv1d_scan_fwd.argtypes = (
         [p, p, p, p, p, p, i, p, f, f, p, f, i64, i, i, p, p, i64, i64, i64, i64, i, i, p,
          ctypes.c_size_t, p])
@@ -133,6 +135,21 @@ def varlen_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk
     return int(lib.ssd_scan_fwd_path_workspace_size(
         batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, 1,
         path_code(kernel_path)))
+
+
+def taken_path(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, varlen=False,
+               kernel_path: str = "auto") -> str:
+    """Name of the kernel path a call with these arguments takes ("staged",
+    "fused_head", "fused_group", "chain" or "step"); raises SsdError for
+    arguments the call would reject."""
+    code = int(load_library().ssd_scan_fwd_taken_path(
+        int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups),
+        int(chunk_size), int(dtype), 1 if varlen else 0, path_code(kernel_path)))
+    if code < 0:
+        raise SsdError(code, status_string(code))
+    names = {v: k for k, v in KERNEL_PATHS.items()}
+    names[6] = "step"
+    return names[code]
 
 
 def wait_status(workspace_ptr, workspace_bytes, batch, seqlen, nheads, headdim, dstate, ngroups,

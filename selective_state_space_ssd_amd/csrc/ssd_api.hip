@@ -459,6 +459,21 @@ size_t ssd_scan_fwd_path_workspace_size(int64_t batch, int64_t seqlen, int64_t n
   return lay.total;
 }
 
+int ssd_scan_fwd_taken_path(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int ngroups, int chunk_size, int dtype, int varlen,
+                            int kernel_path) {
+  Layout lay;
+  int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype,
+                        varlen != 0, kernel_path, &lay);
+  if (st != SSD_OK) return st;
+  if (lay.decode) return SSD_PATH_STEP;
+  if (lay.chain) return SSD_PATH_CHAIN;
+  if (lay.fused)
+    return kernel_path == SSD_PATH_FUSED_GROUP && !varlen ? SSD_PATH_FUSED_GROUP
+                                                         : SSD_PATH_FUSED_HEAD;
+  return SSD_PATH_STAGED;
+}
+
 int ssd_scan_fwd_wait_status(const void* workspace, size_t workspace_bytes, int64_t batch,
                              int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                              int ngroups, int chunk_size, int dtype, int varlen, int kernel_path,

@@ -38,6 +38,7 @@ def test_header_declares_the_entry_points():
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
                  "ssd_timing_read", "ssd_timing_destroy", "ssd_scan_fwd_path",
                  "ssd_scan_fwd_path_workspace_size", "ssd_scan_fwd_wait_status",
+                 "ssd_scan_fwd_taken_path",
                  "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size",
                  "ssd_split_conv1d_scan_fwd", "ssd_split_conv1d_scan_fwd_workspace_size",
                  "ssd_scan_bwd", "ssd_scan_bwd_workspace_size"):
@@ -346,6 +347,22 @@ def test_path_entry_point_rejections():
     assert call_path(3, ws=0xC0000000, ws_bytes=need - 1, **bf) == WORKSPACE
     # seq_idx on the path entry point: packed-sequence rules apply
     assert call_path(0, seq=0xD0000002) == ALIGN
+
+
+def test_taken_path():
+    """The path each call takes, after the documented fallbacks."""
+    tp = ssd.taken_path
+    assert tp(8, 4096, 64, 64, 128, 8, 256, 1) == "chain"           # pairs fill the machine
+    assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "fused_head"    # 64 pairs: fused
+    assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # fp32
+    assert tp(2, 16, 32, 64, 128, 1, 128, 1) == "step"              # seqlen <= 16
+    assert tp(2, 400, 6, 64, 128, 2, 256, 1, kernel_path="chain") == "fused_head"  # odd group
+    assert tp(2, 400, 8, 64, 16, 2, 256, 1, kernel_path="chain") == "staged"       # dstate 16
+    assert tp(2, 400, 8, 64, 128, 2, 256, 1, kernel_path="fused_group") == "fused_group"
+    assert tp(2, 400, 8, 64, 128, 2, 256, 1, True, "fused_group") == "fused_head"  # packed
+    assert tp(2, 400, 8, 64, 128, 2, 256, 0, kernel_path="chain") == "staged"      # fp32
+    with pytest.raises(ssd.SsdError):
+        tp(2, 400, 8, 64, 128, 3, 256, 1)
 
 
 def test_wait_status_rejections_without_gpu():

@@ -179,6 +179,34 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
                  int64_t headdim, int64_t dstate, int dtype, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * ssd_scan_fwd_noalloc -- ssd_scan_fwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, checks,
+ * status codes and results are those of ssd_scan_fwd (same kernels, same
+ * path), except that the workspace is a library-owned device array of
+ * SSD_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the library's first
+ * use on that GPU until the process ends.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine).  A problem whose workspace is
+ * larger than the array runs in slices of batch rows, one after another on
+ * `stream`, on the path the whole problem takes; SSD_ERR_WORKSPACE when a
+ * single batch row needs more than SSD_NOALLOC_SCRATCH_BYTES (e.g. fp32
+ * sequences of 65536 steps at 32 heads x 64 x 128).  Every call on a GPU
+ * uses that GPU's one array: calls that overlap in time on one GPU (two
+ * streams, two threads) race and give wrong results; calls enqueued on one
+ * stream are ordered and safe.  What must start at zero (the fused path's
+ * tickets, flags and error word) is cleared by a kernel at every call.  The
+ * first call on a device looks the array's address up (SSD_ERR_HIP if that
+ * fails).
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssd_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* dt_bias,
+                         float dt_min, float dt_max, int chunk_size, int ngroups,
+                         const float* initial_states, void* out, float* final_states,
+                         int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                         int64_t dstate, int dtype, hipStream_t stream);
+
 /* Bytes of workspace ssd_scan_fwd needs for these sizes (0 for an empty
  * problem, for seqlen <= 16, on the chain path, and for arguments ssd_scan_fwd
  * would reject); pure host computation, no HIP call.  The workspace holds

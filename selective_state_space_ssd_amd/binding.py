@@ -24,6 +24,7 @@ STAGES = ("prep", "chunk_state", "state_passing", "chunk_scan")
 KERNEL_PATHS = {"auto": 0, "staged": 1, "fused": 2, "fused_head": 3, "fused_group": 4,
                 "chain": 5}
 SSD_ERR_WAIT = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -67,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ssd_scan_fwd_wait_status.argtypes = [p, ctypes.c_size_t, i64, i64, i64, i64, i64, i, i,
                                              i, i, i, p]
     lib.ssd_scan_fwd_wait_status.restype = i
+    lib.ssd_scan_fwd_noalloc.argtypes = fwd_args[:21] + [p]
+    lib.ssd_scan_fwd_noalloc.restype = i
     lib.ssd_scan_fwd_taken_path.argtypes = [i64, i64, i64, i64, i64, i, i, i, i, i]
     lib.ssd_scan_fwd_taken_path.restype = i
     lib.ssd_split_conv1d_scan_fwd.argtypes = (
@@ -234,6 +237,17 @@ def scan_fwd_path_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_
         float(dt_max), int(chunk_size), int(ngroups), init_ptr, out_ptr, final_ptr, seq_ptr,
         int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(dtype), code, ws_ptr,
         int(ws_bytes), stream))
+
+
+def scan_fwd_noalloc_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min,
+                         dt_max, chunk_size, ngroups, init_ptr, out_ptr, final_ptr, batch, seqlen,
+                         nheads, headdim, dstate, dtype, stream) -> int:
+    """Direct call of ``ssd_scan_fwd_noalloc`` (no workspace argument: the
+    library's own scratch); returns the status."""
+    return int(load_library().ssd_scan_fwd_noalloc(
+        x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, float(dt_min),
+        float(dt_max), int(chunk_size), int(ngroups), init_ptr, out_ptr, final_ptr, int(batch),
+        int(seqlen), int(nheads), int(headdim), int(dstate), int(dtype), stream))
 
 
 def scan_fwd_varlen_raw(x_ptr, dt_ptr, A_ptr, B_ptr, C_ptr, D_ptr, z_ptr, dt_bias_ptr, dt_min,

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 
 #include "ssd.h"
@@ -174,7 +175,7 @@ int validate(const void* x, const void* dt, const float* A, const void* B, const
              int chunk_size, int ngroups, const float* initial_states, void* out,
              float* final_states, const int32_t* seq_idx, bool varlen, int64_t batch,
              int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int dtype, int path,
-             void* workspace, size_t workspace_bytes, Layout* lay) {
+             void* workspace, size_t workspace_bytes, Layout* lay, bool check_workspace = true) {
   int st = check_shapes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, varlen,
                         path, lay);
   if (st != SSD_OK) return st;
@@ -220,7 +221,7 @@ int validate(const void* x, const void* dt, const float* A, const void* B, const
     if (hits(sfin, s)) return SSD_ERR_INVALID_ARG;
   if (final_states != initial_states && hits(sfin, sinit)) return SSD_ERR_INVALID_ARG;
   // the workspace is checked last: a call that gets past it launches kernels
-  if (lay->total > 0) {
+  if (check_workspace && lay->total > 0) {
     if (!workspace || workspace_bytes < lay->total) return SSD_ERR_WORKSPACE;
     if (!aligned(workspace, kAlign)) return SSD_ERR_ALIGNMENT;
   }
@@ -412,6 +413,30 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   return SSD_OK;
 }
 
+// ---- allocation-free entry point ------------------------------------------
+// Its workspace is this library-owned array (one copy per GPU, alive until the
+// process ends).  Host code never uses the array's name as an address: the
+// name is a host-side stand-in, and a kernel handed it would fault.  The
+// device address is looked up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];  // written once per device, under its once_flag
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, const void* C,
@@ -423,6 +448,65 @@ int ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* B, c
   return run(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups, initial_states,
              out, final_states, nullptr, false, batch, seqlen, nheads, headdim, dstate, dtype,
              SSD_PATH_AUTO, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssd_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const void* B,
+                         const void* C, const float* D, const void* z, const float* dt_bias,
+                         float dt_min, float dt_max, int chunk_size, int ngroups,
+                         const float* initial_states, void* out, float* final_states,
+                         int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                         int64_t dstate, int dtype, hipStream_t stream) {
+  // every argument of the whole call first, with no workspace (the scratch is
+  // library memory no caller tensor can overlap)
+  Layout lay;
+  int st = validate(x, dt, A, B, C, D, z, dt_bias, dt_min, dt_max, chunk_size, ngroups,
+                    initial_states, out, final_states, nullptr, false, batch, seqlen, nheads,
+                    headdim, dstate, dtype, SSD_PATH_AUTO, nullptr, 0, &lay, false);
+  if (st != SSD_OK) return st;
+  if (batch == 0) return SSD_OK;
+  // batch rows are independent: rows whose workspace does not fit the scratch
+  // at once run in slices of rows, one after the other on `stream`, all on
+  // the kernel path the whole call takes (so the result does not depend on
+  // the slicing)
+  const int taken = ssd_scan_fwd_taken_path(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                            chunk_size, dtype, 0, SSD_PATH_AUTO);
+  if (taken < 0) return taken;
+  const int path = taken == SSD_PATH_STAGED ? SSD_PATH_STAGED
+                   : taken == SSD_PATH_FUSED_HEAD ? SSD_PATH_FUSED_HEAD
+                                                  : SSD_PATH_AUTO;
+  int64_t rows = batch;
+  if (lay.total > SSD_NOALLOC_SCRATCH_BYTES) {
+    Layout one;
+    if (check_shapes(1, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false, path,
+                     &one) != SSD_OK || one.total > SSD_NOALLOC_SCRATCH_BYTES)
+      return SSD_ERR_WORKSPACE;  // one batch row needs more than the scratch holds
+    rows = (int64_t)(SSD_NOALLOC_SCRATCH_BYTES / one.total);
+    for (;; --rows) {  // the layout is not exactly linear in the rows (alignment)
+      Layout part;
+      if (check_shapes(rows, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, false,
+                       path, &part) == SSD_OK && part.total <= SSD_NOALLOC_SCRATCH_BYTES)
+        break;
+    }
+  }
+  void* ws = scratch_address();
+  if (!ws) return SSD_ERR_HIP;
+  const int64_t es = dtype == SSD_BF16 ? 2 : 4;
+  const int64_t xrow = seqlen * nheads * headdim * es, dtrow = seqlen * nheads * es;
+  const int64_t bcrow = seqlen * (int64_t)ngroups * dstate * es, strow = nheads * headdim * dstate;
+  for (int64_t b0 = 0; b0 < batch; b0 += rows) {
+    const int64_t nb = batch - b0 < rows ? batch - b0 : rows;
+    auto at = [b0](const void* p, int64_t row_bytes) -> const char* {
+      return p ? static_cast<const char*>(p) + b0 * row_bytes : nullptr;
+    };
+    st = run(at(x, xrow), at(dt, dtrow), A, at(B, bcrow), at(C, bcrow), D, at(z, xrow), dt_bias,
+             dt_min, dt_max, chunk_size, ngroups,
+             initial_states ? initial_states + b0 * strow : nullptr,
+             const_cast<char*>(at(out, xrow)), final_states ? final_states + b0 * strow : nullptr,
+             nullptr, false, nb, seqlen, nheads, headdim, dstate, dtype, path, ws,
+             SSD_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+    if (st != SSD_OK) return st;
+  }
+  return SSD_OK;
 }
 
 int ssd_scan_fwd_varlen(const void* x, const void* dt, const float* A, const void* B,

@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points():
                  "ssd_abi_version", "ssd_scan_fwd_timed", "ssd_timing_create",
                  "ssd_timing_read", "ssd_timing_destroy", "ssd_scan_fwd_path",
                  "ssd_scan_fwd_path_workspace_size", "ssd_scan_fwd_wait_status",
-                 "ssd_scan_fwd_taken_path",
+                 "ssd_scan_fwd_taken_path", "ssd_scan_fwd_noalloc",
                  "ssd_scan_fwd_varlen", "ssd_scan_fwd_varlen_workspace_size",
                  "ssd_split_conv1d_scan_fwd", "ssd_split_conv1d_scan_fwd_workspace_size",
                  "ssd_scan_bwd", "ssd_scan_bwd_workspace_size"):
@@ -372,6 +372,35 @@ def test_wait_status_rejections_without_gpu():
     assert lib.ssd_scan_fwd_wait_status(None, 0, 1, 100, 4, 64, 16, 1, 64, 0, 0, 9, None) == INVALID
     assert lib.ssd_scan_fwd_wait_status(None, 0, 1, 100, 4, 32, 16, 1, 64, 0, 0, 0, None) == \
         UNSUPPORTED
+
+
+def call_noalloc(**changes):
+    a = dict(BASE)
+    a.update(changes)
+    return ssd.scan_fwd_noalloc_raw(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                    a["dt_bias"], a["dt_min"], a["dt_max"], a["chunk_size"],
+                                    a["ngroups"], a["init"], a["out"], a["final"], a["batch"],
+                                    a["seqlen"], a["nheads"], a["headdim"], a["dstate"],
+                                    a["dtype"], a["stream"])
+
+
+NOALLOC_CASES = [c for c in CASES if c[2] != WORKSPACE and "workspace" not in c[0]]
+
+
+@pytest.mark.parametrize("desc,changes,want", NOALLOC_CASES, ids=[c[0] for c in NOALLOC_CASES])
+def test_noalloc_rejected_before_launch(desc, changes, want):
+    """The allocation-free entry point checks every argument as ssd_scan_fwd
+    does, before any HIP call (no case here is valid)."""
+    assert call_noalloc(**changes) == want
+
+
+def test_noalloc_empty_and_too_large():
+    assert call_noalloc(batch=0) == OK
+    # one fp32 row of 65536 steps x 32 heads x 64 x 128 needs ~2.2 GB of
+    # intermediates on the staged path: more than the scratch holds
+    far = {k: (i + 1) << 34 for i, k in enumerate(("x", "dt", "A", "B", "C", "D", "z", "dt_bias",
+                                                   "init", "out", "final"))}
+    assert call_noalloc(seqlen=65536, nheads=32, dstate=128, chunk_size=128, **far) == WORKSPACE
 
 
 def call_varlen(seq=0xD0000000, **changes):

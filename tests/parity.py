@@ -70,12 +70,66 @@ def upload(inp, dtype):
     return t
 
 
+# Every parity call runs with its workspace filled with 0xFF bytes (a NaN in
+# every fp32 and bf16 slot, -1 in every int32 one), its output filled with
+# NaN, and canary bytes on both sides of out and final_states that must come
+# back untouched: a read of an intermediate nobody wrote, an output element
+# nobody wrote, or a store past either end shows up.
+GUARD_BYTES = 4096
+CANARY = 0x5A
+
+
+def poisoned_workspace(nbytes, dev):
+    return torch.full((max(int(nbytes), 1),), 0xFF, dtype=torch.uint8, device=dev)
+
+
+def guarded(shape, dtype, dev):
+    """(buffer, view): `view` has `shape`, lies GUARD_BYTES into `buffer` and
+    is NaN-filled; the GUARD_BYTES before and after it hold CANARY."""
+    es = torch.empty((), dtype=dtype).element_size()
+    n = int(np.prod(shape))
+    g = GUARD_BYTES // es
+    buf = torch.empty(n + 2 * g, dtype=dtype, device=dev)
+    buf.view(torch.uint8).fill_(CANARY)
+    view = buf[g:g + n].view(shape)
+    view.fill_(float("nan"))
+    return buf, view
+
+
+def check_guards(buf, name):
+    raw = buf.view(torch.uint8)
+    head, tail = raw[:GUARD_BYTES], raw[raw.numel() - GUARD_BYTES:]
+    assert bool((head == CANARY).all()) and bool((tail == CANARY).all()), \
+        f"{name}: bytes outside the tensor were written"
+
+
 def run_gpu(t, chunk_size, dt_limit=(0.0, float("inf")), init=None, final=True, **kw):
+    """One call through the C ABI on the kernel path bf16_path set, with a
+    poisoned workspace and guarded outputs unless the caller passes its own."""
     kw.setdefault("kernel_path", current_path())
+    x = t["x"]
+    dev = x.device
+    b, L, H, P = x.shape
+    G, N = t["B"].shape[2], t["B"].shape[3]
+    guards = []
+    if "workspace" not in kw:
+        code = 1 if x.dtype == torch.bfloat16 else 0
+        size_fn = ssd.varlen_workspace_size if kw.get("seq_idx") is not None else \
+            ssd.workspace_size
+        kw["workspace"] = poisoned_workspace(
+            size_fn(b, L, H, P, N, G, chunk_size, code, kw["kernel_path"]), dev)
+    if "out" not in kw:
+        buf, kw["out"] = guarded(tuple(x.shape), x.dtype, dev)
+        guards.append((buf, "out"))
+    if final and "final_states" not in kw:
+        buf, kw["final_states"] = guarded((b, H, P, N), torch.float32, dev)
+        guards.append((buf, "final_states"))
     res = ssd.scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                        dt_bias=t["dt_bias"], dt_limit=dt_limit, chunk_size=chunk_size,
                        initial_states=init, return_final_states=final, **kw)
     torch.cuda.synchronize()
+    for buf, name in guards:
+        check_guards(buf, name)
     return res
 
 

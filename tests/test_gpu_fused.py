@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import TOL, bf16_path, compare, current_path, log, np64, run_gpu, upload
+from parity import (TOL, bf16_path, compare, current_path, log, np64, poisoned_workspace,
+                    run_gpu, upload)
 from ssd_workloads import Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -40,8 +41,8 @@ def test_fused_reuse_and_error_word(kind, b, L, H, N, G):
     w, inp, t = _inputs(600 + L, b, L, H, N, G)
     log(f"test_fused_reuse {kind} b={b} L={L} H={H} N={N} G={G}")
     with bf16_path(kind):
-        ws = torch.empty(ssd.workspace_size(b, L, H, 64, N, G, 256, 1, current_path()),
-                         dtype=torch.uint8, device=t["x"].device)
+        ws = poisoned_workspace(ssd.workspace_size(b, L, H, 64, N, G, 256, 1, current_path()),
+                                t["x"].device)
         o1, f1 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
         assert _wait_status(ws, b, L, H, N, G) == 0
         o2, f2 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
@@ -95,8 +96,8 @@ def test_fused_repeat_bitwise(kind):
     visible would make a call differ."""
     w, inp, t = _inputs(630, b=4, L=2048, H=32, N=128, G=8)
     with bf16_path(kind):
-        ws = torch.empty(ssd.workspace_size(4, 2048, 32, 64, 128, 8, 256, 1, current_path()),
-                         dtype=torch.uint8, device=t["x"].device)
+        ws = poisoned_workspace(
+            ssd.workspace_size(4, 2048, 32, 64, 128, 8, 256, 1, current_path()), t["x"].device)
         o0, f0 = run_gpu(t, 256, init=t["initial_states"], workspace=ws)
         for k in range(12):
             o, f = run_gpu(t, 256, init=t["initial_states"], workspace=ws)

@@ -15,8 +15,8 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import (TOL, bf16_path, compare, current_path, log, np64, paths_for, run_gpu, upload,
-                    ws_regions)
+from parity import (TOL, bf16_path, compare, current_path, log, np64, paths_for,
+                    poisoned_workspace, run_gpu, upload, ws_regions)
 from ssd_workloads import WORKLOADS, Workload, make_inputs, small
 
 pytestmark = pytest.mark.gpu
@@ -84,9 +84,8 @@ def test_stage_intermediates(dtype, Q, N):
     inp = make_inputs(w)
     t = upload(inp, dtype)
     with bf16_path("staged"):  # the intermediates live in the staged path's workspace
-        ws = torch.empty(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16" else 0,
-                                           current_path()),
-                         dtype=torch.uint8, device=t["x"].device)
+        ws = poisoned_workspace(ssd.workspace_size(b, L, H, P, N, G, Q, 1 if dtype == "bf16"
+                                                   else 0, current_path()), t["x"].device)
         run_gpu(t, Q, init=t["initial_states"], workspace=ws)
     got = {k: np64(v) for k, v in ws_regions(ws, b, L, H, P, N, Q).items()}
     ref = oracle.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
@@ -249,9 +248,22 @@ def test_inplace_continuation():
 # the full-size workloads
 # --------------------------------------------------------------------------
 
-def _sample_mask(b, H, k, seed):
+def _sample_mask(b, H, G, k, seed):
+    """(batch, head) pairs the oracle checks on a full-size workload: in every
+    (batch, group) both heads of one randomly chosen pair (2j, 2j + 1) of the
+    group -- so every group, every ticket class of the fused kernels (they are
+    dealt by (batch, group)) and both heads of a chain-kernel pair are covered
+    --, plus `k` random pairs and the last pair."""
     rng = np.random.default_rng(seed)
     mask = np.zeros((b, H), bool)
+    hpg = H // G
+    for bb in range(b):
+        for g in range(G):
+            j = int(rng.integers(0, max(1, hpg // 2)))
+            lo = g * hpg + min(2 * j, hpg - 1)
+            mask[bb, lo] = True
+            if hpg > 1:
+                mask[bb, min(lo + 1, (g + 1) * hpg - 1)] = True
     idx = rng.choice(b * H, size=min(k, b * H), replace=False)
     mask.reshape(-1)[idx] = True
     mask[b - 1, H - 1] = True  # always the last pair
@@ -291,7 +303,10 @@ def test_workload(name):
     t = upload(inp, w.dtype)
     tol = TOL[w.dtype]
     big = w.batch * w.seqlen * w.nheads > 2 * 2048 * 32
-    mask = _sample_mask(w.batch, w.nheads, 6, w.seed) if big else None
+    mask = _sample_mask(w.batch, w.nheads, w.ngroups, 6, w.seed) if big else None
+    if mask is not None:
+        log(f"test_workload {name}: oracle on {int(mask.sum())} of {mask.size} (batch, head) "
+            "pairs (both heads of a pair in every (batch, group))")
     results = {}
     for path in paths_for(w.dtype):
         with bf16_path(path):

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import selective_state_space_ssd_amd as ssd
-from parity import (TOL, bf16_path, compare, current_path, log, np64, paths_for, run_gpu, upload,
-                    ws_regions)
+from parity import (TOL, bf16_path, compare, current_path, log, np64, paths_for,
+                    poisoned_workspace, run_gpu, upload, ws_regions)
 from ssd_workloads import WORKLOADS, Workload, make_inputs, make_seq_idx
 
 pytestmark = pytest.mark.gpu
@@ -145,7 +145,7 @@ def test_varlen_intermediates(dtype, Q, N):
     log(f"test_varlen_intermediates {dtype} Q={Q} N={N}")
     with bf16_path("staged"):  # the intermediates live in the staged path's workspace
         total = ssd.varlen_workspace_size(b, L, H, P, N, G, Q, code, current_path())
-        ws = torch.zeros(total, dtype=torch.uint8, device=t["x"].device)
+        ws = poisoned_workspace(total, t["x"].device)
         run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq), workspace=ws)
     nc = -(-L // Q)
     seg_bytes = (b * nc * Q * 4 + 255) // 256 * 256

@@ -124,7 +124,12 @@ extern "C" {
  * path when each group holds an even number of heads and the head pairs fill
  * the machine: one kernel in which each workgroup carries a pair of heads of one
  * group through the whole sequence in 128-step blocks with the state held on
- * chip (no workspace: ssd_scan_fwd_workspace_size returns 0).  Otherwise they
+ * chip (no workspace: ssd_scan_fwd_workspace_size returns 0).  When the pairs
+ * alone do not fill it but pairs times segments of at least 16 blocks fill a
+ * round of the compute units at least 3/4, the chain runs over segments
+ * (SSD_PATH_CHAIN_SEGMENTED below); the workspace then holds the units' end
+ * states [batch, nheads, units] (headdim x dstate floats, row-major) and
+ * their decays [batch, nheads, units].  Otherwise they
  * take the fused path: one set-up kernel and one scan kernel, in which each
  * workgroup handles 128 timesteps of one (batch, head) and hands the state to
  * the workgroup of the next 128 timesteps through the workspace.  (The
@@ -208,7 +213,7 @@ int ssd_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const vo
                          int64_t dstate, int dtype, hipStream_t stream);
 
 /* Bytes of workspace ssd_scan_fwd needs for these sizes (0 for an empty
- * problem, for seqlen <= 16, on the chain path, and for arguments ssd_scan_fwd
+ * problem, for seqlen <= 16, on the unsegmented chain path, and for arguments ssd_scan_fwd
  * would reject); pure host computation, no HIP call.  The workspace holds
  * the chunked form's intermediates: per-chunk states and the states entering
  * each chunk, as the Mamba-1 CUDA forward on mamba issue #488 keeps its
@@ -231,6 +236,13 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
  *                        calls run the per-head form)
  *   SSD_PATH_CHAIN       the chain bf16 kernel (one workgroup per pair of
  *                        heads of a group for the whole sequence)
+ *   SSD_PATH_CHAIN_SEGMENTED  the chain kernel over segments of the sequence:
+ *                        a state-only pass computes the local end state of
+ *                        every unit of blocks before the last segment, then
+ *                        one workgroup per (pair, segment) runs the chain from
+ *                        the units before it folded into its entering state;
+ *                        as many segments as fill one round of the compute
+ *                        units (at least two; a one-block sequence is one)
  * A path the shape cannot take falls back, always the same way: SSD_PATH_CHAIN
  * with an odd number of heads per group takes the fused path; every fused or
  * chain path takes the staged path unless the inputs are bf16 with headdim 64
@@ -244,6 +256,7 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
 #define SSD_PATH_FUSED_GROUP 4
 #define SSD_PATH_CHAIN 5
 #define SSD_PATH_STEP 6 /* reported by ssd_scan_fwd_taken_path only (seqlen <= 16) */
+#define SSD_PATH_CHAIN_SEGMENTED 7
 
 /*
  * ssd_scan_fwd_path -- ssd_scan_fwd on an explicitly chosen kernel path.
@@ -313,9 +326,8 @@ int ssd_scan_fwd_wait_status(const void* workspace, size_t workspace_bytes, int6
  * same path as ssd_scan_fwd (the chain and fused bf16 kernels count the
  * sequence starts themselves; asked for SSD_PATH_FUSED_GROUP the fused path
  * runs its per-head form) and needs ssd_scan_fwd_varlen_workspace_size(...)
- * bytes of workspace: none on the chain path, on the fused path the fused
- * layout, on the staged path the staged layout
- * followed, on a 256-byte boundary, by
+ * bytes of workspace: that of the plain call on the chain and fused paths, on the
+ * staged path the staged layout followed, on a 256-byte boundary, by
  *   seg [batch, nchunks, chunk_size] int32: for step q of chunk c the number
  *       of sequence starts at steps c*chunk_size .. c*chunk_size + q (steps
  *       past the sequence end repeat the last count).
@@ -460,8 +472,9 @@ int ssd_abi_version(void);
  * transpose of the bf16 kernels, empty when dt/cumsum is fused into the chunk
  * state --, chunk state, state passing, chunk scan).  On the fused path prep
  * is the set-up kernel, the scan kernel is reported as chunk scan and the two
- * middle stages are empty; on the chain path its one kernel is reported as
- * chunk scan and the other stages are empty.  Returns SSD_OK or SSD_ERR_HIP /
+ * middle stages are empty; on the chain path its kernel is reported as chunk
+ * scan (on the segmented chain the state-only pass as chunk state) and the
+ * other stages are empty.  Returns SSD_OK or SSD_ERR_HIP /
  * SSD_ERR_INVALID_ARG.
  */
 #define SSD_NUM_STAGES 4

@@ -22,7 +22,7 @@ SSD_NUM_STAGES = 4
 STAGES = ("prep", "chunk_state", "state_passing", "chunk_scan")
 # Kernel paths of ssd_scan_fwd_path (SSD_PATH_* in include/ssd.h)
 KERNEL_PATHS = {"auto": 0, "staged": 1, "fused": 2, "fused_head": 3, "fused_group": 4,
-                "chain": 5}
+                "chain": 5, "chain_segmented": 7}
 SSD_ERR_WAIT = -6
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SSD_NOALLOC_SCRATCH_BYTES
 
@@ -143,7 +143,7 @@ def varlen_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk
 def taken_path(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, varlen=False,
                kernel_path: str = "auto") -> str:
     """Name of the kernel path a call with these arguments takes ("staged",
-    "fused_head", "fused_group", "chain" or "step"); raises SsdError for
+    "fused_head", "fused_group", "chain", "chain_segmented" or "step"); raises SsdError for
     arguments the call would reject."""
     code = int(load_library().ssd_scan_fwd_taken_path(
         int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups),

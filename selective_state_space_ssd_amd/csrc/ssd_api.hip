@@ -39,7 +39,9 @@ struct Layout {
   int64_t nc = 0;
   bool decode = false;  // seqlen <= kDecodeMaxL: step-by-step kernel, no workspace
   bool fused = false;
-  bool chain = false;  // chain bf16 kernel: no workspace
+  bool chain = false;  // chain bf16 kernel: no workspace unless segmented
+  ssd::ChainPlan plan;
+  size_t off_cs_states = 0, off_cs_decay = 0;
   // staged path (off_seg: packed-sequence counts, varlen calls only)
   // (off_gram: tiles of B C^T for the four-heads chunk scan, ssd::use_gram)
   size_t off_dt = 0, off_cum = 0, off_states = 0, off_states_in = 0, off_bt = 0, off_seg = 0;
@@ -67,17 +69,29 @@ bool fused_path(int dtype, int64_t headdim, int64_t dstate, int path) {
 }
 
 // The chain bf16 kernel: asked for, or chosen by SSD_PATH_AUTO when the head
-// pairs fill the machine (same shape rule as ssd::use_chain_bf16).
-bool chain_path(int dtype, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
-                int ngroups, int path) {
+// pairs fill the machine, or (segmented) when pairs times segments do (same
+// shape rule as ssd::use_chain_bf16).  Fills *plan.
+bool chain_path(int dtype, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                int64_t dstate, int ngroups, int path, ssd::ChainPlan* plan) {
   const bool shape = dtype == SSD_BF16 && headdim == 64 && (dstate == 64 || dstate == 128) &&
                      (nheads / ngroups) % 2 == 0;
   if (!shape) return false;
+  *plan = ssd::ChainPlan{};
+  plan->span = (seqlen + 127) / 128;
   if (path == SSD_PATH_CHAIN) return true;
-  return path == SSD_PATH_AUTO && ssd::chain_fills_machine(batch, nheads);
+  if (path == SSD_PATH_CHAIN_SEGMENTED) {
+    *plan = ssd::chain_plan(batch, seqlen, nheads, true);
+    return true;
+  }
+  if (path != SSD_PATH_AUTO) return false;
+  if (ssd::chain_fills_machine(batch, nheads)) return true;
+  *plan = ssd::chain_plan(batch, seqlen, nheads, false);
+  return plan->nseg > 1;
 }
 
-bool path_valid(int path) { return path >= SSD_PATH_AUTO && path <= SSD_PATH_CHAIN; }
+bool path_valid(int path) {
+  return (path >= SSD_PATH_AUTO && path <= SSD_PATH_CHAIN) || path == SSD_PATH_CHAIN_SEGMENTED;
+}
 
 // Shape checks shared by the workspace query and the entry point.
 // varlen: the call carries seq_idx (packed sequences).  On the staged path its
@@ -118,9 +132,19 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
     lay->total = 0;
     return SSD_OK;
   }
-  if (chain_path(dtype, batch, nheads, headdim, dstate, ngroups, path) && seqlen > 0 && batch > 0) {
+  if (seqlen > 0 && batch > 0 &&
+      chain_path(dtype, batch, seqlen, nheads, headdim, dstate, ngroups, path, &lay->plan)) {
     lay->chain = true;
     lay->total = 0;
+    if (lay->plan.nseg > 1) {  // unit end states and decays of the state-only pass
+      int64_t units, stn;
+      if (!mul_ok(batch * nheads, lay->plan.nunits, &units) || !mul_ok(units, pn, &stn))
+        return SSD_ERR_INVALID_ARG;
+      if (units > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+      lay->off_cs_states = 0;
+      lay->off_cs_decay = round_up((size_t)stn * 4);
+      lay->total = lay->off_cs_decay + round_up((size_t)units * 4);
+    }
     return SSD_OK;
   }
   if (fused_path(dtype, headdim, dstate, path) && seqlen > 0 && batch > 0) {
@@ -346,7 +370,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.b = batch; p.L = seqlen; p.H = nheads; p.P = headdim; p.N = dstate; p.G = ngroups;
   p.Q = chunk_size; p.nc = lay.nc; p.bf16 = dtype == SSD_BF16;
   char* ws = static_cast<char*>(workspace);
-  const bool staged_ws = lay.total && !lay.fused;
+  const bool staged_ws = lay.total && !lay.fused && !lay.chain;
   p.ws_dt = staged_ws ? reinterpret_cast<float*>(ws + lay.off_dt) : nullptr;
   p.ws_cum = staged_ws ? reinterpret_cast<float*>(ws + lay.off_cum) : nullptr;
   p.ws_states = staged_ws ? reinterpret_cast<float*>(ws + lay.off_states) : nullptr;
@@ -358,6 +382,11 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
   p.fs_flags = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_flags) : nullptr;
   p.fs_ctl = lay.fused ? reinterpret_cast<unsigned*>(ws + lay.off_ctl) : nullptr;
   p.fused_kind = path == SSD_PATH_FUSED_HEAD ? 1 : path == SSD_PATH_FUSED_GROUP ? 2 : 0;
+  p.chain = lay.plan;
+  p.cs_states = lay.chain && lay.plan.nseg > 1 ? reinterpret_cast<float*>(ws + lay.off_cs_states)
+                                               : nullptr;
+  p.cs_decay = lay.chain && lay.plan.nseg > 1 ? reinterpret_cast<float*>(ws + lay.off_cs_decay)
+                                              : nullptr;
 
   auto mark = [&](int i) -> bool {
     return !timing || hipEventRecord(timing->ev[i], stream) == hipSuccess;
@@ -372,8 +401,12 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     return SSD_OK;
   }
   if (lay.chain) {
-    if (!mark(1) || !mark(2) || !mark(3)) return SSD_ERR_HIP;
-    if (ssd::launch_chain_bf16(p, stream) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
+    // segmented: the state-only units (reported as the chunk-state stage),
+    // then the chain (reported as the chunk scan)
+    if (!mark(1)) return SSD_ERR_HIP;
+    if (ssd::launch_chain_bf16(p, stream, 0) != hipSuccess || !mark(2) || !mark(3))
+      return SSD_ERR_HIP;
+    if (ssd::launch_chain_bf16(p, stream, 1) != hipSuccess || !mark(4)) return SSD_ERR_HIP;
     if (timing) timing->recorded = true;
     return SSD_OK;
   }
@@ -471,9 +504,10 @@ int ssd_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const vo
   const int taken = ssd_scan_fwd_taken_path(batch, seqlen, nheads, headdim, dstate, ngroups,
                                             chunk_size, dtype, 0, SSD_PATH_AUTO);
   if (taken < 0) return taken;
-  const int path = taken == SSD_PATH_STAGED ? SSD_PATH_STAGED
-                   : taken == SSD_PATH_FUSED_HEAD ? SSD_PATH_FUSED_HEAD
-                                                  : SSD_PATH_AUTO;
+  const int path = taken == SSD_PATH_STAGED                ? SSD_PATH_STAGED
+                   : taken == SSD_PATH_FUSED_HEAD          ? SSD_PATH_FUSED_HEAD
+                   : taken == SSD_PATH_CHAIN_SEGMENTED ? SSD_PATH_CHAIN_SEGMENTED
+                                                           : SSD_PATH_AUTO;
   int64_t rows = batch;
   if (lay.total > SSD_NOALLOC_SCRATCH_BYTES) {
     Layout one;
@@ -551,7 +585,7 @@ int ssd_scan_fwd_taken_path(int64_t batch, int64_t seqlen, int64_t nheads, int64
                         varlen != 0, kernel_path, &lay);
   if (st != SSD_OK) return st;
   if (lay.decode) return SSD_PATH_STEP;
-  if (lay.chain) return SSD_PATH_CHAIN;
+  if (lay.chain) return lay.plan.nseg > 1 ? SSD_PATH_CHAIN_SEGMENTED : SSD_PATH_CHAIN;
   if (lay.fused)
     return kernel_path == SSD_PATH_FUSED_GROUP && !varlen ? SSD_PATH_FUSED_GROUP
                                                          : SSD_PATH_FUSED_HEAD;

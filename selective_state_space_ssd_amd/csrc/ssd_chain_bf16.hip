@@ -130,14 +130,29 @@ struct ChainLds {
 };
 }  // namespace
 
-template <int N, bool GATE>
+// Workgroup wi = (piece, pair) with the pairs fastest (the pairs of a group stay
+// contiguous, so they share an XCD).  A piece is a range of `span` blocks:
+//  * STATE_ONLY = false: a segment of the sequence.  Segment 0 starts from
+//    initial_states (or zero); segment s > 0 from initial_states folded with the
+//    local end states of the units 0 .. s * units_per_seg - 1 (written by a
+//    STATE_ONLY launch before): H = D_u H + E_u in unit order.  The outputs of
+//    the segment's blocks are written; the last segment writes final_states.
+//    Unsegmented: one segment of all blocks.
+//  * STATE_ONLY = true: a unit.  From a zero state, only the state recurrence
+//    runs over the unit's blocks (no C, no output); the end state E_u goes to
+//    seg_states [b, H, nunits] blocks of P x N floats (row-major [p][n]) and
+//    D_u, the product of the blocks' decays (0 where a sequence starts inside
+//    the unit), to seg_decay [b, H, nunits].
+template <int N, bool GATE, bool STATE_ONLY>
 __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const bf16_t* __restrict__ dt_raw, const float* __restrict__ A,
     const float* __restrict__ dt_bias, float dt_min, float dt_max, const float* __restrict__ Dv,
     const bf16_t* __restrict__ z, bf16_t* __restrict__ out, const float* __restrict__ init,
     float* __restrict__ final_states, const int32_t* __restrict__ seq, int64_t L, int64_t H,
-    int64_t G, int64_t nblk, int64_t nwg) {
+    int64_t G, int64_t nblk, int64_t nwg, int64_t npairs, int64_t span,
+    float* __restrict__ seg_states, float* __restrict__ seg_decay, int64_t nunits,
+    int64_t units_per_seg) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
   constexpr int KN = N / 32;                   // contraction steps over n
   constexpr int NT = N / 16;                   // 16-row n tiles of the state
@@ -155,9 +170,13 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
   // division runs on the vector unit and would leave every address derived
   // from it in vector registers); the head pairs of a group share an XCD
   const int wi = (int)xcd_remap(blockIdx.x, nwg);
+  const int piece = __builtin_amdgcn_readfirstlane(wi / (int)npairs);
+  const int pair = __builtin_amdgcn_readfirstlane(wi % (int)npairs);
   const int hp = (int)H / kPair;
-  const int64_t b = __builtin_amdgcn_readfirstlane(wi / hp);
-  const int64_t h = __builtin_amdgcn_readfirstlane(kPair * (wi % hp) + hd);
+  const int64_t b = __builtin_amdgcn_readfirstlane(pair / hp);
+  const int64_t h = __builtin_amdgcn_readfirstlane(kPair * (pair % hp) + hd);
+  const int64_t c_begin = (int64_t)piece * span;
+  const int64_t c_end = c_begin + span < nblk ? c_begin + span : nblk;
   const int64_t grp = __builtin_amdgcn_readfirstlane((int)h / ((int)H / (int)G));
   const int64_t xs = H * kP, bs = G * N;
   const uint32_t xrow = (uint32_t)(xs * 2), brow = (uint32_t)(bs * 2);  // row pitches, bytes
@@ -187,7 +206,23 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
   f4 Hs[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    Hs[j] = init ? ld4(init + ((b * H + h) * kP + pme) * N + 16 * j + 4 * g) : zero4();
+    Hs[j] = init && !STATE_ONLY ? ld4(init + ((b * H + h) * kP + pme) * N + 16 * j + 4 * g)
+                                : zero4();
+  if constexpr (!STATE_ONLY) {
+    // a later segment: fold in the end states of the units before it
+    const int64_t ubase = (b * H + h) * nunits;
+    const int64_t nfold = (int64_t)piece * units_per_seg;
+    for (int64_t u = 0; u < nfold; ++u) {
+      const float du = seg_decay[ubase + u];
+      const float* E = seg_states + ((ubase + u) * kP + pme) * N + 4 * g;
+      f4 e[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) e[j] = ld4(E + 16 * j);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) Hs[j] = Hs[j] * du + e[j];
+    }
+  }
+  float dprod = 1.0f;  // product of the decays of the blocks run (STATE_ONLY)
 
   // ---- prefetch registers: the next block's B, C and x tiles ----
   uint4 pb[PB], pc[PB], px[PX];
@@ -207,7 +242,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
       const uint32_t o = (uint32_t)row * brow + (uint32_t)col * 2;
       pb[k] = bld16(brs, o);
-      pc[k] = bld16(crs, o);
+      if constexpr (!STATE_ONLY) pc[k] = bld16(crs, o);
     }
     const auto xrs = row_rsrc(x + ((b * L + t0) * H + h) * kP, last * xrow + kP * 2);
 #pragma unroll
@@ -291,6 +326,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         dt_l[t] = dv[k];
         k_l[t] = ks[k];
         w_l[t] = ks[k] == klast ? __expf(cum_last - cum[k]) * dv[k] : 0.0f;
+      } else if (STATE_ONLY) {
+        continue;
       } else if (wt == 1) {
         et_l[t] = ks[k] == 0 ? __expf(cum[k]) : 0.0f;
       } else if (wt == 2) {
@@ -301,7 +338,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     }
     // v rows: 1, 2 (wave 0), 3, 4 (wave 1), 5 (wave 2), 6, 7 (wave 3)
 #pragma unroll
-    for (int i = 1; i < CT; ++i) {
+    for (int i = 1; i < (STATE_ONLY ? 1 : CT); ++i) {
       const int owner = i <= 2 ? 0 : i <= 4 ? 1 : i == 5 ? 2 : 3;
       if (owner != wt) continue;
       const float ci = __shfl(cum[1], 8 * i - 1, kWave);
@@ -316,11 +353,46 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     if (wt == 0 && lane == 0) dl_l[hd] = klast == 0 ? __expf(cum_last) : -1.0f;
   };
 
-  prefetch(0);
-  load_dt(0);
-  tables(0);
+  // ---- state: H = exp(cum_last) H + B^T (w o x); slots t = 32 kt + 4 g + j
+  // (j < 4) and 32 kt + 16 + 4 g + j - 4 ----
+  auto state_update = [&]() {
+    const float dlv = dl_l[hd];
+    const float dl = dlv < 0.0f ? 0.0f : dlv;
+    dprod *= dl;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) Hs[j] *= dl;
+#pragma unroll
+    for (int kt = 0; kt < CQ / 32; ++kt) {
+      const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;
+      const s16x4 xa = tr_rows(Xl, kXP, r0, 16 * wt, m), xb = tr_rows(Xl, kXP, r1, 16 * wt, m);
+      const f4 w0 = *reinterpret_cast<const f4*>(w_l + r0);
+      const f4 w1 = *reinterpret_cast<const f4*>(w_l + r1);
+      const float xw[8] = {to_f32((bf16_t)xa[0]) * w0[0], to_f32((bf16_t)xa[1]) * w0[1],
+                           to_f32((bf16_t)xa[2]) * w0[2], to_f32((bf16_t)xa[3]) * w0[3],
+                           to_f32((bf16_t)xb[0]) * w1[0], to_f32((bf16_t)xb[1]) * w1[1],
+                           to_f32((bf16_t)xb[2]) * w1[2], to_f32((bf16_t)xb[3]) * w1[3]};
+      s16x8 whi, wlo;
+      split_bf16x8(xw, whi, wlo);
+#pragma unroll
+      for (int j0 = 0; j0 < NT; j0 += 4) {  // four n-tiles at a time, as in C.H
+        s16x8 bops[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bops[q] = cat8(tr_rows(Bl, BP, r0, 16 * (j0 + q), m),
+                         tr_rows(Bl, BP, r1, 16 * (j0 + q), m));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Hs[j0 + q] = mfma16(bops[q], whi, Hs[j0 + q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Hs[j0 + q] = mfma16(bops[q], wlo, Hs[j0 + q]);
+      }
+    }
+  };
 
-  for (int64_t c = 0; c < nblk; ++c) {
+  prefetch(c_begin);
+  load_dt(c_begin);
+  tables(c_begin);
+
+  for (int64_t c = c_begin; c < c_end; ++c) {
     // A fresh, opaque copy of the lane index each block: per-lane offsets are
     // then recomputed where they are used (a few integer ops) instead of
     // dozens of them being held in registers across the whole loop.
@@ -338,7 +410,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       const int e = k * kChainThreads + tid;
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
       *reinterpret_cast<uint4*>(Bl + row * BP + col) = pb[k];
-      *reinterpret_cast<uint4*>(Cl + row * CP + col) = pc[k];
+      if constexpr (!STATE_ONLY) *reinterpret_cast<uint4*>(Cl + row * CP + col) = pc[k];
     }
 #pragma unroll
     for (int k = 0; k < PX; ++k) {
@@ -349,7 +421,16 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     __syncthreads();
 
     // ---- next block's tiles in flight ----
-    if (c + 1 < nblk) prefetch(c + 1);
+    if (c + 1 < c_end) prefetch(c + 1);
+    if constexpr (STATE_ONLY) {
+      state_update();
+      __syncthreads();  // tiles and step tables read: the next block's may come
+      if (c + 1 < c_end) {
+        load_dt(c + 1);
+        tables(c + 1);
+      }
+      continue;
+    }
     // ---- in-block part: t-tiles wt and 7 - wt of this head ----
     // G^T slots (g, j): n = 32 kn + 8 g + j.  Y^T slots (g, j): s = 32 cc +
     // 4 g + j (j < 4) and 32 cc + 16 + 4 g + j - 4, the rows of the two
@@ -469,46 +550,14 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       }
     }
 
-    // ---- state: H = exp(cum_last) H + B^T (w o x); slots t = 32 kt + 4 g + j
-    // (j < 4) and 32 kt + 16 + 4 g + j - 4 ----
-    {
-      const float dlv = dl_l[hd];
-      const float dl = dlv < 0.0f ? 0.0f : dlv;
-#pragma unroll
-      for (int j = 0; j < NT; ++j) Hs[j] *= dl;
-#pragma unroll
-      for (int kt = 0; kt < CQ / 32; ++kt) {
-        const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;
-        const s16x4 xa = tr_rows(Xl, kXP, r0, 16 * wt, m), xb = tr_rows(Xl, kXP, r1, 16 * wt, m);
-        const f4 w0 = *reinterpret_cast<const f4*>(w_l + r0);
-        const f4 w1 = *reinterpret_cast<const f4*>(w_l + r1);
-        const float xw[8] = {to_f32((bf16_t)xa[0]) * w0[0], to_f32((bf16_t)xa[1]) * w0[1],
-                             to_f32((bf16_t)xa[2]) * w0[2], to_f32((bf16_t)xa[3]) * w0[3],
-                             to_f32((bf16_t)xb[0]) * w1[0], to_f32((bf16_t)xb[1]) * w1[1],
-                             to_f32((bf16_t)xb[2]) * w1[2], to_f32((bf16_t)xb[3]) * w1[3]};
-        s16x8 whi, wlo;
-        split_bf16x8(xw, whi, wlo);
-#pragma unroll
-        for (int j0 = 0; j0 < NT; j0 += 4) {  // four n-tiles at a time, as in C.H
-          s16x8 bops[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            bops[q] = cat8(tr_rows(Bl, BP, r0, 16 * (j0 + q), m),
-                           tr_rows(Bl, BP, r1, 16 * (j0 + q), m));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) Hs[j0 + q] = mfma16(bops[q], whi, Hs[j0 + q]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) Hs[j0 + q] = mfma16(bops[q], wlo, Hs[j0 + q]);
-        }
-      }
-    }
+    state_update();
     __syncthreads();  // staging tiles dead: the output tiles take their space
 
     // The next block's dt, then this block's z, are loaded here, once the
     // output registers are free (held from earlier, they would be spilled, and
     // the wait for a spilled value waits for every load issued before it); the
     // barrier and the table work cover their latency.
-    if (c + 1 < nblk) load_dt(c + 1);
+    if (c + 1 < c_end) load_dt(c + 1);
     // x, z and out rows of this head in the block: the same range
     const uint32_t nxb = (uint32_t)last * xrow + kP * 2;
     uint4 zr[PX];
@@ -536,7 +585,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     __syncthreads();
 
     // the tables are free until the next staging: fill them for block c + 1
-    if (c + 1 < nblk) tables(c + 1);
+    if (c + 1 < c_end) tables(c + 1);
 
     // ---- epilogue: 8 consecutive p of one step per thread piece ----
     const auto ors = row_rsrc(out + ((b * L + t0) * H + h) * kP, nxb);
@@ -566,7 +615,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     __syncthreads();  // the output tiles are read before the next staging
   }
 
-  if (final_states) {
+  if constexpr (STATE_ONLY) {
+    const int64_t slot = (b * H + h) * nunits + piece;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) st4(seg_states + (slot * kP + pme) * N + 16 * j + 4 * g, Hs[j]);
+    if (wt == 0 && lane == 0) seg_decay[slot] = dprod;
+  } else if (final_states && c_end == nblk) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
       st4(final_states + ((b * H + h) * kP + pme) * N + 16 * j + 4 * g, Hs[j]);
@@ -587,32 +641,78 @@ bool chain_fills_machine(int64_t b, int64_t H) {
   return n > 0 && 4 * n >= 3 * kChainCUs * rounds;
 }
 
+ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force) {
+  ChainPlan pl;
+  const int64_t npairs = chain_workgroups(b, H), nblk = (L + CQ - 1) / CQ;
+  pl.nseg = 1;
+  pl.span = nblk;
+  if (npairs <= 0 || nblk < 2) return pl;
+  // segments: as many as fill one round of the compute units; by default only
+  // when each segment keeps at least 16 blocks and the workgroups fill the
+  // round at least 3/4 (below that, the fused path)
+  int64_t nseg = kChainCUs / npairs;
+  if (force) {
+    nseg = nseg < 2 ? 2 : nseg;
+  } else {
+    const int64_t by_len = nblk / 16;
+    nseg = nseg < by_len ? nseg : by_len;
+    if (nseg < 2 || 4 * npairs * nseg < 3 * kChainCUs) return pl;
+  }
+  nseg = nseg < nblk ? nseg : nblk;
+  const int64_t span = (nblk + nseg - 1) / nseg;
+  pl.nseg = (nblk + span - 1) / span;
+  if (pl.nseg < 2) return pl;
+  pl.span = span;
+  // units of the state-only pass: halve the span while it stays even and
+  // above 8 blocks and the pass has fewer than two workgroups per CU
+  int64_t unit = span;
+  while (unit % 2 == 0 && unit > 8 && npairs * (pl.nseg - 1) * (span / unit) < 2 * kChainCUs)
+    unit /= 2;
+  pl.unit = unit;
+  pl.nunits = (pl.nseg - 1) * (span / unit);
+  return pl;
+}
+
 template <int N>
-static void launch_chain_n(const Problem& p, hipStream_t s) {
-  const int64_t nblk = (p.L + CQ - 1) / CQ, nwg = chain_workgroups(p.b, p.H);
-  const dim3 grid((unsigned)nwg);
+static void launch_chain_n(const Problem& p, hipStream_t s, int pass) {
+  const int64_t nblk = (p.L + CQ - 1) / CQ, npairs = chain_workgroups(p.b, p.H);
   const auto* xb = static_cast<const bf16_t*>(p.x);
   const auto* Bb = static_cast<const bf16_t*>(p.B);
   const auto* Cb = static_cast<const bf16_t*>(p.C);
   const auto* db = static_cast<const bf16_t*>(p.dt);
   const auto* zb = static_cast<const bf16_t*>(p.z);
   auto* ob = static_cast<bf16_t*>(p.out);
+  const ChainPlan& pl = p.chain;
+  if (pass == 0) {  // state-only units (segmented path only)
+    const int64_t nwg = npairs * pl.nunits;
+    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false, true>), dim3((unsigned)nwg),
+                       dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
+                       p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
+                       nblk, nwg, npairs, pl.unit, p.cs_states, p.cs_decay, pl.nunits,
+                       pl.unit > 0 ? pl.span / pl.unit : 0);
+    return;
+  }
+  const int64_t nwg = npairs * pl.nseg;
+  const int64_t ups = pl.nseg > 1 ? pl.span / pl.unit : 0;
   if (p.z)
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, true>), grid, dim3(kChainThreads), 0, s, xb, Bb,
-                       Cb, db, p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.init,
-                       p.final_states, p.seq_idx, p.L, p.H, p.G, nblk, nwg);
+    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, true, false>), dim3((unsigned)nwg),
+                       dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
+                       p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
+                       nblk, nwg, npairs, pl.span, p.cs_states, p.cs_decay, pl.nunits, ups);
   else
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false>), grid, dim3(kChainThreads), 0, s, xb, Bb,
-                       Cb, db, p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.init,
-                       p.final_states, p.seq_idx, p.L, p.H, p.G, nblk, nwg);
+    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false, false>), dim3((unsigned)nwg),
+                       dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
+                       p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
+                       nblk, nwg, npairs, pl.span, p.cs_states, p.cs_decay, pl.nunits, ups);
 }
 
-hipError_t launch_chain_bf16(const Problem& p, hipStream_t s) {
+hipError_t launch_chain_bf16(const Problem& p, hipStream_t s, int pass) {
   if (p.L <= 0 || p.b <= 0) return hipSuccess;
+  if (pass == 0 && p.chain.nseg < 2) return hipSuccess;
   if (p.N == 128)
-    launch_chain_n<128>(p, s);
+    launch_chain_n<128>(p, s, pass);
   else
-    launch_chain_n<64>(p, s);
+    launch_chain_n<64>(p, s, pass);
   return hipGetLastError();
 }
 

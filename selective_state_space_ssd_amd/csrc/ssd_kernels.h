@@ -6,6 +6,11 @@
 
 namespace ssd {
 
+// Segments of the chain bf16 kernel (chain_plan below).
+struct ChainPlan {
+  int64_t nseg = 1, span = 0, unit = 0, nunits = 0;
+};
+
 // One validated problem.  Sizes follow the notation of the scan:
 // b = batch, L = seqlen, H = nheads, P = headdim, N = dstate, G = ngroups,
 // Q = chunk_size, nc = ceil(L / Q).
@@ -42,6 +47,10 @@ struct Problem {
   unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
   unsigned* fs_ctl;      // 8 ticket counters, then the error word
   int fused_kind;        // 0: choose, 1: per-head kernel, 2: group kernel
+  // chain bf16 kernel: segments, and the state-only pass's outputs
+  ChainPlan chain;
+  float* cs_states = nullptr;  // [b, H, nunits] P x N row-major unit end states
+  float* cs_decay = nullptr;   // [b, H, nunits] unit decay products
   // Backward re-run only (fp32, four-heads chunk scan): with gate_dout set the
   // chunk scan's epilogue writes dY = dout silu(z) to out and dz = dout y
   // silu'(z) to gate_dz in place of y (z is then the gate input).
@@ -105,7 +114,16 @@ constexpr int64_t kChainCUs = 256;
 bool use_chain_bf16(const Problem& p);
 int64_t chain_workgroups(int64_t b, int64_t H);
 bool chain_fills_machine(int64_t b, int64_t H);
-hipError_t launch_chain_bf16(const Problem& p, hipStream_t stream);
+// Segmented chain: when the head pairs alone do not fill the machine, the
+// sequence is cut into nseg segments of `span` 128-step blocks (one
+// workgroup per (pair, segment)); a state-only launch first computes the
+// local end state of every unit of `unit` blocks before the last segment
+// (nunits per head), and each segment starts from the units before it folded
+// into its entering state.  nseg = 1: the unsegmented chain (no workspace).
+// force: segment whenever the sequence has two blocks or more (testing).
+ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force);
+// pass 0: the state-only units (nothing when nseg = 1); pass 1: the chain.
+hipError_t launch_chain_bf16(const Problem& p, hipStream_t stream, int pass);
 
 // Group form of the fused kernel: one workgroup per (block, group, head set).
 int64_t fused_group_units(const Problem& p);

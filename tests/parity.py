@@ -21,8 +21,9 @@ _PATH = ["auto"]
 
 @contextmanager
 def bf16_path(name):
-    """Run the enclosed run_gpu calls on kernel path `name` ("chain", "fused",
-    "fused_head", "fused_group", "staged" or "auto")."""
+    """Run the enclosed run_gpu calls on kernel path `name` ("chain",
+    "chain_segmented", "fused", "fused_head", "fused_group", "staged" or
+    "auto")."""
     ssd.path_code(name)  # reject unknown names here
     prev = _PATH[0]
     _PATH[0] = name
@@ -39,7 +40,8 @@ def current_path():
 
 def paths_for(dtype):
     """The kernel paths a problem of this dtype can take."""
-    return ("chain", "fused_head", "fused_group", "staged") if dtype == "bf16" else ("auto",)
+    return (("chain", "chain_segmented", "fused_head", "fused_group", "staged") if dtype == "bf16"
+            else ("auto",))
 
 
 def log(msg):

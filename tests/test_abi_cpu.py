@@ -144,6 +144,44 @@ def test_workspace_size_fused_bf16():
             assert _ws(b, L, H, P, N, G, Q, 1, path) == want
 
 
+def _chain_plan(b, L, H, force):
+    """(segments, blocks per segment, blocks per unit, units per head) of the
+    chain bf16 path: one segment unless the pairs alone do not fill the 256
+    compute units; then as many segments as fill one round, by default only
+    with at least 16 blocks each and the round at least 3/4 full."""
+    npairs, nblk = b * H // 2, -(-L // 128)
+    if npairs <= 0 or nblk < 2:
+        return 1, nblk, 0, 0
+    nseg = 256 // npairs
+    if force:
+        nseg = max(nseg, 2)
+    else:
+        nseg = min(nseg, nblk // 16)
+        if nseg < 2 or 4 * npairs * nseg < 3 * 256:
+            return 1, nblk, 0, 0
+    nseg = min(nseg, nblk)
+    span = -(-nblk // nseg)
+    nseg = -(-nblk // span)
+    if nseg < 2:
+        return 1, nblk, 0, 0
+    unit = span
+    while unit % 2 == 0 and unit > 8 and npairs * (nseg - 1) * (span // unit) < 512:
+        unit //= 2
+    return nseg, span, unit, (nseg - 1) * (span // unit)
+
+
+def _seg_ws(b, L, H, P, N, force):
+    nseg, _, _, nunits = _chain_plan(b, L, H, force)
+    return _r(b * H * nunits * P * N * 4) + _r(b * H * nunits * 4) if nseg > 1 else 0
+
+
+def test_chain_plan():
+    assert _chain_plan(1, 65536, 128, False) == (4, 128, 32, 12)   # the long sequence
+    assert _chain_plan(8, 4096, 64, False)[0] == 1                 # 256 pairs: no segments
+    assert _chain_plan(1, 1000, 8, True) == (8, 1, 1, 7)
+    assert _chain_plan(1, 1000, 8, False)[0] == 1
+
+
 def test_workspace_size_default_bf16():
     """Default bf16 path: the chain kernel (no workspace) when the heads of a
     group pair up and the pairs fill the machine, else the fused layout; the
@@ -157,13 +195,19 @@ def test_workspace_size_default_bf16():
             continue
         pairs_up = (H // G) % 2 == 0
         chain = pairs_up and _chain_fills(b, H)
-        assert _ws(b, L, H, P, N, G, Q, 1) == (0 if chain else _fused_ws(b, L, H, P, N))
+        seg = pairs_up and not chain and _chain_plan(b, L, H, False)[0] > 1
+        want = 0 if chain else _seg_ws(b, L, H, P, N, False) if seg else _fused_ws(b, L, H, P, N)
+        assert _ws(b, L, H, P, N, G, Q, 1) == want
+        assert ssd.taken_path(b, L, H, P, N, G, Q, 1) == (
+            "chain" if chain else "chain_segmented" if seg else "fused_head")
         assert _ws(b, L, H, P, N, G, Q, 1, "auto") == _ws(b, L, H, P, N, G, Q, 1)
         assert (_ws(b, L, H, P, N, G, Q, 1, "chain")
                 == (0 if pairs_up else _fused_ws(b, L, H, P, N)))
+        assert (_ws(b, L, H, P, N, G, Q, 1, "chain_segmented")
+                == (_seg_ws(b, L, H, P, N, True) if pairs_up else _fused_ws(b, L, H, P, N)))
         assert _ws(b, L, H, P, N, G, Q, 0, "chain") > 0  # fp32 stays staged
     assert _ws(8, 4096, 64, 64, 128, 8, 256, 1) == 0  # the bf16 8 x 4096 workload: chain
-    assert _ws(1, 65536, 128, 64, 128, 8, 256, 1) > 0  # the 1 x 65536 one: 64 pairs, fused
+    assert _ws(1, 65536, 128, 64, 128, 8, 256, 1) > 0  # the 1 x 65536 one: segmented chain
     assert _chain_fills(6, 64) and not _chain_fills(5, 64)  # 192 of 256 / 160 of 256
     assert _chain_fills(12, 64) and not _chain_fills(11, 64)  # 384 of 512 (3/4) / 352
 
@@ -193,7 +237,7 @@ def test_kernel_path_argument():
     """The path is an argument of each call: out-of-range codes are rejected,
     and asking for one path leaves every later query unchanged."""
     lib = ssd.load_library()
-    for bad in (-1, 6, 99):
+    for bad in (-1, 6, 8, 99):
         assert lib.ssd_scan_fwd_path_workspace_size(2, 300, 8, 64, 128, 2, 128, 1, 0, bad) == 0
     before = _ws(1, 65536, 128, 64, 128, 8, 256, 1)
     assert _ws(1, 65536, 128, 64, 128, 8, 256, 1, "chain") == 0
@@ -335,7 +379,7 @@ def call_path(path, seq=None, **changes):
 
 def test_path_entry_point_rejections():
     """ssd_scan_fwd_path validates like ssd_scan_fwd, and the path code too."""
-    for bad in (-1, 6, 1000):
+    for bad in (-1, 6, 8, 1000):
         assert call_path(bad) == INVALID
     for name, code in ssd.KERNEL_PATHS.items():
         assert call_path(code) == WORKSPACE, name            # valid, stops at workspace
@@ -353,7 +397,8 @@ def test_taken_path():
     """The path each call takes, after the documented fallbacks."""
     tp = ssd.taken_path
     assert tp(8, 4096, 64, 64, 128, 8, 256, 1) == "chain"           # pairs fill the machine
-    assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "fused_head"    # 64 pairs: fused
+    assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "chain_segmented"  # 64 pairs x 4 segments
+    assert tp(1, 1000, 8, 64, 128, 2, 256, 1) == "fused_head"       # too short to segment
     assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # fp32
     assert tp(2, 16, 32, 64, 128, 1, 128, 1) == "step"              # seqlen <= 16
     assert tp(2, 400, 6, 64, 128, 2, 256, 1, kernel_path="chain") == "fused_head"  # odd group

@@ -1,8 +1,9 @@
 """GPU checks specific to the chain bf16 kernel (one workgroup carries a pair
-of heads of one group through the whole sequence, the state in registers):
-block edges, agreement with the staged bf16 kernels, in-place continuation,
-run-to-run determinism, and the fallback for groups with an odd number of
-heads.  Every bf16 parity test elsewhere also runs on this path."""
+of heads of one group through the whole sequence, or one segment of it, the
+state in registers): block and segment edges, agreement with the staged bf16
+kernels, in-place continuation, run-to-run determinism, and the fallback for
+groups with an odd number of heads.  Every bf16 parity test elsewhere also
+runs on both the unsegmented and the segmented chain."""
 import numpy as np
 import pytest
 import torch
@@ -38,13 +39,67 @@ EDGES = [(L, N, H, G) for L in (17, 127, 128, 129, 255, 257) for (N, H, G) in
 @pytest.mark.parametrize("L,N,H,G", EDGES, ids=[f"L{e[0]}-N{e[1]}-H{e[2]}-G{e[3]}" for e in EDGES])
 def test_chain_block_edges(L, N, H, G):
     w, inp, t = _inputs(700 + L + N, 2, L, H, N, G)
-    log(f"test_chain_block_edges L={L} N={N} H={H} G={G}")
-    with bf16_path("chain"):
-        assert ssd.workspace_size(2, L, H, 64, N, G, 256, ssd.SSD_BF16, current_path()) == 0
-        out, fin = run_gpu(t, 256, init=t["initial_states"])
     ref, rfin = _oracle(inp)
-    compare("out", np64(out), ref, TOL["bf16"])
-    compare("final", np64(fin), rfin, TOL["bf16"])
+    for path in ("chain", "chain_segmented"):
+        log(f"test_chain_block_edges L={L} N={N} H={H} G={G} path={path}")
+        with bf16_path(path):
+            ws = ssd.workspace_size(2, L, H, 64, N, G, 256, ssd.SSD_BF16, current_path())
+            taken = ssd.taken_path(2, L, H, 64, N, G, 256, ssd.SSD_BF16, kernel_path=path)
+            # a one-block sequence is one segment; longer ones are cut into
+            # segments of one block here (few pairs), so every block edge is
+            # a segment edge
+            assert taken == ("chain" if path == "chain" or L <= 128 else "chain_segmented")
+            assert (ws == 0) == (taken == "chain")
+            out, fin = run_gpu(t, 256, init=t["initial_states"])
+        compare(f"out {path}", np64(out), ref, TOL["bf16"])
+        compare(f"final {path}", np64(fin), rfin, TOL["bf16"])
+
+
+# segments of several blocks, each cut into units for the state-only pass:
+# (b, L, H, G, N); the workgroups (pairs x segments) fill the 256 compute
+# units, the segment length is not a multiple of the block, L is ragged
+SEGMENTS = [(1, 40 * 128 - 37, 128, 8, 128), (2, 33 * 128 + 5, 64, 8, 64),
+            (1, 24 * 128, 96, 4, 128)]
+
+
+@pytest.mark.parametrize("b,L,H,G,N", SEGMENTS, ids=[f"b{s[0]}-L{s[1]}-H{s[2]}" for s in SEGMENTS])
+def test_chain_segments_with_units(b, L, H, G, N):
+    """Segments of several blocks whose entering states fold several units:
+    against the oracle on both heads of a pair in every (batch, group), and
+    against the unsegmented chain everywhere."""
+    w, inp, t = _inputs(760 + L, b, L, H, N, G)
+    with bf16_path("chain_segmented"):
+        assert ssd.taken_path(b, L, H, 64, N, G, 256, ssd.SSD_BF16,
+                              kernel_path="chain_segmented") == "chain_segmented"
+        log(f"test_chain_segments b={b} L={L} H={H} G={G} N={N}: segmented")
+        out, fin = run_gpu(t, 256, init=t["initial_states"])
+    with bf16_path("chain"):
+        log(f"test_chain_segments b={b} L={L} H={H} G={G} N={N}: unsegmented")
+        out1, fin1 = run_gpu(t, 256, init=t["initial_states"])
+    compare("segmented vs unsegmented out", np64(out), np64(out1), TOL["bf16"])
+    compare("segmented vs unsegmented final", np64(fin), np64(fin1), 1e-4)
+    mask = np.zeros((b, H), bool)
+    hpg = H // G
+    for bb in range(b):
+        for g in range(G):
+            lo = g * hpg + 2 * ((bb + g) % (hpg // 2))
+            mask[bb, lo:lo + 2] = True
+    ref, rfin = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                               z=inp["z"], dt_bias=inp["dt_bias"],
+                               initial_states=inp["initial_states"], return_final_states=True,
+                               head_mask=mask)
+    compare("out (sampled heads)", np64(out), ref, TOL["bf16"],
+            mask=np.broadcast_to(mask[:, None, :, None], ref.shape))
+    compare("final (sampled heads)", np64(fin), rfin, TOL["bf16"],
+            mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))
+
+
+def test_chain_segmented_is_the_default_for_the_long_sequence():
+    """batch 1 x 65536 at 128 heads: 64 pairs, four segments of 128 blocks,
+    units of 32 blocks for the state-only pass."""
+    assert ssd.taken_path(1, 65536, 128, 64, 128, 8, 256, ssd.SSD_BF16) == "chain_segmented"
+    assert ssd.workspace_size(1, 65536, 128, 64, 128, 8, 256, ssd.SSD_BF16) >= \
+        128 * 12 * 64 * 128 * 4
 
 
 @pytest.mark.parametrize("gate,skip,init", [(False, False, False), (True, False, True),
@@ -53,11 +108,12 @@ def test_chain_options(gate, skip, init):
     """Without the z gate, the D skip or an initial state."""
     w, inp, t = _inputs(710, 2, 600, 8, 128, 4, init=init, gate=gate, skip=skip)
     log(f"test_chain_options gate={gate} skip={skip} init={init}")
-    with bf16_path("chain"):
-        out, fin = run_gpu(t, 256, init=t["initial_states"] if init else None)
     ref, rfin = _oracle(inp, init=init)
-    compare("out", np64(out), ref, TOL["bf16"])
-    compare("final", np64(fin), rfin, TOL["bf16"])
+    for path in ("chain", "chain_segmented"):
+        with bf16_path(path):
+            out, fin = run_gpu(t, 256, init=t["initial_states"] if init else None)
+        compare(f"out {path}", np64(out), ref, TOL["bf16"])
+        compare(f"final {path}", np64(fin), rfin, TOL["bf16"])
 
 
 def test_chain_matches_staged():

@@ -130,20 +130,16 @@ struct ChainLds {
 };
 }  // namespace
 
-// Workgroup wi = (piece, pair) with the pairs fastest (the pairs of a group stay
-// contiguous, so they share an XCD).  A piece is a range of `span` blocks:
-//  * STATE_ONLY = false: a segment of the sequence.  Segment 0 starts from
-//    initial_states (or zero); segment s > 0 from initial_states folded with the
-//    local end states of the units 0 .. s * units_per_seg - 1 (written by a
-//    STATE_ONLY launch before): H = D_u H + E_u in unit order.  The outputs of
-//    the segment's blocks are written; the last segment writes final_states.
-//    Unsegmented: one segment of all blocks.
-//  * STATE_ONLY = true: a unit.  From a zero state, only the state recurrence
-//    runs over the unit's blocks (no C, no output); the end state E_u goes to
-//    seg_states [b, H, nunits] blocks of P x N floats (row-major [p][n]) and
-//    D_u, the product of the blocks' decays (0 where a sequence starts inside
-//    the unit), to seg_decay [b, H, nunits].
-template <int N, bool GATE, bool STATE_ONLY>
+// Workgroup wi = (segment, pair) with the pairs fastest (the pairs of a group
+// stay contiguous, so they share an XCD).  A segment is a range of `span`
+// blocks (unsegmented: one segment of all blocks).  Segment 0 starts from
+// initial_states (or zero); segment s > 0 from initial_states folded with the
+// local end states E_u and decays D_u of the units 0 .. s * units_per_seg - 1
+// (seg_states [b, H, nunits] blocks of P x N floats, row-major [p][n], and
+// seg_decay [b, H, nunits], written by the unit-state kernel before): H =
+// D_u H + E_u in unit order.  The outputs of the segment's blocks are written;
+// the last segment writes final_states.
+template <int N, bool GATE>
 __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const bf16_t* __restrict__ dt_raw, const float* __restrict__ A,
@@ -151,7 +147,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const bf16_t* __restrict__ z, bf16_t* __restrict__ out, const float* __restrict__ init,
     float* __restrict__ final_states, const int32_t* __restrict__ seq, int64_t L, int64_t H,
     int64_t G, int64_t nblk, int64_t nwg, int64_t npairs, int64_t span,
-    float* __restrict__ seg_states, float* __restrict__ seg_decay, int64_t nunits,
+    const float* __restrict__ seg_states, const float* __restrict__ seg_decay, int64_t nunits,
     int64_t units_per_seg) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
   constexpr int KN = N / 32;                   // contraction steps over n
@@ -170,7 +166,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
   // division runs on the vector unit and would leave every address derived
   // from it in vector registers); the head pairs of a group share an XCD
   const int wi = (int)xcd_remap(blockIdx.x, nwg);
-  const int piece = __builtin_amdgcn_readfirstlane(wi / (int)npairs);
+  const int piece = __builtin_amdgcn_readfirstlane(wi / (int)npairs);  // the segment
   const int pair = __builtin_amdgcn_readfirstlane(wi % (int)npairs);
   const int hp = (int)H / kPair;
   const int64_t b = __builtin_amdgcn_readfirstlane(pair / hp);
@@ -206,9 +202,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
   f4 Hs[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j)
-    Hs[j] = init && !STATE_ONLY ? ld4(init + ((b * H + h) * kP + pme) * N + 16 * j + 4 * g)
-                                : zero4();
-  if constexpr (!STATE_ONLY) {
+    Hs[j] = init ? ld4(init + ((b * H + h) * kP + pme) * N + 16 * j + 4 * g) : zero4();
+  {
     // a later segment: fold in the end states of the units before it
     const int64_t ubase = (b * H + h) * nunits;
     const int64_t nfold = (int64_t)piece * units_per_seg;
@@ -222,7 +217,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       for (int j = 0; j < NT; ++j) Hs[j] = Hs[j] * du + e[j];
     }
   }
-  float dprod = 1.0f;  // product of the decays of the blocks run (STATE_ONLY)
 
   // ---- prefetch registers: the next block's B, C and x tiles ----
   uint4 pb[PB], pc[PB], px[PX];
@@ -242,7 +236,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
       const uint32_t o = (uint32_t)row * brow + (uint32_t)col * 2;
       pb[k] = bld16(brs, o);
-      if constexpr (!STATE_ONLY) pc[k] = bld16(crs, o);
+      pc[k] = bld16(crs, o);
     }
     const auto xrs = row_rsrc(x + ((b * L + t0) * H + h) * kP, last * xrow + kP * 2);
 #pragma unroll
@@ -326,8 +320,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         dt_l[t] = dv[k];
         k_l[t] = ks[k];
         w_l[t] = ks[k] == klast ? __expf(cum_last - cum[k]) * dv[k] : 0.0f;
-      } else if (STATE_ONLY) {
-        continue;
       } else if (wt == 1) {
         et_l[t] = ks[k] == 0 ? __expf(cum[k]) : 0.0f;
       } else if (wt == 2) {
@@ -338,7 +330,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     }
     // v rows: 1, 2 (wave 0), 3, 4 (wave 1), 5 (wave 2), 6, 7 (wave 3)
 #pragma unroll
-    for (int i = 1; i < (STATE_ONLY ? 1 : CT); ++i) {
+    for (int i = 1; i < CT; ++i) {
       const int owner = i <= 2 ? 0 : i <= 4 ? 1 : i == 5 ? 2 : 3;
       if (owner != wt) continue;
       const float ci = __shfl(cum[1], 8 * i - 1, kWave);
@@ -358,7 +350,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
   auto state_update = [&]() {
     const float dlv = dl_l[hd];
     const float dl = dlv < 0.0f ? 0.0f : dlv;
-    dprod *= dl;
 #pragma unroll
     for (int j = 0; j < NT; ++j) Hs[j] *= dl;
 #pragma unroll
@@ -410,7 +401,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       const int e = k * kChainThreads + tid;
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
       *reinterpret_cast<uint4*>(Bl + row * BP + col) = pb[k];
-      if constexpr (!STATE_ONLY) *reinterpret_cast<uint4*>(Cl + row * CP + col) = pc[k];
+      *reinterpret_cast<uint4*>(Cl + row * CP + col) = pc[k];
     }
 #pragma unroll
     for (int k = 0; k < PX; ++k) {
@@ -422,15 +413,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
 
     // ---- next block's tiles in flight ----
     if (c + 1 < c_end) prefetch(c + 1);
-    if constexpr (STATE_ONLY) {
-      state_update();
-      __syncthreads();  // tiles and step tables read: the next block's may come
-      if (c + 1 < c_end) {
-        load_dt(c + 1);
-        tables(c + 1);
-      }
-      continue;
-    }
     // ---- in-block part: t-tiles wt and 7 - wt of this head ----
     // G^T slots (g, j): n = 32 kn + 8 g + j.  Y^T slots (g, j): s = 32 cc +
     // 4 g + j (j < 4) and 32 cc + 16 + 4 g + j - 4, the rows of the two
@@ -615,12 +597,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     __syncthreads();  // the output tiles are read before the next staging
   }
 
-  if constexpr (STATE_ONLY) {
-    const int64_t slot = (b * H + h) * nunits + piece;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) st4(seg_states + (slot * kP + pme) * N + 16 * j + 4 * g, Hs[j]);
-    if (wt == 0 && lane == 0) seg_decay[slot] = dprod;
-  } else if (final_states && c_end == nblk) {
+  if (final_states && c_end == nblk) {
 #pragma unroll
     for (int j = 0; j < NT; ++j)
       st4(final_states + ((b * H + h) * kP + pme) * N + 16 * j + 4 * g, Hs[j]);
@@ -674,7 +651,7 @@ ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force) {
 }
 
 template <int N>
-static void launch_chain_n(const Problem& p, hipStream_t s, int pass) {
+static void launch_chain_n(const Problem& p, hipStream_t s) {
   const int64_t nblk = (p.L + CQ - 1) / CQ, npairs = chain_workgroups(p.b, p.H);
   const auto* xb = static_cast<const bf16_t*>(p.x);
   const auto* Bb = static_cast<const bf16_t*>(p.B);
@@ -683,24 +660,15 @@ static void launch_chain_n(const Problem& p, hipStream_t s, int pass) {
   const auto* zb = static_cast<const bf16_t*>(p.z);
   auto* ob = static_cast<bf16_t*>(p.out);
   const ChainPlan& pl = p.chain;
-  if (pass == 0) {  // state-only units (segmented path only)
-    const int64_t nwg = npairs * pl.nunits;
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false, true>), dim3((unsigned)nwg),
-                       dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
-                       p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
-                       nblk, nwg, npairs, pl.unit, p.cs_states, p.cs_decay, pl.nunits,
-                       pl.unit > 0 ? pl.span / pl.unit : 0);
-    return;
-  }
   const int64_t nwg = npairs * pl.nseg;
   const int64_t ups = pl.nseg > 1 ? pl.span / pl.unit : 0;
   if (p.z)
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, true, false>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, true>), dim3((unsigned)nwg),
                        dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
                        p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
                        nblk, nwg, npairs, pl.span, p.cs_states, p.cs_decay, pl.nunits, ups);
   else
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false, false>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false>), dim3((unsigned)nwg),
                        dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
                        p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
                        nblk, nwg, npairs, pl.span, p.cs_states, p.cs_decay, pl.nunits, ups);
@@ -708,11 +676,11 @@ static void launch_chain_n(const Problem& p, hipStream_t s, int pass) {
 
 hipError_t launch_chain_bf16(const Problem& p, hipStream_t s, int pass) {
   if (p.L <= 0 || p.b <= 0) return hipSuccess;
-  if (pass == 0 && p.chain.nseg < 2) return hipSuccess;
+  if (pass == 0) return p.chain.nseg < 2 ? hipSuccess : launch_unit_state_bf16(p, s);
   if (p.N == 128)
-    launch_chain_n<128>(p, s, pass);
+    launch_chain_n<128>(p, s);
   else
-    launch_chain_n<64>(p, s, pass);
+    launch_chain_n<64>(p, s);
   return hipGetLastError();
 }
 

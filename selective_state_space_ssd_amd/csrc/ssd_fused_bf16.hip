@@ -558,6 +558,173 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 
 // ---------------------------------------------------------------------------
 
+// Local end states of units of consecutive 128-step blocks, for the
+// segmented chain path: one workgroup per (unit, batch, head), the state
+// recurrence alone run over the unit's blocks from a zero state,
+//   E = exp(cum_last) E + B^T (w o x),  w_t = exp(cum_last - cum_t) dt_t,
+// with the block state product of the fused kernel above (the decay-weighted
+// B^T split hi/lo, x as it is, 32x32x16 bf16 MFMAs, E in the accumulators);
+// the next block's x and B tiles load while the current block is multiplied.
+// Outputs: E row-major [p][n] at seg_states[((b H + h) nunits + u) P N] and
+// D = the product of the blocks' exp(cum_last) (0 where a sequence starts
+// inside a block: the carried state does not survive it) at
+// seg_decay[(b H + h) nunits + u].  Workgroups are numbered with the heads
+// fastest, so the heads of a group (which read the same B rows) stay on one
+// XCD.
+template <int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void unit_state_bf16_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ dt_raw,
+    const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
+    const int32_t* __restrict__ seq, int64_t L, int64_t H, int64_t G, int64_t nblk, int64_t unit,
+    int64_t nunits, int64_t nbh, int64_t nwg, float* __restrict__ seg_states,
+    float* __restrict__ seg_decay) {
+  static_assert(N == 64 || N == 128, "dstate 64 or 128");
+  constexpr int NPT = N == 128 ? 2 : 1;     // p-halves of the state per wave
+  __shared__ __align__(16) bf16_t x_lds[FQ * kP];
+  __shared__ __align__(16) bf16_t b_lds[FQ * N];
+  __shared__ __align__(16) float w_lds[FQ];
+  __shared__ float dlast_lds;
+
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int i = lane % 32, kk = lane / 32;
+  const int wi = (int)xcd_remap(blockIdx.x, nwg);
+  const int64_t u = __builtin_amdgcn_readfirstlane(wi / (int)nbh);
+  const int bhi = __builtin_amdgcn_readfirstlane(wi % (int)nbh);
+  const int64_t b = __builtin_amdgcn_readfirstlane(bhi / (int)H);
+  const int64_t h = __builtin_amdgcn_readfirstlane(bhi % (int)H);
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / ((int)H / (int)G));
+  const int64_t c0 = u * unit, c1 = c0 + unit < nblk ? c0 + unit : nblk;
+  const int64_t xs = H * kP, bs = G * N;
+  const int snt = N == 128 ? wave : wave / 2;
+  const int spt0 = N == 128 ? 0 : wave % 2;
+  const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.0f;
+
+  f16x sacc[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) sacc[j] = zero16();
+  float dprod = 1.0f;
+
+  XTile<FQ> xt;
+  RowTile<FQ, N> bt;
+  auto load = [&](int64_t c) {
+    const int64_t t0 = c * FQ;
+    const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
+    load_x_tile<FQ>(xt, x + ((b * L + t0) * H + h) * kP, xs, last);
+    load_rows<FQ, N>(bt, Bm + ((b * L + t0) * G + g) * N, bs, last);
+  };
+  load(c0);
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * FQ;
+    const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
+    if (wave == 0) {
+      constexpr int E = FQ / kWave;
+      float dtv[E], cum[E], cum_last;
+      wave_dt_cumsum<bf16_t, FQ>(dt_raw, Ah, bias, dt_min, dt_max, b, c, h, L, H, nblk, nullptr,
+                                 nullptr, dtv, cum, &cum_last);
+      int ks[E] = {0, 0};
+      if (seq) {
+        int run = 0;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          const int64_t tt = t0 + lane * E + k;
+          if (tt >= 1 && tt < L) run += seq[b * L + tt] != seq[b * L + tt - 1];
+          ks[k] = run;
+        }
+        int incl = run;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int v = __shfl_up(incl, off, kWave);
+          if (lane >= off) incl += v;
+        }
+#pragma unroll
+        for (int k = 0; k < E; ++k) ks[k] += incl - run;
+      }
+      const int klast = __shfl(ks[1], kWave - 1, kWave);
+#pragma unroll
+      for (int k = 0; k < E; ++k)
+        w_lds[lane * E + k] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
+      if (lane == 0) dlast_lds = klast == 0 ? __expf(cum_last) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < XTile<FQ>::ITER; ++k) {  // x tile, permuted columns, swizzled chunks
+      const int e = (k * 256 + tid) * 8;
+      const int row = e / kP, col = e % kP;
+      const uint4 v = xt.v[k];
+      const uint32_t m = row > last ? 0u : 0xffffffffu;
+      const uint2 even = {((v.x & 0xffffu) | (v.y << 16)) & m, ((v.z & 0xffffu) | (v.w << 16)) & m};
+      const uint2 odd = {((v.x >> 16) | (v.y & 0xffff0000u)) & m,
+                         ((v.z >> 16) | (v.w & 0xffff0000u)) & m};
+      *reinterpret_cast<uint2*>(x_lds + x_off(row, col / 2)) = even;
+      *reinterpret_cast<uint2*>(x_lds + x_off(row, 32 + col / 2)) = odd;
+    }
+#pragma unroll
+    for (int k = 0; k < RowTile<FQ, N>::ITER; ++k) {  // B tile, swizzled chunks
+      const int e = k * 256 + tid;
+      const int row = e / (N / 8), chunk = e % (N / 8);
+      *reinterpret_cast<uint4*>(b_lds + row * N + ((chunk ^ bswz<N>(row)) << 3)) =
+          row > last ? uint4{0u, 0u, 0u, 0u} : bt.v[k];
+    }
+    __syncthreads();
+    if (c + 1 < c1) load(c + 1);  // the next tiles in flight under this block's products
+    const float dl = dlast_lds;
+    dprod *= dl;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) sacc[j] *= dl;
+#pragma unroll 2
+    for (int ks = 0; ks < FQ / 16; ++ks) {
+      const int r0 = 16 * ks + 8 * kk;
+      const s16x8 braw = b_tr_operand<N>(b_lds, r0, r0 + 4, 32 * snt);
+      const f4 w0 = *reinterpret_cast<const f4*>(w_lds + r0);
+      const f4 w1 = *reinterpret_cast<const f4*>(w_lds + r0 + 4);
+      const uint4 bw = __builtin_bit_cast(uint4, braw);
+      const float av[8] = {bf16_lo(bw.x) * w0[0], bf16_hi(bw.x) * w0[1], bf16_lo(bw.y) * w0[2],
+                           bf16_hi(bw.y) * w0[3], bf16_lo(bw.z) * w1[0], bf16_hi(bw.z) * w1[1],
+                           bf16_lo(bw.w) * w1[2], bf16_hi(bw.w) * w1[3]};
+      s16x8 ahi, alo;
+      split_bf16x8(av, ahi, alo);
+#pragma unroll
+      for (int j = 0; j < NPT; ++j) {
+        const s16x8 bop = x_tr_operand(x_lds, r0, r0 + 4, 32 * (spt0 + j));
+        sacc[j] = mfma32x32x16(ahi, bop, sacc[j]);
+        sacc[j] = mfma32x32x16(alo, bop, sacc[j]);
+      }
+    }
+    __syncthreads();  // tiles and w read before the next block is staged
+  }
+  // sacc[j][4 R + e] holds E at p = 2 i + spt0 + j, n = 32 snt + 8 R + 4 kk + e
+  const int64_t slot = (b * H + h) * nunits + u;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int p = 2 * i + spt0 + j;
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+      const int n0 = 32 * snt + 8 * R + 4 * kk;
+      st4(seg_states + (slot * kP + p) * N + n0,
+          f4{sacc[j][4 * R], sacc[j][4 * R + 1], sacc[j][4 * R + 2], sacc[j][4 * R + 3]});
+    }
+  }
+  if (tid == 0) seg_decay[slot] = dprod;
+}
+
+template <int N>
+static void launch_unit_state_n(const Problem& p, hipStream_t s) {
+  const int64_t nblk = fused_blocks(p.L), nbh = p.b * p.H, nwg = nbh * p.chain.nunits;
+  hipLaunchKernelGGL((unit_state_bf16_kernel<N>), dim3((unsigned)nwg), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(p.x), static_cast<const bf16_t*>(p.B),
+                     static_cast<const bf16_t*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max,
+                     p.seq_idx, p.L, p.H, p.G, nblk, p.chain.unit, p.chain.nunits, nbh, nwg,
+                     p.cs_states, p.cs_decay);
+}
+
+hipError_t launch_unit_state_bf16(const Problem& p, hipStream_t s) {
+  if (p.chain.nunits <= 0 || p.L <= 0 || p.b <= 0) return hipSuccess;
+  if (p.N == 128)
+    launch_unit_state_n<128>(p, s);
+  else
+    launch_unit_state_n<64>(p, s);
+  return hipGetLastError();
+}
+
 bool use_fused_bf16(const Problem& p) {
   return p.bf16 && p.P == kP && (p.N == 64 || p.N == 128);
 }

@@ -124,6 +124,9 @@ bool chain_fills_machine(int64_t b, int64_t H);
 ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force);
 // pass 0: the state-only units (nothing when nseg = 1); pass 1: the chain.
 hipError_t launch_chain_bf16(const Problem& p, hipStream_t stream, int pass);
+// The state-only units of the segmented chain (ssd_fused_bf16.hip): one
+// workgroup per (unit, batch, head) writes cs_states / cs_decay.
+hipError_t launch_unit_state_bf16(const Problem& p, hipStream_t stream);
 
 // Group form of the fused kernel: one workgroup per (block, group, head set).
 int64_t fused_group_units(const Problem& p);

@@ -4,6 +4,9 @@
                                            (from a --kernel-trace --stats run)
   python rocprof_summary.py --pmc DIR ...  per-kernel mean of each collected counter
                                            per dispatch (from --pmc runs)
+  python rocprof_summary.py --counters DIR       per kernel: instructions per wave (VALU,
+                                           MFMA, LDS), matrix-core and VALU busy shares
+                                           (from one SQ counter pass; see counters())
   python rocprof_summary.py --traffic FETCH_DIR WRITE_DIR KERNEL COPY_MIB SRC...
       HBM bytes per dispatch of the kernel whose name contains KERNEL, from a
       FETCH_SIZE run and a WRITE_SIZE run of the same command, each scaled by
@@ -54,6 +57,39 @@ def pmc_means(path):
             "select kernel_name, counter_name, value from counters_collection"):
         acc[kname][counter].append(float(value))
     return {k: {c: (sum(v) / len(v), len(v)) for c, v in d.items()} for k, d in acc.items()}
+
+
+SIMDS = 1024  # 256 compute units x 4
+XCDS = 8
+
+
+def counters(path):
+    """Per kernel, from a pass with SQ_WAVES, SQ_INSTS_VALU, SQ_INSTS_MFMA,
+    SQ_INSTS_LDS, SQ_ACTIVE_INST_VALU, SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE: instructions per wave, and the shares of SIMD time the
+    matrix cores and the vector ALU were busy.  GRBM_GUI_ACTIVE reads the
+    sum over the XCDs of each one's active cycles, so one XCD's is the sum / 8.
+    Matrix busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) / (cycles x
+    SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / (cycles x compute units), the
+    vendor's VALUBusy formula.  The matrix share is read against the same
+    counter on the matrix-core loop of libssd_peaks.so (the calibration line
+    of each summary)."""
+    out = {}
+    for k, c in pmc_means(path).items():
+        if "SQ_WAVES" not in c or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        waves = c["SQ_WAVES"][0]
+        cyc = c["GRBM_GUI_ACTIVE"][0] / XCDS
+        row = {"dispatches": c["SQ_WAVES"][1], "waves": waves, "gui_cycles_per_xcd": cyc}
+        for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS"):
+            if name in c and waves:
+                row[name.replace("SQ_INSTS_", "").lower() + "_per_wave"] = c[name][0] / waves
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and cyc:
+            row["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"][0] / (cyc * SIMDS)
+        if "SQ_ACTIVE_INST_VALU" in c and cyc:
+            row["valu_busy"] = c["SQ_ACTIVE_INST_VALU"][0] / (cyc * SIMDS / 4)
+        out[short(k)] = row
+    return out
 
 
 def sources_hash(paths):
@@ -109,6 +145,16 @@ if __name__ == "__main__":
         import json
         fd, wd, kern, mib = sys.argv[2], sys.argv[3], sys.argv[4], float(sys.argv[5])
         print(json.dumps(traffic(fd, wd, kern, mib, sys.argv[6:]), indent=1))
+    elif sys.argv[1] == "--counters":
+        for k, r in sorted(counters(sys.argv[2]).items(), key=lambda kv: -kv[1]["waves"]):
+            parts = [f"{k[:58]:58s} n={r['dispatches']:<4d}"]
+            for name in ("valu_per_wave", "mfma_per_wave", "lds_per_wave"):
+                if name in r:
+                    parts.append(f"{name.split('_')[0]}/wave={r[name]:9.1f}")
+            for name in ("mfma_busy", "valu_busy"):
+                if name in r:
+                    parts.append(f"{name}={100 * r[name]:5.1f}%")
+            print("  ".join(parts))
     elif sys.argv[1] == "--pmc":
         merged = defaultdict(dict)
         for d in sys.argv[2:]:

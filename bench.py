@@ -285,7 +285,7 @@ STAGE_KERNELS = {
     "staged": {"prep": "dt_cumsum_kernel", "chunk_state": "chunk_state kernel",
                "state_passing": "state_passing_kernel", "chunk_scan": "chunk scan kernel"},
     "chain": {"chunk_scan": "chain_scan_bf16_kernel"},
-    "chain_segmented": {"chunk_state": "chain_scan_bf16_kernel (state-only units)",
+    "chain_segmented": {"chunk_state": "unit_state_bf16_kernel",
                         "chunk_scan": "chain_scan_bf16_kernel (segments)"},
     "fused_head": {"prep": "fused set-up kernel", "chunk_scan": "fused_scan_bf16_kernel"},
     "fused_group": {"prep": "fused set-up kernel", "chunk_scan": "fused_group_bf16_kernel"},

@@ -237,7 +237,7 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
  *   SSD_PATH_CHAIN       the chain bf16 kernel (one workgroup per pair of
  *                        heads of a group for the whole sequence)
  *   SSD_PATH_CHAIN_SEGMENTED  the chain kernel over segments of the sequence:
- *                        a state-only pass computes the local end state of
+ *                        a unit-state pass computes the local end state of
  *                        every unit of blocks before the last segment, then
  *                        one workgroup per (pair, segment) runs the chain from
  *                        the units before it folded into its entering state;
@@ -281,8 +281,9 @@ size_t ssd_scan_fwd_path_workspace_size(int64_t batch, int64_t seqlen, int64_t n
                                         int chunk_size, int dtype, int varlen, int kernel_path);
 
 /* The kernel path a call with these arguments takes: SSD_PATH_STAGED,
- * SSD_PATH_FUSED_HEAD, SSD_PATH_FUSED_GROUP, SSD_PATH_CHAIN or SSD_PATH_STEP
- * (the step kernel of seqlen <= 16), after the fallbacks above; kernel_path
+ * SSD_PATH_FUSED_HEAD, SSD_PATH_FUSED_GROUP, SSD_PATH_CHAIN,
+ * SSD_PATH_CHAIN_SEGMENTED or SSD_PATH_STEP (the step kernel of seqlen <= 16),
+ * after the fallbacks above; kernel_path
  * is what the call asks for (SSD_PATH_AUTO for ssd_scan_fwd).  A negative
  * status for arguments the call would reject.  Pure host computation. */
 int ssd_scan_fwd_taken_path(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -473,7 +474,7 @@ int ssd_abi_version(void);
  * state --, chunk state, state passing, chunk scan).  On the fused path prep
  * is the set-up kernel, the scan kernel is reported as chunk scan and the two
  * middle stages are empty; on the chain path its kernel is reported as chunk
- * scan (on the segmented chain the state-only pass as chunk state) and the
+ * scan (on the segmented chain the unit-state pass as chunk state) and the
  * other stages are empty.  Returns SSD_OK or SSD_ERR_HIP /
  * SSD_ERR_INVALID_ARG.
  */

@@ -136,7 +136,7 @@ int check_shapes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
       chain_path(dtype, batch, seqlen, nheads, headdim, dstate, ngroups, path, &lay->plan)) {
     lay->chain = true;
     lay->total = 0;
-    if (lay->plan.nseg > 1) {  // unit end states and decays of the state-only pass
+    if (lay->plan.nseg > 1) {  // unit end states and decays of the unit-state pass
       int64_t units, stn;
       if (!mul_ok(batch * nheads, lay->plan.nunits, &units) || !mul_ok(units, pn, &stn))
         return SSD_ERR_INVALID_ARG;
@@ -401,7 +401,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     return SSD_OK;
   }
   if (lay.chain) {
-    // segmented: the state-only units (reported as the chunk-state stage),
+    // segmented: the unit-state pass (reported as the chunk-state stage),
     // then the chain (reported as the chunk scan)
     if (!mark(1)) return SSD_ERR_HIP;
     if (ssd::launch_chain_bf16(p, stream, 0) != hipSuccess || !mark(2) || !mark(3))

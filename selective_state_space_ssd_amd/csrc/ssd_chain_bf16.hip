@@ -207,14 +207,26 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     // a later segment: fold in the end states of the units before it
     const int64_t ubase = (b * H + h) * nunits;
     const int64_t nfold = (int64_t)piece * units_per_seg;
-    for (int64_t u = 0; u < nfold; ++u) {
+    // two units per step, so that both units' loads are in flight together
+    int64_t u = 0;
+    for (; u + 2 <= nfold; u += 2) {
+      const float d0 = seg_decay[ubase + u], d1 = seg_decay[ubase + u + 1];
+      const float* E0 = seg_states + ((ubase + u) * kP + pme) * N + 4 * g;
+      const float* E1 = E0 + kP * N;
+      f4 e0[NT], e1[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        e0[j] = ld4(E0 + 16 * j);
+        e1[j] = ld4(E1 + 16 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) Hs[j] = (Hs[j] * d0 + e0[j]) * d1 + e1[j];
+    }
+    if (u < nfold) {
       const float du = seg_decay[ubase + u];
       const float* E = seg_states + ((ubase + u) * kP + pme) * N + 4 * g;
-      f4 e[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) e[j] = ld4(E + 16 * j);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) Hs[j] = Hs[j] * du + e[j];
+      for (int j = 0; j < NT; ++j) Hs[j] = Hs[j] * du + ld4(E + 16 * j);
     }
   }
 
@@ -640,10 +652,12 @@ ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force) {
   pl.nseg = (nblk + span - 1) / span;
   if (pl.nseg < 2) return pl;
   pl.span = span;
-  // units of the state-only pass: halve the span while it stays even and
-  // above 8 blocks and the pass has fewer than two workgroups per CU
+  // units of the unit-state pass (one workgroup per pair of heads and unit,
+  // two resident per CU): halve the span while it stays even and above 8
+  // blocks and the pass has fewer than four workgroups per CU, so that its
+  // last, partly filled round is at most a third of it
   int64_t unit = span;
-  while (unit % 2 == 0 && unit > 8 && npairs * (pl.nseg - 1) * (span / unit) < 2 * kChainCUs)
+  while (unit % 2 == 0 && unit > 8 && npairs * (pl.nseg - 1) * (span / unit) < 4 * kChainCUs)
     unit /= 2;
   pl.unit = unit;
   pl.nunits = (pl.nseg - 1) * (span / unit);

@@ -559,68 +559,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 // ---------------------------------------------------------------------------
 
 // Local end states of units of consecutive 128-step blocks, for the
-// segmented chain path: one workgroup per (unit, batch, head), the state
-// recurrence alone run over the unit's blocks from a zero state,
+// segmented chain path: one workgroup per (unit, batch, pair of heads of one
+// group), the state recurrence alone run over the unit's blocks from a zero
+// state,
 //   E = exp(cum_last) E + B^T (w o x),  w_t = exp(cum_last - cum_t) dt_t,
-// with the block state product of the fused kernel above (the decay-weighted
-// B^T split hi/lo, x as it is, 32x32x16 bf16 MFMAs, E in the accumulators);
-// the next block's x and B tiles load while the current block is multiplied.
-// Outputs: E row-major [p][n] at seg_states[((b H + h) nunits + u) P N] and
-// D = the product of the blocks' exp(cum_last) (0 where a sequence starts
-// inside a block: the carried state does not survive it) at
-// seg_decay[(b H + h) nunits + u].  Workgroups are numbered with the heads
-// fastest, so the heads of a group (which read the same B rows) stay on one
+// on 32x32x16 bf16 MFMAs with E in the accumulators.  The pair shares the B
+// tile; wave w takes head w/2 and the p of parity w%2 (the x tile is staged
+// with permuted columns, as in the fused kernel) over all n, so B^T enters
+// the matrix cores as it is and only w o x (the smaller operand) is split
+// into hi/lo bf16.  The next block's tiles load while the current one is
+// multiplied.  Outputs: E row-major [p][n] at seg_states[((b H + h) nunits +
+// u) P N] and D = the product of the blocks' exp(cum_last) (0 where a
+// sequence starts inside a block: the carried state does not survive it) at
+// seg_decay[(b H + h) nunits + u].  Workgroups are numbered with the pairs
+// fastest, so the pairs of a group (which read the same B rows) stay on one
 // XCD.
 template <int N>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void unit_state_bf16_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void unit_state_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ dt_raw,
     const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
     const int32_t* __restrict__ seq, int64_t L, int64_t H, int64_t G, int64_t nblk, int64_t unit,
-    int64_t nunits, int64_t nbh, int64_t nwg, float* __restrict__ seg_states,
+    int64_t nunits, int64_t npairs, int64_t nwg, float* __restrict__ seg_states,
     float* __restrict__ seg_decay) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
-  constexpr int NPT = N == 128 ? 2 : 1;     // p-halves of the state per wave
-  __shared__ __align__(16) bf16_t x_lds[FQ * kP];
+  constexpr int NJ = N / 32;                // n-tiles of 32
+  constexpr int XI = XTile<FQ>::ITER;       // 16-byte pieces of one head's x tile per thread
+  __shared__ __align__(16) bf16_t x_lds[2][FQ * kP];
   __shared__ __align__(16) bf16_t b_lds[FQ * N];
-  __shared__ __align__(16) float w_lds[FQ];
-  __shared__ float dlast_lds;
+  __shared__ __align__(16) float w_lds[2][FQ];
+  __shared__ float dlast_lds[2];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int i = lane % 32, kk = lane / 32;
+  const int hd = wave / 2, pt = wave % 2;  // head of the pair, parity of p
   const int wi = (int)xcd_remap(blockIdx.x, nwg);
-  const int64_t u = __builtin_amdgcn_readfirstlane(wi / (int)nbh);
-  const int bhi = __builtin_amdgcn_readfirstlane(wi % (int)nbh);
-  const int64_t b = __builtin_amdgcn_readfirstlane(bhi / (int)H);
-  const int64_t h = __builtin_amdgcn_readfirstlane(bhi % (int)H);
-  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / ((int)H / (int)G));
+  const int64_t u = __builtin_amdgcn_readfirstlane(wi / (int)npairs);
+  const int pair = __builtin_amdgcn_readfirstlane(wi % (int)npairs);
+  const int hp = (int)H / 2;
+  const int64_t b = __builtin_amdgcn_readfirstlane(pair / hp);
+  const int64_t h0 = __builtin_amdgcn_readfirstlane(2 * (pair % hp));
+  const int64_t h = h0 + hd;
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)h0 / ((int)H / (int)G));
   const int64_t c0 = u * unit, c1 = c0 + unit < nblk ? c0 + unit : nblk;
   const int64_t xs = H * kP, bs = G * N;
-  const int snt = N == 128 ? wave : wave / 2;
-  const int spt0 = N == 128 ? 0 : wave % 2;
-  const float Ah = A[h], bias = dt_bias ? dt_bias[h] : 0.0f;
 
-  f16x sacc[NPT];
+  f16x sacc[NJ];
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) sacc[j] = zero16();
+  for (int j = 0; j < NJ; ++j) sacc[j] = zero16();
   float dprod = 1.0f;
 
-  XTile<FQ> xt;
+  // tiles in flight: both heads' x (thread piece k < XI: head 0, else head 1)
+  // and the shared B tile
+  uint4 xv[2 * XI];
   RowTile<FQ, N> bt;
   auto load = [&](int64_t c) {
     const int64_t t0 = c * FQ;
     const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
-    load_x_tile<FQ>(xt, x + ((b * L + t0) * H + h) * kP, xs, last);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bf16_t* src = x + ((b * L + t0) * H + h0 + q) * kP;
+#pragma unroll
+      for (int k = 0; k < XI; ++k) {
+        const int e = (k * 256 + tid) * 8;
+        const int row = e / kP, col = e % kP;
+        const int r = row < last ? row : last;
+        xv[q * XI + k] = *reinterpret_cast<const uint4*>(src + r * xs + col);
+      }
+    }
     load_rows<FQ, N>(bt, Bm + ((b * L + t0) * G + g) * N, bs, last);
   };
   load(c0);
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * FQ;
     const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
-    if (wave == 0) {
+    if (pt == 0) {  // one wave per head: dt, its running sum, w
       constexpr int E = FQ / kWave;
       float dtv[E], cum[E], cum_last;
-      wave_dt_cumsum<bf16_t, FQ>(dt_raw, Ah, bias, dt_min, dt_max, b, c, h, L, H, nblk, nullptr,
-                                 nullptr, dtv, cum, &cum_last);
+      wave_dt_cumsum<bf16_t, FQ>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c,
+                                 h, L, H, nblk, nullptr, nullptr, dtv, cum, &cum_last);
       int ks[E] = {0, 0};
       if (seq) {
         int run = 0;
@@ -642,20 +658,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void u
       const int klast = __shfl(ks[1], kWave - 1, kWave);
 #pragma unroll
       for (int k = 0; k < E; ++k)
-        w_lds[lane * E + k] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
-      if (lane == 0) dlast_lds = klast == 0 ? __expf(cum_last) : 0.0f;
+        w_lds[hd][lane * E + k] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
+      if (lane == 0) dlast_lds[hd] = klast == 0 ? __expf(cum_last) : 0.0f;
     }
 #pragma unroll
-    for (int k = 0; k < XTile<FQ>::ITER; ++k) {  // x tile, permuted columns, swizzled chunks
-      const int e = (k * 256 + tid) * 8;
-      const int row = e / kP, col = e % kP;
-      const uint4 v = xt.v[k];
-      const uint32_t m = row > last ? 0u : 0xffffffffu;
-      const uint2 even = {((v.x & 0xffffu) | (v.y << 16)) & m, ((v.z & 0xffffu) | (v.w << 16)) & m};
-      const uint2 odd = {((v.x >> 16) | (v.y & 0xffff0000u)) & m,
-                         ((v.z >> 16) | (v.w & 0xffff0000u)) & m};
-      *reinterpret_cast<uint2*>(x_lds + x_off(row, col / 2)) = even;
-      *reinterpret_cast<uint2*>(x_lds + x_off(row, 32 + col / 2)) = odd;
+    for (int q = 0; q < 2; ++q) {  // x tiles, permuted columns, swizzled chunks
+#pragma unroll
+      for (int k = 0; k < XI; ++k) {
+        const int e = (k * 256 + tid) * 8;
+        const int row = e / kP, col = e % kP;
+        const uint4 v = xv[q * XI + k];
+        const uint32_t m = row > last ? 0u : 0xffffffffu;
+        const uint2 even = {((v.x & 0xffffu) | (v.y << 16)) & m,
+                            ((v.z & 0xffffu) | (v.w << 16)) & m};
+        const uint2 odd = {((v.x >> 16) | (v.y & 0xffff0000u)) & m,
+                           ((v.z >> 16) | (v.w & 0xffff0000u)) & m};
+        *reinterpret_cast<uint2*>(x_lds[q] + x_off(row, col / 2)) = even;
+        *reinterpret_cast<uint2*>(x_lds[q] + x_off(row, 32 + col / 2)) = odd;
+      }
     }
 #pragma unroll
     for (int k = 0; k < RowTile<FQ, N>::ITER; ++k) {  // B tile, swizzled chunks
@@ -666,53 +686,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void u
     }
     __syncthreads();
     if (c + 1 < c1) load(c + 1);  // the next tiles in flight under this block's products
-    const float dl = dlast_lds;
+    const float dl = dlast_lds[hd];
     dprod *= dl;
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) sacc[j] *= dl;
+    for (int j = 0; j < NJ; ++j) sacc[j] *= dl;
 #pragma unroll 2
     for (int ks = 0; ks < FQ / 16; ++ks) {
       const int r0 = 16 * ks + 8 * kk;
-      const s16x8 braw = b_tr_operand<N>(b_lds, r0, r0 + 4, 32 * snt);
-      const f4 w0 = *reinterpret_cast<const f4*>(w_lds + r0);
-      const f4 w1 = *reinterpret_cast<const f4*>(w_lds + r0 + 4);
-      const uint4 bw = __builtin_bit_cast(uint4, braw);
-      const float av[8] = {bf16_lo(bw.x) * w0[0], bf16_hi(bw.x) * w0[1], bf16_lo(bw.y) * w0[2],
-                           bf16_hi(bw.y) * w0[3], bf16_lo(bw.z) * w1[0], bf16_hi(bw.z) * w1[1],
-                           bf16_lo(bw.w) * w1[2], bf16_hi(bw.w) * w1[3]};
-      s16x8 ahi, alo;
-      split_bf16x8(av, ahi, alo);
+      // w o x at t = r0 + 0..7, p = 2 i + pt, split hi/lo
+      const uint4 xw = __builtin_bit_cast(uint4, x_tr_operand(x_lds[hd], r0, r0 + 4, 32 * pt));
+      const f4 w0 = *reinterpret_cast<const f4*>(w_lds[hd] + r0);
+      const f4 w1 = *reinterpret_cast<const f4*>(w_lds[hd] + r0 + 4);
+      const float xv8[8] = {bf16_lo(xw.x) * w0[0], bf16_hi(xw.x) * w0[1], bf16_lo(xw.y) * w0[2],
+                            bf16_hi(xw.y) * w0[3], bf16_lo(xw.z) * w1[0], bf16_hi(xw.z) * w1[1],
+                            bf16_lo(xw.w) * w1[2], bf16_hi(xw.w) * w1[3]};
+      s16x8 xhi, xlo;
+      split_bf16x8(xv8, xhi, xlo);
 #pragma unroll
-      for (int j = 0; j < NPT; ++j) {
-        const s16x8 bop = x_tr_operand(x_lds, r0, r0 + 4, 32 * (spt0 + j));
-        sacc[j] = mfma32x32x16(ahi, bop, sacc[j]);
-        sacc[j] = mfma32x32x16(alo, bop, sacc[j]);
+      for (int j = 0; j < NJ; ++j) {
+        const s16x8 bop = b_tr_operand<N>(b_lds, r0, r0 + 4, 32 * j);
+        sacc[j] = mfma32x32x16(bop, xhi, sacc[j]);
+        sacc[j] = mfma32x32x16(bop, xlo, sacc[j]);
       }
     }
     __syncthreads();  // tiles and w read before the next block is staged
   }
-  // sacc[j][4 R + e] holds E at p = 2 i + spt0 + j, n = 32 snt + 8 R + 4 kk + e
+  // sacc[j][4 R + e] holds E at p = 2 i + pt, n = 32 j + 8 R + 4 kk + e
   const int64_t slot = (b * H + h) * nunits + u;
+  const int p = 2 * i + pt;
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    const int p = 2 * i + spt0 + j;
+  for (int j = 0; j < NJ; ++j) {
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      const int n0 = 32 * snt + 8 * R + 4 * kk;
+      const int n0 = 32 * j + 8 * R + 4 * kk;
       st4(seg_states + (slot * kP + p) * N + n0,
           f4{sacc[j][4 * R], sacc[j][4 * R + 1], sacc[j][4 * R + 2], sacc[j][4 * R + 3]});
     }
   }
-  if (tid == 0) seg_decay[slot] = dprod;
+  if (pt == 0 && lane == 0) seg_decay[slot] = dprod;
 }
 
 template <int N>
 static void launch_unit_state_n(const Problem& p, hipStream_t s) {
-  const int64_t nblk = fused_blocks(p.L), nbh = p.b * p.H, nwg = nbh * p.chain.nunits;
+  const int64_t nblk = fused_blocks(p.L), npairs = p.b * p.H / 2, nwg = npairs * p.chain.nunits;
   hipLaunchKernelGGL((unit_state_bf16_kernel<N>), dim3((unsigned)nwg), dim3(256), 0, s,
                      static_cast<const bf16_t*>(p.x), static_cast<const bf16_t*>(p.B),
                      static_cast<const bf16_t*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max,
-                     p.seq_idx, p.L, p.H, p.G, nblk, p.chain.unit, p.chain.nunits, nbh, nwg,
+                     p.seq_idx, p.L, p.H, p.G, nblk, p.chain.unit, p.chain.nunits, npairs, nwg,
                      p.cs_states, p.cs_decay);
 }
 

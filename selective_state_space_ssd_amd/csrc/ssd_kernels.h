@@ -47,7 +47,7 @@ struct Problem {
   unsigned* fs_flags;    // [b*H chains][blocks] "state entering this block is ready"
   unsigned* fs_ctl;      // 8 ticket counters, then the error word
   int fused_kind;        // 0: choose, 1: per-head kernel, 2: group kernel
-  // chain bf16 kernel: segments, and the state-only pass's outputs
+  // chain bf16 kernel: segments, and the unit-state pass's outputs
   ChainPlan chain;
   float* cs_states = nullptr;  // [b, H, nunits] P x N row-major unit end states
   float* cs_decay = nullptr;   // [b, H, nunits] unit decay products
@@ -116,16 +116,16 @@ int64_t chain_workgroups(int64_t b, int64_t H);
 bool chain_fills_machine(int64_t b, int64_t H);
 // Segmented chain: when the head pairs alone do not fill the machine, the
 // sequence is cut into nseg segments of `span` 128-step blocks (one
-// workgroup per (pair, segment)); a state-only launch first computes the
+// workgroup per (pair, segment)); a unit-state launch first computes the
 // local end state of every unit of `unit` blocks before the last segment
 // (nunits per head), and each segment starts from the units before it folded
 // into its entering state.  nseg = 1: the unsegmented chain (no workspace).
 // force: segment whenever the sequence has two blocks or more (testing).
 ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force);
-// pass 0: the state-only units (nothing when nseg = 1); pass 1: the chain.
+// pass 0: the unit-state pass (nothing when nseg = 1); pass 1: the chain.
 hipError_t launch_chain_bf16(const Problem& p, hipStream_t stream, int pass);
-// The state-only units of the segmented chain (ssd_fused_bf16.hip): one
-// workgroup per (unit, batch, head) writes cs_states / cs_decay.
+// The unit-state pass of the segmented chain (ssd_fused_bf16.hip): one
+// workgroup per (unit, batch, pair of heads) writes cs_states / cs_decay.
 hipError_t launch_unit_state_bf16(const Problem& p, hipStream_t stream);
 
 // Group form of the fused kernel: one workgroup per (block, group, head set).

@@ -165,7 +165,7 @@ def _chain_plan(b, L, H, force):
     if nseg < 2:
         return 1, nblk, 0, 0
     unit = span
-    while unit % 2 == 0 and unit > 8 and npairs * (nseg - 1) * (span // unit) < 512:
+    while unit % 2 == 0 and unit > 8 and npairs * (nseg - 1) * (span // unit) < 1024:
         unit //= 2
     return nseg, span, unit, (nseg - 1) * (span // unit)
 
@@ -176,7 +176,7 @@ def _seg_ws(b, L, H, P, N, force):
 
 
 def test_chain_plan():
-    assert _chain_plan(1, 65536, 128, False) == (4, 128, 32, 12)   # the long sequence
+    assert _chain_plan(1, 65536, 128, False) == (4, 128, 16, 24)   # the long sequence
     assert _chain_plan(8, 4096, 64, False)[0] == 1                 # 256 pairs: no segments
     assert _chain_plan(1, 1000, 8, True) == (8, 1, 1, 7)
     assert _chain_plan(1, 1000, 8, False)[0] == 1

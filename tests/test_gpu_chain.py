@@ -55,7 +55,7 @@ def test_chain_block_edges(L, N, H, G):
         compare(f"final {path}", np64(fin), rfin, TOL["bf16"])
 
 
-# segments of several blocks, each cut into units for the state-only pass:
+# segments of several blocks, each cut into units for the unit-state pass:
 # (b, L, H, G, N); the workgroups (pairs x segments) fill the 256 compute
 # units, the segment length is not a multiple of the block, L is ragged
 SEGMENTS = [(1, 40 * 128 - 37, 128, 8, 128), (2, 33 * 128 + 5, 64, 8, 64),
@@ -96,10 +96,10 @@ def test_chain_segments_with_units(b, L, H, G, N):
 
 def test_chain_segmented_is_the_default_for_the_long_sequence():
     """batch 1 x 65536 at 128 heads: 64 pairs, four segments of 128 blocks,
-    units of 32 blocks for the state-only pass."""
+    units of 16 blocks for the unit-state pass."""
     assert ssd.taken_path(1, 65536, 128, 64, 128, 8, 256, ssd.SSD_BF16) == "chain_segmented"
     assert ssd.workspace_size(1, 65536, 128, 64, 128, 8, 256, ssd.SSD_BF16) >= \
-        128 * 12 * 64 * 128 * 4
+        128 * 24 * 64 * 128 * 4
 
 
 @pytest.mark.parametrize("gate,skip,init", [(False, False, False), (True, False, True),

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
 
   // lane indices; refreshed from an opaque copy of threadIdx.x at every block
   // (see the top of the block loop)
-  int tid = threadIdx.x, th = tid & 255, lane = tid & 63, g = lane >> 4, m = lane & 15;
+  int tid = threadIdx.x & (kChainThreads - 1), th = tid & 255, lane = tid & 63, g = lane >> 4,
+      m = lane & 15;
   const int hd = __builtin_amdgcn_readfirstlane(tid >> 8);         // head of the pair (per wave)
   const int wt = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);   // wave within the head
   // workgroup -> (batch, head pair) in 32-bit scalar arithmetic (64-bit
@@ -402,7 +403,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     {
       int t = threadIdx.x;
       asm volatile("" : "+v"(t));
-      tid = t; th = t & 255; lane = t & 63; g = lane >> 4; m = lane & 15;
+      // (masked, so that index arithmetic on it is known non-negative)
+      tid = t & (kChainThreads - 1); th = t & 255; lane = t & 63; g = lane >> 4; m = lane & 15;
     }
     const int64_t t0 = c * CQ;
     const int last = (int)((L - 1 - t0) < (CQ - 1) ? (L - 1 - t0) : (CQ - 1));
@@ -441,11 +443,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
       const int cl = i >> 1;  // the chunk of 32 s holding the diagonal tile
-      // G^T tiles of chunk cc: s-tile 2 cc, and 2 cc + 1 unless it lies above
-      // the diagonal
-      auto gtiles = [&](const int cc, f4& g0, f4& g1) {
+      // G^T tiles of chunk cc: s-tile 2 cc, and 2 cc + 1 when `two`
+      auto gtiles = [&](const int cc, const bool two, f4& g0, f4& g1) {
         const int s0r = 32 * cc + m, s1r = s0r + 16;
-        const bool two = 2 * cc + 1 <= i;
         g0 = zero4();
         g1 = zero4();
 #pragma unroll
@@ -454,47 +454,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
           if (two) g1 = mfma16(ld_bf16x8(Bl + s1r * BP + 32 * kn + 8 * g), cop[kn], g1);
         }
       };
-      f4 g0, g1;
-      gtiles(0, g0, g1);
-      for (int cc = 0; cc <= cl; ++cc) {
-        const bool two = 2 * cc + 1 <= i;
-        // the next chunk's products run on the matrix cores under this
-        // chunk's masking
-        f4 n0 = zero4(), n1 = zero4();
-        if (cc < cl) gtiles(cc + 1, n0, n1);
+      // the masked values of chunk cc times x into acc
+      auto product = [&](const int cc, const float (&mv)[8]) {
         const int sa = 32 * cc + 4 * g, sb = sa + 16;
-        float mv[8];
-        if (cc < cl) {
-          const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
-          const f4 v1 = *reinterpret_cast<const f4*>(v_l + i * CQ + sb);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            mv[r] = g0[r] * v0[r];
-            mv[4 + r] = g1[r] * v1[r];
-          }
-        } else {
-          if (cc > 0) {  // the tiles so far carried exp(cum_r - cum_s): add exp(cum_t - cum_r)
-            const float e = ett_l[t];
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) acc[pt] *= e;
-          }
-          const f4 cs0 = *reinterpret_cast<const f4*>(cum2_l + sa);
-          const f4 ds0 = *reinterpret_cast<const f4*>(dt_l + sa);
-          const int4 k0 = *reinterpret_cast<const int4*>(k_l + sa);
-          const f4 cs1 = *reinterpret_cast<const f4*>(cum2_l + sb);
-          const f4 ds1 = *reinterpret_cast<const f4*>(dt_l + sb);
-          const int4 k1 = *reinterpret_cast<const int4*>(k_l + sb);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ka = r == 0 ? k0.x : r == 1 ? k0.y : r == 2 ? k0.z : k0.w;
-            const int kb = r == 0 ? k1.x : r == 1 ? k1.y : r == 2 ? k1.z : k1.w;
-            const float va = g0[r] * fexp2(ct2 - cs0[r]) * ds0[r];
-            const float vb = g1[r] * fexp2(ct2 - cs1[r]) * ds1[r];
-            mv[r] = sa + r < t ? (ka == kt ? va : 0.0f) : (sa + r == t ? va + Dh : 0.0f);
-            mv[4 + r] = !two ? 0.0f
-                             : (sb + r < t ? (kb == kt ? vb : 0.0f) : (sb + r == t ? vb + Dh : 0.0f));
-          }
-        }
         s16x8 mhi, mlo;
         split_bf16x8(mv, mhi, mlo);
         s16x8 xo[4];
@@ -505,8 +467,61 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(xo[pt], mhi, acc[pt]);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(xo[pt], mlo, acc[pt]);
+      };
+      // chunks below the diagonal one (both s-tiles below t's tile): the
+      // tabulated factors exp(cum_r - cum_s) dt_s [k_s = k_r]; the next
+      // chunk's products run on the matrix cores under this chunk's masking
+      f4 g0, g1;
+      gtiles(0, cl > 0 || (i & 1), g0, g1);
+      for (int cc = 0; cc < cl; ++cc) {
+        f4 n0, n1;
+        gtiles(cc + 1, cc + 1 < cl || (i & 1), n0, n1);
+        const int sa = 32 * cc + 4 * g, sb = sa + 16;
+        const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
+        const f4 v1 = *reinterpret_cast<const f4*>(v_l + i * CQ + sb);
+        float mv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          mv[r] = g0[r] * v0[r];
+          mv[4 + r] = g1[r] * v1[r];
+        }
+        product(cc, mv);
         g0 = n0;
         g1 = n1;
+      }
+      // the diagonal chunk: the tiles so far carried exp(cum_r - cum_s), so
+      // add exp(cum_t - cum_r); then the direct decay, [k_s = k_t] below the
+      // diagonal, D on it, zero above -- selects on flags computed without
+      // branches (a short-circuit form became a branch per element)
+      if (cl > 0) {
+        const float e = ett_l[t];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] *= e;
+      }
+      {
+        const int sa = 32 * cl + 4 * g, sb = sa + 16;
+        const bool two = (i & 1) != 0;  // s-tile 2 cl + 1 lies on or below t's tile
+        const f4 cs0 = *reinterpret_cast<const f4*>(cum2_l + sa);
+        const f4 ds0 = *reinterpret_cast<const f4*>(dt_l + sa);
+        const int4 k0 = *reinterpret_cast<const int4*>(k_l + sa);
+        const f4 cs1 = *reinterpret_cast<const f4*>(cum2_l + sb);
+        const f4 ds1 = *reinterpret_cast<const f4*>(dt_l + sb);
+        const int4 k1 = *reinterpret_cast<const int4*>(k_l + sb);
+        float mv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ka = r == 0 ? k0.x : r == 1 ? k0.y : r == 2 ? k0.z : k0.w;
+          const int kb = r == 0 ? k1.x : r == 1 ? k1.y : r == 2 ? k1.z : k1.w;
+          const float va = g0[r] * fexp2(ct2 - cs0[r]) * ds0[r];
+          const float vb = g1[r] * fexp2(ct2 - cs1[r]) * ds1[r];
+          const bool da = sa + r == t, db = sb + r == t;
+          const bool keep_a = ((sa + r < t) & (ka == kt)) | da;
+          const bool keep_b = two & (((sb + r < t) & (kb == kt)) | db);
+          const float wa = da ? va + Dh : va, wb = db ? vb + Dh : vb;
+          mv[r] = keep_a ? wa : 0.0f;
+          mv[4 + r] = keep_b ? wb : 0.0f;
+        }
+        product(cl, mv);
       }
     };
     f4 ya0[4], ya1[4];

@@ -26,7 +26,7 @@
 //            (a table over (i, s)) times exp(cum_t - cum_r), both <= 1,
 //            the second applied once to the accumulated tiles;
 //   C.H      wave w: Y^T[p][t] (its 16 p, every t) = H[p][n] C^T[n][t],
-//            scaled by exp(cum_t) when written out;
+//            scaled by exp(cum_t) in the epilogue;
 //   state    H = exp(cum_last) H + B^T (w o x), w_t = exp(cum_last - cum_t)
 //            dt_t, accumulated by the MFMAs straight into H's registers;
 //   epilogue the in-block and C.H parts meet in LDS (they are owned by
@@ -587,12 +587,16 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       *reinterpret_cast<f4*>(yin + (16 * (CT - 1 - wt) + m) * kYP + 16 * pt + 4 * g) = ya1[pt];
     }
 #pragma unroll
-    for (int i = 0; i < CT; ++i) {
-      const int t = 16 * i + m;
-      *reinterpret_cast<f4*>(ych + t * kYP + 16 * wt + 4 * g) = ch[i] * et_l[t];
-    }
+    for (int i = 0; i < CT; ++i)
+      *reinterpret_cast<f4*>(ych + (16 * i + m) * kYP + 16 * wt + 4 * g) = ch[i];
     __syncthreads();
 
+    // exp(cum_t) of the epilogue's steps, read before the tables are refilled
+    // (the epilogue applies it: one fma per output instead of a multiply per
+    // C.H value)
+    float etr[PX];
+#pragma unroll
+    for (int k = 0; k < PX; ++k) etr[k] = et_l[(k * 256 + th) / 8];
     // the tables are free until the next staging: fill them for block c + 1
     if (c + 1 < c_end) tables(c + 1);
 
@@ -603,9 +607,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       const int e = k * 256 + th;
       const int row = e / 8, col = (e % 8) * 8;
       const f4 y0 = *reinterpret_cast<const f4*>(yin + row * kYP + col) +
-                    *reinterpret_cast<const f4*>(ych + row * kYP + col);
+                    *reinterpret_cast<const f4*>(ych + row * kYP + col) * etr[k];
       const f4 y1 = *reinterpret_cast<const f4*>(yin + row * kYP + col + 4) +
-                    *reinterpret_cast<const f4*>(ych + row * kYP + col + 4);
+                    *reinterpret_cast<const f4*>(ych + row * kYP + col + 4) * etr[k];
       float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
       if constexpr (GATE) {
         const uint32_t zw[4] = {zr[k].x, zr[k].y, zr[k].z, zr[k].w};

@@ -562,18 +562,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
 // segmented chain path: one workgroup per (unit, batch, pair of heads of one
 // group), the state recurrence alone run over the unit's blocks from a zero
 // state,
-//   E = exp(cum_last) E + B^T (w o x),  w_t = exp(cum_last - cum_t) dt_t,
-// on 32x32x16 bf16 MFMAs with E in the accumulators.  The pair shares the B
-// tile; wave w takes head w/2 and the p of parity w%2 (the x tile is staged
-// with permuted columns, as in the fused kernel) over all n, so B^T enters
+//   E = sum over the unit's blocks c of P_c B_c^T (w_c o x_c),
+//   w_t = exp(cum_last - cum_t) dt_t,  P_c = the product of exp(cum_last) of
+//   the unit's blocks after c,
+// on 32x32x16 bf16 MFMAs with E in the accumulators.  The blocks are taken
+// last to first, so that P_c is a running product folded into w (one
+// multiply per step, where scaling the accumulators by each block's decay
+// would cost one per state element).  The pair shares the B tile; wave w
+// takes head w/2 and p = 32 (w%2) .. 32 (w%2) + 31 over all n, so B^T enters
 // the matrix cores as it is and only w o x (the smaller operand) is split
-// into hi/lo bf16.  The next block's tiles load while the current one is
-// multiplied.  Outputs: E row-major [p][n] at seg_states[((b H + h) nunits +
-// u) P N] and D = the product of the blocks' exp(cum_last) (0 where a
-// sequence starts inside a block: the carried state does not survive it) at
-// seg_decay[(b H + h) nunits + u].  Workgroups are numbered with the pairs
-// fastest, so the pairs of a group (which read the same B rows) stay on one
-// XCD.
+// into hi/lo bf16.  Rows go through buffer resources ending at the block's
+// last row (rows past the sequence end load as zero).  The next block's
+// tiles load while the current one is multiplied.  Outputs: E row-major
+// [p][n] at seg_states[((b H + h) nunits + u) P N] and D = the product of the
+// unit's exp(cum_last) (0 where a sequence starts inside a block: the
+// carried state does not survive it) at seg_decay[(b H + h) nunits + u].
+// Workgroups are numbered with the pairs fastest, so the pairs of a group
+// (which read the same B rows) stay on one XCD.
 template <int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void unit_state_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ dt_raw,
@@ -583,15 +588,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
     float* __restrict__ seg_decay) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
   constexpr int NJ = N / 32;                // n-tiles of 32
-  constexpr int XI = XTile<FQ>::ITER;       // 16-byte pieces of one head's x tile per thread
+  constexpr int XI = FQ * kP / 8 / 256;     // 16-byte pieces of one head's x tile per thread
+  constexpr int BI = FQ * N / 8 / 256;      // ... of the B tile
   __shared__ __align__(16) bf16_t x_lds[2][FQ * kP];
   __shared__ __align__(16) bf16_t b_lds[FQ * N];
   __shared__ __align__(16) float w_lds[2][FQ];
-  __shared__ float dlast_lds[2];
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x & 255, lane = tid % kWave, wave = tid / kWave;
   const int i = lane % 32, kk = lane / 32;
-  const int hd = wave / 2, pt = wave % 2;  // head of the pair, parity of p
+  const int hd = wave / 2, pt = wave % 2;  // head of the pair, half of p
   const int wi = (int)xcd_remap(blockIdx.x, nwg);
   const int64_t u = __builtin_amdgcn_readfirstlane(wi / (int)npairs);
   const int pair = __builtin_amdgcn_readfirstlane(wi % (int)npairs);
@@ -602,37 +607,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
   const int64_t g = __builtin_amdgcn_readfirstlane((int)h0 / ((int)H / (int)G));
   const int64_t c0 = u * unit, c1 = c0 + unit < nblk ? c0 + unit : nblk;
   const int64_t xs = H * kP, bs = G * N;
+  const uint32_t xrow = (uint32_t)(xs * 2), brow = (uint32_t)(bs * 2);  // row pitches, bytes
 
   f16x sacc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) sacc[j] = zero16();
-  float dprod = 1.0f;
+  float P = 1.0f;  // decay of the blocks already taken (kept by the pt == 0 waves)
 
-  // tiles in flight: both heads' x (thread piece k < XI: head 0, else head 1)
-  // and the shared B tile
-  uint4 xv[2 * XI];
-  RowTile<FQ, N> bt;
+  // tiles in flight: both heads' x (pieces k < XI: head 0, else head 1) and
+  // the shared B tile
+  uint4 xv[2 * XI], bv[BI];
   auto load = [&](int64_t c) {
     const int64_t t0 = c * FQ;
-    const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
+    const uint32_t last = (uint32_t)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const bf16_t* src = x + ((b * L + t0) * H + h0 + q) * kP;
+      const auto xr = row_rsrc(x + ((b * L + t0) * H + h0 + q) * kP, last * xrow + kP * 2);
 #pragma unroll
       for (int k = 0; k < XI; ++k) {
-        const int e = (k * 256 + tid) * 8;
-        const int row = e / kP, col = e % kP;
-        const int r = row < last ? row : last;
-        xv[q * XI + k] = *reinterpret_cast<const uint4*>(src + r * xs + col);
+        const uint32_t e = (uint32_t)(k * 256 + tid) * 8;
+        xv[q * XI + k] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, (e / kP) * xrow + (e % kP) * 2, 0, 0));
       }
     }
-    load_rows<FQ, N>(bt, Bm + ((b * L + t0) * G + g) * N, bs, last);
+    const auto br = row_rsrc(Bm + ((b * L + t0) * G + g) * N, last * brow + N * 2);
+#pragma unroll
+    for (int k = 0; k < BI; ++k) {
+      const uint32_t e = (uint32_t)(k * 256 + tid);
+      bv[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            br, (e / (N / 8)) * brow + (e % (N / 8)) * 16, 0, 0));
+    }
   };
-  load(c0);
-  for (int64_t c = c0; c < c1; ++c) {
+  load(c1 - 1);
+  for (int64_t c = c1 - 1; c >= c0; --c) {
     const int64_t t0 = c * FQ;
-    const int last = (int)((L - 1 - t0) < (FQ - 1) ? (L - 1 - t0) : (FQ - 1));
-    if (pt == 0) {  // one wave per head: dt, its running sum, w
+    if (pt == 0) {  // one wave per head: dt, its running sum, w scaled by P
       constexpr int E = FQ / kWave;
       float dtv[E], cum[E], cum_last;
       wave_dt_cumsum<bf16_t, FQ>(dt_raw, A[h], dt_bias ? dt_bias[h] : 0.0f, dt_min, dt_max, b, c,
@@ -655,45 +664,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
 #pragma unroll
         for (int k = 0; k < E; ++k) ks[k] += incl - run;
       }
-      const int klast = __shfl(ks[1], kWave - 1, kWave);
+      const int klast = __shfl(ks[E - 1], kWave - 1, kWave);
 #pragma unroll
       for (int k = 0; k < E; ++k)
-        w_lds[hd][lane * E + k] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] : 0.0f;
-      if (lane == 0) dlast_lds[hd] = klast == 0 ? __expf(cum_last) : 0.0f;
+        w_lds[hd][lane * E + k] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] * P : 0.0f;
+      P *= klast == 0 ? __expf(cum_last) : 0.0f;
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {  // x tiles, permuted columns, swizzled chunks
+    for (int q = 0; q < 2; ++q) {  // x tiles, swizzled chunks
 #pragma unroll
       for (int k = 0; k < XI; ++k) {
         const int e = (k * 256 + tid) * 8;
-        const int row = e / kP, col = e % kP;
-        const uint4 v = xv[q * XI + k];
-        const uint32_t m = row > last ? 0u : 0xffffffffu;
-        const uint2 even = {((v.x & 0xffffu) | (v.y << 16)) & m,
-                            ((v.z & 0xffffu) | (v.w << 16)) & m};
-        const uint2 odd = {((v.x >> 16) | (v.y & 0xffff0000u)) & m,
-                           ((v.z >> 16) | (v.w & 0xffff0000u)) & m};
-        *reinterpret_cast<uint2*>(x_lds[q] + x_off(row, col / 2)) = even;
-        *reinterpret_cast<uint2*>(x_lds[q] + x_off(row, 32 + col / 2)) = odd;
+        *reinterpret_cast<uint4*>(x_lds[q] + x_off(e / kP, e % kP)) = xv[q * XI + k];
       }
     }
 #pragma unroll
-    for (int k = 0; k < RowTile<FQ, N>::ITER; ++k) {  // B tile, swizzled chunks
+    for (int k = 0; k < BI; ++k) {  // B tile, swizzled chunks
       const int e = k * 256 + tid;
       const int row = e / (N / 8), chunk = e % (N / 8);
-      *reinterpret_cast<uint4*>(b_lds + row * N + ((chunk ^ bswz<N>(row)) << 3)) =
-          row > last ? uint4{0u, 0u, 0u, 0u} : bt.v[k];
+      *reinterpret_cast<uint4*>(b_lds + row * N + ((chunk ^ bswz<N>(row)) << 3)) = bv[k];
     }
     __syncthreads();
-    if (c + 1 < c1) load(c + 1);  // the next tiles in flight under this block's products
-    const float dl = dlast_lds[hd];
-    dprod *= dl;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sacc[j] *= dl;
+    if (c > c0) load(c - 1);  // the next tiles in flight under this block's products
 #pragma unroll 2
     for (int ks = 0; ks < FQ / 16; ++ks) {
       const int r0 = 16 * ks + 8 * kk;
-      // w o x at t = r0 + 0..7, p = 2 i + pt, split hi/lo
+      // w o x at t = r0 + 0..7, p = 32 pt + i, split hi/lo
       const uint4 xw = __builtin_bit_cast(uint4, x_tr_operand(x_lds[hd], r0, r0 + 4, 32 * pt));
       const f4 w0 = *reinterpret_cast<const f4*>(w_lds[hd] + r0);
       const f4 w1 = *reinterpret_cast<const f4*>(w_lds[hd] + r0 + 4);
@@ -711,9 +707,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
     }
     __syncthreads();  // tiles and w read before the next block is staged
   }
-  // sacc[j][4 R + e] holds E at p = 2 i + pt, n = 32 j + 8 R + 4 kk + e
+  // sacc[j][4 R + e] holds E at p = 32 pt + i, n = 32 j + 8 R + 4 kk + e
   const int64_t slot = (b * H + h) * nunits + u;
-  const int p = 2 * i + pt;
+  const int p = 32 * pt + i;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -723,7 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
           f4{sacc[j][4 * R], sacc[j][4 * R + 1], sacc[j][4 * R + 2], sacc[j][4 * R + 3]});
     }
   }
-  if (pt == 0 && lane == 0) seg_decay[slot] = dprod;
+  if (pt == 0 && lane == 0) seg_decay[slot] = P;
 }
 
 template <int N>

@@ -41,6 +41,8 @@
 // exp(cum_t) of the C.H part needs k_t = 0, and a pair (s, t) needs
 // k_s = k_t -- split at r like the decay, [k_s = k_r][k_r = k_t], since k
 // never decreases within a block.
+#include <type_traits>
+
 #include "ssd_bf16_tiles.h"
 #include "ssd_dt.h"
 #include "ssd_kernels.h"
@@ -139,7 +141,7 @@ struct ChainLds {
 // seg_decay [b, H, nunits], written by the unit-state kernel before): H =
 // D_u H + E_u in unit order.  The outputs of the segment's blocks are written;
 // the last segment writes final_states.
-template <int N, bool GATE>
+template <int N, bool GATE, bool VARLEN>
 __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
     const bf16_t* __restrict__ dt_raw, const float* __restrict__ A,
@@ -150,6 +152,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const float* __restrict__ seg_states, const float* __restrict__ seg_decay, int64_t nunits,
     int64_t units_per_seg) {
   static_assert(N == 64 || N == 128, "dstate 64 or 128");
+  // without packed sequences every start count is zero: the compiler drops
+  // the counts, their compares and their table
+  if constexpr (!VARLEN) seq = nullptr;
   constexpr int KN = N / 32;                   // contraction steps over n
   constexpr int NT = N / 16;                   // 16-row n tiles of the state
   constexpr int PB = CQ * N / 8 / kChainThreads;  // 16-byte pieces of a B (C) tile per thread
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       if (wt == 0) {
         cum2_l[t] = cum[k] * kLog2e;
         dt_l[t] = dv[k];
-        k_l[t] = ks[k];
+        if constexpr (VARLEN) k_l[t] = ks[k];
         w_l[t] = ks[k] == klast ? __expf(cum_last - cum[k]) * dv[k] : 0.0f;
       } else if (wt == 1) {
         et_l[t] = ks[k] == 0 ? __expf(cum[k]) : 0.0f;
@@ -433,13 +438,16 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     // G^T tiles that lane holds.
     // (two calls with their own accumulators: a loop over the tiles would
     // index the accumulators dynamically and put them in scratch memory)
-    auto in_block = [&](const int i, f4 (&acc)[4]) {
+    // (the tile's parity is a compile-time argument: one of the two tiles is
+    // even, the other odd, and only an odd tile's diagonal chunk holds a tile
+    // wholly below the diagonal)
+    auto in_block = [&](const int i, f4 (&acc)[4], auto odd) {
       const int t = 16 * i + m;
       s16x8 cop[KN];
 #pragma unroll
       for (int kn = 0; kn < KN; ++kn) cop[kn] = ld_bf16x8(Cl + t * CP + 32 * kn + 8 * g);
       const float ct2 = cum2_l[t];
-      const int kt = k_l[t];
+      const int kt = VARLEN ? k_l[t] : 0;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
       const int cl = i >> 1;  // the chunk of 32 s holding the diagonal tile
@@ -472,10 +480,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       // tabulated factors exp(cum_r - cum_s) dt_s [k_s = k_r]; the next
       // chunk's products run on the matrix cores under this chunk's masking
       f4 g0, g1;
-      gtiles(0, cl > 0 || (i & 1), g0, g1);
+      constexpr bool kOdd = decltype(odd)::value;
+      gtiles(0, cl > 0 || kOdd, g0, g1);
       for (int cc = 0; cc < cl; ++cc) {
         f4 n0, n1;
-        gtiles(cc + 1, cc + 1 < cl || (i & 1), n0, n1);
+        gtiles(cc + 1, cc + 1 < cl || kOdd, n0, n1);
         const int sa = 32 * cc + 4 * g, sb = sa + 16;
         const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
         const f4 v1 = *reinterpret_cast<const f4*>(v_l + i * CQ + sb);
@@ -490,43 +499,50 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         g1 = n1;
       }
       // the diagonal chunk: the tiles so far carried exp(cum_r - cum_s), so
-      // add exp(cum_t - cum_r); then the direct decay, [k_s = k_t] below the
-      // diagonal, D on it, zero above -- selects on flags computed without
-      // branches (a short-circuit form became a branch per element)
+      // add exp(cum_t - cum_r)
+      const float e = ett_l[t];
       if (cl > 0) {
-        const float e = ett_l[t];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[pt] *= e;
       }
-      {
-        const int sa = 32 * cl + 4 * g, sb = sa + 16;
-        const bool two = (i & 1) != 0;  // s-tile 2 cl + 1 lies on or below t's tile
-        const f4 cs0 = *reinterpret_cast<const f4*>(cum2_l + sa);
-        const f4 ds0 = *reinterpret_cast<const f4*>(dt_l + sa);
-        const int4 k0 = *reinterpret_cast<const int4*>(k_l + sa);
-        const f4 cs1 = *reinterpret_cast<const f4*>(cum2_l + sb);
-        const f4 ds1 = *reinterpret_cast<const f4*>(dt_l + sb);
-        const int4 k1 = *reinterpret_cast<const int4*>(k_l + sb);
-        float mv[8];
+      // the diagonal s-tile itself: the direct decay, [k_s = k_t] below the
+      // diagonal, D on it, zero above -- selects on flags computed without
+      // branches (a short-circuit form became a branch per element)
+      auto diagonal = [&](const f4& gd, const int sd, float* o) {
+        const f4 cs = *reinterpret_cast<const f4*>(cum2_l + sd);
+        const f4 ds = *reinterpret_cast<const f4*>(dt_l + sd);
+        int4 kd = int4{0, 0, 0, 0};
+        if constexpr (VARLEN) kd = *reinterpret_cast<const int4*>(k_l + sd);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int ka = r == 0 ? k0.x : r == 1 ? k0.y : r == 2 ? k0.z : k0.w;
-          const int kb = r == 0 ? k1.x : r == 1 ? k1.y : r == 2 ? k1.z : k1.w;
-          const float va = g0[r] * fexp2(ct2 - cs0[r]) * ds0[r];
-          const float vb = g1[r] * fexp2(ct2 - cs1[r]) * ds1[r];
-          const bool da = sa + r == t, db = sb + r == t;
-          const bool keep_a = ((sa + r < t) & (ka == kt)) | da;
-          const bool keep_b = two & (((sb + r < t) & (kb == kt)) | db);
-          const float wa = da ? va + Dh : va, wb = db ? vb + Dh : vb;
-          mv[r] = keep_a ? wa : 0.0f;
-          mv[4 + r] = keep_b ? wb : 0.0f;
+          const int ks = r == 0 ? kd.x : r == 1 ? kd.y : r == 2 ? kd.z : kd.w;
+          const float v = gd[r] * fexp2(ct2 - cs[r]) * ds[r];
+          const bool on = sd + r == t;
+          const bool keep = ((sd + r < t) & (ks == kt)) | on;
+          o[r] = keep ? (on ? v + Dh : v) : 0.0f;
         }
-        product(cl, mv);
+      };
+      const int sa = 32 * cl + 4 * g, sb = sa + 16;
+      float mv[8];
+      if constexpr (kOdd) {
+        // s-tile i - 1 lies wholly below t's tile: the tabulated factor
+        // exp(cum_r - cum_s) dt_s [k_s = k_r] times exp(cum_t - cum_r), as
+        // in the chunks before; then the diagonal tile
+        const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mv[r] = g0[r] * v0[r] * e;
+        diagonal(g1, sb, mv + 4);
+      } else {
+        diagonal(g0, sa, mv);
+#pragma unroll
+        for (int r = 4; r < 8; ++r) mv[r] = 0.0f;
       }
+      product(cl, mv);
     };
     f4 ya0[4], ya1[4];
-    in_block(wt, ya0);
-    in_block(CT - 1 - wt, ya1);
+    const int ie = (wt & 1) ? CT - 1 - wt : wt, io = CT - 1 - ie;  // even and odd tile
+    in_block(ie, ya0, std::false_type{});
+    in_block(io, ya1, std::true_type{});
 
     // ---- C.H: rows p = 16 wt + 4 g + r of every t; slots n = 32 kn + 4 g + j
     // (j < 4) and 32 kn + 16 + 4 g + j - 4: the lane's own state registers ----
@@ -583,8 +599,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     // ---- both output parts into LDS ----
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-      *reinterpret_cast<f4*>(yin + (16 * wt + m) * kYP + 16 * pt + 4 * g) = ya0[pt];
-      *reinterpret_cast<f4*>(yin + (16 * (CT - 1 - wt) + m) * kYP + 16 * pt + 4 * g) = ya1[pt];
+      *reinterpret_cast<f4*>(yin + (16 * ie + m) * kYP + 16 * pt + 4 * g) = ya0[pt];
+      *reinterpret_cast<f4*>(yin + (16 * io + m) * kYP + 16 * pt + 4 * g) = ya1[pt];
     }
 #pragma unroll
     for (int i = 0; i < CT; ++i)
@@ -695,16 +711,19 @@ static void launch_chain_n(const Problem& p, hipStream_t s) {
   const ChainPlan& pl = p.chain;
   const int64_t nwg = npairs * pl.nseg;
   const int64_t ups = pl.nseg > 1 ? pl.span / pl.unit : 0;
-  if (p.z)
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, true>), dim3((unsigned)nwg),
-                       dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
-                       p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
-                       nblk, nwg, npairs, pl.span, p.cs_states, p.cs_decay, pl.nunits, ups);
-  else
-    hipLaunchKernelGGL((chain_scan_bf16_kernel<N, false>), dim3((unsigned)nwg),
-                       dim3(kChainThreads), 0, s, xb, Bb, Cb, db, p.A, p.dt_bias, p.dt_min,
-                       p.dt_max, p.D, zb, ob, p.init, p.final_states, p.seq_idx, p.L, p.H, p.G,
-                       nblk, nwg, npairs, pl.span, p.cs_states, p.cs_decay, pl.nunits, ups);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(kChainThreads), 0, s, xb, Bb, Cb, db,
+                       p.A, p.dt_bias, p.dt_min, p.dt_max, p.D, zb, ob, p.init, p.final_states,
+                       p.seq_idx, p.L, p.H, p.G, nblk, nwg, npairs, pl.span, p.cs_states,
+                       p.cs_decay, pl.nunits, ups);
+  };
+  if (p.seq_idx) {
+    if (p.z) go(chain_scan_bf16_kernel<N, true, true>);
+    else go(chain_scan_bf16_kernel<N, false, true>);
+  } else {
+    if (p.z) go(chain_scan_bf16_kernel<N, true, false>);
+    else go(chain_scan_bf16_kernel<N, false, false>);
+  }
 }
 
 hipError_t launch_chain_bf16(const Problem& p, hipStream_t s, int pass) {

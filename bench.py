@@ -662,13 +662,14 @@ def _cpu_model():
 def cpu_baseline(w, inp, min_seconds=10.0, heads_per_pass=16):
     """The oracle (untuned fp64 recurrence, OpenMP over batch x heads) on a
     bounded sample of workload `w`: passes of `heads_per_pass` whole heads
-    (every timestep) until `min_seconds` have passed or every head is done,
-    scaled to tokens/s of the whole workload (tokens x heads done / heads)."""
+    (every timestep, cycling through the heads) until `min_seconds` have
+    passed, scaled to tokens/s of the whole workload (tokens x heads done /
+    heads)."""
     import oracle
     threads = oracle.max_threads()
     H = w.nheads
     done, elapsed, h0 = 0, 0.0, 0
-    while elapsed < min_seconds and done < w.batch * H:
+    while elapsed < min_seconds:
         mask = np.zeros((w.batch, H), bool)
         hs = [(h0 + j) % H for j in range(min(heads_per_pass, H))]
         mask[:, hs] = True
@@ -681,10 +682,10 @@ def cpu_baseline(w, inp, min_seconds=10.0, heads_per_pass=16):
     frac = done / (w.batch * H)
     return {"value": w.tokens * frac / elapsed, "unit": "tokens/s",
             "cores": min(threads, heads_per_pass * w.batch), "kind": "oracle",
-            "sample": f"{done} of {w.batch * H} (batch, head) pairs of the {w.name} workload, "
-                      f"every timestep ({elapsed:.1f} s of fp64 recurrence, OpenMP over the "
-                      f"pairs of a pass, {heads_per_pass} per pass); value = tokens x "
-                      f"{frac:.4f} / time",
+            "sample": f"{done} (batch, head) pair-scans of the {w.batch * H} of the {w.name} "
+                      f"workload (heads cycled), every timestep ({elapsed:.1f} s of fp64 "
+                      f"recurrence, OpenMP over the pairs of a pass, {heads_per_pass} per pass); "
+                      f"value = tokens x {frac:.4f} / time",
             "cpu": _cpu_model(), "threads_available": threads}
 
 

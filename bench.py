@@ -716,6 +716,18 @@ OTHER_SCAN_LINES = (
 )
 
 
+# the further lines by name (bench.py --only NAME runs one of them alone)
+EXTRA_LINES = {
+    "varlen_f32": lambda dev, warmup: varlen_workload(dev, warmup),
+    "varlen_bf16": lambda dev, warmup: varlen_workload(
+        dev, warmup, "bf16_b8_L4096_H64_P64_N128_G8_Q256", 512),
+    "decode": lambda dev, warmup: decode_workload(dev, warmup),
+    "block": lambda dev, warmup: block_workload(dev, warmup),
+    "bwd_f32": lambda dev, warmup: bwd_workload(dev, warmup),
+    "bwd_bf16": lambda dev, warmup: bwd_workload(dev, warmup, dtype="bf16"),
+}
+
+
 def main():
     global MIN_CALLS, WARMUP_SECONDS
     ap = argparse.ArgumentParser()
@@ -728,8 +740,9 @@ def main():
     ap.add_argument("--no-others", action="store_true",
                     help="measure the headline workload only")
     ap.add_argument("--only", default=None,
-                    help="measure only this workload (a name of ssd_workloads.WORKLOADS) and "
-                         "print its line (for counter runs)")
+                    help="measure only this workload (a name of ssd_workloads.WORKLOADS, or one "
+                         "of " + ", ".join(EXTRA_LINES) + ") and print its line (for counter "
+                         "runs)")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--min-calls", type=int, default=MIN_CALLS,
                     help="least number of event-timed calls per line (counter runs use fewer)")
@@ -764,6 +777,11 @@ def main():
         del src, dst
 
     peaks = None if args.no_peaks else measured_peaks(dev)
+    if args.only in EXTRA_LINES:
+        line = EXTRA_LINES[args.only](dev, args.warmup)
+        line["peaks_measured"] = peaks
+        print(json.dumps(line), flush=True)
+        return
     if args.only:
         w1 = WORKLOADS[args.only]
         line = scan_line((args.only,), dev, args.steps, args.warmup, peaks,
@@ -810,14 +828,8 @@ def main():
             others.append(scan_line(names, dev, args.steps, args.warmup, peaks,
                                     copies=2 if (w2.dtype == "f32" and w2.segments == 1) else 1))
             torch.cuda.empty_cache()
-        for fn in (lambda: varlen_workload(dev, args.warmup),
-                   lambda: varlen_workload(dev, args.warmup, "bf16_b8_L4096_H64_P64_N128_G8_Q256",
-                                           512),
-                   lambda: decode_workload(dev, args.warmup),
-                   lambda: block_workload(dev, args.warmup),
-                   lambda: bwd_workload(dev, args.warmup),
-                   lambda: bwd_workload(dev, args.warmup, dtype="bf16")):
-            others.append(fn())
+        for fn in EXTRA_LINES.values():
+            others.append(fn(dev, args.warmup))
             torch.cuda.empty_cache()
         line["other_workloads"] = others
     if not args.no_cpu_baseline:

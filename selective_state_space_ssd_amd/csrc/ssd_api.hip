@@ -749,12 +749,16 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   void* grad[5] = {dx, ddt, dB, dC, dz};
   if (bl.bf16 && nonempty) {
     const int64_t nin[6] = {nx, ndt, nbc, nbc, nx, nx};
+    ssd::ConvList wl;
     for (int k = 0; k < 6; ++k) {
       if (!in[k]) continue;
       float* w = reinterpret_cast<float*>(ws + bl.off_w[k]);
-      if (ssd::launch_widen_bf16(in[k], w, nin[k], stream) != hipSuccess) return SSD_ERR_HIP;
+      wl.src[wl.count] = in[k];
+      wl.dst[wl.count] = w;
+      wl.n[wl.count++] = nin[k];
       in[k] = w;
     }
+    if (ssd::launch_widen_bf16(wl, stream) != hipSuccess) return SSD_ERR_HIP;
     for (int k = 0; k < 5; ++k)
       if (grad[k]) grad[k] = ws + bl.off_w[kWideDx + k];
   }
@@ -821,11 +825,14 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   if (bl.bf16 && nonempty) {
     void* outs_bf16[5] = {dx, ddt, dB, dC, dz};
     const int64_t nout[5] = {nx, ndt, nbc, nbc, nx};
-    for (int k = 0; k < 5; ++k)
-      if (outs_bf16[k] &&
-          ssd::launch_narrow_bf16(static_cast<const float*>(grad[k]), outs_bf16[k], nout[k],
-                                  stream) != hipSuccess)
-        return SSD_ERR_HIP;
+    ssd::ConvList nl;
+    for (int k = 0; k < 5; ++k) {
+      if (!outs_bf16[k]) continue;
+      nl.src[nl.count] = grad[k];
+      nl.dst[nl.count] = outs_bf16[k];
+      nl.n[nl.count++] = nout[k];
+    }
+    if (ssd::launch_narrow_bf16(nl, stream) != hipSuccess) return SSD_ERR_HIP;
   }
   return SSD_OK;
 }

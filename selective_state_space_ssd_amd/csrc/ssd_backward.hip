@@ -754,38 +754,51 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
 // ---- bf16 <-> fp32 for the backward of bf16 inputs --------------------------
 // The backward of bf16 inputs widens them to fp32 (exactly), runs the fp32
 // kernels and rounds the gradients of the bf16 tensors to bf16 (nearest
-// even).  Eight elements per thread; 16-byte accesses when both pointers are
-// 16-byte aligned (`vec`), element by element otherwise and in the tail.
+// even).  One launch converts every tensor of a list (a launch per tensor left
+// each small one's start-up and drain exposed): thread piece p takes eight
+// elements of the tensor whose range of pieces holds p; 16-byte accesses when
+// both pointers of that tensor are 16-byte aligned, element by element
+// otherwise and in its tail.
 
-__global__ __launch_bounds__(256) void widen_bf16_kernel(const bf16_t* __restrict__ src,
-                                                          float* __restrict__ dst, int64_t n,
-                                                          bool vec) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= n) return;
-  if (vec && i + 8 <= n) {
+__device__ __forceinline__ int conv_entry(const ConvList& cl, int64_t piece) {
+  int k = 0;
+  while (k + 1 < cl.count && piece >= cl.start[k + 1]) ++k;
+  return k;
+}
+
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const ConvList cl) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (piece >= cl.start[cl.count]) return;
+  const int k = conv_entry(cl, piece);
+  const bf16_t* __restrict__ src = static_cast<const bf16_t*>(cl.src[k]);
+  float* __restrict__ dst = static_cast<float*>(cl.dst[k]);
+  const int64_t n = cl.n[k], i = (piece - cl.start[k]) * 8;
+  if (cl.vec[k] && i + 8 <= n) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + i);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     f4 a, b;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      a[2 * k] = bf16_lo(w[k]);
-      a[2 * k + 1] = bf16_hi(w[k]);
-      b[2 * k] = bf16_lo(w[k + 2]);
-      b[2 * k + 1] = bf16_hi(w[k + 2]);
+    for (int j = 0; j < 2; ++j) {
+      a[2 * j] = bf16_lo(w[j]);
+      a[2 * j + 1] = bf16_hi(w[j]);
+      b[2 * j] = bf16_lo(w[j + 2]);
+      b[2 * j + 1] = bf16_hi(w[j + 2]);
     }
     st4(dst + i, a);
     st4(dst + i + 4, b);
   } else {
-    for (int64_t k = i; k < n && k < i + 8; ++k) dst[k] = to_f32(src[k]);
+    for (int64_t e = i; e < n && e < i + 8; ++e) dst[e] = to_f32(src[e]);
   }
 }
 
-__global__ __launch_bounds__(256) void narrow_bf16_kernel(const float* __restrict__ src,
-                                                           bf16_t* __restrict__ dst, int64_t n,
-                                                           bool vec) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i >= n) return;
-  if (vec && i + 8 <= n) {
+__global__ __launch_bounds__(256) void narrow_bf16_kernel(const ConvList cl) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (piece >= cl.start[cl.count]) return;
+  const int k = conv_entry(cl, piece);
+  const float* __restrict__ src = static_cast<const float*>(cl.src[k]);
+  bf16_t* __restrict__ dst = static_cast<bf16_t*>(cl.dst[k]);
+  const int64_t n = cl.n[k], i = (piece - cl.start[k]) * 8;
+  if (cl.vec[k] && i + 8 <= n) {
     const f4 a = ld4(src + i), b = ld4(src + i + 4);
     uint4 v;
     v.x = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
@@ -794,25 +807,33 @@ __global__ __launch_bounds__(256) void narrow_bf16_kernel(const float* __restric
     v.w = f32_to_bf16_bits(b[2]) | (f32_to_bf16_bits(b[3]) << 16);
     *reinterpret_cast<uint4*>(dst + i) = v;
   } else {
-    for (int64_t k = i; k < n && k < i + 8; ++k) dst[k] = (bf16_t)f32_to_bf16_bits(src[k]);
+    for (int64_t e = i; e < n && e < i + 8; ++e) dst[e] = (bf16_t)f32_to_bf16_bits(src[e]);
   }
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t threads = (n + 7) / 8;
-  hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(src), dst, n, aligned16(src) && aligned16(dst));
+// Fill the piece ranges of a list; false when it is empty.
+static bool conv_prepare(ConvList& cl) {
+  cl.start[0] = 0;
+  for (int k = 0; k < cl.count; ++k) {
+    cl.vec[k] = aligned16(cl.src[k]) && aligned16(cl.dst[k]);
+    cl.start[k + 1] = cl.start[k] + (cl.n[k] + 7) / 8;
+  }
+  return cl.count > 0 && cl.start[cl.count] > 0;
+}
+
+hipError_t launch_widen_bf16(ConvList cl, hipStream_t s) {
+  if (!conv_prepare(cl)) return hipSuccess;
+  hipLaunchKernelGGL(widen_bf16_kernel, dim3((unsigned)((cl.start[cl.count] + 255) / 256)),
+                     dim3(256), 0, s, cl);
   return hipGetLastError();
 }
 
-hipError_t launch_narrow_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t threads = (n + 7) / 8;
-  hipLaunchKernelGGL(narrow_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                     src, static_cast<bf16_t*>(dst), n, aligned16(src) && aligned16(dst));
+hipError_t launch_narrow_bf16(ConvList cl, hipStream_t s) {
+  if (!conv_prepare(cl)) return hipSuccess;
+  hipLaunchKernelGGL(narrow_bf16_kernel, dim3((unsigned)((cl.start[cl.count] + 255) / 256)),
+                     dim3(256), 0, s, cl);
   return hipGetLastError();
 }
 

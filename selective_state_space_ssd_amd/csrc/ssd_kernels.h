@@ -194,8 +194,20 @@ int64_t bwd_blocks(int64_t L);
 hipError_t launch_bwd(const BwdProblem& q, hipStream_t stream);
 // bf16 [n] -> fp32 [n] (exact) and fp32 -> bf16 (nearest even), for the
 // backward of bf16 inputs.
-hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t stream);
-hipError_t launch_narrow_bf16(const float* src, void* dst, int64_t n, hipStream_t stream);
+// Lists of tensors converted by one launch: bf16 -> fp32 (widen) or fp32 ->
+// bf16 rounded to nearest even (narrow); count <= kConvMax, n elements each;
+// start and vec are filled by the launcher.
+constexpr int kConvMax = 6;
+struct ConvList {
+  const void* src[kConvMax];
+  void* dst[kConvMax];
+  int64_t n[kConvMax];
+  int64_t start[kConvMax + 1];
+  bool vec[kConvMax];
+  int count = 0;
+};
+hipError_t launch_widen_bf16(ConvList list, hipStream_t stream);
+hipError_t launch_narrow_bf16(ConvList list, hipStream_t stream);
 
 // True when (P, N, Q) is one of the compiled tile configurations.
 bool config_supported(int64_t P, int64_t N, int64_t Q);

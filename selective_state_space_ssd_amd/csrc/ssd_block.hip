@@ -34,6 +34,39 @@ constexpr int kConvTT = 32;  // timesteps per prologue workgroup
 // ulps it is off, the rarer a rounding lands on the neighbouring bf16 value.
 __device__ __forceinline__ float silu_accurate(float v) { return v / (1.0f + expf(-v)); }
 
+// The bf16 activation of one conv output, as the exact value rounded to fp32
+// and then to bf16 (nearest even both times).  The fp32 result act of
+// conv = bias + sum_k w_k v_k (W fmas) and silu lies within
+//   E = 1.1 W 2^-24 M + 5 2^-24 |act|,  M = |bias| + sum_k |w_k v_k|
+// of the exact value (each fma rounds once; exp, the sum and the division
+// add at most 5 units in the last place; silu's slope is below 1.1).  Its
+// bf16 rounding can differ from the exact value's only when a bf16 rounding
+// midpoint (low 16 bits 0x8000) lies within 2 E plus one fp32 unit of act:
+// such rare values are recomputed in fp64, summed in the order
+// sum_k w_k v_k + bias.  (Before this, about 700 of the 25 million values of
+// a batch row of the 8 x 4096 block landed on the neighbouring bf16 value,
+// and the gated norm turned those into 1.4e-2 of the output's 2e-2 bar.)
+template <int W>
+__device__ __forceinline__ uint32_t conv_silu_bf16(const float (&w)[W], const float* v, float bias,
+                                                   float act, float mag) {
+  const uint32_t u = __float_as_uint(act);
+  const int ex = (int)((u >> 23) & 0xffu);
+  if (ex == 0xff) return f32_to_bf16_bits(act);  // inf or NaN: as is
+  if (ex > 23) {  // |act| >= 2^-103 (smaller ones take the fp64 path)
+    const float ulp = __uint_as_float((uint32_t)(ex - 23) << 23);  // 2^(e - 23)
+    const float err = 1.1f * W * 0x1p-24f * mag + 5.0f * 0x1p-24f * fabsf(act);
+    const float k = (2.0f * err + ulp) / ulp + 2.0f;  // in fp32 units of act
+    const int lo = (int)(u & 0xffffu);
+    if (fabsf((float)(lo - 0x8000)) > k) return f32_to_bf16_bits(act);
+  }
+  double conv = 0.0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) conv += (double)w[i] * (double)v[i];
+  conv += (double)bias;
+  const double ad = conv / (1.0 + exp(-conv));
+  return f32_to_bf16_bits((float)ad);
+}
+
 template <typename T>
 __device__ __forceinline__ T from_f32(float v) {
   if constexpr (sizeof(T) == 2)
@@ -93,10 +126,18 @@ __global__ __launch_bounds__(256) void conv_split_kernel(
   const float bias = cb ? cb[c] : 0.0f;
 #pragma unroll
   for (int j = 0; j < kConvTT; ++j) {
-    float acc = bias;
+    float acc = bias, mag = fabsf(bias);
 #pragma unroll
-    for (int k = 0; k < W; ++k) acc += w[k] * v[j + k];
-    if (t0 + j < L) dst[(t0 + j) * stride] = from_f32<T>(silu_accurate(acc));
+    for (int k = 0; k < W; ++k) {
+      acc = fmaf(w[k], v[j + k], acc);
+      mag = fmaf(fabsf(w[k]), fabsf(v[j + k]), mag);
+    }
+    if (t0 + j < L) {
+      if constexpr (sizeof(T) == 2)
+        dst[(t0 + j) * stride] = (T)conv_silu_bf16<W>(w, v + j, bias, silu_accurate(acc), mag);
+      else
+        dst[(t0 + j) * stride] = silu_accurate(acc);
+    }
   }
 }
 

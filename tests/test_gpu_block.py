@@ -167,12 +167,13 @@ def test_block_prologue_outputs(dtype):
             tol = 0.0 if k == "dt" else 1e-6
             assert np.max(np.abs(got - want) / (1 + np.abs(want))) <= tol, k
         else:
-            # bf16: the GPU rounds its fp32 conv, the oracle its fp64 conv; they
-            # may land on neighbouring bf16 values where the activation sits
-            # within fp32 rounding of a halfway point
-            ulp = 2.0 ** (np.floor(np.log2(np.abs(want) + 1e-30)) - 7)
-            assert np.all(np.abs(got - want) <= ulp + 1e-30), k
-            assert np.mean(got != want) < 1e-2, k
+            # bf16: the prologue rounds each activation as the exact value
+            # would be rounded (values near a rounding midpoint recomputed in
+            # fp64), so it holds the oracle's values bit for bit (a plain fp32
+            # conv, emulated on the CPU, puts 16 of this test's 614400 values
+            # on the neighbouring bf16 value)
+            bad = np.flatnonzero(got != want)
+            assert bad.size == 0, (k, bad.size, bad[:5], got[bad[:5]], want[bad[:5]])
         off += r(sizes[k] * es)
 
 

@@ -405,7 +405,7 @@ def split_conv1d_scan_fwd(zxbcdt, conv1d_weight, conv1d_bias, dt_bias, A, D, chu
 def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.inf),
              chunk_size: int = 128, initial_states=None, return_final_states: bool = False,
              out=None, final_states=None, workspace=None, timing: Optional[Timing] = None,
-             seq_idx=None, kernel_path: str = "auto"):
+             seq_idx=None, kernel_path: str = "auto", check_wait: bool = False):
     """SSD chunked selective-scan forward on the GPU.
 
     x [b, L, H, P], dt [b, L, H], B/C [b, L, G, N], z like x: float32 or
@@ -416,7 +416,11 @@ def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.i
     ``initial_states`` tensor itself (in-place continuation).  ``seq_idx``
     [b, L] int32 packs several sequences per row (the state resets where the
     label changes; ``ssd_scan_fwd_varlen``).  ``kernel_path`` names the
-    kernel path ("auto" is ssd_scan_fwd's own choice; ``ssd_scan_fwd_path``)."""
+    kernel path ("auto" is ssd_scan_fwd's own choice; ``ssd_scan_fwd_path``).
+    On the fused bf16 path a result is valid only if no workgroup gave up its
+    bounded wait for the state entering its block; ``check_wait`` synchronizes
+    the stream after the call and raises SsdError(SSD_ERR_WAIT) if one did
+    (``ssd_scan_fwd_wait_status``; other paths have no such wait)."""
     import torch
 
     load_library()
@@ -476,24 +480,31 @@ def scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_limit=(0.0, math.i
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def waited():
+        if check_wait:
+            _check(wait_status(_ptr(workspace), workspace.numel(), b, L, H, P, N, G, chunk_size,
+                               dtype, seq_idx is not None, kernel_path, stream))
+        return (out, final_states) if return_final_states else out
+
     if code != 0:
         _check(scan_fwd_path_raw(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
             dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),
             _ptr(final_states) if return_final_states else None, _ptr(seq_idx), b, L, H, P, N,
             dtype, code, _ptr(workspace), workspace.numel(), stream))
-        return (out, final_states) if return_final_states else out
+        return waited()
     if seq_idx is not None:
         _check(scan_fwd_varlen_raw(
             _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
             dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),
             _ptr(final_states) if return_final_states else None, _ptr(seq_idx), b, L, H, P, N,
             dtype, _ptr(workspace), workspace.numel(), stream))
-        return (out, final_states) if return_final_states else out
+        return waited()
     status = scan_fwd_raw(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
         dt_limit[0], dt_limit[1], chunk_size, G, _ptr(initial_states), _ptr(out),
         _ptr(final_states) if return_final_states else None, b, L, H, P, N, dtype,
         _ptr(workspace), workspace.numel(), stream, timing)
     _check(status)
-    return (out, final_states) if return_final_states else out
+    return waited()

@@ -109,6 +109,7 @@ def run_gpu(t, chunk_size, dt_limit=(0.0, float("inf")), init=None, final=True, 
     """One call through the C ABI on the kernel path bf16_path set, with a
     poisoned workspace and guarded outputs unless the caller passes its own."""
     kw.setdefault("kernel_path", current_path())
+    kw.setdefault("check_wait", True)  # a fused-path workgroup that gave up waiting fails the call
     x = t["x"]
     dev = x.device
     b, L, H, P = x.shape

@@ -40,34 +40,59 @@ namespace ssd {
 
 namespace {
 constexpr int kBT = 64;   // block length of the backward
-constexpr int kXP = 65;   // padded row stride of 64-wide LDS tiles
+// Row pitches of the LDS tiles (floats): multiples of 4, so that rows are
+// read 16 bytes at a time, and 32 bytes past a multiple of 64 bytes, at which
+// 16-byte reads of 16 rows by four lane quarters measured free of bank
+// conflicts: 64-wide tiles 72, N-wide ones N + 8.
+constexpr int kXP = 72;
+template <int N>
+constexpr int kNP = N + 8;
 constexpr int kBwdThreads = 512;  // block backward kernel: eight waves (sixteen measured the same)
 // reverse state scan: up to 32 state columns, four waves per 16, per workgroup
 template <int N>
 constexpr int kScanThreads = 4 * ((N < 32 ? N : 32) / 16) * kWave;
 
-// One 16 x 16 output tile of a wave on v_mfma_f32_16x16x4_f32: lane l
-// supplies a(l%16, k + l/16) and b(k + l/16, l%16); register r of lane l holds
-// the element (row 4 (l/16) + r, column l%16).
+// One 16 x 16 output tile of a wave on v_mfma_f32_16x16x4_f32: at each
+// step lane l supplies a(l%16, k) and b(k, l%16) for its own k; register r of
+// lane l holds the element (row 4 (l/16) + r, column l%16).
+//
+// The contraction runs in groups of 16: in the group from k0, the lanes of
+// quarter g = l/16 take k = k0 + 4g + q at step q of four.  A lane's operands
+// of a group are thus four consecutive k, which the accessors return as one
+// f4: one 16-byte LDS read where they lie side by side (a row-major tile read
+// along its rows), four 4-byte reads otherwise.
 //
 // NJ tiles of one 16-row strip at once: acc[j] += sum_k a(i, k) * b(j, k, c).
 // The A value is shared by the NJ independent accumulators, so consecutive
-// MFMAs never wait on each other, and the unrolled k loop lets the operand
-// loads of later steps issue early.
+// MFMAs never wait on each other.
 template <int NJ, int K, typename FA, typename FB>
 __device__ __forceinline__ void tiles16(FA a, FB b, f4 (&acc)[NJ]) {
-  const int lane = threadIdx.x % kWave, i = lane % 16, kk = lane / 16;
+  static_assert(K % 16 == 0, "contraction in groups of 16");
+  const int lane = threadIdx.x % kWave, i = lane % 16, kq = 4 * (lane / 16);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = 0; k < K; k += 4) {
-    const float av = a(i, k + kk);
-    float bv[NJ];
+#pragma unroll 2
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const f4 av = a(i, k0 + kq);
+    f4 bv[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bv[j] = b(j, k + kk, i);
+    for (int j = 0; j < NJ; ++j) bv[j] = b(j, k0 + kq, i);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = mfma16x16x4(av, bv[j], acc[j]);
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = mfma16x16x4(av[q], bv[j][q], acc[j]);
   }
+}
+
+// Operand accessors over LDS tiles of row pitch `pitch` floats: four
+// consecutive k along row r (k and pitch multiples of 4), or down column c
+// from row k.
+__device__ __forceinline__ f4 along_row(const float* m, int pitch, int r, int k) {
+  return *reinterpret_cast<const f4*>(m + r * pitch + k);
+}
+__device__ __forceinline__ f4 down_col(const float* m, int pitch, int k, int c) {
+  return f4{m[k * pitch + c], m[(k + 1) * pitch + c], m[(k + 2) * pitch + c],
+            m[(k + 3) * pitch + c]};
 }
 }  // namespace
 
@@ -206,14 +231,14 @@ __global__ __launch_bounds__(kScanThreads<N>) void bwd_state_scan_kernel(
 
 // One workgroup (eight waves) per (batch, block, up to four heads of one
 // group).  Everything the products read is staged in one LDS buffer with
-// 16-byte global loads, regions reused as they die (floats; rows padded by
-// one against bank conflicts; B and C once, the rest per head):
-//   [0, 4160)       x [64][65]                 | then H_in [64][129] over
-//   [4160, 8256)    V [64][64]                 |   x and V (dC phase)
-//   [8256, 12416)   W [64][65]                 G [64][129] over V and W
-//   [12416, 16576)  dY [64][65]                  (first phase)
-//   [16576, 24832)  B [64][129]
-//   [24832, 33088)  C [64][129]
+// 16-byte global loads, regions reused as they die (floats, for N = 128; rows
+// padded to the pitches above; B and C once, the rest per head):
+//   [0, 4608)       x [64][72]                 | then H_in [64][136] over
+//   [4608, 9216)    V^T [64][72]               |   x and V (dC phase)
+//   [9216, 13824)   W [64][72]                 G [64][136] over V and W
+//   [13824, 18432)  dY [64][72]                  (first phase)
+//   [18432, 27136)  B [64][136]
+//   [27136, 35840)  C [64][136]
 // Phases per head: the products with G (G.B for dX, X.G for dB, x . (G B))
 // with G in LDS, kept in registers; R, and with K = C B^T (formed once per
 // workgroup, in registers) V and W in place of G; dX and dB;
@@ -228,7 +253,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     const float* __restrict__ dy, float* __restrict__ dx, float* __restrict__ dBh,
     float* __restrict__ dCh, float* __restrict__ ddt_raw, float* __restrict__ dA_p,
     float* __restrict__ dD_p, int64_t L, int64_t H, int64_t G, int64_t nb) {
-  constexpr int P = 64, T = kBT, NJ = N / 16, NS = N + 1;
+  constexpr int P = 64, T = kBT, NJ = N / 16, NS = kNP<N>;
   // NW waves: wave w takes the 16-row strip w % 4 of every product and
   // column group w / 4 of its column tiles (several waves per SIMD hide each
   // other's LDS and memory latency; with four waves, one per SIMD, they did
@@ -238,19 +263,20 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   constexpr int NCG = NW / 4;                      // column groups
   constexpr int NJ4 = 4 / NCG;                     // 64-wide column tiles per wave
   constexpr int NJW = NJ >= NCG ? NJ / NCG : 1;    // N-wide column tiles per wave
-  constexpr int OX = 0, OV = 4160, OW = 8256, OY = 12416, OB = 16576, OC = OB + T * NS;
-  static_assert(T * kXP == 4160 && OV + T * 64 == OW && OW + T * kXP == OY &&
-                OY + T * kXP == OB && T * NS <= OV + T * 64 && T * NS <= OY - OV, "LDS map");
+  constexpr int OX = 0, OV = T * kXP, OW = OV + T * kXP, OY = OW + T * kXP, OB = OY + T * kXP,
+                OC = OB + T * NS;
+  static_assert(P * NS <= OY - OV && P * NS <= OW - OX && kXP % 4 == 0 && NS % 4 == 0,
+                "LDS map");
   __shared__ __align__(16) float lds[OC + T * NS];
-  float* const xs_ = lds + OX;   // x[t][p]      stride 65
-  float* const vm = lds + OV;    // K, then V    stride 64
-  float* const wm = lds + OW;    // R, then W    stride 65
-  float* const ys_ = lds + OY;   // dY[t][p]     stride 65
-  float* const bs_ = lds + OB;   // B[t][n]      stride N+1
-  float* const cs_ = lds + OC;   // C[t][n]      stride N+1
-  float* const gs_ = lds + OV;   // G[p][n]      stride N+1 (first phase)
-  float* const hs_ = lds + OX;   // H_in[p][n]   stride N+1 (dC phase)
-  __shared__ float cum_l[T], dt_l[T];
+  float* const xs_ = lds + OX;   // x[t][p]      pitch kXP
+  float* const vm = lds + OV;    // V^T[s][t]    pitch kXP
+  float* const wm = lds + OW;    // W[t][s]      pitch kXP
+  float* const ys_ = lds + OY;   // dY[t][p]     pitch kXP
+  float* const bs_ = lds + OB;   // B[t][n]      pitch NS
+  float* const cs_ = lds + OC;   // C[t][n]      pitch NS
+  float* const gs_ = lds + OV;   // G[p][n]      pitch NS (first phase)
+  float* const hs_ = lds + OX;   // H_in[p][n]   pitch NS (dC phase)
+  __shared__ __align__(16) float cum_l[T], dt_l[T];
   __shared__ float ecum[T], wdt[T];  // exp(cum_t); w_t = exp(cl - cum_t) dt_t
   // per-half row sums and per-strip column sums, added in a fixed order
   __shared__ float rowv[NCG][T], xgb[NCG][T], yod[NCG][T], red[2 * NW];
@@ -301,11 +327,8 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     for (int q = 0; q < QB; ++q) {
       const int e = 4 * (q * NTH + tid), t = e / N, n = e % N;
       if (e < T * N) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          bs_[t * NS + n + c] = bv[q][c];
-          cs_[t * NS + n + c] = cv[q][c];
-        }
+        *reinterpret_cast<f4*>(bs_ + t * NS + n) = bv[q];
+        *reinterpret_cast<f4*>(cs_ + t * NS + n) = cv[q];
       }
     }
   }
@@ -323,8 +346,9 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // K = C B^T is the same for every head of the group: formed once, kept in
   // registers (rows t in [16 strip, 16 strip + 16), this wave's s tiles).
   f4 kall[NJ4];
-  tiles16<NJ4, N>([&](int r, int k) { return cs_[(16 * strip + r) * NS + k]; },
-                [&](int j, int k, int c) { return bs_[(16 * (j4 + j) + c) * NS + k]; }, kall);
+  tiles16<NJ4, N>([&](int r, int k) { return along_row(cs_, NS, 16 * strip + r, k); },
+                  [&](int j, int k, int c) { return along_row(bs_, NS, 16 * (j4 + j) + c, k); },
+                  kall);
 
   for (int hk = 0; hk < HPW; ++hk) {
   const int64_t h = hq * HPW + hk;
@@ -350,19 +374,13 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
 #pragma unroll
     for (int q = 0; q < QX; ++q) {
       const int e = 4 * (q * NTH + tid), t = e / P, p = e % P;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        xs_[t * kXP + p + c] = xv[q][c];
-        ys_[t * kXP + p + c] = yv[q][c];
-      }
+      *reinterpret_cast<f4*>(xs_ + t * kXP + p) = xv[q];
+      *reinterpret_cast<f4*>(ys_ + t * kXP + p) = yv[q];
     }
 #pragma unroll
     for (int q = 0; q < QG; ++q) {
       const int e = 4 * (q * NTH + tid), p = e / N, n = e % N;
-      if (e < P * N) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) gs_[p * NS + n + c] = gv[q][c];
-      }
+      if (e < P * N) *reinterpret_cast<f4*>(gs_ + p * NS + n) = gv[q];
     }
   }
   if (tid < T) {
@@ -394,11 +412,13 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // ---- products with G: GB[s][p] = B_s . G_p (dX), XG[s][n] = x_s^T G (dB) --
   // rows s in [16 strip, 16 strip + 16)
   f4 gball[NJ4], xgall[NJW];
-  tiles16<NJ4, N>([&](int r, int k) { return bs_[(16 * strip + r) * NS + k]; },
-                [&](int j, int k, int c) { return gs_[(16 * (j4 + j) + c) * NS + k]; }, gball);
+  tiles16<NJ4, N>([&](int r, int k) { return along_row(bs_, NS, 16 * strip + r, k); },
+                  [&](int j, int k, int c) { return along_row(gs_, NS, 16 * (j4 + j) + c, k); },
+                  gball);
   if (hasn)
-    tiles16<NJW, P>([&](int r, int k) { return xs_[(16 * strip + r) * kXP + k]; },
-                    [&](int j, int k, int c) { return gs_[k * NS + 16 * (jn + j) + c]; }, xgall);
+    tiles16<NJW, P>([&](int r, int k) { return along_row(xs_, kXP, 16 * strip + r, k); },
+                    [&](int j, int k, int c) { return down_col(gs_, NS, k, 16 * (jn + j) + c); },
+                    xgall);
   {
     float xsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -418,8 +438,9 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   // rows t in [16 strip, 16 strip + 16), this wave's column tiles of s
   float rsum[4] = {0.f, 0.f, 0.f, 0.f};
   f4 rall[NJ4];
-  tiles16<NJ4, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
-                  [&](int j, int k, int c) { return xs_[(16 * (j4 + j) + c) * kXP + k]; }, rall);
+  tiles16<NJ4, P>([&](int r, int k) { return along_row(ys_, kXP, 16 * strip + r, k); },
+                  [&](int j, int k, int c) { return along_row(xs_, kXP, 16 * (j4 + j) + c, k); },
+                  rall);
 #pragma unroll
   for (int j = 0; j < NJ4; ++j) {
     const f4 kacc = kall[j], racc = rall[j];
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
       const float m = s <= t ? expf(cum_l[t] - cum_l[s]) : 0.0f;
       const float v0 = m * kacc[r] * racc[r];
       const float v = v0 * dt_l[s];
-      vm[t * 64 + s] = m * kacc[r] * dt_l[s];
+      vm[s * kXP + t] = m * kacc[r] * dt_l[s];
       wm[t * kXP + s] = m * racc[r];
       rsum[r] += v;
       cs += v;
@@ -455,8 +476,9 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   {
     const auto dxr = row_rsrc(dx + xo, xbytes);
     f4 vall[NJ4];
-    tiles16<NJ4, T>([&](int r, int k) { return vm[k * 64 + 16 * strip + r]; },
-                  [&](int j, int k, int c) { return ys_[k * kXP + 16 * (j4 + j) + c]; }, vall);
+    tiles16<NJ4, T>([&](int r, int k) { return along_row(vm, kXP, 16 * strip + r, k); },
+                    [&](int j, int k, int c) { return down_col(ys_, kXP, k, 16 * (j4 + j) + c); },
+                    vall);
 #pragma unroll
     for (int j = 0; j < NJ4; ++j) {
       const int p = 16 * (j4 + j) + i;
@@ -469,8 +491,9 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     }
     if (hasn) {
     f4 a1[NJW];
-    tiles16<NJW, T>([&](int r, int k) { return wm[k * kXP + 16 * strip + r]; },
-                    [&](int j, int k, int c) { return cs_[k * NS + 16 * (jn + j) + c]; }, a1);
+    tiles16<NJW, T>([&](int r, int k) { return down_col(wm, kXP, k, 16 * strip + r); },
+                    [&](int j, int k, int c) { return down_col(cs_, NS, k, 16 * (jn + j) + c); },
+                    a1);
 #pragma unroll
     for (int j = 0; j < NJW; ++j)
 #pragma unroll
@@ -503,11 +526,9 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
       if (q * NTH + tid >= P * N / 4) break;
       int p, n;
       state_tile_coords(q * NTH + tid, N, &p, &n);
+      *reinterpret_cast<f4*>(hs_ + p * NS + n) = hv[q];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        hs_[p * NS + n + c] = hv[q][c];
-        gh += hv[q][c] * gv2[q][c];
-      }
+      for (int c = 0; c < 4; ++c) gh += hv[q][c] * gv2[q][c];
     }
   }
   __syncthreads();
@@ -516,10 +537,12 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   float ysum[4] = {0.f, 0.f, 0.f, 0.f};
   if (hasn) {
     f4 a1[NJW], a2[NJW];
-    tiles16<NJW, P>([&](int r, int k) { return ys_[(16 * strip + r) * kXP + k]; },
-                    [&](int j, int k, int c) { return hs_[k * NS + 16 * (jn + j) + c]; }, a1);
-    tiles16<NJW, T>([&](int r, int k) { return wm[(16 * strip + r) * kXP + k] * dt_l[k]; },
-                    [&](int j, int k, int c) { return bs_[k * NS + 16 * (jn + j) + c]; }, a2);
+    tiles16<NJW, P>([&](int r, int k) { return along_row(ys_, kXP, 16 * strip + r, k); },
+                    [&](int j, int k, int c) { return down_col(hs_, NS, k, 16 * (jn + j) + c); },
+                    a1);
+    tiles16<NJW, T>(
+        [&](int r, int k) { return along_row(wm, kXP, 16 * strip + r, k) * along_row(dt_l, 0, 0, k); },
+        [&](int j, int k, int c) { return down_col(bs_, NS, k, 16 * (jn + j) + c); }, a2);
 #pragma unroll
     for (int j = 0; j < NJW; ++j) {
       const int n = 16 * (jn + j) + i;

@@ -41,12 +41,14 @@ namespace ssd {
 namespace {
 constexpr int kBT = 64;   // block length of the backward
 // Row pitches of the LDS tiles (floats): multiples of 4, so that rows are
-// read 16 bytes at a time, and 32 bytes past a multiple of 64 bytes, at which
-// 16-byte reads of 16 rows by four lane quarters measured free of bank
-// conflicts: 64-wide tiles 72, N-wide ones N + 8.
+// read 16 bytes at a time.  64-wide tiles 72 (32 bytes past a multiple of 64
+// bytes, at which 16-byte reads of 16 rows by four lane quarters measured
+// free of bank conflicts); N-wide ones N + 4 (16 bytes past: the four lane
+// quarters' 4-byte reads down a column, rows 4 apart, fall in distinct banks),
+// since most of their reads go down columns.
 constexpr int kXP = 72;
 template <int N>
-constexpr int kNP = N + 8;
+constexpr int kNP = N + 4;
 constexpr int kBwdThreads = 512;  // block backward kernel: eight waves (sixteen measured the same)
 // reverse state scan: up to 32 state columns, four waves per 16, per workgroup
 template <int N>
@@ -233,12 +235,12 @@ __global__ __launch_bounds__(kScanThreads<N>) void bwd_state_scan_kernel(
 // group).  Everything the products read is staged in one LDS buffer with
 // 16-byte global loads, regions reused as they die (floats, for N = 128; rows
 // padded to the pitches above; B and C once, the rest per head):
-//   [0, 4608)       x [64][72]                 | then H_in [64][136] over
+//   [0, 4608)       x [64][72]                 | then H_in [64][132] over
 //   [4608, 9216)    V^T [64][72]               |   x and V (dC phase)
-//   [9216, 13824)   W [64][72]                 G [64][136] over V and W
+//   [9216, 13824)   W [64][72]                 G [64][132] over V and W
 //   [13824, 18432)  dY [64][72]                  (first phase)
-//   [18432, 27136)  B [64][136]
-//   [27136, 35840)  C [64][136]
+//   [18432, 26880)  B [64][132]
+//   [26880, 35328)  C [64][132]
 // Phases per head: the products with G (G.B for dX, X.G for dB, x . (G B))
 // with G in LDS, kept in registers; R, and with K = C B^T (formed once per
 // workgroup, in registers) V and W in place of G; dX and dB;

@@ -296,6 +296,8 @@ def describe(w):
 STAGE_KERNELS = {
     "staged": {"prep": "dt_cumsum_kernel", "chunk_state": "chunk_state kernel",
                "state_passing": "state_passing_kernel", "chunk_scan": "chunk scan kernel"},
+    "staged_scan": {"chunk_state": "state_scan_kernel (stages 1-3)",
+                    "chunk_scan": "chunk scan kernel"},
     "chain": {"chunk_scan": "chain_scan_bf16_kernel"},
     "chain_segmented": {"chunk_state": "unit_state_bf16_kernel",
                         "chunk_scan": "chain_scan_bf16_kernel (segments)"},

@@ -257,6 +257,11 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
 #define SSD_PATH_CHAIN 5
 #define SSD_PATH_STEP 6 /* reported by ssd_scan_fwd_taken_path only (seqlen <= 16) */
 #define SSD_PATH_CHAIN_SEGMENTED 7
+/* reported by ssd_scan_fwd_taken_path only: the staged path with its first
+ * three stages as one pass (fp32, no seq_idx, dstate 64 or 128, chunk 64 or
+ * 128, at most 32 chunks per sequence, batch x nheads x dstate/32 between
+ * half and all of the 256 compute units) */
+#define SSD_PATH_STAGED_SCAN 8
 
 /*
  * ssd_scan_fwd_path -- ssd_scan_fwd on an explicitly chosen kernel path.
@@ -281,8 +286,9 @@ size_t ssd_scan_fwd_path_workspace_size(int64_t batch, int64_t seqlen, int64_t n
                                         int chunk_size, int dtype, int varlen, int kernel_path);
 
 /* The kernel path a call with these arguments takes: SSD_PATH_STAGED,
- * SSD_PATH_FUSED_HEAD, SSD_PATH_FUSED_GROUP, SSD_PATH_CHAIN,
- * SSD_PATH_CHAIN_SEGMENTED or SSD_PATH_STEP (the step kernel of seqlen <= 16),
+ * SSD_PATH_STAGED_SCAN, SSD_PATH_FUSED_HEAD, SSD_PATH_FUSED_GROUP,
+ * SSD_PATH_CHAIN, SSD_PATH_CHAIN_SEGMENTED or SSD_PATH_STEP (the step kernel
+ * of seqlen <= 16),
  * after the fallbacks above; kernel_path
  * is what the call asks for (SSD_PATH_AUTO for ssd_scan_fwd).  A negative
  * status for arguments the call would reject.  Pure host computation. */

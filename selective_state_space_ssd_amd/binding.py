@@ -143,8 +143,8 @@ def varlen_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk
 def taken_path(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype, varlen=False,
                kernel_path: str = "auto") -> str:
     """Name of the kernel path a call with these arguments takes ("staged",
-    "fused_head", "fused_group", "chain", "chain_segmented" or "step"); raises SsdError for
-    arguments the call would reject."""
+    "staged_scan", "fused_head", "fused_group", "chain", "chain_segmented" or "step"); raises
+    SsdError for arguments the call would reject."""
     code = int(load_library().ssd_scan_fwd_taken_path(
         int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(ngroups),
         int(chunk_size), int(dtype), 1 if varlen else 0, path_code(kernel_path)))
@@ -152,6 +152,7 @@ def taken_path(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtyp
         raise SsdError(code, status_string(code))
     names = {v: k for k, v in KERNEL_PATHS.items()}
     names[6] = "step"
+    names[8] = "staged_scan"
     return names[code]
 
 

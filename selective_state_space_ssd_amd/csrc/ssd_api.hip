@@ -419,8 +419,16 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     return SSD_OK;
   }
   const bool bf16k = ssd::use_bf16_kernels(p);
+  // fp32 with few chunks: stages 1-3 in one pass (reported as the chunk-state
+  // stage, with an empty state-passing stage)
+  const bool scan23 = seqlen > 0 && !bf16k &&
+                      ssd::use_state_scan(p.bf16, varlen, batch, seqlen, nheads, dstate,
+                                          chunk_size);
   if (p.ws_seg && ssd::launch_seq_count(p, stream) != hipSuccess) return SSD_ERR_HIP;
-  if (seqlen > 0 && bf16k) {
+  if (scan23) {
+    if (!mark(1) || ssd::launch_state_scan(p, stream) != hipSuccess || !mark(2))
+      return SSD_ERR_HIP;
+  } else if (seqlen > 0 && bf16k) {
     // prep (B^T), then the chunk state with dt/cumsum fused in
     if (ssd::launch_bf16_stage(p, stream, 0) != hipSuccess || !mark(1)) return SSD_ERR_HIP;
     if (ssd::launch_bf16_stage(p, stream, 1) != hipSuccess || !mark(2)) return SSD_ERR_HIP;
@@ -433,7 +441,7 @@ static int run(const void* x, const void* dt, const float* A, const void* B, con
     return SSD_ERR_HIP;
   }
   // state passing also covers seqlen == 0: final = initial state (or zeros)
-  if (seqlen > 0 || final_states) {
+  if (!scan23 && (seqlen > 0 || final_states)) {
     if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
   }
   if (!mark(3)) return SSD_ERR_HIP;
@@ -504,7 +512,7 @@ int ssd_scan_fwd_noalloc(const void* x, const void* dt, const float* A, const vo
   const int taken = ssd_scan_fwd_taken_path(batch, seqlen, nheads, headdim, dstate, ngroups,
                                             chunk_size, dtype, 0, SSD_PATH_AUTO);
   if (taken < 0) return taken;
-  const int path = taken == SSD_PATH_STAGED                ? SSD_PATH_STAGED
+  const int path = taken == SSD_PATH_STAGED || taken == SSD_PATH_STAGED_SCAN ? SSD_PATH_STAGED
                    : taken == SSD_PATH_FUSED_HEAD          ? SSD_PATH_FUSED_HEAD
                    : taken == SSD_PATH_CHAIN_SEGMENTED ? SSD_PATH_CHAIN_SEGMENTED
                                                            : SSD_PATH_AUTO;
@@ -589,7 +597,10 @@ int ssd_scan_fwd_taken_path(int64_t batch, int64_t seqlen, int64_t nheads, int64
   if (lay.fused)
     return kernel_path == SSD_PATH_FUSED_GROUP && !varlen ? SSD_PATH_FUSED_GROUP
                                                          : SSD_PATH_FUSED_HEAD;
-  return SSD_PATH_STAGED;
+  return ssd::use_state_scan(dtype == SSD_BF16, varlen != 0, batch, seqlen, nheads, dstate,
+                             chunk_size)
+             ? SSD_PATH_STAGED_SCAN
+             : SSD_PATH_STAGED;
 }
 
 int ssd_scan_fwd_wait_status(const void* workspace, size_t workspace_bytes, int64_t batch,
@@ -784,10 +795,14 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   if (nonempty) {
     // the forward again (64-step blocks, no gate): dt, cum, states, and the
     // ungated y, which only dz needs (no gate: no y)
-    if (!ssd::chunk_state_fuses_dt(p) && ssd::launch_dt_cumsum(p, stream) != hipSuccess)
-      return SSD_ERR_HIP;
-    if (ssd::launch_chunk_state(p, stream) != hipSuccess) return SSD_ERR_HIP;
-    if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    if (ssd::use_state_scan(false, false, batch, seqlen, nheads, dstate, 64)) {
+      if (ssd::launch_state_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    } else {
+      if (!ssd::chunk_state_fuses_dt(p) && ssd::launch_dt_cumsum(p, stream) != hipSuccess)
+        return SSD_ERR_HIP;
+      if (ssd::launch_chunk_state(p, stream) != hipSuccess) return SSD_ERR_HIP;
+      if (ssd::launch_state_passing(p, stream) != hipSuccess) return SSD_ERR_HIP;
+    }
     // With a gate and the four-heads chunk scan, its epilogue forms dY and dz
     // from y directly (no y round trip, no gate kernel)
     if (fuse_gate) {

@@ -39,13 +39,30 @@ __device__ __forceinline__ float softplus(float u) {
 // is the cum of its last real step.  Writes dt and cum to the workspace and
 // returns them in dt_out / cum_out (the lane's E values) and the chunk's last
 // cum in *cum_last.  ws_dt / ws_cum may be null (nothing stored).
+//
+// In two parts, so that a wave handling several chunks can issue every load
+// first: wave_dt_load reads the lane's raw dt values (0 past the end), and
+// wave_dt_scan forms the rest from them.
 template <typename T, int Q>
-__device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, float a, float bias,
-                                               float dt_min, float dt_max, int64_t b, int64_t c,
-                                               int64_t h, int64_t L, int64_t H, int64_t nc,
-                                               float* __restrict__ ws_dt,
-                                               float* __restrict__ ws_cum, float (&dt_out)[Q / 64],
-                                               float (&cum_out)[Q / 64], float* cum_last) {
+__device__ __forceinline__ void wave_dt_load(const T* __restrict__ dt_raw, int64_t b, int64_t c,
+                                             int64_t h, int64_t L, int64_t H,
+                                             float (&raw)[Q / 64]) {
+  constexpr int E = Q / kWave;
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const int64_t t = c * Q + (int64_t)lane * E + i;
+    raw[i] = t < L ? ld1(dt_raw + (b * L + t) * H + h) : 0.0f;
+  }
+}
+
+template <int Q>
+__device__ __forceinline__ void wave_dt_scan(const float (&raw)[Q / 64], float a, float bias,
+                                             float dt_min, float dt_max, int64_t b, int64_t c,
+                                             int64_t h, int64_t L, int64_t H, int64_t nc,
+                                             float* __restrict__ ws_dt,
+                                             float* __restrict__ ws_cum, float (&dt_out)[Q / 64],
+                                             float (&cum_out)[Q / 64], float* cum_last) {
   constexpr int E = Q / kWave;
   const int lane = threadIdx.x % kWave;
   float run[E];
@@ -55,7 +72,7 @@ __device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, flo
     const int64_t t = c * Q + (int64_t)lane * E + i;
     float d = 0.0f;
     if (t < L) {
-      d = softplus(ld1(dt_raw + (b * L + t) * H + h) + bias);
+      d = softplus(raw[i] + bias);
       // comparisons (not fminf/fmaxf) so that a NaN input stays NaN
       d = d < dt_min ? dt_min : d;
       d = d > dt_max ? dt_max : d;
@@ -81,6 +98,19 @@ __device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, flo
       ws_cum[o + i] = cum_out[i];
     }
   }
+}
+
+template <typename T, int Q>
+__device__ __forceinline__ void wave_dt_cumsum(const T* __restrict__ dt_raw, float a, float bias,
+                                               float dt_min, float dt_max, int64_t b, int64_t c,
+                                               int64_t h, int64_t L, int64_t H, int64_t nc,
+                                               float* __restrict__ ws_dt,
+                                               float* __restrict__ ws_cum, float (&dt_out)[Q / 64],
+                                               float (&cum_out)[Q / 64], float* cum_last) {
+  float raw[Q / kWave];
+  wave_dt_load<T, Q>(dt_raw, b, c, h, L, H, raw);
+  wave_dt_scan<Q>(raw, a, bias, dt_min, dt_max, b, c, h, L, H, nc, ws_dt, ws_cum, dt_out,
+                  cum_out, cum_last);
 }
 
 }  // namespace ssd

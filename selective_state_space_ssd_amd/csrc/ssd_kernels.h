@@ -65,6 +65,11 @@ hipError_t launch_dt_cumsum(const Problem& p, hipStream_t stream);
 hipError_t launch_seq_count(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_passing(const Problem& p, hipStream_t stream);
+// fp32 stages 2 and 3 as one pass (and stage 1 with them; the chunk scan's
+// G^T tiles beside it), for the shapes use_state_scan accepts
+bool use_state_scan(bool bf16, bool varlen, int64_t b, int64_t L, int64_t H, int64_t N,
+                    int64_t Q);
+hipError_t launch_state_scan(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
 
 // The four-heads-per-workgroup chunk-scan kernel (fp32 scan of fp32 inputs,

@@ -18,7 +18,7 @@
 // B C^T, once per (chunk, group), into the workspace.  They depend on the
 // inputs alone; here their matrix work runs beside a pass that is bound by
 // memory and leaves the matrix cores idle.
-#include "ssd_device.h"
+#include "ssd_dt.h"
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -32,8 +32,9 @@ namespace ssd {
 // taken as zero.  The same products in the same order as the chunk scan's own
 // G phase (lane l supplies B[32 si + l%32][(N/2)(l/32) + k] and C[32 ti +
 // l%32][...] for k = 0 .. N/2-1), so both give identical tiles; stored in
-// register order (ssd_device.h).
-template <typename T, int Q, int N>
+// register order (ssd_device.h).  The operands are loaded in NB batches (one
+// memory latency per batch; NB > 1 where registers are short).
+template <typename T, int Q, int N, int NB = 1>
 __device__ __forceinline__ void gram_tile(const T* __restrict__ Bm, const T* __restrict__ Cm,
                                           float* __restrict__ gram, int64_t job, int64_t L,
                                           int64_t G, int64_t nc, int lane) {
@@ -54,20 +55,25 @@ __device__ __forceinline__ void gram_tile(const T* __restrict__ Bm, const T* __r
   // every operand load at once (one memory latency per tile; the pass beside
   // it keeps the memory system busy, so a tile that waited batch by batch
   // would wait several times), then the 4 KQ products
+  static_assert(KQ % NB == 0, "batches");
+  constexpr int KB = KQ / NB;
   f16x acc = zero16();
-  f4 bv[KQ], cv[KQ];
 #pragma unroll
-  for (int q = 0; q < KQ; ++q) {
-    bv[q] = ld4(bp + 4 * q);
-    cv[q] = ld4(cp + 4 * q);
+  for (int nb = 0; nb < NB; ++nb) {
+    f4 bv[KB], cv[KB];
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      bv[q] = ld4(bp + 4 * (nb * KB + q));
+      cv[q] = ld4(cp + 4 * (nb * KB + q));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
+#pragma unroll
+    for (int q = 0; q < KB; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = mfma32x32x2(__uint_as_float(__float_as_uint(bv[q][e]) & ms),
+                          __uint_as_float(__float_as_uint(cv[q][e]) & mt), acc);
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
-#pragma unroll
-  for (int q = 0; q < KQ; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = mfma32x32x2(__uint_as_float(__float_as_uint(bv[q][e]) & ms),
-                        __uint_as_float(__float_as_uint(cv[q][e]) & mt), acc);
   float* dst = gram + (unit * NG + tau) * 1024 + 4 * lane;
 #pragma unroll
   for (int R = 0; R < 4; ++R) {
@@ -133,6 +139,229 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     }
   }
   if (final_states) st4(final_states + (b * H + h) * PN + p * N + n, hs);
+}
+
+// ---------------------------------------------------------------------------
+// stages 2 and 3 in one pass
+// ---------------------------------------------------------------------------
+
+// For fp32 inputs with few chunks per sequence, one workgroup per (batch,
+// head, 32 state columns) walks the chunks in order: it forms each chunk's
+// contribution S_c on the matrix cores (as stage 2) and folds it into the
+// state it carries in registers (as above), so the chunk states never go
+// through memory and the two launches become one.  The walk is sequential in
+// c, but the S_c products are independent and the fold is four fmas per
+// lane, so the matrix work of the chunks follows back to back; the
+// parallelism is batch x heads x N/32 workgroups instead of also x chunks,
+// which is why the pass is chosen only when that fills the machine.
+//
+// Eight waves; wave w holds the 16 x 16 tile (state columns 16 (w % 2) of the
+// slice, rows 16 (w / 2)) of S^T = B^T diag(w) X on v_mfma_f32_16x16x4_f32:
+// lane (i, g = l/16) supplies B[t][n] and w_t x[t][p] for t = k0 + 4g + q at
+// step q of each group of 16 steps (its four rows of the chunk's LDS tiles),
+// and register r holds column n = 4g + r of row p = i, i.e. four consecutive
+// n of one p: one float4 of the tiled state layout.  A chunk's x rows and the
+// slice's B rows are staged in LDS (row pitches 68 and 36 floats: the four
+// lane quarters read rows four apart, which land in distinct banks); the rows
+// of the chunk after next are loaded into a second register set while the
+// current one computes, so each load has two chunks' time to arrive.
+// dt, the running sums and w_t of every chunk are formed first (a wave per
+// chunk, the slice-0 workgroup also writing them for the chunk scan) and kept
+// in LDS, and the staged x rows are scaled by w_t on the way in.  The chunk
+// scan's G^T tiles are formed by the same workgroups, a wave per tile, while
+// their first loads are in flight.
+constexpr int kScanChunksMax = 32;
+constexpr int kScanSlice = 32;  // state columns per workgroup
+
+template <int Q, int N>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void state_scan_kernel(
+    const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ dt_raw,
+    const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
+    const float* init, float* __restrict__ ws_dt, float* __restrict__ ws_cum,
+    float* __restrict__ states_in, float* final_states, int64_t L, int64_t H, int64_t G,
+    int64_t nc, int64_t nscan, const float* __restrict__ Cm, float* __restrict__ gram,
+    int64_t gram_jobs) {
+  constexpr int P = 64, NT = 512, XP = 68, BP = 36, E = Q / kWave;
+  constexpr int QX = Q * P / (4 * NT), QB = Q * kScanSlice / (4 * NT);
+  static_assert(QX >= 1 && QB >= 1 && Q * P % (4 * NT) == 0 && Q * kScanSlice % (4 * NT) == 0,
+                "staging");
+  __shared__ __align__(16) float xs[Q * XP];                // x[t][p] of the chunk
+  __shared__ __align__(16) float bs[Q * BP];                // B[t][n] of the slice
+  __shared__ __align__(16) float wl[kScanChunksMax * Q];    // w_t of every chunk
+  __shared__ float dec[kScanChunksMax];                     // exp(cum_last) of every chunk
+
+  // the slices of one head are b H workgroups apart: on one XCD (sharing the
+  // x rows in its L2) when b H is a multiple of 8
+  const int64_t BH = nscan / (N / kScanSlice);
+  const int64_t bh = blockIdx.x % BH, sl = blockIdx.x / BH;
+  const int64_t b = bh / H, h = bh % H;
+  // 32-bit and wave-uniform: the B buffer resource needs a scalar base
+  const int64_t g = __builtin_amdgcn_readfirstlane((int)h / (int)(H / G));
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int i = lane % 16, kq = 4 * (lane / 16);
+  const int nl = 16 * (wave & 1), p0 = 16 * (wave >> 1);  // tile within the slice
+  const int n = kScanSlice * (int)sl + nl + kq, p = p0 + i;  // this lane's float4 of the state
+  constexpr int64_t PN = (int64_t)P * N;
+
+  const uint32_t xrow = (uint32_t)(H * P * 4), brow = (uint32_t)(G * N * 4);
+  // rows past the sequence end read as zero (their w is zero too); chunks
+  // past the last are not read
+  auto load = [&](int64_t c, f4 (&xv)[QX], f4 (&bv)[QB]) {
+    if (c >= nc) return;
+    const int64_t t0 = c * Q;
+    const uint32_t last = (uint32_t)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
+    const auto xr = row_rsrc(x + ((b * L + t0) * H + h) * P, last * xrow + P * 4);
+    const auto br = row_rsrc(Bm + ((b * L + t0) * G + g) * N + kScanSlice * sl,
+                             last * brow + kScanSlice * 4);
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+      const int e = 4 * (q * NT + tid);
+      xv[q] = bld4(xr, (uint32_t)(e / P) * xrow + (uint32_t)(e % P) * 4);
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int e = 4 * (q * NT + tid);
+      bv[q] = bld4(br, (uint32_t)(e / kScanSlice) * brow + (uint32_t)(e % kScanSlice) * 4);
+    }
+  };
+  // init and final_states may be the same buffer: each lane reads its four
+  // elements of init before it writes the same four of final.  Loaded first:
+  // the prologue's wait then covers it, and the loop never waits on it (a
+  // load still in flight at the loop would make every chunk wait for all).
+  f4 hs = init ? ld4(init + bh * PN + p * N + n) : f4{0.f, 0.f, 0.f, 0.f};
+  f4 xa[QX], ba[QB], xb[QX], bb[QB];  // register sets of even and odd chunks
+  load(0, xa, ba);
+  load(1, xb, bb);
+
+  // the chunk scan's G^T tiles, a wave per tile, while those loads are in
+  // flight: tile j goes to workgroup j % nscan, wave j / nscan
+  for (int64_t job = (int64_t)wave * nscan + blockIdx.x; job < gram_jobs;
+       job += (NT / kWave) * nscan)
+    gram_tile<float, Q, N, N / 64>(Bm, Cm, gram, job, L, G, nc, lane);
+
+  // dt, running sums (stored once, by the slice-0 workgroup) and w_t, a wave
+  // per chunk
+  {
+    constexpr int CW = kScanChunksMax / (NT / kWave);  // chunks per wave, at most
+    const float a = A[h], bias = dt_bias ? dt_bias[h] : 0.0f;
+    float raw[CW][E];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int64_t c = wave + (NT / kWave) * j;
+      if (c < nc) wave_dt_load<float, Q>(dt_raw, b, c, h, L, H, raw[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      const int64_t c = wave + (NT / kWave) * j;
+      if (c < nc) {
+        float dtv[E], cum[E], cl;
+        wave_dt_scan<Q>(raw[j], a, bias, dt_min, dt_max, b, c, h, L, H, nc,
+                        sl == 0 ? ws_dt : nullptr, ws_cum, dtv, cum, &cl);
+#pragma unroll
+        for (int k = 0; k < E; ++k) wl[c * Q + lane * E + k] = __expf(cl - cum[k]) * dtv[k];
+        if (lane == 0) dec[c] = __expf(cl);
+      }
+    }
+  }
+
+  __syncthreads();  // every w_t is in LDS before the first staging scales by it
+  float* dst = states_in + (b * nc * H + h) * PN + state_tile_offset(p, n, N);
+  const int64_t cstride = H * PN;
+  // chunk c: stage its rows from their register set (x scaled by w_t), load
+  // chunk c + 2 into that set, then form S_c and fold it in
+  auto step = [&](int64_t c, f4 (&xv)[QX], f4 (&bv)[QB]) {
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+      const int e = 4 * (q * NT + tid);
+      const float w = wl[c * Q + e / P];
+      f4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = w * xv[q][k];
+      *reinterpret_cast<f4*>(xs + (e / P) * XP + e % P) = v;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int e = 4 * (q * NT + tid);
+      *reinterpret_cast<f4*>(bs + (e / kScanSlice) * BP + e % kScanSlice) = bv[q];
+    }
+    __syncthreads();  // chunk c staged
+    load(c + 2, xv, bv);
+    // the operands of the chunk's first half read, then its second half's,
+    // whose reads run under the first half's products; four accumulators,
+    // one per step of a group, so that consecutive MFMAs are independent
+    constexpr int NGR = Q / 16, HG = NGR / 2;
+    f4 bq[NGR], xq[NGR];
+    auto read = [&](int gr) {
+      const int k = 16 * gr + kq;
+      bq[gr] = f4{bs[k * BP + nl + i], bs[(k + 1) * BP + nl + i], bs[(k + 2) * BP + nl + i],
+                  bs[(k + 3) * BP + nl + i]};
+      xq[gr] = f4{xs[k * XP + p], xs[(k + 1) * XP + p], xs[(k + 2) * XP + p],
+                  xs[(k + 3) * XP + p]};
+    };
+    f4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gr = 0; gr < HG; ++gr) read(gr);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gr = HG; gr < NGR; ++gr) read(gr);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gr = 0; gr < HG; ++gr)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = mfma16x16x4(bq[gr][q], xq[gr][q], acc[q]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gr = HG; gr < NGR; ++gr)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = mfma16x16x4(bq[gr][q], xq[gr][q], acc[q]);
+    st4(dst + c * cstride, hs);
+    const float d = dec[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      hs[e] = d * hs[e] + ((acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]));
+    __syncthreads();  // chunk c's tiles are read before the next is staged
+  };
+  for (int64_t c = 0; c < nc; c += 2) {
+    step(c, xa, ba);
+    if (c + 1 < nc) step(c + 1, xb, bb);
+  }
+  if (final_states) st4(final_states + bh * PN + p * N + n, hs);
+}
+
+// Chosen when its workgroups fill the compute units in one round (at least
+// half of them): two rounds measured no faster than the two launches (batch 4
+// x 2048, 32 heads: 630 vs 635 us for four calls), a quarter of the machine
+// would leave the per-chunk work to few units.
+bool use_state_scan(bool bf16, bool varlen, int64_t b, int64_t L, int64_t H, int64_t N,
+                    int64_t Q) {
+  if (bf16 || varlen || !(N == 64 || N == 128) || !(Q == 64 || Q == 128) || L < 1) return false;
+  const int64_t nc = (L + Q - 1) / Q, nscan = b * H * (N / kScanSlice);
+  return nc <= kScanChunksMax && 2 * nscan >= kChainCUs && nscan <= kChainCUs;
+}
+
+template <int Q, int N>
+static void launch_scan_qn(const Problem& p, hipStream_t s) {
+  const int64_t nscan = p.b * p.H * (N / kScanSlice);
+  const int64_t jobs = p.ws_gram ? p.b * p.nc * p.G * (gram_tile_floats(Q) / 1024) : 0;
+  hipLaunchKernelGGL((state_scan_kernel<Q, N>), dim3((unsigned)nscan), dim3(512), 0, s,
+                     static_cast<const float*>(p.x), static_cast<const float*>(p.B),
+                     static_cast<const float*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.init,
+                     p.ws_dt, p.ws_cum, p.ws_states_in, p.final_states, p.L, p.H, p.G, p.nc,
+                     nscan, static_cast<const float*>(p.C), p.ws_gram, jobs);
+}
+
+hipError_t launch_state_scan(const Problem& p, hipStream_t stream) {
+  if (p.Q == 64) {
+    if (p.N == 64) launch_scan_qn<64, 64>(p, stream);
+    else launch_scan_qn<64, 128>(p, stream);
+  } else {
+    if (p.N == 64) launch_scan_qn<128, 64>(p, stream);
+    else launch_scan_qn<128, 128>(p, stream);
+  }
+  return hipGetLastError();
 }
 
 int64_t gram_planes(int64_t b, int64_t nc, int64_t H, int64_t N, int64_t G, int64_t Q) {

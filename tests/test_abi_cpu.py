@@ -399,7 +399,15 @@ def test_taken_path():
     assert tp(8, 4096, 64, 64, 128, 8, 256, 1) == "chain"           # pairs fill the machine
     assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "chain_segmented"  # 64 pairs x 4 segments
     assert tp(1, 1000, 8, 64, 128, 2, 256, 1) == "fused_head"       # too short to segment
-    assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # fp32
+    assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # fp32, one round
+    assert tp(4, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # fp32, two rounds
+    assert tp(2, 2048, 32, 64, 64, 4, 64, 0) == "staged_scan"       # half the units
+    assert tp(1, 2048, 32, 64, 64, 4, 64, 0) == "staged"            # a quarter
+    assert tp(2, 8192, 32, 64, 128, 1, 128, 0) == "staged"          # 64 chunks
+    assert tp(2, 4096, 32, 64, 128, 1, 128, 0) == "staged_scan"     # 32 chunks
+    assert tp(2, 2048, 32, 64, 32, 1, 128, 0) == "staged"           # dstate 32
+    assert tp(2, 2048, 32, 64, 128, 1, 256, 0) == "staged"          # chunk 256
+    assert tp(2, 2048, 32, 64, 128, 1, 128, 0, varlen=True) == "staged"
     assert tp(2, 16, 32, 64, 128, 1, 128, 1) == "step"              # seqlen <= 16
     assert tp(2, 400, 6, 64, 128, 2, 256, 1, kernel_path="chain") == "fused_head"  # odd group
     assert tp(2, 400, 8, 64, 16, 2, 256, 1, kernel_path="chain") == "staged"       # dstate 16

@@ -99,6 +99,41 @@ def test_stage_intermediates(dtype, Q, N):
     compare("states_in", got["states_in"], ref["states_in"], TOL[dtype])
 
 
+# Shapes whose first three stages run as one pass (fp32, batch x heads x
+# dstate/32 between half and all of the 256 compute units): dt and the
+# running sums (written by the slice-0 workgroups), the states entering each
+# chunk (no chunk states go through memory there), out and the final states.
+SCAN23 = [(128, 128, 2, 300, True), (64, 64, 4, 5 * 64 + 7, False), (128, 128, 1, 128, True),
+          (64, 128, 2, 32 * 64 - 5, True)]
+
+
+@pytest.mark.parametrize("Q,N,G,L,init", SCAN23,
+                         ids=[f"Q{q}-N{n}-G{g}-L{l}-{'init' if i else 'zero'}"
+                              for q, n, g, l, i in SCAN23])
+def test_state_scan_pass(Q, N, G, L, init):
+    b, H, P = 2, 32, 64
+    w = _case(880 + Q + N + L, b, L, H, P, N, G, Q, "f32", init=init)
+    log(f"test_state_scan_pass Q={Q} N={N} G={G} L={L} init={init}")
+    assert ssd.taken_path(b, L, H, P, N, G, Q, 0) == "staged_scan"
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    i0 = inp["initial_states"] if init else None
+    ws = poisoned_workspace(ssd.workspace_size(b, L, H, P, N, G, Q, 0), t["x"].device)
+    out, fin = run_gpu(t, Q, init=t["initial_states"] if init else None, workspace=ws)
+    got = {k: np64(v) for k, v in ws_regions(ws, b, L, H, P, N, Q).items()}
+    ref = oracle.chunk_intermediates(inp["x"], inp["dt"], inp["A"], inp["B"], Q,
+                                     dt_bias=inp["dt_bias"], initial_states=i0)
+    nc = -(-L // Q)
+    valid = np.zeros((b, H, nc, Q), bool)
+    valid.reshape(b, H, -1)[:, :, :L] = True
+    compare("dt", got["dt"], ref["dt"], 1e-5, mask=valid)
+    compare("dA_cumsum", got["cum"], ref["cum"], 1e-4, mask=valid)
+    compare("states_in", got["states_in"], ref["states_in"], TOL["f32"])
+    ro, rf = _oracle(inp, init=i0)
+    compare("out", np64(out), ro, TOL["f32"])
+    compare("final", np64(fin), rf, TOL["f32"])
+
+
 # --------------------------------------------------------------------------
 # edge cases
 # --------------------------------------------------------------------------

@@ -18,6 +18,8 @@
 // B C^T, once per (chunk, group), into the workspace.  They depend on the
 // inputs alone; here their matrix work runs beside a pass that is bound by
 // memory and leaves the matrix cores idle.
+#include <type_traits>
+
 #include "ssd_dt.h"
 #include "ssd_kernels.h"
 
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 // ---------------------------------------------------------------------------
 
 // For fp32 inputs with few chunks per sequence, one workgroup per (batch,
-// head, 32 state columns) walks the chunks in order: it forms each chunk's
+// head, SL = 32 or 64 state columns) walks the chunks in order: it forms each chunk's
 // contribution S_c on the matrix cores (as stage 2) and folds it into the
 // state it carries in registers (as above), so the chunk states never go
 // through memory and the two launches become one.  The walk is sequential in
@@ -155,8 +157,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 // parallelism is batch x heads x N/32 workgroups instead of also x chunks,
 // which is why the pass is chosen only when that fills the machine.
 //
-// Eight waves; wave w holds the 16 x 16 tile (state columns 16 (w % 2) of the
-// slice, rows 16 (w / 2)) of S^T = B^T diag(w) X on v_mfma_f32_16x16x4_f32:
+// Eight waves; wave w holds SL/32 16 x 16 tiles (state columns 16 (SL/32
+// (w % 2) + j) of the slice, rows 16 (w / 2); with two, they share the x
+// operand) of S^T = B^T diag(w) X on v_mfma_f32_16x16x4_f32:
 // lane (i, g = l/16) supplies B[t][n] and w_t x[t][p] for t = k0 + 4g + q at
 // step q of each group of 16 steps (its four rows of the chunk's LDS tiles),
 // and register r holds column n = 4g + r of row p = i, i.e. four consecutive
@@ -164,16 +167,17 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 // slice's B rows are staged in LDS (row pitches 68 and 36 floats: the four
 // lane quarters read rows four apart, which land in distinct banks); the rows
 // of the chunk after next are loaded into a second register set while the
-// current one computes, so each load has two chunks' time to arrive.
+// current one computes, so each load has two chunks' time to arrive.  64
+// columns are taken when 32 would need two rounds of workgroups: half the
+// workgroups, and fewer LDS and L1 bytes per product.
 // dt, the running sums and w_t of every chunk are formed first (a wave per
 // chunk, the slice-0 workgroup also writing them for the chunk scan) and kept
 // in LDS, and the staged x rows are scaled by w_t on the way in.  The chunk
 // scan's G^T tiles are formed by the same workgroups, a wave per tile, while
 // their first loads are in flight.
 constexpr int kScanChunksMax = 32;
-constexpr int kScanSlice = 32;  // state columns per workgroup
 
-template <int Q, int N>
+template <int Q, int N, int SL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void state_scan_kernel(
     const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ dt_raw,
     const float* __restrict__ A, const float* __restrict__ dt_bias, float dt_min, float dt_max,
@@ -181,18 +185,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     float* __restrict__ states_in, float* final_states, int64_t L, int64_t H, int64_t G,
     int64_t nc, int64_t nscan, const float* __restrict__ Cm, float* __restrict__ gram,
     int64_t gram_jobs) {
-  constexpr int P = 64, NT = 512, XP = 68, BP = 36, E = Q / kWave;
-  constexpr int QX = Q * P / (4 * NT), QB = Q * kScanSlice / (4 * NT);
-  static_assert(QX >= 1 && QB >= 1 && Q * P % (4 * NT) == 0 && Q * kScanSlice % (4 * NT) == 0,
-                "staging");
-  __shared__ __align__(16) float xs[Q * XP];                // x[t][p] of the chunk
+  constexpr int P = 64, NT = 512, XP = 68, BP = SL + 4, E = Q / kWave, NTW = SL / 32;
+  constexpr int QX = Q * P / (4 * NT), QB = Q * SL / (4 * NT);
+  static_assert(QX >= 1 && QB >= 1 && Q * P % (4 * NT) == 0 && Q * SL % (4 * NT) == 0 &&
+                (SL == 32 || SL == 64), "staging");
+  __shared__ __align__(16) float xs[Q * XP];                // w_t x[t][p] of the chunk
   __shared__ __align__(16) float bs[Q * BP];                // B[t][n] of the slice
   __shared__ __align__(16) float wl[kScanChunksMax * Q];    // w_t of every chunk
   __shared__ float dec[kScanChunksMax];                     // exp(cum_last) of every chunk
 
   // the slices of one head are b H workgroups apart: on one XCD (sharing the
   // x rows in its L2) when b H is a multiple of 8
-  const int64_t BH = nscan / (N / kScanSlice);
+  const int64_t BH = nscan / (N / SL);
   const int64_t bh = blockIdx.x % BH, sl = blockIdx.x / BH;
   const int64_t b = bh / H, h = bh % H;
   // 32-bit and wave-uniform: the B buffer resource needs a scalar base
@@ -200,8 +204,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i = lane % 16, kq = 4 * (lane / 16);
-  const int nl = 16 * (wave & 1), p0 = 16 * (wave >> 1);  // tile within the slice
-  const int n = kScanSlice * (int)sl + nl + kq, p = p0 + i;  // this lane's float4 of the state
+  const int nl = 16 * NTW * (wave & 1), p0 = 16 * (wave >> 1);  // first tile in the slice
+  const int n = SL * (int)sl + nl + kq, p = p0 + i;  // this lane's first float4 of the state
   constexpr int64_t PN = (int64_t)P * N;
 
   const uint32_t xrow = (uint32_t)(H * P * 4), brow = (uint32_t)(G * N * 4);
@@ -212,8 +216,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int64_t t0 = c * Q;
     const uint32_t last = (uint32_t)((L - 1 - t0) < (Q - 1) ? (L - 1 - t0) : (Q - 1));
     const auto xr = row_rsrc(x + ((b * L + t0) * H + h) * P, last * xrow + P * 4);
-    const auto br = row_rsrc(Bm + ((b * L + t0) * G + g) * N + kScanSlice * sl,
-                             last * brow + kScanSlice * 4);
+    const auto br = row_rsrc(Bm + ((b * L + t0) * G + g) * N + SL * sl, last * brow + SL * 4);
 #pragma unroll
     for (int q = 0; q < QX; ++q) {
       const int e = 4 * (q * NT + tid);
@@ -222,14 +225,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const int e = 4 * (q * NT + tid);
-      bv[q] = bld4(br, (uint32_t)(e / kScanSlice) * brow + (uint32_t)(e % kScanSlice) * 4);
+      bv[q] = bld4(br, (uint32_t)(e / SL) * brow + (uint32_t)(e % SL) * 4);
     }
   };
   // init and final_states may be the same buffer: each lane reads its four
   // elements of init before it writes the same four of final.  Loaded first:
   // the prologue's wait then covers it, and the loop never waits on it (a
   // load still in flight at the loop would make every chunk wait for all).
-  f4 hs = init ? ld4(init + bh * PN + p * N + n) : f4{0.f, 0.f, 0.f, 0.f};
+  f4 hs[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+    hs[j] = init ? ld4(init + bh * PN + p * N + n + 16 * j) : f4{0.f, 0.f, 0.f, 0.f};
   f4 xa[QX], ba[QB], xb[QX], bb[QB];  // register sets of even and odd chunks
   load(0, xa, ba);
   load(1, xb, bb);
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 
   __syncthreads();  // every w_t is in LDS before the first staging scales by it
-  float* dst = states_in + (b * nc * H + h) * PN + state_tile_offset(p, n, N);
+  float* const sbase = states_in + (b * nc * H + h) * PN;
   const int64_t cstride = H * PN;
   // chunk c: stage its rows from their register set (x scaled by w_t), load
   // chunk c + 2 into that set, then form S_c and fold it in
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       const int e = 4 * (q * NT + tid);
-      *reinterpret_cast<f4*>(bs + (e / kScanSlice) * BP + e % kScanSlice) = bv[q];
+      *reinterpret_cast<f4*>(bs + (e / SL) * BP + e % SL) = bv[q];
     }
     __syncthreads();  // chunk c staged
     load(c + 2, xv, bv);
@@ -291,17 +297,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     // whose reads run under the first half's products; four accumulators,
     // one per step of a group, so that consecutive MFMAs are independent
     constexpr int NGR = Q / 16, HG = NGR / 2;
-    f4 bq[NGR], xq[NGR];
+    f4 bq[NTW][NGR], xq[NGR];
     auto read = [&](int gr) {
       const int k = 16 * gr + kq;
-      bq[gr] = f4{bs[k * BP + nl + i], bs[(k + 1) * BP + nl + i], bs[(k + 2) * BP + nl + i],
-                  bs[(k + 3) * BP + nl + i]};
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int cn = nl + 16 * j + i;
+        bq[j][gr] = f4{bs[k * BP + cn], bs[(k + 1) * BP + cn], bs[(k + 2) * BP + cn],
+                       bs[(k + 3) * BP + cn]};
+      }
       xq[gr] = f4{xs[k * XP + p], xs[(k + 1) * XP + p], xs[(k + 2) * XP + p],
                   xs[(k + 3) * XP + p]};
     };
-    f4 acc[4];
+    f4 acc[NTW][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[j][q] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int gr = 0; gr < HG; ++gr) read(gr);
     __builtin_amdgcn_sched_barrier(0);
@@ -311,42 +323,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
     for (int gr = 0; gr < HG; ++gr)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = mfma16x16x4(bq[gr][q], xq[gr][q], acc[q]);
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[j][q] = mfma16x16x4(bq[j][gr][q], xq[gr][q], acc[j][q]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int gr = HG; gr < NGR; ++gr)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = mfma16x16x4(bq[gr][q], xq[gr][q], acc[q]);
-    st4(dst + c * cstride, hs);
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[j][q] = mfma16x16x4(bq[j][gr][q], xq[gr][q], acc[j][q]);
     const float d = dec[c];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      hs[e] = d * hs[e] + ((acc[0][e] + acc[1][e]) + (acc[2][e] + acc[3][e]));
+    for (int j = 0; j < NTW; ++j) {
+      st4(sbase + c * cstride + state_tile_offset(p, n + 16 * j, N), hs[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hs[j][e] = d * hs[j][e] + ((acc[j][0][e] + acc[j][1][e]) + (acc[j][2][e] + acc[j][3][e]));
+    }
     __syncthreads();  // chunk c's tiles are read before the next is staged
   };
   for (int64_t c = 0; c < nc; c += 2) {
     step(c, xa, ba);
     if (c + 1 < nc) step(c + 1, xb, bb);
   }
-  if (final_states) st4(final_states + bh * PN + p * N + n, hs);
+  if (final_states) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) st4(final_states + bh * PN + p * N + n + 16 * j, hs[j]);
+  }
 }
 
 // Chosen when its workgroups fill the compute units in one round (at least
-// half of them): two rounds measured no faster than the two launches (batch 4
-// x 2048, 32 heads: 630 vs 635 us for four calls), a quarter of the machine
-// would leave the per-chunk work to few units.
-bool use_state_scan(bool bf16, bool varlen, int64_t b, int64_t L, int64_t H, int64_t N,
-                    int64_t Q) {
-  if (bf16 || varlen || !(N == 64 || N == 128) || !(Q == 64 || Q == 128) || L < 1) return false;
-  const int64_t nc = (L + Q - 1) / Q, nscan = b * H * (N / kScanSlice);
-  return nc <= kScanChunksMax && 2 * nscan >= kChainCUs && nscan <= kChainCUs;
+// half of them), with 32-column slices, or else with 64: two rounds of
+// 32-column workgroups measured no faster than the two launches (batch 4 x
+// 2048, 32 heads: 630 vs 635 us for four calls), and a quarter of the
+// machine would leave the per-chunk work to few units.  Returns the slice
+// width, 0 when the pass is not taken.
+int state_scan_slice(bool bf16, bool varlen, int64_t b, int64_t L, int64_t H, int64_t N,
+                     int64_t Q) {
+  if (bf16 || varlen || !(N == 64 || N == 128) || !(Q == 64 || Q == 128) || L < 1) return 0;
+  if ((L + Q - 1) / Q > kScanChunksMax) return 0;
+  for (int sl : {32, 64}) {
+    const int64_t nscan = b * H * (N / sl);
+    if (2 * nscan >= kChainCUs && nscan <= kChainCUs) return sl;
+  }
+  return 0;
 }
 
-template <int Q, int N>
+bool use_state_scan(bool bf16, bool varlen, int64_t b, int64_t L, int64_t H, int64_t N,
+                    int64_t Q) {
+  return state_scan_slice(bf16, varlen, b, L, H, N, Q) != 0;
+}
+
+template <int Q, int N, int SL>
 static void launch_scan_qn(const Problem& p, hipStream_t s) {
-  const int64_t nscan = p.b * p.H * (N / kScanSlice);
+  const int64_t nscan = p.b * p.H * (N / SL);
   const int64_t jobs = p.ws_gram ? p.b * p.nc * p.G * (gram_tile_floats(Q) / 1024) : 0;
-  hipLaunchKernelGGL((state_scan_kernel<Q, N>), dim3((unsigned)nscan), dim3(512), 0, s,
+  hipLaunchKernelGGL((state_scan_kernel<Q, N, SL>), dim3((unsigned)nscan), dim3(512), 0, s,
                      static_cast<const float*>(p.x), static_cast<const float*>(p.B),
                      static_cast<const float*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.init,
                      p.ws_dt, p.ws_cum, p.ws_states_in, p.final_states, p.L, p.H, p.G, p.nc,
@@ -354,12 +389,20 @@ static void launch_scan_qn(const Problem& p, hipStream_t s) {
 }
 
 hipError_t launch_state_scan(const Problem& p, hipStream_t stream) {
+  const bool wide = state_scan_slice(p.bf16, p.seq_idx != nullptr, p.b, p.L, p.H, p.N, p.Q) == 64;
+  auto go = [&](auto q, auto n) {
+    constexpr int Q = decltype(q)::value, N = decltype(n)::value;
+    if (wide) launch_scan_qn<Q, N, 64>(p, stream);
+    else launch_scan_qn<Q, N, 32>(p, stream);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
   if (p.Q == 64) {
-    if (p.N == 64) launch_scan_qn<64, 64>(p, stream);
-    else launch_scan_qn<64, 128>(p, stream);
+    if (p.N == 64) go(I64{}, I64{});
+    else go(I64{}, I128{});
   } else {
-    if (p.N == 64) launch_scan_qn<128, 64>(p, stream);
-    else launch_scan_qn<128, 128>(p, stream);
+    if (p.N == 64) go(I128{}, I64{});
+    else go(I128{}, I128{});
   }
   return hipGetLastError();
 }

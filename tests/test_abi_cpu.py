@@ -400,7 +400,8 @@ def test_taken_path():
     assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "chain_segmented"  # 64 pairs x 4 segments
     assert tp(1, 1000, 8, 64, 128, 2, 256, 1) == "fused_head"       # too short to segment
     assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # fp32, one round
-    assert tp(4, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # fp32, two rounds
+    assert tp(4, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # 64-column slices
+    assert tp(8, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # two rounds even so
     assert tp(2, 2048, 32, 64, 64, 4, 64, 0) == "staged_scan"       # half the units
     assert tp(1, 2048, 32, 64, 64, 4, 64, 0) == "staged"            # a quarter
     assert tp(2, 8192, 32, 64, 128, 1, 128, 0) == "staged"          # 64 chunks

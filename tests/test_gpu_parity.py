@@ -103,17 +103,20 @@ def test_stage_intermediates(dtype, Q, N):
 # dstate/32 between half and all of the 256 compute units): dt and the
 # running sums (written by the slice-0 workgroups), the states entering each
 # chunk (no chunk states go through memory there), out and the final states.
-SCAN23 = [(128, 128, 2, 300, True), (64, 64, 4, 5 * 64 + 7, False), (128, 128, 1, 128, True),
-          (64, 128, 2, 32 * 64 - 5, True)]
+# (the last two: enough heads that 32-column slices would need two rounds,
+# so the pass takes 64-column ones)
+SCAN23 = [(128, 128, 2, 300, True, 32), (64, 64, 4, 5 * 64 + 7, False, 32),
+          (128, 128, 1, 128, True, 32), (64, 128, 2, 32 * 64 - 5, True, 32),
+          (128, 128, 4, 300, True, 64), (64, 64, 8, 3 * 64 + 1, False, 128)]
 
 
-@pytest.mark.parametrize("Q,N,G,L,init", SCAN23,
-                         ids=[f"Q{q}-N{n}-G{g}-L{l}-{'init' if i else 'zero'}"
-                              for q, n, g, l, i in SCAN23])
-def test_state_scan_pass(Q, N, G, L, init):
-    b, H, P = 2, 32, 64
+@pytest.mark.parametrize("Q,N,G,L,init,H", SCAN23,
+                         ids=[f"Q{q}-N{n}-G{g}-L{l}-{'init' if i else 'zero'}-H{h}"
+                              for q, n, g, l, i, h in SCAN23])
+def test_state_scan_pass(Q, N, G, L, init, H):
+    b, P = 2, 64
     w = _case(880 + Q + N + L, b, L, H, P, N, G, Q, "f32", init=init)
-    log(f"test_state_scan_pass Q={Q} N={N} G={G} L={L} init={init}")
+    log(f"test_state_scan_pass Q={Q} N={N} G={G} L={L} init={init} H={H}")
     assert ssd.taken_path(b, L, H, P, N, G, Q, 0) == "staged_scan"
     inp = make_inputs(w)
     t = upload(inp, "f32")

@@ -282,6 +282,31 @@ def test_inplace_continuation():
     compare("final in place", np64(state), np64(ffin), TOL["f32"])
 
 
+@pytest.mark.parametrize("H", [32, 64], ids=["slices32", "slices64"])
+def test_inplace_continuation_state_scan(H):
+    """The same on shapes whose stages 1-3 run as one pass (32- and 64-column
+    state slices): each lane reads its init elements before it writes the
+    same final ones."""
+    w = _case(510 + H, 2, 2 * 300, H, 64, 128, 4, 128, "f32", init=True)
+    assert ssd.taken_path(2, 300, H, 64, 128, 4, 128, 0) == "staged_scan"
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    full, ffin = run_gpu(t, 128, init=t["initial_states"])
+    state = t["initial_states"].clone()
+    outs = []
+    for lo, hi in ((0, 300), (300, 600)):
+        seg = {k: (v[:, lo:hi].contiguous() if k in ("x", "z", "B", "C", "dt") else v)
+               for k, v in t.items()}
+        out, fin = run_gpu(seg, 128, init=state, final_states=state)
+        assert fin.data_ptr() == state.data_ptr()
+        outs.append(out)
+    compare("segments vs full", np64(torch.cat(outs, dim=1)), np64(full), TOL["f32"])
+    compare("final in place", np64(state), np64(ffin), TOL["f32"])
+    ref, rfin = _oracle(inp, init=inp["initial_states"])
+    compare("out vs oracle", np64(torch.cat(outs, dim=1)), ref, TOL["f32"])
+    compare("final vs oracle", np64(state), rfin, TOL["f32"])
+
+
 # --------------------------------------------------------------------------
 # the full-size workloads
 # --------------------------------------------------------------------------

@@ -258,8 +258,8 @@ size_t ssd_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads
 #define SSD_PATH_STEP 6 /* reported by ssd_scan_fwd_taken_path only (seqlen <= 16) */
 #define SSD_PATH_CHAIN_SEGMENTED 7
 /* reported by ssd_scan_fwd_taken_path only: the staged path with its first
- * three stages as one pass (fp32, no seq_idx, dstate 64 or 128, chunk 64 or
- * 128, at most 32 chunks per sequence, batch x nheads x dstate/32, or else
+ * three stages as one pass (fp32, dstate 64 or 128, chunk 64 or 128, at
+ * most 32 chunks per sequence row, batch x nheads x dstate/32, or else
  * x dstate/64, between half and all of the 256 compute units) */
 #define SSD_PATH_STAGED_SCAN 8
 

@@ -174,7 +174,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 // chunk, the slice-0 workgroup also writing them for the chunk scan) and kept
 // in LDS, and the staged x rows are scaled by w_t on the way in.  The chunk
 // scan's G^T tiles are formed by the same workgroups, a wave per tile, while
-// their first loads are in flight.
+// their first loads are in flight.  Packed sequences as in stages 2 and 3:
+// w_t = 0 for the steps of a chunk's earlier sequences, and a chunk in which
+// a sequence starts drops the carried state (its decay taken as 0).
 constexpr int kScanChunksMax = 32;
 
 template <int Q, int N, int SL>
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const float* init, float* __restrict__ ws_dt, float* __restrict__ ws_cum,
     float* __restrict__ states_in, float* final_states, int64_t L, int64_t H, int64_t G,
     int64_t nc, int64_t nscan, const float* __restrict__ Cm, float* __restrict__ gram,
-    int64_t gram_jobs) {
+    int64_t gram_jobs, const int32_t* __restrict__ seg) {
   constexpr int P = 64, NT = 512, XP = 68, BP = SL + 4, E = Q / kWave, NTW = SL / 32;
   constexpr int QX = Q * P / (4 * NT), QB = Q * SL / (4 * NT);
   static_assert(QX >= 1 && QB >= 1 && Q * P % (4 * NT) == 0 && Q * SL % (4 * NT) == 0 &&
@@ -264,9 +266,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         float dtv[E], cum[E], cl;
         wave_dt_scan<Q>(raw[j], a, bias, dt_min, dt_max, b, c, h, L, H, nc,
                         sl == 0 ? ws_dt : nullptr, ws_cum, dtv, cum, &cl);
+        const int32_t* sc = seg ? seg + (b * nc + c) * Q : nullptr;
+        const int32_t slast = sc ? sc[Q - 1] : 0;
 #pragma unroll
-        for (int k = 0; k < E; ++k) wl[c * Q + lane * E + k] = __expf(cl - cum[k]) * dtv[k];
-        if (lane == 0) dec[c] = __expf(cl);
+        for (int k = 0; k < E; ++k) {
+          const bool keep = !sc || sc[lane * E + k] == slast;
+          wl[c * Q + lane * E + k] = keep ? __expf(cl - cum[k]) * dtv[k] : 0.0f;
+        }
+        if (lane == 0) dec[c] = slast == 0 ? __expf(cl) : 0.0f;
       }
     }
   }
@@ -363,7 +370,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // width, 0 when the pass is not taken.
 int state_scan_slice(bool bf16, bool varlen, int64_t b, int64_t L, int64_t H, int64_t N,
                      int64_t Q) {
-  if (bf16 || varlen || !(N == 64 || N == 128) || !(Q == 64 || Q == 128) || L < 1) return 0;
+  (void)varlen;  // packed sequences are handled as in stages 2 and 3
+  if (bf16 || !(N == 64 || N == 128) || !(Q == 64 || Q == 128) || L < 1) return 0;
   if ((L + Q - 1) / Q > kScanChunksMax) return 0;
   for (int sl : {32, 64}) {
     const int64_t nscan = b * H * (N / sl);
@@ -385,7 +393,7 @@ static void launch_scan_qn(const Problem& p, hipStream_t s) {
                      static_cast<const float*>(p.x), static_cast<const float*>(p.B),
                      static_cast<const float*>(p.dt), p.A, p.dt_bias, p.dt_min, p.dt_max, p.init,
                      p.ws_dt, p.ws_cum, p.ws_states_in, p.final_states, p.L, p.H, p.G, p.nc,
-                     nscan, static_cast<const float*>(p.C), p.ws_gram, jobs);
+                     nscan, static_cast<const float*>(p.C), p.ws_gram, jobs, p.ws_seg);
 }
 
 hipError_t launch_state_scan(const Problem& p, hipStream_t stream) {

@@ -408,7 +408,7 @@ def test_taken_path():
     assert tp(2, 4096, 32, 64, 128, 1, 128, 0) == "staged_scan"     # 32 chunks
     assert tp(2, 2048, 32, 64, 32, 1, 128, 0) == "staged"           # dstate 32
     assert tp(2, 2048, 32, 64, 128, 1, 256, 0) == "staged"          # chunk 256
-    assert tp(2, 2048, 32, 64, 128, 1, 128, 0, varlen=True) == "staged"
+    assert tp(2, 2048, 32, 64, 128, 1, 128, 0, varlen=True) == "staged_scan"  # packed too
     assert tp(2, 16, 32, 64, 128, 1, 128, 1) == "step"              # seqlen <= 16
     assert tp(2, 400, 6, 64, 128, 2, 256, 1, kernel_path="chain") == "fused_head"  # odd group
     assert tp(2, 400, 8, 64, 16, 2, 256, 1, kernel_path="chain") == "staged"       # dstate 16

@@ -179,6 +179,34 @@ def test_varlen_step_kernel(dtype, L):
     compare("final", np64(fin), rfin, TOL[dtype])
 
 
+# shapes whose stages 1-3 run as one pass (32- and 64-column state slices):
+# (Q, N, H, G)
+SCAN23 = [(128, 128, 32, 2), (64, 64, 32, 4), (128, 128, 64, 4)]
+
+
+@pytest.mark.parametrize("Q,N,H,G", SCAN23, ids=[f"Q{q}-N{n}-H{h}-G{g}" for q, n, h, g in SCAN23])
+def test_varlen_state_scan_pass(Q, N, H, G):
+    """Packed sequences on the one-pass stages 1-3 (the mask of a chunk's
+    earlier sequences, the dropped carry where one starts): mean lengths 4,
+    Q/2 and 3Q, sequences starting on and next to chunk edges, and every
+    step its own sequence."""
+    b, L = 2, 2 * Q + Q // 2 + 7
+    assert ssd.taken_path(b, L, H, 64, N, G, Q, 0, varlen=True) == "staged_scan"
+    w = Workload(f"var23{Q}{N}{H}", b, L, H, 64, N, G, Q, "f32", 3700 + Q + N + H, init=True)
+    inp = make_inputs(w)
+    t = upload(inp, "f32")
+    seqs = [(f"mean {m}", make_seq_idx(b, L, {"Q/2": Q / 2, "3Q": 3 * Q}.get(m, m), 50 + i))
+            for i, m in enumerate(MEANS)]
+    seqs.append(("chunk edges", _from_lengths(b, L, [Q, Q - 1, 2, Q + 1])))
+    seqs.append(("every step", np.tile(np.arange(L, dtype=np.int32), (b, 1))))
+    for desc, seq in seqs:
+        log(f"test_varlen_state_scan_pass Q={Q} N={N} H={H} G={G} {desc}")
+        out, fin = run_gpu(t, Q, init=t["initial_states"], seq_idx=_seq(seq))
+        ref, rfin = _oracle(inp, seq, inp["initial_states"])
+        compare(f"out {desc}", np64(out), ref, TOL["f32"])
+        compare(f"final {desc}", np64(fin), rfin, TOL["f32"])
+
+
 def test_varlen_every_step_new():
     """Every step its own sequence: only each token's own term remains."""
     Q, b, L = 128, 2, 260

@@ -137,6 +137,23 @@ def test_state_scan_pass(Q, N, G, L, init, H):
     compare("final", np64(fin), rf, TOL["f32"])
 
 
+def test_state_scan_pass_limits_and_groups():
+    """The one-pass stages with dt_limit clamping softplus(dt + dt_bias) on
+    both sides, and with two heads per group (the general chunk scan after
+    it, no C·Bᵀ tiles in the workspace), D and the gate off."""
+    b, H, P, N, Q, L = 2, 32, 64, 128, 128, 3 * 128 - 9
+    for G, lim, gate in ((2, (0.01, 0.05), True), (16, (0.0, math.inf), False)):
+        w = _case(900 + G, b, L, H, P, N, G, Q, "f32", init=True, gate=gate, skip=gate)
+        assert ssd.taken_path(b, L, H, P, N, G, Q, 0) == "staged_scan"
+        log(f"test_state_scan_pass_limits_and_groups G={G} dt_limit={lim} gate={gate}")
+        inp = make_inputs(w)
+        t = upload(inp, "f32")
+        out, fin = run_gpu(t, Q, dt_limit=lim, init=t["initial_states"])
+        ref, rfin = _oracle(inp, dt_limit=lim, init=inp["initial_states"])
+        compare(f"out G={G}", np64(out), ref, TOL["f32"])
+        compare(f"final G={G}", np64(fin), rfin, TOL["f32"])
+
+
 # --------------------------------------------------------------------------
 # edge cases
 # --------------------------------------------------------------------------

@@ -708,8 +708,12 @@ __global__ __launch_bounds__(kHeadSumThreads) void bwd_head_sum_kernel(
 int64_t bwd_blocks(int64_t L) { return (L + kBT - 1) / kBT; }
 
 // Heads of one group the block kernel handles per workgroup: 4, else 2, else 1.
-static int bwd_heads_per_workgroup(int64_t H, int64_t G) {
+// Heads of one group per block workgroup: 8 when that still fills the
+// compute units (one round of batch x blocks x H/8 workgroups), else 4, 2 or
+// 1, as the heads per group divide.
+static int bwd_heads_per_workgroup(int64_t H, int64_t G, int64_t bnb) {
   const int64_t hpg = H / G;
+  if (hpg % 8 == 0 && bnb * (H / 8) >= kChainCUs) return 8;
   return hpg % 4 == 0 ? 4 : hpg % 2 == 0 ? 2 : 1;
 }
 
@@ -728,7 +732,7 @@ static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
   const Problem& p = q.fwd;
   const int64_t units = p.b * p.nc * p.H;
   launch_state_scan<N>(q, s, p.nc);
-  const int hpw = bwd_heads_per_workgroup(p.H, p.G);
+  const int hpw = bwd_heads_per_workgroup(p.H, p.G, p.b * p.nc);
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)(units / hpw)), dim3(kBwdThreads), 0, s,
                        static_cast<const float*>(p.x), static_cast<const float*>(p.B),
@@ -736,7 +740,9 @@ static void launch_bwd_n(const BwdProblem& q, hipStream_t s) {
                        p.dt_min, p.dt_max, p.A, p.D, p.ws_dt, p.ws_cum, p.ws_states_in, q.gst,
                        q.dy, q.dx, q.dBh, q.dCh, q.ddt, q.dA_p, q.dD_p, p.L, p.H, p.G, p.nc);
   };
-  if (hpw == 4)
+  if (hpw == 8)
+    launch(block_bwd_kernel<N, 8>);
+  else if (hpw == 4)
     launch(block_bwd_kernel<N, 4>);
   else if (hpw == 2)
     launch(block_bwd_kernel<N, 2>);
@@ -761,7 +767,8 @@ hipError_t launch_bwd(const BwdProblem& q, hipStream_t s) {
     }
     const int64_t nbc = p.b * p.L * p.G * p.N;
     hipLaunchKernelGGL(bwd_group_sum_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0,
-                       s, q.dBh, q.dCh, q.dB, q.dC, nbc, p.H / bwd_heads_per_workgroup(p.H, p.G),
+                       s, q.dBh, q.dCh, q.dB, q.dC, nbc,
+                       p.H / bwd_heads_per_workgroup(p.H, p.G, p.b * p.nc),
                        p.G, p.N);
   } else if (q.dinit) {  // no steps: the initial state's gradient is dfinal (or 0)
     switch (p.N) {

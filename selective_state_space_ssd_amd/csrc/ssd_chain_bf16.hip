@@ -448,22 +448,35 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       for (int kn = 0; kn < KN; ++kn) cop[kn] = ld_bf16x8(Cl + t * CP + 32 * kn + 8 * g);
       const float ct2 = cum2_l[t];
       const int kt = VARLEN ? k_l[t] : 0;
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
       const int cl = i >> 1;  // the chunk of 32 s holding the diagonal tile
-      // G^T tiles of chunk cc: s-tile 2 cc, and 2 cc + 1 when `two`
+      // G^T tiles of chunk cc: s-tile 2 cc, and 2 cc + 1 when `two`.  Both
+      // tiles' B rows are read first (rows of the staged block either way),
+      // so the reads are in flight together; a branch on `two` around each
+      // product would make every read wait alone before its product.
       auto gtiles = [&](const int cc, const bool two, f4& g0, f4& g1) {
         const int s0r = 32 * cc + m, s1r = s0r + 16;
+        s16x8 b0[KN], b1[KN];
+#pragma unroll
+        for (int kn = 0; kn < KN; ++kn) b0[kn] = ld_bf16x8(Bl + s0r * BP + 32 * kn + 8 * g);
+#pragma unroll
+        for (int kn = 0; kn < KN; ++kn) b1[kn] = ld_bf16x8(Bl + s1r * BP + 32 * kn + 8 * g);
         g0 = zero4();
         g1 = zero4();
+        if (two) {
 #pragma unroll
-        for (int kn = 0; kn < KN; ++kn) {
-          g0 = mfma16(ld_bf16x8(Bl + s0r * BP + 32 * kn + 8 * g), cop[kn], g0);
-          if (two) g1 = mfma16(ld_bf16x8(Bl + s1r * BP + 32 * kn + 8 * g), cop[kn], g1);
+          for (int kn = 0; kn < KN; ++kn) {
+            g0 = mfma16(b0[kn], cop[kn], g0);
+            g1 = mfma16(b1[kn], cop[kn], g1);
+          }
+        } else {
+#pragma unroll
+          for (int kn = 0; kn < KN; ++kn) g0 = mfma16(b0[kn], cop[kn], g0);
         }
       };
-      // the masked values of chunk cc times x into acc
-      auto product = [&](const int cc, const float (&mv)[8]) {
+      // the masked values of chunk cc times x into acc (the first product of
+      // the tile starts from zero: a constant operand of the MFMA instead of
+      // zeroed registers)
+      auto product = [&](const int cc, const float (&mv)[8], auto first) {
         const int sa = 32 * cc + 4 * g, sb = sa + 16;
         s16x8 mhi, mlo;
         split_bf16x8(mv, mhi, mlo);
@@ -472,7 +485,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         for (int pt = 0; pt < 4; ++pt)
           xo[pt] = cat8(tr_rows(Xl, kXP, sa, 16 * pt, m), tr_rows(Xl, kXP, sb, 16 * pt, m));
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(xo[pt], mhi, acc[pt]);
+        for (int pt = 0; pt < 4; ++pt)
+          acc[pt] = mfma16(xo[pt], mhi, decltype(first)::value ? zero4() : acc[pt]);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(xo[pt], mlo, acc[pt]);
       };
@@ -482,7 +496,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       f4 g0, g1;
       constexpr bool kOdd = decltype(odd)::value;
       gtiles(0, cl > 0 || kOdd, g0, g1);
-      for (int cc = 0; cc < cl; ++cc) {
+      auto below = [&](const int cc, auto first) {
         f4 n0, n1;
         gtiles(cc + 1, cc + 1 < cl || kOdd, n0, n1);
         const int sa = 32 * cc + 4 * g, sb = sa + 16;
@@ -494,17 +508,13 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
           mv[r] = g0[r] * v0[r];
           mv[4 + r] = g1[r] * v1[r];
         }
-        product(cc, mv);
+        product(cc, mv, first);
         g0 = n0;
         g1 = n1;
-      }
+      };
       // the diagonal chunk: the tiles so far carried exp(cum_r - cum_s), so
       // add exp(cum_t - cum_r)
       const float e = ett_l[t];
-      if (cl > 0) {
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] *= e;
-      }
       // the diagonal s-tile itself: the direct decay, [k_s = k_t] below the
       // diagonal, D on it, zero above -- selects on flags computed without
       // branches (a short-circuit form became a branch per element)
@@ -522,22 +532,34 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
           o[r] = keep ? (on ? v + Dh : v) : 0.0f;
         }
       };
-      const int sa = 32 * cl + 4 * g, sb = sa + 16;
-      float mv[8];
-      if constexpr (kOdd) {
-        // s-tile i - 1 lies wholly below t's tile: the tabulated factor
-        // exp(cum_r - cum_s) dt_s [k_s = k_r] times exp(cum_t - cum_r), as
-        // in the chunks before; then the diagonal tile
-        const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
+      auto last = [&](auto first) {
+        const int sa = 32 * cl + 4 * g, sb = sa + 16;
+        float mv[8];
+        if constexpr (kOdd) {
+          // s-tile i - 1 lies wholly below t's tile: the tabulated factor
+          // exp(cum_r - cum_s) dt_s [k_s = k_r] times exp(cum_t - cum_r), as
+          // in the chunks before; then the diagonal tile
+          const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mv[r] = g0[r] * v0[r] * e;
-        diagonal(g1, sb, mv + 4);
+          for (int r = 0; r < 4; ++r) mv[r] = g0[r] * v0[r] * e;
+          diagonal(g1, sb, mv + 4);
+        } else {
+          diagonal(g0, sa, mv);
+#pragma unroll
+          for (int r = 4; r < 8; ++r) mv[r] = 0.0f;
+        }
+        product(cl, mv, first);
+      };
+      // the first chunk's product starts the accumulators (peeled)
+      if (cl > 0) {
+        below(0, std::true_type{});
+        for (int cc = 1; cc < cl; ++cc) below(cc, std::false_type{});
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] *= e;
+        last(std::false_type{});
       } else {
-        diagonal(g0, sa, mv);
-#pragma unroll
-        for (int r = 4; r < 8; ++r) mv[r] = 0.0f;
+        last(std::true_type{});
       }
-      product(cl, mv);
     };
     f4 ya0[4], ya1[4];
     const int ie = (wt & 1) ? CT - 1 - wt : wt, io = CT - 1 - ie;  // even and odd tile

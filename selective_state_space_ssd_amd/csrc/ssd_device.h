@@ -164,6 +164,11 @@ __device__ __forceinline__ s16x8 to_bf16x8(const float (&v)[8]) {
   return __builtin_bit_cast(s16x8, w);
 }
 
+// bf16_lo by one v_perm_b32: bytes 1, 0 of w into bytes 3, 2, zeros below.
+__device__ __forceinline__ float bf16_lo_perm(uint32_t w) {
+  return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu));
+}
+
 // Split eight fp32 into two bf16 operands, hi = bf16(v) and lo = bf16(v - hi)
 // (v - hi is exact in fp32).  hi + lo carries 16 significant bits, so the
 // pair of products A.hi + A.lo of an exact bf16 operand A is accurate to about
@@ -174,10 +179,13 @@ __device__ __forceinline__ void split_bf16x8(const float (&v)[8], s16x8& hi, s16
   h.y = pack_bf16x2(v[2], v[3]);
   h.z = pack_bf16x2(v[4], v[5]);
   h.w = pack_bf16x2(v[6], v[7]);
-  l.x = pack_bf16x2(v[0] - bf16_lo(h.x), v[1] - bf16_hi(h.x));
-  l.y = pack_bf16x2(v[2] - bf16_lo(h.y), v[3] - bf16_hi(h.y));
-  l.z = pack_bf16x2(v[4] - bf16_lo(h.z), v[5] - bf16_hi(h.z));
-  l.w = pack_bf16x2(v[6] - bf16_lo(h.w), v[7] - bf16_hi(h.w));
+  // The low half's value is moved up with a byte permute rather than a
+  // shift: through a shift the compiler forms it with a conversion of its own
+  // and then shifts it, one instruction more per pair.
+  l.x = pack_bf16x2(v[0] - bf16_lo_perm(h.x), v[1] - bf16_hi(h.x));
+  l.y = pack_bf16x2(v[2] - bf16_lo_perm(h.y), v[3] - bf16_hi(h.y));
+  l.z = pack_bf16x2(v[4] - bf16_lo_perm(h.z), v[5] - bf16_hi(h.z));
+  l.w = pack_bf16x2(v[6] - bf16_lo_perm(h.w), v[7] - bf16_hi(h.w));
   hi = __builtin_bit_cast(s16x8, h);
   lo = __builtin_bit_cast(s16x8, l);
 }

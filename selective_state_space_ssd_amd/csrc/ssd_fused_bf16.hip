@@ -696,14 +696,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
       const float xv8[8] = {bf16_lo(xw.x) * w0[0], bf16_hi(xw.x) * w0[1], bf16_lo(xw.y) * w0[2],
                             bf16_hi(xw.y) * w0[3], bf16_lo(xw.z) * w1[0], bf16_hi(xw.z) * w1[1],
                             bf16_lo(xw.w) * w1[2], bf16_hi(xw.w) * w1[3]};
+      // every n-tile's B operand read before the products (read next to its
+      // product, each read waits alone); the hi products of all tiles, then
+      // the lo ones, so that consecutive MFMAs are independent
+      s16x8 bop[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bop[j] = b_tr_operand<N>(b_lds, r0, r0 + 4, 32 * j);
       s16x8 xhi, xlo;
       split_bf16x8(xv8, xhi, xlo);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const s16x8 bop = b_tr_operand<N>(b_lds, r0, r0 + 4, 32 * j);
-        sacc[j] = mfma32x32x16(bop, xhi, sacc[j]);
-        sacc[j] = mfma32x32x16(bop, xlo, sacc[j]);
-      }
+      for (int j = 0; j < NJ; ++j) sacc[j] = mfma32x32x16(bop[j], xhi, sacc[j]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sacc[j] = mfma32x32x16(bop[j], xlo, sacc[j]);
     }
     __syncthreads();  // tiles and w read before the next block is staged
   }

@@ -298,16 +298,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       run += d * Ah;
       cum[k] = run;
     }
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float v = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += v;
-    }
+    const float incl = wave_incl_sum(run);
     const float base = incl - run;
     cum[0] += base;
     cum[1] += base;
-    const float cum_last = __shfl(incl, kWave - 1, kWave);
+    const float cum_last = wave_read(incl, kWave - 1);
     int ks[2] = {0, 0};
     if (seq) {
       int cnt = 0;
@@ -317,16 +312,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         if (t >= 1 && t < L) cnt += seq[b * L + t] != seq[b * L + t - 1];
         ks[k] = cnt;
       }
-      int ic = cnt;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int v = __shfl_up(ic, off, kWave);
-        if (lane >= off) ic += v;
-      }
+      const int ic = wave_incl_sum(cnt);
       ks[0] += ic - cnt;
       ks[1] += ic - cnt;
     }
-    const int klast = __shfl(ks[1], kWave - 1, kWave);
+    const int klast = wave_read(ks[1], kWave - 1);
     // reference step r = 16 i - 1 of this lane's tile i = lane / 8 (tile 0 has none)
     const int ti = lane >> 3;
     const int rsrc = ti > 0 ? 8 * ti - 1 : 0;
@@ -351,8 +341,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     for (int i = 1; i < CT; ++i) {
       const int owner = i <= 2 ? 0 : i <= 4 ? 1 : i == 5 ? 2 : 3;
       if (owner != wt) continue;
-      const float ci = __shfl(cum[1], 8 * i - 1, kWave);
-      const int ki = __shfl(ks[1], 8 * i - 1, kWave);
+      const float ci = wave_read(cum[1], 8 * i - 1);
+      const int ki = wave_read(ks[1], 8 * i - 1);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int sv = 2 * lane + k;
@@ -449,11 +439,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       const float ct2 = cum2_l[t];
       const int kt = VARLEN ? k_l[t] : 0;
       const int cl = i >> 1;  // the chunk of 32 s holding the diagonal tile
-      // G^T tiles of chunk cc: s-tile 2 cc, and 2 cc + 1 when `two`.  Both
-      // tiles' B rows are read first (rows of the staged block either way),
-      // so the reads are in flight together; a branch on `two` around each
-      // product would make every read wait alone before its product.
-      auto gtiles = [&](const int cc, const bool two, f4& g0, f4& g1) {
+      // G^T tiles of chunk cc: s-tiles 2 cc and 2 cc + 1 (rows of the staged
+      // block; the second is not used when the first holds the diagonal of
+      // an even t-tile).  Both tiles' B rows are read first, so the reads are
+      // in flight together: formed only when used, the second tile's reads
+      // moved behind the branch and each waited alone before its product.
+      auto gtiles = [&](const int cc, f4& g0, f4& g1) {
         const int s0r = 32 * cc + m, s1r = s0r + 16;
         s16x8 b0[KN], b1[KN];
 #pragma unroll
@@ -462,15 +453,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
         for (int kn = 0; kn < KN; ++kn) b1[kn] = ld_bf16x8(Bl + s1r * BP + 32 * kn + 8 * g);
         g0 = zero4();
         g1 = zero4();
-        if (two) {
 #pragma unroll
-          for (int kn = 0; kn < KN; ++kn) {
-            g0 = mfma16(b0[kn], cop[kn], g0);
-            g1 = mfma16(b1[kn], cop[kn], g1);
-          }
-        } else {
-#pragma unroll
-          for (int kn = 0; kn < KN; ++kn) g0 = mfma16(b0[kn], cop[kn], g0);
+        for (int kn = 0; kn < KN; ++kn) {
+          g0 = mfma16(b0[kn], cop[kn], g0);
+          g1 = mfma16(b1[kn], cop[kn], g1);
         }
       };
       // the masked values of chunk cc times x into acc (the first product of
@@ -495,10 +481,10 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
       // chunk's products run on the matrix cores under this chunk's masking
       f4 g0, g1;
       constexpr bool kOdd = decltype(odd)::value;
-      gtiles(0, cl > 0 || kOdd, g0, g1);
+      gtiles(0, g0, g1);
       auto below = [&](const int cc, auto first) {
         f4 n0, n1;
-        gtiles(cc + 1, cc + 1 < cl || kOdd, n0, n1);
+        gtiles(cc + 1, n0, n1);
         const int sa = 32 * cc + 4 * g, sb = sa + 16;
         const f4 v0 = *reinterpret_cast<const f4*>(v_l + i * CQ + sa);
         const f4 v1 = *reinterpret_cast<const f4*>(v_l + i * CQ + sb);

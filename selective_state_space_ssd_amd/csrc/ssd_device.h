@@ -258,6 +258,40 @@ __device__ __forceinline__ void tile_of(int tau, int* si, int* ti) {
 // 2^x on v_exp_f32 (results below the normal range flush to zero) and 1/x on
 // v_rcp_f32 (1 ulp): the decays and gates here are all in (0, 1] or feed a
 // bf16/fp32 output far coarser than these errors.
+// ---- wave-wide scans on the DPP lane moves ---------------------------------
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes within each row of 16, then each row's total broadcast into the rows
+// after it (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+// Lanes without a source add 0.  Six register-to-register moves where a
+// shuffle-up scan takes six LDS permutes, each waited for.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ float wave_incl_sum(float v) {
+  auto mv = [](float x, int y) { return x + __int_as_float(y); };
+  v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+  v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+  v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+  v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+  v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+// The value of lane `src` (wave-uniform) in every lane: one scalar read.
+__device__ __forceinline__ float wave_read(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ int wave_read(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 // silu(v) = v * sigmoid(v) = v / (1 + e^-v)

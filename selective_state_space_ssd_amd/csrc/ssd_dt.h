@@ -81,14 +81,9 @@ __device__ __forceinline__ void wave_dt_scan(const float (&raw)[Q / 64], float a
     total += d * a;
     run[i] = total;
   }
-  float incl = total;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float v = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += v;
-  }
+  const float incl = wave_incl_sum(total);
   const float base = incl - total;
-  *cum_last = __shfl(incl, kWave - 1, kWave);
+  *cum_last = wave_read(incl, kWave - 1);
   const int64_t o = ((b * H + h) * nc + c) * Q + (int64_t)lane * E;
 #pragma unroll
   for (int i = 0; i < E; ++i) {

@@ -48,12 +48,7 @@ __global__ __launch_bounds__(256) void seq_count_kernel(const int32_t* __restric
     if (t >= 1 && t < L) total += seq[b * L + t] != seq[b * L + t - 1];
     run[i] = total;
   }
-  int incl = total;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int v = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += v;
-  }
+  const int incl = wave_incl_sum(total);
   const int base = incl - total;
   int32_t* dst = ws_seg + u * Q + lane * E;
 #pragma unroll

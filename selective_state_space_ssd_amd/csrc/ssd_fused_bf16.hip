@@ -237,17 +237,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void f
         if (tt >= 1 && tt < L) run += seq[b * L + tt] != seq[b * L + tt - 1];
         ks[k] = run;
       }
-      int incl = run;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int v = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += v;
-      }
+      const int incl = wave_incl_sum(run);
 #pragma unroll
       for (int k = 0; k < E; ++k) ks[k] += incl - run;
     }
     const int kend = __shfl(ks[1], 16 * (lane / 16) + 15, kWave);
-    const int klast = __shfl(ks[1], kWave - 1, kWave);
+    const int klast = wave_read(ks[1], kWave - 1);
 #pragma unroll
     for (int k = 0; k < E; ++k) {
       const int t = lane * E + k;
@@ -655,16 +650,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
           if (tt >= 1 && tt < L) run += seq[b * L + tt] != seq[b * L + tt - 1];
           ks[k] = run;
         }
-        int incl = run;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int v = __shfl_up(incl, off, kWave);
-          if (lane >= off) incl += v;
-        }
+        const int incl = wave_incl_sum(run);
 #pragma unroll
         for (int k = 0; k < E; ++k) ks[k] += incl - run;
       }
-      const int klast = __shfl(ks[E - 1], kWave - 1, kWave);
+      const int klast = wave_read(ks[E - 1], kWave - 1);
 #pragma unroll
       for (int k = 0; k < E; ++k)
         w_lds[hd][lane * E + k] = ks[k] == klast ? __expf(cum_last - cum[k]) * dtv[k] * P : 0.0f;

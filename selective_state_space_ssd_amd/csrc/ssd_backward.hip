@@ -399,17 +399,10 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
 
   // Sums over a row of a wave's 16 x 64 strip (16 lanes x 4 tiles) or a column
   // (4 lane groups x 4 registers x 4 waves) are taken in a fixed order: lane
-  // shuffles within the wave, then the per-wave parts in wave order, so the
-  // gradients are identical from run to run.
-  auto sum16 = [](float v) {  // over the 16 lanes of a row group
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-  };
-  auto sum4g = [](float v) {  // over the four 16-lane groups
-    v += __shfl_xor(v, 16, kWave);
-    return v + __shfl_xor(v, 32, kWave);
-  };
+  // moves within the wave (DPP and row swaps, no LDS), then the per-wave parts
+  // in wave order, so the gradients are identical from run to run.
+  auto sum16 = [](float v) { return row_sum16(v); };  // over the 16 lanes of a row group
+  auto sum4g = [](float v) { return rows_sum4(v); };  // over the four 16-lane groups
 
   // ---- products with G: GB[s][p] = B_s . G_p (dX), XG[s][n] = x_s^T G (dB) --
   // rows s in [16 strip, 16 strip + 16)
@@ -451,7 +444,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * strip + 4 * kk + r;
-      const float m = s <= t ? expf(cum_l[t] - cum_l[s]) : 0.0f;
+      const float m = s <= t ? __expf(cum_l[t] - cum_l[s]) : 0.0f;
       const float v0 = m * kacc[r] * racc[r];
       const float v = v0 * dt_l[s];
       vm[s * kXP + t] = m * kacc[r] * dt_l[s];
@@ -564,11 +557,8 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
   }
 
   // ---- <G, H_in> and dY . x across the workgroup ------------------------------
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    gh += __shfl_xor(gh, off, kWave);
-    dd += __shfl_xor(dd, off, kWave);
-  }
+  gh = wave_sum(gh);
+  dd = wave_sum(dd);
   if (lane == 0) {
     red[wave] = gh;
     red[NW + wave] = dd;
@@ -586,9 +576,7 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
       yo += yod[q][t];
     }
     const float us = wdt[t] * xg;
-    float usum = us;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) usum += __shfl_xor(usum, off, kWave);
+    const float usum = wave_sum(us);
     float ghs = 0.0f, dds = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -598,25 +586,18 @@ __global__ __launch_bounds__(kBwdThreads) void block_bwd_kernel(
     const float colv = colw[0][t] + colw[1][t] + colw[2][t] + colw[3][t];
     const float col0 = col0w[0][t] + col0w[1][t] + col0w[2][t] + col0w[3][t];
     float dc = rv + yo - colv - us;
-    if (t == T - 1) dc += usum + expf(cl) * ghs;
-    // suffix sum over t
-    float rc = dc;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float o = __shfl_down(rc, off, kWave);
-      if (t + off < kWave) rc += o;
-    }
+    if (t == T - 1) dc += usum + __expf(cl) * ghs;
+    // suffix sum over t: the prefix sum of the lanes in reverse order
+    const float rc = wave_reverse(wave_incl_sum(wave_reverse(dc)));
     const float Ah = A[h];
-    const float ddt = col0 + expf(cl - cum_l[t]) * xg + Ah * rc;
-    float da = dt_l[t] * rc;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) da += __shfl_xor(da, off, kWave);
+    const float ddt = col0 + __expf(cl - cum_l[t]) * xg + Ah * rc;
+    const float da = wave_sum(dt_l[t] * rc);
     if (t <= last) {
       const int64_t o = (b * L + t0 + t) * H + h;
       const float uu = dt_raw[o] + (dt_bias ? dt_bias[h] : 0.0f);
       const float sp = softplus(uu);
       const bool pass = sp >= dt_min && sp <= dt_max;
-      ddt_raw[o] = pass ? ddt / (1.0f + expf(-uu)) : 0.0f;
+      ddt_raw[o] = pass ? ddt * fast_rcp(1.0f + __expf(-uu)) : 0.0f;
     }
     if (t == 0) {
       dA_p[u] = da;
@@ -680,12 +661,9 @@ __global__ __launch_bounds__(kHeadSumThreads) void bwd_head_sum_kernel(
     sd += dD_p[k * H + h];
   }
   for (int64_t k = tid; k < b * L; k += kHeadSumThreads) sbias += ddt_raw[k * H + h];
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    sa += __shfl_xor(sa, off, kWave);
-    sd += __shfl_xor(sd, off, kWave);
-    sbias += __shfl_xor(sbias, off, kWave);
-  }
+  sa = wave_sum(sa);
+  sd = wave_sum(sd);
+  sbias = wave_sum(sbias);
   if (lane == 0) {
     red[0][wave] = sa;
     red[1][wave] = sd;
@@ -707,7 +685,6 @@ __global__ __launch_bounds__(kHeadSumThreads) void bwd_head_sum_kernel(
 
 int64_t bwd_blocks(int64_t L) { return (L + kBT - 1) / kBT; }
 
-// Heads of one group the block kernel handles per workgroup: 4, else 2, else 1.
 // Heads of one group per block workgroup: 8 when that still fills the
 // compute units (one round of batch x blocks x H/8 workgroups), else 4, 2 or
 // 1, as the heads per group divide.

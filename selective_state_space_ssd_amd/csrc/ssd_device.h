@@ -284,6 +284,40 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
   v = mv(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
   return v;
 }
+// Sum over the 16 lanes of each row of a wave, every lane of the row left
+// with it: the pairings of xor shuffles by 1, 2, 4 and 8 (quad_perm [1,0,3,2]
+// and [2,3,0,1], then the half-row and row mirrors) on DPP lane moves.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));
+  return v;
+}
+// Sum over the four rows at each lane position (the pairings of xor shuffles
+// by 16 and 32) on the row swaps of gfx950: v_permlane16_swap exchanges the
+// odd rows of its first operand with the even rows of its second,
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; with both operands v, the two results hold each lane's partner.
+__device__ __forceinline__ float rows_sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+// Sum over the wave, in every lane.
+__device__ __forceinline__ float wave_sum(float v) { return rows_sum4(row_sum16(v)); }
+// Lane l takes the value of lane 63 - l: the row mirror, then the rows in
+// reverse order through the two row swaps.
+__device__ __forceinline__ float wave_reverse(float v) {
+  const int lane = threadIdx.x % kWave;
+  v = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(lane < 32 ? a[1] : a[0]);  // halves exchanged
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 16) ? c[0] : c[1]);  // rows of each half exchanged
+}
+
 // The value of lane `src` (wave-uniform) in every lane: one scalar read.
 __device__ __forceinline__ float wave_read(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));

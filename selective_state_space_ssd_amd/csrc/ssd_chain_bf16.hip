@@ -360,18 +360,27 @@ __global__ __launch_bounds__(kChainThreads) void chain_scan_bf16_kernel(
     const float dl = dlv < 0.0f ? 0.0f : dlv;
 #pragma unroll
     for (int j = 0; j < NT; ++j) Hs[j] *= dl;
+    // x rows and w of step group kt + 1 are read while group kt is multiplied
+    s16x4 xa, xb;
+    f4 w0, w1;
+    auto read_xw = [&](int kt) {
+      const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;
+      xa = tr_rows(Xl, kXP, r0, 16 * wt, m);
+      xb = tr_rows(Xl, kXP, r1, 16 * wt, m);
+      w0 = *reinterpret_cast<const f4*>(w_l + r0);
+      w1 = *reinterpret_cast<const f4*>(w_l + r1);
+    };
+    read_xw(0);
 #pragma unroll
     for (int kt = 0; kt < CQ / 32; ++kt) {
       const int r0 = 32 * kt + 4 * g, r1 = r0 + 16;
-      const s16x4 xa = tr_rows(Xl, kXP, r0, 16 * wt, m), xb = tr_rows(Xl, kXP, r1, 16 * wt, m);
-      const f4 w0 = *reinterpret_cast<const f4*>(w_l + r0);
-      const f4 w1 = *reinterpret_cast<const f4*>(w_l + r1);
       const float xw[8] = {to_f32((bf16_t)xa[0]) * w0[0], to_f32((bf16_t)xa[1]) * w0[1],
                            to_f32((bf16_t)xa[2]) * w0[2], to_f32((bf16_t)xa[3]) * w0[3],
                            to_f32((bf16_t)xb[0]) * w1[0], to_f32((bf16_t)xb[1]) * w1[1],
                            to_f32((bf16_t)xb[2]) * w1[2], to_f32((bf16_t)xb[3]) * w1[3]};
       s16x8 whi, wlo;
       split_bf16x8(xw, whi, wlo);
+      if (kt + 1 < CQ / 32) read_xw(kt + 1);
 #pragma unroll
       for (int j0 = 0; j0 < NT; j0 += 4) {  // four n-tiles at a time, as in C.H
         s16x8 bops[4];

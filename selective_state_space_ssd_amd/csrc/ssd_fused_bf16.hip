@@ -676,13 +676,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
     }
     __syncthreads();
     if (c > c0) load(c - 1);  // the next tiles in flight under this block's products
+    // x rows and w of step group ks + 1 are read while group ks is multiplied
+    uint4 xw;
+    f4 w0, w1;
+    auto read_xw = [&](int ks) {
+      const int r0 = 16 * ks + 8 * kk;
+      xw = __builtin_bit_cast(uint4, x_tr_operand(x_lds[hd], r0, r0 + 4, 32 * pt));
+      w0 = *reinterpret_cast<const f4*>(w_lds[hd] + r0);
+      w1 = *reinterpret_cast<const f4*>(w_lds[hd] + r0 + 4);
+    };
+    read_xw(0);
 #pragma unroll 2
     for (int ks = 0; ks < FQ / 16; ++ks) {
       const int r0 = 16 * ks + 8 * kk;
       // w o x at t = r0 + 0..7, p = 32 pt + i, split hi/lo
-      const uint4 xw = __builtin_bit_cast(uint4, x_tr_operand(x_lds[hd], r0, r0 + 4, 32 * pt));
-      const f4 w0 = *reinterpret_cast<const f4*>(w_lds[hd] + r0);
-      const f4 w1 = *reinterpret_cast<const f4*>(w_lds[hd] + r0 + 4);
       const float xv8[8] = {bf16_lo(xw.x) * w0[0], bf16_hi(xw.x) * w0[1], bf16_lo(xw.y) * w0[2],
                             bf16_hi(xw.y) * w0[3], bf16_lo(xw.z) * w1[0], bf16_hi(xw.z) * w1[1],
                             bf16_lo(xw.w) * w1[2], bf16_hi(xw.w) * w1[3]};
@@ -694,6 +701,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void u
       for (int j = 0; j < NJ; ++j) bop[j] = b_tr_operand<N>(b_lds, r0, r0 + 4, 32 * j);
       s16x8 xhi, xlo;
       split_bf16x8(xv8, xhi, xlo);
+      if (ks + 1 < FQ / 16) read_xw(ks + 1);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) sacc[j] = mfma32x32x16(bop[j], xhi, sacc[j]);
 #pragma unroll

@@ -754,15 +754,21 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   if (batch == 0) return SSD_OK;
 
   char* ws = static_cast<char*>(workspace);
-  // bf16: every step below runs on fp32 copies; the gradients of the bf16
+  // With a gate and the four-heads chunk scan, the re-run's chunk scan forms
+  // dY and dz from y in its epilogue (no y round trip, no gate kernel); it
+  // reads z and dout, and writes dz, in their own dtype.
+  const bool fuse_gate = nonempty && z && ssd::use_group_scan(nheads, dstate, ngroups, 64, false);
+  // bf16: every other step runs on fp32 copies; the gradients of the bf16
   // tensors land in fp32 buffers and are rounded into the caller's at the end
+  // (z, dout and dz stay bf16 when the chunk scan's epilogue is their only
+  // user)
   const void* in[6] = {x, dt, B, C, z, dout};
   void* grad[5] = {dx, ddt, dB, dC, dz};
   if (bl.bf16 && nonempty) {
     const int64_t nin[6] = {nx, ndt, nbc, nbc, nx, nx};
     ssd::ConvList wl;
     for (int k = 0; k < 6; ++k) {
-      if (!in[k]) continue;
+      if (!in[k] || (fuse_gate && k >= 4)) continue;
       float* w = reinterpret_cast<float*>(ws + bl.off_w[k]);
       wl.src[wl.count] = in[k];
       wl.dst[wl.count] = w;
@@ -771,7 +777,7 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
     }
     if (ssd::launch_widen_bf16(wl, stream) != hipSuccess) return SSD_ERR_HIP;
     for (int k = 0; k < 5; ++k)
-      if (grad[k]) grad[k] = ws + bl.off_w[kWideDx + k];
+      if (grad[k] && !(fuse_gate && k == 4)) grad[k] = ws + bl.off_w[kWideDx + k];
   }
   x = in[0]; dt = in[1]; B = in[2]; C = in[3]; z = in[4]; dout = in[5];
   ssd::Problem p;
@@ -791,7 +797,6 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
   p.ws_gram = nullptr;  // the chunk scan forms its tiles of B C^T itself
   p.fs_ring = nullptr; p.fs_flags = nullptr; p.fs_ctl = nullptr;
   p.fused_kind = 0;
-  const bool fuse_gate = nonempty && z && ssd::use_group_scan(nheads, dstate, ngroups, 64, false);
   if (nonempty) {
     // the forward again (64-step blocks, no gate): dt, cum, states, and the
     // ungated y, which only dz needs (no gate: no y)
@@ -807,13 +812,15 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
     // from y directly (no y round trip, no gate kernel)
     if (fuse_gate) {
       p.z = z;
-      p.gate_dout = static_cast<const float*>(dout);
-      p.gate_dz = static_cast<float*>(grad[4]);
+      p.gate_dout = dout;
+      p.gate_dz = grad[4];
+      p.gate_bf16 = bl.bf16;
     }
     if (z && ssd::launch_chunk_scan(p, stream) != hipSuccess) return SSD_ERR_HIP;
     p.z = nullptr;
     p.gate_dout = nullptr;
     p.gate_dz = nullptr;
+    p.gate_bf16 = false;
   }
   ssd::BwdProblem q;
   q.fwd = p;
@@ -842,7 +849,7 @@ int ssd_scan_bwd(const void* x, const void* dt, const float* A, const void* B, c
     const int64_t nout[5] = {nx, ndt, nbc, nbc, nx};
     ssd::ConvList nl;
     for (int k = 0; k < 5; ++k) {
-      if (!outs_bf16[k]) continue;
+      if (!outs_bf16[k] || (fuse_gate && k == 4)) continue;  // dz: written as bf16
       nl.src[nl.count] = grad[k];
       nl.dst[nl.count] = outs_bf16[k];
       nl.n[nl.count++] = nout[k];

@@ -228,16 +228,20 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
 // per lane, two full 256-byte rows per instruction.
 // ---------------------------------------------------------------------------
 
-template <typename T, int Q, int N, bool GATE, bool PRE, bool GB = false>
+// ZT: the type of z (and, in the gate gradient epilogue, of dout and dz).
+template <typename T, int Q, int N, bool GATE, bool PRE, bool GB = false, typename ZT = T>
 __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
-    const float* __restrict__ Dv, const T* __restrict__ z, const float* __restrict__ ws_dt,
+    const float* __restrict__ Dv, const ZT* __restrict__ z, const float* __restrict__ ws_dt,
     const float* __restrict__ ws_cum, const float* __restrict__ states_in,
     const float* __restrict__ gram, T* __restrict__ out,
     const int32_t* __restrict__ seg, int64_t L, int64_t H, int64_t G, int64_t nc, int64_t nunits,
-    const T* __restrict__ gd, T* __restrict__ gdz) {
+    const ZT* __restrict__ gd, ZT* __restrict__ gdz) {
   constexpr int P = 64, NT = Q / 32, CS = N + 4, NG = NT * (NT + 1) / 2, KQ = N / 8;
   static_assert(!(GB && GATE), "the gate gradient epilogue takes the ungated y");
+  // byte offsets of the ZT tensors: those of the T tensors over kZS
+  constexpr uint32_t kZS = sizeof(T) / sizeof(ZT);
+  static_assert(kZS == 1 || (kZS == 2 && sizeof(T) == 4), "z type");
   constexpr int NW = 8;                   // waves: two per head
   constexpr int GW = (NG + NW - 1) / NW;  // G tiles per wave, at most
   constexpr int NS = NT / 2;              // t-tiles per wave
@@ -327,11 +331,17 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   const uint32_t rowb = (uint32_t)(xs * sizeof(T));  // bytes from one step to the next
   const uint32_t nbytes = (uint32_t)((last * xs + P) * sizeof(T));
   const auto xr = row_rsrc(x + hoff, nbytes);
-  const auto zr = row_rsrc(GATE || GB ? z + hoff : x + hoff, nbytes);  // read only when GATE or GB
+  const auto zr = row_rsrc(GATE || GB ? static_cast<const void*>(z + hoff)
+                                      : static_cast<const void*>(x + hoff),
+                           nbytes / kZS);  // read only when GATE or GB
   const auto orr = row_rsrc(out + hoff, nbytes);
   // gate gradient epilogue: dout in, dz out (same rows)
-  const auto dr = row_rsrc(GB ? gd + hoff : x + hoff, nbytes);
-  const auto dzr = row_rsrc(GB ? gdz + hoff : out + hoff, nbytes);
+  const auto dr = row_rsrc(GB ? static_cast<const void*>(gd + hoff)
+                              : static_cast<const void*>(x + hoff),
+                           nbytes / kZS);
+  const auto dzr = row_rsrc(GB ? static_cast<const void*>(gdz + hoff)
+                               : static_cast<const void*>(out + hoff),
+                            nbytes / kZS);
   const uint32_t lane_b = (uint32_t)((4 * kk * xs + 2 * i) * sizeof(T));  // row 4 kk, column 2 i
   const float* hs = states_in + ((b * nc + c) * H + h) * (int64_t)(P * N) + 4 * lane;
   f4 hv[HR][2];
@@ -353,13 +363,14 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
   f2 zv[16];
   auto load_z = [&](int ti) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) zv[m] = bld2(zr, lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb, T{});
+    for (int m = 0; m < 16; ++m)
+      zv[m] = bld2(zr, (lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb) / kZS, ZT{});
   };
   f2 dv[GB ? 16 : 1];  // dout rows of that t-tile (gate gradient epilogue)
   auto load_d = [&](int ti) {
 #pragma unroll
     for (int m = 0; m < (GB ? 16 : 1); ++m)
-      dv[m] = bld2(dr, lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb, T{});
+      dv[m] = bld2(dr, (lane_b + (32 * ti + 8 * (m / 4) + m % 4) * rowb) / kZS, ZT{});
   };
   __builtin_amdgcn_sched_barrier(0);  // every set-up load is issued above
 
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(512) void chunk_scan_group_kernel(
             dzv[e] = d * y[e] * sg * (1.0f + zz * (1.0f - sg));
           }
           bst2(orr, off, dyv, T{});
-          bst2(dzr, off, dzv, T{});
+          bst2(dzr, off / kZS, dzv, ZT{});
         } else {
           if constexpr (GATE) {
             y[0] *= silu(zv[r][0]);
@@ -611,15 +622,14 @@ int64_t gram_tile_floats(int64_t Q) {
   return nt * (nt + 1) / 2 * 1024;
 }
 
-template <typename T, int Q, int N, bool GATE, bool PRE, bool GB = false>
+template <typename T, int Q, int N, bool GATE, bool PRE, bool GB = false, typename ZT = T>
 static void launch_group(const Problem& p, hipStream_t s, int64_t nunits) {
-  hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, GATE, PRE, GB>), dim3((unsigned)nunits),
+  hipLaunchKernelGGL((chunk_scan_group_kernel<T, Q, N, GATE, PRE, GB, ZT>), dim3((unsigned)nunits),
                      dim3(512), 0, s, static_cast<const T*>(p.x), static_cast<const T*>(p.B),
-                     static_cast<const T*>(p.C), p.D, static_cast<const T*>(p.z), p.ws_dt,
+                     static_cast<const T*>(p.C), p.D, static_cast<const ZT*>(p.z), p.ws_dt,
                      p.ws_cum, p.ws_states_in, p.ws_gram, static_cast<T*>(p.out), p.ws_seg, p.L,
                      p.H, p.G, p.nc, nunits,
-                     static_cast<const T*>(static_cast<const void*>(p.gate_dout)),
-                     static_cast<T*>(static_cast<void*>(p.gate_dz)));
+                     static_cast<const ZT*>(p.gate_dout), static_cast<ZT*>(p.gate_dz));
 }
 
 template <typename T, int Q, int N>
@@ -629,7 +639,8 @@ static void launch_qn(const Problem& p, hipStream_t s) {
       const int64_t nunits = p.b * p.nc * (p.H / 4);
       if constexpr (std::is_same<T, float>::value && Q == 64) {
         if (p.gate_dout) {  // the backward's re-run: the gate gradient epilogue
-          launch_group<T, Q, N, false, false, true>(p, s, nunits);
+          if (p.gate_bf16) launch_group<T, Q, N, false, false, true, bf16_t>(p, s, nunits);
+          else launch_group<T, Q, N, false, false, true>(p, s, nunits);
           return;
         }
       }

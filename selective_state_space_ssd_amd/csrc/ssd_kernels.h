@@ -53,9 +53,12 @@ struct Problem {
   float* cs_decay = nullptr;   // [b, H, nunits] unit decay products
   // Backward re-run only (fp32, four-heads chunk scan): with gate_dout set the
   // chunk scan's epilogue writes dY = dout silu(z) to out and dz = dout y
-  // silu'(z) to gate_dz in place of y (z is then the gate input).
-  const float* gate_dout = nullptr;
-  float* gate_dz = nullptr;
+  // silu'(z) to gate_dz in place of y (z is then the gate input).  z, dout
+  // and dz are bf16 when gate_bf16 is set (fp32 otherwise), whatever the
+  // other inputs are.
+  const void* gate_dout = nullptr;
+  void* gate_dz = nullptr;
+  bool gate_bf16 = false;
 };
 
 // Each launcher enqueues one stage on `stream` and returns hipGetLastError().

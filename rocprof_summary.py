@@ -7,6 +7,9 @@
   python rocprof_summary.py --counters DIR       per kernel: instructions per wave (VALU,
                                            MFMA, LDS), matrix-core and VALU busy shares
                                            (from one SQ counter pass; see counters())
+  python rocprof_summary.py --stalls DIR         per kernel: shares of the waves' cycles
+                                           issuing, waiting on dependencies and waiting
+                                           for their turn (see stalls())
   python rocprof_summary.py --traffic FETCH_DIR WRITE_DIR KERNEL COPY_MIB SRC...
       HBM bytes per dispatch of the kernel whose name contains KERNEL, from a
       FETCH_SIZE run and a WRITE_SIZE run of the same command, each scaled by
@@ -92,6 +95,27 @@ def counters(path):
     return out
 
 
+def stalls(path):
+    """Per kernel, from a pass with SQ_WAVES, SQ_WAVE_CYCLES, SQ_WAIT_ANY,
+    SQ_WAIT_INST_ANY and SQ_ACTIVE_INST_ANY: the shares of the waves' cycles
+    spent issuing instructions (ACTIVE_INST_ANY), waiting on their
+    dependencies -- an s_waitcnt for loads or LDS reads, or a barrier --
+    (WAIT_ANY), and ready but waiting for their turn to issue
+    (WAIT_INST_ANY), each over SQ_WAVE_CYCLES."""
+    out = {}
+    for k, c in pmc_means(path).items():
+        if "SQ_WAVE_CYCLES" not in c or not c["SQ_WAVE_CYCLES"][0]:
+            continue
+        wc = c["SQ_WAVE_CYCLES"][0]
+        row = {"dispatches": c["SQ_WAVE_CYCLES"][1], "waves": c.get("SQ_WAVES", (0, 0))[0]}
+        for name, key in (("SQ_ACTIVE_INST_ANY", "issue"), ("SQ_WAIT_ANY", "wait_dep"),
+                          ("SQ_WAIT_INST_ANY", "wait_turn")):
+            if name in c:
+                row[key] = c[name][0] / wc
+        out[short(k)] = row
+    return out
+
+
 def sources_hash(paths):
     import hashlib
     h = hashlib.sha256()
@@ -152,6 +176,13 @@ if __name__ == "__main__":
                 if name in r:
                     parts.append(f"{name.split('_')[0]}/wave={r[name]:9.1f}")
             for name in ("mfma_busy", "valu_busy"):
+                if name in r:
+                    parts.append(f"{name}={100 * r[name]:5.1f}%")
+            print("  ".join(parts))
+    elif sys.argv[1] == "--stalls":
+        for k, r in sorted(stalls(sys.argv[2]).items(), key=lambda kv: -kv[1]["waves"]):
+            parts = [f"{k[:58]:58s} n={r['dispatches']:<4d} waves={r['waves']:<7.0f}"]
+            for name in ("issue", "wait_dep", "wait_turn"):
                 if name in r:
                     parts.append(f"{name}={100 * r[name]:5.1f}%")
             print("  ".join(parts))

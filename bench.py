@@ -652,13 +652,23 @@ def bwd_workload(dev, warmup, name="f32_b2_L2048_H32_P64_N128_G1_Q128", dtype="f
 # --------------------------------------------------------------------------
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers (a virtualised host may give only the vendor's name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
+            if not line.strip() and fields:
+                break
     except OSError:
         pass
-    return "unknown"
+    if not fields:
+        return "unknown"
+    extra = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return fields.get("model name", "unknown") + (f" ({extra})" if extra else "")
 
 
 def cpu_baseline(w, inp, min_seconds=10.0, heads_per_pass=16):

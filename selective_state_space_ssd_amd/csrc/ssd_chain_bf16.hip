@@ -688,16 +688,17 @@ ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force) {
   pl.nseg = 1;
   pl.span = nblk;
   if (npairs <= 0 || nblk < 2) return pl;
-  // segments: as many as fill one round of the compute units; by default only
-  // when each segment keeps at least 16 blocks and the workgroups fill the
-  // round at least 3/4 (below that, the fused path)
+  // segments: as many as fill one round of the compute units (at most one
+  // per block); by default from 8 blocks on and when the workgroups fill at
+  // least half the round (below that, the fused path).  Segments of one or
+  // two blocks measured faster than the fused per-head kernel from 8 blocks
+  // on, slower at 4.
   int64_t nseg = kChainCUs / npairs;
   if (force) {
     nseg = nseg < 2 ? 2 : nseg;
   } else {
-    const int64_t by_len = nblk / 16;
-    nseg = nseg < by_len ? nseg : by_len;
-    if (nseg < 2 || 4 * npairs * nseg < 3 * kChainCUs) return pl;
+    nseg = nseg < nblk ? nseg : nblk;
+    if (nblk < 8 || nseg < 2 || 2 * npairs * nseg < kChainCUs) return pl;
   }
   nseg = nseg < nblk ? nseg : nblk;
   const int64_t span = (nblk + nseg - 1) / nseg;

@@ -147,8 +147,9 @@ def test_workspace_size_fused_bf16():
 def _chain_plan(b, L, H, force):
     """(segments, blocks per segment, blocks per unit, units per head) of the
     chain bf16 path: one segment unless the pairs alone do not fill the 256
-    compute units; then as many segments as fill one round, by default only
-    with at least 16 blocks each and the round at least 3/4 full."""
+    compute units; then as many segments as fill one round (at most one per
+    block), by default from 8 blocks on and with the round at least half
+    full."""
     npairs, nblk = b * H // 2, -(-L // 128)
     if npairs <= 0 or nblk < 2:
         return 1, nblk, 0, 0
@@ -156,8 +157,8 @@ def _chain_plan(b, L, H, force):
     if force:
         nseg = max(nseg, 2)
     else:
-        nseg = min(nseg, nblk // 16)
-        if nseg < 2 or 4 * npairs * nseg < 3 * 256:
+        nseg = min(nseg, nblk)
+        if nblk < 8 or nseg < 2 or 2 * npairs * nseg < 256:
             return 1, nblk, 0, 0
     nseg = min(nseg, nblk)
     span = -(-nblk // nseg)
@@ -179,7 +180,11 @@ def test_chain_plan():
     assert _chain_plan(1, 65536, 128, False) == (4, 128, 16, 24)   # the long sequence
     assert _chain_plan(8, 4096, 64, False)[0] == 1                 # 256 pairs: no segments
     assert _chain_plan(1, 1000, 8, True) == (8, 1, 1, 7)
-    assert _chain_plan(1, 1000, 8, False)[0] == 1
+    assert _chain_plan(1, 1000, 8, False)[0] == 1                  # a quarter of the CUs
+    assert _chain_plan(2, 2048, 32, False) == (8, 2, 2, 7)         # 32 pairs, 16 blocks
+    assert _chain_plan(2, 1024, 32, False) == (8, 1, 1, 7)         # one block per segment
+    assert _chain_plan(2, 512, 32, False)[0] == 1                  # 4 blocks: fused
+    assert _chain_plan(1, 2048, 16, False) == (16, 1, 1, 15)       # half the CUs
 
 
 def test_workspace_size_default_bf16():
@@ -398,7 +403,9 @@ def test_taken_path():
     tp = ssd.taken_path
     assert tp(8, 4096, 64, 64, 128, 8, 256, 1) == "chain"           # pairs fill the machine
     assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "chain_segmented"  # 64 pairs x 4 segments
-    assert tp(1, 1000, 8, 64, 128, 2, 256, 1) == "fused_head"       # too short to segment
+    assert tp(1, 1000, 8, 64, 128, 2, 256, 1) == "fused_head"       # too few pairs to segment
+    assert tp(2, 2048, 32, 64, 128, 1, 256, 1) == "chain_segmented"  # 32 pairs x 8 segments
+    assert tp(2, 512, 32, 64, 128, 1, 256, 1) == "fused_head"       # 4 blocks
     assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # fp32, one round
     assert tp(4, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # 64-column slices
     assert tp(8, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # two rounds even so

@@ -125,9 +125,9 @@ extern "C" {
  * the machine: one kernel in which each workgroup carries a pair of heads of one
  * group through the whole sequence in 128-step blocks with the state held on
  * chip (no workspace: ssd_scan_fwd_workspace_size returns 0).  When the pairs
- * alone do not fill it, the sequence has at least 8 blocks and pairs times
- * segments (at most one per block) fill at least half a round of the compute
- * units, the chain runs over segments
+ * alone do not fill it but pairs times segments (at most one per block) fill
+ * a round of the compute units at least 3/4, or half of it when the sequence
+ * has at least 8 blocks, the chain runs over segments
  * (SSD_PATH_CHAIN_SEGMENTED below); the workspace then holds the units' end
  * states [batch, nheads, units] (headdim x dstate floats, row-major) and
  * their decays [batch, nheads, units].  Otherwise they

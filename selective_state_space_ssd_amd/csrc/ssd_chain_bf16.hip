@@ -689,16 +689,18 @@ ChainPlan chain_plan(int64_t b, int64_t L, int64_t H, bool force) {
   pl.span = nblk;
   if (npairs <= 0 || nblk < 2) return pl;
   // segments: as many as fill one round of the compute units (at most one
-  // per block); by default from 8 blocks on and when the workgroups fill at
-  // least half the round (below that, the fused path).  Segments of one or
-  // two blocks measured faster than the fused per-head kernel from 8 blocks
-  // on, slower at 4.
+  // per block); by default when the workgroups fill the round at least 3/4,
+  // or from 8 blocks on at least half of it (below that, the fused path).
+  // Segments of one or two blocks measured faster than the fused per-head
+  // kernel in both cases, slower with 4 blocks filling half the round.
   int64_t nseg = kChainCUs / npairs;
   if (force) {
     nseg = nseg < 2 ? 2 : nseg;
   } else {
     nseg = nseg < nblk ? nseg : nblk;
-    if (nblk < 8 || nseg < 2 || 2 * npairs * nseg < kChainCUs) return pl;
+    const bool full = 4 * npairs * nseg >= 3 * kChainCUs;
+    const bool half_long = nblk >= 8 && 2 * npairs * nseg >= kChainCUs;
+    if (nseg < 2 || !(full || half_long)) return pl;
   }
   nseg = nseg < nblk ? nseg : nblk;
   const int64_t span = (nblk + nseg - 1) / nseg;

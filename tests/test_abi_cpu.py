@@ -148,8 +148,8 @@ def _chain_plan(b, L, H, force):
     """(segments, blocks per segment, blocks per unit, units per head) of the
     chain bf16 path: one segment unless the pairs alone do not fill the 256
     compute units; then as many segments as fill one round (at most one per
-    block), by default from 8 blocks on and with the round at least half
-    full."""
+    block), by default when they fill it at least 3/4, or from 8 blocks on at
+    least half."""
     npairs, nblk = b * H // 2, -(-L // 128)
     if npairs <= 0 or nblk < 2:
         return 1, nblk, 0, 0
@@ -158,7 +158,9 @@ def _chain_plan(b, L, H, force):
         nseg = max(nseg, 2)
     else:
         nseg = min(nseg, nblk)
-        if nblk < 8 or nseg < 2 or 2 * npairs * nseg < 256:
+        full = 4 * npairs * nseg >= 3 * 256
+        half_long = nblk >= 8 and 2 * npairs * nseg >= 256
+        if nseg < 2 or not (full or half_long):
             return 1, nblk, 0, 0
     nseg = min(nseg, nblk)
     span = -(-nblk // nseg)
@@ -183,7 +185,9 @@ def test_chain_plan():
     assert _chain_plan(1, 1000, 8, False)[0] == 1                  # a quarter of the CUs
     assert _chain_plan(2, 2048, 32, False) == (8, 2, 2, 7)         # 32 pairs, 16 blocks
     assert _chain_plan(2, 1024, 32, False) == (8, 1, 1, 7)         # one block per segment
-    assert _chain_plan(2, 512, 32, False)[0] == 1                  # 4 blocks: fused
+    assert _chain_plan(2, 512, 32, False)[0] == 1                  # 4 blocks, half: fused
+    assert _chain_plan(8, 512, 32, False) == (2, 2, 2, 1)          # 128 pairs x 2: full
+    assert _chain_plan(2, 768, 32, False) == (6, 1, 1, 5)          # 3/4 of the round
     assert _chain_plan(1, 2048, 16, False) == (16, 1, 1, 15)       # half the CUs
 
 
@@ -405,7 +409,8 @@ def test_taken_path():
     assert tp(1, 65536, 128, 64, 128, 8, 256, 1) == "chain_segmented"  # 64 pairs x 4 segments
     assert tp(1, 1000, 8, 64, 128, 2, 256, 1) == "fused_head"       # too few pairs to segment
     assert tp(2, 2048, 32, 64, 128, 1, 256, 1) == "chain_segmented"  # 32 pairs x 8 segments
-    assert tp(2, 512, 32, 64, 128, 1, 256, 1) == "fused_head"       # 4 blocks
+    assert tp(2, 512, 32, 64, 128, 1, 256, 1) == "fused_head"       # 4 blocks, half the CUs
+    assert tp(8, 512, 32, 64, 128, 4, 256, 1) == "chain_segmented"  # 128 pairs x 2 segments
     assert tp(2, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # fp32, one round
     assert tp(4, 2048, 32, 64, 128, 1, 128, 0) == "staged_scan"     # 64-column slices
     assert tp(8, 2048, 32, 64, 128, 1, 128, 0) == "staged"          # two rounds even so

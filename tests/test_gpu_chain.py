@@ -94,6 +94,31 @@ def test_chain_segments_with_units(b, L, H, G, N):
             mask=np.broadcast_to(mask[:, :, None, None], rfin.shape))
 
 
+# shapes whose default path is the segmented chain with segments of one or two
+# blocks: (b, L, H, G); 8 blocks in one-block segments, the same with a ragged
+# last block, 4 blocks in two segments of two filling the round
+SHORT = [(2, 1024, 32, 4), (2, 1024 - 37, 32, 4), (8, 512, 32, 4)]
+
+
+@pytest.mark.parametrize("b,L,H,G", SHORT, ids=[f"b{s[0]}-L{s[1]}-H{s[2]}" for s in SHORT])
+def test_chain_short_segments_default(b, L, H, G):
+    """The default path of these shapes is the segmented chain with segments
+    of a block or two (each folding up to seven one-block units): every head
+    against the oracle, final states included, and against the unsegmented
+    chain."""
+    w, inp, t = _inputs(790 + L + b, b, L, H, 128, G)
+    assert ssd.taken_path(b, L, H, 64, 128, G, 256, ssd.SSD_BF16) == "chain_segmented"
+    log(f"test_chain_short_segments_default b={b} L={L} H={H} G={G}")
+    out, fin = run_gpu(t, 256, init=t["initial_states"])
+    with bf16_path("chain"):
+        out1, fin1 = run_gpu(t, 256, init=t["initial_states"])
+    compare("segmented vs unsegmented out", np64(out), np64(out1), TOL["bf16"])
+    compare("segmented vs unsegmented final", np64(fin), np64(fin1), 1e-4)
+    ref, rfin = _oracle(inp)
+    compare("out", np64(out), ref, TOL["bf16"])
+    compare("final", np64(fin), rfin, TOL["bf16"])
+
+
 def test_chain_segmented_is_the_default_for_the_long_sequence():
     """batch 1 x 65536 at 128 heads: 64 pairs, four segments of 128 blocks,
     units of 16 blocks for the unit-state pass."""
